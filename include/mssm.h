@@ -1,0 +1,189 @@
+/*
+ * mssm.h -- C ABI of libmssm, the MI355X (gfx950) selective-scan forward.
+ *
+ * Sources (web pages on selective state-space models, cited by title and
+ * section):
+ *   [ybb]  "Mamba状态空间模型的硬件感知推理优化：从选择性扫描到并行前缀和"
+ *          (ybb.press/llm/14642) -- section 1: recurrence h_t = A h_{t-1} +
+ *          B x_t, output y_t = C h_t; section 3.1: one fused kernel computing
+ *          the decay exp(A*softplus(dt)), the input term, the scan and
+ *          y = C.h + D*x, returning the final state; section 4: the Mamba-2
+ *          scalar per-step decay; section 5: chunked walk keeping the state
+ *          on chip.
+ *   [mhpq] essay at www.mhpq.cn/news/984979 -- section 2.2: zero-order-hold
+ *          step A_d = exp(A dt) and the skip term D u; section 2.3: the pair
+ *          operator (A1,B1) (+) (A2,B2) = (A2 A1, A2 B1 + B2) whose prefix is
+ *          the scan; section 3.1: diagonal A, elementwise exponential.
+ *   [csdn] "从硬件感知到算法革命：Mamba如何重塑序列建模的计算效率"
+ *          (tencentcloud.csdn.net) -- section 2: Delta = softplus(.), B and C
+ *          input-dependent; section 3: SSM output merged with a SiLU gate.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor arguments are DEVICE pointers owned by the caller, contiguous in
+ *     the stated row-major layouts, 16-byte aligned for the fast path (any
+ *     4-byte (f32) / 2-byte (bf16) aligned pointer is accepted).  They must
+ *     stay valid until the work queued on `stream` has finished.  The library
+ *     keeps no pointer after a call returns.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *     asynchronous: a return of MSSM_OK means the work was queued.  Faults
+ *     inside a kernel surface at the caller's next synchronisation.
+ *   - Outputs are overwritten, never accumulated into.  Outputs must not
+ *     overlap any input (checked on the pointer ranges; MSSM_ERR_INVALID_ARG).
+ *   - Validation happens before any HIP call.  On failure nothing is queued,
+ *     the status is returned and mssm_last_error() (thread-local) describes
+ *     it.  No call aborts, throws or prints.
+ *   - Arithmetic is float32 with float32 state whatever the I/O dtype; bf16
+ *     outputs are rounded to nearest even.
+ *   - Scratch memory, where a kernel variant needs it, is allocated and freed
+ *     stream-ordered on `stream` (hipMallocAsync/hipFreeAsync).
+ */
+#ifndef MSSM_H
+#define MSSM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MSSM_OK = 0,
+    MSSM_ERR_INVALID_ARG = 1,   /* null required pointer, bad dims, aliasing   */
+    MSSM_ERR_UNSUPPORTED = 2,   /* valid but outside this build's limits       */
+    MSSM_ERR_HIP = 3,           /* a HIP runtime call or launch failed          */
+    MSSM_ERR_ALLOC = 4          /* scratch allocation failed                    */
+} mssm_status;
+
+typedef enum {
+    MSSM_F32 = 0,
+    MSSM_BF16 = 1
+} mssm_dtype;
+
+/* Kernel variant selection (for tests and tuning; AUTO picks by shape). */
+typedef enum {
+    MSSM_VARIANT_AUTO = 0,
+    MSSM_VARIANT_ROWSERIAL = 1, /* one lane per (b,d) row, whole-L serial walk */
+    MSSM_VARIANT_CHUNKED = 2,   /* lanes over (row, n), L walked in chunks     */
+    MSSM_VARIANT_LOOKBACK = 3,  /* L split across workgroups, decoupled carry  */
+    MSSM_VARIANT_SSD_RECURRENT = 4,
+    MSSM_VARIANT_SSD_CHUNKED = 5
+} mssm_variant;
+
+/* Sizes of a selective-scan problem. */
+typedef struct {
+    int64_t batch;   /* >= 0 */
+    int64_t seqlen;  /* L >= 0 */
+    int64_t dim;     /* channels D >= 0 */
+    int64_t dstate;  /* state size N, 1 <= N <= MSSM_MAX_DSTATE */
+} mssm_scan_dims;
+
+/* Storage dtypes.  `io` covers the activations (u, delta, B, C, z, y; for
+ * SSD x, dt, B, C, y).  `param` covers A, D, delta_bias / dt_bias and must
+ * be MSSM_F32.  h_last is always float32. */
+typedef struct {
+    int32_t io;      /* mssm_dtype */
+    int32_t param;   /* mssm_dtype, MSSM_F32 only */
+} mssm_dtypes;
+
+#define MSSM_MAX_DSTATE 64      /* selective scan: largest N this build runs */
+#define MSSM_SSD_MAX_DSTATE 256 /* SSD: largest N */
+#define MSSM_SSD_MAX_HEADDIM 256
+
+/*
+ * Selective-scan forward ([ybb] sections 1, 3.1; [mhpq] sections 2.2-2.3,
+ * 3.1; [csdn] sections 2-3).  For every batch b and channel d, from h = 0:
+ *
+ *   dl        = softplus(delta[b,d,t] + delta_bias[d])
+ *   h[n]      = exp(dl * A[d,n]) * h[n] + dl * B[b,n,t] * u[b,d,t]
+ *   y[b,d,t]  = (sum_n C[b,n,t] * h[n] + D[d] * u[b,d,t]) * silu(z[b,d,t])
+ *   h_last[b,d,n] = h[n] after t = L-1
+ *
+ * The recurrence is evaluated as a parallel scan over the pair operator
+ * (a1,b1) (+) (a2,b2) = (a2 a1, a2 b1 + b2); the result equals the
+ * sequential loop up to float32 rounding order.
+ *
+ * Arguments (device pointers unless stated):
+ *   u, delta   (batch, dim, L), dtype `io`           required
+ *   delta_bias (dim) float32                         nullable -> 0
+ *   A          (dim, N) float32 (expected < 0)       required
+ *   B, C       (batch, N, L), dtype `io`             required
+ *   D          (dim) float32                         nullable -> no skip term
+ *   z          (batch, dim, L), dtype `io`           nullable -> no gate
+ *   y          (batch, dim, L), dtype `io`           required (output)
+ *   h_last     (batch, dim, N) float32               nullable (output)
+ * Errors: MSSM_ERR_INVALID_ARG for a null required pointer, a negative
+ * size, N < 1, an unknown dtype, or an output overlapping an input;
+ * MSSM_ERR_UNSUPPORTED for N > MSSM_MAX_DSTATE or param dtype != F32.
+ * batch == 0 or dim == 0: nothing to do, MSSM_OK.  L == 0: h_last is
+ * zero-filled, y is empty.
+ */
+mssm_status mssm_selective_scan_fwd(const void *u, const void *delta,
+                                    const float *delta_bias, const float *A,
+                                    const void *B, const void *C,
+                                    const float *D, const void *z, void *y,
+                                    float *h_last, mssm_scan_dims dims,
+                                    mssm_dtypes dtypes, void *stream);
+
+/* Sizes of a Mamba-2 scalar-decay (SSD) problem. */
+typedef struct {
+    int64_t batch;
+    int64_t seqlen;   /* L */
+    int64_t nheads;   /* H */
+    int64_t headdim;  /* P, 1 <= P <= MSSM_SSD_MAX_HEADDIM */
+    int64_t dstate;   /* N, 1 <= N <= MSSM_SSD_MAX_DSTATE */
+    int64_t ngroups;  /* G >= 1, H % G == 0; head h reads group h / (H/G) */
+    int64_t chunk;    /* chunk length of the matrix-core form; 0 -> 256 */
+} mssm_ssd_dims;
+
+/*
+ * Mamba-2 scalar-decay forward ([ybb] section 4: one decay per step and head,
+ * shared by all state elements; section 6.2: cumulative products taken in
+ * log space).  For every batch b and head h (group g), from S = 0:
+ *
+ *   dl          = softplus(dt[b,t,h] + dt_bias[h])
+ *   S[p][n]     = exp(dl * A[h]) * S[p][n] + dl * x[b,t,h,p] * B[b,t,g,n]
+ *   y[b,t,h,p]  = sum_n C[b,t,g,n] * S[p][n] + D[h] * x[b,t,h,p]
+ *   h_last[b,h,p,n] = S[p][n] after t = L-1
+ *
+ * Arguments (device pointers unless stated):
+ *   x        (batch, L, H, P), dtype `io`     required
+ *   dt       (batch, L, H),    dtype `io`     required
+ *   dt_bias  (H) float32                      nullable -> 0
+ *   A        (H) float32                      required
+ *   B, C     (batch, L, G, N), dtype `io`     required
+ *   D        (H) float32                      nullable -> no skip term
+ *   y        (batch, L, H, P), dtype `io`     required (output)
+ *   h_last   (batch, H, P, N) float32         nullable (output)
+ * Errors as for mssm_selective_scan_fwd; also MSSM_ERR_INVALID_ARG when
+ * H % G != 0 or chunk < 0, MSSM_ERR_UNSUPPORTED beyond the P/N limits.
+ */
+mssm_status mssm_ssd_scalar_fwd(const void *x, const void *dt,
+                                const float *dt_bias, const float *A,
+                                const void *B, const void *C, const float *D,
+                                void *y, float *h_last, mssm_ssd_dims dims,
+                                mssm_dtypes dtypes, void *stream);
+
+/* Force a kernel variant for subsequent calls made by THIS thread
+ * (MSSM_VARIANT_AUTO restores the shape-based choice).  A variant that does
+ * not apply to the entry point or shape makes that call return
+ * MSSM_ERR_UNSUPPORTED.  Returns the previous setting. */
+mssm_variant mssm_force_variant(mssm_variant v);
+
+/* The variant the most recent successful call on this thread launched. */
+mssm_variant mssm_last_variant(void);
+
+/* Static description of a status code (never NULL). */
+const char *mssm_status_string(mssm_status s);
+
+/* Thread-local text of the last error on this thread ("" if none).  The
+ * pointer stays valid until the next library call on the same thread. */
+const char *mssm_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int mssm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSSM_H */

@@ -1,0 +1,104 @@
+"""ctypes declaration of the libmssm C ABI (``include/mssm.h``).
+
+Argument marshalling only.  The library is looked up next to this file;
+if it is absent or fails to load, :func:`lib` raises -- there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmssm.so")
+
+MSSM_OK = 0
+MSSM_ERR_INVALID_ARG = 1
+MSSM_ERR_UNSUPPORTED = 2
+MSSM_ERR_HIP = 3
+MSSM_ERR_ALLOC = 4
+
+MSSM_F32 = 0
+MSSM_BF16 = 1
+
+VARIANT_AUTO = 0
+VARIANT_ROWSERIAL = 1
+VARIANT_CHUNKED = 2
+VARIANT_LOOKBACK = 3
+VARIANT_SSD_RECURRENT = 4
+VARIANT_SSD_CHUNKED = 5
+
+MAX_DSTATE = 64
+SSD_MAX_DSTATE = 256
+SSD_MAX_HEADDIM = 256
+
+# Every symbol the header declares.
+EXPORTED = (
+    "mssm_selective_scan_fwd",
+    "mssm_ssd_scalar_fwd",
+    "mssm_force_variant",
+    "mssm_last_variant",
+    "mssm_status_string",
+    "mssm_last_error",
+    "mssm_version",
+)
+
+
+class ScanDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64)]
+
+
+class SSDDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("chunk", ctypes.c_int64)]
+
+
+class DTypes(ctypes.Structure):
+    _fields_ = [("io", ctypes.c_int32), ("param", ctypes.c_int32)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def _declare(L):
+    vp = ctypes.c_void_p
+    fp = ctypes.c_void_p          # float* passed as raw device addresses
+    L.mssm_selective_scan_fwd.argtypes = [vp, vp, fp, fp, vp, vp, fp, vp, vp,
+                                          fp, ScanDims, DTypes, vp]
+    L.mssm_selective_scan_fwd.restype = ctypes.c_int
+    L.mssm_ssd_scalar_fwd.argtypes = [vp, vp, fp, fp, vp, vp, fp, vp, fp,
+                                      SSDDims, DTypes, vp]
+    L.mssm_ssd_scalar_fwd.restype = ctypes.c_int
+    L.mssm_force_variant.argtypes = [ctypes.c_int]
+    L.mssm_force_variant.restype = ctypes.c_int
+    L.mssm_last_variant.argtypes = []
+    L.mssm_last_variant.restype = ctypes.c_int
+    L.mssm_status_string.argtypes = [ctypes.c_int]
+    L.mssm_status_string.restype = ctypes.c_char_p
+    L.mssm_last_error.argtypes = []
+    L.mssm_last_error.restype = ctypes.c_char_p
+    L.mssm_version.argtypes = []
+    L.mssm_version.restype = ctypes.c_int
+    return L
+
+
+def load(path: str = LIB_PATH):
+    """Load and declare a libmssm build (raises OSError if it cannot)."""
+    if not os.path.exists(path):
+        raise OSError(
+            "libmssm.so not found at %s: build it first "
+            "(python -c 'import __graft_entry__ as g; g.build()')" % path)
+    return _declare(ctypes.CDLL(path))
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            _lib = load()
+    return _lib

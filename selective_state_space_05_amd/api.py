@@ -1,0 +1,170 @@
+"""torch-tensor front end of libmssm.
+
+Each function checks tensor metadata, allocates the outputs with torch
+(device memory), and passes raw device pointers plus the current HIP stream
+to the C ABI.  No arithmetic of the method happens here.
+"""
+from __future__ import annotations
+
+import contextlib
+
+import torch
+
+from . import _lib
+
+
+class MssmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (_status_name(status), message))
+        self.status = status
+
+
+def _status_name(s: int) -> str:
+    try:
+        return _lib.lib().mssm_status_string(s).decode()
+    except OSError:
+        return "status %d" % s
+
+
+def _check(status: int):
+    if status != _lib.MSSM_OK:
+        msg = _lib.lib().mssm_last_error().decode()
+        raise MssmError(status, msg)
+
+
+def _io_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return _lib.MSSM_F32
+    if t.dtype == torch.bfloat16:
+        return _lib.MSSM_BF16
+    raise TypeError("activations must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype=None, device=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if device is not None and t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
+
+
+def _stream_handle(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def version() -> int:
+    return int(_lib.lib().mssm_version())
+
+
+@contextlib.contextmanager
+def forced_variant(variant: int):
+    """Run the enclosed calls (on this thread) with a fixed kernel variant."""
+    L = _lib.lib()
+    prev = L.mssm_force_variant(int(variant))
+    try:
+        yield
+    finally:
+        L.mssm_force_variant(prev)
+
+
+def last_variant() -> int:
+    return int(_lib.lib().mssm_last_variant())
+
+
+def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                       return_last_state=True, out=None, h_out=None):
+    """Selective-scan forward on the GPU.
+
+    u, delta, z: (batch, dim, L) float32 or bfloat16 (all the same dtype);
+    B, C: (batch, N, L) same dtype; A: (dim, N) float32; D, delta_bias:
+    (dim,) float32.  Returns ``(y, h_last)`` with y like u and h_last
+    (batch, dim, N) float32 (None if ``return_last_state`` is False).
+    """
+    L = _lib.lib()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    io = u.dtype
+    for name, t in (("u", u), ("delta", delta), ("B", B), ("C", C), ("z", z)):
+        _need(t, name, io, dev)
+    for name, t in (("A", A), ("D", D), ("delta_bias", delta_bias)):
+        _need(t, name, torch.float32, dev)
+    batch, dim, seqlen = u.shape
+    N = A.shape[1]
+    if delta.shape != u.shape or (z is not None and z.shape != u.shape):
+        raise ValueError("u, delta, z must share one (batch, dim, L) shape")
+    if tuple(A.shape) != (dim, N):
+        raise ValueError("A must be (dim, N)")
+    if tuple(B.shape) != (batch, N, seqlen) or tuple(C.shape) != (batch, N, seqlen):
+        raise ValueError("B and C must be (batch, N, L)")
+    for name, t in (("D", D), ("delta_bias", delta_bias)):
+        if t is not None and tuple(t.shape) != (dim,):
+            raise ValueError("%s must be (dim,)" % name)
+    y = out if out is not None else torch.empty_like(u)
+    _need(y, "out", io, dev)
+    h_last = None
+    if return_last_state:
+        h_last = h_out if h_out is not None else torch.empty(
+            (batch, dim, N), dtype=torch.float32, device=dev)
+        _need(h_last, "h_out", torch.float32, dev)
+    dims = _lib.ScanDims(batch, seqlen, dim, N)
+    dt = _lib.DTypes(_io_dtype(u), _lib.MSSM_F32)
+    with torch.cuda.device(dev):
+        st = L.mssm_selective_scan_fwd(
+            _ptr(u), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C),
+            _ptr(D), _ptr(z), _ptr(y), _ptr(h_last), dims, dt,
+            _stream_handle(dev))
+    _check(st)
+    return y, h_last
+
+
+def ssd_scalar_fwd(x, dt, A, B, C, D=None, dt_bias=None, chunk=0,
+                   return_last_state=True, out=None, h_out=None):
+    """Mamba-2 scalar-decay forward on the GPU.
+
+    x: (batch, L, H, P); dt: (batch, L, H); B, C: (batch, L, G, N), all in
+    one activation dtype; A, D, dt_bias: (H,) float32.  Returns
+    ``(y, h_last)``: y like x, h_last (batch, H, P, N) float32.
+    """
+    L = _lib.lib()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    io = x.dtype
+    for name, t in (("x", x), ("dt", dt), ("B", B), ("C", C)):
+        _need(t, name, io, dev)
+    for name, t in (("A", A), ("D", D), ("dt_bias", dt_bias)):
+        _need(t, name, torch.float32, dev)
+    batch, seqlen, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if tuple(dt.shape) != (batch, seqlen, H):
+        raise ValueError("dt must be (batch, L, H)")
+    if tuple(B.shape) != (batch, seqlen, G, N) or tuple(C.shape) != tuple(B.shape):
+        raise ValueError("B and C must be (batch, L, G, N)")
+    for name, t in (("A", A), ("D", D), ("dt_bias", dt_bias)):
+        if t is not None and tuple(t.shape) != (H,):
+            raise ValueError("%s must be (H,)" % name)
+    y = out if out is not None else torch.empty_like(x)
+    _need(y, "out", io, dev)
+    h_last = None
+    if return_last_state:
+        h_last = h_out if h_out is not None else torch.empty(
+            (batch, H, P, N), dtype=torch.float32, device=dev)
+        _need(h_last, "h_out", torch.float32, dev)
+    dims = _lib.SSDDims(batch, seqlen, H, P, N, G, int(chunk))
+    dtp = _lib.DTypes(_io_dtype(x), _lib.MSSM_F32)
+    with torch.cuda.device(dev):
+        st = L.mssm_ssd_scalar_fwd(
+            _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
+            _ptr(D), _ptr(y), _ptr(h_last), dims, dtp, _stream_handle(dev))
+    _check(st)
+    return y, h_last

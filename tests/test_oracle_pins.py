@@ -1,0 +1,339 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+CPU only.  Each test names the fact it pins; tolerances are for float64
+against float64 (different association orders agree to a few hundred ulps).
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import pins
+from selective_state_space_05_amd import inputs
+
+TOL = 1e-12
+
+
+def _small(batch, L, dim, N, seed, io="f32", bias="scalar", gate=False,
+           skip=True):
+    p = inputs.ScanProblem("t", batch, L, dim, N, io, bias, gate, skip, seed)
+    return inputs.scan_inputs(p)
+
+
+def _run(oracle_mod, x, **kw):
+    return oracle_mod.selective_scan(x["u"], x["delta"], x["A"], x["B"],
+                                     x["C"], x["D"], x["z"], x["delta_bias"],
+                                     **kw)
+
+
+# -- closed form ---------------------------------------------------------------
+def test_tiny_workload_matches_closed_form(oracle_mod):
+    """The 1x64x8x4 fp32 workload: oracle == unrolled closed form."""
+    x = inputs.scan_inputs(inputs.TINY)
+    y, hl = _run(oracle_mod, x)
+    yc, hc = pins.scan_closed_form(x["u"], x["delta"], x["A"], x["B"], x["C"],
+                                   x["D"], x["z"], x["delta_bias"])
+    assert pins.rel_err(y, yc) < TOL
+    assert pins.rel_err(hl, hc) < TOL
+
+
+@settings(max_examples=25, deadline=None)
+@given(batch=st.integers(1, 2), L=st.integers(1, 23), dim=st.integers(1, 3),
+       N=st.integers(1, 5), seed=st.integers(0, 10_000),
+       gate=st.booleans(), skip=st.booleans(),
+       bias=st.sampled_from([None, "scalar", "per_channel"]))
+def test_random_small_matches_closed_form(oracle_mod, batch, L, dim, N, seed,
+                                          gate, skip, bias):
+    x = _small(batch, L, dim, N, seed, bias=bias, gate=gate, skip=skip)
+    y, hl = _run(oracle_mod, x)
+    yc, hc = pins.scan_closed_form(x["u"], x["delta"], x["A"], x["B"], x["C"],
+                                   x["D"], x["z"], x["delta_bias"])
+    assert pins.rel_err(y, yc) < TOL
+    assert pins.rel_err(hl, hc) < TOL
+
+
+def test_nonzero_initial_state_matches_closed_form(oracle_mod):
+    x = _small(2, 17, 3, 4, 11, gate=True)
+    h0 = np.random.default_rng(5).standard_normal((2, 3, 4))
+    y, hl = _run(oracle_mod, x, h0=h0)
+    yc, hc = pins.scan_closed_form(x["u"], x["delta"], x["A"], x["B"], x["C"],
+                                   x["D"], x["z"], x["delta_bias"], h0=h0)
+    assert pins.rel_err(y, yc) < TOL
+    assert pins.rel_err(hl, hc) < TOL
+
+
+def test_bf16_valued_inputs_match_closed_form(oracle_mod):
+    x = _small(1, 40, 4, 16, 3, io="bf16", gate=True)
+    y, hl = _run(oracle_mod, x)
+    yc, hc = pins.scan_closed_form(x["u"], x["delta"], x["A"], x["B"], x["C"],
+                                   x["D"], x["z"], x["delta_bias"])
+    assert pins.rel_err(y, yc) < TOL
+    assert pins.rel_err(hl, hc) < TOL
+
+
+# -- lifting / association order -----------------------------------------------
+@pytest.mark.parametrize("L", [1, 2, 37, 64, 200])
+def test_lifting_prefix_products_match(oracle_mod, L):
+    x = _small(2, L, 3, 4, 100 + L, gate=True, bias="per_channel")
+    y, hl = _run(oracle_mod, x)
+    yl, hll = pins.scan_lifting(x["u"], x["delta"], x["A"], x["B"], x["C"],
+                                x["D"], x["z"], x["delta_bias"])
+    assert pins.rel_err(y, yl) < TOL
+    assert pins.rel_err(hl, hll) < TOL
+
+
+def test_pair_operator_associative_exactly():
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        p, q, r = pins.random_rational_pairs(rng, 3)
+        assert pins.combine(pins.combine(p, q), r) == pins.combine(p, pins.combine(q, r))
+
+
+def test_pair_operator_identity_and_noncommutative():
+    rng = np.random.default_rng(1)
+    e = (Fraction(1), Fraction(0))
+    p, q = pins.random_rational_pairs(rng, 2)
+    assert pins.combine(e, p) == p and pins.combine(p, e) == p
+    assert pins.combine(p, q) != pins.combine(q, p)
+
+
+@pytest.mark.parametrize("n", [1, 2, 5, 37, 64])
+def test_any_bracketing_equals_sequential_fold_exactly(n):
+    rng = np.random.default_rng(n)
+    pairs = pins.random_rational_pairs(rng, n)
+    seq = pins.fold_sequential(pairs)
+    assert pins.fold_tree(pairs) == seq
+    for k in (1, 3, 8, n):
+        assert pins.fold_chunked(pairs, k) == seq
+
+
+def test_blelloch_exclusive_scan_equals_sequential_prefixes_exactly():
+    rng = np.random.default_rng(7)
+    pairs = pins.random_rational_pairs(rng, 32)
+    e = (Fraction(1), Fraction(0))
+    excl = pins.exclusive_scan_blelloch(pairs, e)
+    acc = e
+    for i, p in enumerate(pairs):
+        assert excl[i] == acc
+        acc = pins.combine(acc, p)
+
+
+def test_exact_fold_of_oracle_step_terms_equals_oracle_state(oracle_mod):
+    """The float64 decays/inputs of one row, folded exactly with the pair
+    operator, give the oracle's final state to float64 accuracy."""
+    x = _small(1, 300, 1, 3, 9)
+    _, hl = _run(oracle_mod, x)
+    _, a, bu = pins._step_terms(x["u"], x["delta"], x["A"], x["B"],
+                                x["delta_bias"], 0, 0)
+    for n in range(3):
+        pairs = [(Fraction(float(a[t, n])), Fraction(float(bu[t, n]))) for t in range(300)]
+        ref = float(pins.fold_tree(pairs)[1])
+        assert abs(hl[0, 0, n] - ref) <= 1e-13 * max(1.0, abs(ref))
+
+
+# -- special cases -------------------------------------------------------------
+def test_zero_A_is_cumsum(oracle_mod):
+    x = _small(2, 50, 3, 4, 21, skip=False)
+    x["A"] = np.zeros_like(x["A"])
+    y, hl = _run(oracle_mod, x)
+    for b in range(2):
+        for d in range(3):
+            h = pins.cumsum_case(x["u"], x["delta"], x["B"], x["delta_bias"], b, d)
+            yref = np.einsum("nt,tn->t", x["C"][b].astype(np.float64), h)
+            assert pins.rel_err(y[b, d], yref) < TOL
+            assert pins.rel_err(hl[b, d], h[-1]) < TOL
+
+
+@pytest.mark.parametrize("L", [1, 10, 4096, 1 << 20])
+def test_constant_step_is_geometric_series(oracle_mod, L):
+    """Constant delta, u, B: h_t = b (1 - a^{t+1}) / (1 - a), up to the
+    million-step length."""
+    dr, bias, Aval, uval, Bval = -1.3, 0.5, -2.7, 0.8, 1.1
+    u = np.full((1, 1, L), uval)
+    delta = np.full((1, 1, L), dr)
+    B = np.full((1, 1, L), Bval)
+    C = np.ones((1, 1, L))
+    A = np.array([[Aval]])
+    y, hl = oracle_mod.selective_scan(u, delta, A, B, C, None, None,
+                                      np.array([bias]))
+    dl = math.log1p(math.exp(dr + bias))
+    a = math.exp(dl * Aval)
+    h = pins.geometric_case(a, dl * Bval * uval, L)
+    assert pins.max_rel_elem(y[0, 0], h) < 1e-10
+    assert abs(hl[0, 0, 0] - h[-1]) <= 1e-10 * abs(h[-1])
+
+
+def test_constant_decay_is_first_order_iir(oracle_mod):
+    """N = 1 and constant delta: h = lfilter([1], [1, -a], delta * B * u)."""
+    L = 500
+    rng = np.random.default_rng(3)
+    u = rng.standard_normal((1, 1, L))
+    B = rng.standard_normal((1, 1, L))
+    C = rng.standard_normal((1, 1, L))
+    delta = np.full((1, 1, L), -0.7)
+    A = np.array([[-0.4]])
+    y, hl = oracle_mod.selective_scan(u, delta, A, B, C, None, None, None)
+    dl = math.log1p(math.exp(-0.7))
+    h = pins.lfilter_case(math.exp(dl * -0.4), dl * B[0, 0] * u[0, 0])
+    assert pins.rel_err(y[0, 0], C[0, 0] * h) < TOL
+    assert abs(hl[0, 0, 0] - h[-1]) <= TOL * abs(h[-1])
+
+
+def test_very_negative_A_is_memoryless(oracle_mod):
+    """delta*A -> -inf: every decay underflows to 0 and h_t = delta_t B_t u_t,
+    so y_t = delta_t u_t (C_t . B_t) + D u_t."""
+    x = _small(2, 30, 3, 5, 8)
+    x["A"] = np.full_like(x["A"], -1e4)
+    y, hl = _run(oracle_mod, x)
+    for b in range(2):
+        for d in range(3):
+            dl = pins.softplus_lib(x["delta"][b, d].astype(np.float64) + x["delta_bias"][d])
+            cb = np.einsum("nt,nt->t", x["C"][b].astype(np.float64), x["B"][b].astype(np.float64))
+            ud = x["u"][b, d].astype(np.float64)
+            ref = dl * ud * cb + float(x["D"][d]) * ud
+            assert pins.rel_err(y[b, d], ref) < TOL
+
+
+def test_state_bounded_and_finite(oracle_mod):
+    """A < 0 and delta > 0 give decays in (0, 1), so
+    |h_t[n]| <= max|delta B u| / (1 - max decay); no NaN/Inf anywhere."""
+    x = _small(2, 300, 4, 16, 13, gate=True)
+    y, hl = _run(oracle_mod, x)
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(hl))
+    for b in range(2):
+        for d in range(4):
+            _, a, bu = pins._step_terms(x["u"], x["delta"], x["A"], x["B"],
+                                        x["delta_bias"], b, d)
+            assert np.all(a > 0) and np.all(a < 1)
+            bound = np.max(np.abs(bu), axis=0) / (1 - np.max(a, axis=0))
+            assert np.all(np.abs(hl[b, d]) <= bound * (1 + 1e-12))
+
+
+def test_linear_in_u_without_gate(oracle_mod):
+    x1 = _small(2, 60, 3, 4, 30)
+    x2 = _small(2, 60, 3, 4, 31)
+    al, be = 0.75, -1.5
+    y1, h1 = _run(oracle_mod, x1)
+    x2s = dict(x1, u=x2["u"])
+    y2, h2 = _run(oracle_mod, x2s)
+    x3 = dict(x1, u=al * x1["u"].astype(np.float64) + be * x2["u"].astype(np.float64))
+    y3, h3 = _run(oracle_mod, x3)
+    assert pins.rel_err(y3, al * y1 + be * y2) < TOL
+    assert pins.rel_err(h3, al * h1 + be * h2) < TOL
+
+
+@pytest.mark.parametrize("split", [1, 17, 63])
+def test_resume_from_h_last(oracle_mod, split):
+    x = _small(2, 64, 3, 4, 44, gate=True, bias="per_channel")
+    y, hl = _run(oracle_mod, x)
+    first = {k: (v[..., :split] if k in ("u", "delta", "z", "B", "C") and v is not None else v)
+             for k, v in x.items()}
+    rest = {k: (v[..., split:] if k in ("u", "delta", "z", "B", "C") and v is not None else v)
+            for k, v in x.items()}
+    y1, h1 = _run(oracle_mod, first)
+    y2, h2 = _run(oracle_mod, rest, h0=h1)
+    assert pins.rel_err(np.concatenate([y1, y2], axis=-1), y) < 1e-13
+    assert pins.rel_err(h2, hl) < 1e-13
+
+
+def test_rows_independent_sampling(oracle_mod):
+    x = _small(2, 33, 5, 4, 2, gate=True)
+    y, hl = _run(oracle_mod, x)
+    rows = [(1, 4), (0, 0), (1, 2)]
+    ys, hs = oracle_mod.selective_scan_rows(rows, x["u"], x["delta"], x["A"],
+                                            x["B"], x["C"], x["D"], x["z"],
+                                            x["delta_bias"])
+    for i, (b, d) in enumerate(rows):
+        assert np.array_equal(ys[i], y[b, d]) and np.array_equal(hs[i], hl[b, d])
+
+
+def test_thread_count_does_not_change_bits(oracle_mod):
+    x = _small(2, 100, 16, 4, 6, gate=True)
+    y1, h1 = _run(oracle_mod, x, nthreads=1)
+    y8, h8 = _run(oracle_mod, x, nthreads=8)
+    assert np.array_equal(y1, y8) and np.array_equal(h1, h8)
+
+
+def test_empty_sequence(oracle_mod):
+    x = _small(1, 1, 2, 3, 0)
+    x = {k: (v[..., :0] if k in ("u", "delta", "z", "B", "C") and v is not None else v)
+         for k, v in x.items()}
+    y, hl = _run(oracle_mod, x)
+    assert y.shape == (1, 2, 0) and np.all(hl == 0)
+
+
+def test_softplus_and_silu_match_library_routines(oracle_mod):
+    xs = np.concatenate([np.linspace(-40, 40, 801), [-745.0, -30.5, 1e-300, 700.0]])
+    sp = np.array([oracle_mod.softplus(v) for v in xs])
+    assert pins.max_rel_elem(sp, pins.softplus_lib(xs)) < 1e-15
+    zs = np.linspace(-30, 30, 601)
+    si = np.array([oracle_mod.silu(v) for v in zs])
+    ref = pins.silu_lib(zs)
+    assert np.max(np.abs(si - ref) / np.maximum(np.abs(ref), 1e-300)) < 1e-15
+
+
+# -- SSD -----------------------------------------------------------------------
+def _ssd_small(batch, L, H, P, N, G, seed, bias=True):
+    p = inputs.SSDProblem("t", batch, L, H, P, N, G, "f32", seed, bias=bias)
+    return inputs.ssd_inputs(p)
+
+
+def _ssd_run(oracle_mod, s, **kw):
+    return oracle_mod.ssd(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"],
+                          s["dt_bias"], **kw)
+
+
+def test_ssd_equals_tied_selective_scan(oracle_mod):
+    s = _ssd_small(2, 45, 3, 4, 6, 1, 1)
+    y, hl = _ssd_run(oracle_mod, s)
+    t = pins.ssd_as_scan(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["dt_bias"])
+    ys, hs = oracle_mod.selective_scan(t["u"], t["delta"], t["A"], t["B"], t["C"],
+                                       t["D"], None, t["delta_bias"])
+    batch, L, H, P = s["x"].shape
+    assert pins.rel_err(ys.reshape(batch, H, P, L).transpose(0, 3, 1, 2), y, axis=1) < 1e-13
+    assert pins.rel_err(hs.reshape(batch, H, P, -1), hl) < 1e-13
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_ssd_quadratic_form(oracle_mod, G):
+    s = _ssd_small(2, 70, 4, 3, 8, G, 2 + G)
+    y, _ = _ssd_run(oracle_mod, s)
+    yq = pins.ssd_quadratic(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["dt_bias"])
+    assert pins.rel_err(y, yq, axis=1) < TOL
+
+
+@pytest.mark.parametrize("Q", [1, 7, 64, 256, 300])
+def test_ssd_chunked_form_equals_recurrence(oracle_mod, Q):
+    s = _ssd_small(1, 300, 2, 5, 16, 1, 9)
+    y, hl = _ssd_run(oracle_mod, s)
+    yc, hc = pins.ssd_chunked(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"],
+                              s["dt_bias"], Q=Q)
+    assert pins.rel_err(y, yc, axis=1) < TOL
+    assert pins.rel_err(hl, hc) < TOL
+
+
+def test_ssd_rows_sampling(oracle_mod):
+    s = _ssd_small(2, 20, 4, 3, 5, 2, 12)
+    y, hl = _ssd_run(oracle_mod, s)
+    rows = [(0, 3, 2), (1, 0, 0), (1, 2, 1)]
+    ys, hs = oracle_mod.ssd_rows(rows, s["x"], s["dt"], s["A"], s["B"], s["C"],
+                                 s["D"], s["dt_bias"])
+    for i, (b, h, p) in enumerate(rows):
+        assert np.array_equal(ys[i], y[b, :, h, p])
+        assert np.array_equal(hs[i], hl[b, h, p])
+
+
+def test_ssd_resume(oracle_mod):
+    s = _ssd_small(1, 40, 2, 3, 4, 1, 5)
+    y, hl = _ssd_run(oracle_mod, s)
+    cut = 13
+    a = dict(s, x=s["x"][:, :cut], dt=s["dt"][:, :cut], B=s["B"][:, :cut], C=s["C"][:, :cut])
+    b = dict(s, x=s["x"][:, cut:], dt=s["dt"][:, cut:], B=s["B"][:, cut:], C=s["C"][:, cut:])
+    y1, h1 = _ssd_run(oracle_mod, a)
+    y2, h2 = _ssd_run(oracle_mod, b, h0=h1)
+    assert pins.rel_err(np.concatenate([y1, y2], axis=1), y, axis=1) < 1e-13
+    assert pins.rel_err(h2, hl) < 1e-13
