@@ -42,6 +42,12 @@
 
 #include <stdint.h>
 
+#if defined(MSSM_BUILDING_LIBRARY)
+#define MSSM_API __attribute__((visibility("default")))
+#else
+#define MSSM_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -117,7 +123,7 @@ typedef struct {
  * batch == 0 or dim == 0: nothing to do, MSSM_OK.  L == 0: h_last is
  * zero-filled, y is empty.
  */
-mssm_status mssm_selective_scan_fwd(const void *u, const void *delta,
+MSSM_API mssm_status mssm_selective_scan_fwd(const void *u, const void *delta,
                                     const float *delta_bias, const float *A,
                                     const void *B, const void *C,
                                     const float *D, const void *z, void *y,
@@ -157,7 +163,7 @@ typedef struct {
  * Errors as for mssm_selective_scan_fwd; also MSSM_ERR_INVALID_ARG when
  * H % G != 0 or chunk < 0, MSSM_ERR_UNSUPPORTED beyond the P/N limits.
  */
-mssm_status mssm_ssd_scalar_fwd(const void *x, const void *dt,
+MSSM_API mssm_status mssm_ssd_scalar_fwd(const void *x, const void *dt,
                                 const float *dt_bias, const float *A,
                                 const void *B, const void *C, const float *D,
                                 void *y, float *h_last, mssm_ssd_dims dims,
@@ -167,20 +173,20 @@ mssm_status mssm_ssd_scalar_fwd(const void *x, const void *dt,
  * (MSSM_VARIANT_AUTO restores the shape-based choice).  A variant that does
  * not apply to the entry point or shape makes that call return
  * MSSM_ERR_UNSUPPORTED.  Returns the previous setting. */
-mssm_variant mssm_force_variant(mssm_variant v);
+MSSM_API mssm_variant mssm_force_variant(mssm_variant v);
 
 /* The variant the most recent successful call on this thread launched. */
-mssm_variant mssm_last_variant(void);
+MSSM_API mssm_variant mssm_last_variant(void);
 
 /* Static description of a status code (never NULL). */
-const char *mssm_status_string(mssm_status s);
+MSSM_API const char *mssm_status_string(mssm_status s);
 
 /* Thread-local text of the last error on this thread ("" if none).  The
  * pointer stays valid until the next library call on the same thread. */
-const char *mssm_last_error(void);
+MSSM_API const char *mssm_last_error(void);
 
 /* Library version as major*10000 + minor*100 + patch. */
-int mssm_version(void);
+MSSM_API int mssm_version(void);
 
 #ifdef __cplusplus
 }

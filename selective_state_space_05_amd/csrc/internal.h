@@ -1,0 +1,54 @@
+// internal.h -- interface between the C-ABI front end (mssm_api.cpp) and the
+// kernel translation units.  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mssm {
+
+enum IoType : int { IO_F32 = 0, IO_BF16 = 1 };
+
+// One selective-scan problem, already validated.  Layouts as in mssm.h:
+// u, delta, z, y (batch, dim, L); B, C (batch, N, L); A (dim, N);
+// delta_bias, D (dim); h_last (batch, dim, N).
+struct ScanArgs {
+    const void *u;
+    const void *delta;
+    const float *delta_bias;  // may be null
+    const float *A;
+    const void *B;
+    const void *C;
+    const float *D;           // may be null
+    const void *z;            // may be null
+    void *y;
+    float *h_last;            // may be null
+    int64_t batch, L, dim, N;
+    IoType io;
+};
+
+// One SSD problem, already validated.  Layouts as in mssm.h.
+struct SSDArgs {
+    const void *x;
+    const void *dt;
+    const float *dt_bias;     // may be null
+    const float *A;
+    const void *B;
+    const void *C;
+    const float *D;           // may be null
+    void *y;
+    float *h_last;            // may be null
+    int64_t batch, L, H, P, N, G, chunk;
+    IoType io;
+};
+
+// Each launcher queues its kernel(s) on `stream` and returns the launch
+// status.  Shapes have been checked against the launcher's limits by the
+// caller (see the *_supported helpers).
+hipError_t launch_scan_rowserial(const ScanArgs &a, hipStream_t stream);
+bool scan_rowserial_supported(const ScanArgs &a);
+
+hipError_t launch_ssd_recurrent(const SSDArgs &a, hipStream_t stream);
+bool ssd_recurrent_supported(const SSDArgs &a);
+
+}  // namespace mssm

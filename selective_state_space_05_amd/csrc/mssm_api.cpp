@@ -1,0 +1,261 @@
+// mssm_api.cpp -- the C ABI of libmssm (declared in include/mssm.h):
+// argument validation, kernel-variant choice and launch on the caller's
+// stream.  Validation runs before any HIP call, so every error path can be
+// exercised without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+#include <string>
+
+#include "internal.h"
+#include "mssm.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local mssm_variant g_forced = MSSM_VARIANT_AUTO;
+thread_local mssm_variant g_last_variant = MSSM_VARIANT_AUTO;
+
+mssm_status fail(mssm_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+mssm_status hip_fail(hipError_t e, const char *what) {
+    return fail(MSSM_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), static_cast<int>(e));
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out) {
+    return !__builtin_mul_overflow(a, b, out);
+}
+
+// Byte range [p, p + n) of one operand, for the overlap check.
+struct Range {
+    const char *name;
+    uintptr_t lo, hi;
+};
+
+Range range(const char *name, const void *p, int64_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{name, lo, p ? lo + static_cast<uintptr_t>(bytes) : lo};
+}
+
+bool overlaps(const Range &a, const Range &b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Fill n floats with zero.  A kernel rather than hipMemsetAsync so that the
+// call stays safe to record into a HIP graph.
+__global__ void zero_fill_kernel(float *p, int64_t n) {
+    int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (; i < n; i += stride) p[i] = 0.0f;
+}
+
+hipError_t zero_fill(float *p, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
+mssm_status check_dtypes(mssm_dtypes dt) {
+    if (dt.io != MSSM_F32 && dt.io != MSSM_BF16)
+        return fail(MSSM_ERR_INVALID_ARG, "unknown io dtype %d", dt.io);
+    if (dt.param != MSSM_F32 && dt.param != MSSM_BF16)
+        return fail(MSSM_ERR_INVALID_ARG, "unknown param dtype %d", dt.param);
+    if (dt.param != MSSM_F32)
+        return fail(MSSM_ERR_UNSUPPORTED, "param dtype must be MSSM_F32");
+    return MSSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mssm_status mssm_selective_scan_fwd(const void *u, const void *delta,
+                                    const float *delta_bias, const float *A,
+                                    const void *B, const void *C,
+                                    const float *D, const void *z, void *y,
+                                    float *h_last, mssm_scan_dims dims,
+                                    mssm_dtypes dtypes, void *stream) {
+    g_last_error.clear();
+    if (mssm_status s = check_dtypes(dtypes)) return s;
+    const int64_t batch = dims.batch, L = dims.seqlen, dim = dims.dim, N = dims.dstate;
+    if (batch < 0 || L < 0 || dim < 0)
+        return fail(MSSM_ERR_INVALID_ARG, "negative size (batch %lld, L %lld, dim %lld)",
+                    (long long)batch, (long long)L, (long long)dim);
+    if (N < 1) return fail(MSSM_ERR_INVALID_ARG, "dstate must be >= 1, got %lld", (long long)N);
+    if (N > MSSM_MAX_DSTATE)
+        return fail(MSSM_ERR_UNSUPPORTED, "dstate %lld exceeds MSSM_MAX_DSTATE (%d)",
+                    (long long)N, MSSM_MAX_DSTATE);
+    const int64_t esz = dtypes.io == MSSM_F32 ? 4 : 2;
+    int64_t rows, act, act_bytes, bc, bc_bytes, dn, hl;
+    if (!mul_ok(batch, dim, &rows) || !mul_ok(rows, L, &act) || !mul_ok(act, esz, &act_bytes) ||
+        !mul_ok(batch, N, &bc) || !mul_ok(bc, L, &bc) || !mul_ok(bc, esz, &bc_bytes) ||
+        !mul_ok(dim, N, &dn) || !mul_ok(rows, N, &hl) || !mul_ok(hl, 4, &hl))
+        return fail(MSSM_ERR_INVALID_ARG, "sizes overflow int64");
+    if (rows == 0) {
+        g_last_variant = MSSM_VARIANT_AUTO;
+        return MSSM_OK;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (L == 0) {
+        if (h_last) {
+            hipError_t e = zero_fill(h_last, rows * N, st);
+            if (e != hipSuccess) return hip_fail(e, "zero-fill of h_last");
+        }
+        g_last_variant = MSSM_VARIANT_AUTO;
+        return MSSM_OK;
+    }
+    if (!u) return fail(MSSM_ERR_INVALID_ARG, "u is null");
+    if (!delta) return fail(MSSM_ERR_INVALID_ARG, "delta is null");
+    if (!A) return fail(MSSM_ERR_INVALID_ARG, "A is null");
+    if (!B) return fail(MSSM_ERR_INVALID_ARG, "B is null");
+    if (!C) return fail(MSSM_ERR_INVALID_ARG, "C is null");
+    if (!y) return fail(MSSM_ERR_INVALID_ARG, "y is null");
+
+    const Range ins[] = {
+        range("u", u, act_bytes),          range("delta", delta, act_bytes),
+        range("z", z, act_bytes),          range("B", B, bc_bytes),
+        range("C", C, bc_bytes),           range("A", A, dn * 4),
+        range("D", D, dim * 4),            range("delta_bias", delta_bias, dim * 4)};
+    const Range outs[] = {range("y", y, act_bytes), range("h_last", h_last, hl)};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlaps(o, i))
+                return fail(MSSM_ERR_INVALID_ARG, "output %s overlaps input %s", o.name, i.name);
+    if (overlaps(outs[0], outs[1])) return fail(MSSM_ERR_INVALID_ARG, "y overlaps h_last");
+
+    mssm::ScanArgs a{u, delta, delta_bias, A, B, C, D, z, y, h_last, batch, L, dim, N,
+                     dtypes.io == MSSM_F32 ? mssm::IO_F32 : mssm::IO_BF16};
+
+    mssm_variant v = g_forced;
+    if (v == MSSM_VARIANT_AUTO) v = MSSM_VARIANT_ROWSERIAL;
+    hipError_t e;
+    switch (v) {
+        case MSSM_VARIANT_ROWSERIAL:
+            if (!mssm::scan_rowserial_supported(a))
+                return fail(MSSM_ERR_UNSUPPORTED, "row-serial variant does not support this shape");
+            e = mssm::launch_scan_rowserial(a, st);
+            break;
+        default:
+            return fail(MSSM_ERR_UNSUPPORTED, "variant %d does not apply to the selective scan",
+                        static_cast<int>(v));
+    }
+    if (e != hipSuccess) return hip_fail(e, "selective-scan launch");
+    g_last_variant = v;
+    return MSSM_OK;
+}
+
+mssm_status mssm_ssd_scalar_fwd(const void *x, const void *dt, const float *dt_bias,
+                                const float *A, const void *B, const void *C,
+                                const float *D, void *y, float *h_last,
+                                mssm_ssd_dims dims, mssm_dtypes dtypes, void *stream) {
+    g_last_error.clear();
+    if (mssm_status s = check_dtypes(dtypes)) return s;
+    const int64_t batch = dims.batch, L = dims.seqlen, H = dims.nheads, P = dims.headdim,
+                  N = dims.dstate, G = dims.ngroups, Q = dims.chunk;
+    if (batch < 0 || L < 0 || H < 0)
+        return fail(MSSM_ERR_INVALID_ARG, "negative size (batch %lld, L %lld, H %lld)",
+                    (long long)batch, (long long)L, (long long)H);
+    if (P < 1 || N < 1) return fail(MSSM_ERR_INVALID_ARG, "headdim and dstate must be >= 1");
+    if (G < 1) return fail(MSSM_ERR_INVALID_ARG, "ngroups must be >= 1");
+    if (H % G != 0)
+        return fail(MSSM_ERR_INVALID_ARG, "nheads %lld is not a multiple of ngroups %lld",
+                    (long long)H, (long long)G);
+    if (Q < 0) return fail(MSSM_ERR_INVALID_ARG, "chunk must be >= 0");
+    if (P > MSSM_SSD_MAX_HEADDIM || N > MSSM_SSD_MAX_DSTATE)
+        return fail(MSSM_ERR_UNSUPPORTED, "headdim %lld / dstate %lld beyond limits (%d / %d)",
+                    (long long)P, (long long)N, MSSM_SSD_MAX_HEADDIM, MSSM_SSD_MAX_DSTATE);
+    const int64_t esz = dtypes.io == MSSM_F32 ? 4 : 2;
+    int64_t bl, xs, x_bytes, dts, dt_bytes, bcs, bc_bytes, pairs, hl;
+    if (!mul_ok(batch, L, &bl) || !mul_ok(bl, H, &dts) || !mul_ok(dts, P, &xs) ||
+        !mul_ok(xs, esz, &x_bytes) || !mul_ok(dts, esz, &dt_bytes) ||
+        !mul_ok(bl, G, &bcs) || !mul_ok(bcs, N, &bcs) || !mul_ok(bcs, esz, &bc_bytes) ||
+        !mul_ok(batch, H, &pairs) || !mul_ok(pairs, P, &hl) || !mul_ok(hl, N, &hl) ||
+        !mul_ok(hl, 4, &hl))
+        return fail(MSSM_ERR_INVALID_ARG, "sizes overflow int64");
+    if (pairs == 0) {
+        g_last_variant = MSSM_VARIANT_AUTO;
+        return MSSM_OK;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (L == 0) {
+        if (h_last) {
+            hipError_t e = zero_fill(h_last, hl / 4, st);
+            if (e != hipSuccess) return hip_fail(e, "zero-fill of h_last");
+        }
+        g_last_variant = MSSM_VARIANT_AUTO;
+        return MSSM_OK;
+    }
+    if (!x) return fail(MSSM_ERR_INVALID_ARG, "x is null");
+    if (!dt) return fail(MSSM_ERR_INVALID_ARG, "dt is null");
+    if (!A) return fail(MSSM_ERR_INVALID_ARG, "A is null");
+    if (!B) return fail(MSSM_ERR_INVALID_ARG, "B is null");
+    if (!C) return fail(MSSM_ERR_INVALID_ARG, "C is null");
+    if (!y) return fail(MSSM_ERR_INVALID_ARG, "y is null");
+    const Range ins[] = {range("x", x, x_bytes),   range("dt", dt, dt_bytes),
+                         range("B", B, bc_bytes),  range("C", C, bc_bytes),
+                         range("A", A, H * 4),     range("D", D, H * 4),
+                         range("dt_bias", dt_bias, H * 4)};
+    const Range outs[] = {range("y", y, x_bytes), range("h_last", h_last, hl)};
+    for (const Range &o : outs)
+        for (const Range &i : ins)
+            if (overlaps(o, i))
+                return fail(MSSM_ERR_INVALID_ARG, "output %s overlaps input %s", o.name, i.name);
+    if (overlaps(outs[0], outs[1])) return fail(MSSM_ERR_INVALID_ARG, "y overlaps h_last");
+
+    mssm::SSDArgs a{x, dt, dt_bias, A, B, C, D, y, h_last, batch, L, H, P, N, G,
+                    Q == 0 ? 256 : Q, dtypes.io == MSSM_F32 ? mssm::IO_F32 : mssm::IO_BF16};
+    mssm_variant v = g_forced;
+    if (v == MSSM_VARIANT_AUTO) v = MSSM_VARIANT_SSD_RECURRENT;
+    hipError_t e;
+    switch (v) {
+        case MSSM_VARIANT_SSD_RECURRENT:
+            if (!mssm::ssd_recurrent_supported(a))
+                return fail(MSSM_ERR_UNSUPPORTED, "recurrent SSD variant does not support this shape");
+            e = mssm::launch_ssd_recurrent(a, st);
+            break;
+        default:
+            return fail(MSSM_ERR_UNSUPPORTED, "variant %d does not apply to the SSD scan",
+                        static_cast<int>(v));
+    }
+    if (e != hipSuccess) return hip_fail(e, "SSD launch");
+    g_last_variant = v;
+    return MSSM_OK;
+}
+
+mssm_variant mssm_force_variant(mssm_variant v) {
+    mssm_variant prev = g_forced;
+    g_forced = v;
+    return prev;
+}
+
+mssm_variant mssm_last_variant(void) { return g_last_variant; }
+
+const char *mssm_status_string(mssm_status s) {
+    switch (s) {
+        case MSSM_OK: return "MSSM_OK";
+        case MSSM_ERR_INVALID_ARG: return "MSSM_ERR_INVALID_ARG";
+        case MSSM_ERR_UNSUPPORTED: return "MSSM_ERR_UNSUPPORTED";
+        case MSSM_ERR_HIP: return "MSSM_ERR_HIP";
+        case MSSM_ERR_ALLOC: return "MSSM_ERR_ALLOC";
+    }
+    return "MSSM_ERR_UNKNOWN";
+}
+
+const char *mssm_last_error(void) { return g_last_error.c_str(); }
+
+int mssm_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,261 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on
+identical seeded inputs.  Needs an MI355X; marked ``gpu``.
+
+Small problems are compared element by element over the whole output; the
+full-size workloads run in the same launch configuration the benchmark
+times and are compared on sampled rows, which the oracle computes exactly
+as in the full problem because rows are independent.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import gates
+from oracle import oracle
+from selective_state_space_05_amd import _lib, inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+SCAN_VARIANTS = [_lib.VARIANT_ROWSERIAL]
+SSD_VARIANTS = [_lib.VARIANT_SSD_RECURRENT]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def to_dev(a, io, dev):
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if io == "bf16" and a.ndim > 1:
+        t = t.to(torch.bfloat16)     # exact: values are already bf16
+    return t.to(dev)
+
+
+def scan_to_dev(x, io, dev):
+    out = {}
+    for k, v in x.items():
+        if k in ("A", "D", "delta_bias"):
+            out[k] = None if v is None else torch.from_numpy(v).to(dev)
+        else:
+            out[k] = to_dev(v, io, dev)
+    return out
+
+
+def run_scan(t, variant=_lib.VARIANT_AUTO, stream=None):
+    import selective_state_space_05_amd as mssm
+    from selective_state_space_05_amd.api import forced_variant
+    with forced_variant(variant):
+        if stream is None:
+            y, h = mssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"],
+                                           t["D"], t["z"], t["delta_bias"])
+        else:
+            with torch.cuda.stream(stream):
+                y, h = mssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"],
+                                               t["C"], t["D"], t["z"], t["delta_bias"])
+            stream.synchronize()
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64), h.cpu().numpy().astype(np.float64)
+
+
+def scan_problem(batch, L, dim, N, io, seed, bias="scalar", gate=True, skip=True):
+    return inputs.ScanProblem("case", batch, L, dim, N, io, bias, gate, skip, seed)
+
+
+def announce(msg):
+    print("\n[gpu case] %s" % msg, flush=True)
+
+
+SMALL_CASES = [
+    # batch, L, dim, N, io, bias, gate, skip
+    (1, 64, 8, 4, "f32", "scalar", False, True),          # the tiny workload
+    (2, 1000, 37, 16, "f32", "per_channel", True, True),   # ragged L and dim
+    (2, 1000, 37, 16, "bf16", "scalar", True, True),
+    (1, 1, 5, 16, "f32", "scalar", True, True),            # single step
+    (3, 7, 3, 1, "f32", None, False, False),               # N = 1, no extras
+    (1, 333, 64, 5, "bf16", "per_channel", False, True),   # odd N
+    (2, 4096 + 37, 40, 16, "bf16", "scalar", True, True),  # several chunks
+    (1, 2048, 130, 32, "f32", "scalar", True, True),       # N = 32
+    (1, 300, 9, 64, "f32", "scalar", True, True),          # N = 64 (limit)
+]
+
+
+@pytest.mark.parametrize("variant", SCAN_VARIANTS)
+@pytest.mark.parametrize("case", SMALL_CASES)
+def test_scan_small_full_compare(dev, variant, case):
+    batch, L, dim, N, io, bias, gate, skip = case
+    p = scan_problem(batch, L, dim, N, io, 1000 + L + dim, bias, gate, skip)
+    announce("scan variant=%d %s" % (variant, case))
+    x = inputs.scan_inputs(p)
+    y, h = run_scan(scan_to_dev(x, io, dev), variant)
+    yo, ho = oracle.selective_scan(x["u"], x["delta"], x["A"], x["B"], x["C"],
+                                   x["D"], x["z"], x["delta_bias"])
+    gates.check(y, yo, io, "y")
+    gates.check_state(h, ho, io, "h_last")
+
+
+def _sampled(p, variant, dev, nrows=12, seed=0):
+    x = inputs.scan_inputs(p)
+    announce("scan variant=%d workload=%s" % (variant, p.name))
+    y, h = run_scan(scan_to_dev(x, p.io, dev), variant)
+    rng = np.random.default_rng(seed)
+    rows = [(0, 0), (p.batch - 1, p.dim - 1)] + [
+        (int(rng.integers(p.batch)), int(rng.integers(p.dim))) for _ in range(nrows - 2)]
+    yo, ho = oracle.selective_scan_rows(rows, x["u"], x["delta"], x["A"], x["B"], x["C"],
+                                        x["D"], x["z"], x["delta_bias"])
+    ys = np.stack([y[b, d] for b, d in rows])
+    hs = np.stack([h[b, d] for b, d in rows])
+    gates.check(ys, yo, p.io, "y %s" % p.name)
+    gates.check_state(hs, ho, p.io, "h_last %s" % p.name)
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(h))
+
+
+FULL = [inputs.MAMBA_130M, inputs.MAMBA_2_8B, inputs.MILLION]
+
+
+@pytest.mark.parametrize("variant", [_lib.VARIANT_AUTO] + SCAN_VARIANTS)
+@pytest.mark.parametrize("p", FULL, ids=[q.name for q in FULL])
+def test_scan_full_size_sampled_rows(dev, variant, p):
+    _sampled(p, variant, dev)
+
+
+@pytest.mark.parametrize("p", FULL, ids=[q.name for q in FULL])
+def test_scan_full_size_scan_isolated(dev, p):
+    """No skip term and no gate: y = C.h exactly, so the scan's own error is
+    not hidden behind D*u."""
+    _sampled(p.replace(skip=False, gate=False), _lib.VARIANT_AUTO, dev, nrows=8, seed=1)
+
+
+@pytest.mark.parametrize("p", [inputs.MAMBA_2_8B, inputs.MILLION],
+                         ids=["mamba2.8b", "million"])
+def test_scan_full_size_per_channel_bias(dev, p):
+    """The other reading of the bias distribution (per channel U(-4, -2))."""
+    _sampled(p.replace(bias="per_channel"), _lib.VARIANT_AUTO, dev, nrows=8, seed=2)
+
+
+def test_scan_deterministic(dev):
+    p = scan_problem(2, 3000, 64, 16, "bf16", 5)
+    t = scan_to_dev(inputs.scan_inputs(p), "bf16", dev)
+    announce("scan determinism")
+    y1, h1 = run_scan(t)
+    y2, h2 = run_scan(t)
+    assert np.array_equal(y1, y2) and np.array_equal(h1, h2)
+
+
+def test_scan_on_side_stream(dev):
+    p = scan_problem(2, 500, 33, 16, "f32", 6)
+    x = inputs.scan_inputs(p)
+    t = scan_to_dev(x, "f32", dev)
+    announce("scan side stream")
+    s = torch.cuda.Stream(dev)
+    y, h = run_scan(t, stream=s)
+    yo, ho = oracle.selective_scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"],
+                                   x["z"], x["delta_bias"])
+    gates.check(y, yo, "f32", "y")
+    gates.check_state(h, ho, "f32", "h_last")
+
+
+def test_scan_zero_length_zero_fills_state(dev):
+    import selective_state_space_05_amd as mssm
+    announce("scan L=0")
+    u = torch.empty((2, 3, 0), device=dev)
+    A = -torch.ones((3, 4), device=dev)
+    B = torch.empty((2, 4, 0), device=dev)
+    h_out = torch.full((2, 3, 4), 7.0, device=dev)
+    y, h = mssm.selective_scan_fwd(u, u.clone(), A, B, B.clone(), h_out=h_out)
+    torch.cuda.synchronize()
+    assert y.shape == (2, 3, 0) and torch.all(h == 0)
+
+
+def test_scan_reports_variant(dev):
+    from selective_state_space_05_amd.api import last_variant
+    p = scan_problem(1, 64, 8, 4, "f32", 7)
+    run_scan(scan_to_dev(inputs.scan_inputs(p), "f32", dev))
+    assert last_variant() != _lib.VARIANT_AUTO
+
+
+# ---------------------------------------------------------------------------
+# SSD
+# ---------------------------------------------------------------------------
+def ssd_to_dev(s, io, dev):
+    out = {}
+    for k, v in s.items():
+        if k in ("A", "D", "dt_bias"):
+            out[k] = None if v is None else torch.from_numpy(v).to(dev)
+        else:
+            out[k] = to_dev(v, io, dev)
+    return out
+
+
+def run_ssd(t, variant=_lib.VARIANT_AUTO, chunk=0):
+    import selective_state_space_05_amd as mssm
+    from selective_state_space_05_amd.api import forced_variant
+    with forced_variant(variant):
+        y, h = mssm.ssd_scalar_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"],
+                                   t["dt_bias"], chunk=chunk)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64), h.cpu().numpy().astype(np.float64)
+
+
+def ssd_rows_of(y):
+    """(batch, L, H, P) -> rows (batch, H, P) of length L."""
+    return np.moveaxis(y, 1, -1)
+
+
+SSD_SMALL = [
+    # batch, L, H, P, N, G, io
+    (1, 300, 2, 8, 16, 1, "f32"),
+    (2, 513, 4, 64, 128, 1, "bf16"),
+    (1, 77, 6, 5, 7, 3, "f32"),
+    (2, 1, 2, 16, 32, 2, "bf16"),
+]
+
+
+@pytest.mark.parametrize("variant", SSD_VARIANTS)
+@pytest.mark.parametrize("case", SSD_SMALL)
+def test_ssd_small_full_compare(dev, variant, case):
+    batch, L, H, P, N, G, io = case
+    announce("ssd variant=%d %s" % (variant, case))
+    p = inputs.SSDProblem("case", batch, L, H, P, N, G, io, 50 + L)
+    s = inputs.ssd_inputs(p)
+    y, h = run_ssd(ssd_to_dev(s, io, dev), variant)
+    yo, ho = oracle.ssd(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["dt_bias"])
+    gates.check(ssd_rows_of(y), ssd_rows_of(yo), io, "y")
+    gates.check_state(h, ho, io, "h_last")
+
+
+@pytest.mark.parametrize("variant", [_lib.VARIANT_AUTO] + SSD_VARIANTS)
+def test_ssd_full_size_sampled_rows(dev, variant):
+    p = inputs.SSD_LAYER
+    announce("ssd variant=%d workload=%s" % (variant, p.name))
+    s = inputs.ssd_inputs(p)
+    y, h = run_ssd(ssd_to_dev(s, p.io, dev), variant)
+    rng = np.random.default_rng(3)
+    rows = [(0, 0, 0), (p.batch - 1, p.nheads - 1, p.headdim - 1)] + [
+        (int(rng.integers(p.batch)), int(rng.integers(p.nheads)), int(rng.integers(p.headdim)))
+        for _ in range(6)]
+    yo, ho = oracle.ssd_rows(rows, s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["dt_bias"])
+    ys = np.stack([y[b, :, hh, pp] for b, hh, pp in rows])
+    hs = np.stack([h[b, hh, pp] for b, hh, pp in rows])
+    gates.check(ys, yo, p.io, "y")
+    gates.check_state(hs, ho, p.io, "h_last")
+    assert np.all(np.isfinite(y))
+
+
+def test_ssd_zero_length_zero_fills_state(dev):
+    import selective_state_space_05_amd as mssm
+    announce("ssd L=0")
+    x = torch.empty((1, 0, 2, 4), device=dev)
+    dt = torch.empty((1, 0, 2), device=dev)
+    B = torch.empty((1, 0, 1, 8), device=dev)
+    A = -torch.ones(2, device=dev)
+    h_out = torch.full((1, 2, 4, 8), 3.0, device=dev)
+    y, h = mssm.ssd_scalar_fwd(x, dt, A, B, B.clone(), h_out=h_out)
+    torch.cuda.synchronize()
+    assert torch.all(h == 0)
