@@ -39,16 +39,16 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // log2(x) on the hardware unit (v_log_f32).
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// log(1 + w) for w >= 0, accurate to a few ulp for every w, including
-// w < 2^-24 where 1 + w rounds to 1.  With s = 1 + w rounded, the ratio
-// log(s) / (s - 1) is evaluated at the point actually represented, which
-// cancels the rounding of s (D. Goldberg, "What every computer scientist
-// should know about floating-point arithmetic", 1991, Theorem 4).
-__device__ __forceinline__ float log1p_nonneg(float w) {
-    float s = 1.0f + w;
-    float ds = s - 1.0f;
-    float r = fast_log2(s) * kLn2 * __builtin_amdgcn_rcpf(ds) * w;
-    return ds == 0.0f ? w : r;
+// log(1 + w) for w in [0, 1], accurate to about 1 ulp for every w including
+// w < 2^-24, where 1 + w rounds to 1.  With s = fl(1 + w), the rounding
+// error c = w - (s - 1) is exact (both subtractions are exact by Sterbenz's
+// lemma), 1 + w = s + c, and log(1 + w) = log(s) + c/s + O(c^2); replacing
+// c/s by c costs at most |c| (s - 1) <= 2^-24 w.  v_log_f32 is accurate to
+// ~1 ulp on (1, 2].
+__device__ __forceinline__ float log1p_unit(float w) {
+    const float s = 1.0f + w;
+    const float c = w - (s - 1.0f);
+    return fmaf(fast_log2(s), kLn2, c);
 }
 
 // softplus(x) = log(1 + e^x) = max(x, 0) + log(1 + e^{-|x|}), through the
@@ -63,8 +63,8 @@ __device__ __forceinline__ float silu_libm(float z) { return z / (1.0f + expf(-z
 
 // softplus on the hardware exponential/logarithm units.
 __device__ __forceinline__ float softplus(float x) {
-    float w = fast_exp2(-fabsf(x) * kLog2e);
-    return fmaxf(x, 0.0f) + log1p_nonneg(w);
+    const float w = fast_exp2(-fabsf(x) * kLog2e);
+    return fmaxf(x, 0.0f) + log1p_unit(w);
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^{-z}).

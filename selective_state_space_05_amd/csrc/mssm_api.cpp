@@ -78,6 +78,14 @@ mssm_status check_dtypes(mssm_dtypes dt) {
     return MSSM_OK;
 }
 
+// Shape-based choice.  Short sequences take the row-serial walk (its single
+// lane per row has nothing to amortise); otherwise the chunked kernel, which
+// evaluates the recurrence in order with one lane per state element.
+mssm_variant choose_scan_variant(const mssm::ScanArgs &a) {
+    if (a.L < 128 || !mssm::scan_chunked_supported(a)) return MSSM_VARIANT_ROWSERIAL;
+    return MSSM_VARIANT_CHUNKED;
+}
+
 }  // namespace
 
 extern "C" {
@@ -140,13 +148,18 @@ mssm_status mssm_selective_scan_fwd(const void *u, const void *delta,
                      dtypes.io == MSSM_F32 ? mssm::IO_F32 : mssm::IO_BF16};
 
     mssm_variant v = g_forced;
-    if (v == MSSM_VARIANT_AUTO) v = MSSM_VARIANT_ROWSERIAL;
+    if (v == MSSM_VARIANT_AUTO) v = choose_scan_variant(a);
     hipError_t e;
     switch (v) {
         case MSSM_VARIANT_ROWSERIAL:
             if (!mssm::scan_rowserial_supported(a))
                 return fail(MSSM_ERR_UNSUPPORTED, "row-serial variant does not support this shape");
             e = mssm::launch_scan_rowserial(a, st);
+            break;
+        case MSSM_VARIANT_CHUNKED:
+            if (!mssm::scan_chunked_supported(a))
+                return fail(MSSM_ERR_UNSUPPORTED, "chunked variant does not support this shape");
+            e = mssm::launch_scan_chunked(a, st);
             break;
         default:
             return fail(MSSM_ERR_UNSUPPORTED, "variant %d does not apply to the selective scan",

@@ -18,7 +18,7 @@ from selective_state_space_05_amd import _lib, inputs
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-SCAN_VARIANTS = [_lib.VARIANT_ROWSERIAL]
+SCAN_VARIANTS = [_lib.VARIANT_ROWSERIAL, _lib.VARIANT_CHUNKED]
 SSD_VARIANTS = [_lib.VARIANT_SSD_RECURRENT]
 
 
@@ -204,8 +204,12 @@ def run_ssd(t, variant=_lib.VARIANT_AUTO, chunk=0):
 
 
 def ssd_rows_of(y):
-    """(batch, L, H, P) -> rows (batch, H, P) of length L."""
-    return np.moveaxis(y, 1, -1)
+    """(batch, L, H, P) -> rows (batch, H) of length L*P.
+
+    A head's whole output block is one row for the normwise gate, so that a
+    row never degenerates to a single bf16-rounded element (L = 1)."""
+    b, L, H, P = y.shape
+    return np.ascontiguousarray(np.moveaxis(y, 2, 1)).reshape(b, H, L * P)
 
 
 SSD_SMALL = [
