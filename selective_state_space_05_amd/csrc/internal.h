@@ -50,7 +50,6 @@ bool scan_rowserial_supported(const ScanArgs &a);
 
 hipError_t launch_scan_chunked(const ScanArgs &a, hipStream_t stream);
 bool scan_chunked_supported(const ScanArgs &a);
-int64_t scan_chunked_waves(const ScanArgs &a);
 
 hipError_t launch_ssd_recurrent(const SSDArgs &a, hipStream_t stream);
 bool ssd_recurrent_supported(const SSDArgs &a);
