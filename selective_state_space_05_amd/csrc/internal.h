@@ -50,6 +50,13 @@ bool scan_rowserial_supported(const ScanArgs &a);
 
 hipError_t launch_scan_chunked(const ScanArgs &a, hipStream_t stream);
 bool scan_chunked_supported(const ScanArgs &a);
+int64_t scan_chunked_waves(const ScanArgs &a);
+// Rows start 16-byte aligned and L % 4 == 0: activations move as vectors.
+bool scan_rows_vectorizable(const ScanArgs &a);
+
+// Chunk-parallel variant; allocates its look-back scratch stream-ordered.
+hipError_t launch_scan_lookback(const ScanArgs &a, hipStream_t stream);
+bool scan_lookback_supported(const ScanArgs &a);
 
 hipError_t launch_ssd_recurrent(const SSDArgs &a, hipStream_t stream);
 bool ssd_recurrent_supported(const SSDArgs &a);

@@ -29,6 +29,8 @@ mssm_status fail(mssm_status s, const char *fmt, ...) {
 }
 
 mssm_status hip_fail(hipError_t e, const char *what) {
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
+        return fail(MSSM_ERR_ALLOC, "%s: %s (%d)", what, hipGetErrorString(e), static_cast<int>(e));
     return fail(MSSM_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), static_cast<int>(e));
 }
 
@@ -79,10 +81,14 @@ mssm_status check_dtypes(mssm_dtypes dt) {
 }
 
 // Shape-based choice.  Short sequences take the row-serial walk (its single
-// lane per row has nothing to amortise); otherwise the chunked kernel, which
-// evaluates the recurrence in order with one lane per state element.
+// lane per row has nothing to amortise).  Long sequences whose channels give
+// the chunked kernel less than one wave per SIMD (1024 on the chip) are cut
+// into segments and take the look-back kernel; everything else takes the
+// chunked kernel, which walks each row in order.
 mssm_variant choose_scan_variant(const mssm::ScanArgs &a) {
     if (a.L < 128 || !mssm::scan_chunked_supported(a)) return MSSM_VARIANT_ROWSERIAL;
+    if (a.L >= 2048 && mssm::scan_chunked_waves(a) < 1024 && mssm::scan_lookback_supported(a))
+        return MSSM_VARIANT_LOOKBACK;
     return MSSM_VARIANT_CHUNKED;
 }
 
@@ -160,6 +166,11 @@ mssm_status mssm_selective_scan_fwd(const void *u, const void *delta,
             if (!mssm::scan_chunked_supported(a))
                 return fail(MSSM_ERR_UNSUPPORTED, "chunked variant does not support this shape");
             e = mssm::launch_scan_chunked(a, st);
+            break;
+        case MSSM_VARIANT_LOOKBACK:
+            if (!mssm::scan_lookback_supported(a))
+                return fail(MSSM_ERR_UNSUPPORTED, "look-back variant does not support this shape");
+            e = mssm::launch_scan_lookback(a, st);
             break;
         default:
             return fail(MSSM_ERR_UNSUPPORTED, "variant %d does not apply to the selective scan",

@@ -1,0 +1,247 @@
+// scan_lookback.hip -- chunk-parallel selective-scan forward for shapes whose
+// channels alone cannot fill the GPU (few channels, very long sequences).
+//
+// The sequence is cut into segments; every (segment k, 16-channel group)
+// pair is one workgroup.  Over a segment the recurrence
+// h_t = a_t h_{t-1} + b_t composes into one pair (P, h_loc): the product of
+// the decays and the state reached from h = 0, and a segment's pair applied
+// to the state entering it gives the state leaving it -- the pair operator
+// (P1,h1) (+) (P2,h2) = (P2 P1, P2 h1 + h2) (www.mhpq.cn/news/984979 essay
+// section 2.3, and its three-phase grid scan: local sweep, carry of block
+// tails, fix-up).  Each workgroup:
+//
+//   1. walks its segment from h = 0 without output (the state-only walk of
+//      scan_core.h), giving h_loc, and forms P = exp(A * sum dl) in log space
+//      ("Mamba状态空间模型的硬件感知推理优化" (ybb.press) section 6.2);
+//   2. waits for the inclusive state of segment k-1 (the true state at its
+//      end), which is its incoming state h_in, and publishes its own
+//      inclusive state P h_in + h_loc;
+//   3. walks its segment again from h_in, now forming y.
+//
+// Steps 1 and 3 -- all of the exponentials -- run in parallel over every
+// segment; only step 2, one fused multiply-add per state element, is
+// chained.  Waiting on the immediate predecessor alone (a look-back of one)
+// fixes the association order, so results are bitwise repeatable.
+//
+// Work is handed out by an atomic ticket in segment-major order, so a
+// workgroup only ever waits for a ticket taken before its own, by a
+// workgroup that is already running: every wait ends.  Published states
+// cross the eight XCDs' separate L2 caches.  Every access to them and to the
+// flags is an agent-scope (coherent) atomic: a writer waits for its state
+// stores to be acknowledged, synchronises the workgroup, then stores the
+// flag; a reader polls the flag, synchronises the workgroup, then loads.
+//
+// The result differs from the sequential loop only by the association of
+// the carried state across segment boundaries and the rounding of P.
+#include <algorithm>
+
+#include "internal.h"
+#include "scan_core.h"
+
+namespace mssm {
+namespace {
+
+using core::kCh;
+
+constexpr uint32_t kFlagInclusive = 1;   // true state at the segment end published
+constexpr uint32_t kFlagTimedOut = 2;    // local marker: the wait gave up
+constexpr uint32_t kMaxSpins = 1u << 24;
+
+__device__ __forceinline__ void store_agent(float *p, float v) {
+    __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's stores have been acknowledged.  The published
+// states are agent-scope (coherent) stores, so once they are acknowledged any
+// agent-scope load sees them; no cache write-back or invalidate is needed --
+// the release/acquire fences of the memory model would write back or drop
+// the whole L2 of this XCD at every hand-over.
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ float load_agent(const float *p) {
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Scratch layout: per item (segment k, global group index gidx) the
+// inclusive state (`slots` floats), then one flag per item, then the ticket
+// counter.
+struct Scratch {
+    float *pay;
+    uint32_t *flags;
+    uint32_t *ticket;
+};
+
+template <typename T, int W, int NPL, bool GATE, bool VEC>
+__global__ __launch_bounds__(64 * W) void scan_lookback_kernel(
+    const T *__restrict__ u, const T *__restrict__ delta,
+    const float *__restrict__ delta_bias, const float *__restrict__ A,
+    const T *__restrict__ Bm, const T *__restrict__ Cm,
+    const float *__restrict__ Dskip, const T *__restrict__ z, T *__restrict__ y,
+    float *__restrict__ h_last, int64_t L, int dim, int N, int groups_per_batch,
+    int total_groups, int64_t seg_len, int nseg, Scratch s) {
+    constexpr int kSlots = 4 * W * NPL * kCh;
+    __shared__ core::Smem<W> sm;
+    __shared__ uint32_t sh_item, sh_flag;
+
+    const int tid = threadIdx.x;
+    if (tid == 0) sh_item = __hip_atomic_fetch_add(s.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int item = static_cast<int>(sh_item);
+    const int k = item / total_groups;               // segment
+    const int gidx = item - k * total_groups;        // (batch, group)
+    const int64_t b = gidx / groups_per_batch;
+    const int d0 = (gidx - static_cast<int>(b) * groups_per_batch) * kCh;
+
+    core::Walker<T, W, NPL, GATE, VEC> wk;
+    wk.init(u, delta, delta_bias, A, Bm, Cm, Dskip, z, y, L, dim, N, b, d0);
+    const int64_t t_begin = static_cast<int64_t>(k) * seg_len;
+    const int64_t t_end = min(L, t_begin + seg_len);
+
+    // ---- 1. local pair of the segment ---------------------------------------
+    float h[NPL];
+#pragma unroll
+    for (int g = 0; g < NPL; ++g) h[g] = 0.0f;
+    wk.template walk<false>(t_begin, t_end, h, sm);
+    const float sdl = wk.channel_dl_sum(sm);
+    float P[NPL];
+#pragma unroll
+    for (int g = 0; g < NPL; ++g) P[g] = fast_exp2(wk.A2[g] * sdl);
+
+    // ---- 2. carry-in from the predecessor, inclusive state out ----------------
+    auto slot = [&](int g) { return (wk.prow * NPL + g) * kCh + wk.j; };
+    auto inc = [&](int seg) {
+        return s.pay + (static_cast<int64_t>(seg) * total_groups + gidx) * kSlots;
+    };
+    float h_in[NPL];
+#pragma unroll
+    for (int g = 0; g < NPL; ++g) h_in[g] = 0.0f;
+    if (k > 0) {
+        if (tid == 0) {
+            const uint32_t *f = s.flags + static_cast<int64_t>(k - 1) * total_groups + gidx;
+            uint32_t v;
+            uint32_t spins = 0;
+            while ((v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
+                __builtin_amdgcn_s_sleep(2);
+                // Bounded wait (about a second): a predecessor that never
+                // publishes would be a bug; the state becomes NaN instead of
+                // the kernel hanging, so the failure is visible.
+                if (++spins == kMaxSpins) { v = kFlagTimedOut; break; }
+            }
+            sh_flag = v;
+        }
+        __syncthreads();
+        const bool timed_out = sh_flag == kFlagTimedOut;
+#pragma unroll
+        for (int g = 0; g < NPL; ++g)
+            h_in[g] = timed_out ? __builtin_nanf("") : load_agent(inc(k - 1) + slot(g));
+    }
+    // inclusive state of this segment: the pair (P, h_loc) applied to h_in
+#pragma unroll
+    for (int g = 0; g < NPL; ++g) store_agent(inc(k) + slot(g), fmaf(P[g], h_in[g], h[g]));
+    stores_done();
+    __syncthreads();
+    if (tid == 0)
+        __hip_atomic_store(s.flags + static_cast<int64_t>(k) * total_groups + gidx, kFlagInclusive,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // ---- 3. output walk from the true incoming state ---------------------------
+#pragma unroll
+    for (int g = 0; g < NPL; ++g) h[g] = h_in[g];
+    wk.template walk<true>(t_begin, t_end, h, sm);
+    if (k == nseg - 1 && h_last && d0 + wk.j < dim) {
+#pragma unroll
+        for (int g = 0; g < NPL; ++g)
+            if (wk.nok[g])
+                h_last[(b * dim + d0 + wk.j) * static_cast<int64_t>(N) + wk.prow * NPL + g] = h[g];
+    }
+}
+
+__global__ void zero_u32_kernel(uint32_t *p, int64_t n) {
+    int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (; i < n; i += stride) p[i] = 0u;
+}
+
+struct Plan {
+    int groups_per_batch, total_groups, nseg;
+    int64_t seg_len;
+};
+
+// Segments: about as many (segment, group) workgroups as the chip holds at
+// once (three per compute unit, 256 units), so every segment runs
+// concurrently and the chained hand-over never waits for a workgroup to be
+// scheduled; each segment is a whole number of 32-step chunks and at least
+// 256 steps long.
+Plan make_plan(const ScanArgs &a) {
+    Plan p;
+    p.groups_per_batch = static_cast<int>((a.dim + kCh - 1) / kCh);
+    p.total_groups = static_cast<int>(a.batch * p.groups_per_batch);
+    const int64_t target_items = 3 * 256;
+    int64_t nseg = (target_items + p.total_groups - 1) / p.total_groups;
+    int64_t seg = (a.L + nseg - 1) / nseg;
+    seg = (seg + core::kT - 1) / core::kT * core::kT;
+    if (seg < 256) seg = 256;
+    p.seg_len = seg;
+    p.nseg = static_cast<int>((a.L + seg - 1) / seg);
+    return p;
+}
+
+template <typename T, int W, int NPL>
+hipError_t launch_typed(const ScanArgs &a, hipStream_t stream) {
+    constexpr int kSlots = 4 * W * NPL * kCh;
+    const Plan p = make_plan(a);
+    const int64_t items = static_cast<int64_t>(p.nseg) * p.total_groups;
+    const size_t pay_bytes = static_cast<size_t>(items) * kSlots * sizeof(float);
+    const size_t flag_bytes = static_cast<size_t>(items + 1) * sizeof(uint32_t);
+    void *mem = nullptr;
+    hipError_t e = hipMallocAsync(&mem, pay_bytes + flag_bytes, stream);
+    if (e != hipSuccess) return e;
+    Scratch s;
+    s.pay = static_cast<float *>(mem);
+    s.flags = reinterpret_cast<uint32_t *>(static_cast<char *>(mem) + pay_bytes);
+    s.ticket = s.flags + items;
+    const int64_t nflags = items + 1;
+    const int zb = static_cast<int>(std::min<int64_t>((nflags + 255) / 256, 1024));
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(zb), dim3(256), 0, stream, s.flags, nflags);
+    e = hipGetLastError();
+    if (e == hipSuccess) {
+        const bool vec = scan_rows_vectorizable(a);
+        decltype(&scan_lookback_kernel<T, W, NPL, true, true>) kern;
+        if (a.z) kern = vec ? scan_lookback_kernel<T, W, NPL, true, true> : scan_lookback_kernel<T, W, NPL, true, false>;
+        else kern = vec ? scan_lookback_kernel<T, W, NPL, false, true> : scan_lookback_kernel<T, W, NPL, false, false>;
+        hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(items)), dim3(64 * W), 0, stream,
+                           static_cast<const T *>(a.u), static_cast<const T *>(a.delta),
+                           a.delta_bias, a.A, static_cast<const T *>(a.B),
+                           static_cast<const T *>(a.C), a.D, static_cast<const T *>(a.z),
+                           static_cast<T *>(a.y), a.h_last, a.L, static_cast<int>(a.dim),
+                           static_cast<int>(a.N), p.groups_per_batch, p.total_groups, p.seg_len,
+                           p.nseg, s);
+        e = hipGetLastError();
+    }
+    const hipError_t ef = hipFreeAsync(mem, stream);
+    return e != hipSuccess ? e : ef;
+}
+
+template <typename T>
+hipError_t launch_by_n(const ScanArgs &a, hipStream_t stream) {
+    if (a.N <= 16) return launch_typed<T, 4, 1>(a, stream);
+    if (a.N <= 32) return launch_typed<T, 2, 4>(a, stream);
+    return launch_typed<T, 2, 8>(a, stream);
+}
+
+}  // namespace
+
+bool scan_lookback_supported(const ScanArgs &a) {
+    if (a.N < 1 || a.N > 64) return false;
+    const int64_t groups = a.batch * ((a.dim + kCh - 1) / kCh);
+    if (groups >= (int64_t(1) << 20)) return false;
+    const Plan p = make_plan(a);
+    return static_cast<int64_t>(p.nseg) * p.total_groups < (int64_t(1) << 31);
+}
+
+hipError_t launch_scan_lookback(const ScanArgs &a, hipStream_t stream) {
+    if (a.io == IO_F32) return launch_by_n<float>(a, stream);
+    return launch_by_n<uint16_t>(a, stream);
+}
+
+}  // namespace mssm

@@ -18,7 +18,7 @@ from selective_state_space_05_amd import _lib, inputs
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-SCAN_VARIANTS = [_lib.VARIANT_ROWSERIAL, _lib.VARIANT_CHUNKED]
+SCAN_VARIANTS = [_lib.VARIANT_ROWSERIAL, _lib.VARIANT_CHUNKED, _lib.VARIANT_LOOKBACK]
 SSD_VARIANTS = [_lib.VARIANT_SSD_RECURRENT]
 
 
@@ -83,6 +83,8 @@ SMALL_CASES = [
     (2, 4096 + 37, 40, 16, "bf16", "scalar", True, True),  # several chunks
     (1, 2048, 130, 32, "f32", "scalar", True, True),       # N = 32
     (1, 300, 9, 64, "f32", "scalar", True, True),          # N = 64 (limit)
+    (1, 20000 + 3, 17, 16, "bf16", "per_channel", True, True),  # many segments, ragged
+    (3, 6000, 8, 7, "f32", "scalar", False, True),         # N = 7, three batches
 ]
 
 
@@ -171,6 +173,28 @@ def test_scan_zero_length_zero_fills_state(dev):
     y, h = mssm.selective_scan_fwd(u, u.clone(), A, B, B.clone(), h_out=h_out)
     torch.cuda.synchronize()
     assert y.shape == (2, 3, 0) and torch.all(h == 0)
+
+
+def test_scan_auto_picks_lookback_for_few_long_rows(dev):
+    from selective_state_space_05_amd.api import last_variant
+    p = scan_problem(1, 8192, 32, 16, "bf16", 8)
+    announce("scan auto look-back")
+    x = inputs.scan_inputs(p)
+    y, h = run_scan(scan_to_dev(x, "bf16", dev))
+    assert last_variant() == _lib.VARIANT_LOOKBACK
+    yo, ho = oracle.selective_scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"],
+                                   x["z"], x["delta_bias"])
+    gates.check(y, yo, "bf16", "y")
+    gates.check_state(h, ho, "bf16", "h_last")
+
+
+def test_scan_lookback_deterministic(dev):
+    p = scan_problem(1, 50000, 16, 16, "f32", 9, bias="per_channel")
+    t = scan_to_dev(inputs.scan_inputs(p), "f32", dev)
+    announce("scan look-back determinism")
+    y1, h1 = run_scan(t, _lib.VARIANT_LOOKBACK)
+    y2, h2 = run_scan(t, _lib.VARIANT_LOOKBACK)
+    assert np.array_equal(y1, y2) and np.array_equal(h1, h2)
 
 
 def test_scan_reports_variant(dev):
