@@ -61,4 +61,8 @@ bool scan_lookback_supported(const ScanArgs &a);
 hipError_t launch_ssd_recurrent(const SSDArgs &a, hipStream_t stream);
 bool ssd_recurrent_supported(const SSDArgs &a);
 
+// Chunked matrix-core form (bf16 I/O, N <= 128, chunk 64 / 128 / 256).
+hipError_t launch_ssd_chunked(const SSDArgs &a, hipStream_t stream);
+bool ssd_chunked_supported(const SSDArgs &a);
+
 }  // namespace mssm

@@ -241,14 +241,24 @@ mssm_status mssm_ssd_scalar_fwd(const void *x, const void *dt, const float *dt_b
 
     mssm::SSDArgs a{x, dt, dt_bias, A, B, C, D, y, h_last, batch, L, H, P, N, G,
                     Q == 0 ? 256 : Q, dtypes.io == MSSM_F32 ? mssm::IO_F32 : mssm::IO_BF16};
+    // The matrix-core form needs bf16 operands and a few chunks to pay off;
+    // everything else takes the recurrent form.
     mssm_variant v = g_forced;
-    if (v == MSSM_VARIANT_AUTO) v = MSSM_VARIANT_SSD_RECURRENT;
+    if (v == MSSM_VARIANT_AUTO)
+        v = (mssm::ssd_chunked_supported(a) && a.L >= 2 * a.chunk) ? MSSM_VARIANT_SSD_CHUNKED
+                                                                    : MSSM_VARIANT_SSD_RECURRENT;
     hipError_t e;
     switch (v) {
         case MSSM_VARIANT_SSD_RECURRENT:
             if (!mssm::ssd_recurrent_supported(a))
                 return fail(MSSM_ERR_UNSUPPORTED, "recurrent SSD variant does not support this shape");
             e = mssm::launch_ssd_recurrent(a, st);
+            break;
+        case MSSM_VARIANT_SSD_CHUNKED:
+            if (!mssm::ssd_chunked_supported(a))
+                return fail(MSSM_ERR_UNSUPPORTED, "chunked SSD variant needs bf16 I/O, dstate <= 128 "
+                            "and chunk 64, 128 or 256");
+            e = mssm::launch_ssd_chunked(a, st);
             break;
         default:
             return fail(MSSM_ERR_UNSUPPORTED, "variant %d does not apply to the SSD scan",

@@ -19,7 +19,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 SCAN_VARIANTS = [_lib.VARIANT_ROWSERIAL, _lib.VARIANT_CHUNKED, _lib.VARIANT_LOOKBACK]
-SSD_VARIANTS = [_lib.VARIANT_SSD_RECURRENT]
+SSD_VARIANTS = [_lib.VARIANT_SSD_RECURRENT, _lib.VARIANT_SSD_CHUNKED]
 
 
 @pytest.fixture(scope="module")
@@ -239,9 +239,12 @@ def ssd_rows_of(y):
 SSD_SMALL = [
     # batch, L, H, P, N, G, io
     (1, 300, 2, 8, 16, 1, "f32"),
-    (2, 513, 4, 64, 128, 1, "bf16"),
+    (2, 513, 4, 64, 128, 1, "bf16"),      # three chunks, ragged
     (1, 77, 6, 5, 7, 3, "f32"),
-    (2, 1, 2, 16, 32, 2, "bf16"),
+    (2, 1, 2, 16, 32, 2, "bf16"),         # single step
+    (1, 1000, 3, 40, 7, 3, "bf16"),       # two head-dim tiles, odd N, groups
+    (1, 700, 2, 64, 100, 1, "bf16"),      # N not a multiple of 8
+    (2, 2048, 4, 32, 64, 2, "bf16"),
 ]
 
 
@@ -249,6 +252,8 @@ SSD_SMALL = [
 @pytest.mark.parametrize("case", SSD_SMALL)
 def test_ssd_small_full_compare(dev, variant, case):
     batch, L, H, P, N, G, io = case
+    if variant == _lib.VARIANT_SSD_CHUNKED and io != "bf16":
+        pytest.skip("the matrix-core form takes bf16 activations only")
     announce("ssd variant=%d %s" % (variant, case))
     p = inputs.SSDProblem("case", batch, L, H, P, N, G, io, 50 + L)
     s = inputs.ssd_inputs(p)
@@ -274,6 +279,28 @@ def test_ssd_full_size_sampled_rows(dev, variant):
     gates.check(ys, yo, p.io, "y")
     gates.check_state(hs, ho, p.io, "h_last")
     assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_ssd_chunk_lengths_agree(dev, chunk):
+    """The chunk length changes only the association order, not the result."""
+    p = inputs.SSDProblem("case", 1, 1000, 2, 64, 128, 1, "bf16", 77)
+    announce("ssd chunked chunk=%d" % chunk)
+    s = inputs.ssd_inputs(p)
+    y, h = run_ssd(ssd_to_dev(s, "bf16", dev), _lib.VARIANT_SSD_CHUNKED, chunk=chunk)
+    yo, ho = oracle.ssd(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["dt_bias"])
+    gates.check(ssd_rows_of(y), ssd_rows_of(yo), "bf16", "y")
+    gates.check_state(h, ho, "bf16", "h_last")
+
+
+def test_ssd_chunked_rejects_f32(dev):
+    import selective_state_space_05_amd as mssm
+    from selective_state_space_05_amd.api import MssmError, forced_variant
+    p = inputs.SSDProblem("case", 1, 64, 2, 8, 16, 1, "f32", 3)
+    t = ssd_to_dev(inputs.ssd_inputs(p), "f32", dev)
+    with forced_variant(_lib.VARIANT_SSD_CHUNKED):
+        with pytest.raises(MssmError):
+            mssm.ssd_scalar_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["dt_bias"])
 
 
 def test_ssd_zero_length_zero_fills_state(dev):
