@@ -56,10 +56,41 @@ __device__ __forceinline__ uint16_t bf16_bits(__bf16 v) { return __builtin_bit_c
 __device__ __forceinline__ float bf16_val(__bf16 v) {
     return __uint_as_float(static_cast<uint32_t>(bf16_bits(v)) << 16);
 }
+// Two floats rounded to bf16 (nearest even), packed low half first.
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    const bf2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
 // Two-term split: v ~= hi + lo with both parts bf16 (about 16 significant bits).
 __device__ __forceinline__ void split(float v, __bf16 &hi, __bf16 &lo) {
     hi = static_cast<__bf16>(v);
     lo = static_cast<__bf16>(v - bf16_val(hi));
+}
+
+// Eight consecutive bf16 of row `t` starting at column c8 of a row-major
+// (rows x cols) slice with row stride `stride`; zero past the last row or
+// column.  Branch-free: out-of-range reads are redirected to element 0 and
+// the value is discarded, so all loads of a phase are in flight together.
+// vec: rows start 16-byte aligned and cols % 8 == 0.
+__device__ __forceinline__ uint4 load_row8(const uint16_t *base, int64_t t, int c8, int64_t rows,
+                                           int cols, int64_t stride, bool vec) {
+    const bool okt = t < rows;
+    if (vec) {
+        const bool ok = okt && c8 < cols;
+        const uint4 v = *reinterpret_cast<const uint4 *>(base + (ok ? t * stride + c8 : 0));
+        return ok ? v : make_uint4(0, 0, 0, 0);
+    }
+    uint16_t e[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const bool ok = okt && c8 + r < cols;
+        const uint16_t w = base[ok ? t * stride + c8 + r : 0];
+        e[r] = ok ? w : 0;
+    }
+    uint4 v;
+    __builtin_memcpy(&v, e, 16);
+    return v;
 }
 
 template <typename T> struct Ld;
@@ -70,15 +101,20 @@ template <> struct Ld<uint16_t> {
 // LDS of one workgroup (bf16 data held as raw uint16_t).
 template <int Q, int NP>
 struct __align__(16) Smem {
-    static constexpr int BP = NP + 8;   // row pitch of B (elements)
-    static constexpr int XP = Q + 8;    // row pitch of the transposed x tiles
-    static constexpr int HP = NP + 8;   // row pitch of h_prev
-    uint16_t B[Q * BP];                 // B[s][n]
-    uint16_t X[kPt * XP];               // x[s][p] stored as X[p][s]
-    uint16_t Xwh[kPt * XP], Xwl[kPt * XP];   // x * w, high / low parts
-    uint16_t Hh[kPt * HP], Hl[kPt * HP];     // h_prev[p][n], high / low parts
-    float cum[Q];
+    // Row pitches (elements) chosen so the operand reads of one instruction
+    // fall in distinct LDS banks: 8-byte reads of X need a row stride of
+    // 2 mod 64 dwords, 16-byte reads of Xw, B and h_prev 4 mod 64 dwords.
+    static constexpr int BP = NP + 8;   // B[s][n]
+    static constexpr int XP = Q + 4;    // x[s][p] stored as X[p][s]
+    static constexpr int WP = Q + 8;    // x * w, stored like X
+    static constexpr int HP = NP + 8;   // h_prev[p][n]
+    uint16_t B[Q * BP];
+    uint16_t X[kPt * XP];
+    uint16_t Xwh[kPt * WP], Xwl[kPt * WP];   // high / low bf16 parts
+    uint16_t Hh[kPt * HP], Hl[kPt * HP];     // high / low bf16 parts
+    float cum[Q];      // inclusive sum of the log2 decay over the chunk
     float dl[Q];
+    float fs[Q];       // 2^(cum at the end of s's 32-step block - cum_s) dl_s
     float wsum[kThreads / 64];
 };
 
@@ -88,8 +124,10 @@ __global__ __launch_bounds__(kThreads) void ssd_chunked_kernel(
     const float *__restrict__ dt_bias, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm,
     const float *__restrict__ Dskip, uint16_t *__restrict__ y,
-    float *__restrict__ h_last, int64_t L, int H, int P, int N, int G, int ptiles, bool vec) {
-    // vec: B and C rows start 16-byte aligned (N % 8 == 0 and aligned bases)
+    float *__restrict__ h_last, int64_t L, int H, int P, int N, int G, int ptiles, bool vec,
+    bool vecx) {
+    // vec: B and C rows start 16-byte aligned (N % 8 == 0 and aligned bases);
+    // vecx: the same for x (P % 8 == 0 and an aligned base)
     using S = Smem<Q, NP>;
     constexpr int NT = Q / 32;          // 32-step time blocks per chunk
     constexpr int KN = NP / 16;         // K steps over the state index
@@ -131,41 +169,39 @@ __global__ __launch_bounds__(kThreads) void ssd_chunked_kernel(
         // ---- stage B (Q x NP) and x (Q x 32, transposed); dl and its scan ---
         for (int u = tid; u < Q * (NP / 8); u += kThreads) {
             const int s = u / (NP / 8), n8 = (u % (NP / 8)) * 8;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (t0 + s < L) {
-                if (vec && n8 + 8 <= N) {
-                    v = *reinterpret_cast<const uint4 *>(Bg + (t0 + s) * rowBC + n8);
-                } else {
-                    uint16_t e[8];
-#pragma unroll
-                    for (int r = 0; r < 8; ++r) e[r] = n8 + r < N ? Bg[(t0 + s) * rowBC + n8 + r] : 0;
-                    __builtin_memcpy(&v, e, 16);
-                }
-            }
-            *reinterpret_cast<uint4 *>(&sm.B[s * S::BP + n8]) = v;
+            *reinterpret_cast<uint4 *>(&sm.B[s * S::BP + n8]) = load_row8(Bg, t0 + s, n8, L, N, rowBC, vec);
         }
-        // x: units of 8 head-dim columns of one step; thread tid owns units
-        // tid, tid + 256, ... (Q * 4 units)
-        constexpr int XU = Q * (kPt / 8) / kThreads;   // units per thread
-        float xr[XU][8];
+        // x: units of (two consecutive steps, 8 head-dim columns); each unit
+        // is written transposed as 8 dwords (step pair packed) -- no
+        // sub-dword LDS writes.  Q / 128 units per thread (one half of the
+        // threads when Q = 64).
+        constexpr int XU = (2 * Q + kThreads - 1) / kThreads;
+        float xr[XU][2][8];
 #pragma unroll
         for (int k = 0; k < XU; ++k) {
             const int u = tid + k * kThreads;
-            const int s = u / (kPt / 8), pg = (u % (kPt / 8)) * 8;
-            const bool okt = t0 + s < L;
+            if (u < 2 * Q) {
+                const int s2 = 2 * (u / (kPt / 8)), pg = (u % (kPt / 8)) * 8;
+                const uint4 v0 = load_row8(xg, t0 + s2, pg, L, P - p0, rowX, vecx);
+                const uint4 v1 = load_row8(xg, t0 + s2 + 1, pg, L, P - p0, rowX, vecx);
+                uint16_t e0[8], e1[8];
+                __builtin_memcpy(e0, &v0, 16);
+                __builtin_memcpy(e1, &v1, 16);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const bool ok = okt && p0 + pg + r < P;
-                const uint16_t e = ok ? xg[(t0 + s) * rowX + pg + r] : 0;
-                xr[k][r] = __uint_as_float(static_cast<uint32_t>(e) << 16);
-                sm.X[(pg + r) * S::XP + s] = e;
+                for (int r = 0; r < 8; ++r) {
+                    xr[k][0][r] = __uint_as_float(static_cast<uint32_t>(e0[r]) << 16);
+                    xr[k][1][r] = __uint_as_float(static_cast<uint32_t>(e1[r]) << 16);
+                    *reinterpret_cast<uint32_t *>(&sm.X[(pg + r) * S::XP + s2]) =
+                        static_cast<uint32_t>(e0[r]) | (static_cast<uint32_t>(e1[r]) << 16);
+                }
             }
         }
         // dl and the log decay of step tid (threads >= Q idle here)
         float ell = 0.0f;
         if (tid < Q) {
-            float dlv = 0.0f;
-            if (t0 + tid < L) dlv = softplus(Ld<uint16_t>::f(dtg, (t0 + tid) * H) + bias);
+            const bool okt = t0 + tid < L;
+            const float dr = Ld<uint16_t>::f(dtg, okt ? (t0 + tid) * H : 0);
+            const float dlv = okt ? softplus(dr + bias) : 0.0f;
             sm.dl[tid] = dlv;
             ell = dlv * A2;                          // log2 of the step decay
         }
@@ -186,18 +222,29 @@ __global__ __launch_bounds__(kThreads) void ssd_chunked_kernel(
         __syncthreads();
 
         const float cum_end = sm.cum[Q - 1];
-        // ---- x * w, w_s = 2^(cum_end - cum_s) dl_s, as bf16 high / low ------
+        // ---- per-step factors of the decay, x * w as bf16 high / low --------
+        if (tid < Q) {
+            const float cb = sm.cum[(tid | 31)];
+            sm.fs[tid] = fast_exp2(cb - sm.cum[tid]) * sm.dl[tid];
+        }
 #pragma unroll
         for (int k = 0; k < XU; ++k) {
             const int u = tid + k * kThreads;
-            const int s = u / (kPt / 8), pg = (u % (kPt / 8)) * 8;
-            const float w = fast_exp2(cum_end - sm.cum[s]) * sm.dl[s];
+            if (u < 2 * Q) {
+                const int s2 = 2 * (u / (kPt / 8)), pg = (u % (kPt / 8)) * 8;
+                // w_s = 2^(cum_end - cum_s) dl_s: the weight of step s in the
+                // state at the chunk end
+                const float w0 = fast_exp2(cum_end - sm.cum[s2]) * sm.dl[s2];
+                const float w1 = fast_exp2(cum_end - sm.cum[s2 + 1]) * sm.dl[s2 + 1];
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                __bf16 hi, lo;
-                split(xr[k][r] * w, hi, lo);
-                sm.Xwh[(pg + r) * S::XP + s] = bf16_bits(hi);
-                sm.Xwl[(pg + r) * S::XP + s] = bf16_bits(lo);
+                for (int r = 0; r < 8; ++r) {
+                    const float a0 = xr[k][0][r] * w0, a1 = xr[k][1][r] * w1;
+                    const uint32_t hi = pack2(a0, a1);
+                    const uint32_t lo = pack2(a0 - __uint_as_float(hi << 16),
+                                              a1 - __uint_as_float(hi & 0xffff0000u));
+                    *reinterpret_cast<uint32_t *>(&sm.Xwh[(pg + r) * S::WP + s2]) = hi;
+                    *reinterpret_cast<uint32_t *>(&sm.Xwl[(pg + r) * S::WP + s2]) = lo;
+                }
             }
         }
         __syncthreads();
@@ -212,19 +259,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunked_kernel(
             bf8 cf[KN];
 #pragma unroll
             for (int jn = 0; jn < KN; ++jn) {
-                const int n8 = 16 * jn + 8 * half;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (t0 + tl < L) {
-                    if (vec && n8 + 8 <= N) {
-                        v = *reinterpret_cast<const uint4 *>(Cg + (t0 + tl) * rowBC + n8);
-                    } else {
-                        uint16_t e[8];
-#pragma unroll
-                        for (int r = 0; r < 8; ++r) e[r] = n8 + r < N ? Cg[(t0 + tl) * rowBC + n8 + r] : 0;
-                        __builtin_memcpy(&v, e, 16);
-                    }
-                }
-                cf[jn] = __builtin_bit_cast(bf8, v);
+                cf[jn] = __builtin_bit_cast(bf8, load_row8(Cg, t0 + tl, 16 * jn + 8 * half, L, N, rowBC, vec));
             }
             const float cum_t = sm.cum[tl];
             f16x yd;
@@ -243,15 +278,37 @@ __global__ __launch_bounds__(kThreads) void ssd_chunked_kernel(
                 }
                 // M[t][s] = G'[s][t] 2^(cum_t - cum_s) dl_s for s <= t, else 0.
                 // This lane holds column t = tl and rows s(v) = 8(v/4) + 4 half + v%4.
+                // Off the diagonal block every s < t and the decay factors as
+                // 2^(cum_t - cb) * fs[s], cb the cum at the end of block sb:
+                // both factors are <= 1 (and <= dl_s), so nothing overflows.
+                // On the diagonal block the exponent is formed directly and
+                // steps s > t are masked out by selection.
+                float mval[16];
+                if (sb < tb) {
+                    const float et = fast_exp2(cum_t - sm.cum[sb * 32 + 31]);
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int sl = sb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+                        mval[v] = gacc[v] * (et * sm.fs[sl]);
+                    }
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int sl = sb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+                        const float mv = gacc[v] * fast_exp2(cum_t - sm.cum[sl]) * sm.dl[sl];
+                        mval[v] = sl <= tl ? mv : 0.0f;
+                    }
+                }
                 bf8 mh[2], ml[2];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int sl = sb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
-                    const float m = sl <= tl ? gacc[v] * fast_exp2(cum_t - sm.cum[sl]) * sm.dl[sl] : 0.0f;
-                    __bf16 hi, lo;
-                    split(m, hi, lo);
-                    mh[v / 8][v % 8] = hi;
-                    ml[v / 8][v % 8] = lo;
+                for (int v = 0; v < 16; v += 2) {
+                    const uint32_t hi = pack2(mval[v], mval[v + 1]);
+                    const uint32_t lo = pack2(mval[v] - __uint_as_float(hi << 16),
+                                              mval[v + 1] - __uint_as_float(hi & 0xffff0000u));
+                    mh[v / 8][v % 8] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hi));
+                    mh[v / 8][v % 8 + 1] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hi >> 16));
+                    ml[v / 8][v % 8] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lo));
+                    ml[v / 8][v % 8 + 1] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lo >> 16));
                 }
                 // Y_diag[t][p] += sum_s M[t][s] x[s][p], K order s(v) as above:
                 // operand lane (p = l32, half) reads x[s(v)][p] for the same v.
@@ -298,8 +355,8 @@ __global__ __launch_bounds__(kThreads) void ssd_chunked_kernel(
 #pragma unroll 4
             for (int kq = 0; kq < KQ; ++kq) {
                 const int s8 = 16 * kq + 8 * half;
-                const bf8 ah = *reinterpret_cast<const bf8 *>(&sm.Xwh[l32 * S::XP + s8]);
-                const bf8 al = *reinterpret_cast<const bf8 *>(&sm.Xwl[l32 * S::XP + s8]);
+                const bf8 ah = *reinterpret_cast<const bf8 *>(&sm.Xwh[l32 * S::WP + s8]);
+                const bf8 al = *reinterpret_cast<const bf8 *>(&sm.Xwl[l32 * S::WP + s8]);
                 bf8 bb;
 #pragma unroll
                 for (int r = 0; r < 8; ++r)
@@ -341,12 +398,13 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     const int64_t grid = a.batch * a.H * ptiles;
     auto aligned = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
     const bool vec = a.N % 8 == 0 && aligned(a.B) && aligned(a.C);
+    const bool vecx = a.P % 8 == 0 && aligned(a.x);
     hipLaunchKernelGGL((ssd_chunked_kernel<Q, NP>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads),
                        0, stream, static_cast<const uint16_t *>(a.x),
                        static_cast<const uint16_t *>(a.dt), a.dt_bias, a.A,
                        static_cast<const uint16_t *>(a.B), static_cast<const uint16_t *>(a.C), a.D,
                        static_cast<uint16_t *>(a.y), a.h_last, a.L, static_cast<int>(a.H),
-                       static_cast<int>(a.P), static_cast<int>(a.N), static_cast<int>(a.G), ptiles, vec);
+                       static_cast<int>(a.P), static_cast<int>(a.N), static_cast<int>(a.G), ptiles, vec, vecx);
     return hipGetLastError();
 }
 
