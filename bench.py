@@ -1,23 +1,27 @@
 #!/usr/bin/env python3
 """Benchmark of the selective-scan forward on one MI355X.
 
-One step = one call of the hot path (softplus step size, discretisation,
-scan, output with skip term and gate, final state) over one batch of the
-workload's synthetic inputs, which are already resident in HBM.  Default
-workload: the Mamba-2.8B-shaped layer (batch 2, L 4096, 5120 channels,
-N 16, bf16 activations, fp32 state).
+One step = one call of the hot path over one batch of the workload's
+synthetic inputs, which are already resident in HBM:
+  * selective scan (default): softplus step size, discretisation, scan,
+    output with skip term and gate, final state;
+  * SSD (--workload mamba2_ssd_layer_bf16): the Mamba-2 scalar-decay forward.
+Default workload: the Mamba-2.8B-shaped layer (batch 2, L 4096, 5120
+channels, N 16, bf16 activations, fp32 state).
 
 Prints one JSON line:
-  metric/value/unit   scan elements per second (batch * L * channels * N)
+  metric/value/unit   scan elements per second (batch * L * channels * N;
+                      SSD: batch * L * heads * headdim * N)
   hbm                 minimum-traffic bytes per step / kernel time, and its
                       fraction of the 8 TB/s HBM peak
-  roofline            the bound of the dominant kernel (VALU issue slots,
-                      see the design doc for the per-element slot count and peak)
+  roofline            the bound of the dominant kernel: VALU issue slots for
+                      the selective scan, bf16 matrix-core flops for SSD
   cpu_baseline        the float64 CPU oracle timed on this host
   parity              sampled-row comparison with the oracle
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--variant auto|rowserial|chunked|...] [--no-cpu]
+                       [--copy-probe-mib M]
 """
 from __future__ import annotations
 
@@ -33,10 +37,13 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+METRIC = "scan elements/s (B*L*D*N) and achieved HBM GB/s as % of MI355X peak"
 HBM_PEAK_GBS = 8000.0
 # VALU issue rate of one MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 # (non-packed fp32 lane-operations per second).
 VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Dense bf16 matrix-core peak of one MI355X (TFLOP/s).
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 VARIANTS = {"auto": 0, "rowserial": 1, "chunked": 2, "lookback": 3,
             "ssd_recurrent": 4, "ssd_chunked": 5}
@@ -55,6 +62,22 @@ def scan_slots(p) -> float:
     per_row_step = 4 + 3 + 1 + (1 if p.skip else 0) + (4 + 2 + 1 if p.gate else 0)
     rows_steps = p.batch * p.dim * p.seqlen
     return per_elem * p.elements + per_row_step * rows_steps
+
+
+def ssd_flops(p, chunk: int = 256) -> float:
+    """Algorithmic matrix-core flops of the chunked SSD form, chunk length Q.
+
+    Per (batch, chunk): the causal half of C B^T, Q(Q+1)/2 * N multiply-adds,
+    once per group.  Per (batch, chunk, head): the causal intra-chunk product
+    Q(Q+1)/2 * P, the chunk state P * Q * N and the inter-chunk output
+    Q * N * P multiply-adds.  Two flops per multiply-add.
+    """
+    nchunks = -(-p.seqlen // chunk)
+    q, n, hp = chunk, p.dstate, p.headdim
+    tri = q * (q + 1) // 2
+    per_group = tri * n
+    per_head = tri * hp + hp * q * n + q * n * hp
+    return 2.0 * p.batch * nchunks * (p.ngroups * per_group + p.nheads * per_head)
 
 
 def kernel_source_sha() -> str:
@@ -80,118 +103,49 @@ def load_traffic(workload: str, sha: str):
     return c.get("hbm_bytes_per_launch")
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mamba2.8b_layer_bf16")
-    ap.add_argument("--variant", default="auto", choices=sorted(VARIANTS))
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-parity", action="store_true")
-    ap.add_argument("--rotate", type=int, default=0,
-                    help="input/output buffer sets cycled across steps (0: enough to exceed the 256 MB Infinity Cache)")
-    args = ap.parse_args()
+def g1(a, r):
+    """Largest row-wise relative 2-norm error."""
+    return float(np.max(np.sqrt(np.sum((a - r) ** 2, -1)) /
+                        np.maximum(np.sqrt(np.sum(r ** 2, -1)), 1e-300)))
 
-    if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
 
-    import torch
-    from selective_state_space_05_amd import api, inputs
+class ScanBench:
+    """Mamba-1 selective scan: inputs, one step, parity rows, CPU baseline."""
 
-    if args.workload not in inputs.SCAN_PROBLEMS:
-        raise SystemExit("unknown workload %s; choose from %s" % (
-            args.workload, sorted(inputs.SCAN_PROBLEMS)))
-    p = inputs.SCAN_PROBLEMS[args.workload]
-    dev = torch.device("cuda:0")
-    print("[bench] workload %s: drawing inputs" % p.name, file=sys.stderr, flush=True)
-    x = inputs.scan_inputs(p)
+    def __init__(self, p, dev, torch):
+        from selective_state_space_05_amd import api, inputs
+        self.p, self.dev, self.torch, self.api = p, dev, torch, api
+        self.x = inputs.scan_inputs(p)
+        self.io_t = torch.bfloat16 if p.io == "bf16" else torch.float32
 
-    io_t = torch.bfloat16 if p.io == "bf16" else torch.float32
-
-    def upload():
+    def upload(self):
+        torch, p = self.torch, self.p
         t = {}
-        for k, v in x.items():
+        for k, v in self.x.items():
             if v is None:
                 t[k] = None
             elif k in ("A", "D", "delta_bias"):
-                t[k] = torch.from_numpy(v).to(dev)
+                t[k] = torch.from_numpy(v).to(self.dev)
             else:
-                t[k] = torch.from_numpy(v).to(io_t).to(dev)
+                t[k] = torch.from_numpy(v).to(self.io_t).to(self.dev)
         t["y"] = torch.empty_like(t["u"])
-        t["h"] = torch.empty((p.batch, p.dim, p.dstate), dtype=torch.float32, device=dev)
+        t["h"] = torch.empty((p.batch, p.dim, p.dstate), dtype=torch.float32, device=self.dev)
         return t
 
-    footprint = p.min_traffic_bytes()
-    rotate = args.rotate or max(1, min(4, -(-(1 << 30) // footprint)))
-    sets = [upload() for _ in range(rotate)]
-    torch.cuda.synchronize()
+    def step(self, t):
+        self.api.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"],
+                                    t["z"], t["delta_bias"], out=t["y"], h_out=t["h"])
 
-    variant = VARIANTS[args.variant]
+    def roofline(self, sec):
+        slots = scan_slots(self.p)
+        a = slots / sec / 1e12
+        return {"bound": "alu", "achieved": a, "peak": VALU_PEAK_TSLOTS,
+                "unit": "T VALU lane-slots/s", "frac": a / VALU_PEAK_TSLOTS,
+                "slots_per_launch": slots}
 
-    def step(i):
-        t = sets[i % rotate]
-        api.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"],
-                               t["z"], t["delta_bias"], out=t["y"], h_out=t["h"])
-
-    print("[bench] warmup %d, timed %d steps, %d buffer sets" % (args.warmup, args.steps, rotate),
-          file=sys.stderr, flush=True)
-    with api.forced_variant(variant):
-        for i in range(args.warmup):
-            step(i)
-        torch.cuda.synchronize()
-        used = VARIANT_NAMES.get(api.last_variant(), str(api.last_variant()))
-        stream = torch.cuda.current_stream(dev)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(args.steps):
-            step(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / args.steps
-    sec = ms_step / 1e3
-
-    value = p.elements / sec
-    hbm_gbs = footprint / sec / 1e9
-    slots = scan_slots(p)
-    achieved_t = slots / sec / 1e12
-    sha = kernel_source_sha()
-    traffic = load_traffic(p.name, sha)
-
-    out = {
-        "metric": "scan elements/s (B*L*D*N) and achieved HBM GB/s as % of MI355X peak",
-        "value": value,
-        "unit": "elements/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic (seeded numpy draws; no dataset or trained weights)",
-        "config": {"workload": p.name, "batch": p.batch, "seqlen": p.seqlen,
-                   "dim": p.dim, "dstate": p.dstate, "io": p.io,
-                   "gate": p.gate, "skip": p.skip, "variant": used,
-                   "buffer_sets": rotate},
-        "hbm": {"min_traffic_bytes": footprint, "achieved_gbs": hbm_gbs,
-                "peak_gbs": HBM_PEAK_GBS, "frac": hbm_gbs / HBM_PEAK_GBS},
-        "roofline": {"bound": "alu", "achieved": achieved_t, "peak": VALU_PEAK_TSLOTS,
-                     "unit": "T VALU lane-slots/s", "frac": achieved_t / VALU_PEAK_TSLOTS,
-                     "traffic": traffic, "slots_per_launch": slots,
-                     "kernel_source_sha": sha},
-    }
-
-    if not args.no_parity:
-        print("[bench] parity on sampled rows", file=sys.stderr, flush=True)
+    def parity(self, t):
         from oracle import oracle
-        t = sets[(args.steps - 1) % rotate]
+        p, x = self.p, self.x
         rng = np.random.default_rng(123)
         rows = [(0, 0), (p.batch - 1, p.dim - 1)] + [
             (int(rng.integers(p.batch)), int(rng.integers(p.dim))) for _ in range(6)]
@@ -201,32 +155,24 @@ def main():
         hg = t["h"].cpu().numpy().astype(np.float64)
         ys = np.stack([yg[b, d] for b, d in rows])
         hs = np.stack([hg[b, d] for b, d in rows])
+        return len(rows), g1(ys, yo), g1(hs, ho)
 
-        def g1(a, r):
-            return float(np.max(np.sqrt(np.sum((a - r) ** 2, -1)) /
-                                np.maximum(np.sqrt(np.sum(r ** 2, -1)), 1e-300)))
-        tol = 1e-4 if p.io == "f32" else 3e-3
-        out["parity"] = {"rows": len(rows), "g1_y": g1(ys, yo), "g1_h_last": g1(hs, ho),
-                         "tol": tol, "ok": bool(g1(ys, yo) <= tol and g1(hs, ho) <= tol)}
-
-    if not args.no_cpu:
+    def cpu_baseline(self, threads, budget_s=15.0):
+        """Time the oracle on whole (batch, channel) rows: as many as about
+        `budget_s` seconds of work at the measured single-row rate."""
         from oracle import oracle
-        threads = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "16")), 16)
-        # Bounded sample: whole rows, as many as ~15 s of CPU work at the
-        # measured single-row rate (the oracle's rows are independent).
-        print("[bench] CPU oracle baseline (%d threads)" % threads, file=sys.stderr, flush=True)
+        p, x = self.p, self.x
         t0 = time.time()
         oracle.selective_scan_rows([(0, 0)], x["u"], x["delta"], x["A"], x["B"], x["C"],
                                    x["D"], x["z"], x["delta_bias"], nthreads=1)
         per_row = max(time.time() - t0, 1e-4)
         rows_total = p.batch * p.dim
-        n_rows = int(min(rows_total, max(threads, 15.0 * threads / per_row)))
-        n_rows = max(threads, (n_rows // threads) * threads) if rows_total >= threads else rows_total
+        n_rows = int(min(rows_total, max(threads, budget_s * threads / per_row)))
+        if rows_total >= threads:
+            n_rows = max(threads, (n_rows // threads) * threads)
         n_rows = min(n_rows, rows_total)
-        # a contiguous block of rows of batch 0 (then batch 1 ...)
         flat = np.arange(n_rows)
         bsel, dsel = flat // p.dim, flat % p.dim
-        sub = {k: v for k, v in x.items()}
         t0 = time.time()
         done = 0
         for b in np.unique(bsel):
@@ -242,12 +188,226 @@ def main():
             done += hi - lo
         cpu_s = time.time() - t0
         elems = done * p.seqlen * p.dstate
-        out["cpu_baseline"] = {
-            "value": elems / cpu_s, "unit": "elements/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "%d of %d (batch, channel) rows, full length %d, float64, %.1f s" % (
-                done, rows_total, p.seqlen, cpu_s)}
-        del sub
+        return elems / cpu_s, "%d of %d (batch, channel) rows, full length %d, float64, %.1f s" % (
+            done, rows_total, p.seqlen, cpu_s)
+
+    def config(self):
+        p = self.p
+        return {"workload": p.name, "batch": p.batch, "seqlen": p.seqlen, "dim": p.dim,
+                "dstate": p.dstate, "io": p.io, "gate": p.gate, "skip": p.skip}
+
+
+class SSDBench:
+    """Mamba-2 scalar-decay forward."""
+
+    def __init__(self, p, dev, torch, chunk=256):
+        from selective_state_space_05_amd import api, inputs
+        self.p, self.dev, self.torch, self.api, self.chunk = p, dev, torch, api, chunk
+        self.x = inputs.ssd_inputs(p)
+        self.io_t = torch.bfloat16 if p.io == "bf16" else torch.float32
+
+    def upload(self):
+        torch, p = self.torch, self.p
+        t = {}
+        for k, v in self.x.items():
+            if v is None:
+                t[k] = None
+            elif k in ("A", "D", "dt_bias"):
+                t[k] = torch.from_numpy(v).to(self.dev)
+            else:
+                t[k] = torch.from_numpy(v).to(self.io_t).to(self.dev)
+        t["y"] = torch.empty_like(t["x"])
+        t["h"] = torch.empty((p.batch, p.nheads, p.headdim, p.dstate), dtype=torch.float32,
+                             device=self.dev)
+        return t
+
+    def step(self, t):
+        self.api.ssd_scalar_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["dt_bias"],
+                                chunk=self.chunk, out=t["y"], h_out=t["h"])
+
+    def roofline(self, sec):
+        fl = ssd_flops(self.p, self.chunk)
+        a = fl / sec / 1e12
+        return {"bound": "mfma", "achieved": a, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": a / MFMA_BF16_PEAK_TFLOPS,
+                "flops_per_launch": fl}
+
+    def parity(self, t):
+        from oracle import oracle
+        p, s = self.p, self.x
+        rng = np.random.default_rng(3)
+        rows = [(0, 0, 0), (p.batch - 1, p.nheads - 1, p.headdim - 1)] + [
+            (int(rng.integers(p.batch)), int(rng.integers(p.nheads)),
+             int(rng.integers(p.headdim))) for _ in range(6)]
+        yo, ho = oracle.ssd_rows(rows, s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"],
+                                 s["dt_bias"])
+        yg = t["y"].float().cpu().numpy().astype(np.float64)
+        hg = t["h"].cpu().numpy().astype(np.float64)
+        ys = np.stack([yg[b, :, hh, pp] for b, hh, pp in rows])
+        hs = np.stack([hg[b, hh, pp] for b, hh, pp in rows])
+        return len(rows), g1(ys, yo), g1(hs, ho)
+
+    def cpu_baseline(self, threads, budget_s=15.0):
+        """Time the oracle on whole (batch, head) blocks, as many as about
+        `budget_s` seconds of work at the measured single-head rate."""
+        from oracle import oracle
+        p, s = self.p, self.x
+        G = p.ngroups
+        hpg = p.nheads // G
+
+        def run(b, h0, h1, nth):
+            g0 = h0 // hpg
+            g1_ = (h1 - 1) // hpg + 1
+            # heads [h0, h1) that share groups [g0, g1_) with the full problem
+            oracle.ssd(s["x"][b:b + 1, :, h0:h1], s["dt"][b:b + 1, :, h0:h1], s["A"][h0:h1],
+                       s["B"][b:b + 1, :, g0:g1_], s["C"][b:b + 1, :, g0:g1_],
+                       None if s["D"] is None else s["D"][h0:h1],
+                       None if s["dt_bias"] is None else s["dt_bias"][h0:h1], nthreads=nth)
+
+        t0 = time.time()
+        run(0, 0, hpg if G > 1 else 1, 1)
+        per_head = max(time.time() - t0, 1e-4) / (hpg if G > 1 else 1)
+        heads_total = p.batch * p.nheads
+        want = int(max(1, min(heads_total, budget_s * threads / per_head)))
+        if G == 1:
+            nh = min(p.nheads, want)
+            t0 = time.time()
+            run(0, 0, nh, threads)
+            done = nh
+        else:
+            ng = max(1, min(G, want // hpg))
+            t0 = time.time()
+            run(0, 0, ng * hpg, threads)
+            done = ng * hpg
+        cpu_s = time.time() - t0
+        elems = done * p.seqlen * p.headdim * p.dstate
+        return elems / cpu_s, "%d of %d (batch, head) blocks, full length %d, float64, %.1f s" % (
+            done, heads_total, p.seqlen, cpu_s)
+
+    def config(self):
+        p = self.p
+        return {"workload": p.name, "batch": p.batch, "seqlen": p.seqlen, "nheads": p.nheads,
+                "headdim": p.headdim, "dstate": p.dstate, "ngroups": p.ngroups, "io": p.io,
+                "chunk": self.chunk}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mamba2.8b_layer_bf16")
+    ap.add_argument("--variant", default="auto", choices=sorted(VARIANTS))
+    ap.add_argument("--chunk", type=int, default=256, help="SSD chunk length")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input/output buffer sets cycled across steps (0: enough to exceed the "
+                         "256 MB Infinity Cache)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed steps, copy a buffer of this many MiB three times "
+                         "(a plain kernel of known traffic for calibrating HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from selective_state_space_05_amd import api, inputs
+
+    dev = torch.device("cuda:0")
+    if args.workload in inputs.SCAN_PROBLEMS:
+        p = inputs.SCAN_PROBLEMS[args.workload]
+        print("[bench] workload %s: drawing inputs" % p.name, file=sys.stderr, flush=True)
+        wb = ScanBench(p, dev, torch)
+    elif args.workload in inputs.SSD_PROBLEMS:
+        p = inputs.SSD_PROBLEMS[args.workload]
+        print("[bench] workload %s: drawing inputs" % p.name, file=sys.stderr, flush=True)
+        wb = SSDBench(p, dev, torch, args.chunk)
+    else:
+        raise SystemExit("unknown workload %s; choose from %s" % (
+            args.workload, sorted(inputs.SCAN_PROBLEMS) + sorted(inputs.SSD_PROBLEMS)))
+
+    footprint = p.min_traffic_bytes()
+    rotate = args.rotate or max(1, min(4, -(-(1 << 30) // footprint)))
+    sets = [wb.upload() for _ in range(rotate)]
+    torch.cuda.synchronize()
+
+    variant = VARIANTS[args.variant]
+    print("[bench] warmup %d, timed %d steps, %d buffer sets" % (args.warmup, args.steps, rotate),
+          file=sys.stderr, flush=True)
+    with api.forced_variant(variant):
+        for i in range(args.warmup):
+            wb.step(sets[i % rotate])
+        torch.cuda.synchronize()
+        used = VARIANT_NAMES.get(api.last_variant(), str(api.last_variant()))
+        # the library launches on torch's current stream; the events are
+        # recorded on that same stream
+        stream = torch.cuda.current_stream(dev)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            wb.step(sets[i % rotate])
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    sec = ms_step / 1e3
+
+    hbm_gbs = footprint / sec / 1e9
+    roof = wb.roofline(sec)
+    sha = kernel_source_sha()
+    roof["traffic"] = load_traffic(p.name, sha)
+    roof["kernel_source_sha"] = sha
+    cfg = wb.config()
+    cfg.update({"variant": used, "buffer_sets": rotate})
+
+    out = {
+        "metric": METRIC,
+        "value": p.elements / sec,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded numpy draws; no dataset or trained weights)",
+        "config": cfg,
+        "hbm": {"min_traffic_bytes": footprint, "achieved_gbs": hbm_gbs,
+                "peak_gbs": HBM_PEAK_GBS, "frac": hbm_gbs / HBM_PEAK_GBS},
+        "roofline": roof,
+    }
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 18          # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes_each_way"] = n * 4
+        del src, dst
+
+    if not args.no_parity:
+        print("[bench] parity on sampled rows", file=sys.stderr, flush=True)
+        t = sets[(args.steps - 1) % rotate]
+        nrows, ey, eh = wb.parity(t)
+        tol = 1e-4 if p.io == "f32" else 3e-3
+        out["parity"] = {"rows": nrows, "g1_y": ey, "g1_h_last": eh, "tol": tol,
+                         "ok": bool(ey <= tol and eh <= tol)}
+
+    if not args.no_cpu:
+        threads = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "16")), 16)
+        print("[bench] CPU oracle baseline (%d threads)" % threads, file=sys.stderr, flush=True)
+        v, sample = wb.cpu_baseline(threads)
+        out["cpu_baseline"] = {"value": v, "unit": "elements/s", "cores": threads,
+                               "kind": "oracle", "sample": sample}
 
     print(json.dumps(out), flush=True)
 

@@ -51,7 +51,10 @@ bool scan_rowserial_supported(const ScanArgs &a);
 hipError_t launch_scan_chunked(const ScanArgs &a, hipStream_t stream);
 bool scan_chunked_supported(const ScanArgs &a);
 int64_t scan_chunked_waves(const ScanArgs &a);
-// Rows start 16-byte aligned and L % 4 == 0: activations move as vectors.
+// Rows start 16-byte aligned and L % 8 == 0: activations move as vectors.
+// The chunk walk addresses 16 channel rows and the N rows of B / C with
+// 32-bit byte offsets: max(16, N) * L elements must fit in 2^31 bytes.
+bool scan_offsets_fit(const ScanArgs &a);
 bool scan_rows_vectorizable(const ScanArgs &a);
 
 // Chunk-parallel variant; allocates its look-back scratch stream-ordered.

@@ -72,13 +72,18 @@ hipError_t launch_by_n(const ScanArgs &a, hipStream_t stream) {
 
 bool scan_rows_vectorizable(const ScanArgs &a) {
     auto aligned = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-    return (a.L % 4 == 0) && aligned(a.u) && aligned(a.delta) && aligned(a.y) &&
+    return (a.L % 8 == 0) && aligned(a.u) && aligned(a.delta) && aligned(a.y) &&
            (!a.z || aligned(a.z));
+}
+
+bool scan_offsets_fit(const ScanArgs &a) {
+    const int64_t esz = a.io == IO_F32 ? 4 : 2;
+    return (a.N > kCh ? a.N : kCh) * a.L * esz < (int64_t(1) << 31);
 }
 
 bool scan_chunked_supported(const ScanArgs &a) {
     const int64_t groups = (a.dim + kCh - 1) / kCh;
-    return a.N >= 1 && a.N <= 64 && a.dim <= (int64_t(1) << 30) &&
+    return a.N >= 1 && a.N <= 64 && a.dim <= (int64_t(1) << 30) && scan_offsets_fit(a) &&
            a.batch * groups < (int64_t(1) << 31);
 }
 

@@ -109,38 +109,6 @@ struct Pack {
     }
 };
 
-// Owner loads of one chunk: OS steps of u, delta (and z) of one channel.
-template <typename T, int OS, bool VEC, bool GATE>
-struct OwnerIn {
-    float u[OS], dr[OS], z[OS];
-    typename Pack<T, OS>::raw ru, rd, rz;
-    __device__ void load(const T *pu, const T *pd, const T *pz, int64_t off, int64_t nvalid) {
-        if (VEC && nvalid >= OS) {
-            ru = Pack<T, OS>::load(pu + off);
-            rd = Pack<T, OS>::load(pd + off);
-            if (GATE) rz = Pack<T, OS>::load(pz + off);
-        } else {
-            // tail (or unaligned rows): gather the valid steps, zero the rest
-            T su[OS], sd[OS], sz[OS];
-#pragma unroll
-            for (int i = 0; i < OS; ++i) {
-                const bool ok = i < nvalid;
-                su[i] = ok ? pu[off + i] : T(0);
-                sd[i] = ok ? pd[off + i] : T(0);
-                sz[i] = (ok && GATE) ? pz[off + i] : T(0);
-            }
-            __builtin_memcpy(&ru, su, sizeof(ru));
-            __builtin_memcpy(&rd, sd, sizeof(rd));
-            __builtin_memcpy(&rz, sz, sizeof(rz));
-        }
-    }
-    __device__ void unpack() {
-        Pack<T, OS>::unpack(ru, u);
-        Pack<T, OS>::unpack(rd, dr);
-        if (GATE) Pack<T, OS>::unpack(rz, z);
-    }
-};
-
 // LDS of one workgroup.  dl / dl*u are double-buffered so that the
 // state-only walk needs one barrier per chunk.
 template <int W>
@@ -156,20 +124,38 @@ struct Walker {
     static constexpr int kRows = 4 * W;            // rows of 16 lanes
     static constexpr int OS = kT * kCh / (64 * W); // steps per owner thread (4 or 2)
     static constexpr int OPC = kT / OS;            // owner threads per channel
+    using Raw = typename Pack<T, OS>::raw;
+
+    // Inputs of one chunk exactly as loaded; they are converted where they
+    // are first used, a chunk after the loads were issued, so the loads
+    // overlap a whole chunk of work.
+    struct In {
+        Raw ru, rd, rz;            // owner: OS steps of u, delta (and z)
+        T rb[2][NPL], rc[2][NPL];  // scan lane: B, C at steps t0 + 16 q + j
+    };
 
     // scan-lane role
     int prow, j;
     float A2[NPL];
-    int64_t bcrow[NPL];
+    uint32_t bco[NPL];     // byte offset of this lane's B / C rows in the batch
     bool nok[NPL];
-    const T *Bm, *Cm;
+    const T *Bb, *Cb;      // B, C of this batch (workgroup-uniform)
     // owner role
     int oc, ok;
-    const T *pu, *pd, *pz;
-    T *py;                 // null when the owner's channel is past the end
+    uint32_t oo;           // byte offset of the owner's channel row
+    const T *ub, *db, *zb; // rows of the workgroup's first channel (uniform)
+    T *yb;
     float bias, skip;
-    int64_t L;
+    int L;
     float sdl;             // owner's running sum of dl over the walked steps
+
+    // Offsets are 32-bit byte offsets from workgroup-uniform bases, which
+    // keeps per-load address arithmetic to one 32-bit add; the launchers
+    // guarantee 16 * L and N * L elements fit in 2^31 bytes.
+    template <typename V>
+    __device__ static V ld(const T *base, uint32_t off) {
+        return *reinterpret_cast<const V *>(reinterpret_cast<const char *>(base) + off);
+    }
 
     __device__ void init(const T *u, const T *delta, const float *delta_bias, const float *A,
                          const T *B, const T *C, const float *Dskip, const T *z, T *y,
@@ -178,110 +164,140 @@ struct Walker {
         const int lane = tid & 63;
         prow = (tid >> 6) * 4 + (lane >> 4);
         j = lane & 15;
-        L = L_;
-        Bm = B;
-        Cm = C;
+        L = static_cast<int>(L_);
+        Bb = B + b * N * L_;
+        Cb = C + b * N * L_;
         const int dS = min(d0 + j, dim - 1);
 #pragma unroll
         for (int g = 0; g < NPL; ++g) {
             const int n = prow * NPL + g;
             nok[g] = n < N;
             A2[g] = nok[g] ? A[static_cast<int64_t>(dS) * N + n] * kLog2e : 0.0f;
-            bcrow[g] = (b * N + min(n, N - 1)) * L;
+            bco[g] = static_cast<uint32_t>(min(n, N - 1)) * static_cast<uint32_t>(L) * sizeof(T);
         }
         oc = tid / OPC;
         ok = tid % OPC;
+        // Channels past the last one compute on the last channel's inputs
+        // (scan lanes and owners alike), so their outputs equal that
+        // channel's outputs bit for bit; storing them into its row rewrites
+        // the same values and needs no branch around the store.
         const int dO = min(d0 + oc, dim - 1);
-        const int64_t orow = (b * dim + dO) * L;
+        const int64_t row0 = (b * dim + d0) * L_;
+        oo = static_cast<uint32_t>(dO - d0) * static_cast<uint32_t>(L) * sizeof(T);
         bias = delta_bias ? delta_bias[dO] : 0.0f;
         skip = Dskip ? Dskip[dO] : 0.0f;
-        pu = u + orow;
-        pd = delta + orow;
-        pz = GATE ? z + orow : nullptr;
-        py = (y && d0 + oc < dim) ? y + orow : nullptr;
+        ub = u + row0;
+        db = delta + row0;
+        zb = GATE ? z + row0 : nullptr;
+        yb = y ? y + row0 : nullptr;
         sdl = 0.0f;
     }
 
-    // B / C values this lane contributes to the row broadcasts of one chunk.
-    __device__ void load_bc(int64_t t0, int64_t t_end, float (&bs)[2][NPL], float (&cs)[2][NPL],
-                            bool with_c) const {
+    // Issue the loads of the chunk starting at step t0, from indices clamped
+    // into the row and with no branch, so that nothing waits for them before
+    // their use.  Values of steps past the walked range are discarded there.
+    template <bool OUT>
+    __device__ void load(int t0, In &in) const {
+        const int off = t0 + OS * ok;
+        if constexpr (VEC) {
+            // rows 16-byte aligned and L % 8 == 0 with OS | 8: the OS steps
+            // are all inside the row or all past its end
+            static_assert(8 % OS == 0, "vector owner loads need OS | 8");
+            const uint32_t o = oo + static_cast<uint32_t>(off + OS <= L ? off : L - OS) * sizeof(T);
+            in.ru = ld<Raw>(ub, o);
+            in.rd = ld<Raw>(db, o);
+            if (GATE && OUT) in.rz = ld<Raw>(zb, o);
+        } else {
+            T su[OS], sd[OS], sz[OS];
+#pragma unroll
+            for (int i = 0; i < OS; ++i) {
+                const uint32_t o = oo + static_cast<uint32_t>(off + i < L ? off + i : L - 1) * sizeof(T);
+                su[i] = ld<T>(ub, o);
+                sd[i] = ld<T>(db, o);
+                sz[i] = (GATE && OUT) ? ld<T>(zb, o) : T(0);
+            }
+            __builtin_memcpy(&in.ru, su, sizeof(Raw));
+            __builtin_memcpy(&in.rd, sd, sizeof(Raw));
+            __builtin_memcpy(&in.rz, sz, sizeof(Raw));
+        }
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const int64_t t = t0 + 16 * q + j;
+            const int t = t0 + 16 * q + j;
+            const uint32_t to = static_cast<uint32_t>(t < L ? t : L - 1) * sizeof(T);
 #pragma unroll
             for (int g = 0; g < NPL; ++g) {
-                const bool ok2 = t < t_end && nok[g];
-                bs[q][g] = ok2 ? Io<T>::load(Bm, bcrow[g] + t) : 0.0f;
-                cs[q][g] = (ok2 && with_c) ? Io<T>::load(Cm, bcrow[g] + t) : 0.0f;
+                in.rb[q][g] = ld<T>(Bb, bco[g] + to);
+                if (OUT) in.rc[q][g] = ld<T>(Cb, bco[g] + to);
             }
         }
     }
 
-    // Walk steps [t_begin, t_end) from state h (updated in place).  OUT: also
-    // form and store y; otherwise only the state and the owner's sum of dl.
-    // t_begin must be a multiple of OS; every thread of the workgroup calls
-    // this with the same range.
-    template <bool OUT>
-    __device__ void walk(int64_t t_begin, int64_t t_end, float (&h)[NPL], Smem<W> &sm) {
-        const int64_t nchunks = (t_end - t_begin + kT - 1) / kT;
-        OwnerIn<T, OS, VEC, GATE && OUT> nxt;
-        float nb[2][NPL], nc[2][NPL];
-        {
-            const int64_t off = t_begin + OS * ok;
-            nxt.load(pu, pd, pz, off, t_end - off);
-            load_bc(t_begin, t_end, nb, nc, OUT);
+    __device__ static float to_f32(T v) {
+        if constexpr (sizeof(T) == 4) return v;
+        else return __uint_as_float(static_cast<uint32_t>(v) << 16);
+    }
+
+    // One chunk of kT steps starting at t0.  FULL: all kT steps lie inside
+    // [t0, t_end).  OUT: form and store y; otherwise only the state and the
+    // owner's sum of dl.  buf selects the dl / dl*u buffer (state-only walks
+    // alternate buffers and need one barrier per chunk).
+    template <bool OUT, bool FULL>
+    __device__ void chunk(int t0, int t_end, const In &in, float (&h)[NPL], Smem<W> &sm, int buf) {
+        // ---- B, C of the row broadcasts: zero past the end and for state
+        // rows past N ------------------------------------------------------
+        float cb[2][NPL], cc[2][NPL];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const bool tok = FULL || t0 + 16 * q + j < t_end;
+#pragma unroll
+            for (int g = 0; g < NPL; ++g) {
+                const bool okv = tok && nok[g];
+                cb[q][g] = okv ? to_f32(in.rb[q][g]) : 0.0f;
+                cc[q][g] = (OUT && okv) ? to_f32(in.rc[q][g]) : 0.0f;
+            }
         }
-        for (int64_t c = 0; c < nchunks; ++c) {
-            const int64_t t0 = t_begin + c * kT;
-            const int buf = OUT ? 0 : static_cast<int>(c & 1);
-            OwnerIn<T, OS, VEC, GATE && OUT> cur = nxt;
-            float cb[2][NPL], cc[2][NPL];
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-#pragma unroll
-                for (int g = 0; g < NPL; ++g) { cb[q][g] = nb[q][g]; cc[q][g] = nc[q][g]; }
-            if (c + 1 < nchunks) {
-                const int64_t off = t0 + kT + OS * ok;
-                nxt.load(pu, pd, pz, off, t_end - off);
-                load_bc(t0 + kT, t_end, nb, nc, OUT);
-            }
 
-            // ---- A: per-step scalars of this thread's OS steps --------------
-            cur.unpack();
-            float dl[OS], du[OS], sk[OS], gz[OS];
+        // ---- A: per-step scalars of this thread's OS steps ------------------
+        float u[OS], dr[OS], zz[OS];
+        Pack<T, OS>::unpack(in.ru, u);
+        Pack<T, OS>::unpack(in.rd, dr);
+        if (GATE && OUT) Pack<T, OS>::unpack(in.rz, zz);
+        int rem = OS;                       // steps of this owner inside the range
+        if (!FULL) rem = min(t_end - (t0 + OS * ok), OS);
+        float dl[OS], du[OS], sk[OS], gz[OS];
 #pragma unroll
-            for (int i = 0; i < OS; ++i) {
-                // computed unconditionally (inputs past the end are zero),
-                // then steps past the end become the identity step dl = 0
-                const float sp = softplus(cur.dr[i] + bias);
-                dl[i] = t0 + OS * ok + i < t_end ? sp : 0.0f;
-                du[i] = dl[i] * cur.u[i];
-                if (OUT) {
-                    sk[i] = skip * cur.u[i];
-                    gz[i] = GATE ? silu(cur.z[i]) : 1.0f;
-                } else {
-                    sdl += dl[i];
-                }
+        for (int i = 0; i < OS; ++i) {
+            // computed unconditionally; steps past the end become the
+            // identity step dl = 0, dl*u = 0
+            const float sp = softplus(dr[i] + bias);
+            dl[i] = (FULL || i < rem) ? sp : 0.0f;
+            du[i] = (FULL || i < rem) ? sp * u[i] : 0.0f;
+            if (OUT) {
+                sk[i] = skip * u[i];
+                gz[i] = (GATE && OUT) ? silu(zz[i]) : 1.0f;
+            } else {
+                sdl += dl[i];
             }
+        }
 #pragma unroll
-            for (int i = 0; i < OS; i += 2) {
-                *reinterpret_cast<float2 *>(sm.dl[buf] + oc * kPitch + OS * ok + i) = make_float2(dl[i], dl[i + 1]);
-                *reinterpret_cast<float2 *>(sm.du[buf] + oc * kPitch + OS * ok + i) = make_float2(du[i], du[i + 1]);
-            }
-            __syncthreads();
+        for (int i = 0; i < OS; i += 2) {
+            *reinterpret_cast<float2 *>(sm.dl[buf] + oc * kPitch + OS * ok + i) = make_float2(dl[i], dl[i + 1]);
+            *reinterpret_cast<float2 *>(sm.du[buf] + oc * kPitch + OS * ok + i) = make_float2(du[i], du[i + 1]);
+        }
+        __syncthreads();
 
-            // ---- B: 32 steps of the recurrence for this lane ----------------
+        // ---- B: 32 steps of the recurrence for this lane ----------------------
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                float dls[16], dus[16], p[16];
-                const float4 *pdl = reinterpret_cast<const float4 *>(sm.dl[buf] + j * kPitch + 16 * q);
-                const float4 *pdu = reinterpret_cast<const float4 *>(sm.du[buf] + j * kPitch + 16 * q);
+        for (int q = 0; q < 2; ++q) {
+            float dls[16], dus[16], p[16];
+            const float4 *pdl = reinterpret_cast<const float4 *>(sm.dl[buf] + j * kPitch + 16 * q);
+            const float4 *pdu = reinterpret_cast<const float4 *>(sm.du[buf] + j * kPitch + 16 * q);
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const float4 a = pdl[k], e = pdu[k];
-                    dls[4 * k] = a.x; dls[4 * k + 1] = a.y; dls[4 * k + 2] = a.z; dls[4 * k + 3] = a.w;
-                    dus[4 * k] = e.x; dus[4 * k + 1] = e.y; dus[4 * k + 2] = e.z; dus[4 * k + 3] = e.w;
-                }
+            for (int k = 0; k < 4; ++k) {
+                const float4 a = pdl[k], e = pdu[k];
+                dls[4 * k] = a.x; dls[4 * k + 1] = a.y; dls[4 * k + 2] = a.z; dls[4 * k + 3] = a.w;
+                dus[4 * k] = e.x; dus[4 * k + 1] = e.y; dus[4 * k + 2] = e.z; dus[4 * k + 3] = e.w;
+            }
 #define MSSM_STEP(S)                                                           \
     {                                                                          \
         float acc = 0.0f;                                                      \
@@ -293,47 +309,84 @@ struct Walker {
         }                                                                      \
         p[S] = acc;                                                            \
     }
-                MSSM_STEP(0) MSSM_STEP(1) MSSM_STEP(2) MSSM_STEP(3)
-                MSSM_STEP(4) MSSM_STEP(5) MSSM_STEP(6) MSSM_STEP(7)
-                MSSM_STEP(8) MSSM_STEP(9) MSSM_STEP(10) MSSM_STEP(11)
-                MSSM_STEP(12) MSSM_STEP(13) MSSM_STEP(14) MSSM_STEP(15)
+            MSSM_STEP(0) MSSM_STEP(1) MSSM_STEP(2) MSSM_STEP(3)
+            MSSM_STEP(4) MSSM_STEP(5) MSSM_STEP(6) MSSM_STEP(7)
+            MSSM_STEP(8) MSSM_STEP(9) MSSM_STEP(10) MSSM_STEP(11)
+            MSSM_STEP(12) MSSM_STEP(13) MSSM_STEP(14) MSSM_STEP(15)
 #undef MSSM_STEP
-                if (OUT) {
-                    float4 *dst = reinterpret_cast<float4 *>(sm.p + (prow * kCh + j) * kPitch + 16 * q);
+            if (OUT) {
+                float4 *dst = reinterpret_cast<float4 *>(sm.p + (prow * kCh + j) * kPitch + 16 * q);
 #pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        dst[k] = make_float4(p[4 * k], p[4 * k + 1], p[4 * k + 2], p[4 * k + 3]);
-                }
+                for (int k = 0; k < 4; ++k)
+                    dst[k] = make_float4(p[4 * k], p[4 * k + 1], p[4 * k + 2], p[4 * k + 3]);
             }
-            if (!OUT) continue;
-            __syncthreads();
+        }
+        if (!OUT) return;
+        __syncthreads();
 
-            // ---- C: reduce the partial sums, skip term, gate, store ---------
-            float yv[OS];
+        // ---- C: reduce the partial sums, skip term, gate, store --------------
+        float yv[OS];
 #pragma unroll
-            for (int i = 0; i < OS; ++i) yv[i] = 0.0f;
+        for (int i = 0; i < OS; ++i) yv[i] = 0.0f;
 #pragma unroll
-            for (int r = 0; r < kRows; ++r) {
-                const float *src = sm.p + (r * kCh + oc) * kPitch + OS * ok;
+        for (int r = 0; r < kRows; ++r) {
+            const float *src = sm.p + (r * kCh + oc) * kPitch + OS * ok;
 #pragma unroll
-                for (int i = 0; i < OS; i += 2) {
-                    const float2 v = *reinterpret_cast<const float2 *>(src + i);
-                    yv[i] += v.x;
-                    yv[i + 1] += v.y;
-                }
+            for (int i = 0; i < OS; i += 2) {
+                const float2 v = *reinterpret_cast<const float2 *>(src + i);
+                yv[i] += v.x;
+                yv[i + 1] += v.y;
             }
+        }
 #pragma unroll
-            for (int i = 0; i < OS; ++i) yv[i] = (yv[i] + sk[i]) * gz[i];
-            const int64_t tt = t0 + OS * ok;
-            if (py) {
-                if (VEC && tt + OS <= t_end) {
-                    Pack<T, OS>::store(py + tt, yv);
-                } else {
+        for (int i = 0; i < OS; ++i) yv[i] = (yv[i] + sk[i]) * gz[i];
+        T *py = reinterpret_cast<T *>(reinterpret_cast<char *>(yb) + oo) + (t0 + OS * ok);
+        if (FULL) {
+            if (VEC) {
+                Pack<T, OS>::store(py, yv);
+            } else {
 #pragma unroll
-                    for (int i = 0; i < OS; ++i)
-                        if (tt + i < t_end) Io<T>::store(py, tt + i, yv[i]);
-                }
+                for (int i = 0; i < OS; ++i) Io<T>::store(py, i, yv[i]);
             }
+        } else {
+#pragma unroll
+            for (int i = 0; i < OS; ++i)
+                if (i < rem) Io<T>::store(py, i, yv[i]);
+        }
+    }
+
+    // Walk steps [t_begin, t_end) from state h (updated in place).  OUT: also
+    // form and store y; otherwise only the state and the owner's sum of dl.
+    // t_begin must be a multiple of OS; every thread of the workgroup calls
+    // this with the same range.  The chunk barriers make the loop's LDS
+    // reuse safe: y-walks reuse one buffer (their second barrier orders the
+    // next chunk's writes), state-only walks alternate two (even chunks use
+    // buffer 0).
+    template <bool OUT>
+    __device__ void walk(int t_begin, int t_end, float (&h)[NPL], Smem<W> &sm) {
+        const int nfull = (t_end - t_begin) / kT;
+        // Two input sets used in turn: the loads of chunk c + 1 go straight
+        // into the registers that chunk c + 1 reads, with no copy in between
+        // (a copy would have to wait for the loads).
+        In x0, x1;
+        load<OUT>(t_begin, x0);
+        int c = 0;
+        for (; c + 1 < nfull; c += 2) {
+            const int t0 = t_begin + c * kT;
+            load<OUT>(t0 + kT, x1);
+            chunk<OUT, true>(t0, t_end, x0, h, sm, 0);
+            load<OUT>(t0 + 2 * kT, x0);
+            chunk<OUT, true>(t0 + kT, t_end, x1, h, sm, OUT ? 0 : 1);
+        }
+        // x0 holds the inputs of chunk c; loads past the range are clamped
+        // and their values unused
+        const int t0 = t_begin + c * kT;
+        if (c < nfull) {
+            load<OUT>(t0 + kT, x1);
+            chunk<OUT, true>(t0, t_end, x0, h, sm, 0);
+            if (t0 + kT < t_end) chunk<OUT, false>(t0 + kT, t_end, x1, h, sm, OUT ? 0 : 1);
+        } else if (t0 < t_end) {
+            chunk<OUT, false>(t0, t_end, x0, h, sm, 0);
         }
     }
 

@@ -94,8 +94,8 @@ __global__ __launch_bounds__(64 * W) void scan_lookback_kernel(
 
     core::Walker<T, W, NPL, GATE, VEC> wk;
     wk.init(u, delta, delta_bias, A, Bm, Cm, Dskip, z, y, L, dim, N, b, d0);
-    const int64_t t_begin = static_cast<int64_t>(k) * seg_len;
-    const int64_t t_end = min(L, t_begin + seg_len);
+    const int t_begin = static_cast<int>(static_cast<int64_t>(k) * seg_len);
+    const int t_end = static_cast<int>(min(L, static_cast<int64_t>(t_begin) + seg_len));
 
     // ---- 1. local pair of the segment ---------------------------------------
     float h[NPL];
@@ -232,7 +232,7 @@ hipError_t launch_by_n(const ScanArgs &a, hipStream_t stream) {
 }  // namespace
 
 bool scan_lookback_supported(const ScanArgs &a) {
-    if (a.N < 1 || a.N > 64) return false;
+    if (a.N < 1 || a.N > 64 || !scan_offsets_fit(a)) return false;
     const int64_t groups = a.batch * ((a.dim + kCh - 1) / kCh);
     if (groups >= (int64_t(1) << 20)) return false;
     const Plan p = make_plan(a);
