@@ -1,41 +1,42 @@
-// ssd_chunked.hip -- Mamba-2 scalar-decay (SSD) forward in the chunked
-// matrix form, on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
+// ssd_chunked.hip -- Mamba-2 scalar-decay (SSD) forward in the chunked matrix
+// form on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16), parallel over
+// chunks.
 //
-// Per batch b and head h, with dl_t = softplus(dt_t + dt_bias[h]) and the
-// log decay l_t = dl_t A[h] ("Mamba状态空间模型的硬件感知推理优化" (ybb.press)
+// Per batch b and head h, with dl_t = softplus(dt_t + dt_bias[h]) and the log
+// decay l_t = dl_t A[h] ("Mamba状态空间模型的硬件感知推理优化" (ybb.press)
 // section 4: one scalar decay per step and head; section 6.2: cumulative
 // products taken in log space), the sequence is cut into chunks of Q steps.
-// Inside a chunk, with cum_t the inclusive sum of l over the chunk up to t:
+// With cum_t the inclusive sum of l over the chunk up to t and h_in the state
+// entering the chunk:
 //
+//   S[p,n]      = sum_s exp(cum_end - cum_s) dl_s x_s[p] B_s[n]      (chunk state)
+//   h_out       = exp(cum_end) h_in + S                                (state pass)
 //   Y_diag[t,p] = sum_{s<=t} (C_t . B_s) exp(cum_t - cum_s) dl_s x_s[p]
-//   Y_off[t,p]  = exp(cum_t) sum_n C_t[n] h_prev[p,n]
-//   S[p,n]      = sum_s exp(cum_end - cum_s) dl_s x_s[p] B_s[n]
-//   h[p,n]      = exp(cum_end) h_prev[p,n] + S[p,n]
+//   Y_off[t,p]  = exp(cum_t) sum_n C_t[n] h_in[p,n]
 //   y[t,p]      = Y_diag + Y_off + D[h] x_t[p]
 //
 // which is the recurrence S_t = a_t S_{t-1} + dl_t x_t B_t^T, y = C_t S_t +
-// D x_t unrolled over the chunk (the cumulative-product closed form of the
-// same ybb.press section).  Chunks are walked in order, so h never leaves
-// the chip.
+// D x_t unrolled over a chunk (the cumulative-product closed form of the
+// same ybb.press section; its chunk-by-chunk state carry is section 5).
 //
-// Work decomposition.  A workgroup of four waves owns one (batch, head,
-// 32-wide slice of the head dimension) and walks every chunk.  Per chunk:
-//   * B (Q x N) is staged in LDS as bf16, x (Q x 32) transposed to (32 x Q),
-//     and x * exp(cum_end - cum_s) dl_s split into bf16 high and low parts;
-//   * wave w takes the 32-row time blocks w and Q/32-1-w (balanced causal
-//     work).  For each earlier-or-equal source block it forms
-//     G' = B_s C_t^T on the matrix cores, scales it by exp(cum_t - cum_s)
-//     dl_s under the causal mask in registers, splits the result into bf16
-//     high/low parts, and feeds them straight back as the A operand of the
-//     product with x -- the accumulator layout of G' (column = target step)
-//     is the operand layout with a permuted K order, and x is read in the
-//     same permuted order, so no LDS round trip is needed;
-//   * the off-diagonal term C_t h_prev^T reads h_prev (bf16 high/low) from
-//     LDS; y is assembled in registers and stored;
-//   * wave w also forms the chunk state S for state columns 32w..32w+31.
-// Products whose operands are not exact bf16 values (the masked decay
-// matrix, x * decay, the carried state) use a two-term bf16 split, so every
-// product carries about 16 significant bits; accumulation is float32.
+// Three kernels, so that every chunk is worked on at once:
+//   1. ssd_state_kernel: the chunk state S as a matrix-core product
+//      (x * weight)^T B over the chunk's steps, and the chunk's total log2
+//      decay;
+//   2. ssd_pass_kernel: walks the chunks of each (batch, head) in order,
+//      elementwise over the P x N state, replacing each chunk state by the
+//      state entering that chunk and writing h_last;
+//   3. ssd_output_kernel: the outputs, computed transposed
+//      (Y^T = X^T M^T + H C^T) so that each lane owns one step t: the decay
+//      factors become per-lane scalars and each lane stores four consecutive
+//      head-dimension values at once.
+// Kernels 1 and 3 give each workgroup one (batch, chunk) and a run of heads
+// of one B / C group: B (and C) of the chunk are staged once and serve every
+// head of the run, and the next head's x rows are prefetched into registers
+// while the current head is computed.
+// Products whose operands are not exact bf16 values (x * weight, the masked
+// decay matrix, the carried state) use a two-term bf16 split (hi + lo), so
+// each product carries about 16 significant bits; accumulation is float32.
 #include "device_math.h"
 #include "internal.h"
 
@@ -45,34 +46,35 @@ namespace {
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef float f16x __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
-constexpr int kPt = 32;                 // head-dimension columns per workgroup
+constexpr int kPG = 64;     // head-dimension columns per workgroup (two 32-wide tiles)
 
 __device__ __forceinline__ f16x mfma(bf8 a, bf8 b, f16x c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint16_t bf16_bits(__bf16 v) { return __builtin_bit_cast(uint16_t, v); }
-__device__ __forceinline__ float bf16_val(__bf16 v) {
-    return __uint_as_float(static_cast<uint32_t>(bf16_bits(v)) << 16);
+__device__ __forceinline__ f16x zero16() {
+    f16x z;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) z[v] = 0.0f;
+    return z;
 }
+
 // Two floats rounded to bf16 (nearest even), packed low half first.
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
     const bf2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
     return __builtin_bit_cast(uint32_t, v);
 }
-// Two-term split: v ~= hi + lo with both parts bf16 (about 16 significant bits).
-__device__ __forceinline__ void split(float v, __bf16 &hi, __bf16 &lo) {
-    hi = static_cast<__bf16>(v);
-    lo = static_cast<__bf16>(v - bf16_val(hi));
+// Two-term split of two floats: hi = bf16(v), lo = bf16(v - hi).
+__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = pack2(a, b);
+    lo = pack2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
-// Eight consecutive bf16 of row `t` starting at column c8 of a row-major
-// (rows x cols) slice with row stride `stride`; zero past the last row or
-// column.  Branch-free: out-of-range reads are redirected to element 0 and
-// the value is discarded, so all loads of a phase are in flight together.
-// vec: rows start 16-byte aligned and cols % 8 == 0.
+// Eight consecutive bf16 of row t starting at column c8 of a row-major slice
+// with row stride `stride`; zero past the last row or column.  Out-of-range
+// reads are redirected to element 0 (always valid) and discarded, so the
+// load needs no branch.  vec: rows 16-byte aligned and cols % 8 == 0.
 __device__ __forceinline__ uint4 load_row8(const uint16_t *base, int64_t t, int c8, int64_t rows,
                                            int cols, int64_t stride, bool vec) {
     const bool okt = t < rows;
@@ -93,204 +95,399 @@ __device__ __forceinline__ uint4 load_row8(const uint16_t *base, int64_t t, int 
     return v;
 }
 
-template <typename T> struct Ld;
-template <> struct Ld<uint16_t> {
-    __device__ static float f(const uint16_t *p, int64_t i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ float bits_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bits_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+struct Geom {
+    int64_t L;
+    int H, P, N, G, nch, npg;
 };
 
-// LDS of one workgroup (bf16 data held as raw uint16_t).
+// Work item of the state and output kernels: one (batch, chunk) and a run of
+// heads that read the same B / C group, so B and C are staged once and reused
+// by every head of the run; within a run, item i covers head h0 + i / npg and
+// head-dimension slice i % npg.
+struct Run {
+    int64_t b;
+    int c, h0, items, grp;
+};
+
+__device__ __forceinline__ Run decode_run(const Geom &g, int runs_per_chunk, int heads_per_run) {
+    int64_t id = blockIdx.x;
+    const int r = static_cast<int>(id % runs_per_chunk);
+    id /= runs_per_chunk;
+    Run run;
+    run.c = static_cast<int>(id % g.nch);
+    run.b = id / g.nch;
+    run.h0 = r * heads_per_run;
+    const int h1 = min(g.H, run.h0 + heads_per_run);
+    run.items = (h1 - run.h0) * g.npg;
+    run.grp = run.h0 / (g.H / g.G);
+    return run;
+}
+
+// ---------------------------------------------------------------------------
+// 1. chunk states
+// ---------------------------------------------------------------------------
 template <int Q, int NP>
-struct __align__(16) Smem {
-    // Row pitches (elements) chosen so the operand reads of one instruction
-    // fall in distinct LDS banks: 8-byte reads of X need a row stride of
-    // 2 mod 64 dwords, 16-byte reads of Xw, B and h_prev 4 mod 64 dwords.
-    static constexpr int BP = NP + 8;   // B[s][n]
-    static constexpr int XP = Q + 4;    // x[s][p] stored as X[p][s]
-    static constexpr int WP = Q + 8;    // x * w, stored like X
-    static constexpr int HP = NP + 8;   // h_prev[p][n]
-    uint16_t B[Q * BP];
-    uint16_t X[kPt * XP];
-    uint16_t Xwh[kPt * WP], Xwl[kPt * WP];   // high / low bf16 parts
-    uint16_t Hh[kPt * HP], Hl[kPt * HP];     // high / low bf16 parts
-    float cum[Q];      // inclusive sum of the log2 decay over the chunk
-    float dl[Q];
-    float fs[Q];       // 2^(cum at the end of s's 32-step block - cum_s) dl_s
-    float wsum[kThreads / 64];
+struct __align__(16) StateSmem {
+    static constexpr int XP = Q + 8;     // row pitch (elements) of the transposed tiles
+    uint16_t BT[NP * XP];                // B^T of the chunk
+    uint16_t Xh[kPG * XP], Xl[kPG * XP]; // (x * weight)^T, bf16 high / low parts
+    float cum[Q], dl[Q], wsum[4];
+};
+
+// x rows of one item, prefetched into registers: unit u of this thread covers
+// steps 2 s2, 2 s2 + 1 and head-dimension columns p8 .. p8 + 7.
+template <int Q>
+struct XRegs {
+    static constexpr int U = (Q / 2) * (kPG / 8) / 256;
+    uint4 v[U][2];
+    float dt;
+};
+
+template <int Q>
+__device__ __forceinline__ void load_x(XRegs<Q> &r, const uint16_t *x, const uint16_t *dt,
+                                       const Geom &g, const Run &run, int item, bool vecX) {
+    const int tid = threadIdx.x;
+    const int hh = run.h0 + item / g.npg, pbase = (item % g.npg) * kPG;
+    const int64_t t0 = static_cast<int64_t>(run.c) * Q;
+    const int64_t rowX = static_cast<int64_t>(g.H) * g.P;
+    const uint16_t *xg = x + run.b * g.L * rowX + static_cast<int64_t>(hh) * g.P + pbase;
+#pragma unroll
+    for (int k = 0; k < XRegs<Q>::U; ++k) {
+        const int u = tid + 256 * k;
+        const int s2 = 2 * (u / (kPG / 8)), p8 = (u % (kPG / 8)) * 8;
+        r.v[k][0] = load_row8(xg, t0 + s2, p8, g.L, g.P - pbase, rowX, vecX);
+        r.v[k][1] = load_row8(xg, t0 + s2 + 1, p8, g.L, g.P - pbase, rowX, vecX);
+    }
+    const int64_t t = t0 + (tid < Q ? tid : 0);
+    r.dt = bf16_to_f32(dt[(run.b * g.L + (t < g.L ? t : g.L - 1)) * g.H + hh]);
+}
+
+// dl and the inclusive sum of the log2 decay over the chunk's Q steps from a
+// prefetched raw dt value (thread s < Q holds step s).  Ends with a barrier.
+template <int Q>
+__device__ void chunk_decay_from(float dr, int64_t t0, int64_t L, float A2, float bias,
+                                 float *s_cum, float *s_dl, float *s_wsum) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    float dlv = 0.0f, ell = 0.0f;
+    if (tid < Q && t0 + tid < L) {
+        dlv = softplus(dr + bias);
+        ell = dlv * A2;
+    }
+    float sc = ell;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_up(sc, off, 64);
+        if (lane >= off) sc += o;
+    }
+    if (lane == 63) s_wsum[wave] = sc;
+    __syncthreads();
+    if (tid < Q) {
+        float base = 0.0f;
+        for (int w2 = 0; w2 < wave; ++w2) base += s_wsum[w2];
+        s_cum[tid] = sc + base;
+        s_dl[tid] = dlv;
+    }
+    __syncthreads();
+}
+
+template <int Q, int NP>
+__global__ __launch_bounds__(256) void ssd_state_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt,
+    const float *__restrict__ dt_bias, const float *__restrict__ A,
+    const uint16_t *__restrict__ Bm, float *__restrict__ S, float *__restrict__ ce, Geom g,
+    int runs_per_chunk, int heads_per_run, bool vecB, bool vecX) {
+    using Sm = StateSmem<Q, NP>;
+    constexpr int XP = Sm::XP;
+    __shared__ Sm sm;
+    const int tid = threadIdx.x;
+    // wave index as a scalar, so control flow that depends on it stays uniform
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+    const Run run = decode_run(g, runs_per_chunk, heads_per_run);
+    const int64_t t0 = static_cast<int64_t>(run.c) * Q;
+    const int64_t rowBC = static_cast<int64_t>(g.G) * g.N;
+    const uint16_t *Bg = Bm + run.b * g.L * rowBC + static_cast<int64_t>(run.grp) * g.N;
+
+    XRegs<Q> xr;
+    load_x<Q>(xr, x, dt, g, run, 0, vecX);
+    // B^T of the chunk, exact bf16 values re-packed as step pairs
+    for (int u = tid; u < (Q / 2) * (NP / 8); u += 256) {
+        const int s2 = 2 * (u / (NP / 8)), n8 = (u % (NP / 8)) * 8;
+        const uint4 v0 = load_row8(Bg, t0 + s2, n8, g.L, g.N, rowBC, vecB);
+        const uint4 v1 = load_row8(Bg, t0 + s2 + 1, n8, g.L, g.N, rowBC, vecB);
+        const uint32_t a[4] = {v0.x, v0.y, v0.z, v0.w}, e[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            *reinterpret_cast<uint32_t *>(&sm.BT[(n8 + 2 * r) * XP + s2]) = (a[r] & 0xffffu) | (e[r] << 16);
+            *reinterpret_cast<uint32_t *>(&sm.BT[(n8 + 2 * r + 1) * XP + s2]) = (a[r] >> 16) | (e[r] & 0xffff0000u);
+        }
+    }
+    const int nt = wave;                // this wave's 32-wide tile of the state index
+#pragma unroll 1
+    for (int item = 0; item < run.items; ++item) {
+        const int hh = run.h0 + item / g.npg, pbase = (item % g.npg) * kPG;
+        const int pcols = g.P - pbase;
+        // (the decay scan starts with a barrier: the previous item's MFMA
+        // reads of Xh / Xl are done before they are overwritten below)
+        __syncthreads();
+        chunk_decay_from<Q>(xr.dt, t0, g.L, A[hh] * kLog2e, dt_bias ? dt_bias[hh] : 0.0f, sm.cum,
+                            sm.dl, sm.wsum);
+        const float cum_end = sm.cum[Q - 1];
+        // (x * w)^T with w_s = 2^(cum_end - cum_s) dl_s, split into bf16 parts
+#pragma unroll
+        for (int k = 0; k < XRegs<Q>::U; ++k) {
+            const int u = tid + 256 * k;
+            const int s2 = 2 * (u / (kPG / 8)), p8 = (u % (kPG / 8)) * 8;
+            const float w0 = fast_exp2(cum_end - sm.cum[s2]) * sm.dl[s2];
+            const float w1 = fast_exp2(cum_end - sm.cum[s2 + 1]) * sm.dl[s2 + 1];
+            const uint4 v0 = xr.v[k][0], v1 = xr.v[k][1];
+            const uint32_t a[4] = {v0.x, v0.y, v0.z, v0.w}, e[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                uint32_t hi, lo;
+                split2(bits_lo(a[r]) * w0, bits_lo(e[r]) * w1, hi, lo);
+                *reinterpret_cast<uint32_t *>(&sm.Xh[(p8 + 2 * r) * XP + s2]) = hi;
+                *reinterpret_cast<uint32_t *>(&sm.Xl[(p8 + 2 * r) * XP + s2]) = lo;
+                split2(bits_hi(a[r]) * w0, bits_hi(e[r]) * w1, hi, lo);
+                *reinterpret_cast<uint32_t *>(&sm.Xh[(p8 + 2 * r + 1) * XP + s2]) = hi;
+                *reinterpret_cast<uint32_t *>(&sm.Xl[(p8 + 2 * r + 1) * XP + s2]) = lo;
+            }
+        }
+        __syncthreads();
+        // next item's x (the last item re-reads its own rows; unused)
+        load_x<Q>(xr, x, dt, g, run, item + 1 < run.items ? item + 1 : item, vecX);
+        // S[p][n] = sum_s (x w)^T[p][s] B^T[n][s]: A rows p, B operand columns n
+        f16x acc[2] = {zero16(), zero16()};
+        if (nt * 32 < NP) {
+#pragma unroll 2
+            for (int kq = 0; kq < Q / 16; ++kq) {
+                const int s8 = 16 * kq + 8 * half;
+                const bf8 bb = *reinterpret_cast<const bf8 *>(&sm.BT[(nt * 32 + l32) * XP + s8]);
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) {
+                    const bf8 ah = *reinterpret_cast<const bf8 *>(&sm.Xh[(pt * 32 + l32) * XP + s8]);
+                    const bf8 al = *reinterpret_cast<const bf8 *>(&sm.Xl[(pt * 32 + l32) * XP + s8]);
+                    acc[pt] = mfma(ah, bb, acc[pt]);
+                    acc[pt] = mfma(al, bb, acc[pt]);
+                }
+            }
+            // lane (column n, half) holds S[p(v)][n], p(v) = 8 (v / 4) + 4 half + v % 4
+            const int n = nt * 32 + l32;
+            if (n < g.N) {
+                float *Sg = S + ((run.b * g.nch + run.c) * g.H + hh) * static_cast<int64_t>(g.P) * g.N;
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int p = pt * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+                        if (p < pcols) Sg[static_cast<int64_t>(pbase + p) * g.N + n] = acc[pt][v];
+                    }
+            }
+        }
+        if (pbase == 0 && tid == 0) ce[(run.b * g.nch + run.c) * g.H + hh] = cum_end;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 2. state pass: S[chunk] <- state entering the chunk; h_last <- final state
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void ssd_pass_kernel(float *__restrict__ S,
+                                                       const float *__restrict__ ce,
+                                                       float *__restrict__ h_last, Geom g,
+                                                       int blocks_per_head) {
+    const int64_t PN = static_cast<int64_t>(g.P) * g.N;
+    const int64_t bh = blockIdx.x / blocks_per_head;         // batch * H + head
+    const int64_t e = static_cast<int64_t>(blockIdx.x % blocks_per_head) * 256 + threadIdx.x;
+    if (e >= PN) return;
+    const int64_t b = bh / g.H, hh = bh % g.H;
+    float h = 0.0f;
+    constexpr int U = 4;    // chunks whose states are loaded ahead of the chain
+    int c = 0;
+    for (; c + U <= g.nch; c += U) {
+        float s[U], a[U];
+        int64_t idx[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t bc = (b * g.nch + c + k) * g.H + hh;
+            idx[k] = bc * PN + e;
+            s[k] = S[idx[k]];
+            a[k] = fast_exp2(ce[bc]);
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            S[idx[k]] = h;
+            h = fmaf(a[k], h, s[k]);
+        }
+    }
+    for (; c < g.nch; ++c) {
+        const int64_t bc = (b * g.nch + c) * g.H + hh;
+        const float s = S[bc * PN + e];
+        S[bc * PN + e] = h;
+        h = fmaf(fast_exp2(ce[bc]), h, s);
+    }
+    if (h_last) h_last[bh * PN + e] = h;
+}
+
+// ---------------------------------------------------------------------------
+// 3. outputs
+// ---------------------------------------------------------------------------
+template <int Q, int NP>
+struct __align__(16) OutSmem {
+    static constexpr int BP = NP + 8;    // B row pitch (elements)
+    static constexpr int XP = Q + 8;     // x^T row pitch
+    static constexpr int HP = NP + 8;    // h_in row pitch
+    uint16_t B[Q * BP];                  // B of the chunk, exact bf16
+    uint16_t XT[kPG * XP];               // x^T, exact bf16
+    uint16_t Hh[kPG * HP], Hl[kPG * HP]; // state entering the chunk, bf16 parts
+    float cum[Q], dl[Q];
+    float fs[Q];   // 2^(cum at the end of s's 32-step block - cum_s) dl_s
+    float wsum[4];
+};
+
+// h_in of one item prefetched into registers: unit u covers row p, columns
+// n2, n2 + 1 of the 64 x NP tile.
+template <int NP>
+struct HRegs {
+    static constexpr int U = kPG * (NP / 2) / 256;
+    float2 v[U];
 };
 
 template <int Q, int NP>
-__global__ __launch_bounds__(kThreads) void ssd_chunked_kernel(
+__device__ __forceinline__ void load_h(HRegs<NP> &r, const float *Hin, const Geom &g, const Run &run,
+                                       int item) {
+    const int tid = threadIdx.x;
+    const int hh = run.h0 + item / g.npg, pbase = (item % g.npg) * kPG;
+    const int pcols = g.P - pbase;
+    const float *Hg = Hin + ((run.b * g.nch + run.c) * g.H + hh) * static_cast<int64_t>(g.P) * g.N;
+#pragma unroll
+    for (int k = 0; k < HRegs<NP>::U; ++k) {
+        const int u = tid + 256 * k;
+        const int p = u / (NP / 2), n2 = (u % (NP / 2)) * 2;
+        const bool okp = p < pcols;
+        const int64_t base = static_cast<int64_t>(pbase + (okp ? p : 0)) * g.N;
+        const float h0 = Hg[base + (n2 < g.N ? n2 : 0)];
+        const float h1 = Hg[base + (n2 + 1 < g.N ? n2 + 1 : 0)];
+        r.v[k] = make_float2(okp && n2 < g.N ? h0 : 0.0f, okp && n2 + 1 < g.N ? h1 : 0.0f);
+    }
+}
+
+template <int Q, int NP>
+__global__ __launch_bounds__(256) void ssd_output_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt,
     const float *__restrict__ dt_bias, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm,
-    const float *__restrict__ Dskip, uint16_t *__restrict__ y,
-    float *__restrict__ h_last, int64_t L, int H, int P, int N, int G, int ptiles, bool vec,
-    bool vecx) {
-    // vec: B and C rows start 16-byte aligned (N % 8 == 0 and aligned bases);
-    // vecx: the same for x (P % 8 == 0 and an aligned base)
-    using S = Smem<Q, NP>;
-    constexpr int NT = Q / 32;          // 32-step time blocks per chunk
+    const float *__restrict__ Dskip, const float *__restrict__ Hin, uint16_t *__restrict__ y,
+    Geom g, int runs_per_chunk, int heads_per_run, bool vecB, bool vecX) {
+    using Sm = OutSmem<Q, NP>;
+    constexpr int BP = Sm::BP, XP = Sm::XP, HP = Sm::HP;
+    constexpr int NT = Q / 32;          // 32-step blocks per chunk
     constexpr int KN = NP / 16;         // K steps over the state index
-    constexpr int KQ = Q / 16;          // K steps over a chunk
-    __shared__ S sm;
-
+    __shared__ Sm sm;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int l32 = lane & 31;
-    const int half = lane >> 5;
-    const int pt = blockIdx.x % ptiles;
-    const int hh = (blockIdx.x / ptiles) % H;
-    const int64_t b = blockIdx.x / (static_cast<int64_t>(ptiles) * H);
-    const int g = hh / (H / G);
-    const int p0 = pt * kPt;
-    const float A2 = A[hh] * kLog2e;
-    const float bias = dt_bias ? dt_bias[hh] : 0.0f;
-    const float skip = Dskip ? Dskip[hh] : 0.0f;
-    const int64_t rowBC = static_cast<int64_t>(G) * N;   // stride of B/C between steps
-    const int64_t rowX = static_cast<int64_t>(H) * P;    // stride of x/y between steps
-    const uint16_t *Bg = Bm + (b * L * G + g) * N;
-    const uint16_t *Cg = Cm + (b * L * G + g) * N;
-    const uint16_t *xg = x + b * L * rowX + static_cast<int64_t>(hh) * P + p0;
-    uint16_t *yg = y + b * L * rowX + static_cast<int64_t>(hh) * P + p0;
-    const uint16_t *dtg = dt + b * L * H + hh;
+    // wave index as a scalar, so control flow that depends on it stays uniform
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+    const Run run = decode_run(g, runs_per_chunk, heads_per_run);
+    const int64_t t0 = static_cast<int64_t>(run.c) * Q;
+    const int64_t rowX = static_cast<int64_t>(g.H) * g.P;
+    const int64_t rowBC = static_cast<int64_t>(g.G) * g.N;
+    const uint16_t *Bg = Bm + run.b * g.L * rowBC + static_cast<int64_t>(run.grp) * g.N;
+    const uint16_t *Cg = Cm + run.b * g.L * rowBC + static_cast<int64_t>(run.grp) * g.N;
 
-    // State h[p][n] for p = p(v), n = 32 * wave + l32, in the 32x32 result
-    // layout: p(v) = 8 (v / 4) + 4 half + v % 4.
-    f16x hst;
+    XRegs<Q> xr;
+    load_x<Q>(xr, x, dt, g, run, 0, vecX);
+    // B of the chunk (rows s), shared by every head of the run
+    for (int u = tid; u < Q * (NP / 8); u += 256) {
+        const int s = u / (NP / 8), n8 = (u % (NP / 8)) * 8;
+        *reinterpret_cast<uint4 *>(&sm.B[s * BP + n8]) = load_row8(Bg, t0 + s, n8, g.L, g.N, rowBC, vecB);
+    }
+    // Each wave owns the 32-step blocks tb = wave and NT-1-wave (balanced
+    // causal work); with fewer than 8 blocks only the first NT/2 waves work.
+    // C_t fragments of those blocks: row t, state indices 16 jn + 8 half ...
+    const bool active = 2 * wave < NT;
+    bf8 cf[2][KN];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) hst[v] = 0.0f;
-    const int nS = 32 * wave + l32;      // this lane's state column
-    for (int i = tid; i < kPt * S::HP; i += kThreads) { sm.Hh[i] = 0; sm.Hl[i] = 0; }
+    for (int which = 0; which < 2; ++which) {
+        const int tb = which == 0 ? wave : NT - 1 - wave;
+#pragma unroll
+        for (int jn = 0; jn < KN; ++jn)
+            cf[which][jn] = __builtin_bit_cast(
+                bf8, load_row8(Cg, t0 + (active ? tb : 0) * 32 + l32, 16 * jn + 8 * half, g.L, g.N, rowBC, vecB));
+    }
 
-    const int64_t nchunks = (L + Q - 1) / Q;
-    for (int64_t c = 0; c < nchunks; ++c) {
-        const int64_t t0 = c * Q;
-        // ---- stage B (Q x NP) and x (Q x 32, transposed); dl and its scan ---
-        for (int u = tid; u < Q * (NP / 8); u += kThreads) {
-            const int s = u / (NP / 8), n8 = (u % (NP / 8)) * 8;
-            *reinterpret_cast<uint4 *>(&sm.B[s * S::BP + n8]) = load_row8(Bg, t0 + s, n8, L, N, rowBC, vec);
-        }
-        // x: units of (two consecutive steps, 8 head-dim columns); each unit
-        // is written transposed as 8 dwords (step pair packed) -- no
-        // sub-dword LDS writes.  Q / 128 units per thread (one half of the
-        // threads when Q = 64).
-        constexpr int XU = (2 * Q + kThreads - 1) / kThreads;
-        float xr[XU][2][8];
-#pragma unroll
-        for (int k = 0; k < XU; ++k) {
-            const int u = tid + k * kThreads;
-            if (u < 2 * Q) {
-                const int s2 = 2 * (u / (kPt / 8)), pg = (u % (kPt / 8)) * 8;
-                const uint4 v0 = load_row8(xg, t0 + s2, pg, L, P - p0, rowX, vecx);
-                const uint4 v1 = load_row8(xg, t0 + s2 + 1, pg, L, P - p0, rowX, vecx);
-                uint16_t e0[8], e1[8];
-                __builtin_memcpy(e0, &v0, 16);
-                __builtin_memcpy(e1, &v1, 16);
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    xr[k][0][r] = __uint_as_float(static_cast<uint32_t>(e0[r]) << 16);
-                    xr[k][1][r] = __uint_as_float(static_cast<uint32_t>(e1[r]) << 16);
-                    *reinterpret_cast<uint32_t *>(&sm.X[(pg + r) * S::XP + s2]) =
-                        static_cast<uint32_t>(e0[r]) | (static_cast<uint32_t>(e1[r]) << 16);
-                }
-            }
-        }
-        // dl and the log decay of step tid (threads >= Q idle here)
-        float ell = 0.0f;
-        if (tid < Q) {
-            const bool okt = t0 + tid < L;
-            const float dr = Ld<uint16_t>::f(dtg, okt ? (t0 + tid) * H : 0);
-            const float dlv = okt ? softplus(dr + bias) : 0.0f;
-            sm.dl[tid] = dlv;
-            ell = dlv * A2;                          // log2 of the step decay
-        }
-        // inclusive scan of ell over the chunk: within waves, then across
-        float sc = ell;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float o = __shfl_up(sc, off, 64);
-            if (lane >= off) sc += o;
-        }
-        if (lane == 63) sm.wsum[wave] = sc;
-        __syncthreads();
-        if (tid < Q) {
-            float base = 0.0f;
-            for (int w2 = 0; w2 < wave; ++w2) base += sm.wsum[w2];
-            sm.cum[tid] = sc + base;
-        }
-        __syncthreads();
-
-        const float cum_end = sm.cum[Q - 1];
-        // ---- per-step factors of the decay, x * w as bf16 high / low --------
-        if (tid < Q) {
-            const float cb = sm.cum[(tid | 31)];
-            sm.fs[tid] = fast_exp2(cb - sm.cum[tid]) * sm.dl[tid];
-        }
-#pragma unroll
-        for (int k = 0; k < XU; ++k) {
-            const int u = tid + k * kThreads;
-            if (u < 2 * Q) {
-                const int s2 = 2 * (u / (kPt / 8)), pg = (u % (kPt / 8)) * 8;
-                // w_s = 2^(cum_end - cum_s) dl_s: the weight of step s in the
-                // state at the chunk end
-                const float w0 = fast_exp2(cum_end - sm.cum[s2]) * sm.dl[s2];
-                const float w1 = fast_exp2(cum_end - sm.cum[s2 + 1]) * sm.dl[s2 + 1];
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const float a0 = xr[k][0][r] * w0, a1 = xr[k][1][r] * w1;
-                    const uint32_t hi = pack2(a0, a1);
-                    const uint32_t lo = pack2(a0 - __uint_as_float(hi << 16),
-                                              a1 - __uint_as_float(hi & 0xffff0000u));
-                    *reinterpret_cast<uint32_t *>(&sm.Xwh[(pg + r) * S::WP + s2]) = hi;
-                    *reinterpret_cast<uint32_t *>(&sm.Xwl[(pg + r) * S::WP + s2]) = lo;
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- output rows: time blocks tb = wave and NT - 1 - wave -----------
-        // (with NT < 8 blocks, only waves 0 .. NT/2 - 1 have rows)
 #pragma unroll 1
-        for (int which = 0; which < 2 && 2 * wave < NT; ++which) {
-            const int tb = which == 0 ? wave : NT - 1 - wave;
-            const int tl = tb * 32 + l32;            // this lane's target step (in chunk)
-            // C fragments of the 32 target steps: row tl, n = 16 j + 8 half + r
-            bf8 cf[KN];
+    for (int item = 0; item < run.items; ++item) {
+        const int hh = run.h0 + item / g.npg, pbase = (item % g.npg) * kPG;
+        const int pcols = g.P - pbase;
+        const float skip = Dskip ? Dskip[hh] : 0.0f;
+        const uint16_t *xg = x + run.b * g.L * rowX + static_cast<int64_t>(hh) * g.P + pbase;
+        uint16_t *yg = y + run.b * g.L * rowX + static_cast<int64_t>(hh) * g.P + pbase;
+        __syncthreads();   // the previous item's LDS reads are done
+        // state entering the chunk; its loads overlap the decay scan
+        HRegs<NP> hr;
+        load_h<Q, NP>(hr, Hin, g, run, item);
+        chunk_decay_from<Q>(xr.dt, t0, g.L, A[hh] * kLog2e, dt_bias ? dt_bias[hh] : 0.0f, sm.cum,
+                            sm.dl, sm.wsum);
+        if (tid < Q) sm.fs[tid] = fast_exp2(sm.cum[tid | 31] - sm.cum[tid]) * sm.dl[tid];
+        // x^T as step pairs; h_in split into bf16 parts
 #pragma unroll
-            for (int jn = 0; jn < KN; ++jn) {
-                cf[jn] = __builtin_bit_cast(bf8, load_row8(Cg, t0 + tl, 16 * jn + 8 * half, L, N, rowBC, vec));
+        for (int k = 0; k < XRegs<Q>::U; ++k) {
+            const int u = tid + 256 * k;
+            const int s2 = 2 * (u / (kPG / 8)), p8 = (u % (kPG / 8)) * 8;
+            const uint4 v0 = xr.v[k][0], v1 = xr.v[k][1];
+            const uint32_t a[4] = {v0.x, v0.y, v0.z, v0.w}, e[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                *reinterpret_cast<uint32_t *>(&sm.XT[(p8 + 2 * r) * XP + s2]) = (a[r] & 0xffffu) | (e[r] << 16);
+                *reinterpret_cast<uint32_t *>(&sm.XT[(p8 + 2 * r + 1) * XP + s2]) = (a[r] >> 16) | (e[r] & 0xffff0000u);
             }
+        }
+#pragma unroll
+        for (int k = 0; k < HRegs<NP>::U; ++k) {
+            const int u = tid + 256 * k;
+            const int p = u / (NP / 2), n2 = (u % (NP / 2)) * 2;
+            uint32_t hi, lo;
+            split2(hr.v[k].x, hr.v[k].y, hi, lo);
+            *reinterpret_cast<uint32_t *>(&sm.Hh[p * HP + n2]) = hi;
+            *reinterpret_cast<uint32_t *>(&sm.Hl[p * HP + n2]) = lo;
+        }
+        __syncthreads();
+        // next item's x (the last item re-reads its own; unused)
+        load_x<Q>(xr, x, dt, g, run, item + 1 < run.items ? item + 1 : item, vecX);
+        if (!active) continue;
+
+        // Output tiles Y^T[p][t]: lane (column t, half) holds rows
+        // p(v) = 8 (v / 4) + 4 half + v % 4.
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            const int tb = which == 0 ? wave : NT - 1 - wave;
+            const int tl = tb * 32 + l32;            // this lane's step within the chunk
             const float cum_t = sm.cum[tl];
-            f16x yd;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) yd[v] = 0.0f;
+            f16x yd[2] = {zero16(), zero16()};
+#pragma unroll 1
             for (int sb = 0; sb <= tb; ++sb) {
-                // G'[s][t] = B_s . C_t for s in block sb, t in block tb
-                f16x gacc;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) gacc[v] = 0.0f;
+                // G'[s][t] = B_s . C_t: A operand rows s of B
+                f16x gacc = zero16();
 #pragma unroll
                 for (int jn = 0; jn < KN; ++jn) {
-                    const bf8 a = *reinterpret_cast<const bf8 *>(
-                        &sm.B[(sb * 32 + l32) * S::BP + 16 * jn + 8 * half]);
-                    gacc = mfma(a, cf[jn], gacc);
+                    const bf8 ab = *reinterpret_cast<const bf8 *>(&sm.B[(sb * 32 + l32) * BP + 16 * jn + 8 * half]);
+                    gacc = mfma(ab, cf[which][jn], gacc);
                 }
-                // M[t][s] = G'[s][t] 2^(cum_t - cum_s) dl_s for s <= t, else 0.
-                // This lane holds column t = tl and rows s(v) = 8(v/4) + 4 half + v%4.
-                // Off the diagonal block every s < t and the decay factors as
-                // 2^(cum_t - cb) * fs[s], cb the cum at the end of block sb:
-                // both factors are <= 1 (and <= dl_s), so nothing overflows.
-                // On the diagonal block the exponent is formed directly and
-                // steps s > t are masked out by selection.
+                // M[t][s] = G'[s][t] 2^(cum_t - cum_s) dl_s for s <= t (else 0),
+                // at s(v) = 32 sb + 8 (v / 4) + 4 half + v % 4.  Off the diagonal
+                // block the decay factors as 2^(cum_t - cb) fs[s], cb the cum at
+                // the end of block sb, both factors <= 1.
                 float mval[16];
                 if (sb < tb) {
                     const float et = fast_exp2(cum_t - sm.cum[sb * 32 + 31]);
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int sl = sb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
-                        mval[v] = gacc[v] * (et * sm.fs[sl]);
-                    }
+                    for (int v = 0; v < 16; ++v)
+                        mval[v] = gacc[v] * (et * sm.fs[sb * 32 + 8 * (v / 4) + 4 * half + (v % 4)]);
                 } else {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
@@ -299,113 +496,129 @@ __global__ __launch_bounds__(kThreads) void ssd_chunked_kernel(
                         mval[v] = sl <= tl ? mv : 0.0f;
                     }
                 }
-                bf8 mh[2], ml[2];
+                uint32_t mh[8], ml[8];
 #pragma unroll
-                for (int v = 0; v < 16; v += 2) {
-                    const uint32_t hi = pack2(mval[v], mval[v + 1]);
-                    const uint32_t lo = pack2(mval[v] - __uint_as_float(hi << 16),
-                                              mval[v + 1] - __uint_as_float(hi & 0xffff0000u));
-                    mh[v / 8][v % 8] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hi));
-                    mh[v / 8][v % 8 + 1] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(hi >> 16));
-                    ml[v / 8][v % 8] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lo));
-                    ml[v / 8][v % 8 + 1] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(lo >> 16));
-                }
-                // Y_diag[t][p] += sum_s M[t][s] x[s][p], K order s(v) as above:
-                // operand lane (p = l32, half) reads x[s(v)][p] for the same v.
+                for (int v = 0; v < 16; v += 2) split2(mval[v], mval[v + 1], mh[v / 2], ml[v / 2]);
+                // Y^T[p][t] += sum_s x^T[p][s] M[t][s], K slot order s(v) as above:
+                // A operand row p reads x at s(8 kk + 0..3) and s(8 kk + 4..7)
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const int sA = sb * 32 + 16 * kk + 4 * half;   // s(8kk + 0..3)
-                    const uint16_t *xp = &sm.X[l32 * S::XP];
-                    uint2 lo4 = *reinterpret_cast<const uint2 *>(xp + sA);
-                    uint2 hi4 = *reinterpret_cast<const uint2 *>(xp + sA + 8);
-                    const uint4 xv4 = make_uint4(lo4.x, lo4.y, hi4.x, hi4.y);
-                    const bf8 xb = __builtin_bit_cast(bf8, xv4);
-                    yd = mfma(mh[kk], xb, yd);
-                    yd = mfma(ml[kk], xb, yd);
+                    const bf8 bh = __builtin_bit_cast(bf8, make_uint4(mh[4 * kk], mh[4 * kk + 1], mh[4 * kk + 2], mh[4 * kk + 3]));
+                    const bf8 bl = __builtin_bit_cast(bf8, make_uint4(ml[4 * kk], ml[4 * kk + 1], ml[4 * kk + 2], ml[4 * kk + 3]));
+                    const int sA = sb * 32 + 16 * kk + 4 * half;
+#pragma unroll
+                    for (int pt = 0; pt < 2; ++pt) {
+                        const uint16_t *xp = &sm.XT[(pt * 32 + l32) * XP];
+                        const uint2 lo4 = *reinterpret_cast<const uint2 *>(xp + sA);
+                        const uint2 hi4 = *reinterpret_cast<const uint2 *>(xp + sA + 8);
+                        const bf8 xa = __builtin_bit_cast(bf8, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+                        yd[pt] = mfma(xa, bh, yd[pt]);
+                        yd[pt] = mfma(xa, bl, yd[pt]);
+                    }
                 }
             }
-            // Y_off[t][p] = sum_n C_t[n] h_prev[p][n]
-            f16x yo;
+            // Y_off^T[p][t] = sum_n h_in[p][n] C_t[n]; y = Y_diag + 2^cum_t Y_off + D x
+            const float et = fast_exp2(cum_t);
+            const int64_t t = t0 + tl;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) yo[v] = 0.0f;
+            for (int pt = 0; pt < 2; ++pt) {
+                if (pt * 32 >= pcols) break;
+                f16x yo = zero16();
 #pragma unroll
-            for (int jn = 0; jn < KN; ++jn) {
-                const int n8 = 16 * jn + 8 * half;
-                const bf8 bh = *reinterpret_cast<const bf8 *>(&sm.Hh[l32 * S::HP + n8]);
-                const bf8 bl = *reinterpret_cast<const bf8 *>(&sm.Hl[l32 * S::HP + n8]);
-                yo = mfma(cf[jn], bh, yo);
-                yo = mfma(cf[jn], bl, yo);
+                for (int jn = 0; jn < KN; ++jn) {
+                    const int n8 = 16 * jn + 8 * half;
+                    const bf8 ah = *reinterpret_cast<const bf8 *>(&sm.Hh[(pt * 32 + l32) * HP + n8]);
+                    const bf8 al = *reinterpret_cast<const bf8 *>(&sm.Hl[(pt * 32 + l32) * HP + n8]);
+                    yo = mfma(ah, cf[which][jn], yo);
+                    yo = mfma(al, cf[which][jn], yo);
+                }
+                if (t < g.L) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        // four consecutive p = pt*32 + 8 q4 + 4 half + 0..3; x
+                        // from the staged x^T
+                        const int p = pt * 32 + 8 * q4 + 4 * half;
+                        float yv[4];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const float xs = bf16_to_f32(sm.XT[(p + k) * XP + tl]);
+                            yv[k] = fmaf(skip, xs, fmaf(et, yo[4 * q4 + k], yd[pt][4 * q4 + k]));
+                        }
+                        if (vecX && p + 4 <= pcols) {
+                            *reinterpret_cast<uint2 *>(yg + t * rowX + p) =
+                                make_uint2(pack2(yv[0], yv[1]), pack2(yv[2], yv[3]));
+                        } else {
+#pragma unroll
+                            for (int k = 0; k < 4; ++k)
+                                if (p + k < pcols) yg[t * rowX + p + k] = f32_to_bf16(yv[k]);
+                        }
+                    }
+                }
             }
-            // y[t][p], this lane: p = l32, t(v) = 8(v/4) + 4 half + v%4
-            const int p = p0 + l32;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int tv = tb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
-                const float xs = __uint_as_float(static_cast<uint32_t>(sm.X[l32 * S::XP + tv]) << 16);
-                const float yv = yd[v] + fast_exp2(sm.cum[tv]) * yo[v] + skip * xs;
-                if (t0 + tv < L && p < P) yg[(t0 + tv) * rowX + l32] = f32_to_bf16(yv);
-            }
-        }
-
-        // ---- chunk state for state columns n = 32 wave .. 32 wave + 31 -------
-        f16x sacc;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sacc[v] = 0.0f;
-        if (32 * wave < NP) {
-#pragma unroll 4
-            for (int kq = 0; kq < KQ; ++kq) {
-                const int s8 = 16 * kq + 8 * half;
-                const bf8 ah = *reinterpret_cast<const bf8 *>(&sm.Xwh[l32 * S::WP + s8]);
-                const bf8 al = *reinterpret_cast<const bf8 *>(&sm.Xwl[l32 * S::WP + s8]);
-                bf8 bb;
-#pragma unroll
-                for (int r = 0; r < 8; ++r)
-                    bb[r] = __builtin_bit_cast(__bf16, sm.B[(s8 + r) * S::BP + nS]);
-                sacc = mfma(ah, bb, sacc);
-                sacc = mfma(al, bb, sacc);
-            }
-        }
-        __syncthreads();   // every wave is done with B, x, x*w and h_prev
-
-        // ---- h = 2^(cum_end) h + S; publish h_prev for the next chunk -------
-        const float decay = fast_exp2(cum_end);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            hst[v] = fmaf(decay, hst[v], sacc[v]);
-            const int pv = 8 * (v / 4) + 4 * half + (v % 4);
-            if (32 * wave < NP) {
-                __bf16 hi, lo;
-                split(hst[v], hi, lo);
-                sm.Hh[pv * S::HP + nS] = bf16_bits(hi);
-                sm.Hl[pv * S::HP + nS] = bf16_bits(lo);
-            }
-        }
-        __syncthreads();
-    }
-
-    if (h_last && 32 * wave < NP && nS < N) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int pv = p0 + 8 * (v / 4) + 4 * half + (v % 4);
-            if (pv < P) h_last[((b * H + hh) * static_cast<int64_t>(P) + pv) * N + nS] = hst[v];
         }
     }
 }
 
+// Heads per run: runs never straddle a B / C group, and the grid keeps at
+// least two runs per compute unit when the problem allows.
+int heads_per_run(const SSDArgs &a, int64_t nch) {
+    const int hpg = static_cast<int>(a.H / a.G);
+    int best = 1;
+    for (int d = 1; d <= hpg; ++d) {
+        if (hpg % d) continue;
+        if (a.batch * nch * a.G * (hpg / d) >= 512) best = d;
+    }
+    return best;
+}
+
 template <int Q, int NP>
 hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
-    const int ptiles = static_cast<int>((a.P + kPt - 1) / kPt);
-    const int64_t grid = a.batch * a.H * ptiles;
+    Geom g;
+    g.L = a.L;
+    g.H = static_cast<int>(a.H);
+    g.P = static_cast<int>(a.P);
+    g.N = static_cast<int>(a.N);
+    g.G = static_cast<int>(a.G);
+    g.nch = static_cast<int>((a.L + Q - 1) / Q);
+    g.npg = static_cast<int>((a.P + kPG - 1) / kPG);
     auto aligned = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-    const bool vec = a.N % 8 == 0 && aligned(a.B) && aligned(a.C);
-    const bool vecx = a.P % 8 == 0 && aligned(a.x);
-    hipLaunchKernelGGL((ssd_chunked_kernel<Q, NP>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads),
-                       0, stream, static_cast<const uint16_t *>(a.x),
-                       static_cast<const uint16_t *>(a.dt), a.dt_bias, a.A,
-                       static_cast<const uint16_t *>(a.B), static_cast<const uint16_t *>(a.C), a.D,
-                       static_cast<uint16_t *>(a.y), a.h_last, a.L, static_cast<int>(a.H),
-                       static_cast<int>(a.P), static_cast<int>(a.N), static_cast<int>(a.G), ptiles, vec, vecx);
-    return hipGetLastError();
+    const bool vecB = a.N % 8 == 0 && aligned(a.B) && aligned(a.C);
+    const bool vecX = a.P % 8 == 0 && aligned(a.x) && aligned(a.y);
+    const int hpr = heads_per_run(a, g.nch);
+    const int rpc = static_cast<int>((a.H + hpr - 1) / hpr);
+
+    const int64_t chunks = a.batch * g.nch * a.H;
+    const int64_t PN = a.P * a.N;
+    const size_t s_bytes = static_cast<size_t>(chunks * PN) * sizeof(float);
+    const size_t ce_bytes = static_cast<size_t>(chunks) * sizeof(float);
+    void *mem = nullptr;
+    hipError_t e = hipMallocAsync(&mem, s_bytes + ce_bytes, stream);
+    if (e != hipSuccess) return e;
+    float *S = static_cast<float *>(mem);
+    float *ce = reinterpret_cast<float *>(static_cast<char *>(mem) + s_bytes);
+
+    const auto *x = static_cast<const uint16_t *>(a.x);
+    const auto *dt = static_cast<const uint16_t *>(a.dt);
+    const auto *B = static_cast<const uint16_t *>(a.B);
+    const auto *C = static_cast<const uint16_t *>(a.C);
+    const int64_t grid = a.batch * g.nch * rpc;
+    hipLaunchKernelGGL((ssd_state_kernel<Q, NP>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
+                       stream, x, dt, a.dt_bias, a.A, B, S, ce, g, rpc, hpr, vecB, vecX);
+    e = hipGetLastError();
+    if (e == hipSuccess) {
+        const int bph = static_cast<int>((PN + 255) / 256);
+        hipLaunchKernelGGL(ssd_pass_kernel, dim3(static_cast<uint32_t>(a.batch * a.H * bph)),
+                           dim3(256), 0, stream, S, ce, a.h_last, g, bph);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL((ssd_output_kernel<Q, NP>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
+                           stream, x, dt, a.dt_bias, a.A, B, C, a.D, S, static_cast<uint16_t *>(a.y),
+                           g, rpc, hpr, vecB, vecX);
+        e = hipGetLastError();
+    }
+    const hipError_t ef = hipFreeAsync(mem, stream);
+    return e != hipSuccess ? e : ef;
 }
 
 template <int Q>
@@ -419,9 +632,11 @@ hipError_t launch_by_n(const SSDArgs &a, hipStream_t stream) {
 }  // namespace
 
 bool ssd_chunked_supported(const SSDArgs &a) {
+    const int64_t nch = (a.L + a.chunk - 1) / (a.chunk > 0 ? a.chunk : 1);
     return a.io == IO_BF16 && a.N >= 1 && a.N <= 128 && a.P >= 1 &&
            (a.chunk == 64 || a.chunk == 128 || a.chunk == 256) &&
-           a.batch * a.H * ((a.P + kPt - 1) / kPt) < (int64_t(1) << 31);
+           a.batch * nch * a.H * ((a.P + kPG - 1) / kPG) < (int64_t(1) << 31) &&
+           nch < (int64_t(1) << 30);
 }
 
 hipError_t launch_ssd_chunked(const SSDArgs &a, hipStream_t stream) {
