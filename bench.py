@@ -22,6 +22,8 @@ Prints one JSON line:
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--variant auto|rowserial|chunked|...] [--no-cpu]
                        [--copy-probe-mib M]
+       python bench.py --workload NAME --steps K --warmup W --copy-probe-mib M
+                       --counters FETCH_CSV WRITE_CSV      (summary only)
 """
 from __future__ import annotations
 
@@ -101,6 +103,58 @@ def load_traffic(workload: str, sha: str):
     if c.get("source_sha") != sha:
         return None
     return c.get("hbm_bytes_per_launch")
+
+
+def summarize_counters(workload: str, fetch_csv: str, write_csv: str, probe_mib: int,
+                       steps: int) -> dict:
+    """HBM bytes per step from two rocprofv3 --pmc runs of this bench (one
+    with FETCH_SIZE, one with WRITE_SIZE, both run with --copy-probe-mib).
+
+    Each counter is scaled by the copy probe's known traffic (probe_mib MiB
+    read and written) divided by what the same counter reads, per dispatch,
+    for the copy kernel.  The library's kernels (mssm namespace) are summed
+    over all their dispatches and divided by the number of steps the run
+    made (warmup + timed).
+    """
+    import csv
+
+    def read(path, counter):
+        lib, copy = {}, {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                name, d, v = r["Kernel_Name"], r["Dispatch_Id"], float(r["Counter_Value"])
+                if "mssm::" in name:
+                    key = name.replace("(anonymous namespace)::", "").split("(")[0]
+                    key = key.replace("void ", "")
+                    lib.setdefault(key, {}).setdefault(d, 0.0)
+                    lib[key][d] += v
+                elif "copyBuffer" in name:
+                    copy[d] = copy.get(d, 0.0) + v
+        # the probe's three copies are the largest copy dispatches (torch's
+        # uploads of the small operands use the same copy kernel)
+        probe = sorted(copy.values())[-3:]
+        return lib, probe
+
+    out = {"workload": workload, "source_sha": kernel_source_sha(),
+           "copy_probe_mib": probe_mib, "steps": steps, "kernels": {}, "scale": {}}
+    per_step = 0.0
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        lib, copy = read(path, counter)
+        if not copy:
+            raise SystemExit("no copy-probe dispatches in %s" % path)
+        copy_kib = sum(copy) / len(copy)
+        scale = probe_mib * 1024.0 / copy_kib
+        out["scale"][counter] = scale
+        out["copy_%s_kib" % counter] = copy_kib
+        for name, ds in lib.items():
+            k = out["kernels"].setdefault(name, {})
+            k[counter + "_kib_per_dispatch"] = sum(ds.values()) / len(ds)
+            k["dispatches"] = len(ds)
+            per_step += sum(ds.values()) * 1024.0 * scale / steps
+    out["hbm_bytes_per_launch"] = per_step
+    return out
 
 
 def g1(a, r):
@@ -307,7 +361,24 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many MiB three times "
                          "(a plain kernel of known traffic for calibrating HBM byte counters)")
+    ap.add_argument("--counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: summarize the counter_collection.csv files of two "
+                         "rocprofv3 --pmc runs of this bench (FETCH_SIZE, then WRITE_SIZE; "
+                         "same --workload/--steps/--warmup/--copy-probe-mib) into "
+                         "profiles/counters_<workload>.json")
     args = ap.parse_args()
+
+    if args.counters:
+        if args.copy_probe_mib <= 0:
+            raise SystemExit("--counters needs the --copy-probe-mib the runs used")
+        res = summarize_counters(args.workload, args.counters[0], args.counters[1],
+                                 args.copy_probe_mib, args.steps + args.warmup)
+        path = os.path.join(ROOT, "profiles", "counters_%s.json" % args.workload)
+        with open(path, "w") as f:
+            json.dump(res, f, indent=1)
+            f.write("\n")
+        print(json.dumps(res))
+        return
 
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
