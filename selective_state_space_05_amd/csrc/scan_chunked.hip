@@ -53,17 +53,13 @@ hipError_t launch_typed(const ScanArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Four waves with one state element per lane double the waves in flight,
-// which matters when the grid is small; two waves with two per lane write
-// half the partial sums.  Chosen by how many waves the two-wave form would
-// put on each of the chip's 1024 SIMDs.
+// Four waves with one state element per lane: the most waves in flight, and
+// the partial sums of a wave's four state rows are added in registers.
+// Larger N puts more state elements on each lane.
 template <typename T>
 hipError_t launch_by_n(const ScanArgs &a, hipStream_t stream) {
-    const int64_t groups = a.batch * ((a.dim + kCh - 1) / kCh);
-    const bool few = groups * 2 < 4 * 1024;
-    if (a.N <= 16 && few) return launch_typed<T, 4, 1>(a, stream);
     if (a.N <= 8) return launch_typed<T, 2, 1>(a, stream);
-    if (a.N <= 16) return launch_typed<T, 2, 2>(a, stream);
+    if (a.N <= 16) return launch_typed<T, 4, 1>(a, stream);
     if (a.N <= 32) return launch_typed<T, 2, 4>(a, stream);
     return launch_typed<T, 2, 8>(a, stream);
 }
@@ -89,7 +85,7 @@ bool scan_chunked_supported(const ScanArgs &a) {
 
 int64_t scan_chunked_waves(const ScanArgs &a) {
     const int64_t groups = a.batch * ((a.dim + kCh - 1) / kCh);
-    return groups * ((a.N <= 16 && groups * 2 < 4 * 1024) ? 4 : 2);
+    return groups * (a.N <= 16 && a.N > 8 ? 4 : 2);
 }
 
 hipError_t launch_scan_chunked(const ScanArgs &a, hipStream_t stream) {

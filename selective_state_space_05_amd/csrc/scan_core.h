@@ -115,8 +115,32 @@ template <int W>
 struct Smem {
     float dl[2][kCh * kPitch];
     float du[2][kCh * kPitch];
-    float p[4 * W * kCh * kPitch];
+    float p[W * kCh * kPitch];      // per wave: partial sums over its 4 state rows
 };
+
+// Sum of a value over the four 16-lane rows of a wave, for 32 values at
+// once (p[k] belongs to step k), with cross-row swaps instead of LDS:
+// v_permlane32_swap pairs rows (0, 2) and (1, 3) for steps k and k + 16,
+// v_permlane16_swap then pairs rows (0, 1) and (2, 3) for steps k and k + 8.
+// On return lane (row r, column j) holds in q[i] the four-row sum of step
+// 8 r + i for its column.
+__device__ __forceinline__ void rows_reduce(const float (&p)[32], float (&q)[8]) {
+    float z[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[k]), __float_as_uint(p[k + 16]),
+                                                        false, false);
+        // rows 0, 1: step k, rows {0, 2} / {1, 3}; rows 2, 3: step k + 16
+        z[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(z[k]), __float_as_uint(z[k + 8]),
+                                                        false, false);
+        // row 0: step k, row 1: k + 8, row 2: k + 16, row 3: k + 24
+        q[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+}
 
 // Per-thread view of one (batch, 16-channel group) problem slice.
 template <typename T, int W, int NPL, bool GATE, bool VEC>
@@ -287,9 +311,10 @@ struct Walker {
         __syncthreads();
 
         // ---- B: 32 steps of the recurrence for this lane ----------------------
+        float p[32];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            float dls[16], dus[16], p[16];
+            float dls[16], dus[16];
             const float4 *pdl = reinterpret_cast<const float4 *>(sm.dl[buf] + j * kPitch + 16 * q);
             const float4 *pdu = reinterpret_cast<const float4 *>(sm.du[buf] + j * kPitch + 16 * q);
 #pragma unroll
@@ -307,21 +332,25 @@ struct Walker {
             if (OUT) acc = g == 0 ? row_bcast<S>(cc[q][g]) * h[g]              \
                                   : fmaf(row_bcast<S>(cc[q][g]), h[g], acc);   \
         }                                                                      \
-        p[S] = acc;                                                            \
+        p[16 * q + S] = acc;                                                   \
     }
             MSSM_STEP(0) MSSM_STEP(1) MSSM_STEP(2) MSSM_STEP(3)
             MSSM_STEP(4) MSSM_STEP(5) MSSM_STEP(6) MSSM_STEP(7)
             MSSM_STEP(8) MSSM_STEP(9) MSSM_STEP(10) MSSM_STEP(11)
             MSSM_STEP(12) MSSM_STEP(13) MSSM_STEP(14) MSSM_STEP(15)
 #undef MSSM_STEP
-            if (OUT) {
-                float4 *dst = reinterpret_cast<float4 *>(sm.p + (prow * kCh + j) * kPitch + 16 * q);
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    dst[k] = make_float4(p[4 * k], p[4 * k + 1], p[4 * k + 2], p[4 * k + 3]);
-            }
         }
         if (!OUT) return;
+        {
+            // the wave's four state rows summed in registers; lane (row r,
+            // column j) stores steps 8 r .. 8 r + 7 of channel j
+            float qs[8];
+            rows_reduce(p, qs);
+            const int r = (threadIdx.x >> 4) & 3;
+            float4 *dst = reinterpret_cast<float4 *>(sm.p + ((threadIdx.x >> 6) * kCh + j) * kPitch + 8 * r);
+            dst[0] = make_float4(qs[0], qs[1], qs[2], qs[3]);
+            dst[1] = make_float4(qs[4], qs[5], qs[6], qs[7]);
+        }
         __syncthreads();
 
         // ---- C: reduce the partial sums, skip term, gate, store --------------
@@ -329,7 +358,7 @@ struct Walker {
 #pragma unroll
         for (int i = 0; i < OS; ++i) yv[i] = 0.0f;
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) {
+        for (int r = 0; r < W; ++r) {
             const float *src = sm.p + (r * kCh + oc) * kPitch + OS * ok;
 #pragma unroll
             for (int i = 0; i < OS; i += 2) {
