@@ -74,20 +74,24 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
 // Eight consecutive bf16 of row t starting at column c8 of a row-major slice
 // with row stride `stride`; zero past the last row or column.  Out-of-range
 // reads are redirected to element 0 (always valid) and discarded, so the
-// load needs no branch.  vec: rows 16-byte aligned and cols % 8 == 0.
-__device__ __forceinline__ uint4 load_row8(const uint16_t *base, int64_t t, int c8, int64_t rows,
-                                           int cols, int64_t stride, bool vec) {
+// load needs no branch.  VEC: rows 16-byte aligned and cols % 8 == 0.
+// Element offsets within a slice fit in 31 bits (checked by the launcher).
+template <bool VEC>
+__device__ __forceinline__ uint4 load_row8(const uint16_t *base, int t, int c8, int rows, int cols,
+                                           int stride) {
     const bool okt = t < rows;
-    if (vec) {
+    if (VEC) {
         const bool ok = okt && c8 < cols;
-        const uint4 v = *reinterpret_cast<const uint4 *>(base + (ok ? t * stride + c8 : 0));
+        const uint32_t i = ok ? static_cast<uint32_t>(t) * static_cast<uint32_t>(stride) + c8 : 0u;
+        const uint4 v = *reinterpret_cast<const uint4 *>(base + i);
         return ok ? v : make_uint4(0, 0, 0, 0);
     }
     uint16_t e[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         const bool ok = okt && c8 + r < cols;
-        const uint16_t w = base[ok ? t * stride + c8 + r : 0];
+        const uint32_t i = ok ? static_cast<uint32_t>(t) * static_cast<uint32_t>(stride) + c8 + r : 0u;
+        const uint16_t w = base[i];
         e[r] = ok ? w : 0;
     }
     uint4 v;
@@ -99,8 +103,7 @@ __device__ __forceinline__ float bits_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bits_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 struct Geom {
-    int64_t L;
-    int H, P, N, G, nch, npg;
+    int L, H, P, N, G, nch, npg;
 };
 
 // Work item of the state and output kernels: one (batch, chunk) and a run of
@@ -146,29 +149,29 @@ struct XRegs {
     float dt;
 };
 
-template <int Q>
+template <int Q, bool VEC>
 __device__ __forceinline__ void load_x(XRegs<Q> &r, const uint16_t *x, const uint16_t *dt,
-                                       const Geom &g, const Run &run, int item, bool vecX) {
+                                       const Geom &g, const Run &run, int item) {
     const int tid = threadIdx.x;
     const int hh = run.h0 + item / g.npg, pbase = (item % g.npg) * kPG;
-    const int64_t t0 = static_cast<int64_t>(run.c) * Q;
-    const int64_t rowX = static_cast<int64_t>(g.H) * g.P;
-    const uint16_t *xg = x + run.b * g.L * rowX + static_cast<int64_t>(hh) * g.P + pbase;
+    const int t0 = run.c * Q;
+    const int rowX = g.H * g.P;
+    const uint16_t *xg = x + run.b * g.L * static_cast<int64_t>(rowX) + hh * g.P + pbase;
 #pragma unroll
     for (int k = 0; k < XRegs<Q>::U; ++k) {
         const int u = tid + 256 * k;
         const int s2 = 2 * (u / (kPG / 8)), p8 = (u % (kPG / 8)) * 8;
-        r.v[k][0] = load_row8(xg, t0 + s2, p8, g.L, g.P - pbase, rowX, vecX);
-        r.v[k][1] = load_row8(xg, t0 + s2 + 1, p8, g.L, g.P - pbase, rowX, vecX);
+        r.v[k][0] = load_row8<VEC>(xg, t0 + s2, p8, g.L, g.P - pbase, rowX);
+        r.v[k][1] = load_row8<VEC>(xg, t0 + s2 + 1, p8, g.L, g.P - pbase, rowX);
     }
-    const int64_t t = t0 + (tid < Q ? tid : 0);
-    r.dt = bf16_to_f32(dt[(run.b * g.L + (t < g.L ? t : g.L - 1)) * g.H + hh]);
+    const int t = t0 + (tid < Q ? tid : 0);
+    r.dt = bf16_to_f32(dt[run.b * g.L * static_cast<int64_t>(g.H) + (t < g.L ? t : g.L - 1) * g.H + hh]);
 }
 
 // dl and the inclusive sum of the log2 decay over the chunk's Q steps from a
 // prefetched raw dt value (thread s < Q holds step s).  Ends with a barrier.
 template <int Q>
-__device__ void chunk_decay_from(float dr, int64_t t0, int64_t L, float A2, float bias,
+__device__ void chunk_decay_from(float dr, int t0, int L, float A2, float bias,
                                  float *s_cum, float *s_dl, float *s_wsum) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -195,12 +198,12 @@ __device__ void chunk_decay_from(float dr, int64_t t0, int64_t L, float A2, floa
     __syncthreads();
 }
 
-template <int Q, int NP>
+template <int Q, int NP, bool VEC>
 __global__ __launch_bounds__(256) void ssd_state_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt,
     const float *__restrict__ dt_bias, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, float *__restrict__ S, float *__restrict__ ce, Geom g,
-    int runs_per_chunk, int heads_per_run, bool vecB, bool vecX) {
+    int runs_per_chunk, int heads_per_run) {
     using Sm = StateSmem<Q, NP>;
     constexpr int XP = Sm::XP;
     __shared__ Sm sm;
@@ -209,17 +212,17 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
     const Run run = decode_run(g, runs_per_chunk, heads_per_run);
-    const int64_t t0 = static_cast<int64_t>(run.c) * Q;
-    const int64_t rowBC = static_cast<int64_t>(g.G) * g.N;
-    const uint16_t *Bg = Bm + run.b * g.L * rowBC + static_cast<int64_t>(run.grp) * g.N;
+    const int t0 = run.c * Q;
+    const int rowBC = g.G * g.N;
+    const uint16_t *Bg = Bm + run.b * g.L * static_cast<int64_t>(rowBC) + run.grp * g.N;
 
     XRegs<Q> xr;
-    load_x<Q>(xr, x, dt, g, run, 0, vecX);
+    load_x<Q, VEC>(xr, x, dt, g, run, 0);
     // B^T of the chunk, exact bf16 values re-packed as step pairs
     for (int u = tid; u < (Q / 2) * (NP / 8); u += 256) {
         const int s2 = 2 * (u / (NP / 8)), n8 = (u % (NP / 8)) * 8;
-        const uint4 v0 = load_row8(Bg, t0 + s2, n8, g.L, g.N, rowBC, vecB);
-        const uint4 v1 = load_row8(Bg, t0 + s2 + 1, n8, g.L, g.N, rowBC, vecB);
+        const uint4 v0 = load_row8<VEC>(Bg, t0 + s2, n8, g.L, g.N, rowBC);
+        const uint4 v1 = load_row8<VEC>(Bg, t0 + s2 + 1, n8, g.L, g.N, rowBC);
         const uint32_t a[4] = {v0.x, v0.y, v0.z, v0.w}, e[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -260,7 +263,7 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(
         }
         __syncthreads();
         // next item's x (the last item re-reads its own rows; unused)
-        load_x<Q>(xr, x, dt, g, run, item + 1 < run.items ? item + 1 : item, vecX);
+        load_x<Q, VEC>(xr, x, dt, g, run, item + 1 < run.items ? item + 1 : item);
         // S[p][n] = sum_s (x w)^T[p][s] B^T[n][s]: A rows p, B operand columns n
         f16x acc[2] = {zero16(), zero16()};
         if (nt * 32 < NP) {
@@ -376,13 +379,13 @@ __device__ __forceinline__ void load_h(HRegs<NP> &r, const float *Hin, const Geo
     }
 }
 
-template <int Q, int NP>
+template <int Q, int NP, bool VEC>
 __global__ __launch_bounds__(256) void ssd_output_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt,
     const float *__restrict__ dt_bias, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm,
     const float *__restrict__ Dskip, const float *__restrict__ Hin, uint16_t *__restrict__ y,
-    Geom g, int runs_per_chunk, int heads_per_run, bool vecB, bool vecX) {
+    Geom g, int runs_per_chunk, int heads_per_run) {
     using Sm = OutSmem<Q, NP>;
     constexpr int BP = Sm::BP, XP = Sm::XP, HP = Sm::HP;
     constexpr int NT = Q / 32;          // 32-step blocks per chunk
@@ -393,18 +396,18 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
     const Run run = decode_run(g, runs_per_chunk, heads_per_run);
-    const int64_t t0 = static_cast<int64_t>(run.c) * Q;
-    const int64_t rowX = static_cast<int64_t>(g.H) * g.P;
-    const int64_t rowBC = static_cast<int64_t>(g.G) * g.N;
-    const uint16_t *Bg = Bm + run.b * g.L * rowBC + static_cast<int64_t>(run.grp) * g.N;
-    const uint16_t *Cg = Cm + run.b * g.L * rowBC + static_cast<int64_t>(run.grp) * g.N;
+    const int t0 = run.c * Q;
+    const int rowX = g.H * g.P;
+    const int rowBC = g.G * g.N;
+    const uint16_t *Bg = Bm + run.b * g.L * static_cast<int64_t>(rowBC) + run.grp * g.N;
+    const uint16_t *Cg = Cm + run.b * g.L * static_cast<int64_t>(rowBC) + run.grp * g.N;
 
     XRegs<Q> xr;
-    load_x<Q>(xr, x, dt, g, run, 0, vecX);
+    load_x<Q, VEC>(xr, x, dt, g, run, 0);
     // B of the chunk (rows s), shared by every head of the run
     for (int u = tid; u < Q * (NP / 8); u += 256) {
         const int s = u / (NP / 8), n8 = (u % (NP / 8)) * 8;
-        *reinterpret_cast<uint4 *>(&sm.B[s * BP + n8]) = load_row8(Bg, t0 + s, n8, g.L, g.N, rowBC, vecB);
+        *reinterpret_cast<uint4 *>(&sm.B[s * BP + n8]) = load_row8<VEC>(Bg, t0 + s, n8, g.L, g.N, rowBC);
     }
     // Each wave owns the 32-step blocks tb = wave and NT-1-wave (balanced
     // causal work); with fewer than 8 blocks only the first NT/2 waves work.
@@ -417,7 +420,7 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
 #pragma unroll
         for (int jn = 0; jn < KN; ++jn)
             cf[which][jn] = __builtin_bit_cast(
-                bf8, load_row8(Cg, t0 + (active ? tb : 0) * 32 + l32, 16 * jn + 8 * half, g.L, g.N, rowBC, vecB));
+                bf8, load_row8<VEC>(Cg, t0 + (active ? tb : 0) * 32 + l32, 16 * jn + 8 * half, g.L, g.N, rowBC));
     }
 
 #pragma unroll 1
@@ -425,8 +428,8 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
         const int hh = run.h0 + item / g.npg, pbase = (item % g.npg) * kPG;
         const int pcols = g.P - pbase;
         const float skip = Dskip ? Dskip[hh] : 0.0f;
-        const uint16_t *xg = x + run.b * g.L * rowX + static_cast<int64_t>(hh) * g.P + pbase;
-        uint16_t *yg = y + run.b * g.L * rowX + static_cast<int64_t>(hh) * g.P + pbase;
+        const uint16_t *xg = x + run.b * g.L * static_cast<int64_t>(rowX) + hh * g.P + pbase;
+        uint16_t *yg = y + run.b * g.L * static_cast<int64_t>(rowX) + hh * g.P + pbase;
         __syncthreads();   // the previous item's LDS reads are done
         // state entering the chunk; its loads overlap the decay scan
         HRegs<NP> hr;
@@ -458,7 +461,7 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
         }
         __syncthreads();
         // next item's x (the last item re-reads its own; unused)
-        load_x<Q>(xr, x, dt, g, run, item + 1 < run.items ? item + 1 : item, vecX);
+        load_x<Q, VEC>(xr, x, dt, g, run, item + 1 < run.items ? item + 1 : item);
         if (!active) continue;
 
         // Output tiles Y^T[p][t]: lane (column t, half) holds rows
@@ -519,7 +522,7 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
             }
             // Y_off^T[p][t] = sum_n h_in[p][n] C_t[n]; y = Y_diag + 2^cum_t Y_off + D x
             const float et = fast_exp2(cum_t);
-            const int64_t t = t0 + tl;
+            const int t = t0 + tl;
 #pragma unroll
             for (int pt = 0; pt < 2; ++pt) {
                 if (pt * 32 >= pcols) break;
@@ -533,24 +536,31 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
                     yo = mfma(al, cf[which][jn], yo);
                 }
                 if (t < g.L) {
+                    const uint32_t row = static_cast<uint32_t>(t) * static_cast<uint32_t>(rowX);
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
-                        // four consecutive p = pt*32 + 8 q4 + 4 half + 0..3; x
-                        // from the staged x^T
+                        // four consecutive p = pt*32 + 8 q4 + 4 half + 0..3
                         const int p = pt * 32 + 8 * q4 + 4 * half;
-                        float yv[4];
+                        if (VEC) {
+                            if (p < pcols) {
+                                const uint2 xv = *reinterpret_cast<const uint2 *>(xg + row + p);
+                                const float xs[4] = {bits_lo(xv.x), bits_hi(xv.x), bits_lo(xv.y), bits_hi(xv.y)};
+                                float yv[4];
 #pragma unroll
-                        for (int k = 0; k < 4; ++k) {
-                            const float xs = bf16_to_f32(sm.XT[(p + k) * XP + tl]);
-                            yv[k] = fmaf(skip, xs, fmaf(et, yo[4 * q4 + k], yd[pt][4 * q4 + k]));
-                        }
-                        if (vecX && p + 4 <= pcols) {
-                            *reinterpret_cast<uint2 *>(yg + t * rowX + p) =
-                                make_uint2(pack2(yv[0], yv[1]), pack2(yv[2], yv[3]));
+                                for (int k = 0; k < 4; ++k)
+                                    yv[k] = fmaf(skip, xs[k], fmaf(et, yo[4 * q4 + k], yd[pt][4 * q4 + k]));
+                                *reinterpret_cast<uint2 *>(yg + row + p) =
+                                    make_uint2(pack2(yv[0], yv[1]), pack2(yv[2], yv[3]));
+                            }
                         } else {
 #pragma unroll
-                            for (int k = 0; k < 4; ++k)
-                                if (p + k < pcols) yg[t * rowX + p + k] = f32_to_bf16(yv[k]);
+                            for (int k = 0; k < 4; ++k) {
+                                if (p + k < pcols) {
+                                    const float xs = bf16_to_f32(xg[row + p + k]);
+                                    yg[row + p + k] = f32_to_bf16(
+                                        fmaf(skip, xs, fmaf(et, yo[4 * q4 + k], yd[pt][4 * q4 + k])));
+                                }
+                            }
                         }
                     }
                 }
@@ -574,7 +584,7 @@ int heads_per_run(const SSDArgs &a, int64_t nch) {
 template <int Q, int NP>
 hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     Geom g;
-    g.L = a.L;
+    g.L = static_cast<int>(a.L);
     g.H = static_cast<int>(a.H);
     g.P = static_cast<int>(a.P);
     g.N = static_cast<int>(a.N);
@@ -602,8 +612,13 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     const auto *B = static_cast<const uint16_t *>(a.B);
     const auto *C = static_cast<const uint16_t *>(a.C);
     const int64_t grid = a.batch * g.nch * rpc;
-    hipLaunchKernelGGL((ssd_state_kernel<Q, NP>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
-                       stream, x, dt, a.dt_bias, a.A, B, S, ce, g, rpc, hpr, vecB, vecX);
+    const bool vec = vecB && vecX;
+    if (vec)
+        hipLaunchKernelGGL((ssd_state_kernel<Q, NP, true>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
+                           stream, x, dt, a.dt_bias, a.A, B, S, ce, g, rpc, hpr);
+    else
+        hipLaunchKernelGGL((ssd_state_kernel<Q, NP, false>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
+                           stream, x, dt, a.dt_bias, a.A, B, S, ce, g, rpc, hpr);
     e = hipGetLastError();
     if (e == hipSuccess) {
         const int bph = static_cast<int>((PN + 255) / 256);
@@ -612,9 +627,14 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
-        hipLaunchKernelGGL((ssd_output_kernel<Q, NP>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
-                           stream, x, dt, a.dt_bias, a.A, B, C, a.D, S, static_cast<uint16_t *>(a.y),
-                           g, rpc, hpr, vecB, vecX);
+        if (vec)
+            hipLaunchKernelGGL((ssd_output_kernel<Q, NP, true>), dim3(static_cast<uint32_t>(grid)), dim3(256),
+                               0, stream, x, dt, a.dt_bias, a.A, B, C, a.D, S,
+                               static_cast<uint16_t *>(a.y), g, rpc, hpr);
+        else
+            hipLaunchKernelGGL((ssd_output_kernel<Q, NP, false>), dim3(static_cast<uint32_t>(grid)), dim3(256),
+                               0, stream, x, dt, a.dt_bias, a.A, B, C, a.D, S,
+                               static_cast<uint16_t *>(a.y), g, rpc, hpr);
         e = hipGetLastError();
     }
     const hipError_t ef = hipFreeAsync(mem, stream);
@@ -633,6 +653,9 @@ hipError_t launch_by_n(const SSDArgs &a, hipStream_t stream) {
 
 bool ssd_chunked_supported(const SSDArgs &a) {
     const int64_t nch = (a.L + a.chunk - 1) / (a.chunk > 0 ? a.chunk : 1);
+    // element offsets within one batch's x and B / C slices fit in 31 bits
+    const int64_t lim = int64_t(1) << 31;
+    if (a.L * a.H * a.P >= lim || a.L * a.G * a.N >= lim || a.L * a.H >= lim) return false;
     return a.io == IO_BF16 && a.N >= 1 && a.N <= 128 && a.P >= 1 &&
            (a.chunk == 64 || a.chunk == 128 || a.chunk == 256) &&
            a.batch * nch * a.H * ((a.P + kPG - 1) / kPG) < (int64_t(1) << 31) &&

@@ -245,7 +245,27 @@ SSD_SMALL = [
     (1, 1000, 3, 40, 7, 3, "bf16"),       # two head-dim tiles, odd N, groups
     (1, 700, 2, 64, 100, 1, "bf16"),      # N not a multiple of 8
     (2, 2048, 4, 32, 64, 2, "bf16"),
+    (1, 600, 2, 80, 96, 1, "bf16"),       # two 64-column head-dim slices, N tile 96
+    (1, 520, 2, 20, 24, 2, "bf16"),       # P, N not multiples of 8: scalar loads
 ]
+
+
+def test_ssd_runs_of_heads(dev):
+    """Many chunks: each workgroup of the matrix-core form serves a run of
+    several heads of one B / C group (two groups here), reusing the staged
+    chunk of B for each of them."""
+    p = inputs.SSDProblem("case", 2, 24576, 8, 32, 32, 2, "bf16", 91)
+    announce("ssd runs of heads %s" % (p,))
+    s = inputs.ssd_inputs(p)
+    y, h = run_ssd(ssd_to_dev(s, p.io, dev), _lib.VARIANT_SSD_CHUNKED)
+    rng = np.random.default_rng(5)
+    rows = [(int(rng.integers(p.batch)), int(rng.integers(p.nheads)), int(rng.integers(p.headdim)))
+            for _ in range(10)] + [(1, 7, 31), (0, 4, 0)]
+    yo, ho = oracle.ssd_rows(rows, s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["dt_bias"])
+    ys = np.stack([y[b, :, hh, pp] for b, hh, pp in rows])
+    hs = np.stack([h[b, hh, pp] for b, hh, pp in rows])
+    gates.check(ys, yo, p.io, "y")
+    gates.check_state(hs, ho, p.io, "h_last")
 
 
 @pytest.mark.parametrize("variant", SSD_VARIANTS)
