@@ -82,10 +82,29 @@ def ssd_flops(p, chunk: int = 256) -> float:
     return 2.0 * p.batch * nchunks * (p.ngroups * per_group + p.nheads * per_head)
 
 
-def kernel_source_sha() -> str:
+# The sources each workload family's kernels are compiled from.  A counter
+# summary is tied to their hash, so a change to those kernels (and only to
+# those) retires it.
+KERNEL_SOURCES = {
+    "scan": ("device_math.h", "scan_core.h", "scan_chunked.hip", "scan_lookback.hip",
+             "scan_rowserial.hip"),
+    "ssd": ("device_math.h", "ssd_chunked.hip", "ssd_recurrent.hip"),
+}
+
+
+def workload_family(workload: str) -> str:
+    from selective_state_space_05_amd import inputs
+    if workload in inputs.SCAN_PROBLEMS:
+        return "scan"
+    if workload in inputs.SSD_PROBLEMS:
+        return "ssd"
+    raise SystemExit("unknown workload %s" % workload)
+
+
+def kernel_source_sha(family: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_05_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES[family]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -137,7 +156,7 @@ def summarize_counters(workload: str, fetch_csv: str, write_csv: str, probe_mib:
         probe = sorted(copy.values())[-3:]
         return lib, probe
 
-    out = {"workload": workload, "source_sha": kernel_source_sha(),
+    out = {"workload": workload, "source_sha": kernel_source_sha(workload_family(workload)),
            "copy_probe_mib": probe_mib, "steps": steps, "kernels": {}, "scale": {}}
     per_step = 0.0
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -165,6 +184,7 @@ def g1(a, r):
 
 class ScanBench:
     """Mamba-1 selective scan: inputs, one step, parity rows, CPU baseline."""
+    dtype = "f32"   # float32 arithmetic and state whatever the I/O dtype
 
     def __init__(self, p, dev, torch):
         from selective_state_space_05_amd import api, inputs
@@ -253,6 +273,7 @@ class ScanBench:
 
 class SSDBench:
     """Mamba-2 scalar-decay forward."""
+    dtype = "bf16"  # bf16 matrix-core products (two-term splits), float32 accumulation
 
     def __init__(self, p, dev, torch, chunk=256):
         from selective_state_space_05_amd import api, inputs
@@ -430,7 +451,7 @@ def main():
 
     hbm_gbs = footprint / sec / 1e9
     roof = wb.roofline(sec)
-    sha = kernel_source_sha()
+    sha = kernel_source_sha(workload_family(p.name))
     roof["traffic"] = load_traffic(p.name, sha)
     roof["kernel_source_sha"] = sha
     cfg = wb.config()
@@ -447,7 +468,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": wb.dtype,
         "data": "synthetic (seeded numpy draws; no dataset or trained weights)",
         "config": cfg,
         "hbm": {"min_traffic_bytes": footprint, "achieved_gbs": hbm_gbs,

@@ -55,13 +55,14 @@ hipError_t launch_typed(const ScanArgs &a, hipStream_t stream) {
 
 // Four waves with one state element per lane: the most waves in flight, and
 // the partial sums of a wave's four state rows are added in registers.
-// Larger N puts more state elements on each lane.
+// Larger N puts more state elements on each lane (four per lane for N <= 32
+// in two waves, four per lane in four waves up to N = 64).
 template <typename T>
 hipError_t launch_by_n(const ScanArgs &a, hipStream_t stream) {
     if (a.N <= 8) return launch_typed<T, 2, 1>(a, stream);
     if (a.N <= 16) return launch_typed<T, 4, 1>(a, stream);
     if (a.N <= 32) return launch_typed<T, 2, 4>(a, stream);
-    return launch_typed<T, 2, 8>(a, stream);
+    return launch_typed<T, 4, 4>(a, stream);
 }
 
 }  // namespace
@@ -85,7 +86,7 @@ bool scan_chunked_supported(const ScanArgs &a) {
 
 int64_t scan_chunked_waves(const ScanArgs &a) {
     const int64_t groups = a.batch * ((a.dim + kCh - 1) / kCh);
-    return groups * (a.N <= 16 && a.N > 8 ? 4 : 2);
+    return groups * ((a.N > 8 && a.N <= 16) || a.N > 32 ? 4 : 2);
 }
 
 hipError_t launch_scan_chunked(const ScanArgs &a, hipStream_t stream) {

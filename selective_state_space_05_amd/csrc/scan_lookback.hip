@@ -226,7 +226,7 @@ template <typename T>
 hipError_t launch_by_n(const ScanArgs &a, hipStream_t stream) {
     if (a.N <= 16) return launch_typed<T, 4, 1>(a, stream);
     if (a.N <= 32) return launch_typed<T, 2, 4>(a, stream);
-    return launch_typed<T, 2, 8>(a, stream);
+    return launch_typed<T, 4, 4>(a, stream);
 }
 
 }  // namespace

@@ -83,6 +83,7 @@ SMALL_CASES = [
     (2, 4096 + 37, 40, 16, "bf16", "scalar", True, True),  # several chunks
     (1, 2048, 130, 32, "f32", "scalar", True, True),       # N = 32
     (1, 300, 9, 64, "f32", "scalar", True, True),          # N = 64 (limit)
+    (2, 2500 + 5, 20, 48, "bf16", "per_channel", True, True),  # 32 < N < 64, several chunks
     (1, 20000 + 3, 17, 16, "bf16", "per_channel", True, True),  # many segments, ragged
     (3, 6000, 8, 7, "f32", "scalar", False, True),         # N = 7, three batches
 ]
