@@ -5,17 +5,21 @@ One step = one call of the hot path over one batch of the workload's
 synthetic inputs, which are already resident in HBM:
   * selective scan (default): softplus step size, discretisation, scan,
     output with skip term and gate, final state;
-  * SSD (--workload mamba2_ssd_layer_bf16): the Mamba-2 scalar-decay forward.
+  * SSD (--workload mamba2_ssd_layer_bf16): the Mamba-2 scalar-decay forward;
+  * decode (--workload mamba2.8b_decode_bf16): one time step on a cached
+    state (batch 256 of the Mamba-2.8B layer), in place.
 Default workload: the Mamba-2.8B-shaped layer (batch 2, L 4096, 5120
 channels, N 16, bf16 activations, fp32 state).
 
 Prints one JSON line:
   metric/value/unit   scan elements per second (batch * L * channels * N;
-                      SSD: batch * L * heads * headdim * N)
+                      SSD: batch * L * heads * headdim * N; decode:
+                      batch * channels * N)
   hbm                 minimum-traffic bytes per step / kernel time, and its
                       fraction of the 8 TB/s HBM peak
   roofline            the bound of the dominant kernel: VALU issue slots for
-                      the selective scan, bf16 matrix-core flops for SSD
+                      the selective scan, bf16 matrix-core flops for SSD,
+                      HBM bytes for the decode step
   cpu_baseline        the float64 CPU oracle timed on this host
   parity              sampled-row comparison with the oracle
 
@@ -89,6 +93,7 @@ KERNEL_SOURCES = {
     "scan": ("device_math.h", "scan_core.h", "scan_chunked.hip", "scan_lookback.hip",
              "scan_rowserial.hip"),
     "ssd": ("device_math.h", "ssd_chunked.hip", "ssd_recurrent.hip"),
+    "step": ("device_math.h", "state_update.hip"),
 }
 
 
@@ -98,6 +103,8 @@ def workload_family(workload: str) -> str:
         return "scan"
     if workload in inputs.SSD_PROBLEMS:
         return "ssd"
+    if workload in inputs.STEP_PROBLEMS:
+        return "step"
     raise SystemExit("unknown workload %s" % workload)
 
 
@@ -366,6 +373,77 @@ class SSDBench:
                 "chunk": self.chunk}
 
 
+class StepBench:
+    """One decode step (selective_state_update) on a cached float32 state."""
+    dtype = "f32"
+
+    def __init__(self, p, dev, torch):
+        from selective_state_space_05_amd import api, inputs
+        self.p, self.dev, self.torch, self.api = p, dev, torch, api
+        self.x = inputs.step_inputs(p)
+        self.io_t = torch.bfloat16 if p.io == "bf16" else torch.float32
+
+    def upload(self):
+        torch = self.torch
+        t = {}
+        for k, v in self.x.items():
+            if v is None:
+                t[k] = None
+            elif k in ("A", "D", "dt_bias", "state"):
+                t[k] = torch.from_numpy(v).to(self.dev)
+            else:
+                t[k] = torch.from_numpy(v).to(self.io_t).to(self.dev)
+        t["y"] = torch.empty_like(t["x"])
+        return t
+
+    def step(self, t):
+        self.api.selective_state_update(t["state"], t["x"], t["dt"], t["A"], t["B"], t["C"],
+                                        t["D"], t["z"], t["dt_bias"], out=t["y"])
+
+    def roofline(self, sec):
+        nbytes = self.p.min_traffic_bytes()
+        a = nbytes / sec / 1e9
+        return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": a / HBM_PEAK_GBS, "bytes_per_launch": nbytes}
+
+    def _oracle(self, nthreads=0):
+        from oracle import oracle
+        x = self.x
+        col = lambda a: None if a is None else a[..., None]   # noqa: E731
+        return oracle.selective_scan(col(x["x"]), col(x["dt"]), x["A"], col(x["B"]),
+                                     col(x["C"]), x["D"], col(x["z"]), x["dt_bias"],
+                                     h0=x["state"], nthreads=nthreads)
+
+    def parity(self, t):
+        """One step from the drawn state (the timed steps advanced the
+        uploaded copies), compared with the oracle over every row."""
+        torch = self.torch
+        fresh = dict(t)
+        fresh["state"] = torch.from_numpy(self.x["state"]).to(self.dev)
+        fresh["y"] = torch.empty_like(t["x"])
+        self.step(fresh)
+        torch.cuda.synchronize()
+        yo, ho = self._oracle()
+        yg = fresh["y"].float().cpu().numpy().astype(np.float64)
+        hg = fresh["state"].cpu().numpy().astype(np.float64)
+        return self.p.batch, g1(yg, yo[..., 0]), g1(hg, ho)
+
+    def cpu_baseline(self, threads, budget_s=10.0):
+        """The oracle on the whole step, repeated for about `budget_s`."""
+        reps, t0 = 0, time.time()
+        while reps == 0 or time.time() - t0 < budget_s:
+            self._oracle(nthreads=threads)
+            reps += 1
+        cpu_s = time.time() - t0
+        return reps * self.p.elements / cpu_s, "the whole step (%d rows) %d times, float64, %.1f s" % (
+            self.p.batch * self.p.dim, reps, cpu_s)
+
+    def config(self):
+        p = self.p
+        return {"workload": p.name, "batch": p.batch, "dim": p.dim, "dstate": p.dstate,
+                "io": p.io, "gate": p.gate, "skip": p.skip}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -418,9 +496,14 @@ def main():
         p = inputs.SSD_PROBLEMS[args.workload]
         print("[bench] workload %s: drawing inputs" % p.name, file=sys.stderr, flush=True)
         wb = SSDBench(p, dev, torch, args.chunk)
+    elif args.workload in inputs.STEP_PROBLEMS:
+        p = inputs.STEP_PROBLEMS[args.workload]
+        print("[bench] workload %s: drawing inputs" % p.name, file=sys.stderr, flush=True)
+        wb = StepBench(p, dev, torch)
     else:
         raise SystemExit("unknown workload %s; choose from %s" % (
-            args.workload, sorted(inputs.SCAN_PROBLEMS) + sorted(inputs.SSD_PROBLEMS)))
+            args.workload, sorted(inputs.SCAN_PROBLEMS) + sorted(inputs.SSD_PROBLEMS) +
+            sorted(inputs.STEP_PROBLEMS)))
 
     footprint = p.min_traffic_bytes()
     rotate = args.rotate or max(1, min(4, -(-(1 << 30) // footprint)))

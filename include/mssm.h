@@ -17,6 +17,12 @@
  *   [csdn] "从硬件感知到算法革命：Mamba如何重塑序列建模的计算效率"
  *          (tencentcloud.csdn.net) -- section 2: Delta = softplus(.), B and C
  *          input-dependent; section 3: SSM output merged with a SiLU gate.
+ *   [mlqm] essay at www.mlqm.cn/news/983902 -- section 5.4: token-by-token
+ *          decoding keeps only the fixed-size evolving state between steps.
+ * [ybb] section 2.1 also writes the recurrence as a product of augmented
+ * matrices applied to [h_0; 1], and its section 5 walks the chunks from an
+ * initial state h0; [mhpq] section 4.2 keeps the state in a preallocated
+ * buffer updated in place.
  *
  * Conventions shared by every entry point:
  *   - Tensor arguments are DEVICE pointers owned by the caller, contiguous in
@@ -168,6 +174,73 @@ MSSM_API mssm_status mssm_ssd_scalar_fwd(const void *x, const void *dt,
                                 const void *B, const void *C, const float *D,
                                 void *y, float *h_last, mssm_ssd_dims dims,
                                 mssm_dtypes dtypes, void *stream);
+
+/*
+ * Both forwards from a given initial state ([ybb] sections 2.1 and 5): the
+ * recurrence starts at h0 instead of 0, so a long sequence can be processed
+ * in pieces, each call continuing from the h_last of the previous one.
+ *
+ *   h0  (batch, dim, N) float32 for the selective scan,
+ *       (batch, H, P, N) float32 for SSD          nullable -> 0
+ *
+ * h0 may be the very buffer passed as h_last (same pointer): the state is
+ * then advanced in place.  Any other overlap of h0 with an output is
+ * MSSM_ERR_INVALID_ARG.  L == 0 copies h0 to h_last.  Everything else --
+ * layouts, variants, errors -- is as for the entry points without h0, which
+ * equal these with h0 = NULL.
+ */
+MSSM_API mssm_status mssm_selective_scan_fwd_h0(const void *u, const void *delta,
+                                       const float *delta_bias, const float *A,
+                                       const void *B, const void *C,
+                                       const float *D, const void *z,
+                                       const float *h0, void *y, float *h_last,
+                                       mssm_scan_dims dims, mssm_dtypes dtypes,
+                                       void *stream);
+MSSM_API mssm_status mssm_ssd_scalar_fwd_h0(const void *x, const void *dt,
+                                   const float *dt_bias, const float *A,
+                                   const void *B, const void *C, const float *D,
+                                   const float *h0, void *y, float *h_last,
+                                   mssm_ssd_dims dims, mssm_dtypes dtypes,
+                                   void *stream);
+
+/* Sizes of one decode step. */
+typedef struct {
+    int64_t batch;   /* >= 0 */
+    int64_t dim;     /* channels D >= 0 */
+    int64_t dstate;  /* state size N, 1 <= N <= MSSM_MAX_DSTATE */
+} mssm_step_dims;
+
+/*
+ * One decode step of the selective scan ([mlqm] section 5.4: incremental
+ * decoding carries only the fixed-size state; [mhpq] section 4.2: the state
+ * cache is a preallocated buffer; the step itself is the recurrence of
+ * mssm_selective_scan_fwd at a single time t):
+ *
+ *   dl              = softplus(dt[b,d] + dt_bias[d])
+ *   state[b,d,n]    = exp(dl * A[d,n]) * state[b,d,n] + dl * B[b,n] * x[b,d]
+ *   y[b,d]          = (sum_n C[b,n] * state[b,d,n] + D[d] * x[b,d]) * silu(z[b,d])
+ *
+ * It equals mssm_selective_scan_fwd_h0 with L = 1 and h0 = h_last = state.
+ *
+ * Arguments (device pointers unless stated):
+ *   state    (batch, dim, N) float32       required, read and overwritten
+ *   x, dt    (batch, dim), dtype `io`      required
+ *   dt_bias  (dim) float32                 nullable -> 0
+ *   A        (dim, N) float32              required
+ *   B, C     (batch, N), dtype `io`        required
+ *   D        (dim) float32                 nullable -> no skip term
+ *   z        (batch, dim), dtype `io`      nullable -> no gate
+ *   y        (batch, dim), dtype `io`      required (output)
+ * Errors: as for mssm_selective_scan_fwd; state and y must not overlap any
+ * input or each other.  batch == 0 or dim == 0: nothing to do, MSSM_OK.
+ */
+MSSM_API mssm_status mssm_selective_state_update(float *state, const void *x,
+                                        const void *dt, const float *dt_bias,
+                                        const float *A, const void *B,
+                                        const void *C, const float *D,
+                                        const void *z, void *y,
+                                        mssm_step_dims dims, mssm_dtypes dtypes,
+                                        void *stream);
 
 /* Force a kernel variant for subsequent calls made by THIS thread
  * (MSSM_VARIANT_AUTO restores the shape-based choice).  A variant that does

@@ -37,6 +37,9 @@ SSD_MAX_HEADDIM = 256
 EXPORTED = (
     "mssm_selective_scan_fwd",
     "mssm_ssd_scalar_fwd",
+    "mssm_selective_scan_fwd_h0",
+    "mssm_ssd_scalar_fwd_h0",
+    "mssm_selective_state_update",
     "mssm_force_variant",
     "mssm_last_variant",
     "mssm_status_string",
@@ -57,6 +60,11 @@ class SSDDims(ctypes.Structure):
                 ("chunk", ctypes.c_int64)]
 
 
+class StepDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("dim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64)]
+
+
 class DTypes(ctypes.Structure):
     _fields_ = [("io", ctypes.c_int32), ("param", ctypes.c_int32)]
 
@@ -74,6 +82,15 @@ def _declare(L):
     L.mssm_ssd_scalar_fwd.argtypes = [vp, vp, fp, fp, vp, vp, fp, vp, fp,
                                       SSDDims, DTypes, vp]
     L.mssm_ssd_scalar_fwd.restype = ctypes.c_int
+    L.mssm_selective_scan_fwd_h0.argtypes = [vp, vp, fp, fp, vp, vp, fp, vp, fp,
+                                             vp, fp, ScanDims, DTypes, vp]
+    L.mssm_selective_scan_fwd_h0.restype = ctypes.c_int
+    L.mssm_ssd_scalar_fwd_h0.argtypes = [vp, vp, fp, fp, vp, vp, fp, fp, vp, fp,
+                                         SSDDims, DTypes, vp]
+    L.mssm_ssd_scalar_fwd_h0.restype = ctypes.c_int
+    L.mssm_selective_state_update.argtypes = [fp, vp, vp, fp, fp, vp, vp, fp, vp, vp,
+                                              StepDims, DTypes, vp]
+    L.mssm_selective_state_update.restype = ctypes.c_int
     L.mssm_force_variant.argtypes = [ctypes.c_int]
     L.mssm_force_variant.restype = ctypes.c_int
     L.mssm_last_variant.argtypes = []

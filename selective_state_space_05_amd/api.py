@@ -81,13 +81,15 @@ def last_variant() -> int:
 
 
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
-                       return_last_state=True, out=None, h_out=None):
+                       return_last_state=True, out=None, h_out=None, h0=None):
     """Selective-scan forward on the GPU.
 
     u, delta, z: (batch, dim, L) float32 or bfloat16 (all the same dtype);
     B, C: (batch, N, L) same dtype; A: (dim, N) float32; D, delta_bias:
-    (dim,) float32.  Returns ``(y, h_last)`` with y like u and h_last
-    (batch, dim, N) float32 (None if ``return_last_state`` is False).
+    (dim,) float32; h0: (batch, dim, N) float32 initial state (None: zero;
+    it may be passed as ``h_out`` too, to advance a state in place).
+    Returns ``(y, h_last)`` with y like u and h_last (batch, dim, N) float32
+    (None if ``return_last_state`` is False).
     """
     L = _lib.lib()
     dev = u.device
@@ -96,10 +98,12 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     io = u.dtype
     for name, t in (("u", u), ("delta", delta), ("B", B), ("C", C), ("z", z)):
         _need(t, name, io, dev)
-    for name, t in (("A", A), ("D", D), ("delta_bias", delta_bias)):
+    for name, t in (("A", A), ("D", D), ("delta_bias", delta_bias), ("h0", h0)):
         _need(t, name, torch.float32, dev)
     batch, dim, seqlen = u.shape
     N = A.shape[1]
+    if h0 is not None and tuple(h0.shape) != (batch, dim, N):
+        raise ValueError("h0 must be (batch, dim, N)")
     if delta.shape != u.shape or (z is not None and z.shape != u.shape):
         raise ValueError("u, delta, z must share one (batch, dim, L) shape")
     if tuple(A.shape) != (dim, N):
@@ -119,20 +123,27 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     dims = _lib.ScanDims(batch, seqlen, dim, N)
     dt = _lib.DTypes(_io_dtype(u), _lib.MSSM_F32)
     with torch.cuda.device(dev):
-        st = L.mssm_selective_scan_fwd(
-            _ptr(u), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C),
-            _ptr(D), _ptr(z), _ptr(y), _ptr(h_last), dims, dt,
-            _stream_handle(dev))
+        if h0 is None:
+            st = L.mssm_selective_scan_fwd(
+                _ptr(u), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C),
+                _ptr(D), _ptr(z), _ptr(y), _ptr(h_last), dims, dt,
+                _stream_handle(dev))
+        else:
+            st = L.mssm_selective_scan_fwd_h0(
+                _ptr(u), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C),
+                _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last), dims, dt,
+                _stream_handle(dev))
     _check(st)
     return y, h_last
 
 
 def ssd_scalar_fwd(x, dt, A, B, C, D=None, dt_bias=None, chunk=0,
-                   return_last_state=True, out=None, h_out=None):
+                   return_last_state=True, out=None, h_out=None, h0=None):
     """Mamba-2 scalar-decay forward on the GPU.
 
     x: (batch, L, H, P); dt: (batch, L, H); B, C: (batch, L, G, N), all in
-    one activation dtype; A, D, dt_bias: (H,) float32.  Returns
+    one activation dtype; A, D, dt_bias: (H,) float32; h0: (batch, H, P, N)
+    float32 initial state (None: zero; may also be ``h_out``).  Returns
     ``(y, h_last)``: y like x, h_last (batch, H, P, N) float32.
     """
     L = _lib.lib()
@@ -142,10 +153,12 @@ def ssd_scalar_fwd(x, dt, A, B, C, D=None, dt_bias=None, chunk=0,
     io = x.dtype
     for name, t in (("x", x), ("dt", dt), ("B", B), ("C", C)):
         _need(t, name, io, dev)
-    for name, t in (("A", A), ("D", D), ("dt_bias", dt_bias)):
+    for name, t in (("A", A), ("D", D), ("dt_bias", dt_bias), ("h0", h0)):
         _need(t, name, torch.float32, dev)
     batch, seqlen, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
+    if h0 is not None and tuple(h0.shape) != (batch, H, P, N):
+        raise ValueError("h0 must be (batch, H, P, N)")
     if tuple(dt.shape) != (batch, seqlen, H):
         raise ValueError("dt must be (batch, L, H)")
     if tuple(B.shape) != (batch, seqlen, G, N) or tuple(C.shape) != tuple(B.shape):
@@ -163,8 +176,58 @@ def ssd_scalar_fwd(x, dt, A, B, C, D=None, dt_bias=None, chunk=0,
     dims = _lib.SSDDims(batch, seqlen, H, P, N, G, int(chunk))
     dtp = _lib.DTypes(_io_dtype(x), _lib.MSSM_F32)
     with torch.cuda.device(dev):
-        st = L.mssm_ssd_scalar_fwd(
-            _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
-            _ptr(D), _ptr(y), _ptr(h_last), dims, dtp, _stream_handle(dev))
+        if h0 is None:
+            st = L.mssm_ssd_scalar_fwd(
+                _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
+                _ptr(D), _ptr(y), _ptr(h_last), dims, dtp, _stream_handle(dev))
+        else:
+            st = L.mssm_ssd_scalar_fwd_h0(
+                _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
+                _ptr(D), _ptr(h0), _ptr(y), _ptr(h_last), dims, dtp,
+                _stream_handle(dev))
     _check(st)
     return y, h_last
+
+
+def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
+                           out=None):
+    """One decode step on the GPU, advancing ``state`` in place.
+
+    state: (batch, dim, N) float32; x, dt, z: (batch, dim) float32 or
+    bfloat16 (one dtype); B, C: (batch, N) same dtype; A: (dim, N) float32;
+    D, dt_bias: (dim,) float32.  Returns y (batch, dim) like x.
+    """
+    L = _lib.lib()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    io = x.dtype
+    for name, t in (("x", x), ("dt", dt), ("B", B), ("C", C), ("z", z)):
+        _need(t, name, io, dev)
+    for name, t in (("state", state), ("A", A), ("D", D), ("dt_bias", dt_bias)):
+        _need(t, name, torch.float32, dev)
+    if x.dim() != 2:
+        raise ValueError("x must be (batch, dim)")
+    batch, dim = x.shape
+    N = A.shape[1]
+    if tuple(state.shape) != (batch, dim, N):
+        raise ValueError("state must be (batch, dim, N)")
+    if tuple(dt.shape) != (batch, dim) or (z is not None and tuple(z.shape) != (batch, dim)):
+        raise ValueError("dt and z must be (batch, dim)")
+    if tuple(A.shape) != (dim, N):
+        raise ValueError("A must be (dim, N)")
+    if tuple(B.shape) != (batch, N) or tuple(C.shape) != (batch, N):
+        raise ValueError("B and C must be (batch, N)")
+    for name, t in (("D", D), ("dt_bias", dt_bias)):
+        if t is not None and tuple(t.shape) != (dim,):
+            raise ValueError("%s must be (dim,)" % name)
+    y = out if out is not None else torch.empty_like(x)
+    _need(y, "out", io, dev)
+    dims = _lib.StepDims(batch, dim, N)
+    dtp = _lib.DTypes(_io_dtype(x), _lib.MSSM_F32)
+    with torch.cuda.device(dev):
+        st = L.mssm_selective_state_update(
+            _ptr(state), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
+            _ptr(D), _ptr(z), _ptr(y), dims, dtp, _stream_handle(dev))
+    _check(st)
+    return y

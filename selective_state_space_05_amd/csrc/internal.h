@@ -11,7 +11,9 @@ enum IoType : int { IO_F32 = 0, IO_BF16 = 1 };
 
 // One selective-scan problem, already validated.  Layouts as in mssm.h:
 // u, delta, z, y (batch, dim, L); B, C (batch, N, L); A (dim, N);
-// delta_bias, D (dim); h_last (batch, dim, N).
+// delta_bias, D (dim); h0, h_last (batch, dim, N).  h0 may be the same
+// buffer as h_last (each element is read before it is overwritten) but
+// overlaps nothing else.
 struct ScanArgs {
     const void *u;
     const void *delta;
@@ -21,6 +23,7 @@ struct ScanArgs {
     const void *C;
     const float *D;           // may be null
     const void *z;            // may be null
+    const float *h0;          // may be null -> the state starts at 0
     void *y;
     float *h_last;            // may be null
     int64_t batch, L, dim, N;
@@ -36,9 +39,28 @@ struct SSDArgs {
     const void *B;
     const void *C;
     const float *D;           // may be null
+    const float *h0;          // may be null; may be the same buffer as h_last
     void *y;
     float *h_last;            // may be null
     int64_t batch, L, H, P, N, G, chunk;
+    IoType io;
+};
+
+// One decode step of the selective scan, already validated: state
+// (batch, dim, N) float32 updated in place; x, dt, z, y (batch, dim);
+// B, C (batch, N); A (dim, N); dt_bias, D (dim).
+struct StepArgs {
+    float *state;
+    const void *x;
+    const void *dt;
+    const float *dt_bias;     // may be null
+    const float *A;
+    const void *B;
+    const void *C;
+    const float *D;           // may be null
+    const void *z;            // may be null
+    void *y;
+    int64_t batch, dim, N;
     IoType io;
 };
 
@@ -60,6 +82,9 @@ bool scan_rows_vectorizable(const ScanArgs &a);
 // Chunk-parallel variant; allocates its look-back scratch stream-ordered.
 hipError_t launch_scan_lookback(const ScanArgs &a, hipStream_t stream);
 bool scan_lookback_supported(const ScanArgs &a);
+
+hipError_t launch_state_update(const StepArgs &a, hipStream_t stream);
+bool state_update_supported(const StepArgs &a);
 
 hipError_t launch_ssd_recurrent(const SSDArgs &a, hipStream_t stream);
 bool ssd_recurrent_supported(const SSDArgs &a);

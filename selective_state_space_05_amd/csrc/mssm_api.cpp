@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <cstring>
 #include <string>
 
 #include "internal.h"
@@ -92,16 +93,32 @@ mssm_variant choose_scan_variant(const mssm::ScanArgs &a) {
     return MSSM_VARIANT_CHUNKED;
 }
 
-}  // namespace
+// Outputs may not overlap inputs, nor each other; the one exception is an
+// initial-state input passed as the final-state output itself (the same
+// buffer, exactly), which continues a sequence in place.
+mssm_status check_overlaps(const Range *ins, int nin, const Range *outs, int nout,
+                           const void *h0, const void *h_last) {
+    const bool in_place = h0 && h0 == h_last;
+    for (int o = 0; o < nout; ++o)
+        for (int i = 0; i < nin; ++i) {
+            if (in_place && std::strcmp(ins[i].name, "h0") == 0 &&
+                std::strcmp(outs[o].name, "h_last") == 0)
+                continue;
+            if (overlaps(outs[o], ins[i]))
+                return fail(MSSM_ERR_INVALID_ARG, "output %s overlaps input %s", outs[o].name,
+                            ins[i].name);
+        }
+    for (int o = 0; o < nout; ++o)
+        for (int p = o + 1; p < nout; ++p)
+            if (overlaps(outs[o], outs[p]))
+                return fail(MSSM_ERR_INVALID_ARG, "%s overlaps %s", outs[o].name, outs[p].name);
+    return MSSM_OK;
+}
 
-extern "C" {
-
-mssm_status mssm_selective_scan_fwd(const void *u, const void *delta,
-                                    const float *delta_bias, const float *A,
-                                    const void *B, const void *C,
-                                    const float *D, const void *z, void *y,
-                                    float *h_last, mssm_scan_dims dims,
-                                    mssm_dtypes dtypes, void *stream) {
+mssm_status scan_fwd(const void *u, const void *delta, const float *delta_bias, const float *A,
+                     const void *B, const void *C, const float *D, const void *z, const float *h0,
+                     void *y, float *h_last, mssm_scan_dims dims, mssm_dtypes dtypes,
+                     void *stream) {
     g_last_error.clear();
     if (mssm_status s = check_dtypes(dtypes)) return s;
     const int64_t batch = dims.batch, L = dims.seqlen, dim = dims.dim, N = dims.dstate;
@@ -124,9 +141,16 @@ mssm_status mssm_selective_scan_fwd(const void *u, const void *delta,
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (L == 0) {
-        if (h_last) {
-            hipError_t e = zero_fill(h_last, rows * N, st);
-            if (e != hipSuccess) return hip_fail(e, "zero-fill of h_last");
+        if (h_last && h0 != h_last) {
+            if (h0) {
+                if (overlaps(range("h_last", h_last, hl), range("h0", h0, hl)))
+                    return fail(MSSM_ERR_INVALID_ARG, "output h_last overlaps input h0");
+                hipError_t e = hipMemcpyAsync(h_last, h0, hl, hipMemcpyDeviceToDevice, st);
+                if (e != hipSuccess) return hip_fail(e, "copy of h0 to h_last");
+            } else {
+                hipError_t e = zero_fill(h_last, rows * N, st);
+                if (e != hipSuccess) return hip_fail(e, "zero-fill of h_last");
+            }
         }
         g_last_variant = MSSM_VARIANT_AUTO;
         return MSSM_OK;
@@ -142,15 +166,12 @@ mssm_status mssm_selective_scan_fwd(const void *u, const void *delta,
         range("u", u, act_bytes),          range("delta", delta, act_bytes),
         range("z", z, act_bytes),          range("B", B, bc_bytes),
         range("C", C, bc_bytes),           range("A", A, dn * 4),
-        range("D", D, dim * 4),            range("delta_bias", delta_bias, dim * 4)};
+        range("D", D, dim * 4),            range("delta_bias", delta_bias, dim * 4),
+        range("h0", h0, hl)};
     const Range outs[] = {range("y", y, act_bytes), range("h_last", h_last, hl)};
-    for (const Range &o : outs)
-        for (const Range &i : ins)
-            if (overlaps(o, i))
-                return fail(MSSM_ERR_INVALID_ARG, "output %s overlaps input %s", o.name, i.name);
-    if (overlaps(outs[0], outs[1])) return fail(MSSM_ERR_INVALID_ARG, "y overlaps h_last");
+    if (mssm_status c = check_overlaps(ins, 9, outs, 2, h0, h_last)) return c;
 
-    mssm::ScanArgs a{u, delta, delta_bias, A, B, C, D, z, y, h_last, batch, L, dim, N,
+    mssm::ScanArgs a{u, delta, delta_bias, A, B, C, D, z, h0, y, h_last, batch, L, dim, N,
                      dtypes.io == MSSM_F32 ? mssm::IO_F32 : mssm::IO_BF16};
 
     mssm_variant v = g_forced;
@@ -181,10 +202,9 @@ mssm_status mssm_selective_scan_fwd(const void *u, const void *delta,
     return MSSM_OK;
 }
 
-mssm_status mssm_ssd_scalar_fwd(const void *x, const void *dt, const float *dt_bias,
-                                const float *A, const void *B, const void *C,
-                                const float *D, void *y, float *h_last,
-                                mssm_ssd_dims dims, mssm_dtypes dtypes, void *stream) {
+mssm_status ssd_fwd(const void *x, const void *dt, const float *dt_bias, const float *A,
+                    const void *B, const void *C, const float *D, const float *h0, void *y,
+                    float *h_last, mssm_ssd_dims dims, mssm_dtypes dtypes, void *stream) {
     g_last_error.clear();
     if (mssm_status s = check_dtypes(dtypes)) return s;
     const int64_t batch = dims.batch, L = dims.seqlen, H = dims.nheads, P = dims.headdim,
@@ -215,9 +235,16 @@ mssm_status mssm_ssd_scalar_fwd(const void *x, const void *dt, const float *dt_b
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (L == 0) {
-        if (h_last) {
-            hipError_t e = zero_fill(h_last, hl / 4, st);
-            if (e != hipSuccess) return hip_fail(e, "zero-fill of h_last");
+        if (h_last && h0 != h_last) {
+            if (h0) {
+                if (overlaps(range("h_last", h_last, hl), range("h0", h0, hl)))
+                    return fail(MSSM_ERR_INVALID_ARG, "output h_last overlaps input h0");
+                hipError_t e = hipMemcpyAsync(h_last, h0, hl, hipMemcpyDeviceToDevice, st);
+                if (e != hipSuccess) return hip_fail(e, "copy of h0 to h_last");
+            } else {
+                hipError_t e = zero_fill(h_last, hl / 4, st);
+                if (e != hipSuccess) return hip_fail(e, "zero-fill of h_last");
+            }
         }
         g_last_variant = MSSM_VARIANT_AUTO;
         return MSSM_OK;
@@ -231,15 +258,11 @@ mssm_status mssm_ssd_scalar_fwd(const void *x, const void *dt, const float *dt_b
     const Range ins[] = {range("x", x, x_bytes),   range("dt", dt, dt_bytes),
                          range("B", B, bc_bytes),  range("C", C, bc_bytes),
                          range("A", A, H * 4),     range("D", D, H * 4),
-                         range("dt_bias", dt_bias, H * 4)};
+                         range("dt_bias", dt_bias, H * 4), range("h0", h0, hl)};
     const Range outs[] = {range("y", y, x_bytes), range("h_last", h_last, hl)};
-    for (const Range &o : outs)
-        for (const Range &i : ins)
-            if (overlaps(o, i))
-                return fail(MSSM_ERR_INVALID_ARG, "output %s overlaps input %s", o.name, i.name);
-    if (overlaps(outs[0], outs[1])) return fail(MSSM_ERR_INVALID_ARG, "y overlaps h_last");
+    if (mssm_status c = check_overlaps(ins, 8, outs, 2, h0, h_last)) return c;
 
-    mssm::SSDArgs a{x, dt, dt_bias, A, B, C, D, y, h_last, batch, L, H, P, N, G,
+    mssm::SSDArgs a{x, dt, dt_bias, A, B, C, D, h0, y, h_last, batch, L, H, P, N, G,
                     Q == 0 ? 256 : Q, dtypes.io == MSSM_F32 ? mssm::IO_F32 : mssm::IO_BF16};
     // The matrix-core form needs bf16 operands and a few chunks to pay off;
     // everything else takes the recurrent form.
@@ -266,6 +289,92 @@ mssm_status mssm_ssd_scalar_fwd(const void *x, const void *dt, const float *dt_b
     }
     if (e != hipSuccess) return hip_fail(e, "SSD launch");
     g_last_variant = v;
+    return MSSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mssm_status mssm_selective_scan_fwd(const void *u, const void *delta,
+                                    const float *delta_bias, const float *A,
+                                    const void *B, const void *C,
+                                    const float *D, const void *z, void *y,
+                                    float *h_last, mssm_scan_dims dims,
+                                    mssm_dtypes dtypes, void *stream) {
+    return scan_fwd(u, delta, delta_bias, A, B, C, D, z, nullptr, y, h_last, dims, dtypes,
+                    stream);
+}
+
+mssm_status mssm_selective_scan_fwd_h0(const void *u, const void *delta,
+                                       const float *delta_bias, const float *A,
+                                       const void *B, const void *C, const float *D,
+                                       const void *z, const float *h0, void *y,
+                                       float *h_last, mssm_scan_dims dims,
+                                       mssm_dtypes dtypes, void *stream) {
+    return scan_fwd(u, delta, delta_bias, A, B, C, D, z, h0, y, h_last, dims, dtypes, stream);
+}
+
+mssm_status mssm_ssd_scalar_fwd(const void *x, const void *dt, const float *dt_bias,
+                                const float *A, const void *B, const void *C,
+                                const float *D, void *y, float *h_last,
+                                mssm_ssd_dims dims, mssm_dtypes dtypes, void *stream) {
+    return ssd_fwd(x, dt, dt_bias, A, B, C, D, nullptr, y, h_last, dims, dtypes, stream);
+}
+
+mssm_status mssm_ssd_scalar_fwd_h0(const void *x, const void *dt, const float *dt_bias,
+                                   const float *A, const void *B, const void *C,
+                                   const float *D, const float *h0, void *y, float *h_last,
+                                   mssm_ssd_dims dims, mssm_dtypes dtypes, void *stream) {
+    return ssd_fwd(x, dt, dt_bias, A, B, C, D, h0, y, h_last, dims, dtypes, stream);
+}
+
+mssm_status mssm_selective_state_update(float *state, const void *x, const void *dt,
+                                        const float *dt_bias, const float *A, const void *B,
+                                        const void *C, const float *D, const void *z, void *y,
+                                        mssm_step_dims dims, mssm_dtypes dtypes, void *stream) {
+    g_last_error.clear();
+    if (mssm_status s = check_dtypes(dtypes)) return s;
+    const int64_t batch = dims.batch, dim = dims.dim, N = dims.dstate;
+    if (batch < 0 || dim < 0)
+        return fail(MSSM_ERR_INVALID_ARG, "negative size (batch %lld, dim %lld)", (long long)batch,
+                    (long long)dim);
+    if (N < 1) return fail(MSSM_ERR_INVALID_ARG, "dstate must be >= 1, got %lld", (long long)N);
+    if (N > MSSM_MAX_DSTATE)
+        return fail(MSSM_ERR_UNSUPPORTED, "dstate %lld exceeds MSSM_MAX_DSTATE (%d)",
+                    (long long)N, MSSM_MAX_DSTATE);
+    const int64_t esz = dtypes.io == MSSM_F32 ? 4 : 2;
+    int64_t rows, row_bytes, st_bytes, bc_bytes, dn;
+    if (!mul_ok(batch, dim, &rows) || !mul_ok(rows, esz, &row_bytes) ||
+        !mul_ok(rows, N, &st_bytes) || !mul_ok(st_bytes, 4, &st_bytes) ||
+        !mul_ok(batch, N, &bc_bytes) || !mul_ok(bc_bytes, esz, &bc_bytes) ||
+        !mul_ok(dim, N, &dn))
+        return fail(MSSM_ERR_INVALID_ARG, "sizes overflow int64");
+    if (rows == 0) {
+        g_last_variant = MSSM_VARIANT_AUTO;
+        return MSSM_OK;
+    }
+    if (!state) return fail(MSSM_ERR_INVALID_ARG, "state is null");
+    if (!x) return fail(MSSM_ERR_INVALID_ARG, "x is null");
+    if (!dt) return fail(MSSM_ERR_INVALID_ARG, "dt is null");
+    if (!A) return fail(MSSM_ERR_INVALID_ARG, "A is null");
+    if (!B) return fail(MSSM_ERR_INVALID_ARG, "B is null");
+    if (!C) return fail(MSSM_ERR_INVALID_ARG, "C is null");
+    if (!y) return fail(MSSM_ERR_INVALID_ARG, "y is null");
+    const Range ins[] = {range("x", x, row_bytes),   range("dt", dt, row_bytes),
+                         range("z", z, row_bytes),   range("B", B, bc_bytes),
+                         range("C", C, bc_bytes),    range("A", A, dn * 4),
+                         range("D", D, dim * 4),     range("dt_bias", dt_bias, dim * 4)};
+    const Range outs[] = {range("y", y, row_bytes), range("state", state, st_bytes)};
+    if (mssm_status c = check_overlaps(ins, 8, outs, 2, nullptr, nullptr)) return c;
+
+    mssm::StepArgs a{state, x, dt, dt_bias, A, B, C, D, z, y, batch, dim, N,
+                     dtypes.io == MSSM_F32 ? mssm::IO_F32 : mssm::IO_BF16};
+    if (!mssm::state_update_supported(a))
+        return fail(MSSM_ERR_UNSUPPORTED, "state update does not support this shape");
+    const hipError_t e = mssm::launch_state_update(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "state-update launch");
+    g_last_variant = MSSM_VARIANT_AUTO;
     return MSSM_OK;
 }
 

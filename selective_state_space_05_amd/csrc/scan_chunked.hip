@@ -1,5 +1,5 @@
 // scan_chunked.hip -- selective-scan forward: one workgroup per (batch,
-// 16-channel group) walks the whole sequence from h = 0 with the fused chunk
+// 16-channel group) walks the whole sequence from h0 (or 0) with the fused chunk
 // walk of scan_core.h.  Parallelism is over channels and state elements; the
 // sequence itself is walked in order, so the recurrence is evaluated exactly
 // as its sequential definition ("Mamba状态空间模型的硬件感知推理优化"
@@ -17,18 +17,25 @@ __global__ __launch_bounds__(64 * W) void scan_chunked_kernel(
     const T *__restrict__ u, const T *__restrict__ delta,
     const float *__restrict__ delta_bias, const float *__restrict__ A,
     const T *__restrict__ Bm, const T *__restrict__ Cm,
-    const float *__restrict__ Dskip, const T *__restrict__ z, T *__restrict__ y,
-    float *__restrict__ h_last, int64_t L, int dim, int N, int groups_per_batch) {
+    const float *__restrict__ Dskip, const T *__restrict__ z, const float *h0, T *__restrict__ y,
+    float *h_last, int64_t L, int dim, int N, int groups_per_batch) {
     __shared__ core::Smem<W> sm;
     const int64_t b = blockIdx.x / groups_per_batch;
     const int d0 = (blockIdx.x - static_cast<int>(b) * groups_per_batch) * kCh;
     core::Walker<T, W, NPL, GATE, VEC> wk;
     wk.init(u, delta, delta_bias, A, Bm, Cm, Dskip, z, y, L, dim, N, b, d0);
+    // Lanes of channels past the last one mirror the last channel (their
+    // owners store its y again), so they start from its initial state too.
     float h[NPL];
+    const bool row_ok = d0 + wk.j < dim;
+    const int dS = min(d0 + wk.j, dim - 1);
 #pragma unroll
-    for (int g = 0; g < NPL; ++g) h[g] = 0.0f;
+    for (int g = 0; g < NPL; ++g)
+        h[g] = (h0 && wk.nok[g])
+                   ? h0[(b * dim + dS) * static_cast<int64_t>(N) + wk.prow * NPL + g]
+                   : 0.0f;
     wk.template walk<true>(0, L, h, sm);
-    if (h_last && d0 + wk.j < dim) {
+    if (h_last && row_ok) {
 #pragma unroll
         for (int g = 0; g < NPL; ++g)
             if (wk.nok[g])
@@ -47,7 +54,7 @@ hipError_t launch_typed(const ScanArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(64 * W), 0, stream,
                        static_cast<const T *>(a.u), static_cast<const T *>(a.delta),
                        a.delta_bias, a.A, static_cast<const T *>(a.B),
-                       static_cast<const T *>(a.C), a.D, static_cast<const T *>(a.z),
+                       static_cast<const T *>(a.C), a.D, static_cast<const T *>(a.z), a.h0,
                        static_cast<T *>(a.y), a.h_last, a.L, static_cast<int>(a.dim),
                        static_cast<int>(a.N), groups);
     return hipGetLastError();

@@ -14,8 +14,9 @@
 //      scan_core.h), giving h_loc, and forms P = exp(A * sum dl) in log space
 //      ("Mamba状态空间模型的硬件感知推理优化" (ybb.press) section 6.2);
 //   2. waits for the inclusive state of segment k-1 (the true state at its
-//      end), which is its incoming state h_in, and publishes its own
-//      inclusive state P h_in + h_loc;
+//      end), which is its incoming state h_in (the caller's initial state for
+//      the first segment), and publishes its own inclusive state
+//      P h_in + h_loc;
 //   3. walks its segment again from h_in, now forming y.
 //
 // Steps 1 and 3 -- all of the exponentials -- run in parallel over every
@@ -76,8 +77,8 @@ __global__ __launch_bounds__(64 * W) void scan_lookback_kernel(
     const T *__restrict__ u, const T *__restrict__ delta,
     const float *__restrict__ delta_bias, const float *__restrict__ A,
     const T *__restrict__ Bm, const T *__restrict__ Cm,
-    const float *__restrict__ Dskip, const T *__restrict__ z, T *__restrict__ y,
-    float *__restrict__ h_last, int64_t L, int dim, int N, int groups_per_batch,
+    const float *__restrict__ Dskip, const T *__restrict__ z, const float *h0, T *__restrict__ y,
+    float *h_last, int64_t L, int dim, int N, int groups_per_batch,
     int total_groups, int64_t seg_len, int nseg, Scratch s) {
     constexpr int kSlots = 4 * W * NPL * kCh;
     __shared__ core::Smem<W> sm;
@@ -112,9 +113,20 @@ __global__ __launch_bounds__(64 * W) void scan_lookback_kernel(
     auto inc = [&](int seg) {
         return s.pay + (static_cast<int64_t>(seg) * total_groups + gidx) * kSlots;
     };
+    // The first segment starts from the caller's initial state (lanes of
+    // channels past the last one mirror the last channel, whose y their
+    // owners store again, so they take its initial state).  When h0 is the
+    // h_last buffer, the write of h_last by the last segment comes after this
+    // read: it waits for the chain of inclusive states that this segment
+    // starts once it has read h0.
     float h_in[NPL];
+    const bool row_ok = d0 + wk.j < dim;
+    const int dS = min(d0 + wk.j, dim - 1);
 #pragma unroll
-    for (int g = 0; g < NPL; ++g) h_in[g] = 0.0f;
+    for (int g = 0; g < NPL; ++g)
+        h_in[g] = (k == 0 && h0 && wk.nok[g])
+                      ? h0[(b * dim + dS) * static_cast<int64_t>(N) + wk.prow * NPL + g]
+                      : 0.0f;
     if (k > 0) {
         if (tid == 0) {
             const uint32_t *f = s.flags + static_cast<int64_t>(k - 1) * total_groups + gidx;
@@ -148,7 +160,7 @@ __global__ __launch_bounds__(64 * W) void scan_lookback_kernel(
 #pragma unroll
     for (int g = 0; g < NPL; ++g) h[g] = h_in[g];
     wk.template walk<true>(t_begin, t_end, h, sm);
-    if (k == nseg - 1 && h_last && d0 + wk.j < dim) {
+    if (k == nseg - 1 && h_last && row_ok) {
 #pragma unroll
         for (int g = 0; g < NPL; ++g)
             if (wk.nok[g])
@@ -212,7 +224,7 @@ hipError_t launch_typed(const ScanArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(items)), dim3(64 * W), 0, stream,
                            static_cast<const T *>(a.u), static_cast<const T *>(a.delta),
                            a.delta_bias, a.A, static_cast<const T *>(a.B),
-                           static_cast<const T *>(a.C), a.D, static_cast<const T *>(a.z),
+                           static_cast<const T *>(a.C), a.D, static_cast<const T *>(a.z), a.h0,
                            static_cast<T *>(a.y), a.h_last, a.L, static_cast<int>(a.dim),
                            static_cast<int>(a.N), p.groups_per_batch, p.total_groups, p.seg_len,
                            p.nseg, s);

@@ -23,8 +23,8 @@ __global__ __launch_bounds__(256) void scan_rowserial_kernel(
     const T *__restrict__ u, const T *__restrict__ delta,
     const float *__restrict__ delta_bias, const float *__restrict__ A,
     const T *__restrict__ B, const T *__restrict__ C,
-    const float *__restrict__ Dskip, const T *__restrict__ z, T *__restrict__ y,
-    float *__restrict__ h_last, int64_t batch, int64_t L, int64_t dim, int N) {
+    const float *__restrict__ Dskip, const T *__restrict__ z, const float *h0, T *__restrict__ y,
+    float *h_last, int64_t batch, int64_t L, int64_t dim, int N) {
     const int64_t row = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (row >= batch * dim) return;
     const int64_t b = row / dim;
@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void scan_rowserial_kernel(
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
         A2[n] = n < N ? A[d * N + n] * kLog2e : 0.0f;   // exp(x) = 2^(x log2 e)
-        h[n] = 0.0f;
+        h[n] = (h0 && n < N) ? h0[row * N + n] : 0.0f;
     }
     const float bias = delta_bias ? delta_bias[d] : 0.0f;
     const float skip = Dskip ? Dskip[d] : 0.0f;
@@ -76,7 +76,7 @@ hipError_t launch_typed(const ScanArgs &a, hipStream_t stream) {
                        dim3(block), 0, stream, static_cast<const T *>(a.u),
                        static_cast<const T *>(a.delta), a.delta_bias, a.A,
                        static_cast<const T *>(a.B), static_cast<const T *>(a.C), a.D,
-                       static_cast<const T *>(a.z), static_cast<T *>(a.y), a.h_last,
+                       static_cast<const T *>(a.z), a.h0, static_cast<T *>(a.y), a.h_last,
                        a.batch, a.L, a.dim, static_cast<int>(a.N));
     return hipGetLastError();
 }

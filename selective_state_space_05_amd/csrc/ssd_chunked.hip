@@ -24,8 +24,9 @@
 //      (x * weight)^T B over the chunk's steps, and the chunk's total log2
 //      decay;
 //   2. ssd_pass_kernel: walks the chunks of each (batch, head) in order,
-//      elementwise over the P x N state, replacing each chunk state by the
-//      state entering that chunk and writing h_last;
+//      elementwise over the P x N state and starting from the initial state
+//      (zero unless given), replacing each chunk state by the state entering
+//      that chunk and writing h_last;
 //   3. ssd_output_kernel: the outputs, computed transposed
 //      (Y^T = X^T M^T + H C^T) so that each lane owns one step t: the decay
 //      factors become per-lane scalars and each lane stores four consecutive
@@ -132,25 +133,46 @@ __device__ __forceinline__ Run decode_run(const Geom &g, int runs_per_chunk, int
 // ---------------------------------------------------------------------------
 // 1. chunk states
 // ---------------------------------------------------------------------------
+// Threads of the chunk-state kernel: eight waves (two per SIMD, so one
+// wave's matrix-core work overlaps the other's staging) when the chunk has
+// enough steps to give each thread a unit of x.
+template <int Q>
+constexpr int state_threads() { return Q >= 128 ? 512 : 256; }
+
+// Row pitches (elements) of the transposed tiles.  B^T rows are read as
+// 16-byte pieces (pitch a multiple of 8).  The x tiles are written as 4-byte
+// step pairs by groups of 8 lanes whose rows lie 8 apart, and read as 8-byte
+// pieces: a pitch of Q + 4 (an odd number of 8-byte pieces) spreads those
+// 8 rows over 4 bank groups instead of 2.
 template <int Q, int NP>
 struct __align__(16) StateSmem {
-    static constexpr int XP = Q + 8;     // row pitch (elements) of the transposed tiles
+    static constexpr int XP = Q + 8;     // B^T row pitch
+    static constexpr int XQ = Q + 4;     // (x w)^T row pitch
     uint16_t BT[NP * XP];                // B^T of the chunk
-    uint16_t Xh[kPG * XP], Xl[kPG * XP]; // (x * weight)^T, bf16 high / low parts
-    float cum[Q], dl[Q], wsum[4];
+    uint16_t Xh[kPG * XQ], Xl[kPG * XQ]; // (x * weight)^T, bf16 high / low parts
+    float cum[Q], dl[Q], wsum[8];
 };
 
-// x rows of one item, prefetched into registers: unit u of this thread covers
-// steps 2 s2, 2 s2 + 1 and head-dimension columns p8 .. p8 + 7.
-template <int Q>
+// Eight consecutive bf16 of an LDS row as two 8-byte reads (8-byte aligned).
+__device__ __forceinline__ bf8 lds_read8(const uint16_t *p) {
+    const uint2 a = *reinterpret_cast<const uint2 *>(p);
+    const uint2 b = *reinterpret_cast<const uint2 *>(p + 4);
+    return __builtin_bit_cast(bf8, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+// x rows of one item, prefetched into registers by NT threads: unit u of
+// this thread covers steps 2 s2, 2 s2 + 1 and head-dimension columns
+// p8 .. p8 + 7.
+template <int Q, int NT>
 struct XRegs {
-    static constexpr int U = (Q / 2) * (kPG / 8) / 256;
+    static constexpr int U = (Q / 2) * (kPG / 8) / NT;
+    static_assert(U >= 1 && U * NT == (Q / 2) * (kPG / 8), "every thread holds whole units");
     uint4 v[U][2];
     float dt;
 };
 
-template <int Q, bool VEC>
-__device__ __forceinline__ void load_x(XRegs<Q> &r, const uint16_t *x, const uint16_t *dt,
+template <int Q, int NT, bool VEC>
+__device__ __forceinline__ void load_x(XRegs<Q, NT> &r, const uint16_t *x, const uint16_t *dt,
                                        const Geom &g, const Run &run, int item) {
     const int tid = threadIdx.x;
     const int hh = run.h0 + item / g.npg, pbase = (item % g.npg) * kPG;
@@ -158,8 +180,8 @@ __device__ __forceinline__ void load_x(XRegs<Q> &r, const uint16_t *x, const uin
     const int rowX = g.H * g.P;
     const uint16_t *xg = x + run.b * g.L * static_cast<int64_t>(rowX) + hh * g.P + pbase;
 #pragma unroll
-    for (int k = 0; k < XRegs<Q>::U; ++k) {
-        const int u = tid + 256 * k;
+    for (int k = 0; k < XRegs<Q, NT>::U; ++k) {
+        const int u = tid + NT * k;
         const int s2 = 2 * (u / (kPG / 8)), p8 = (u % (kPG / 8)) * 8;
         r.v[k][0] = load_row8<VEC>(xg, t0 + s2, p8, g.L, g.P - pbase, rowX);
         r.v[k][1] = load_row8<VEC>(xg, t0 + s2 + 1, p8, g.L, g.P - pbase, rowX);
@@ -169,7 +191,8 @@ __device__ __forceinline__ void load_x(XRegs<Q> &r, const uint16_t *x, const uin
 }
 
 // dl and the inclusive sum of the log2 decay over the chunk's Q steps from a
-// prefetched raw dt value (thread s < Q holds step s).  Ends with a barrier.
+// prefetched raw dt value (thread s < Q holds step s; s_wsum holds one float
+// per wave of the workgroup).  Ends with a barrier.
 template <int Q>
 __device__ void chunk_decay_from(float dr, int t0, int L, float A2, float bias,
                                  float *s_cum, float *s_dl, float *s_wsum) {
@@ -199,13 +222,18 @@ __device__ void chunk_decay_from(float dr, int t0, int L, float A2, float bias,
 }
 
 template <int Q, int NP, bool VEC>
-__global__ __launch_bounds__(256) void ssd_state_kernel(
+__global__ __launch_bounds__(state_threads<Q>()) void ssd_state_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt,
     const float *__restrict__ dt_bias, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, float *__restrict__ S, float *__restrict__ ce, Geom g,
     int runs_per_chunk, int heads_per_run) {
     using Sm = StateSmem<Q, NP>;
-    constexpr int XP = Sm::XP;
+    constexpr int XP = Sm::XP, XQ = Sm::XQ;
+    constexpr int NT = state_threads<Q>();
+    constexpr int kWaves = NT / 64;
+    // output tiles of 32 x 32: eight waves take one each (pt = wave & 1,
+    // nt = wave / 2), four waves take both head-dimension tiles of one nt
+    constexpr int kPtPerWave = kWaves == 8 ? 1 : 2;
     __shared__ Sm sm;
     const int tid = threadIdx.x;
     // wave index as a scalar, so control flow that depends on it stays uniform
@@ -216,10 +244,10 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(
     const int rowBC = g.G * g.N;
     const uint16_t *Bg = Bm + run.b * g.L * static_cast<int64_t>(rowBC) + run.grp * g.N;
 
-    XRegs<Q> xr;
-    load_x<Q, VEC>(xr, x, dt, g, run, 0);
+    XRegs<Q, NT> xr;
+    load_x<Q, NT, VEC>(xr, x, dt, g, run, 0);
     // B^T of the chunk, exact bf16 values re-packed as step pairs
-    for (int u = tid; u < (Q / 2) * (NP / 8); u += 256) {
+    for (int u = tid; u < (Q / 2) * (NP / 8); u += NT) {
         const int s2 = 2 * (u / (NP / 8)), n8 = (u % (NP / 8)) * 8;
         const uint4 v0 = load_row8<VEC>(Bg, t0 + s2, n8, g.L, g.N, rowBC);
         const uint4 v1 = load_row8<VEC>(Bg, t0 + s2 + 1, n8, g.L, g.N, rowBC);
@@ -230,7 +258,8 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(
             *reinterpret_cast<uint32_t *>(&sm.BT[(n8 + 2 * r + 1) * XP + s2]) = (a[r] >> 16) | (e[r] & 0xffff0000u);
         }
     }
-    const int nt = wave;                // this wave's 32-wide tile of the state index
+    const int nt = kWaves == 8 ? wave >> 1 : wave;     // 32-wide tile of the state index
+    const int pt0 = kWaves == 8 ? wave & 1 : 0;        // first 32-wide head-dimension tile
 #pragma unroll 1
     for (int item = 0; item < run.items; ++item) {
         const int hh = run.h0 + item / g.npg, pbase = (item % g.npg) * kPG;
@@ -243,8 +272,8 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(
         const float cum_end = sm.cum[Q - 1];
         // (x * w)^T with w_s = 2^(cum_end - cum_s) dl_s, split into bf16 parts
 #pragma unroll
-        for (int k = 0; k < XRegs<Q>::U; ++k) {
-            const int u = tid + 256 * k;
+        for (int k = 0; k < XRegs<Q, NT>::U; ++k) {
+            const int u = tid + NT * k;
             const int s2 = 2 * (u / (kPG / 8)), p8 = (u % (kPG / 8)) * 8;
             const float w0 = fast_exp2(cum_end - sm.cum[s2]) * sm.dl[s2];
             const float w1 = fast_exp2(cum_end - sm.cum[s2 + 1]) * sm.dl[s2 + 1];
@@ -254,29 +283,32 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(
             for (int r = 0; r < 4; ++r) {
                 uint32_t hi, lo;
                 split2(bits_lo(a[r]) * w0, bits_lo(e[r]) * w1, hi, lo);
-                *reinterpret_cast<uint32_t *>(&sm.Xh[(p8 + 2 * r) * XP + s2]) = hi;
-                *reinterpret_cast<uint32_t *>(&sm.Xl[(p8 + 2 * r) * XP + s2]) = lo;
+                *reinterpret_cast<uint32_t *>(&sm.Xh[(p8 + 2 * r) * XQ + s2]) = hi;
+                *reinterpret_cast<uint32_t *>(&sm.Xl[(p8 + 2 * r) * XQ + s2]) = lo;
                 split2(bits_hi(a[r]) * w0, bits_hi(e[r]) * w1, hi, lo);
-                *reinterpret_cast<uint32_t *>(&sm.Xh[(p8 + 2 * r + 1) * XP + s2]) = hi;
-                *reinterpret_cast<uint32_t *>(&sm.Xl[(p8 + 2 * r + 1) * XP + s2]) = lo;
+                *reinterpret_cast<uint32_t *>(&sm.Xh[(p8 + 2 * r + 1) * XQ + s2]) = hi;
+                *reinterpret_cast<uint32_t *>(&sm.Xl[(p8 + 2 * r + 1) * XQ + s2]) = lo;
             }
         }
         __syncthreads();
         // next item's x (the last item re-reads its own rows; unused)
-        load_x<Q, VEC>(xr, x, dt, g, run, item + 1 < run.items ? item + 1 : item);
+        load_x<Q, NT, VEC>(xr, x, dt, g, run, item + 1 < run.items ? item + 1 : item);
         // S[p][n] = sum_s (x w)^T[p][s] B^T[n][s]: A rows p, B operand columns n
-        f16x acc[2] = {zero16(), zero16()};
+        f16x acc[kPtPerWave];
+#pragma unroll
+        for (int i = 0; i < kPtPerWave; ++i) acc[i] = zero16();
         if (nt * 32 < NP) {
 #pragma unroll 2
             for (int kq = 0; kq < Q / 16; ++kq) {
                 const int s8 = 16 * kq + 8 * half;
                 const bf8 bb = *reinterpret_cast<const bf8 *>(&sm.BT[(nt * 32 + l32) * XP + s8]);
 #pragma unroll
-                for (int pt = 0; pt < 2; ++pt) {
-                    const bf8 ah = *reinterpret_cast<const bf8 *>(&sm.Xh[(pt * 32 + l32) * XP + s8]);
-                    const bf8 al = *reinterpret_cast<const bf8 *>(&sm.Xl[(pt * 32 + l32) * XP + s8]);
-                    acc[pt] = mfma(ah, bb, acc[pt]);
-                    acc[pt] = mfma(al, bb, acc[pt]);
+                for (int i = 0; i < kPtPerWave; ++i) {
+                    const int pt = pt0 + i;
+                    const bf8 ah = lds_read8(&sm.Xh[(pt * 32 + l32) * XQ + s8]);
+                    const bf8 al = lds_read8(&sm.Xl[(pt * 32 + l32) * XQ + s8]);
+                    acc[i] = mfma(ah, bb, acc[i]);
+                    acc[i] = mfma(al, bb, acc[i]);
                 }
             }
             // lane (column n, half) holds S[p(v)][n], p(v) = 8 (v / 4) + 4 half + v % 4
@@ -284,11 +316,11 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(
             if (n < g.N) {
                 float *Sg = S + ((run.b * g.nch + run.c) * g.H + hh) * static_cast<int64_t>(g.P) * g.N;
 #pragma unroll
-                for (int pt = 0; pt < 2; ++pt)
+                for (int i = 0; i < kPtPerWave; ++i)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        const int p = pt * 32 + 8 * (v / 4) + 4 * half + (v % 4);
-                        if (p < pcols) Sg[static_cast<int64_t>(pbase + p) * g.N + n] = acc[pt][v];
+                        const int p = (pt0 + i) * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+                        if (p < pcols) Sg[static_cast<int64_t>(pbase + p) * g.N + n] = acc[i][v];
                     }
             }
         }
@@ -301,14 +333,14 @@ __global__ __launch_bounds__(256) void ssd_state_kernel(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void ssd_pass_kernel(float *__restrict__ S,
                                                        const float *__restrict__ ce,
-                                                       float *__restrict__ h_last, Geom g,
+                                                       const float *h0, float *h_last, Geom g,
                                                        int blocks_per_head) {
     const int64_t PN = static_cast<int64_t>(g.P) * g.N;
     const int64_t bh = blockIdx.x / blocks_per_head;         // batch * H + head
     const int64_t e = static_cast<int64_t>(blockIdx.x % blocks_per_head) * 256 + threadIdx.x;
     if (e >= PN) return;
     const int64_t b = bh / g.H, hh = bh % g.H;
-    float h = 0.0f;
+    float h = h0 ? h0[bh * PN + e] : 0.0f;   // state entering the first chunk
     constexpr int U = 4;    // chunks whose states are loaded ahead of the chain
     int c = 0;
     for (; c + U <= g.nch; c += U) {
@@ -342,7 +374,7 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(float *__restrict__ S,
 template <int Q, int NP>
 struct __align__(16) OutSmem {
     static constexpr int BP = NP + 8;    // B row pitch (elements)
-    static constexpr int XP = Q + 8;     // x^T row pitch
+    static constexpr int XP = Q + 4;     // x^T row pitch (8-byte reads; see StateSmem)
     static constexpr int HP = NP + 8;    // h_in row pitch
     uint16_t B[Q * BP];                  // B of the chunk, exact bf16
     uint16_t XT[kPG * XP];               // x^T, exact bf16
@@ -402,8 +434,8 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
     const uint16_t *Bg = Bm + run.b * g.L * static_cast<int64_t>(rowBC) + run.grp * g.N;
     const uint16_t *Cg = Cm + run.b * g.L * static_cast<int64_t>(rowBC) + run.grp * g.N;
 
-    XRegs<Q> xr;
-    load_x<Q, VEC>(xr, x, dt, g, run, 0);
+    XRegs<Q, 256> xr;
+    load_x<Q, 256, VEC>(xr, x, dt, g, run, 0);
     // B of the chunk (rows s), shared by every head of the run
     for (int u = tid; u < Q * (NP / 8); u += 256) {
         const int s = u / (NP / 8), n8 = (u % (NP / 8)) * 8;
@@ -428,7 +460,6 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
         const int hh = run.h0 + item / g.npg, pbase = (item % g.npg) * kPG;
         const int pcols = g.P - pbase;
         const float skip = Dskip ? Dskip[hh] : 0.0f;
-        const uint16_t *xg = x + run.b * g.L * static_cast<int64_t>(rowX) + hh * g.P + pbase;
         uint16_t *yg = y + run.b * g.L * static_cast<int64_t>(rowX) + hh * g.P + pbase;
         __syncthreads();   // the previous item's LDS reads are done
         // state entering the chunk; its loads overlap the decay scan
@@ -439,7 +470,7 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
         if (tid < Q) sm.fs[tid] = fast_exp2(sm.cum[tid | 31] - sm.cum[tid]) * sm.dl[tid];
         // x^T as step pairs; h_in split into bf16 parts
 #pragma unroll
-        for (int k = 0; k < XRegs<Q>::U; ++k) {
+        for (int k = 0; k < XRegs<Q, 256>::U; ++k) {
             const int u = tid + 256 * k;
             const int s2 = 2 * (u / (kPG / 8)), p8 = (u % (kPG / 8)) * 8;
             const uint4 v0 = xr.v[k][0], v1 = xr.v[k][1];
@@ -461,7 +492,7 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
         }
         __syncthreads();
         // next item's x (the last item re-reads its own; unused)
-        load_x<Q, VEC>(xr, x, dt, g, run, item + 1 < run.items ? item + 1 : item);
+        load_x<Q, 256, VEC>(xr, x, dt, g, run, item + 1 < run.items ? item + 1 : item);
         if (!active) continue;
 
         // Output tiles Y^T[p][t]: lane (column t, half) holds rows
@@ -474,17 +505,35 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
             f16x yd[2] = {zero16(), zero16()};
 #pragma unroll 1
             for (int sb = 0; sb <= tb; ++sb) {
+                // The block's LDS operands are all read up front, so their
+                // latencies overlap one another and the matrix-core work
+                // instead of being exposed one product at a time.
+                bf8 ab[KN];
+#pragma unroll
+                for (int jn = 0; jn < KN; ++jn)
+                    ab[jn] = *reinterpret_cast<const bf8 *>(&sm.B[(sb * 32 + l32) * BP + 16 * jn + 8 * half]);
+                // x^T operands of the block: A operand row p reads x at
+                // s(8 kk + 0..3) and s(8 kk + 4..7), s(v) as below
+                bf8 xa[2][2];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int pt = 0; pt < 2; ++pt) {
+                        const uint16_t *xp = &sm.XT[(pt * 32 + l32) * XP + sb * 32 + 16 * kk + 4 * half];
+                        const uint2 lo4 = *reinterpret_cast<const uint2 *>(xp);
+                        const uint2 hi4 = *reinterpret_cast<const uint2 *>(xp + 8);
+                        xa[kk][pt] = __builtin_bit_cast(bf8, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+                    }
                 // G'[s][t] = B_s . C_t: A operand rows s of B
                 f16x gacc = zero16();
 #pragma unroll
-                for (int jn = 0; jn < KN; ++jn) {
-                    const bf8 ab = *reinterpret_cast<const bf8 *>(&sm.B[(sb * 32 + l32) * BP + 16 * jn + 8 * half]);
-                    gacc = mfma(ab, cf[which][jn], gacc);
-                }
+                for (int jn = 0; jn < KN; ++jn) gacc = mfma(ab[jn], cf[which][jn], gacc);
                 // M[t][s] = G'[s][t] 2^(cum_t - cum_s) dl_s for s <= t (else 0),
-                // at s(v) = 32 sb + 8 (v / 4) + 4 half + v % 4.  Off the diagonal
-                // block the decay factors as 2^(cum_t - cb) fs[s], cb the cum at
-                // the end of block sb, both factors <= 1.
+                // at s(v) = 32 sb + 8 (v / 4) + 4 half + v % 4, plus the skip
+                // weight D on the diagonal s = t, so the product with x^T also
+                // forms D x_t.  Off the diagonal block the decay factors as
+                // 2^(cum_t - cb) fs[s], cb the cum at the end of block sb, both
+                // factors <= 1.
                 float mval[16];
                 if (sb < tb) {
                     const float et = fast_exp2(cum_t - sm.cum[sb * 32 + 31]);
@@ -496,31 +545,25 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
                     for (int v = 0; v < 16; ++v) {
                         const int sl = sb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
                         const float mv = gacc[v] * fast_exp2(cum_t - sm.cum[sl]) * sm.dl[sl];
-                        mval[v] = sl <= tl ? mv : 0.0f;
+                        mval[v] = sl < tl ? mv : (sl == tl ? mv + skip : 0.0f);
                     }
                 }
                 uint32_t mh[8], ml[8];
 #pragma unroll
                 for (int v = 0; v < 16; v += 2) split2(mval[v], mval[v + 1], mh[v / 2], ml[v / 2]);
-                // Y^T[p][t] += sum_s x^T[p][s] M[t][s], K slot order s(v) as above:
-                // A operand row p reads x at s(8 kk + 0..3) and s(8 kk + 4..7)
+                // Y^T[p][t] += sum_s x^T[p][s] M[t][s], K slot order s(v) as above
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     const bf8 bh = __builtin_bit_cast(bf8, make_uint4(mh[4 * kk], mh[4 * kk + 1], mh[4 * kk + 2], mh[4 * kk + 3]));
                     const bf8 bl = __builtin_bit_cast(bf8, make_uint4(ml[4 * kk], ml[4 * kk + 1], ml[4 * kk + 2], ml[4 * kk + 3]));
-                    const int sA = sb * 32 + 16 * kk + 4 * half;
 #pragma unroll
                     for (int pt = 0; pt < 2; ++pt) {
-                        const uint16_t *xp = &sm.XT[(pt * 32 + l32) * XP];
-                        const uint2 lo4 = *reinterpret_cast<const uint2 *>(xp + sA);
-                        const uint2 hi4 = *reinterpret_cast<const uint2 *>(xp + sA + 8);
-                        const bf8 xa = __builtin_bit_cast(bf8, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
-                        yd[pt] = mfma(xa, bh, yd[pt]);
-                        yd[pt] = mfma(xa, bl, yd[pt]);
+                        yd[pt] = mfma(xa[kk][pt], bh, yd[pt]);
+                        yd[pt] = mfma(xa[kk][pt], bl, yd[pt]);
                     }
                 }
             }
-            // Y_off^T[p][t] = sum_n h_in[p][n] C_t[n]; y = Y_diag + 2^cum_t Y_off + D x
+            // Y_off^T[p][t] = sum_n h_in[p][n] C_t[n]; y = Y_diag (with D x) + 2^cum_t Y_off
             const float et = fast_exp2(cum_t);
             const int t = t0 + tl;
 #pragma unroll
@@ -541,26 +584,17 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
                     for (int q4 = 0; q4 < 4; ++q4) {
                         // four consecutive p = pt*32 + 8 q4 + 4 half + 0..3
                         const int p = pt * 32 + 8 * q4 + 4 * half;
-                        if (VEC) {
-                            if (p < pcols) {
-                                const uint2 xv = *reinterpret_cast<const uint2 *>(xg + row + p);
-                                const float xs[4] = {bits_lo(xv.x), bits_hi(xv.x), bits_lo(xv.y), bits_hi(xv.y)};
-                                float yv[4];
+                        float yv[4];
 #pragma unroll
-                                for (int k = 0; k < 4; ++k)
-                                    yv[k] = fmaf(skip, xs[k], fmaf(et, yo[4 * q4 + k], yd[pt][4 * q4 + k]));
+                        for (int k = 0; k < 4; ++k) yv[k] = fmaf(et, yo[4 * q4 + k], yd[pt][4 * q4 + k]);
+                        if (VEC) {
+                            if (p < pcols)
                                 *reinterpret_cast<uint2 *>(yg + row + p) =
                                     make_uint2(pack2(yv[0], yv[1]), pack2(yv[2], yv[3]));
-                            }
                         } else {
 #pragma unroll
-                            for (int k = 0; k < 4; ++k) {
-                                if (p + k < pcols) {
-                                    const float xs = bf16_to_f32(xg[row + p + k]);
-                                    yg[row + p + k] = f32_to_bf16(
-                                        fmaf(skip, xs, fmaf(et, yo[4 * q4 + k], yd[pt][4 * q4 + k])));
-                                }
-                            }
+                            for (int k = 0; k < 4; ++k)
+                                if (p + k < pcols) yg[row + p + k] = f32_to_bf16(yv[k]);
                         }
                     }
                 }
@@ -613,17 +647,18 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     const auto *C = static_cast<const uint16_t *>(a.C);
     const int64_t grid = a.batch * g.nch * rpc;
     const bool vec = vecB && vecX;
+    constexpr int nts = state_threads<Q>();
     if (vec)
-        hipLaunchKernelGGL((ssd_state_kernel<Q, NP, true>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
+        hipLaunchKernelGGL((ssd_state_kernel<Q, NP, true>), dim3(static_cast<uint32_t>(grid)), dim3(nts), 0,
                            stream, x, dt, a.dt_bias, a.A, B, S, ce, g, rpc, hpr);
     else
-        hipLaunchKernelGGL((ssd_state_kernel<Q, NP, false>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
+        hipLaunchKernelGGL((ssd_state_kernel<Q, NP, false>), dim3(static_cast<uint32_t>(grid)), dim3(nts), 0,
                            stream, x, dt, a.dt_bias, a.A, B, S, ce, g, rpc, hpr);
     e = hipGetLastError();
     if (e == hipSuccess) {
         const int bph = static_cast<int>((PN + 255) / 256);
         hipLaunchKernelGGL(ssd_pass_kernel, dim3(static_cast<uint32_t>(a.batch * a.H * bph)),
-                           dim3(256), 0, stream, S, ce, a.h_last, g, bph);
+                           dim3(256), 0, stream, S, ce, a.h0, a.h_last, g, bph);
         e = hipGetLastError();
     }
     if (e == hipSuccess) {

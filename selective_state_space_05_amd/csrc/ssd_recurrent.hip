@@ -21,8 +21,8 @@ __global__ __launch_bounds__(64) void ssd_recurrent_kernel(
     const T *__restrict__ x, const T *__restrict__ dt,
     const float *__restrict__ dt_bias, const float *__restrict__ A,
     const T *__restrict__ B, const T *__restrict__ C,
-    const float *__restrict__ Dskip, T *__restrict__ y,
-    float *__restrict__ h_last, int64_t L, int H, int P, int N, int G) {
+    const float *__restrict__ Dskip, const float *h0, T *__restrict__ y,
+    float *h_last, int64_t L, int H, int P, int N, int G) {
     // grid: x = p-tiles of 64, y = head, z = batch
     const int p = blockIdx.x * 64 + threadIdx.x;
     const int h = blockIdx.y;
@@ -30,9 +30,10 @@ __global__ __launch_bounds__(64) void ssd_recurrent_kernel(
     const int g = h / (H / G);
     const bool live = p < P;
 
+    const int64_t sbase = ((b * H + h) * static_cast<int64_t>(P) + p) * N;
     float S[NS];
 #pragma unroll
-    for (int n = 0; n < NS; ++n) S[n] = 0.0f;
+    for (int n = 0; n < NS; ++n) S[n] = (h0 && live && n < N) ? h0[sbase + n] : 0.0f;
     const float A2 = A[h] * kLog2e;
     const float bias = dt_bias ? dt_bias[h] : 0.0f;
     const float skip = Dskip ? Dskip[h] : 0.0f;
@@ -55,10 +56,9 @@ __global__ __launch_bounds__(64) void ssd_recurrent_kernel(
         if (live) Io<T>::store(y, xi, fmaf(skip, xp, acc));
     }
     if (h_last && live) {
-        const int64_t base = ((b * H + h) * static_cast<int64_t>(P) + p) * N;
 #pragma unroll
         for (int n = 0; n < NS; ++n)
-            if (n < N) h_last[base + n] = S[n];
+            if (n < N) h_last[sbase + n] = S[n];
     }
 }
 
@@ -69,7 +69,7 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((ssd_recurrent_kernel<T, NS>), grid, dim3(64), 0, stream,
                        static_cast<const T *>(a.x), static_cast<const T *>(a.dt),
                        a.dt_bias, a.A, static_cast<const T *>(a.B),
-                       static_cast<const T *>(a.C), a.D, static_cast<T *>(a.y),
+                       static_cast<const T *>(a.C), a.D, a.h0, static_cast<T *>(a.y),
                        a.h_last, a.L, static_cast<int>(a.H), static_cast<int>(a.P),
                        static_cast<int>(a.N), static_cast<int>(a.G));
     return hipGetLastError();

@@ -1,0 +1,145 @@
+// state_update.hip -- one decode step of the selective scan: the recurrence
+// advanced by a single time step on a state kept between calls.
+//
+// Per batch b and channel d ("Mamba状态空间模型的硬件感知推理优化" (ybb.press)
+// sections 1 and 3.1: h_t = exp(A dl) h_{t-1} + dl B x_t, y = C.h + D x; the
+// tencentcloud.csdn.net article on Mamba, section 3: the SiLU gate; the
+// www.mhpq.cn essay, section 2.2: the zero-order-hold decay):
+//
+//   dl       = softplus(dt[b,d] + dt_bias[d])
+//   state[n] = exp(dl * A[d,n]) * state[n] + dl * B[b,n] * x[b,d]
+//   y[b,d]   = (sum_n C[b,n] * state[n] + D[d] * x[b,d]) * silu(z[b,d])
+//
+// The step reads and writes the whole float32 state once and does a handful
+// of operations per element, so it is bound by HBM bandwidth.  The layout
+// follows from that: a group of GS lanes owns one (b, d) row, each lane four
+// consecutive state elements moved as one 16-byte load and store, so a wave
+// streams 64 x 16 contiguous bytes of state; the output dot product is summed
+// across the group with lane shuffles.
+#include "device_math.h"
+#include "internal.h"
+
+namespace mssm {
+namespace {
+
+template <typename T> struct Quad;
+template <> struct Quad<float> {
+    // four consecutive elements at p (16-byte aligned)
+    __device__ __forceinline__ static float4 load(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+};
+template <> struct Quad<uint16_t> {
+    // four consecutive elements at p (8-byte aligned)
+    __device__ __forceinline__ static float4 load(const uint16_t *p) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(p);
+        return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                           __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+    }
+};
+
+// Elements n0 .. n0 + 3 of a row of length N; VEC: all four exist and the
+// row start is aligned for a vector load; otherwise missing ones read as 0.
+template <bool VEC, typename T>
+__device__ __forceinline__ float4 load4(const T *row, int n0, int N) {
+    if (VEC) return Quad<T>::load(row + n0);
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = n0 + k < N ? Io<T>::load(row, n0 + k) : 0.0f;
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+template <typename T, int GS, bool VEC>
+__global__ __launch_bounds__(256) void state_update_kernel(
+    float *__restrict__ state, const T *__restrict__ x, const T *__restrict__ dt,
+    const float *__restrict__ dt_bias, const float *__restrict__ A, const T *__restrict__ B,
+    const T *__restrict__ C, const float *__restrict__ Dskip, const T *__restrict__ z,
+    T *__restrict__ y, int64_t rows, int dim, int N) {
+    constexpr int kRows = 256 / GS;
+    const int q = threadIdx.x % GS;                      // quad of this lane
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * kRows + threadIdx.x / GS;
+    if (row >= rows) return;                             // whole groups leave together
+    const int64_t b = row / dim;
+    const int d = static_cast<int>(row - b * dim);
+    const int n0 = 4 * q;
+    const bool live = n0 < N;
+
+    const float xv = Io<T>::load(x, row);
+    const float dl = softplus(Io<T>::load(dt, row) + (dt_bias ? dt_bias[d] : 0.0f));
+    const float dx = dl * xv;
+    float acc = 0.0f;
+    if (live) {
+        float *srow = state + row * N;
+        const float4 h = load4<VEC>(srow, n0, N);
+        const float4 a = load4<VEC>(A + static_cast<int64_t>(d) * N, n0, N);
+        const float4 bq = load4<VEC>(B + b * N, n0, N);
+        const float4 cq = load4<VEC>(C + b * N, n0, N);
+        const float s = dl * kLog2e;
+        float4 hn;
+        hn.x = fmaf(fast_exp2(s * a.x), h.x, dx * bq.x);
+        hn.y = fmaf(fast_exp2(s * a.y), h.y, dx * bq.y);
+        hn.z = fmaf(fast_exp2(s * a.z), h.z, dx * bq.z);
+        hn.w = fmaf(fast_exp2(s * a.w), h.w, dx * bq.w);
+        acc = fmaf(cq.x, hn.x, fmaf(cq.y, hn.y, fmaf(cq.z, hn.z, cq.w * hn.w)));
+        if (VEC) {
+            *reinterpret_cast<float4 *>(srow + n0) = hn;
+        } else {
+            const float hv[4] = {hn.x, hn.y, hn.z, hn.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (n0 + k < N) srow[n0 + k] = hv[k];
+        }
+    }
+    // sum over the group's lanes (aligned runs of GS lanes of one wave)
+#pragma unroll
+    for (int m = GS / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, GS);
+    if (q == 0) {
+        float yv = fmaf(Dskip ? Dskip[d] : 0.0f, xv, acc);
+        if (z) yv *= silu(Io<T>::load(z, row));
+        Io<T>::store(y, row, yv);
+    }
+}
+
+template <typename T, int GS>
+hipError_t launch_gs(const StepArgs &a, hipStream_t stream) {
+    const int64_t rows = a.batch * a.dim;
+    constexpr int kRows = 256 / GS;
+    const int64_t grid = (rows + kRows - 1) / kRows;
+    // Vector path: every quad complete, rows of state / A / B / C aligned.
+    const int64_t bsz = a.io == IO_F32 ? 16 : 8;
+    auto al = [](const void *p, int64_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; };
+    const bool vec = a.N % 4 == 0 && al(a.state, 16) && al(a.A, 16) && al(a.B, bsz) && al(a.C, bsz);
+    auto kern = vec ? state_update_kernel<T, GS, true> : state_update_kernel<T, GS, false>;
+    hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream, a.state,
+                       static_cast<const T *>(a.x), static_cast<const T *>(a.dt), a.dt_bias, a.A,
+                       static_cast<const T *>(a.B), static_cast<const T *>(a.C), a.D,
+                       static_cast<const T *>(a.z), static_cast<T *>(a.y), rows,
+                       static_cast<int>(a.dim), static_cast<int>(a.N));
+    return hipGetLastError();
+}
+
+// Lanes per row: the quads of a row, rounded up to a power of two.
+template <typename T>
+hipError_t launch_typed(const StepArgs &a, hipStream_t stream) {
+    const int64_t quads = (a.N + 3) / 4;
+    if (quads <= 1) return launch_gs<T, 1>(a, stream);
+    if (quads <= 2) return launch_gs<T, 2>(a, stream);
+    if (quads <= 4) return launch_gs<T, 4>(a, stream);
+    if (quads <= 8) return launch_gs<T, 8>(a, stream);
+    return launch_gs<T, 16>(a, stream);
+}
+
+}  // namespace
+
+bool state_update_supported(const StepArgs &a) {
+    if (a.N < 1 || a.N > 64 || a.dim > (int64_t(1) << 31) - 1) return false;
+    const int64_t quads = (a.N + 3) / 4;
+    int gs = 1;
+    while (gs < quads) gs *= 2;
+    return (a.batch * a.dim + 256 / gs - 1) / (256 / gs) < (int64_t(1) << 31);
+}
+
+hipError_t launch_state_update(const StepArgs &a, hipStream_t stream) {
+    if (a.io == IO_F32) return launch_typed<float>(a, stream);
+    return launch_typed<uint16_t>(a, stream);
+}
+
+}  // namespace mssm

@@ -22,6 +22,12 @@ activations of bf16 problems):
     dt_bias       ~ U(-4, -2) per head
     theta         ~ U(0, ln 16)
 
+  decode step (one time step on a cached state): the selective-scan recipe
+  above with L = 1 (the length axis dropped), then from a second stream
+  (seed + 1) the state ~ N(0, 1) of shape (batch, dim, N).
+  initial states of the scans (``initial_state``): N(0, 1) float32 from
+  their own stream.
+
 The named workloads below carry the layer shapes the pages talk about (a
 Mamba-130M layer, a Mamba-2.8B layer, a million-step sequence, a Mamba-2
 layer); no dataset or trained weight is involved.
@@ -124,6 +130,41 @@ class SSDProblem:
         return dataclasses.replace(self, **kw)
 
 
+@dataclasses.dataclass(frozen=True)
+class StepProblem:
+    """One decode step: a batch of sequences advanced by one time step."""
+    name: str
+    batch: int
+    dim: int
+    dstate: int
+    io: str
+    bias: Optional[str]
+    gate: bool
+    skip: bool
+    seed: int
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.dim * self.dstate
+
+    @property
+    def io_bytes(self) -> int:
+        return 4 if self.io == "f32" else 2
+
+    def min_traffic_bytes(self) -> int:
+        """The state read and written once, every other operand once."""
+        s = self.io_bytes
+        state = 2 * 4 * self.batch * self.dim * self.dstate
+        act = (4 if self.gate else 3) * self.batch * self.dim * s
+        bc = 2 * self.batch * self.dstate * s
+        par = 4 * self.dim * self.dstate
+        par += 4 * self.dim * ((1 if self.skip else 0) + (1 if self.bias else 0))
+        return state + act + bc + par
+
+    def replace(self, **kw) -> "StepProblem":
+        return dataclasses.replace(self, **kw)
+
+
 # Named workloads.
 TINY = ScanProblem("tiny_f32", 1, 64, 8, 4, "f32", "scalar", False, True, 0)
 MAMBA_130M = ScanProblem("mamba130m_layer_f32", 2, 8192, 1536, 16, "f32",
@@ -135,8 +176,13 @@ MILLION = ScanProblem("million_step_bf16", 1, 1 << 20, 256, 16, "bf16",
 SSD_LAYER = SSDProblem("mamba2_ssd_layer_bf16", 2, 8192, 48, 64, 128, 1,
                        "bf16", 4)
 
+# a decode step of the Mamba-2.8B layer for 256 sequences: 84 MB of state
+DECODE_2_8B = StepProblem("mamba2.8b_decode_bf16", 256, 5120, 16, "bf16", "scalar",
+                          True, True, 12)
+
 SCAN_PROBLEMS = {p.name: p for p in (TINY, MAMBA_130M, MAMBA_2_8B, MILLION)}
 SSD_PROBLEMS = {SSD_LAYER.name: SSD_LAYER}
+STEP_PROBLEMS = {DECODE_2_8B.name: DECODE_2_8B}
 
 
 def scan_inputs(p: ScanProblem) -> dict:
@@ -195,3 +241,24 @@ def ssd_inputs(p: SSDProblem) -> dict:
     if p.io == "bf16":
         x, dt, B, C = (bf16_round(a) for a in (x, dt, B, C))
     return dict(x=x, dt=dt, dt_bias=bias, A=A, B=B, C=C, D=D)
+
+
+def initial_state(shape, seed: int) -> np.ndarray:
+    """A float32 N(0, 1) initial state of the given shape."""
+    return np.random.default_rng(seed).standard_normal(shape, dtype=np.float32)
+
+
+def step_inputs(p: StepProblem) -> dict:
+    """Draw the inputs of one decode step.
+
+    Keys: x, dt, z (batch, dim); B, C (batch, N); A (dim, N); dt_bias, D
+    (dim,); state (batch, dim, N) float32.  x, dt, B, C, z, A, D, dt_bias are
+    the selective-scan draws of the same problem with L = 1.
+    """
+    q = ScanProblem(p.name, p.batch, 1, p.dim, p.dstate, p.io, p.bias, p.gate, p.skip, p.seed)
+    d = scan_inputs(q)
+    sq = {k: (None if d[k] is None else np.ascontiguousarray(d[k][..., 0]))
+          for k in ("u", "delta", "B", "C", "z")}
+    return dict(x=sq["u"], dt=sq["delta"], dt_bias=d["delta_bias"], A=d["A"], B=sq["B"],
+                C=sq["C"], D=d["D"], z=sq["z"],
+                state=initial_state((p.batch, p.dim, p.dstate), p.seed + 1))

@@ -91,6 +91,35 @@ def ssd_call(L, batch=2, seqlen=64, H=4, P=8, N=16, G=1, chunk=0, io=0, param=0,
         _lib.DTypes(io, param), None)
 
 
+def scan_h0_call(L, batch=2, seqlen=64, dim=8, dstate=4, io=0, param=0, **ptrs):
+    p = dict(u=fake(1), delta=fake(2), delta_bias=fake(3), A=fake(4), B=fake(5),
+             C=fake(6), D=fake(7), z=fake(8), h0=fake(11), y=fake(9), h_last=fake(10))
+    p.update(ptrs)
+    return L.mssm_selective_scan_fwd_h0(
+        p["u"], p["delta"], p["delta_bias"], p["A"], p["B"], p["C"], p["D"],
+        p["z"], p["h0"], p["y"], p["h_last"], _lib.ScanDims(batch, seqlen, dim, dstate),
+        _lib.DTypes(io, param), None)
+
+
+def ssd_h0_call(L, batch=2, seqlen=64, H=4, P=8, N=16, G=1, chunk=0, io=0, param=0, **ptrs):
+    p = dict(x=fake(1), dt=fake(2), dt_bias=fake(3), A=fake(4), B=fake(5), C=fake(6),
+             D=fake(7), h0=fake(11), y=fake(9), h_last=fake(10))
+    p.update(ptrs)
+    return L.mssm_ssd_scalar_fwd_h0(
+        p["x"], p["dt"], p["dt_bias"], p["A"], p["B"], p["C"], p["D"], p["h0"], p["y"],
+        p["h_last"], _lib.SSDDims(batch, seqlen, H, P, N, G, chunk),
+        _lib.DTypes(io, param), None)
+
+
+def step_call(L, batch=2, dim=8, dstate=4, io=0, param=0, **ptrs):
+    p = dict(state=fake(10), x=fake(1), dt=fake(2), dt_bias=fake(3), A=fake(4), B=fake(5),
+             C=fake(6), D=fake(7), z=fake(8), y=fake(9))
+    p.update(ptrs)
+    return L.mssm_selective_state_update(
+        p["state"], p["x"], p["dt"], p["dt_bias"], p["A"], p["B"], p["C"], p["D"], p["z"],
+        p["y"], _lib.StepDims(batch, dim, dstate), _lib.DTypes(io, param), None)
+
+
 @pytest.mark.parametrize("name", ["u", "delta", "A", "B", "C", "y"])
 def test_scan_null_required_pointer(L, name):
     assert scan_call(L, **{name: None}) == _lib.MSSM_ERR_INVALID_ARG
@@ -148,6 +177,75 @@ def test_scan_empty_problem_is_noop(L):
     # L == 0 without h_last: nothing to write, no launch
     assert scan_call(L, seqlen=0, u=None, delta=None, B=None, C=None, y=None,
                      h_last=None) == _lib.MSSM_OK
+
+
+def test_scan_h0_overlapping_an_output(L):
+    # h0 is an input: no output may overlap it ...
+    assert scan_h0_call(L, h0=fake(20), y=fake(20) + 4) == _lib.MSSM_ERR_INVALID_ARG
+    assert b"h0" in L.mssm_last_error()
+    # ... except h_last being the very same buffer (state advanced in place)
+    assert scan_h0_call(L, h0=fake(20), h_last=fake(20) + 16) == _lib.MSSM_ERR_INVALID_ARG
+    prev = L.mssm_force_variant(_lib.VARIANT_SSD_RECURRENT)
+    try:
+        st = scan_h0_call(L, h0=fake(20), h_last=fake(20))
+    finally:
+        L.mssm_force_variant(prev)
+    assert st == _lib.MSSM_ERR_UNSUPPORTED      # validation passed; stopped at the variant
+    assert b"variant" in L.mssm_last_error()
+
+
+def test_scan_h0_validation_matches_scan(L):
+    for kw in (dict(u=None), dict(dstate=0), dict(batch=-1), dict(io=3)):
+        assert scan_h0_call(L, **kw) == scan_call(L, **kw) == _lib.MSSM_ERR_INVALID_ARG
+    assert scan_h0_call(L, dstate=_lib.MAX_DSTATE + 1) == _lib.MSSM_ERR_UNSUPPORTED
+    assert scan_h0_call(L, batch=0) == _lib.MSSM_OK
+    # L == 0 with the state kept in place: nothing to copy, no launch
+    assert scan_h0_call(L, seqlen=0, u=None, delta=None, B=None, C=None, y=None,
+                        h0=fake(20), h_last=fake(20)) == _lib.MSSM_OK
+
+
+def test_ssd_h0_overlapping_an_output(L):
+    assert ssd_h0_call(L, h0=fake(20), y=fake(20) + 2) == _lib.MSSM_ERR_INVALID_ARG
+    assert ssd_h0_call(L, h0=fake(20), h_last=fake(20) + 4) == _lib.MSSM_ERR_INVALID_ARG
+    prev = L.mssm_force_variant(_lib.VARIANT_CHUNKED)
+    try:
+        st = ssd_h0_call(L, h0=fake(20), h_last=fake(20))
+    finally:
+        L.mssm_force_variant(prev)
+    assert st == _lib.MSSM_ERR_UNSUPPORTED
+    assert b"variant" in L.mssm_last_error()
+    assert ssd_h0_call(L, seqlen=0, h0=fake(20), h_last=fake(20)) == _lib.MSSM_OK
+
+
+@pytest.mark.parametrize("name", ["state", "x", "dt", "A", "B", "C", "y"])
+def test_step_null_required_pointer(L, name):
+    assert step_call(L, **{name: None}) == _lib.MSSM_ERR_INVALID_ARG
+    assert name.encode() in L.mssm_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), 1), (dict(dim=-1), 1), (dict(dstate=0), 1), (dict(io=4), 1),
+    (dict(param=1), 2), (dict(dstate=_lib.MAX_DSTATE + 1), 2),
+    (dict(batch=1 << 40, dim=1 << 30), 1)])
+def test_step_validation(L, kw, status):
+    assert step_call(L, **kw) == status
+    assert L.mssm_last_error()
+
+
+@pytest.mark.parametrize("out,inp", [("y", "x"), ("y", "z"), ("state", "A"), ("state", "B"),
+                                     ("state", "dt"), ("y", "D")])
+def test_step_output_aliasing_input(L, out, inp):
+    assert step_call(L, **{out: fake(20), inp: fake(20) + 2}) == _lib.MSSM_ERR_INVALID_ARG
+    assert b"overlaps" in L.mssm_last_error()
+
+
+def test_step_y_overlapping_state(L):
+    assert step_call(L, y=fake(20), state=fake(20) + 8) == _lib.MSSM_ERR_INVALID_ARG
+
+
+def test_step_empty_problem_is_noop(L):
+    assert step_call(L, batch=0) == _lib.MSSM_OK
+    assert step_call(L, dim=0, state=None, x=None, y=None) == _lib.MSSM_OK
 
 
 @pytest.mark.parametrize("name", ["x", "dt", "A", "B", "C", "y"])
