@@ -142,16 +142,21 @@ void oracle_selective_scan_f64(int64_t batch, int64_t L, int64_t D, int64_t N,
  *       a  = exp(dl * A[h])
  *       S[p][n] = a * S[p][n] + dl * x[b,t,h,p] * B[b,t,g,n]
  *       y[b,t,h,p] = sum_n C[b,t,g,n] * S[p][n] + Dskip[h] * x[b,t,h,p]
+ *       if z: y[b,t,h,p] *= silu(z[b,t,h,p])
  *   h_last[b,h,:,:] = S
  *
- * Layouts: x, y (batch, L, H, P); dt (batch, L, H); B, C (batch, L, G, N);
+ * The optional gate multiplies the whole output, skip term included, as in
+ * the selective scan (the tencentcloud.csdn.net article on Mamba, section 3:
+ * a SiLU branch gates the SSM output).
+ *
+ * Layouts: x, z, y (batch, L, H, P); dt (batch, L, H); B, C (batch, L, G, N);
  * A, dt_bias, Dskip (H); h0, h_last (batch, H, P, N).
  */
 void oracle_ssd_f64(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
                     int64_t G, const double *x, const double *dt,
                     const double *dt_bias, const double *A, const double *B,
-                    const double *C, const double *Dskip, const double *h0,
-                    double *y, double *h_last, int nthreads)
+                    const double *C, const double *Dskip, const double *z,
+                    const double *h0, double *y, double *h_last, int nthreads)
 {
     int64_t pairs = batch * H;
     int64_t heads_per_group = H / G;
@@ -177,6 +182,7 @@ void oracle_ssd_f64(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
             const double *Bt = B + ((b * L + t) * G + g) * N;
             const double *Ct = C + ((b * L + t) * G + g) * N;
             double *yt = y + ((b * L + t) * H + hh) * P;
+            const double *zt = z ? z + ((b * L + t) * H + hh) * P : 0;
             for (int64_t p = 0; p < P; ++p) {
                 double acc = 0.0;
                 double dx = dl * xt[p];
@@ -185,6 +191,7 @@ void oracle_ssd_f64(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
                     acc += Ct[n] * S[p * N + n];
                 }
                 yt[p] = acc + skip * xt[p];
+                if (zt) yt[p] *= oracle_silu(zt[p]);
             }
         }
         if (h_last)

@@ -59,7 +59,7 @@ def _bind(path: str):
     lib.oracle_selective_scan_f64.restype = None
     lib.oracle_ssd_f64.argtypes = [
         i64, i64, i64, i64, i64, i64, _dp, _dp, _dp, _dp, _dp, _dp,
-        _dp, _dp, _dp, _dp, ctypes.c_int]
+        _dp, _dp, _dp, _dp, _dp, ctypes.c_int]
     lib.oracle_ssd_f64.restype = None
     lib.oracle_softplus_f64.argtypes = [ctypes.c_double]
     lib.oracle_softplus_f64.restype = ctypes.c_double
@@ -155,14 +155,15 @@ def selective_scan_rows(rows, u, delta, A, B, C, D=None, z=None,
 
 
 def ssd(x, dt, A, B, C, D=None, dt_bias=None, h0=None, nthreads: int = 0,
-        lib=None):
+        lib=None, z=None):
     """Float64 Mamba-2 scalar-decay scan.  Returns ``(y, h_last)``.
 
-    x: (batch, L, H, P); dt: (batch, L, H); B, C: (batch, L, G, N);
-    A, D, dt_bias: (H,); h0: (batch, H, P, N).
+    x, z: (batch, L, H, P); dt: (batch, L, H); B, C: (batch, L, G, N);
+    A, D, dt_bias: (H,); h0: (batch, H, P, N).  z (optional) gates the
+    output with silu(z).
     """
     x, dt, A, B, C = map(_f64, (x, dt, A, B, C))
-    D, dt_bias, h0 = map(_f64, (D, dt_bias, h0))
+    D, dt_bias, h0, z = map(_f64, (D, dt_bias, h0, z))
     batch, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     assert dt.shape == (batch, L, H) and A.shape == (H,)
@@ -171,18 +172,19 @@ def ssd(x, dt, A, B, C, D=None, dt_bias=None, h0=None, nthreads: int = 0,
     assert D is None or D.shape == (H,)
     assert dt_bias is None or dt_bias.shape == (H,)
     assert h0 is None or h0.shape == (batch, H, P, N)
+    assert z is None or z.shape == x.shape
     if P * N > 65536:
         raise ValueError("oracle supports P*N <= 65536")
     y = np.empty((batch, L, H, P), np.float64)
     h_last = np.empty((batch, H, P, N), np.float64)
     (lib or _load()).oracle_ssd_f64(
         batch, L, H, P, N, G, _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A),
-        _ptr(B), _ptr(C), _ptr(D), _ptr(h0), _ptr(y), _ptr(h_last),
+        _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last),
         int(nthreads))
     return y, h_last
 
 
-def ssd_rows(rows, x, dt, A, B, C, D=None, dt_bias=None, nthreads: int = 0):
+def ssd_rows(rows, x, dt, A, B, C, D=None, dt_bias=None, nthreads: int = 0, z=None):
     """Oracle on sampled independent (b, h, p) rows of a large SSD problem.
 
     With a scalar decay per (b, t, h), every headdim index p evolves its own
@@ -199,7 +201,8 @@ def ssd_rows(rows, x, dt, A, B, C, D=None, dt_bias=None, nthreads: int = 0):
             A[h:h + 1], B[b:b + 1, :, g:g + 1], C[b:b + 1, :, g:g + 1],
             None if D is None else D[h:h + 1],
             None if dt_bias is None else dt_bias[h:h + 1],
-            nthreads=nthreads)
+            nthreads=nthreads,
+            z=None if z is None else z[b:b + 1, :, h:h + 1, p:p + 1])
         ys.append(y[0, :, 0, 0])
         hs.append(hl[0, 0, 0])
     return np.stack(ys), np.stack(hs)

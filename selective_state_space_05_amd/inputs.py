@@ -16,8 +16,9 @@ activations of bf16 problems):
     theta         ~ U(0, ln 10)  -> A log-uniform in [-10, -1]; the
                     -exp(theta) form keeps every decay exp(delta*A) in (0, 1)
                     (www.mhpq.cn/news/984979 essay, section 3.1).
-  SSD, draw order: x, dt_raw, dt_bias, theta (A_h = -exp(theta)), B, C, D
-    x, B, C, D    ~ N(0, 1)
+  SSD, draw order: x, dt_raw, dt_bias, theta (A_h = -exp(theta)), B, C, D,
+  z (when gated)
+    x, B, C, D, z ~ N(0, 1)
     dt_raw        ~ N(-2, 0.5)
     dt_bias       ~ U(-4, -2) per head
     theta         ~ U(0, ln 16)
@@ -108,6 +109,7 @@ class SSDProblem:
     seed: int
     bias: bool = True
     skip: bool = True
+    gate: bool = False        # z present (drawn after D)
 
     @property
     def elements(self) -> int:
@@ -124,7 +126,7 @@ class SSDProblem:
         dt = self.batch * self.seqlen * self.nheads * s
         par = 4 * self.nheads * (1 + (1 if self.bias else 0) + (1 if self.skip else 0))
         hl = 4 * self.batch * self.nheads * self.headdim * self.dstate
-        return 2 * x + bc + dt + par + hl
+        return (3 if self.gate else 2) * x + bc + dt + par + hl
 
     def replace(self, **kw) -> "SSDProblem":
         return dataclasses.replace(self, **kw)
@@ -224,7 +226,7 @@ def ssd_inputs(p: SSDProblem) -> dict:
     """Draw the inputs of a Mamba-2 scalar-decay problem.
 
     Keys: x (batch, L, H, P), dt (batch, L, H), dt_bias (H,), A (H,),
-    B, C (batch, L, G, N), D (H,).
+    B, C (batch, L, G, N), D (H,), z (batch, L, H, P) or None.
     """
     rng = np.random.default_rng(p.seed)
     f32 = np.float32
@@ -238,9 +240,12 @@ def ssd_inputs(p: SSDProblem) -> dict:
     B = rng.standard_normal((p.batch, p.seqlen, p.ngroups, p.dstate), dtype=f32)
     C = rng.standard_normal((p.batch, p.seqlen, p.ngroups, p.dstate), dtype=f32)
     D = rng.standard_normal(p.nheads, dtype=f32) if p.skip else None
+    z = rng.standard_normal(x.shape, dtype=f32) if p.gate else None
     if p.io == "bf16":
         x, dt, B, C = (bf16_round(a) for a in (x, dt, B, C))
-    return dict(x=x, dt=dt, dt_bias=bias, A=A, B=B, C=C, D=D)
+        if z is not None:
+            z = bf16_round(z)
+    return dict(x=x, dt=dt, dt_bias=bias, A=A, B=B, C=C, D=D, z=z)
 
 
 def initial_state(shape, seed: int) -> np.ndarray:

@@ -215,9 +215,10 @@ def ssd_dl(dt, dt_bias, b, h):
     return softplus_lib(np.asarray(dt[b, :, h], np.float64) + bias)
 
 
-def ssd_quadratic(x, dt, A, B, C, D=None, dt_bias=None):
+def ssd_quadratic(x, dt, A, B, C, D=None, dt_bias=None, z=None):
     """y_t = sum_{s<=t} (C_t . B_s) exp(A_h (cum_t - cum_s)) dl_s x_s + D x_t,
-    with cum the running sum of dl (log-space cumulative product)."""
+    with cum the running sum of dl (log-space cumulative product); with z,
+    times silu(z_t) (scipy's logistic function)."""
     x = np.asarray(x, np.float64)
     batch, L, H, P = x.shape
     G = B.shape[2]
@@ -238,6 +239,8 @@ def ssd_quadratic(x, dt, A, B, C, D=None, dt_bias=None):
             y[b, :, h] = M @ x[b, :, h]
             if D is not None:
                 y[b, :, h] += float(D[h]) * x[b, :, h]
+    if z is not None:
+        y = y * silu_lib(z)
     return y
 
 
@@ -279,10 +282,11 @@ def ssd_chunked(x, dt, A, B, C, D=None, dt_bias=None, Q=64):
     return y, hl
 
 
-def ssd_as_scan(x, dt, A, B, C, D=None, dt_bias=None):
+def ssd_as_scan(x, dt, A, B, C, D=None, dt_bias=None, z=None):
     """Tie an SSD problem to the selective scan: channel (h, p) gets
     u = x[:, :, h, p], delta_raw = dt[:, :, h], bias = dt_bias[h], A[(h,p), n]
-    = A_h, B and C of its group transposed to (batch, N, L), D = D_h."""
+    = A_h, B and C of its group transposed to (batch, N, L), D = D_h, and
+    gate z[:, :, h, p]."""
     x = np.asarray(x, np.float64)
     batch, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
@@ -294,7 +298,8 @@ def ssd_as_scan(x, dt, A, B, C, D=None, dt_bias=None):
     Bs = np.asarray(B[:, :, 0, :], np.float64).transpose(0, 2, 1)
     Cs = np.asarray(C[:, :, 0, :], np.float64).transpose(0, 2, 1)
     Dm = None if D is None else np.repeat(np.asarray(D, np.float64), P)
-    return dict(u=u, delta=dl, A=Am, B=Bs, C=Cs, D=Dm, delta_bias=bias)
+    zs = None if z is None else np.asarray(z, np.float64).transpose(0, 2, 3, 1).reshape(batch, H * P, L)
+    return dict(u=u, delta=dl, A=Am, B=Bs, C=Cs, D=Dm, delta_bias=bias, z=zs)
 
 
 # ----------------------------------------------------------------------------

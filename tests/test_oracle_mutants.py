@@ -51,6 +51,11 @@ SSD_MUTANTS = {
     "ssd_decay_after_input": [("S[p * N + n] = a * S[p * N + n] + dx * Bt[n];",
                                "S[p * N + n] = a * (S[p * N + n] + dx * Bt[n]);")],
     "ssd_dt_index_wrong_head": [("dt[(b * L + t) * H + hh]", "dt[(b * L + t) * H + 0]")],
+    "ssd_gate_ignored": [("if (zt) yt[p] *= oracle_silu(zt[p]);", "")],
+    "ssd_sigmoid_gate_not_silu": [("if (zt) yt[p] *= oracle_silu(zt[p]);",
+                                   "if (zt) yt[p] *= 1.0 / (1.0 + exp(-zt[p]));")],
+    "ssd_gate_before_skip": [("yt[p] = acc + skip * xt[p];\n                if (zt) yt[p] *= oracle_silu(zt[p]);",
+                              "yt[p] = (zt ? acc * oracle_silu(zt[p]) : acc) + skip * xt[p];")],
 }
 
 
@@ -99,6 +104,13 @@ def _ssd_pins(lib):
     yq = pins.ssd_quadratic(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["dt_bias"])
     if not pins.rel_err(y, yq, axis=1) < 1e-12:
         failed.append("quadratic")
+    sg = inputs.ssd_inputs(p.replace(gate=True))
+    yg, _ = oracle_py.ssd(sg["x"], sg["dt"], sg["A"], sg["B"], sg["C"], sg["D"],
+                          sg["dt_bias"], z=sg["z"], lib=lib)
+    yqg = pins.ssd_quadratic(sg["x"], sg["dt"], sg["A"], sg["B"], sg["C"], sg["D"],
+                             sg["dt_bias"], z=sg["z"])
+    if not pins.rel_err(yg, yqg, axis=1) < 1e-12:
+        failed.append("gated_quadratic")
     yc, hc = pins.ssd_chunked(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"],
                               s["dt_bias"], Q=16)
     if not (pins.rel_err(y, yc, axis=1) < 1e-12 and pins.rel_err(hl, hc) < 1e-12):

@@ -277,8 +277,8 @@ def test_softplus_and_silu_match_library_routines(oracle_mod):
 
 
 # -- SSD -----------------------------------------------------------------------
-def _ssd_small(batch, L, H, P, N, G, seed, bias=True):
-    p = inputs.SSDProblem("t", batch, L, H, P, N, G, "f32", seed, bias=bias)
+def _ssd_small(batch, L, H, P, N, G, seed, bias=True, gate=False):
+    p = inputs.SSDProblem("t", batch, L, H, P, N, G, "f32", seed, bias=bias, gate=gate)
     return inputs.ssd_inputs(p)
 
 
@@ -296,6 +296,30 @@ def test_ssd_equals_tied_selective_scan(oracle_mod):
     batch, L, H, P = s["x"].shape
     assert pins.rel_err(ys.reshape(batch, H, P, L).transpose(0, 3, 1, 2), y, axis=1) < 1e-13
     assert pins.rel_err(hs.reshape(batch, H, P, -1), hl) < 1e-13
+
+
+def test_ssd_gated_equals_tied_gated_selective_scan(oracle_mod):
+    """With a gate, each (h, p) row is a gated selective-scan channel."""
+    s = _ssd_small(2, 33, 3, 4, 6, 1, 21, gate=True)
+    y, hl = _ssd_run(oracle_mod, s, z=s["z"])
+    t = pins.ssd_as_scan(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["dt_bias"], z=s["z"])
+    ys, hs = oracle_mod.selective_scan(t["u"], t["delta"], t["A"], t["B"], t["C"],
+                                       t["D"], t["z"], t["delta_bias"])
+    batch, L, H, P = s["x"].shape
+    assert pins.rel_err(ys.reshape(batch, H, P, L).transpose(0, 3, 1, 2), y, axis=1) < 1e-13
+    assert pins.rel_err(hs.reshape(batch, H, P, -1), hl) < 1e-13
+
+
+@pytest.mark.parametrize("G", [1, 3])
+def test_ssd_gated_quadratic_form(oracle_mod, G):
+    """The gate multiplies the whole output (skip term included) by
+    silu(z) = z * logistic(z); the state does not see it."""
+    s = _ssd_small(1, 50, 3, 4, 7, G, 30 + G, gate=True)
+    y, hl = _ssd_run(oracle_mod, s, z=s["z"])
+    yq = pins.ssd_quadratic(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["dt_bias"], z=s["z"])
+    assert pins.rel_err(y, yq, axis=1) < TOL
+    _, hu = _ssd_run(oracle_mod, s)
+    assert np.array_equal(hl, hu)
 
 
 @pytest.mark.parametrize("G", [1, 2])
