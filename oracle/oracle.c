@@ -198,3 +198,35 @@ void oracle_ssd_f64(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t N,
             for (int64_t i = 0; i < P * N; ++i) h_last[r * P * N + i] = S[i];
     }
 }
+
+/*
+ * Causal depthwise convolution of width K followed by SiLU, the local
+ * convolution the Mamba block applies to its SSM branch before the scan
+ * ([csdn] section 3: a local convolution captures short-range patterns,
+ * kernel size 4, SiLU activation; [mlqm] section 3.3: d_conv = 4).  For every
+ * batch b, channel d and step t:
+ *
+ *   u[b,d,t] = silu(conv_b[d] + sum_{k=0..K-1} conv_w[d,k] * x[b,d,t-(K-1)+k])
+ *
+ * with x = 0 before the first step (causal: step t sees steps t-K+1 .. t).
+ * Layouts: x, u (batch, D, L); conv_w (D, K); conv_b (D) nullable -> 0.
+ */
+void oracle_conv1d_silu_f64(int64_t batch, int64_t D, int64_t L, int64_t K,
+                            const double *x, const double *conv_w,
+                            const double *conv_b, double *u)
+{
+    for (int64_t r = 0; r < batch * D; ++r) {
+        int64_t d = r % D;
+        const double *xr = x + r * L;
+        const double *w = conv_w + d * K;
+        double bias = conv_b ? conv_b[d] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            double acc = bias;
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t s = t - (K - 1) + k;
+                if (s >= 0) acc += w[k] * xr[s];
+            }
+            u[r * L + t] = oracle_silu(acc);
+        }
+    }
+}

@@ -61,6 +61,8 @@ def _bind(path: str):
         i64, i64, i64, i64, i64, i64, _dp, _dp, _dp, _dp, _dp, _dp,
         _dp, _dp, _dp, _dp, _dp, ctypes.c_int]
     lib.oracle_ssd_f64.restype = None
+    lib.oracle_conv1d_silu_f64.argtypes = [i64, i64, i64, i64, _dp, _dp, _dp, _dp]
+    lib.oracle_conv1d_silu_f64.restype = None
     lib.oracle_softplus_f64.argtypes = [ctypes.c_double]
     lib.oracle_softplus_f64.restype = ctypes.c_double
     lib.oracle_silu_f64.argtypes = [ctypes.c_double]
@@ -129,6 +131,33 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last),
         int(nthreads))
     return y, h_last
+
+
+def conv1d_silu(x, conv_w, conv_b=None, lib=None):
+    """Float64 causal depthwise convolution + SiLU: u = silu(conv_b + sum_k
+    conv_w[:, k] * x[..., t - (K-1) + k]), zero before the first step.
+
+    x: (batch, Dch, L); conv_w: (Dch, K); conv_b: (Dch,).  Returns u like x.
+    """
+    x, conv_w = _f64(x), _f64(conv_w)
+    conv_b = _f64(conv_b)
+    batch, Dch, L = x.shape
+    K = conv_w.shape[1]
+    assert conv_w.shape == (Dch, K)
+    assert conv_b is None or conv_b.shape == (Dch,)
+    u = np.empty_like(x)
+    (lib or _load()).oracle_conv1d_silu_f64(batch, Dch, L, K, _ptr(x), _ptr(conv_w),
+                                            _ptr(conv_b), _ptr(u))
+    return u
+
+
+def selective_scan_conv(x, conv_w, conv_b, delta, A, B, C, D=None, z=None, delta_bias=None,
+                        h0=None, nthreads: int = 0, lib=None):
+    """The selective scan fed by the convolution prologue: the scan of
+    ``u = conv1d_silu(x, conv_w, conv_b)``, skip term D * u.  Returns
+    ``(y, h_last)``."""
+    u = conv1d_silu(x, conv_w, conv_b, lib=lib)
+    return selective_scan(u, delta, A, B, C, D, z, delta_bias, h0=h0, nthreads=nthreads, lib=lib)
 
 
 def selective_scan_rows(rows, u, delta, A, B, C, D=None, z=None,

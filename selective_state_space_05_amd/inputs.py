@@ -23,6 +23,9 @@ activations of bf16 problems):
     dt_bias       ~ U(-4, -2) per head
     theta         ~ U(0, ln 16)
 
+  convolution prologue (when ``conv``): after z, conv_w ~ 0.5 N(0, 1) of
+  shape (dim, 4) and conv_b ~ 0.1 N(0, 1) per channel; u is then the
+  prologue's input.
   decode step (one time step on a cached state): the selective-scan recipe
   above with L = 1 (the length axis dropped), then from a second stream
   (seed + 1) the state ~ N(0, 1) of shape (batch, dim, N).
@@ -61,6 +64,9 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
+CONV_WIDTH = 4   # the prologue's convolution width (the pages' d_conv)
+
+
 @dataclasses.dataclass(frozen=True)
 class ScanProblem:
     name: str
@@ -73,6 +79,7 @@ class ScanProblem:
     gate: bool                # z present
     skip: bool                # D present
     seed: int
+    conv: bool = False        # u is the input of a width-4 causal conv + SiLU prologue
 
     @property
     def elements(self) -> int:
@@ -89,6 +96,7 @@ class ScanProblem:
         bc = 2 * self.batch * self.dstate * self.seqlen * s
         par = 4 * self.dim * self.dstate
         par += 4 * self.dim * ((1 if self.skip else 0) + (1 if self.bias else 0))
+        par += 4 * self.dim * (CONV_WIDTH + 1) if self.conv else 0
         hl = 4 * self.batch * self.dim * self.dstate
         return act + bc + par + hl
 
@@ -191,9 +199,10 @@ def scan_inputs(p: ScanProblem) -> dict:
     """Draw the inputs of a selective-scan problem.
 
     Returns float32 numpy arrays (bf16 problems: activations already rounded
-    to bf16 values).  Keys: u, delta, delta_bias, A, B, C, D, z (absent
-    operands are None).  Layouts: u, delta, z (batch, dim, L); B, C
-    (batch, N, L); A (dim, N); delta_bias, D (dim,).
+    to bf16 values).  Keys: u, delta, delta_bias, A, B, C, D, z, conv_w,
+    conv_b (absent operands are None).  Layouts: u, delta, z (batch, dim, L);
+    B, C (batch, N, L); A (dim, N); delta_bias, D, conv_b (dim,); conv_w
+    (dim, 4).  With ``conv``, u is the input of the convolution prologue.
     """
     rng = np.random.default_rng(p.seed)
     f32 = np.float32
@@ -214,12 +223,16 @@ def scan_inputs(p: ScanProblem) -> dict:
     C = rng.standard_normal((p.batch, p.dstate, p.seqlen), dtype=f32)
     D = rng.standard_normal(p.dim, dtype=f32) if p.skip else None
     z = rng.standard_normal(sh, dtype=f32) if p.gate else None
+    conv_w = conv_b = None
+    if p.conv:
+        conv_w = rng.standard_normal((p.dim, CONV_WIDTH), dtype=f32) * f32(0.5)
+        conv_b = rng.standard_normal(p.dim, dtype=f32) * f32(0.1)
     if p.io == "bf16":
         u, delta, B, C = (bf16_round(a) for a in (u, delta, B, C))
         if z is not None:
             z = bf16_round(z)
     return dict(u=u, delta=delta, delta_bias=bias, A=A.astype(f32), B=B, C=C,
-                D=D, z=z)
+                D=D, z=z, conv_w=conv_w, conv_b=conv_b)
 
 
 def ssd_inputs(p: SSDProblem) -> dict:

@@ -59,6 +59,16 @@ SSD_MUTANTS = {
 }
 
 
+CONV_MUTANTS = {
+    "identity": [],
+    "conv_not_causal": [("int64_t s = t - (K - 1) + k;\n                if (s >= 0)",
+                         "int64_t s = t + k;\n                if (s < L)")],
+    "conv_taps_reversed": [("acc += w[k] * xr[s];", "acc += w[K - 1 - k] * xr[s];")],
+    "conv_drop_bias": [("double bias = conv_b ? conv_b[d] : 0.0;", "double bias = 0.0;")],
+    "conv_no_silu": [("u[r * L + t] = oracle_silu(acc);", "u[r * L + t] = acc;")],
+}
+
+
 def _build_variant(tmpdir, name, edits):
     src = open(ORACLE_C).read()
     for old, new in edits:
@@ -132,6 +142,28 @@ def test_scan_mutant_is_caught(tmp_path, name):
 def test_ssd_mutant_is_caught(tmp_path, name):
     lib = _build_variant(str(tmp_path), name, SSD_MUTANTS[name])
     failed = _ssd_pins(lib)
+    if name == "identity":
+        assert failed == []
+    else:
+        assert failed, "mutant %s passed every pin" % name
+
+
+def _conv_pins(lib):
+    import scipy.signal
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((2, 3, 25))
+    w = rng.standard_normal((3, 4))
+    b = rng.standard_normal(3)
+    u = oracle_py.conv1d_silu(x, w, b, lib=lib)
+    ref = np.stack([[scipy.signal.lfilter(w[d, ::-1], [1.0], x[bb, d]) + b[d] for d in range(3)]
+                    for bb in range(2)])
+    return [] if pins.rel_err(u, pins.silu_lib(ref)) < 1e-14 else ["fir"]
+
+
+@pytest.mark.parametrize("name", sorted(CONV_MUTANTS))
+def test_conv_mutant_is_caught(tmp_path, name):
+    lib = _build_variant(str(tmp_path), name, CONV_MUTANTS[name])
+    failed = _conv_pins(lib)
     if name == "identity":
         assert failed == []
     else:

@@ -9,6 +9,7 @@ import math
 from fractions import Fraction
 
 import numpy as np
+import scipy.signal
 import pytest
 from hypothesis import given, settings, strategies as st
 
@@ -361,3 +362,53 @@ def test_ssd_resume(oracle_mod):
     y2, h2 = _ssd_run(oracle_mod, b, h0=h1)
     assert pins.rel_err(np.concatenate([y1, y2], axis=1), y, axis=1) < 1e-13
     assert pins.rel_err(h2, hl) < 1e-13
+
+
+# ---------------------------------------------------------------------------
+# convolution prologue
+# ---------------------------------------------------------------------------
+def _conv_case(seed, batch=2, dim=5, L=40):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((batch, dim, L))
+    w = rng.standard_normal((dim, 4))
+    b = rng.standard_normal(dim)
+    return x, w, b
+
+
+def test_conv1d_silu_is_fir_filter_then_silu(oracle_mod):
+    """u = silu(b + sum_k w[k] x[t - 3 + k]) is scipy's FIR filter with the
+    taps reversed, started from rest, plus the bias, through the logistic."""
+    x, w, b = _conv_case(3)
+    u = oracle_mod.conv1d_silu(x, w, b)
+    ref = np.empty_like(x)
+    for bb in range(x.shape[0]):
+        for d in range(x.shape[1]):
+            ref[bb, d] = scipy.signal.lfilter(w[d, ::-1], [1.0], x[bb, d]) + b[d]
+    assert pins.rel_err(u, pins.silu_lib(ref)) < 1e-14
+
+
+def test_conv1d_one_hot_taps(oracle_mod):
+    """Tap 3 alone is the identity: u = silu(x); tap 0 alone delays by three
+    steps, with zeros before the first step (causal, zero-padded)."""
+    x, _, _ = _conv_case(4)
+    ident = np.zeros((x.shape[1], 4)); ident[:, 3] = 1.0
+    # (the oracle forms silu as z / (1 + e^-z), the pin as z * logistic(z):
+    # equal up to rounding)
+    assert pins.rel_err(oracle_mod.conv1d_silu(x, ident), pins.silu_lib(x)) < 1e-15
+    delay = np.zeros((x.shape[1], 4)); delay[:, 0] = 1.0
+    u = oracle_mod.conv1d_silu(x, delay)
+    assert np.all(u[..., :3] == 0.0)
+    assert pins.rel_err(u[..., 3:], pins.silu_lib(x[..., :-3])) < 1e-15
+
+
+def test_scan_with_conv_is_scan_of_conv_output(oracle_mod):
+    p = inputs.ScanProblem("t", 2, 30, 3, 4, "f32", "scalar", True, True, 8, conv=True)
+    x = inputs.scan_inputs(p)
+    y, h = oracle_mod.selective_scan_conv(x["u"], x["conv_w"], x["conv_b"], x["delta"], x["A"],
+                                          x["B"], x["C"], x["D"], x["z"], x["delta_bias"])
+    uc = pins.silu_lib(np.stack([[scipy.signal.lfilter(x["conv_w"][d, ::-1].astype(np.float64), [1.0],
+                                                        x["u"][bb, d].astype(np.float64)) + x["conv_b"][d]
+                                  for d in range(3)] for bb in range(2)]))
+    yc, hc = pins.scan_closed_form(uc, x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"],
+                                   x["delta_bias"])
+    assert pins.rel_err(y, yc) < 1e-12 and pins.rel_err(h, hc) < 1e-12
