@@ -62,10 +62,12 @@ def scan_slots(p) -> float:
     Per element (b, t, d, n): dl*A (1), 2^x (1 transcendental = 2 slots, it
     issues at half rate), (dl*u)*B (1), state FMA (1), output FMA (1) = 6.
     Per (b, t, d): softplus (exp + log = 4 slots + 3), dl*u (1), D*u (1),
-    and with a gate silu (exp + rcp = 4 slots + 2) and the product (1).
+    with a gate silu (exp + rcp = 4 slots + 2) and the product (1), and with
+    the convolution prologue 4 FMAs and a silu (4 slots + 2).
     """
     per_elem = 6
     per_row_step = 4 + 3 + 1 + (1 if p.skip else 0) + (4 + 2 + 1 if p.gate else 0)
+    per_row_step += (4 + 4 + 2) if getattr(p, "conv", False) else 0
     rows_steps = p.batch * p.dim * p.seqlen
     return per_elem * p.elements + per_row_step * rows_steps
 
@@ -205,7 +207,7 @@ class ScanBench:
         for k, v in self.x.items():
             if v is None:
                 t[k] = None
-            elif k in ("A", "D", "delta_bias"):
+            elif k in ("A", "D", "delta_bias", "conv_w", "conv_b"):
                 t[k] = torch.from_numpy(v).to(self.dev)
             else:
                 t[k] = torch.from_numpy(v).to(self.io_t).to(self.dev)
@@ -214,8 +216,13 @@ class ScanBench:
         return t
 
     def step(self, t):
-        self.api.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"],
-                                    t["z"], t["delta_bias"], out=t["y"], h_out=t["h"])
+        if self.p.conv:
+            self.api.selective_scan_conv_fwd(t["u"], t["conv_w"], t["delta"], t["A"], t["B"], t["C"],
+                                             t["D"], t["z"], t["delta_bias"], conv_b=t["conv_b"],
+                                             out=t["y"], h_out=t["h"])
+        else:
+            self.api.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"],
+                                        t["z"], t["delta_bias"], out=t["y"], h_out=t["h"])
 
     def roofline(self, sec):
         slots = scan_slots(self.p)
@@ -224,13 +231,24 @@ class ScanBench:
                 "unit": "T VALU lane-slots/s", "frac": a / VALU_PEAK_TSLOTS,
                 "slots_per_launch": slots}
 
+    def _u_rows(self):
+        """The scan input the oracle sees: u itself, or with the convolution
+        prologue the oracle's convolution of it."""
+        from oracle import oracle
+        x = self.x
+        if not self.p.conv:
+            return x["u"]
+        if getattr(self, "_uc", None) is None:
+            self._uc = oracle.conv1d_silu(x["u"], x["conv_w"], x["conv_b"])
+        return self._uc
+
     def parity(self, t):
         from oracle import oracle
         p, x = self.p, self.x
         rng = np.random.default_rng(123)
         rows = [(0, 0), (p.batch - 1, p.dim - 1)] + [
             (int(rng.integers(p.batch)), int(rng.integers(p.dim))) for _ in range(6)]
-        yo, ho = oracle.selective_scan_rows(rows, x["u"], x["delta"], x["A"], x["B"], x["C"],
+        yo, ho = oracle.selective_scan_rows(rows, self._u_rows(), x["delta"], x["A"], x["B"], x["C"],
                                             x["D"], x["z"], x["delta_bias"])
         yg = t["y"].float().cpu().numpy().astype(np.float64)
         hg = t["h"].cpu().numpy().astype(np.float64)
@@ -243,9 +261,10 @@ class ScanBench:
         `budget_s` seconds of work at the measured single-row rate."""
         from oracle import oracle
         p, x = self.p, self.x
+        u = self._u_rows()
         t0 = time.time()
-        oracle.selective_scan_rows([(0, 0)], x["u"], x["delta"], x["A"], x["B"], x["C"],
-                                   x["D"], x["z"], x["delta_bias"], nthreads=1)
+        oracle.selective_scan_rows([(0, 0)], u, x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"],
+                                   x["delta_bias"], nthreads=1)
         per_row = max(time.time() - t0, 1e-4)
         rows_total = p.batch * p.dim
         n_rows = int(min(rows_total, max(threads, budget_s * threads / per_row)))
@@ -259,13 +278,15 @@ class ScanBench:
         for b in np.unique(bsel):
             ds = dsel[bsel == b]
             lo, hi = int(ds[0]), int(ds[-1]) + 1
-            oracle.selective_scan(
-                x["u"][b:b + 1, lo:hi], x["delta"][b:b + 1, lo:hi], x["A"][lo:hi],
-                x["B"][b:b + 1], x["C"][b:b + 1],
-                None if x["D"] is None else x["D"][lo:hi],
-                None if x["z"] is None else x["z"][b:b + 1, lo:hi],
-                None if x["delta_bias"] is None else x["delta_bias"][lo:hi],
-                nthreads=threads)
+            args = (x["delta"][b:b + 1, lo:hi], x["A"][lo:hi], x["B"][b:b + 1], x["C"][b:b + 1],
+                    None if x["D"] is None else x["D"][lo:hi],
+                    None if x["z"] is None else x["z"][b:b + 1, lo:hi],
+                    None if x["delta_bias"] is None else x["delta_bias"][lo:hi])
+            if p.conv:
+                oracle.selective_scan_conv(x["u"][b:b + 1, lo:hi], x["conv_w"][lo:hi],
+                                           x["conv_b"][lo:hi], *args, nthreads=threads)
+            else:
+                oracle.selective_scan(x["u"][b:b + 1, lo:hi], *args, nthreads=threads)
             done += hi - lo
         cpu_s = time.time() - t0
         elems = done * p.seqlen * p.dstate
@@ -275,7 +296,7 @@ class ScanBench:
     def config(self):
         p = self.p
         return {"workload": p.name, "batch": p.batch, "seqlen": p.seqlen, "dim": p.dim,
-                "dstate": p.dstate, "io": p.io, "gate": p.gate, "skip": p.skip}
+                "dstate": p.dstate, "io": p.io, "gate": p.gate, "skip": p.skip, "conv": p.conv}
 
 
 class SSDBench:

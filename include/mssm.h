@@ -136,6 +136,35 @@ MSSM_API mssm_status mssm_selective_scan_fwd(const void *u, const void *delta,
                                     float *h_last, mssm_scan_dims dims,
                                     mssm_dtypes dtypes, void *stream);
 
+/*
+ * The selective-scan forward fed by its convolution prologue ([csdn]
+ * section 3: a local convolution and a SiLU precede the selective SSM in the
+ * Mamba block, kernel size 4; [mlqm] section 3.3: d_conv = 4).  The scan
+ * input is formed on chip from x and never stored:
+ *
+ *   u[b,d,t] = silu(conv_b[d] + sum_{k=0..3} conv_w[d,k] * x[b,d,t-3+k])
+ *
+ * with x = 0 before step 0 (a causal, zero-padded depthwise convolution);
+ * then the selective scan of mssm_selective_scan_fwd_h0 on u, including
+ * the skip term D[d] * u.
+ *
+ *   x       (batch, dim, L), dtype `io`        required (the prologue input)
+ *   conv_w  (dim, MSSM_CONV_WIDTH) float32     required
+ *   conv_b  (dim) float32                      nullable -> 0
+ * Everything else (delta ... h_last, errors, variants) is as for
+ * mssm_selective_scan_fwd_h0; h0 does not carry the convolution's window,
+ * so a continued sequence restarts it from zero.
+ */
+#define MSSM_CONV_WIDTH 4
+MSSM_API mssm_status mssm_selective_scan_fwd_conv(const void *x, const float *conv_w,
+                                         const float *conv_b, const void *delta,
+                                         const float *delta_bias, const float *A,
+                                         const void *B, const void *C,
+                                         const float *D, const void *z,
+                                         const float *h0, void *y, float *h_last,
+                                         mssm_scan_dims dims, mssm_dtypes dtypes,
+                                         void *stream);
+
 /* Sizes of a Mamba-2 scalar-decay (SSD) problem. */
 typedef struct {
     int64_t batch;
@@ -202,6 +231,26 @@ MSSM_API mssm_status mssm_ssd_scalar_fwd_h0(const void *x, const void *dt,
                                    const float *h0, void *y, float *h_last,
                                    mssm_ssd_dims dims, mssm_dtypes dtypes,
                                    void *stream);
+
+/*
+ * The SSD forward with a SiLU gate on its output ([csdn] section 3: a SiLU
+ * branch gates the SSM output; the same reading as the selective scan's z):
+ *
+ *   y[b,t,h,p] = (sum_n C[b,t,g,n] * S[p][n] + D[h] * x[b,t,h,p]) * silu(z[b,t,h,p])
+ *
+ *   z    (batch, L, H, P), dtype `io`, like x   nullable -> no gate
+ *   h0   (batch, H, P, N) float32               nullable -> 0 (as in the
+ *                                               _h0 entry point)
+ * Everything else is as for mssm_ssd_scalar_fwd_h0, which equals this with
+ * z = NULL.
+ */
+MSSM_API mssm_status mssm_ssd_scalar_fwd_gated(const void *x, const void *dt,
+                                      const float *dt_bias, const float *A,
+                                      const void *B, const void *C,
+                                      const float *D, const void *z,
+                                      const float *h0, void *y, float *h_last,
+                                      mssm_ssd_dims dims, mssm_dtypes dtypes,
+                                      void *stream);
 
 /* Sizes of one decode step. */
 typedef struct {

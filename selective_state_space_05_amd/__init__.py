@@ -10,11 +10,12 @@ call raises -- there is no CPU fallback.
 """
 from .api import (  # noqa: F401
     MssmError,
+    selective_scan_conv_fwd,
     selective_scan_fwd,
     selective_state_update,
     ssd_scalar_fwd,
     version,
 )
 
-__all__ = ["MssmError", "selective_scan_fwd", "selective_state_update", "ssd_scalar_fwd",
-           "version"]
+__all__ = ["MssmError", "selective_scan_conv_fwd", "selective_scan_fwd", "selective_state_update",
+           "ssd_scalar_fwd", "version"]

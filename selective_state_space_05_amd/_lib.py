@@ -30,6 +30,7 @@ VARIANT_SSD_RECURRENT = 4
 VARIANT_SSD_CHUNKED = 5
 
 MAX_DSTATE = 64
+CONV_WIDTH = 4
 SSD_MAX_DSTATE = 256
 SSD_MAX_HEADDIM = 256
 
@@ -38,7 +39,9 @@ EXPORTED = (
     "mssm_selective_scan_fwd",
     "mssm_ssd_scalar_fwd",
     "mssm_selective_scan_fwd_h0",
+    "mssm_selective_scan_fwd_conv",
     "mssm_ssd_scalar_fwd_h0",
+    "mssm_ssd_scalar_fwd_gated",
     "mssm_selective_state_update",
     "mssm_force_variant",
     "mssm_last_variant",
@@ -85,9 +88,15 @@ def _declare(L):
     L.mssm_selective_scan_fwd_h0.argtypes = [vp, vp, fp, fp, vp, vp, fp, vp, fp,
                                              vp, fp, ScanDims, DTypes, vp]
     L.mssm_selective_scan_fwd_h0.restype = ctypes.c_int
+    L.mssm_selective_scan_fwd_conv.argtypes = [vp, fp, fp, vp, fp, fp, vp, vp, fp, vp, fp,
+                                               vp, fp, ScanDims, DTypes, vp]
+    L.mssm_selective_scan_fwd_conv.restype = ctypes.c_int
     L.mssm_ssd_scalar_fwd_h0.argtypes = [vp, vp, fp, fp, vp, vp, fp, fp, vp, fp,
                                          SSDDims, DTypes, vp]
     L.mssm_ssd_scalar_fwd_h0.restype = ctypes.c_int
+    L.mssm_ssd_scalar_fwd_gated.argtypes = [vp, vp, fp, fp, vp, vp, fp, vp, fp, vp, fp,
+                                            SSDDims, DTypes, vp]
+    L.mssm_ssd_scalar_fwd_gated.restype = ctypes.c_int
     L.mssm_selective_state_update.argtypes = [fp, vp, vp, fp, fp, vp, vp, fp, vp, vp,
                                               StepDims, DTypes, vp]
     L.mssm_selective_state_update.restype = ctypes.c_int

@@ -137,21 +137,78 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     return y, h_last
 
 
+def selective_scan_conv_fwd(x, conv_w, delta, A, B, C, D=None, z=None, delta_bias=None,
+                            conv_b=None, h0=None, return_last_state=True, out=None, h_out=None):
+    """Selective-scan forward fed by its convolution prologue on the GPU:
+    the scan of u = silu(conv_b + causal width-4 depthwise conv(x)), with u
+    formed on chip.
+
+    x: (batch, dim, L) like the scan's u; conv_w: (dim, 4) float32; conv_b:
+    (dim,) float32.  Other arguments and the result as for
+    ``selective_scan_fwd``.
+    """
+    L = _lib.lib()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    _need(conv_w, "conv_w", torch.float32, dev)
+    _need(conv_b, "conv_b", torch.float32, dev)
+    batch, dim, seqlen = x.shape
+    if tuple(conv_w.shape) != (dim, _lib.CONV_WIDTH):
+        raise ValueError("conv_w must be (dim, %d)" % _lib.CONV_WIDTH)
+    if conv_b is not None and tuple(conv_b.shape) != (dim,):
+        raise ValueError("conv_b must be (dim,)")
+    io = x.dtype
+    for name, t in (("x", x), ("delta", delta), ("B", B), ("C", C), ("z", z)):
+        _need(t, name, io, dev)
+    for name, t in (("A", A), ("D", D), ("delta_bias", delta_bias), ("h0", h0)):
+        _need(t, name, torch.float32, dev)
+    N = A.shape[1]
+    if delta.shape != x.shape or (z is not None and z.shape != x.shape):
+        raise ValueError("x, delta, z must share one (batch, dim, L) shape")
+    if tuple(A.shape) != (dim, N):
+        raise ValueError("A must be (dim, N)")
+    if tuple(B.shape) != (batch, N, seqlen) or tuple(C.shape) != (batch, N, seqlen):
+        raise ValueError("B and C must be (batch, N, L)")
+    if h0 is not None and tuple(h0.shape) != (batch, dim, N):
+        raise ValueError("h0 must be (batch, dim, N)")
+    for name, t in (("D", D), ("delta_bias", delta_bias)):
+        if t is not None and tuple(t.shape) != (dim,):
+            raise ValueError("%s must be (dim,)" % name)
+    y = out if out is not None else torch.empty_like(x)
+    _need(y, "out", io, dev)
+    h_last = None
+    if return_last_state:
+        h_last = h_out if h_out is not None else torch.empty(
+            (batch, dim, N), dtype=torch.float32, device=dev)
+        _need(h_last, "h_out", torch.float32, dev)
+    dims = _lib.ScanDims(batch, seqlen, dim, N)
+    dtp = _lib.DTypes(_io_dtype(x), _lib.MSSM_F32)
+    with torch.cuda.device(dev):
+        st = L.mssm_selective_scan_fwd_conv(
+            _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(delta), _ptr(delta_bias), _ptr(A),
+            _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last), dims, dtp,
+            _stream_handle(dev))
+    _check(st)
+    return y, h_last
+
+
 def ssd_scalar_fwd(x, dt, A, B, C, D=None, dt_bias=None, chunk=0,
-                   return_last_state=True, out=None, h_out=None, h0=None):
+                   return_last_state=True, out=None, h_out=None, h0=None, z=None):
     """Mamba-2 scalar-decay forward on the GPU.
 
-    x: (batch, L, H, P); dt: (batch, L, H); B, C: (batch, L, G, N), all in
-    one activation dtype; A, D, dt_bias: (H,) float32; h0: (batch, H, P, N)
-    float32 initial state (None: zero; may also be ``h_out``).  Returns
-    ``(y, h_last)``: y like x, h_last (batch, H, P, N) float32.
+    x, z: (batch, L, H, P); dt: (batch, L, H); B, C: (batch, L, G, N), all
+    in one activation dtype; A, D, dt_bias: (H,) float32; h0: (batch, H, P,
+    N) float32 initial state (None: zero; may also be ``h_out``); z gates
+    the output with silu(z) (None: no gate).  Returns ``(y, h_last)``: y
+    like x, h_last (batch, H, P, N) float32.
     """
     L = _lib.lib()
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("tensors must live on a GPU device")
     io = x.dtype
-    for name, t in (("x", x), ("dt", dt), ("B", B), ("C", C)):
+    for name, t in (("x", x), ("dt", dt), ("B", B), ("C", C), ("z", z)):
         _need(t, name, io, dev)
     for name, t in (("A", A), ("D", D), ("dt_bias", dt_bias), ("h0", h0)):
         _need(t, name, torch.float32, dev)
@@ -159,6 +216,8 @@ def ssd_scalar_fwd(x, dt, A, B, C, D=None, dt_bias=None, chunk=0,
     G, N = B.shape[2], B.shape[3]
     if h0 is not None and tuple(h0.shape) != (batch, H, P, N):
         raise ValueError("h0 must be (batch, H, P, N)")
+    if z is not None and z.shape != x.shape:
+        raise ValueError("z must be shaped like x")
     if tuple(dt.shape) != (batch, seqlen, H):
         raise ValueError("dt must be (batch, L, H)")
     if tuple(B.shape) != (batch, seqlen, G, N) or tuple(C.shape) != tuple(B.shape):
@@ -176,7 +235,12 @@ def ssd_scalar_fwd(x, dt, A, B, C, D=None, dt_bias=None, chunk=0,
     dims = _lib.SSDDims(batch, seqlen, H, P, N, G, int(chunk))
     dtp = _lib.DTypes(_io_dtype(x), _lib.MSSM_F32)
     with torch.cuda.device(dev):
-        if h0 is None:
+        if z is not None:
+            st = L.mssm_ssd_scalar_fwd_gated(
+                _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
+                _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last), dims, dtp,
+                _stream_handle(dev))
+        elif h0 is None:
             st = L.mssm_ssd_scalar_fwd(
                 _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
                 _ptr(D), _ptr(y), _ptr(h_last), dims, dtp, _stream_handle(dev))

@@ -28,6 +28,11 @@ struct ScanArgs {
     float *h_last;            // may be null
     int64_t batch, L, dim, N;
     IoType io;
+    // Convolution prologue: when conv_w is set, u holds the input x of a
+    // causal width-4 depthwise convolution (conv_w (dim, 4), conv_b (dim)
+    // may be null) and the scan runs on silu(conv(x)).
+    const float *conv_w = nullptr;
+    const float *conv_b = nullptr;
 };
 
 // One SSD problem, already validated.  Layouts as in mssm.h.
@@ -39,6 +44,7 @@ struct SSDArgs {
     const void *B;
     const void *C;
     const float *D;           // may be null
+    const void *z;            // may be null -> no gate; (batch, L, H, P) like x
     const float *h0;          // may be null; may be the same buffer as h_last
     void *y;
     float *h_last;            // may be null

@@ -118,7 +118,7 @@ mssm_status check_overlaps(const Range *ins, int nin, const Range *outs, int nou
 mssm_status scan_fwd(const void *u, const void *delta, const float *delta_bias, const float *A,
                      const void *B, const void *C, const float *D, const void *z, const float *h0,
                      void *y, float *h_last, mssm_scan_dims dims, mssm_dtypes dtypes,
-                     void *stream) {
+                     void *stream, const float *conv_w = nullptr, const float *conv_b = nullptr) {
     g_last_error.clear();
     if (mssm_status s = check_dtypes(dtypes)) return s;
     const int64_t batch = dims.batch, L = dims.seqlen, dim = dims.dim, N = dims.dstate;
@@ -167,12 +167,13 @@ mssm_status scan_fwd(const void *u, const void *delta, const float *delta_bias, 
         range("z", z, act_bytes),          range("B", B, bc_bytes),
         range("C", C, bc_bytes),           range("A", A, dn * 4),
         range("D", D, dim * 4),            range("delta_bias", delta_bias, dim * 4),
-        range("h0", h0, hl)};
+        range("h0", h0, hl),               range("conv_w", conv_w, dim * 4 * MSSM_CONV_WIDTH),
+        range("conv_b", conv_b, dim * 4)};
     const Range outs[] = {range("y", y, act_bytes), range("h_last", h_last, hl)};
-    if (mssm_status c = check_overlaps(ins, 9, outs, 2, h0, h_last)) return c;
+    if (mssm_status c = check_overlaps(ins, 11, outs, 2, h0, h_last)) return c;
 
     mssm::ScanArgs a{u, delta, delta_bias, A, B, C, D, z, h0, y, h_last, batch, L, dim, N,
-                     dtypes.io == MSSM_F32 ? mssm::IO_F32 : mssm::IO_BF16};
+                     dtypes.io == MSSM_F32 ? mssm::IO_F32 : mssm::IO_BF16, conv_w, conv_b};
 
     mssm_variant v = g_forced;
     if (v == MSSM_VARIANT_AUTO) v = choose_scan_variant(a);
@@ -203,8 +204,9 @@ mssm_status scan_fwd(const void *u, const void *delta, const float *delta_bias, 
 }
 
 mssm_status ssd_fwd(const void *x, const void *dt, const float *dt_bias, const float *A,
-                    const void *B, const void *C, const float *D, const float *h0, void *y,
-                    float *h_last, mssm_ssd_dims dims, mssm_dtypes dtypes, void *stream) {
+                    const void *B, const void *C, const float *D, const void *z, const float *h0,
+                    void *y, float *h_last, mssm_ssd_dims dims, mssm_dtypes dtypes,
+                    void *stream) {
     g_last_error.clear();
     if (mssm_status s = check_dtypes(dtypes)) return s;
     const int64_t batch = dims.batch, L = dims.seqlen, H = dims.nheads, P = dims.headdim,
@@ -258,11 +260,12 @@ mssm_status ssd_fwd(const void *x, const void *dt, const float *dt_bias, const f
     const Range ins[] = {range("x", x, x_bytes),   range("dt", dt, dt_bytes),
                          range("B", B, bc_bytes),  range("C", C, bc_bytes),
                          range("A", A, H * 4),     range("D", D, H * 4),
-                         range("dt_bias", dt_bias, H * 4), range("h0", h0, hl)};
+                         range("dt_bias", dt_bias, H * 4), range("h0", h0, hl),
+                         range("z", z, x_bytes)};
     const Range outs[] = {range("y", y, x_bytes), range("h_last", h_last, hl)};
-    if (mssm_status c = check_overlaps(ins, 8, outs, 2, h0, h_last)) return c;
+    if (mssm_status c = check_overlaps(ins, 9, outs, 2, h0, h_last)) return c;
 
-    mssm::SSDArgs a{x, dt, dt_bias, A, B, C, D, h0, y, h_last, batch, L, H, P, N, G,
+    mssm::SSDArgs a{x, dt, dt_bias, A, B, C, D, z, h0, y, h_last, batch, L, H, P, N, G,
                     Q == 0 ? 256 : Q, dtypes.io == MSSM_F32 ? mssm::IO_F32 : mssm::IO_BF16};
     // The matrix-core form needs bf16 operands and a few chunks to pay off;
     // everything else takes the recurrent form.
@@ -315,18 +318,40 @@ mssm_status mssm_selective_scan_fwd_h0(const void *u, const void *delta,
     return scan_fwd(u, delta, delta_bias, A, B, C, D, z, h0, y, h_last, dims, dtypes, stream);
 }
 
+mssm_status mssm_selective_scan_fwd_conv(const void *x, const float *conv_w,
+                                         const float *conv_b, const void *delta,
+                                         const float *delta_bias, const float *A, const void *B,
+                                         const void *C, const float *D, const void *z,
+                                         const float *h0, void *y, float *h_last,
+                                         mssm_scan_dims dims, mssm_dtypes dtypes, void *stream) {
+    if (!conv_w) {
+        g_last_error.clear();
+        return fail(MSSM_ERR_INVALID_ARG, "conv_w is null");
+    }
+    return scan_fwd(x, delta, delta_bias, A, B, C, D, z, h0, y, h_last, dims, dtypes, stream,
+                    conv_w, conv_b);
+}
+
 mssm_status mssm_ssd_scalar_fwd(const void *x, const void *dt, const float *dt_bias,
                                 const float *A, const void *B, const void *C,
                                 const float *D, void *y, float *h_last,
                                 mssm_ssd_dims dims, mssm_dtypes dtypes, void *stream) {
-    return ssd_fwd(x, dt, dt_bias, A, B, C, D, nullptr, y, h_last, dims, dtypes, stream);
+    return ssd_fwd(x, dt, dt_bias, A, B, C, D, nullptr, nullptr, y, h_last, dims, dtypes, stream);
 }
 
 mssm_status mssm_ssd_scalar_fwd_h0(const void *x, const void *dt, const float *dt_bias,
                                    const float *A, const void *B, const void *C,
                                    const float *D, const float *h0, void *y, float *h_last,
                                    mssm_ssd_dims dims, mssm_dtypes dtypes, void *stream) {
-    return ssd_fwd(x, dt, dt_bias, A, B, C, D, h0, y, h_last, dims, dtypes, stream);
+    return ssd_fwd(x, dt, dt_bias, A, B, C, D, nullptr, h0, y, h_last, dims, dtypes, stream);
+}
+
+mssm_status mssm_ssd_scalar_fwd_gated(const void *x, const void *dt, const float *dt_bias,
+                                      const float *A, const void *B, const void *C,
+                                      const float *D, const void *z, const float *h0, void *y,
+                                      float *h_last, mssm_ssd_dims dims, mssm_dtypes dtypes,
+                                      void *stream) {
+    return ssd_fwd(x, dt, dt_bias, A, B, C, D, z, h0, y, h_last, dims, dtypes, stream);
 }
 
 mssm_status mssm_selective_state_update(float *state, const void *x, const void *dt,

@@ -12,18 +12,19 @@ namespace {
 
 using core::kCh;
 
-template <typename T, int W, int NPL, bool GATE, bool VEC>
+template <typename T, int W, int NPL, bool GATE, bool VEC, bool CONV>
 __global__ __launch_bounds__(64 * W) void scan_chunked_kernel(
     const T *__restrict__ u, const T *__restrict__ delta,
     const float *__restrict__ delta_bias, const float *__restrict__ A,
     const T *__restrict__ Bm, const T *__restrict__ Cm,
     const float *__restrict__ Dskip, const T *__restrict__ z, const float *h0, T *__restrict__ y,
-    float *h_last, int64_t L, int dim, int N, int groups_per_batch) {
+    float *h_last, int64_t L, int dim, int N, int groups_per_batch,
+    const float *__restrict__ conv_w, const float *__restrict__ conv_b) {
     __shared__ core::Smem<W> sm;
     const int64_t b = blockIdx.x / groups_per_batch;
     const int d0 = (blockIdx.x - static_cast<int>(b) * groups_per_batch) * kCh;
-    core::Walker<T, W, NPL, GATE, VEC> wk;
-    wk.init(u, delta, delta_bias, A, Bm, Cm, Dskip, z, y, L, dim, N, b, d0);
+    core::Walker<T, W, NPL, GATE, VEC, CONV> wk;
+    wk.init(u, delta, delta_bias, A, Bm, Cm, Dskip, z, y, L, dim, N, b, d0, conv_w, conv_b);
     // Lanes of channels past the last one mirror the last channel (their
     // owners store its y again), so they start from its initial state too.
     float h[NPL];
@@ -43,21 +44,26 @@ __global__ __launch_bounds__(64 * W) void scan_chunked_kernel(
     }
 }
 
-template <typename T, int W, int NPL>
+template <typename T, int W, int NPL, bool CONV>
 hipError_t launch_typed(const ScanArgs &a, hipStream_t stream) {
     const int groups = static_cast<int>((a.dim + kCh - 1) / kCh);
     const int64_t grid = a.batch * groups;
     const bool vec = scan_rows_vectorizable(a);
-    decltype(&scan_chunked_kernel<T, W, NPL, true, true>) kern;
-    if (a.z) kern = vec ? scan_chunked_kernel<T, W, NPL, true, true> : scan_chunked_kernel<T, W, NPL, true, false>;
-    else kern = vec ? scan_chunked_kernel<T, W, NPL, false, true> : scan_chunked_kernel<T, W, NPL, false, false>;
+    decltype(&scan_chunked_kernel<T, W, NPL, true, true, CONV>) kern;
+    if (a.z) kern = vec ? scan_chunked_kernel<T, W, NPL, true, true, CONV> : scan_chunked_kernel<T, W, NPL, true, false, CONV>;
+    else kern = vec ? scan_chunked_kernel<T, W, NPL, false, true, CONV> : scan_chunked_kernel<T, W, NPL, false, false, CONV>;
     hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(64 * W), 0, stream,
                        static_cast<const T *>(a.u), static_cast<const T *>(a.delta),
                        a.delta_bias, a.A, static_cast<const T *>(a.B),
                        static_cast<const T *>(a.C), a.D, static_cast<const T *>(a.z), a.h0,
                        static_cast<T *>(a.y), a.h_last, a.L, static_cast<int>(a.dim),
-                       static_cast<int>(a.N), groups);
+                       static_cast<int>(a.N), groups, a.conv_w, a.conv_b);
     return hipGetLastError();
+}
+
+template <typename T, int W, int NPL>
+hipError_t launch_conv(const ScanArgs &a, hipStream_t stream) {
+    return a.conv_w ? launch_typed<T, W, NPL, true>(a, stream) : launch_typed<T, W, NPL, false>(a, stream);
 }
 
 // Four waves with one state element per lane: the most waves in flight, and
@@ -66,10 +72,10 @@ hipError_t launch_typed(const ScanArgs &a, hipStream_t stream) {
 // in two waves, four per lane in four waves up to N = 64).
 template <typename T>
 hipError_t launch_by_n(const ScanArgs &a, hipStream_t stream) {
-    if (a.N <= 8) return launch_typed<T, 2, 1>(a, stream);
-    if (a.N <= 16) return launch_typed<T, 4, 1>(a, stream);
-    if (a.N <= 32) return launch_typed<T, 2, 4>(a, stream);
-    return launch_typed<T, 4, 4>(a, stream);
+    if (a.N <= 8) return launch_conv<T, 2, 1>(a, stream);
+    if (a.N <= 16) return launch_conv<T, 4, 1>(a, stream);
+    if (a.N <= 32) return launch_conv<T, 2, 4>(a, stream);
+    return launch_conv<T, 4, 4>(a, stream);
 }
 
 }  // namespace

@@ -42,6 +42,13 @@
 // Steps past the end of the range get dl = 0 and dl*u = 0, i.e. the identity
 // pair (decay 1, input 0), so the state passes through unchanged.  Channels
 // beyond the last compute on clamped inputs and store nothing.
+//
+// With the convolution prologue (CONV), the activation row holds the input x
+// of a causal width-4 depthwise convolution, and the owner forms
+// u_t = silu(conv_b + sum_k conv_w[k] x_{t-3+k}) (x = 0 before step 0) from
+// its own steps and the four before them (the tencentcloud.csdn.net article
+// on Mamba, section 3: a local convolution and SiLU precede the selective
+// SSM), so u never goes through HBM.
 #pragma once
 
 #include "device_math.h"
@@ -142,19 +149,23 @@ __device__ __forceinline__ void rows_reduce(const float (&p)[32], float (&q)[8])
     }
 }
 
+constexpr int kConv = 4;           // width of the convolution prologue
+
 // Per-thread view of one (batch, 16-channel group) problem slice.
-template <typename T, int W, int NPL, bool GATE, bool VEC>
+template <typename T, int W, int NPL, bool GATE, bool VEC, bool CONV = false>
 struct Walker {
     static constexpr int kRows = 4 * W;            // rows of 16 lanes
     static constexpr int OS = kT * kCh / (64 * W); // steps per owner thread (4 or 2)
     static constexpr int OPC = kT / OS;            // owner threads per channel
+    static constexpr int kPrev = kConv / OS;       // raws holding the 4 steps before
     using Raw = typename Pack<T, OS>::raw;
 
     // Inputs of one chunk exactly as loaded; they are converted where they
     // are first used, a chunk after the loads were issued, so the loads
     // overlap a whole chunk of work.
     struct In {
-        Raw ru, rd, rz;            // owner: OS steps of u, delta (and z)
+        Raw ru, rd, rz;            // owner: OS steps of u (CONV: x), delta (and z)
+        Raw rp[CONV ? kPrev : 1];  // CONV: x at the 4 steps before the owner's first
         T rb[2][NPL], rc[2][NPL];  // scan lane: B, C at steps t0 + 16 q + j
     };
 
@@ -170,6 +181,7 @@ struct Walker {
     const T *ub, *db, *zb; // rows of the workgroup's first channel (uniform)
     T *yb;
     float bias, skip;
+    float cw[kConv], cbias; // CONV: the owner channel's taps and bias
     int L;
     float sdl;             // owner's running sum of dl over the walked steps
 
@@ -183,7 +195,8 @@ struct Walker {
 
     __device__ void init(const T *u, const T *delta, const float *delta_bias, const float *A,
                          const T *B, const T *C, const float *Dskip, const T *z, T *y,
-                         int64_t L_, int dim, int N, int64_t b, int d0) {
+                         int64_t L_, int dim, int N, int64_t b, int d0,
+                         const float *conv_w = nullptr, const float *conv_b = nullptr) {
         const int tid = threadIdx.x;
         const int lane = tid & 63;
         prow = (tid >> 6) * 4 + (lane >> 4);
@@ -210,6 +223,11 @@ struct Walker {
         oo = static_cast<uint32_t>(dO - d0) * static_cast<uint32_t>(L) * sizeof(T);
         bias = delta_bias ? delta_bias[dO] : 0.0f;
         skip = Dskip ? Dskip[dO] : 0.0f;
+        if constexpr (CONV) {
+#pragma unroll
+            for (int k = 0; k < kConv; ++k) cw[k] = conv_w[static_cast<int64_t>(dO) * kConv + k];
+            cbias = conv_b ? conv_b[dO] : 0.0f;
+        }
         ub = u + row0;
         db = delta + row0;
         zb = GATE ? z + row0 : nullptr;
@@ -231,6 +249,16 @@ struct Walker {
             in.ru = ld<Raw>(ub, o);
             in.rd = ld<Raw>(db, o);
             if (GATE && OUT) in.rz = ld<Raw>(zb, o);
+            if constexpr (CONV) {
+                // the 4 steps before, as kPrev aligned raws; indices clamped
+                // into the row (those before step 0 are zeroed at the use)
+#pragma unroll
+                for (int m = 0; m < kPrev; ++m) {
+                    const int s = off - kConv + m * OS;
+                    const int sc = s < 0 ? 0 : (s + OS <= L ? s : L - OS);
+                    in.rp[m] = ld<Raw>(ub, oo + static_cast<uint32_t>(sc) * sizeof(T));
+                }
+            }
         } else {
             T su[OS], sd[OS], sz[OS];
 #pragma unroll
@@ -243,6 +271,16 @@ struct Walker {
             __builtin_memcpy(&in.ru, su, sizeof(Raw));
             __builtin_memcpy(&in.rd, sd, sizeof(Raw));
             __builtin_memcpy(&in.rz, sz, sizeof(Raw));
+            if constexpr (CONV) {
+                T sp[kConv];
+#pragma unroll
+                for (int k = 0; k < kConv; ++k) {
+                    const int s = off - kConv + k;
+                    const int sc = s < 0 ? 0 : (s < L ? s : L - 1);
+                    sp[k] = ld<T>(ub, oo + static_cast<uint32_t>(sc) * sizeof(T));
+                }
+                __builtin_memcpy(in.rp, sp, sizeof(sp));
+            }
         }
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
@@ -285,6 +323,26 @@ struct Walker {
         float u[OS], dr[OS], zz[OS];
         Pack<T, OS>::unpack(in.ru, u);
         Pack<T, OS>::unpack(in.rd, dr);
+        if constexpr (CONV) {
+            // xx[0..3]: x at the 4 steps before the owner's first (0 before
+            // step 0), xx[4..]: the owner's own steps
+            float xx[kConv + OS];
+#pragma unroll
+            for (int m = 0; m < kPrev; ++m) Pack<T, OS>::unpack(in.rp[m], xx + m * OS);
+            const int first = t0 + OS * ok;
+#pragma unroll
+            for (int k = 0; k < kConv; ++k)
+                if (first - kConv + k < 0) xx[k] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < OS; ++i) xx[kConv + i] = u[i];
+#pragma unroll
+            for (int i = 0; i < OS; ++i) {
+                float c = cbias;
+#pragma unroll
+                for (int k = 0; k < kConv; ++k) c = fmaf(cw[k], xx[i + 1 + k], c);
+                u[i] = silu(c);
+            }
+        }
         if (GATE && OUT) Pack<T, OS>::unpack(in.rz, zz);
         int rem = OS;                       // steps of this owner inside the range
         if (!FULL) rem = min(t_end - (t0 + OS * ok), OS);

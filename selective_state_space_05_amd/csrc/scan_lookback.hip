@@ -72,14 +72,15 @@ struct Scratch {
     uint32_t *ticket;
 };
 
-template <typename T, int W, int NPL, bool GATE, bool VEC>
+template <typename T, int W, int NPL, bool GATE, bool VEC, bool CONV>
 __global__ __launch_bounds__(64 * W) void scan_lookback_kernel(
     const T *__restrict__ u, const T *__restrict__ delta,
     const float *__restrict__ delta_bias, const float *__restrict__ A,
     const T *__restrict__ Bm, const T *__restrict__ Cm,
     const float *__restrict__ Dskip, const T *__restrict__ z, const float *h0, T *__restrict__ y,
     float *h_last, int64_t L, int dim, int N, int groups_per_batch,
-    int total_groups, int64_t seg_len, int nseg, Scratch s) {
+    int total_groups, int64_t seg_len, int nseg, Scratch s, const float *__restrict__ conv_w,
+    const float *__restrict__ conv_b) {
     constexpr int kSlots = 4 * W * NPL * kCh;
     __shared__ core::Smem<W> sm;
     __shared__ uint32_t sh_item, sh_flag;
@@ -93,8 +94,8 @@ __global__ __launch_bounds__(64 * W) void scan_lookback_kernel(
     const int64_t b = gidx / groups_per_batch;
     const int d0 = (gidx - static_cast<int>(b) * groups_per_batch) * kCh;
 
-    core::Walker<T, W, NPL, GATE, VEC> wk;
-    wk.init(u, delta, delta_bias, A, Bm, Cm, Dskip, z, y, L, dim, N, b, d0);
+    core::Walker<T, W, NPL, GATE, VEC, CONV> wk;
+    wk.init(u, delta, delta_bias, A, Bm, Cm, Dskip, z, y, L, dim, N, b, d0, conv_w, conv_b);
     const int t_begin = static_cast<int>(static_cast<int64_t>(k) * seg_len);
     const int t_end = static_cast<int>(min(L, static_cast<int64_t>(t_begin) + seg_len));
 
@@ -198,7 +199,7 @@ Plan make_plan(const ScanArgs &a) {
     return p;
 }
 
-template <typename T, int W, int NPL>
+template <typename T, int W, int NPL, bool CONV>
 hipError_t launch_typed(const ScanArgs &a, hipStream_t stream) {
     constexpr int kSlots = 4 * W * NPL * kCh;
     const Plan p = make_plan(a);
@@ -218,27 +219,32 @@ hipError_t launch_typed(const ScanArgs &a, hipStream_t stream) {
     e = hipGetLastError();
     if (e == hipSuccess) {
         const bool vec = scan_rows_vectorizable(a);
-        decltype(&scan_lookback_kernel<T, W, NPL, true, true>) kern;
-        if (a.z) kern = vec ? scan_lookback_kernel<T, W, NPL, true, true> : scan_lookback_kernel<T, W, NPL, true, false>;
-        else kern = vec ? scan_lookback_kernel<T, W, NPL, false, true> : scan_lookback_kernel<T, W, NPL, false, false>;
+        decltype(&scan_lookback_kernel<T, W, NPL, true, true, CONV>) kern;
+        if (a.z) kern = vec ? scan_lookback_kernel<T, W, NPL, true, true, CONV> : scan_lookback_kernel<T, W, NPL, true, false, CONV>;
+        else kern = vec ? scan_lookback_kernel<T, W, NPL, false, true, CONV> : scan_lookback_kernel<T, W, NPL, false, false, CONV>;
         hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(items)), dim3(64 * W), 0, stream,
                            static_cast<const T *>(a.u), static_cast<const T *>(a.delta),
                            a.delta_bias, a.A, static_cast<const T *>(a.B),
                            static_cast<const T *>(a.C), a.D, static_cast<const T *>(a.z), a.h0,
                            static_cast<T *>(a.y), a.h_last, a.L, static_cast<int>(a.dim),
                            static_cast<int>(a.N), p.groups_per_batch, p.total_groups, p.seg_len,
-                           p.nseg, s);
+                           p.nseg, s, a.conv_w, a.conv_b);
         e = hipGetLastError();
     }
     const hipError_t ef = hipFreeAsync(mem, stream);
     return e != hipSuccess ? e : ef;
 }
 
+template <typename T, int W, int NPL>
+hipError_t launch_conv(const ScanArgs &a, hipStream_t stream) {
+    return a.conv_w ? launch_typed<T, W, NPL, true>(a, stream) : launch_typed<T, W, NPL, false>(a, stream);
+}
+
 template <typename T>
 hipError_t launch_by_n(const ScanArgs &a, hipStream_t stream) {
-    if (a.N <= 16) return launch_typed<T, 4, 1>(a, stream);
-    if (a.N <= 32) return launch_typed<T, 2, 4>(a, stream);
-    return launch_typed<T, 4, 4>(a, stream);
+    if (a.N <= 16) return launch_conv<T, 4, 1>(a, stream);
+    if (a.N <= 32) return launch_conv<T, 2, 4>(a, stream);
+    return launch_conv<T, 4, 4>(a, stream);
 }
 
 }  // namespace

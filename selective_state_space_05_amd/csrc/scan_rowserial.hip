@@ -24,7 +24,8 @@ __global__ __launch_bounds__(256) void scan_rowserial_kernel(
     const float *__restrict__ delta_bias, const float *__restrict__ A,
     const T *__restrict__ B, const T *__restrict__ C,
     const float *__restrict__ Dskip, const T *__restrict__ z, const float *h0, T *__restrict__ y,
-    float *h_last, int64_t batch, int64_t L, int64_t dim, int N) {
+    float *h_last, int64_t batch, int64_t L, int64_t dim, int N, const float *__restrict__ conv_w,
+    const float *__restrict__ conv_b) {
     const int64_t row = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (row >= batch * dim) return;
     const int64_t b = row / dim;
@@ -38,12 +39,27 @@ __global__ __launch_bounds__(256) void scan_rowserial_kernel(
     }
     const float bias = delta_bias ? delta_bias[d] : 0.0f;
     const float skip = Dskip ? Dskip[d] : 0.0f;
+    // convolution prologue: taps, bias and the three previous inputs
+    float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cb = 0.0f, xp[3] = {0.0f, 0.0f, 0.0f};
+    if (conv_w) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cw[k] = conv_w[d * 4 + k];
+        cb = conv_b ? conv_b[d] : 0.0f;
+    }
     const int64_t rbase = row * L;
     const int64_t bbase = b * N * L;
 
     for (int64_t t = 0; t < L; ++t) {
         const float dl = softplus_libm(Io<T>::load(delta, rbase + t) + bias);
-        const float ut = Io<T>::load(u, rbase + t);
+        float ut = Io<T>::load(u, rbase + t);
+        if (conv_w) {
+            // u_t = silu(cb + w0 x_{t-3} + w1 x_{t-2} + w2 x_{t-1} + w3 x_t)
+            const float xt = ut;
+            ut = silu_libm(fmaf(cw[3], xt, fmaf(cw[2], xp[2], fmaf(cw[1], xp[1], fmaf(cw[0], xp[0], cb)))));
+            xp[0] = xp[1];
+            xp[1] = xp[2];
+            xp[2] = xt;
+        }
         const float du = dl * ut;
         float acc = 0.0f;
 #pragma unroll
@@ -77,7 +93,7 @@ hipError_t launch_typed(const ScanArgs &a, hipStream_t stream) {
                        static_cast<const T *>(a.delta), a.delta_bias, a.A,
                        static_cast<const T *>(a.B), static_cast<const T *>(a.C), a.D,
                        static_cast<const T *>(a.z), a.h0, static_cast<T *>(a.y), a.h_last,
-                       a.batch, a.L, a.dim, static_cast<int>(a.N));
+                       a.batch, a.L, a.dim, static_cast<int>(a.N), a.conv_w, a.conv_b);
     return hipGetLastError();
 }
 

@@ -13,7 +13,7 @@
 //   h_out       = exp(cum_end) h_in + S                                (state pass)
 //   Y_diag[t,p] = sum_{s<=t} (C_t . B_s) exp(cum_t - cum_s) dl_s x_s[p]
 //   Y_off[t,p]  = exp(cum_t) sum_n C_t[n] h_in[p,n]
-//   y[t,p]      = Y_diag + Y_off + D[h] x_t[p]
+//   y[t,p]      = (Y_diag + Y_off + D[h] x_t[p]) silu(z[t,p])   (gate optional)
 //
 // which is the recurrence S_t = a_t S_{t-1} + dl_t x_t B_t^T, y = C_t S_t +
 // D x_t unrolled over a chunk (the cumulative-product closed form of the
@@ -411,13 +411,13 @@ __device__ __forceinline__ void load_h(HRegs<NP> &r, const float *Hin, const Geo
     }
 }
 
-template <int Q, int NP, bool VEC>
+template <int Q, int NP, bool VEC, bool GATE>
 __global__ __launch_bounds__(256) void ssd_output_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt,
     const float *__restrict__ dt_bias, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm,
-    const float *__restrict__ Dskip, const float *__restrict__ Hin, uint16_t *__restrict__ y,
-    Geom g, int runs_per_chunk, int heads_per_run) {
+    const float *__restrict__ Dskip, const uint16_t *__restrict__ z, const float *__restrict__ Hin,
+    uint16_t *__restrict__ y, Geom g, int runs_per_chunk, int heads_per_run) {
     using Sm = OutSmem<Q, NP>;
     constexpr int BP = Sm::BP, XP = Sm::XP, HP = Sm::HP;
     constexpr int NT = Q / 32;          // 32-step blocks per chunk
@@ -461,6 +461,7 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
         const int pcols = g.P - pbase;
         const float skip = Dskip ? Dskip[hh] : 0.0f;
         uint16_t *yg = y + run.b * g.L * static_cast<int64_t>(rowX) + hh * g.P + pbase;
+        const uint16_t *zg = GATE ? z + run.b * g.L * static_cast<int64_t>(rowX) + hh * g.P + pbase : nullptr;
         __syncthreads();   // the previous item's LDS reads are done
         // state entering the chunk; its loads overlap the decay scan
         HRegs<NP> hr;
@@ -563,12 +564,25 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
                     }
                 }
             }
-            // Y_off^T[p][t] = sum_n h_in[p][n] C_t[n]; y = Y_diag (with D x) + 2^cum_t Y_off
+            // Y_off^T[p][t] = sum_n h_in[p][n] C_t[n]; y = (Y_diag (with D x) +
+            // 2^cum_t Y_off) * silu(z) when gated
             const float et = fast_exp2(cum_t);
             const int t = t0 + tl;
+            const uint32_t row = static_cast<uint32_t>(t < g.L ? t : 0) * static_cast<uint32_t>(rowX);
 #pragma unroll
             for (int pt = 0; pt < 2; ++pt) {
                 if (pt * 32 >= pcols) break;
+                // gate values of this lane's step for the tile's 16 head-dimension
+                // columns, loaded ahead of the products below (vector path; the
+                // element path loads them at the stores)
+                uint2 zq[4];
+                if (VEC && GATE) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int p = pt * 32 + 8 * q4 + 4 * half;
+                        zq[q4] = p < pcols ? *reinterpret_cast<const uint2 *>(zg + row + p) : make_uint2(0, 0);
+                    }
+                }
                 f16x yo = zero16();
 #pragma unroll
                 for (int jn = 0; jn < KN; ++jn) {
@@ -579,7 +593,6 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
                     yo = mfma(al, cf[which][jn], yo);
                 }
                 if (t < g.L) {
-                    const uint32_t row = static_cast<uint32_t>(t) * static_cast<uint32_t>(rowX);
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
                         // four consecutive p = pt*32 + 8 q4 + 4 half + 0..3
@@ -587,6 +600,21 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
                         float yv[4];
 #pragma unroll
                         for (int k = 0; k < 4; ++k) yv[k] = fmaf(et, yo[4 * q4 + k], yd[pt][4 * q4 + k]);
+                        if (GATE) {
+                            float zf[4];
+                            if (VEC) {
+                                zf[0] = bits_lo(zq[q4].x);
+                                zf[1] = bits_hi(zq[q4].x);
+                                zf[2] = bits_lo(zq[q4].y);
+                                zf[3] = bits_hi(zq[q4].y);
+                            } else {
+#pragma unroll
+                                for (int k = 0; k < 4; ++k)
+                                    zf[k] = p + k < pcols ? bf16_to_f32(zg[row + p + k]) : 0.0f;
+                            }
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) yv[k] *= silu(zf[k]);
+                        }
                         if (VEC) {
                             if (p < pcols)
                                 *reinterpret_cast<uint2 *>(yg + row + p) =
@@ -627,7 +655,7 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     g.npg = static_cast<int>((a.P + kPG - 1) / kPG);
     auto aligned = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
     const bool vecB = a.N % 8 == 0 && aligned(a.B) && aligned(a.C);
-    const bool vecX = a.P % 8 == 0 && aligned(a.x) && aligned(a.y);
+    const bool vecX = a.P % 8 == 0 && aligned(a.x) && aligned(a.y) && (!a.z || aligned(a.z));
     const int hpr = heads_per_run(a, g.nch);
     const int rpc = static_cast<int>((a.H + hpr - 1) / hpr);
 
@@ -645,6 +673,7 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     const auto *dt = static_cast<const uint16_t *>(a.dt);
     const auto *B = static_cast<const uint16_t *>(a.B);
     const auto *C = static_cast<const uint16_t *>(a.C);
+    const auto *zz = static_cast<const uint16_t *>(a.z);
     const int64_t grid = a.batch * g.nch * rpc;
     const bool vec = vecB && vecX;
     constexpr int nts = state_threads<Q>();
@@ -662,14 +691,11 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
-        if (vec)
-            hipLaunchKernelGGL((ssd_output_kernel<Q, NP, true>), dim3(static_cast<uint32_t>(grid)), dim3(256),
-                               0, stream, x, dt, a.dt_bias, a.A, B, C, a.D, S,
-                               static_cast<uint16_t *>(a.y), g, rpc, hpr);
-        else
-            hipLaunchKernelGGL((ssd_output_kernel<Q, NP, false>), dim3(static_cast<uint32_t>(grid)), dim3(256),
-                               0, stream, x, dt, a.dt_bias, a.A, B, C, a.D, S,
-                               static_cast<uint16_t *>(a.y), g, rpc, hpr);
+        decltype(&ssd_output_kernel<Q, NP, true, true>) kern;
+        if (zz) kern = vec ? ssd_output_kernel<Q, NP, true, true> : ssd_output_kernel<Q, NP, false, true>;
+        else kern = vec ? ssd_output_kernel<Q, NP, true, false> : ssd_output_kernel<Q, NP, false, false>;
+        hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream, x, dt, a.dt_bias,
+                           a.A, B, C, a.D, zz, S, static_cast<uint16_t *>(a.y), g, rpc, hpr);
         e = hipGetLastError();
     }
     const hipError_t ef = hipFreeAsync(mem, stream);

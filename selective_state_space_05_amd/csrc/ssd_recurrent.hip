@@ -6,7 +6,7 @@
 // (ybb.press) section 4), every headdim index p evolves independently:
 //   dl   = softplus(dt + dt_bias[h]);  a = exp(dl * A[h])
 //   S[n] = a * S[n] + (dl * x[p]) * B[n]
-//   y[p] = sum_n C[n] * S[n] + D[h] * x[p]
+//   y[p] = (sum_n C[n] * S[n] + D[h] * x[p]) * silu(z[p])   (z optional)
 // The 64 lanes of a wave are consecutive p of one (b, h), so B and C reads
 // are uniform across the wave.  This is the parity form; the chunked
 // matrix-core form is the fast path for long sequences.
@@ -21,7 +21,7 @@ __global__ __launch_bounds__(64) void ssd_recurrent_kernel(
     const T *__restrict__ x, const T *__restrict__ dt,
     const float *__restrict__ dt_bias, const float *__restrict__ A,
     const T *__restrict__ B, const T *__restrict__ C,
-    const float *__restrict__ Dskip, const float *h0, T *__restrict__ y,
+    const float *__restrict__ Dskip, const T *__restrict__ z, const float *h0, T *__restrict__ y,
     float *h_last, int64_t L, int H, int P, int N, int G) {
     // grid: x = p-tiles of 64, y = head, z = batch
     const int p = blockIdx.x * 64 + threadIdx.x;
@@ -53,7 +53,11 @@ __global__ __launch_bounds__(64) void ssd_recurrent_kernel(
                 acc = fmaf(Io<T>::load(C, bc + n), S[n], acc);
             }
         }
-        if (live) Io<T>::store(y, xi, fmaf(skip, xp, acc));
+        if (live) {
+            float yv = fmaf(skip, xp, acc);
+            if (z) yv *= silu_libm(Io<T>::load(z, xi));
+            Io<T>::store(y, xi, yv);
+        }
     }
     if (h_last && live) {
 #pragma unroll
@@ -69,7 +73,8 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((ssd_recurrent_kernel<T, NS>), grid, dim3(64), 0, stream,
                        static_cast<const T *>(a.x), static_cast<const T *>(a.dt),
                        a.dt_bias, a.A, static_cast<const T *>(a.B),
-                       static_cast<const T *>(a.C), a.D, a.h0, static_cast<T *>(a.y),
+                       static_cast<const T *>(a.C), a.D, static_cast<const T *>(a.z), a.h0,
+                       static_cast<T *>(a.y),
                        a.h_last, a.L, static_cast<int>(a.H), static_cast<int>(a.P),
                        static_cast<int>(a.N), static_cast<int>(a.G));
     return hipGetLastError();

@@ -190,7 +190,10 @@ SSD_LAYER = SSDProblem("mamba2_ssd_layer_bf16", 2, 8192, 48, 64, 128, 1,
 DECODE_2_8B = StepProblem("mamba2.8b_decode_bf16", 256, 5120, 16, "bf16", "scalar",
                           True, True, 12)
 
-SCAN_PROBLEMS = {p.name: p for p in (TINY, MAMBA_130M, MAMBA_2_8B, MILLION)}
+# the Mamba-2.8B layer fed by its convolution prologue (u formed on chip)
+MAMBA_2_8B_CONV = MAMBA_2_8B.replace(name="mamba2.8b_layer_conv_bf16", conv=True)
+
+SCAN_PROBLEMS = {p.name: p for p in (TINY, MAMBA_130M, MAMBA_2_8B, MILLION, MAMBA_2_8B_CONV)}
 SSD_PROBLEMS = {SSD_LAYER.name: SSD_LAYER}
 STEP_PROBLEMS = {DECODE_2_8B.name: DECODE_2_8B}
 

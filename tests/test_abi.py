@@ -55,6 +55,7 @@ def test_header_constants_match_binding():
     assert int(re.search(r"#define MSSM_MAX_DSTATE (\d+)", src).group(1)) == _lib.MAX_DSTATE
     assert int(re.search(r"#define MSSM_SSD_MAX_DSTATE (\d+)", src).group(1)) == _lib.SSD_MAX_DSTATE
     assert int(re.search(r"#define MSSM_SSD_MAX_HEADDIM (\d+)", src).group(1)) == _lib.SSD_MAX_HEADDIM
+    assert int(re.search(r"#define MSSM_CONV_WIDTH (\d+)", src).group(1)) == _lib.CONV_WIDTH
 
 
 def test_version_and_status_strings(L):
@@ -108,6 +109,27 @@ def ssd_h0_call(L, batch=2, seqlen=64, H=4, P=8, N=16, G=1, chunk=0, io=0, param
     return L.mssm_ssd_scalar_fwd_h0(
         p["x"], p["dt"], p["dt_bias"], p["A"], p["B"], p["C"], p["D"], p["h0"], p["y"],
         p["h_last"], _lib.SSDDims(batch, seqlen, H, P, N, G, chunk),
+        _lib.DTypes(io, param), None)
+
+
+def scan_conv_call(L, batch=2, seqlen=64, dim=8, dstate=4, io=0, param=0, **ptrs):
+    p = dict(x=fake(1), conv_w=fake(12), conv_b=fake(13), delta=fake(2), delta_bias=fake(3),
+             A=fake(4), B=fake(5), C=fake(6), D=fake(7), z=fake(8), h0=fake(11), y=fake(9),
+             h_last=fake(10))
+    p.update(ptrs)
+    return L.mssm_selective_scan_fwd_conv(
+        p["x"], p["conv_w"], p["conv_b"], p["delta"], p["delta_bias"], p["A"], p["B"], p["C"],
+        p["D"], p["z"], p["h0"], p["y"], p["h_last"], _lib.ScanDims(batch, seqlen, dim, dstate),
+        _lib.DTypes(io, param), None)
+
+
+def ssd_gated_call(L, batch=2, seqlen=64, H=4, P=8, N=16, G=1, chunk=0, io=0, param=0, **ptrs):
+    p = dict(x=fake(1), dt=fake(2), dt_bias=fake(3), A=fake(4), B=fake(5), C=fake(6),
+             D=fake(7), z=fake(8), h0=fake(11), y=fake(9), h_last=fake(10))
+    p.update(ptrs)
+    return L.mssm_ssd_scalar_fwd_gated(
+        p["x"], p["dt"], p["dt_bias"], p["A"], p["B"], p["C"], p["D"], p["z"], p["h0"],
+        p["y"], p["h_last"], _lib.SSDDims(batch, seqlen, H, P, N, G, chunk),
         _lib.DTypes(io, param), None)
 
 
@@ -215,6 +237,41 @@ def test_ssd_h0_overlapping_an_output(L):
     assert st == _lib.MSSM_ERR_UNSUPPORTED
     assert b"variant" in L.mssm_last_error()
     assert ssd_h0_call(L, seqlen=0, h0=fake(20), h_last=fake(20)) == _lib.MSSM_OK
+
+
+def test_scan_conv_validation(L):
+    assert scan_conv_call(L, conv_w=None) == _lib.MSSM_ERR_INVALID_ARG
+    assert b"conv_w" in L.mssm_last_error()
+    assert scan_conv_call(L, x=None) == _lib.MSSM_ERR_INVALID_ARG
+    assert scan_conv_call(L, dstate=_lib.MAX_DSTATE + 1) == _lib.MSSM_ERR_UNSUPPORTED
+    # the taps are inputs: outputs may not overlap them
+    assert scan_conv_call(L, conv_w=fake(20), y=fake(20) + 8) == _lib.MSSM_ERR_INVALID_ARG
+    assert scan_conv_call(L, conv_b=fake(20), h_last=fake(20)) == _lib.MSSM_ERR_INVALID_ARG
+    prev = L.mssm_force_variant(_lib.VARIANT_SSD_RECURRENT)
+    try:
+        st = scan_conv_call(L, conv_b=None, h0=None, z=None)
+    finally:
+        L.mssm_force_variant(prev)
+    assert st == _lib.MSSM_ERR_UNSUPPORTED       # validation passed; stopped at the variant
+    assert b"variant" in L.mssm_last_error()
+
+
+def test_ssd_gated_validation(L):
+    assert ssd_gated_call(L, x=None) == _lib.MSSM_ERR_INVALID_ARG
+    assert ssd_gated_call(L, H=6, G=4) == _lib.MSSM_ERR_INVALID_ARG
+    assert ssd_gated_call(L, N=257) == _lib.MSSM_ERR_UNSUPPORTED
+    # the gate is an input: no output may overlap it
+    assert ssd_gated_call(L, z=fake(20), y=fake(20) + 2) == _lib.MSSM_ERR_INVALID_ARG
+    assert b"z" in L.mssm_last_error()
+    assert ssd_gated_call(L, z=fake(20), h_last=fake(20) + 4) == _lib.MSSM_ERR_INVALID_ARG
+    assert ssd_gated_call(L, batch=0) == _lib.MSSM_OK
+    prev = L.mssm_force_variant(_lib.VARIANT_CHUNKED)
+    try:
+        st = ssd_gated_call(L, z=None, h0=None)
+    finally:
+        L.mssm_force_variant(prev)
+    assert st == _lib.MSSM_ERR_UNSUPPORTED       # optional z and h0 both absent: validation passes
+    assert b"variant" in L.mssm_last_error()
 
 
 @pytest.mark.parametrize("name", ["state", "x", "dt", "A", "B", "C", "y"])

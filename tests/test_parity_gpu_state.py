@@ -158,6 +158,64 @@ def test_ssd_in_pieces_equals_whole(dev, variant):
 
 
 # ---------------------------------------------------------------------------
+# SSD with a SiLU gate on the output
+# ---------------------------------------------------------------------------
+SSD_GATED_CASES = [
+    # batch, L, H, P, N, G, io, with h0
+    (1, 300, 2, 8, 16, 1, "bf16", False),
+    (2, 513, 4, 64, 128, 1, "bf16", True),    # three chunks, ragged, from h0
+    (1, 1000, 3, 40, 7, 3, "bf16", False),    # two head-dim tiles, element path
+    (1, 600, 2, 80, 96, 1, "bf16", True),     # two 64-column head-dim slices
+    (1, 77, 6, 5, 7, 3, "f32", True),
+]
+
+
+@pytest.mark.parametrize("variant", SSD_VARIANTS)
+@pytest.mark.parametrize("case", SSD_GATED_CASES)
+def test_ssd_gated(dev, variant, case):
+    import selective_state_space_05_amd as mssm
+    from selective_state_space_05_amd.api import forced_variant
+    batch, L, H, P, N, G, io, with_h0 = case
+    if variant == _lib.VARIANT_SSD_CHUNKED and io != "bf16":
+        pytest.skip("the matrix-core form takes bf16 activations only")
+    announce("ssd gated variant=%d %s" % (variant, case))
+    p = inputs.SSDProblem("case", batch, L, H, P, N, G, io, 700 + L, gate=True)
+    s = inputs.ssd_inputs(p)
+    h0 = inputs.initial_state((batch, H, P, N), 5 + N) if with_h0 else None
+    t = ssd_to_dev(s, io, dev)
+    with forced_variant(variant):
+        y, h = mssm.ssd_scalar_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"],
+                                   t["dt_bias"], z=t["z"],
+                                   h0=None if h0 is None else torch.from_numpy(h0).to(dev))
+    torch.cuda.synchronize()
+    yo, ho = oracle.ssd(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["dt_bias"],
+                        h0=h0, z=s["z"])
+    gates.check(ssd_rows_of(f64(y)), ssd_rows_of(yo), io, "y")
+    gates.check_state(f64(h), ho, io, "h_last")
+
+
+def test_ssd_gated_full_size_sampled_rows(dev):
+    """The Mamba-2 layer with a gate, in the bench's launch configuration."""
+    import selective_state_space_05_amd as mssm
+    p = inputs.SSD_LAYER.replace(gate=True)
+    announce("ssd gated workload=%s" % p.name)
+    s = inputs.ssd_inputs(p)
+    t = ssd_to_dev(s, p.io, dev)
+    y, h = mssm.ssd_scalar_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["dt_bias"],
+                               z=t["z"])
+    torch.cuda.synchronize()
+    y, h = f64(y), f64(h)
+    rng = np.random.default_rng(8)
+    rows = [(0, 0, 0), (p.batch - 1, p.nheads - 1, p.headdim - 1)] + [
+        (int(rng.integers(p.batch)), int(rng.integers(p.nheads)), int(rng.integers(p.headdim)))
+        for _ in range(6)]
+    yo, ho = oracle.ssd_rows(rows, s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"],
+                             s["dt_bias"], z=s["z"])
+    gates.check(np.stack([y[b, :, hh, pp] for b, hh, pp in rows]), yo, p.io, "y")
+    gates.check_state(np.stack([h[b, hh, pp] for b, hh, pp in rows]), ho, p.io, "h_last")
+
+
+# ---------------------------------------------------------------------------
 # decode step
 # ---------------------------------------------------------------------------
 def step_to_dev(d, io, dev, offset=0):
