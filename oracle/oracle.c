@@ -41,6 +41,7 @@
  * to a single thread.
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <stddef.h>
 #ifdef _OPENMP
@@ -229,4 +230,112 @@ void oracle_conv1d_silu_f64(int64_t batch, int64_t D, int64_t L, int64_t K,
             u[r * L + t] = oracle_silu(acc);
         }
     }
+}
+
+/*
+ * Backward of the selective scan: the reverse-mode derivative of the loop of
+ * oracle_selective_scan_f64 (the recurrence of [ybb] sections 1 and 3.1 and
+ * [mhpq] section 2.2; the forward + backward training use of the block in
+ * [mlqm] section 3.2).  Given the output gradients dy (batch, D, L) and
+ * dh_last (batch, D, N) (nullable -> 0), it forms the gradients of every
+ * input.  For each row (b, d), the states h_t of the row are recomputed
+ * forward and kept; then, with x_t = delta + bias, dl_t = softplus(x_t),
+ * a_t[n] = exp(dl_t A[d,n]), s_t = sum_n C_t[n] h_t[n] + D u_t and
+ * y_t = s_t silu(z_t), for t = L-1 down to 0:
+ *
+ *   ds_t     = dy_t silu(z_t)                    dz_t = dy_t s_t silu'(z_t)
+ *   dh_t[n]  = ds_t C_t[n] + a_{t+1}[n] dh_{t+1}[n]   (dh_L := dh_last)
+ *   dC_t[n] += ds_t h_t[n]                       dD    += ds_t u_t
+ *   dA[n]   += dh_t[n] h_{t-1}[n] a_t[n] dl_t    dB_t[n] += dh_t[n] dl_t u_t
+ *   du_t     = ds_t D + sum_n dh_t[n] dl_t B_t[n]
+ *   d(dl_t)  = sum_n dh_t[n] (h_{t-1}[n] a_t[n] A[n] + B_t[n] u_t)
+ *   ddelta_t = d(dl_t) sigmoid(x_t)              dbias += ddelta_t
+ *
+ * and dh0 = a_0 dh_0.  silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z))).
+ * dB, dC sum over channels, dA, dD, dbias over batches.  Outputs: du,
+ * ddelta, dz like u (dz only when z is given); dB, dC like B; dA like A;
+ * dD, ddelta_bias (D); dh0 like h0.  Every output but du and ddelta is
+ * nullable.  Single-threaded; rows in order, so sums are deterministic.
+ */
+void oracle_selective_scan_bwd_f64(int64_t batch, int64_t L, int64_t D, int64_t N,
+                                   const double *u, const double *delta,
+                                   const double *delta_bias, const double *A,
+                                   const double *B, const double *C,
+                                   const double *Dskip, const double *z,
+                                   const double *h0, const double *dy,
+                                   const double *dh_last, double *du, double *ddelta,
+                                   double *ddelta_bias, double *dA, double *dB,
+                                   double *dC, double *dD, double *dz, double *dh0)
+{
+    double *hist = (double *)malloc(sizeof(double) * (size_t)((L + 1) * N));
+    double *dh = (double *)malloc(sizeof(double) * (size_t)N);
+    double *gB = (double *)calloc((size_t)(batch * N * L), sizeof(double));
+    double *gC = (double *)calloc((size_t)(batch * N * L), sizeof(double));
+    double *gA = (double *)calloc((size_t)(D * N), sizeof(double));
+    double *gD = (double *)calloc((size_t)D, sizeof(double));
+    double *gbias = (double *)calloc((size_t)D, sizeof(double));
+    for (int64_t r = 0; r < batch * D; ++r) {
+        int64_t b = r / D, d = r % D;
+        const double *ur = u + r * L, *dr = delta + r * L;
+        const double *Ad = A + d * N;
+        const double *Bb = B + b * N * L, *Cb = C + b * N * L;
+        double bias = delta_bias ? delta_bias[d] : 0.0;
+        double skip = Dskip ? Dskip[d] : 0.0;
+        /* forward: hist[(t + 1) N + n] = h_t[n], hist[n] = the initial state */
+        for (int64_t n = 0; n < N; ++n) hist[n] = h0 ? h0[r * N + n] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            double dl = oracle_softplus(dr[t] + bias);
+            for (int64_t n = 0; n < N; ++n)
+                hist[(t + 1) * N + n] = exp(dl * Ad[n]) * hist[t * N + n] +
+                                        dl * Bb[n * L + t] * ur[t];
+        }
+        /* reverse: dh carries a_{t+1} dh_{t+1} into step t */
+        for (int64_t n = 0; n < N; ++n) dh[n] = dh_last ? dh_last[r * N + n] : 0.0;
+        for (int64_t t = L - 1; t >= 0; --t) {
+            double x = dr[t] + bias;
+            double dl = oracle_softplus(x);
+            double sig = 1.0 / (1.0 + exp(-x));
+            double dyt = dy[r * L + t];
+            double ds = dyt;
+            if (z) {
+                double zt = z[r * L + t];
+                double sz = 1.0 / (1.0 + exp(-zt));
+                double s = skip * ur[t];
+                for (int64_t n = 0; n < N; ++n) s += Cb[n * L + t] * hist[(t + 1) * N + n];
+                ds = dyt * oracle_silu(zt);
+                if (dz) dz[r * L + t] = dyt * s * sz * (1.0 + zt * (1.0 - sz));
+            }
+            gD[d] += ds * ur[t];
+            double dut = ds * skip;
+            double ddl = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                double Bt = Bb[n * L + t];
+                double a = exp(dl * Ad[n]);
+                double hprev = hist[t * N + n];
+                dh[n] += ds * Cb[n * L + t];
+                gC[b * N * L + n * L + t] += ds * hist[(t + 1) * N + n];
+                gA[d * N + n] += dh[n] * hprev * a * dl;
+                gB[b * N * L + n * L + t] += dh[n] * dl * ur[t];
+                dut += dh[n] * dl * Bt;
+                ddl += dh[n] * (hprev * a * Ad[n] + Bt * ur[t]);
+                dh[n] *= a;
+            }
+            du[r * L + t] = dut;
+            ddelta[r * L + t] = ddl * sig;
+            gbias[d] += ddl * sig;
+        }
+        if (dh0)
+            for (int64_t n = 0; n < N; ++n) dh0[r * N + n] = dh[n];
+    }
+    for (int64_t i = 0; i < batch * N * L; ++i) {
+        if (dB) dB[i] = gB[i];
+        if (dC) dC[i] = gC[i];
+    }
+    for (int64_t i = 0; i < D * N; ++i)
+        if (dA) dA[i] = gA[i];
+    for (int64_t i = 0; i < D; ++i) {
+        if (dD) dD[i] = gD[i];
+        if (ddelta_bias) ddelta_bias[i] = gbias[i];
+    }
+    free(hist); free(dh); free(gB); free(gC); free(gA); free(gD); free(gbias);
 }

@@ -61,6 +61,8 @@ def _bind(path: str):
         i64, i64, i64, i64, i64, i64, _dp, _dp, _dp, _dp, _dp, _dp,
         _dp, _dp, _dp, _dp, _dp, ctypes.c_int]
     lib.oracle_ssd_f64.restype = None
+    lib.oracle_selective_scan_bwd_f64.argtypes = [i64, i64, i64, i64] + [_dp] * 20
+    lib.oracle_selective_scan_bwd_f64.restype = None
     lib.oracle_conv1d_silu_f64.argtypes = [i64, i64, i64, i64, _dp, _dp, _dp, _dp]
     lib.oracle_conv1d_silu_f64.restype = None
     lib.oracle_softplus_f64.argtypes = [ctypes.c_double]
@@ -131,6 +133,37 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(h0), _ptr(y), _ptr(h_last),
         int(nthreads))
     return y, h_last
+
+
+def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=None,
+                       dh_last=None, lib=None):
+    """Float64 gradients of the selective scan for output gradients ``dy``
+    (like u) and ``dh_last`` (batch, Dch, N; None -> 0).
+
+    Returns a dict with du, ddelta, dA, dB, dC, and dD, dz, ddelta_bias,
+    dh0 for the optional inputs that were given (None otherwise).
+    """
+    u, delta, A, B, C, dy = map(_f64, (u, delta, A, B, C, dy))
+    D, z, delta_bias, h0, dh_last = map(_f64, (D, z, delta_bias, h0, dh_last))
+    batch, Dch, L = u.shape
+    N = A.shape[1]
+    assert delta.shape == u.shape and dy.shape == u.shape and A.shape == (Dch, N)
+    assert B.shape == (batch, N, L) and C.shape == (batch, N, L)
+    assert z is None or z.shape == u.shape
+    assert h0 is None or h0.shape == (batch, Dch, N)
+    assert dh_last is None or dh_last.shape == (batch, Dch, N)
+    out = {"du": np.empty_like(u), "ddelta": np.empty_like(u), "dA": np.empty_like(A),
+           "dB": np.empty_like(B), "dC": np.empty_like(C),
+           "dD": None if D is None else np.empty(Dch),
+           "dz": None if z is None else np.empty_like(u),
+           "ddelta_bias": None if delta_bias is None else np.empty(Dch),
+           "dh0": None if h0 is None else np.empty((batch, Dch, N))}
+    (lib or _load()).oracle_selective_scan_bwd_f64(
+        batch, L, Dch, N, _ptr(u), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C),
+        _ptr(D), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(out["du"]),
+        _ptr(out["ddelta"]), _ptr(out["ddelta_bias"]), _ptr(out["dA"]), _ptr(out["dB"]),
+        _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["dh0"]))
+    return out
 
 
 def conv1d_silu(x, conv_w, conv_b=None, lib=None):
