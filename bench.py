@@ -96,6 +96,7 @@ KERNEL_SOURCES = {
              "scan_rowserial.hip"),
     "ssd": ("device_math.h", "ssd_chunked.hip", "ssd_recurrent.hip"),
     "step": ("device_math.h", "state_update.hip"),
+    "bwd": ("device_math.h", "scan_bwd_rowserial.hip"),
 }
 
 
@@ -107,6 +108,8 @@ def workload_family(workload: str) -> str:
         return "ssd"
     if workload in inputs.STEP_PROBLEMS:
         return "step"
+    if workload in inputs.BWD_PROBLEMS:
+        return "bwd"
     raise SystemExit("unknown workload %s" % workload)
 
 
@@ -394,6 +397,94 @@ class SSDBench:
                 "chunk": self.chunk}
 
 
+def bwd_slots(p) -> float:
+    """Algorithmic VALU issue slots of one backward.
+
+    Per element (b, t, d, n): the forward recomputed twice (state pass and
+    segment recompute: 2 x (dl*A, 2^x = 2, (dl*u)*B, FMA) = 10) and the
+    reverse step (2^x = 2, dh FMA, dC product, dA 2, dB product, du FMA,
+    d(dl) 2, carry = 10).  Per (b, t, d): softplus three times (7 each),
+    the logistic of x (4), dl*u twice, the gate's silu and derivative (10).
+    """
+    per_elem = 20
+    per_row_step = 3 * 7 + 4 + 2 + (10 if p.gate else 0)
+    return per_elem * p.elements + per_row_step * p.batch * p.dim * p.seqlen
+
+
+class BwdBench(ScanBench):
+    """Backward of the selective scan (mssm_selective_scan_bwd)."""
+
+    def __init__(self, p, dev, torch):
+        super().__init__(p, dev, torch)
+        from selective_state_space_05_amd import inputs
+        self.g = inputs.output_grads(p)
+
+    def upload(self):
+        t = super().upload()
+        t["dy"] = self.torch.from_numpy(self.g["dy"]).to(self.io_t).to(self.dev)
+        t["dh_last"] = self.torch.from_numpy(self.g["dh_last"]).to(self.dev)
+        return t
+
+    def step(self, t):
+        t["grads"] = self.api.selective_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["dy"],
+                                                 D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
+                                                 dh_last=t["dh_last"])
+
+    def roofline(self, sec):
+        slots = bwd_slots(self.p)
+        a = slots / sec / 1e12
+        return {"bound": "alu", "achieved": a, "peak": VALU_PEAK_TSLOTS,
+                "unit": "T VALU lane-slots/s", "frac": a / VALU_PEAK_TSLOTS,
+                "slots_per_launch": slots}
+
+    def _row_oracle(self, b, d, nthreads=0):
+        from oracle import oracle
+        x, g = self.x, self.g
+        sl = lambda a: None if a is None else a[b:b + 1, d:d + 1]   # noqa: E731
+        pr = lambda a: None if a is None else a[d:d + 1]            # noqa: E731
+        return oracle.selective_scan_bwd(sl(x["u"]), sl(x["delta"]), pr(x["A"]), x["B"][b:b + 1],
+                                         x["C"][b:b + 1], sl(g["dy"]), D=pr(x["D"]), z=sl(x["z"]),
+                                         delta_bias=pr(x["delta_bias"]),
+                                         dh_last=g["dh_last"][b:b + 1, d:d + 1])
+
+    def parity(self, t):
+        """du and ddelta of sampled rows depend on their row alone: the
+        oracle's backward of that row gives them exactly."""
+        p = self.p
+        rng = np.random.default_rng(321)
+        rows = [(0, 0), (p.batch - 1, p.dim - 1)] + [
+            (int(rng.integers(p.batch)), int(rng.integers(p.dim))) for _ in range(2)]
+        du = t["grads"]["du"].float().cpu().numpy().astype(np.float64)
+        dd = t["grads"]["ddelta"].float().cpu().numpy().astype(np.float64)
+        gu, gd = [], []
+        for b, d in rows:
+            o = self._row_oracle(b, d)
+            gu.append((du[b, d], o["du"][0, 0]))
+            gd.append((dd[b, d], o["ddelta"][0, 0]))
+        return (len(rows), g1(np.stack([a for a, _ in gu]), np.stack([r for _, r in gu])),
+                g1(np.stack([a for a, _ in gd]), np.stack([r for _, r in gd])))
+
+    cpu_cores = 1   # the oracle's backward runs on one thread
+
+    def cpu_baseline(self, threads, budget_s=10.0):
+        """The oracle's backward on whole rows (single-threaded, as the
+        oracle is), as many as fit in about ``budget_s``."""
+        p = self.p
+        t0 = time.time()
+        done = 0
+        while done == 0 or time.time() - t0 < budget_s:
+            self._row_oracle(done % p.batch, done % p.dim)
+            done += 1
+        cpu_s = time.time() - t0
+        return done * p.seqlen * p.dstate / cpu_s, "%d (batch, channel) rows, full length %d, float64, %.1f s" % (
+            done, p.seqlen, cpu_s)
+
+    def config(self):
+        c = super().config()
+        c["pass"] = "backward"
+        return c
+
+
 class StepBench:
     """One decode step (selective_state_update) on a cached float32 state."""
     dtype = "f32"
@@ -521,10 +612,14 @@ def main():
         p = inputs.STEP_PROBLEMS[args.workload]
         print("[bench] workload %s: drawing inputs" % p.name, file=sys.stderr, flush=True)
         wb = StepBench(p, dev, torch)
+    elif args.workload in inputs.BWD_PROBLEMS:
+        p = inputs.BWD_PROBLEMS[args.workload]
+        print("[bench] workload %s: drawing inputs" % p.name, file=sys.stderr, flush=True)
+        wb = BwdBench(p, dev, torch)
     else:
         raise SystemExit("unknown workload %s; choose from %s" % (
             args.workload, sorted(inputs.SCAN_PROBLEMS) + sorted(inputs.SSD_PROBLEMS) +
-            sorted(inputs.STEP_PROBLEMS)))
+            sorted(inputs.STEP_PROBLEMS) + sorted(inputs.BWD_PROBLEMS)))
 
     footprint = p.min_traffic_bytes()
     rotate = args.rotate or max(1, min(4, -(-(1 << 30) // footprint)))
@@ -602,7 +697,8 @@ def main():
         threads = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "16")), 16)
         print("[bench] CPU oracle baseline (%d threads)" % threads, file=sys.stderr, flush=True)
         v, sample = wb.cpu_baseline(threads)
-        out["cpu_baseline"] = {"value": v, "unit": "elements/s", "cores": threads,
+        out["cpu_baseline"] = {"value": v, "unit": "elements/s",
+                               "cores": getattr(wb, "cpu_cores", threads),
                                "kind": "oracle", "sample": sample}
 
     print(json.dumps(out), flush=True)

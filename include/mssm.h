@@ -165,6 +165,42 @@ MSSM_API mssm_status mssm_selective_scan_fwd_conv(const void *x, const float *co
                                          mssm_scan_dims dims, mssm_dtypes dtypes,
                                          void *stream);
 
+/*
+ * Backward of the selective scan (the reverse-mode derivative of
+ * mssm_selective_scan_fwd_h0; [mlqm] section 3.2: the block is trained,
+ * forward and backward).  Given the forward's inputs and the gradients of a
+ * loss with respect to y (dy) and h_last (dh_last), it writes the loss's
+ * gradients with respect to every input.  The states are recomputed from
+ * the inputs (stored every few steps in stream-ordered scratch), not read
+ * from the forward.
+ *
+ * Inputs: u ... h0 as for mssm_selective_scan_fwd_h0;
+ *   dy       (batch, dim, L), dtype `io`     required
+ *   dh_last  (batch, dim, N) float32         nullable -> 0
+ * Outputs, all float32 whatever the I/O dtype (like h_last):
+ *   du, ddelta    (batch, dim, L) float32      required
+ *   dz            (batch, dim, L) float32      nullable; needs z
+ *   dB, dC        (batch, N, L) float32        nullable
+ *   dA            (dim, N) float32             nullable
+ *   dD, ddelta_bias (dim) float32              nullable (gradients at D
+ *                                              = 0 / bias = 0 when those
+ *                                              inputs are null)
+ *   dh0           (batch, dim, N) float32      nullable
+ * dB, dC sum over channels and dA, dD, ddelta_bias over batches, with
+ * float32 atomic additions: their last bits depend on the order.  Errors as
+ * for the forward, plus MSSM_ERR_INVALID_ARG for dz without z or any output
+ * overlapping an input or another output.
+ */
+MSSM_API mssm_status mssm_selective_scan_bwd(const void *u, const void *delta,
+                                    const float *delta_bias, const float *A,
+                                    const void *B, const void *C, const float *D,
+                                    const void *z, const float *h0, const void *dy,
+                                    const float *dh_last, float *du, float *ddelta,
+                                    float *ddelta_bias, float *dA, float *dB,
+                                    float *dC, float *dD, float *dz, float *dh0,
+                                    mssm_scan_dims dims, mssm_dtypes dtypes,
+                                    void *stream);
+
 /* Sizes of a Mamba-2 scalar-decay (SSD) problem. */
 typedef struct {
     int64_t batch;

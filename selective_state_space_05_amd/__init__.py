@@ -10,6 +10,7 @@ call raises -- there is no CPU fallback.
 """
 from .api import (  # noqa: F401
     MssmError,
+    selective_scan_bwd,
     selective_scan_conv_fwd,
     selective_scan_fwd,
     selective_state_update,
@@ -17,5 +18,5 @@ from .api import (  # noqa: F401
     version,
 )
 
-__all__ = ["MssmError", "selective_scan_conv_fwd", "selective_scan_fwd", "selective_state_update",
+__all__ = ["MssmError", "selective_scan_bwd", "selective_scan_conv_fwd", "selective_scan_fwd", "selective_state_update",
            "ssd_scalar_fwd", "version"]

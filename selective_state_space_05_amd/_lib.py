@@ -40,6 +40,7 @@ EXPORTED = (
     "mssm_ssd_scalar_fwd",
     "mssm_selective_scan_fwd_h0",
     "mssm_selective_scan_fwd_conv",
+    "mssm_selective_scan_bwd",
     "mssm_ssd_scalar_fwd_h0",
     "mssm_ssd_scalar_fwd_gated",
     "mssm_selective_state_update",
@@ -91,6 +92,10 @@ def _declare(L):
     L.mssm_selective_scan_fwd_conv.argtypes = [vp, fp, fp, vp, fp, fp, vp, vp, fp, vp, fp,
                                                vp, fp, ScanDims, DTypes, vp]
     L.mssm_selective_scan_fwd_conv.restype = ctypes.c_int
+    L.mssm_selective_scan_bwd.argtypes = [vp, vp, fp, fp, vp, vp, fp, vp, fp, vp, fp,
+                                          vp, vp, fp, fp, fp, fp, fp, vp, fp,
+                                          ScanDims, DTypes, vp]
+    L.mssm_selective_scan_bwd.restype = ctypes.c_int
     L.mssm_ssd_scalar_fwd_h0.argtypes = [vp, vp, fp, fp, vp, vp, fp, fp, vp, fp,
                                          SSDDims, DTypes, vp]
     L.mssm_ssd_scalar_fwd_h0.restype = ctypes.c_int

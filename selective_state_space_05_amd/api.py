@@ -193,6 +193,55 @@ def selective_scan_conv_fwd(x, conv_w, delta, A, B, C, D=None, z=None, delta_bia
     return y, h_last
 
 
+def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, h0=None,
+                       dh_last=None):
+    """Gradients of the selective scan on the GPU for output gradients ``dy``
+    (like u) and ``dh_last`` (batch, dim, N) float32 (None: zero).
+
+    Returns a dict of float32 tensors: du, ddelta (batch, dim, L); dA
+    (dim, N); dB, dC (batch, N, L); dD, ddelta_bias (dim,); dz (batch, dim,
+    L, when z is given); dh0 (batch, dim, N).
+    """
+    L = _lib.lib()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    io = u.dtype
+    for name, t in (("u", u), ("delta", delta), ("B", B), ("C", C), ("z", z), ("dy", dy)):
+        _need(t, name, io, dev)
+    for name, t in (("A", A), ("D", D), ("delta_bias", delta_bias), ("h0", h0),
+                    ("dh_last", dh_last)):
+        _need(t, name, torch.float32, dev)
+    batch, dim, seqlen = u.shape
+    N = A.shape[1]
+    if delta.shape != u.shape or dy.shape != u.shape or (z is not None and z.shape != u.shape):
+        raise ValueError("u, delta, z, dy must share one (batch, dim, L) shape")
+    if tuple(A.shape) != (dim, N):
+        raise ValueError("A must be (dim, N)")
+    if tuple(B.shape) != (batch, N, seqlen) or tuple(C.shape) != (batch, N, seqlen):
+        raise ValueError("B and C must be (batch, N, L)")
+    for name, t in (("h0", h0), ("dh_last", dh_last)):
+        if t is not None and tuple(t.shape) != (batch, dim, N):
+            raise ValueError("%s must be (batch, dim, N)" % name)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"du": torch.empty(u.shape, **f32), "ddelta": torch.empty(u.shape, **f32),
+         "dA": torch.empty((dim, N), **f32), "dB": torch.empty((batch, N, seqlen), **f32),
+         "dC": torch.empty((batch, N, seqlen), **f32), "dD": torch.empty((dim,), **f32),
+         "ddelta_bias": torch.empty((dim,), **f32),
+         "dz": None if z is None else torch.empty(u.shape, **f32),
+         "dh0": torch.empty((batch, dim, N), **f32)}
+    dims = _lib.ScanDims(batch, seqlen, dim, N)
+    dtp = _lib.DTypes(_io_dtype(u), _lib.MSSM_F32)
+    with torch.cuda.device(dev):
+        st = L.mssm_selective_scan_bwd(
+            _ptr(u), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(g["du"]), _ptr(g["ddelta"]),
+            _ptr(g["ddelta_bias"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
+            _ptr(g["dz"]), _ptr(g["dh0"]), dims, dtp, _stream_handle(dev))
+    _check(st)
+    return g
+
+
 def ssd_scalar_fwd(x, dt, A, B, C, D=None, dt_bias=None, chunk=0,
                    return_last_state=True, out=None, h_out=None, h0=None, z=None):
     """Mamba-2 scalar-decay forward on the GPU.

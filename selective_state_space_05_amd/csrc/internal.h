@@ -70,6 +70,38 @@ struct StepArgs {
     IoType io;
 };
 
+// One selective-scan backward, already validated: the forward's inputs (as in
+// ScanArgs), the output gradients dy (like u) and dh_last (batch, dim, N;
+// may be null), and the gradient outputs, all float32: du, ddelta, dz
+// (batch, dim, L), dB, dC (batch, N, L), dA (dim, N), dD and ddelta_bias
+// (dim), dh0 (batch, dim, N).  dA, dB, dC, dD and ddelta_bias are
+// accumulated into and must hold zeros on entry.  Optional outputs may be
+// null.
+struct BwdArgs {
+    const void *u;
+    const void *delta;
+    const float *delta_bias;
+    const float *A;
+    const void *B;
+    const void *C;
+    const float *D;
+    const void *z;
+    const float *h0;
+    const void *dy;
+    const float *dh_last;
+    float *du;
+    float *ddelta;
+    float *ddelta_bias;
+    float *dA;
+    float *dB;
+    float *dC;
+    float *dD;
+    float *dz;
+    float *dh0;
+    int64_t batch, L, dim, N;
+    IoType io;
+};
+
 // Each launcher queues its kernel(s) on `stream` and returns the launch
 // status.  Shapes have been checked against the launcher's limits by the
 // caller (see the *_supported helpers).
@@ -88,6 +120,11 @@ bool scan_rows_vectorizable(const ScanArgs &a);
 // Chunk-parallel variant; allocates its look-back scratch stream-ordered.
 hipError_t launch_scan_lookback(const ScanArgs &a, hipStream_t stream);
 bool scan_lookback_supported(const ScanArgs &a);
+
+// Backward: one lane per (batch, channel) row; stream-ordered scratch for the
+// stored states.
+hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t stream);
+bool scan_bwd_supported(const BwdArgs &a);
 
 hipError_t launch_state_update(const StepArgs &a, hipStream_t stream);
 bool state_update_supported(const StepArgs &a);

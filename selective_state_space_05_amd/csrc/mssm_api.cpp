@@ -332,6 +332,95 @@ mssm_status mssm_selective_scan_fwd_conv(const void *x, const float *conv_w,
                     conv_w, conv_b);
 }
 
+mssm_status mssm_selective_scan_bwd(const void *u, const void *delta, const float *delta_bias,
+                                    const float *A, const void *B, const void *C, const float *D,
+                                    const void *z, const float *h0, const void *dy,
+                                    const float *dh_last, float *du, float *ddelta,
+                                    float *ddelta_bias, float *dA, float *dB, float *dC, float *dD,
+                                    float *dz, float *dh0, mssm_scan_dims dims, mssm_dtypes dtypes,
+                                    void *stream) {
+    g_last_error.clear();
+    if (mssm_status s = check_dtypes(dtypes)) return s;
+    const int64_t batch = dims.batch, L = dims.seqlen, dim = dims.dim, N = dims.dstate;
+    if (batch < 0 || L < 0 || dim < 0)
+        return fail(MSSM_ERR_INVALID_ARG, "negative size (batch %lld, L %lld, dim %lld)",
+                    (long long)batch, (long long)L, (long long)dim);
+    if (N < 1) return fail(MSSM_ERR_INVALID_ARG, "dstate must be >= 1, got %lld", (long long)N);
+    if (N > MSSM_MAX_DSTATE)
+        return fail(MSSM_ERR_UNSUPPORTED, "dstate %lld exceeds MSSM_MAX_DSTATE (%d)",
+                    (long long)N, MSSM_MAX_DSTATE);
+    if (dz && !z) return fail(MSSM_ERR_INVALID_ARG, "dz given without z");
+    const int64_t esz = dtypes.io == MSSM_F32 ? 4 : 2;
+    int64_t rows, act, act_bytes, act4, bc, bc_bytes, bc4, dn, hl;
+    if (!mul_ok(batch, dim, &rows) || !mul_ok(rows, L, &act) || !mul_ok(act, esz, &act_bytes) ||
+        !mul_ok(act, 4, &act4) || !mul_ok(batch, N, &bc) || !mul_ok(bc, L, &bc) ||
+        !mul_ok(bc, esz, &bc_bytes) || !mul_ok(bc, 4, &bc4) || !mul_ok(dim, N, &dn) ||
+        !mul_ok(rows, N, &hl) || !mul_ok(hl, 4, &hl))
+        return fail(MSSM_ERR_INVALID_ARG, "sizes overflow int64");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // the accumulated gradients start from zero, whatever else happens
+    auto zero_sums = [&]() -> hipError_t {
+        hipError_t e = hipSuccess;
+        if (e == hipSuccess && dB) e = zero_fill(dB, bc, st);
+        if (e == hipSuccess && dC) e = zero_fill(dC, bc, st);
+        if (e == hipSuccess && dA) e = zero_fill(dA, dn, st);
+        if (e == hipSuccess && dD) e = zero_fill(dD, dim, st);
+        if (e == hipSuccess && ddelta_bias) e = zero_fill(ddelta_bias, dim, st);
+        return e;
+    };
+    if (rows == 0 || L == 0) {
+        const Range outs0[] = {range("dB", dB, bc4), range("dC", dC, bc4), range("dA", dA, dn * 4),
+                               range("dD", dD, dim * 4), range("ddelta_bias", ddelta_bias, dim * 4),
+                               range("dh0", dh0, hl)};
+        for (int i = 0; i < 6; ++i)
+            for (int j = i + 1; j < 6; ++j)
+                if (overlaps(outs0[i], outs0[j]))
+                    return fail(MSSM_ERR_INVALID_ARG, "%s overlaps %s", outs0[i].name, outs0[j].name);
+        hipError_t e = zero_sums();
+        // with L == 0 the initial state is the final state: dh0 = dh_last
+        if (e == hipSuccess && dh0 && rows > 0) {
+            e = dh_last ? hipMemcpyAsync(dh0, dh_last, hl, hipMemcpyDeviceToDevice, st)
+                        : zero_fill(dh0, rows * N, st);
+        }
+        if (e != hipSuccess) return hip_fail(e, "zero-fill of the gradients");
+        g_last_variant = MSSM_VARIANT_AUTO;
+        return MSSM_OK;
+    }
+    if (!u) return fail(MSSM_ERR_INVALID_ARG, "u is null");
+    if (!delta) return fail(MSSM_ERR_INVALID_ARG, "delta is null");
+    if (!A) return fail(MSSM_ERR_INVALID_ARG, "A is null");
+    if (!B) return fail(MSSM_ERR_INVALID_ARG, "B is null");
+    if (!C) return fail(MSSM_ERR_INVALID_ARG, "C is null");
+    if (!dy) return fail(MSSM_ERR_INVALID_ARG, "dy is null");
+    if (!du) return fail(MSSM_ERR_INVALID_ARG, "du is null");
+    if (!ddelta) return fail(MSSM_ERR_INVALID_ARG, "ddelta is null");
+    const Range ins[] = {
+        range("u", u, act_bytes),          range("delta", delta, act_bytes),
+        range("z", z, act_bytes),          range("B", B, bc_bytes),
+        range("C", C, bc_bytes),           range("A", A, dn * 4),
+        range("D", D, dim * 4),            range("delta_bias", delta_bias, dim * 4),
+        range("h0", h0, hl),               range("dy", dy, act_bytes),
+        range("dh_last", dh_last, hl)};
+    const Range outs[] = {
+        range("du", du, act4),             range("ddelta", ddelta, act4),
+        range("dz", dz, act4),             range("dB", dB, bc4),
+        range("dC", dC, bc4),              range("dA", dA, dn * 4),
+        range("dD", dD, dim * 4),          range("ddelta_bias", ddelta_bias, dim * 4),
+        range("dh0", dh0, hl)};
+    if (mssm_status c = check_overlaps(ins, 11, outs, 9, nullptr, nullptr)) return c;
+
+    mssm::BwdArgs a{u, delta, delta_bias, A, B, C, D, z, h0, dy, dh_last, du, ddelta, ddelta_bias,
+                    dA, dB, dC, dD, dz, dh0, batch, L, dim, N,
+                    dtypes.io == MSSM_F32 ? mssm::IO_F32 : mssm::IO_BF16};
+    if (!mssm::scan_bwd_supported(a))
+        return fail(MSSM_ERR_UNSUPPORTED, "backward does not support this shape");
+    hipError_t e = zero_sums();
+    if (e == hipSuccess) e = mssm::launch_scan_bwd(a, st);
+    if (e != hipSuccess) return hip_fail(e, "selective-scan backward launch");
+    g_last_variant = MSSM_VARIANT_ROWSERIAL;
+    return MSSM_OK;
+}
+
 mssm_status mssm_ssd_scalar_fwd(const void *x, const void *dt, const float *dt_bias,
                                 const float *A, const void *B, const void *C,
                                 const float *D, void *y, float *h_last,

@@ -194,6 +194,9 @@ DECODE_2_8B = StepProblem("mamba2.8b_decode_bf16", 256, 5120, 16, "bf16", "scala
 MAMBA_2_8B_CONV = MAMBA_2_8B.replace(name="mamba2.8b_layer_conv_bf16", conv=True)
 
 SCAN_PROBLEMS = {p.name: p for p in (TINY, MAMBA_130M, MAMBA_2_8B, MILLION, MAMBA_2_8B_CONV)}
+# the backward of the Mamba-2.8B layer (output gradients drawn by
+# ``output_grads``)
+BWD_PROBLEMS = {"mamba2.8b_layer_bwd_bf16": MAMBA_2_8B.replace(name="mamba2.8b_layer_bwd_bf16")}
 SSD_PROBLEMS = {SSD_LAYER.name: SSD_LAYER}
 STEP_PROBLEMS = {DECODE_2_8B.name: DECODE_2_8B}
 
@@ -283,3 +286,15 @@ def step_inputs(p: StepProblem) -> dict:
     return dict(x=sq["u"], dt=sq["delta"], dt_bias=d["delta_bias"], A=d["A"], B=sq["B"],
                 C=sq["C"], D=d["D"], z=sq["z"],
                 state=initial_state((p.batch, p.dim, p.dstate), p.seed + 1))
+
+
+def output_grads(p: ScanProblem) -> dict:
+    """Gradients of a loss with respect to the scan's outputs, for its
+    backward: dy ~ N(0, 1) like u (bf16-rounded for bf16 problems) and
+    dh_last ~ N(0, 1) (batch, dim, N), from the stream seed + 2."""
+    rng = np.random.default_rng(p.seed + 2)
+    dy = rng.standard_normal((p.batch, p.dim, p.seqlen), dtype=np.float32)
+    if p.io == "bf16":
+        dy = bf16_round(dy)
+    dhl = rng.standard_normal((p.batch, p.dim, p.dstate), dtype=np.float32)
+    return dict(dy=dy, dh_last=dhl)

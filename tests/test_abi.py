@@ -123,6 +123,15 @@ def scan_conv_call(L, batch=2, seqlen=64, dim=8, dstate=4, io=0, param=0, **ptrs
         _lib.DTypes(io, param), None)
 
 
+def bwd_call(L, batch=2, seqlen=64, dim=8, dstate=4, io=0, param=0, **ptrs):
+    names = ["u", "delta", "delta_bias", "A", "B", "C", "D", "z", "h0", "dy", "dh_last", "du",
+             "ddelta", "ddelta_bias", "dA", "dB", "dC", "dD", "dz", "dh0"]
+    p = {n: fake(30 + i) for i, n in enumerate(names)}
+    p.update(ptrs)
+    return L.mssm_selective_scan_bwd(*[p[n] for n in names], _lib.ScanDims(batch, seqlen, dim, dstate),
+                                     _lib.DTypes(io, param), None)
+
+
 def ssd_gated_call(L, batch=2, seqlen=64, H=4, P=8, N=16, G=1, chunk=0, io=0, param=0, **ptrs):
     p = dict(x=fake(1), dt=fake(2), dt_bias=fake(3), A=fake(4), B=fake(5), C=fake(6),
              D=fake(7), z=fake(8), h0=fake(11), y=fake(9), h_last=fake(10))
@@ -254,6 +263,26 @@ def test_scan_conv_validation(L):
         L.mssm_force_variant(prev)
     assert st == _lib.MSSM_ERR_UNSUPPORTED       # validation passed; stopped at the variant
     assert b"variant" in L.mssm_last_error()
+
+
+@pytest.mark.parametrize("name", ["u", "delta", "A", "B", "C", "dy", "du", "ddelta"])
+def test_bwd_null_required_pointer(L, name):
+    assert bwd_call(L, **{name: None}) == _lib.MSSM_ERR_INVALID_ARG
+    assert name.encode() in L.mssm_last_error()
+
+
+def test_bwd_validation(L):
+    assert bwd_call(L, z=None) == _lib.MSSM_ERR_INVALID_ARG        # dz without z
+    assert b"dz" in L.mssm_last_error()
+    assert bwd_call(L, dstate=0) == _lib.MSSM_ERR_INVALID_ARG
+    assert bwd_call(L, dstate=_lib.MAX_DSTATE + 1) == _lib.MSSM_ERR_UNSUPPORTED
+    assert bwd_call(L, io=7) == _lib.MSSM_ERR_INVALID_ARG
+    assert bwd_call(L, batch=1 << 40, seqlen=1 << 30) == _lib.MSSM_ERR_INVALID_ARG
+    # gradients are outputs: none may overlap an input or another output
+    assert bwd_call(L, du=fake(50), dy=fake(50) + 8) == _lib.MSSM_ERR_INVALID_ARG
+    assert bwd_call(L, dB=fake(50), dC=fake(50) + 16) == _lib.MSSM_ERR_INVALID_ARG
+    assert bwd_call(L, dA=fake(50), A=fake(50)) == _lib.MSSM_ERR_INVALID_ARG
+    assert b"overlaps" in L.mssm_last_error()
 
 
 def test_ssd_gated_validation(L):

@@ -1,0 +1,98 @@
+"""GPU parity of the selective-scan backward (mssm_selective_scan_bwd)
+against the float64 oracle's reverse-mode derivative on identical inputs and
+output gradients.  Needs an MI355X; marked ``gpu``.
+
+Every gradient is float32 whatever the I/O dtype, so every comparison takes
+the float32 gates (the inputs of bf16 problems are exact bf16 values for
+both sides).  Normwise rows: du, ddelta, dz per (b, d) over L (like y);
+dB, dC per (b, n) over L; dA per d over N; dh0 per (b, d) over N; dD and
+the bias gradient as one row each.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import gates
+from oracle import oracle
+from selective_state_space_05_amd import inputs
+from test_parity_gpu import announce, scan_to_dev, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def f64(t):
+    return None if t is None else t.float().cpu().numpy().astype(np.float64)
+
+
+BWD_CASES = [
+    # batch, L, dim, N, io, bias, gate, skip, with h0 / dh_last
+    (2, 300, 37, 16, "f32", "per_channel", True, True, True),   # waves across two batches
+    (2, 300, 64, 16, "bf16", "scalar", True, True, True),       # one batch per wave
+    (1, 77, 9, 5, "f32", None, False, False, False),            # no optional inputs
+    (2, 129, 20, 4, "bf16", "per_channel", True, True, False),
+    (1, 50, 70, 32, "f32", "scalar", True, True, True),
+    (1, 33, 10, 64, "f32", "scalar", False, True, True),        # N = 64 (limit)
+    (3, 1, 5, 8, "f32", "scalar", True, True, True),            # single step
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES)
+def test_scan_backward(dev, case):
+    import selective_state_space_05_amd as mssm
+    batch, L, dim, N, io, bias, gate, skip, extra = case
+    p = inputs.ScanProblem("case", batch, L, dim, N, io, bias, gate, skip, 800 + L + N)
+    announce("scan backward %s" % (case,))
+    x = inputs.scan_inputs(p)
+    rng = np.random.default_rng(L + dim)
+    dy = rng.standard_normal((batch, dim, L)).astype(np.float32)
+    if io == "bf16":
+        dy = inputs.bf16_round(dy)
+    h0 = inputs.initial_state((batch, dim, N), 17) if extra else None
+    dhl = inputs.initial_state((batch, dim, N), 19) if extra else None
+    t = scan_to_dev({k: v for k, v in x.items() if k not in ("conv_w", "conv_b")}, io, dev)
+    g = mssm.selective_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], to_dev(dy, io, dev),
+                                D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
+                                h0=None if h0 is None else torch.from_numpy(h0).to(dev),
+                                dh_last=None if dhl is None else torch.from_numpy(dhl).to(dev))
+    torch.cuda.synchronize()
+    o = oracle.selective_scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"],
+                                  z=x["z"], delta_bias=x["delta_bias"], h0=h0, dh_last=dhl)
+    f = "f32"
+    gates.check(f64(g["du"]), o["du"], f, "du")
+    gates.check(f64(g["ddelta"]), o["ddelta"], f, "ddelta")
+    if gate:
+        gates.check(f64(g["dz"]), o["dz"], f, "dz")
+    gates.check_state(f64(g["dB"]), o["dB"], f, "dB")
+    gates.check_state(f64(g["dC"]), o["dC"], f, "dC")
+    gates.check_state(f64(g["dA"]), o["dA"], f, "dA")
+    if skip:
+        gates.check_state(f64(g["dD"])[None], o["dD"][None], f, "dD")
+    if bias:
+        gates.check_state(f64(g["ddelta_bias"])[None], o["ddelta_bias"][None], f, "ddelta_bias")
+    if extra:
+        gates.check_state(f64(g["dh0"]), o["dh0"], f, "dh0")
+
+
+def test_scan_backward_zero_length(dev):
+    """L = 0: the final state is the initial state, so dh0 = dh_last, and
+    every summed gradient is zero."""
+    import selective_state_space_05_amd as mssm
+    announce("scan backward L=0")
+    u = torch.empty((2, 3, 0), device=dev)
+    A = -torch.ones((3, 4), device=dev)
+    B = torch.empty((2, 4, 0), device=dev)
+    dhl = torch.randn((2, 3, 4), device=dev)
+    g = mssm.selective_scan_bwd(u, u.clone(), A, B, B.clone(), u.clone(), D=torch.ones(3, device=dev),
+                                dh_last=dhl)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dh0"], dhl)
+    assert torch.all(g["dA"] == 0) and torch.all(g["dD"] == 0) and torch.all(g["ddelta_bias"] == 0)
