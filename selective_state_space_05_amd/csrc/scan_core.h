@@ -116,13 +116,13 @@ struct Pack {
     }
 };
 
-// LDS of one workgroup.  dl / dl*u are double-buffered so that the
-// state-only walk needs one barrier per chunk.
+// LDS of one workgroup.  dl / dl*u and the partial sums are double-buffered
+// so that every walk needs one barrier per chunk.
 template <int W>
 struct Smem {
     float dl[2][kCh * kPitch];
     float du[2][kCh * kPitch];
-    float p[W * kCh * kPitch];      // per wave: partial sums over its 4 state rows
+    float p[2][W * kCh * kPitch];   // per wave: partial sums over its 4 state rows
 };
 
 // Sum of a value over the four 16-lane rows of a wave, for 32 values at
@@ -299,27 +299,20 @@ struct Walker {
         else return __uint_as_float(static_cast<uint32_t>(v) << 16);
     }
 
-    // One chunk of kT steps starting at t0.  FULL: all kT steps lie inside
-    // [t0, t_end).  OUT: form and store y; otherwise only the state and the
-    // owner's sum of dl.  buf selects the dl / dl*u buffer (state-only walks
-    // alternate buffers and need one barrier per chunk).
-    template <bool OUT, bool FULL>
-    __device__ void chunk(int t0, int t_end, const In &in, float (&h)[NPL], Smem<W> &sm, int buf) {
-        // ---- B, C of the row broadcasts: zero past the end and for state
-        // rows past N ------------------------------------------------------
-        float cb[2][NPL], cc[2][NPL];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const bool tok = FULL || t0 + 16 * q + j < t_end;
-#pragma unroll
-            for (int g = 0; g < NPL; ++g) {
-                const bool okv = tok && nok[g];
-                cb[q][g] = okv ? to_f32(in.rb[q][g]) : 0.0f;
-                cc[q][g] = (OUT && okv) ? to_f32(in.rc[q][g]) : 0.0f;
-            }
-        }
+    // Per-step values an owner thread keeps from phase A of a chunk to its
+    // phase C: skip term, gate factor, and the number of its steps inside
+    // the range.
+    struct Own {
+        float sk[OS], gz[OS];
+        int rem;
+    };
 
-        // ---- A: per-step scalars of this thread's OS steps ------------------
+    // ---- phase A: per-step scalars of this thread's OS steps of the chunk at
+    // t0, published in LDS buffer buf.  FULL: all kT steps lie inside
+    // [t0, t_end).  OUT: keep the skip term and gate for phase C; otherwise
+    // add dl to the owner's running sum.
+    template <bool OUT, bool FULL>
+    __device__ void phase_a(int t0, int t_end, const In &in, Smem<W> &sm, int buf, Own &o) {
         float u[OS], dr[OS], zz[OS];
         Pack<T, OS>::unpack(in.ru, u);
         Pack<T, OS>::unpack(in.rd, dr);
@@ -346,7 +339,8 @@ struct Walker {
         if (GATE && OUT) Pack<T, OS>::unpack(in.rz, zz);
         int rem = OS;                       // steps of this owner inside the range
         if (!FULL) rem = min(t_end - (t0 + OS * ok), OS);
-        float dl[OS], du[OS], sk[OS], gz[OS];
+        o.rem = rem;
+        float dl[OS], du[OS];
 #pragma unroll
         for (int i = 0; i < OS; ++i) {
             // computed unconditionally; steps past the end become the
@@ -355,8 +349,8 @@ struct Walker {
             dl[i] = (FULL || i < rem) ? sp : 0.0f;
             du[i] = (FULL || i < rem) ? sp * u[i] : 0.0f;
             if (OUT) {
-                sk[i] = skip * u[i];
-                gz[i] = (GATE && OUT) ? silu(zz[i]) : 1.0f;
+                o.sk[i] = skip * u[i];
+                o.gz[i] = GATE ? silu(zz[i]) : 1.0f;
             } else {
                 sdl += dl[i];
             }
@@ -366,27 +360,46 @@ struct Walker {
             *reinterpret_cast<float2 *>(sm.dl[buf] + oc * kPitch + OS * ok + i) = make_float2(dl[i], dl[i + 1]);
             *reinterpret_cast<float2 *>(sm.du[buf] + oc * kPitch + OS * ok + i) = make_float2(du[i], du[i + 1]);
         }
-        __syncthreads();
+    }
 
-        // ---- B: 32 steps of the recurrence for this lane ----------------------
-        float p[32];
+    // dl and dl*u of the 32 steps of this lane's channel, from LDS buffer buf.
+    __device__ static void read_steps(const Smem<W> &sm, int buf, int jj, float (&dls)[kT], float (&dus)[kT]) {
+        const float4 *pdl = reinterpret_cast<const float4 *>(sm.dl[buf] + jj * kPitch);
+        const float4 *pdu = reinterpret_cast<const float4 *>(sm.du[buf] + jj * kPitch);
+#pragma unroll
+        for (int k = 0; k < kT / 4; ++k) {
+            const float4 a = pdl[k], e = pdu[k];
+            dls[4 * k] = a.x; dls[4 * k + 1] = a.y; dls[4 * k + 2] = a.z; dls[4 * k + 3] = a.w;
+            dus[4 * k] = e.x; dus[4 * k + 1] = e.y; dus[4 * k + 2] = e.z; dus[4 * k + 3] = e.w;
+        }
+    }
+
+    // ---- phase B: 32 steps of the recurrence for this lane from the step
+    // scalars dls / dus; with OUT, p[k] is this lane's part of C.h at step k.
+    template <bool OUT, bool FULL>
+    __device__ void phase_b(int t0, int t_end, const In &in, const float (&dls)[kT], const float (&dus)[kT],
+                            float (&h)[NPL], float (&p)[kT]) const {
+        // B, C of the row broadcasts: zero past the end and for state rows
+        // past N
+        float cb[2][NPL], cc[2][NPL];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            float dls[16], dus[16];
-            const float4 *pdl = reinterpret_cast<const float4 *>(sm.dl[buf] + j * kPitch + 16 * q);
-            const float4 *pdu = reinterpret_cast<const float4 *>(sm.du[buf] + j * kPitch + 16 * q);
+            const bool tok = FULL || t0 + 16 * q + j < t_end;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float4 a = pdl[k], e = pdu[k];
-                dls[4 * k] = a.x; dls[4 * k + 1] = a.y; dls[4 * k + 2] = a.z; dls[4 * k + 3] = a.w;
-                dus[4 * k] = e.x; dus[4 * k + 1] = e.y; dus[4 * k + 2] = e.z; dus[4 * k + 3] = e.w;
+            for (int g = 0; g < NPL; ++g) {
+                const bool okv = tok && nok[g];
+                cb[q][g] = okv ? to_f32(in.rb[q][g]) : 0.0f;
+                cc[q][g] = (OUT && okv) ? to_f32(in.rc[q][g]) : 0.0f;
             }
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
 #define MSSM_STEP(S)                                                           \
     {                                                                          \
         float acc = 0.0f;                                                      \
         _Pragma("unroll") for (int g = 0; g < NPL; ++g) {                      \
-            const float a = fast_exp2(dls[S] * A2[g]);                         \
-            h[g] = fmaf(a, h[g], row_bcast<S>(cb[q][g]) * dus[S]);             \
+            const float a = fast_exp2(dls[16 * q + S] * A2[g]);                \
+            h[g] = fmaf(a, h[g], row_bcast<S>(cb[q][g]) * dus[16 * q + S]);    \
             if (OUT) acc = g == 0 ? row_bcast<S>(cc[q][g]) * h[g]              \
                                   : fmaf(row_bcast<S>(cc[q][g]), h[g], acc);   \
         }                                                                      \
@@ -398,26 +411,30 @@ struct Walker {
             MSSM_STEP(12) MSSM_STEP(13) MSSM_STEP(14) MSSM_STEP(15)
 #undef MSSM_STEP
         }
-        if (!OUT) return;
-        {
-            // the wave's four state rows summed in registers; lane (row r,
-            // column j) stores steps 8 r .. 8 r + 7 of channel j
-            float qs[8];
-            rows_reduce(p, qs);
-            const int r = (threadIdx.x >> 4) & 3;
-            float4 *dst = reinterpret_cast<float4 *>(sm.p + ((threadIdx.x >> 6) * kCh + j) * kPitch + 8 * r);
-            dst[0] = make_float4(qs[0], qs[1], qs[2], qs[3]);
-            dst[1] = make_float4(qs[4], qs[5], qs[6], qs[7]);
-        }
-        __syncthreads();
+    }
 
-        // ---- C: reduce the partial sums, skip term, gate, store --------------
+    // The wave's four state rows of p summed in registers; lane (row r,
+    // column j) writes steps 8 r .. 8 r + 7 of channel j to partial-sum
+    // buffer pbuf.
+    __device__ void reduce_store(const float (&p)[kT], Smem<W> &sm, int pbuf) const {
+        float qs[8];
+        rows_reduce(p, qs);
+        const int r = (threadIdx.x >> 4) & 3;
+        float4 *dst = reinterpret_cast<float4 *>(sm.p[pbuf] + ((threadIdx.x >> 6) * kCh + j) * kPitch + 8 * r);
+        dst[0] = make_float4(qs[0], qs[1], qs[2], qs[3]);
+        dst[1] = make_float4(qs[4], qs[5], qs[6], qs[7]);
+    }
+
+    // ---- phase C: the owner adds the W waves' partial sums of its OS steps
+    // of the chunk at t0, applies the skip term and the gate, and stores y.
+    template <bool FULL>
+    __device__ void phase_c(int t0, const Own &o, const Smem<W> &sm, int pbuf) const {
         float yv[OS];
 #pragma unroll
         for (int i = 0; i < OS; ++i) yv[i] = 0.0f;
 #pragma unroll
         for (int r = 0; r < W; ++r) {
-            const float *src = sm.p + (r * kCh + oc) * kPitch + OS * ok;
+            const float *src = sm.p[pbuf] + (r * kCh + oc) * kPitch + OS * ok;
 #pragma unroll
             for (int i = 0; i < OS; i += 2) {
                 const float2 v = *reinterpret_cast<const float2 *>(src + i);
@@ -426,7 +443,7 @@ struct Walker {
             }
         }
 #pragma unroll
-        for (int i = 0; i < OS; ++i) yv[i] = (yv[i] + sk[i]) * gz[i];
+        for (int i = 0; i < OS; ++i) yv[i] = (yv[i] + o.sk[i]) * o.gz[i];
         T *py = reinterpret_cast<T *>(reinterpret_cast<char *>(yb) + oo) + (t0 + OS * ok);
         if (FULL) {
             if (VEC) {
@@ -438,42 +455,140 @@ struct Walker {
         } else {
 #pragma unroll
             for (int i = 0; i < OS; ++i)
-                if (i < rem) Io<T>::store(py, i, yv[i]);
+                if (i < o.rem) Io<T>::store(py, i, yv[i]);
         }
+    }
+
+    // One state-only chunk of kT steps at t0 (no output; the owner's sum of
+    // dl grows).  Buffer buf alternates between chunks, so one barrier per
+    // chunk orders the LDS reuse.
+    template <bool FULL>
+    __device__ void state_chunk(int t0, int t_end, const In &in, float (&h)[NPL], Smem<W> &sm, int buf) {
+        Own o;
+        phase_a<false, FULL>(t0, t_end, in, sm, buf, o);
+        __syncthreads();
+        float dls[kT], dus[kT], p[kT];
+        read_steps(sm, buf, j, dls, dus);
+        phase_b<false, FULL>(t0, t_end, in, dls, dus, h, p);
+    }
+
+    // One stage of the output pipeline, at chunk k of a walk from t_begin:
+    // issues the loads of chunk k + 2 into xk (free: chunk k's scan is done),
+    // publishes chunk k + 1's step scalars and chunk k's partial sums, then,
+    // after the one barrier of the stage, stores chunk k's outputs and runs
+    // chunk k + 1's scan into p.  FN: chunk k + 1 is full.  Chunk k is full.
+    //
+    // LDS reuse: step scalars of chunk c live in buffer c % 2 and partial
+    // sums in partial buffer c % 2.  Each buffer is rewritten two stages after
+    // it was written, and the stage in between holds a barrier that every
+    // reader of the old contents passed first.
+    template <bool FN>
+    __device__ void out_stage(int t_begin, int t_end, int k, In &xk, const In &xk1, const Own &ok_,
+                              Own &ok1, float (&h)[NPL], float (&p)[kT], Smem<W> &sm) {
+        const int tk = t_begin + k * kT;
+        load<true>(tk + 2 * kT, xk);
+        phase_a<true, FN>(tk + kT, t_end, xk1, sm, (k + 1) & 1, ok1);
+        reduce_store(p, sm, k & 1);
+        __syncthreads();
+        float dls[kT], dus[kT];
+        read_steps(sm, (k + 1) & 1, j, dls, dus);
+        phase_c<true>(tk, ok_, sm, k & 1);
+        phase_b<true, FN>(tk + kT, t_end, xk1, dls, dus, h, p);
+    }
+
+    // The last chunk k of a walk: its partial sums, one barrier, its outputs.
+    __device__ void out_last(int t_begin, int k, bool full, const float (&p)[kT], const Own &o, Smem<W> &sm) {
+        reduce_store(p, sm, k & 1);
+        __syncthreads();
+        if (full) phase_c<true>(t_begin + k * kT, o, sm, k & 1);
+        else phase_c<false>(t_begin + k * kT, o, sm, k & 1);
     }
 
     // Walk steps [t_begin, t_end) from state h (updated in place).  OUT: also
     // form and store y; otherwise only the state and the owner's sum of dl.
     // t_begin must be a multiple of OS; every thread of the workgroup calls
-    // this with the same range.  The chunk barriers make the loop's LDS
-    // reuse safe: y-walks reuse one buffer (their second barrier orders the
-    // next chunk's writes), state-only walks alternate two (even chunks use
-    // buffer 0).
+    // this with the same range, after a barrier that follows any earlier use
+    // of the workgroup's LDS.
+    //
+    // The output walk is a pipeline with one barrier per chunk: chunk k's
+    // partial sums and chunk k + 1's step scalars are published together,
+    // so the reduction's cross-lane work and phase A's transcendental chains
+    // fill each other's latencies, and chunk k's stores overlap chunk
+    // k + 1's scan.  Loads run two chunks ahead of the scan.
     template <bool OUT>
     __device__ void walk(int t_begin, int t_end, float (&h)[NPL], Smem<W> &sm) {
-        const int nfull = (t_end - t_begin) / kT;
-        // Two input sets used in turn: the loads of chunk c + 1 go straight
-        // into the registers that chunk c + 1 reads, with no copy in between
-        // (a copy would have to wait for the loads).
-        In x0, x1;
-        load<OUT>(t_begin, x0);
-        int c = 0;
-        for (; c + 1 < nfull; c += 2) {
+        const int len = t_end - t_begin;
+        if (len <= 0) return;
+        const int nfull = len / kT;
+        if constexpr (!OUT) {
+            // Two input sets used in turn: the loads of chunk c + 1 go
+            // straight into the registers that chunk c + 1 reads, with no
+            // copy in between (a copy would have to wait for the loads).
+            In x0, x1;
+            load<false>(t_begin, x0);
+            int c = 0;
+            for (; c + 1 < nfull; c += 2) {
+                const int t0 = t_begin + c * kT;
+                load<false>(t0 + kT, x1);
+                state_chunk<true>(t0, t_end, x0, h, sm, 0);
+                load<false>(t0 + 2 * kT, x0);
+                state_chunk<true>(t0 + kT, t_end, x1, h, sm, 1);
+            }
+            // x0 holds the inputs of chunk c; loads past the range are
+            // clamped and their values unused
             const int t0 = t_begin + c * kT;
-            load<OUT>(t0 + kT, x1);
-            chunk<OUT, true>(t0, t_end, x0, h, sm, 0);
-            load<OUT>(t0 + 2 * kT, x0);
-            chunk<OUT, true>(t0 + kT, t_end, x1, h, sm, OUT ? 0 : 1);
-        }
-        // x0 holds the inputs of chunk c; loads past the range are clamped
-        // and their values unused
-        const int t0 = t_begin + c * kT;
-        if (c < nfull) {
-            load<OUT>(t0 + kT, x1);
-            chunk<OUT, true>(t0, t_end, x0, h, sm, 0);
-            if (t0 + kT < t_end) chunk<OUT, false>(t0 + kT, t_end, x1, h, sm, OUT ? 0 : 1);
-        } else if (t0 < t_end) {
-            chunk<OUT, false>(t0, t_end, x0, h, sm, 0);
+            if (c < nfull) {
+                load<false>(t0 + kT, x1);
+                state_chunk<true>(t0, t_end, x0, h, sm, 0);
+                if (t0 + kT < t_end) state_chunk<false>(t0 + kT, t_end, x1, h, sm, 1);
+            } else if (t0 < t_end) {
+                state_chunk<false>(t0, t_end, x0, h, sm, 0);
+            }
+        } else {
+            const int nch = (len + kT - 1) / kT;
+            In xa, xb;
+            Own oa, ob;
+            float p[kT];
+            load<true>(t_begin, xa);
+            load<true>(t_begin + kT, xb);
+            {
+                float dls[kT], dus[kT];
+                if (nfull > 0) {
+                    phase_a<true, true>(t_begin, t_end, xa, sm, 0, oa);
+                    __syncthreads();
+                    read_steps(sm, 0, j, dls, dus);
+                    phase_b<true, true>(t_begin, t_end, xa, dls, dus, h, p);
+                } else {
+                    phase_a<true, false>(t_begin, t_end, xa, sm, 0, oa);
+                    __syncthreads();
+                    read_steps(sm, 0, j, dls, dus);
+                    phase_b<true, false>(t_begin, t_end, xa, dls, dus, h, p);
+                }
+            }
+            // Stage k needs chunk k + 1 to exist; stages with both chunks
+            // full run two at a time, so the input sets swap roles without a
+            // copy.  At most two stages remain after the loop, the second
+            // one for the partial last chunk.
+            int k = 0;
+            for (; k + 2 < nfull; k += 2) {
+                out_stage<true>(t_begin, t_end, k, xa, xb, oa, ob, h, p, sm);
+                out_stage<true>(t_begin, t_end, k + 1, xb, xa, ob, oa, h, p, sm);
+            }
+            const bool last_full = nch == nfull;
+            if (k + 1 < nch) {
+                if (k + 1 < nfull) out_stage<true>(t_begin, t_end, k, xa, xb, oa, ob, h, p, sm);
+                else out_stage<false>(t_begin, t_end, k, xa, xb, oa, ob, h, p, sm);
+                ++k;
+                if (k + 1 < nch) {
+                    out_stage<false>(t_begin, t_end, k, xb, xa, ob, oa, h, p, sm);
+                    ++k;
+                    out_last(t_begin, k, last_full, p, oa, sm);
+                } else {
+                    out_last(t_begin, k, last_full, p, ob, sm);
+                }
+            } else {
+                out_last(t_begin, k, last_full, p, oa, sm);
+            }
         }
     }
 
@@ -482,11 +597,11 @@ struct Walker {
     // walk; every thread of the workgroup must call it.
     __device__ float channel_dl_sum(Smem<W> &sm) const {
         __syncthreads();                           // last chunk's readers are done
-        sm.p[oc * OPC + ok] = sdl;
+        sm.p[0][oc * OPC + ok] = sdl;
         __syncthreads();
         float s = 0.0f;
 #pragma unroll
-        for (int i = 0; i < OPC; ++i) s += sm.p[j * OPC + i];
+        for (int i = 0; i < OPC; ++i) s += sm.p[0][j * OPC + i];
         __syncthreads();                           // sm.p is reused afterwards
         return s;
     }
