@@ -259,9 +259,10 @@ class ScanBench:
         hs = np.stack([hg[b, d] for b, d in rows])
         return len(rows), g1(ys, yo), g1(hs, ho)
 
-    def cpu_baseline(self, threads, budget_s=15.0):
+    def cpu_baseline(self, threads, budget_s=15.0, min_wall_s=2.0):
         """Time the oracle on whole (batch, channel) rows: as many as about
-        `budget_s` seconds of work at the measured single-row rate."""
+        `budget_s` seconds of work at the measured single-row rate, in passes
+        repeated for at least `min_wall_s` seconds."""
         from oracle import oracle
         p, x = self.p, self.x
         u = self._u_rows()
@@ -276,25 +277,33 @@ class ScanBench:
         n_rows = min(n_rows, rows_total)
         flat = np.arange(n_rows)
         bsel, dsel = flat // p.dim, flat % p.dim
+        # whole passes over the sample, repeated until at least min_wall_s
+        # of wall time has gone by (a pass over a whole layer can take well
+        # under a second on many cores)
         t0 = time.time()
         done = 0
-        for b in np.unique(bsel):
-            ds = dsel[bsel == b]
-            lo, hi = int(ds[0]), int(ds[-1]) + 1
-            args = (x["delta"][b:b + 1, lo:hi], x["A"][lo:hi], x["B"][b:b + 1], x["C"][b:b + 1],
-                    None if x["D"] is None else x["D"][lo:hi],
-                    None if x["z"] is None else x["z"][b:b + 1, lo:hi],
-                    None if x["delta_bias"] is None else x["delta_bias"][lo:hi])
-            if p.conv:
-                oracle.selective_scan_conv(x["u"][b:b + 1, lo:hi], x["conv_w"][lo:hi],
-                                           x["conv_b"][lo:hi], *args, nthreads=threads)
-            else:
-                oracle.selective_scan(x["u"][b:b + 1, lo:hi], *args, nthreads=threads)
-            done += hi - lo
+        passes = 0
+        while True:
+            for b in np.unique(bsel):
+                ds = dsel[bsel == b]
+                lo, hi = int(ds[0]), int(ds[-1]) + 1
+                args = (x["delta"][b:b + 1, lo:hi], x["A"][lo:hi], x["B"][b:b + 1], x["C"][b:b + 1],
+                        None if x["D"] is None else x["D"][lo:hi],
+                        None if x["z"] is None else x["z"][b:b + 1, lo:hi],
+                        None if x["delta_bias"] is None else x["delta_bias"][lo:hi])
+                if p.conv:
+                    oracle.selective_scan_conv(x["u"][b:b + 1, lo:hi], x["conv_w"][lo:hi],
+                                               x["conv_b"][lo:hi], *args, nthreads=threads)
+                else:
+                    oracle.selective_scan(x["u"][b:b + 1, lo:hi], *args, nthreads=threads)
+                done += hi - lo
+            passes += 1
+            if time.time() - t0 >= min_wall_s:
+                break
         cpu_s = time.time() - t0
         elems = done * p.seqlen * p.dstate
-        return elems / cpu_s, "%d of %d (batch, channel) rows, full length %d, float64, %.1f s" % (
-            done, rows_total, p.seqlen, cpu_s)
+        return elems / cpu_s, ("%d of %d (batch, channel) rows, full length %d, float64, %d pass(es), "
+                               "%.1f s wall" % (n_rows, rows_total, p.seqlen, passes, cpu_s))
 
     def config(self):
         p = self.p
@@ -560,7 +569,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps before the timed ones (also lets the GPU clock ramp up)")
     ap.add_argument("--workload", default="mamba2.8b_layer_bf16")
     ap.add_argument("--variant", default="auto", choices=sorted(VARIANTS))
     ap.add_argument("--chunk", type=int, default=256, help="SSD chunk length")

@@ -116,6 +116,36 @@ struct Pack {
     }
 };
 
+// Buffer loads.  A buffer resource names a base address and a size in
+// bytes; a lane's load at a byte offset at or past the size returns zero
+// instead of touching memory.  Walks move the base along the rows chunk by
+// chunk in scalar registers, so per-lane offsets stay fixed and loads past
+// the end of a tensor need no clamping.
+// Sizes are below 2^31 bytes (the launchers check the rows' extent), so
+// they stay in 32-bit scalar arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, int32_t bytes) {
+    // 0x00020000: the raw-buffer format word of the gfx9 family (32-bit data)
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes > 0 ? bytes : 0, 0x00020000);
+}
+template <typename V> __device__ V buffer_ld(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <> __device__ __forceinline__ uint16_t buffer_ld<uint16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+template <> __device__ __forceinline__ float buffer_ld<float>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+template <> __device__ __forceinline__ uint32_t buffer_ld<uint32_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+template <> __device__ __forceinline__ uint2 buffer_ld<uint2>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(v[0], v[1]);
+}
+template <> __device__ __forceinline__ uint4 buffer_ld<uint4>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // LDS of one workgroup.  dl / dl*u and the partial sums are double-buffered
 // so that every walk needs one barrier per chunk.
 template <int W>
@@ -173,7 +203,9 @@ struct Walker {
     int prow, j;
     float A2[NPL];
     uint32_t bco[NPL];     // byte offset of this lane's B / C rows in the batch
+    uint32_t bcj[NPL];     // bco + this lane's step j within a 16-step half
     bool nok[NPL];
+    int32_t rec_a, rec_bc; // bytes from ub / Bb to the end of their rows (< 2^31)
     const T *Bb, *Cb;      // B, C of this batch (workgroup-uniform)
     // owner role
     int oc, ok;
@@ -211,6 +243,7 @@ struct Walker {
             nok[g] = n < N;
             A2[g] = nok[g] ? A[static_cast<int64_t>(dS) * N + n] * kLog2e : 0.0f;
             bco[g] = static_cast<uint32_t>(min(n, N - 1)) * static_cast<uint32_t>(L) * sizeof(T);
+            bcj[g] = bco[g] + static_cast<uint32_t>(j) * sizeof(T);
         }
         oc = tid / OPC;
         ok = tid % OPC;
@@ -232,6 +265,8 @@ struct Walker {
         db = delta + row0;
         zb = GATE ? z + row0 : nullptr;
         yb = y ? y + row0 : nullptr;
+        rec_a = min(kCh, dim - d0) * L * static_cast<int32_t>(sizeof(T));
+        rec_bc = N * L * static_cast<int32_t>(sizeof(T));
         sdl = 0.0f;
     }
 
@@ -241,14 +276,19 @@ struct Walker {
     template <bool OUT>
     __device__ void load(int t0, In &in) const {
         const int off = t0 + OS * ok;
+        // byte offset of step t0 in a row: the resources below start there
+        const int32_t tb = t0 * static_cast<int32_t>(sizeof(T));
         if constexpr (VEC) {
             // rows 16-byte aligned and L % 8 == 0 with OS | 8: the OS steps
-            // are all inside the row or all past its end
+            // are all inside the row or all past its end; past the end of the
+            // row they read the next row (or zero past the last one), values
+            // the chunk discards
             static_assert(8 % OS == 0, "vector owner loads need OS | 8");
-            const uint32_t o = oo + static_cast<uint32_t>(off + OS <= L ? off : L - OS) * sizeof(T);
-            in.ru = ld<Raw>(ub, o);
-            in.rd = ld<Raw>(db, o);
-            if (GATE && OUT) in.rz = ld<Raw>(zb, o);
+            const uint32_t o = oo + static_cast<uint32_t>(OS * ok) * sizeof(T);
+            in.ru = buffer_ld<Raw>(buffer_rsrc(reinterpret_cast<const char *>(ub) + tb, rec_a - tb), o);
+            in.rd = buffer_ld<Raw>(buffer_rsrc(reinterpret_cast<const char *>(db) + tb, rec_a - tb), o);
+            if (GATE && OUT)
+                in.rz = buffer_ld<Raw>(buffer_rsrc(reinterpret_cast<const char *>(zb) + tb, rec_a - tb), o);
             if constexpr (CONV) {
                 // the 4 steps before, as kPrev aligned raws; indices clamped
                 // into the row (those before step 0 are zeroed at the use)
@@ -282,14 +322,17 @@ struct Walker {
                 __builtin_memcpy(in.rp, sp, sizeof(sp));
             }
         }
+        // B, C at steps t0 + 16 q + j (past the end of an n row: the next
+        // row or zero, discarded)
+        const auto rB = buffer_rsrc(reinterpret_cast<const char *>(Bb) + tb, rec_bc - tb);
+        const auto rC = buffer_rsrc(reinterpret_cast<const char *>(Cb) + tb, rec_bc - tb);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const int t = t0 + 16 * q + j;
-            const uint32_t to = static_cast<uint32_t>(t < L ? t : L - 1) * sizeof(T);
 #pragma unroll
             for (int g = 0; g < NPL; ++g) {
-                in.rb[q][g] = ld<T>(Bb, bco[g] + to);
-                if (OUT) in.rc[q][g] = ld<T>(Cb, bco[g] + to);
+                const uint32_t o = bcj[g] + static_cast<uint32_t>(16 * q) * sizeof(T);
+                in.rb[q][g] = buffer_ld<T>(rB, o);
+                if (OUT) in.rc[q][g] = buffer_ld<T>(rC, o);
             }
         }
     }
