@@ -243,7 +243,9 @@ struct Walker {
             nok[g] = n < N;
             A2[g] = nok[g] ? A[static_cast<int64_t>(dS) * N + n] * kLog2e : 0.0f;
             bco[g] = static_cast<uint32_t>(min(n, N - 1)) * static_cast<uint32_t>(L) * sizeof(T);
-            bcj[g] = bco[g] + static_cast<uint32_t>(j) * sizeof(T);
+            // rows past N load through an offset past every buffer's end,
+            // which reads zero: their B and C vanish with no select
+            bcj[g] = nok[g] ? bco[g] + static_cast<uint32_t>(j) * sizeof(T) : 0xffffff00u;
         }
         oc = tid / OPC;
         ok = tid % OPC;
@@ -422,17 +424,16 @@ struct Walker {
     template <bool OUT, bool FULL>
     __device__ void phase_b(int t0, int t_end, const In &in, const float (&dls)[kT], const float (&dus)[kT],
                             float (&h)[NPL], float (&p)[kT]) const {
-        // B, C of the row broadcasts: zero past the end and for state rows
-        // past N
+        // B, C of the row broadcasts: zero past the end (state rows past N
+        // loaded zero)
         float cb[2][NPL], cc[2][NPL];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const bool tok = FULL || t0 + 16 * q + j < t_end;
 #pragma unroll
             for (int g = 0; g < NPL; ++g) {
-                const bool okv = tok && nok[g];
-                cb[q][g] = okv ? to_f32(in.rb[q][g]) : 0.0f;
-                cc[q][g] = (OUT && okv) ? to_f32(in.rc[q][g]) : 0.0f;
+                cb[q][g] = tok ? to_f32(in.rb[q][g]) : 0.0f;
+                cc[q][g] = (OUT && tok) ? to_f32(in.rc[q][g]) : 0.0f;
             }
         }
 #pragma unroll
