@@ -504,15 +504,30 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
             const int tl = tb * 32 + l32;            // this lane's step within the chunk
             const float cum_t = sm.cum[tl];
             f16x yd[2] = {zero16(), zero16()};
-#pragma unroll 1
-            for (int sb = 0; sb <= tb; ++sb) {
-                // The block's LDS operands are all read up front, so their
-                // latencies overlap one another and the matrix-core work
-                // instead of being exposed one product at a time.
+            // G'[s][t] = B_s . C_t of source block sb: A operand rows s of B.
+            // The block's LDS operands are all read up front, so their
+            // latencies overlap one another and the matrix-core work instead
+            // of being exposed one product at a time.
+            auto gblock = [&](int sb) {
                 bf8 ab[KN];
 #pragma unroll
                 for (int jn = 0; jn < KN; ++jn)
                     ab[jn] = *reinterpret_cast<const bf8 *>(&sm.B[(sb * 32 + l32) * BP + 16 * jn + 8 * half]);
+                f16x g = zero16();
+#pragma unroll
+                for (int jn = 0; jn < KN; ++jn) g = mfma(ab[jn], cf[which][jn], g);
+                return g;
+            };
+            // Two-stage pipeline over the source blocks: block sb + 1's G'
+            // products are issued before block sb's decay tile is built, so
+            // the matrix cores work while the vector units do.  The last
+            // stage recomputes block tb's G' (a uniform branch-free loop;
+            // the result is unused).
+            f16x gnext = gblock(0);
+#pragma unroll 1
+            for (int sb = 0; sb <= tb; ++sb) {
+                const f16x gacc = gnext;
+                gnext = gblock(sb < tb ? sb + 1 : sb);
                 // x^T operands of the block: A operand row p reads x at
                 // s(8 kk + 0..3) and s(8 kk + 4..7), s(v) as below
                 bf8 xa[2][2];
@@ -525,10 +540,6 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
                         const uint2 hi4 = *reinterpret_cast<const uint2 *>(xp + 8);
                         xa[kk][pt] = __builtin_bit_cast(bf8, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
                     }
-                // G'[s][t] = B_s . C_t: A operand rows s of B
-                f16x gacc = zero16();
-#pragma unroll
-                for (int jn = 0; jn < KN; ++jn) gacc = mfma(ab[jn], cf[which][jn], gacc);
                 // M[t][s] = G'[s][t] 2^(cum_t - cum_s) dl_s for s <= t (else 0),
                 // at s(v) = 32 sb + 8 (v / 4) + 4 half + v % 4, plus the skip
                 // weight D on the diagonal s = t, so the product with x^T also
