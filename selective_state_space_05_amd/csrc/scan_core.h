@@ -345,10 +345,10 @@ struct Walker {
     }
 
     // Per-step values an owner thread keeps from phase A of a chunk to its
-    // phase C: skip term, gate factor, and the number of its steps inside
-    // the range.
+    // phase C: the scan input u (for the skip term), the gate factor, and the
+    // number of its steps inside the range.
     struct Own {
-        float sk[OS], gz[OS];
+        float uu[OS], gz[OS];
         int rem;
     };
 
@@ -394,7 +394,7 @@ struct Walker {
             dl[i] = (FULL || i < rem) ? sp : 0.0f;
             du[i] = (FULL || i < rem) ? sp * u[i] : 0.0f;
             if (OUT) {
-                o.sk[i] = skip * u[i];
+                o.uu[i] = u[i];
                 o.gz[i] = GATE ? silu(zz[i]) : 1.0f;
             } else {
                 sdl += dl[i];
@@ -486,8 +486,12 @@ struct Walker {
                 yv[i + 1] += v.y;
             }
         }
+        // The skip term as one explicit fused multiply-add: left to the
+        // compiler, D*u + sum is contracted in some inlined copies of this
+        // phase and not in others, which changes the last bit of y between
+        // walks of the same steps.
 #pragma unroll
-        for (int i = 0; i < OS; ++i) yv[i] = (yv[i] + o.sk[i]) * o.gz[i];
+        for (int i = 0; i < OS; ++i) yv[i] = fmaf(skip, o.uu[i], yv[i]) * o.gz[i];
         T *py = reinterpret_cast<T *>(reinterpret_cast<char *>(yb) + oo) + (t0 + OS * ok);
         if (FULL) {
             if (VEC) {

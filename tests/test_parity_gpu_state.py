@@ -90,6 +90,34 @@ def test_scan_in_pieces_equals_whole(dev, variant):
     gates.check_state(f64(state), ho, "bf16", "h_last")
 
 
+SPLIT_CASES = [
+    # batch, L, dim, N, io: every row group cut in two (few groups), and a
+    # grid of 300 groups where the last 44 are cut (300 mod 256 compute units)
+    (2, 2048 + 40, 40, 16, "bf16"),
+    (1, 600, 16 * 300, 16, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES)
+def test_scan_split_groups_equal_whole_walk(dev, case):
+    """The chunked kernel cuts some row groups in two parts to balance the
+    compute units, the second part recomputing the state at the cut with the
+    state-only walk.  That is the same sequential evaluation, so the outputs
+    must equal bit for bit those of the walk that keeps every group whole,
+    which the kernel takes when h0 is the h_last buffer itself."""
+    batch, L, dim, N, io = case
+    p = inputs.ScanProblem("case", batch, L, dim, N, io, "scalar", True, True, 60 + N)
+    announce("scan split vs whole %s" % (case,))
+    x = inputs.scan_inputs(p)
+    t = scan_to_dev(x, io, dev)
+    h0 = torch.from_numpy(inputs.initial_state((batch, dim, N), 61)).to(dev)
+    y_split, h_split = scan_h0(t, h0, _lib.VARIANT_CHUNKED)
+    state = h0.clone()
+    y_whole, h_whole = scan_h0(t, state, _lib.VARIANT_CHUNKED, h_out=state)
+    assert torch.equal(y_split, y_whole)
+    assert torch.equal(h_split, h_whole)
+
+
 def test_scan_zero_length_copies_initial_state(dev):
     import selective_state_space_05_amd as mssm
     announce("scan h0 L=0")
