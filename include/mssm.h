@@ -186,9 +186,11 @@ MSSM_API mssm_status mssm_selective_scan_fwd_conv(const void *x, const float *co
  *                                              = 0 / bias = 0 when those
  *                                              inputs are null)
  *   dh0           (batch, dim, N) float32      nullable
- * dB, dC sum over channels and dA, dD, ddelta_bias over batches, with
- * float32 atomic additions: their last bits depend on the order.  Errors as
- * for the forward, plus MSSM_ERR_INVALID_ARG for dz without z or any output
+ * dB and dC sum over channels in a fixed order (deterministic); dA, dD and
+ * ddelta_bias sum over batches with float32 atomic additions, so their last
+ * bits depend on the order.  Scratch (chunk states and per-wave partial
+ * sums of dB and dC) is allocated stream-ordered.  Errors as for the
+ * forward, plus MSSM_ERR_INVALID_ARG for dz without z or any output
  * overlapping an input or another output.
  */
 MSSM_API mssm_status mssm_selective_scan_bwd(const void *u, const void *delta,

@@ -20,11 +20,19 @@
 // states in registers and walks them backwards.  The stored states take
 // rows * ceil(L / K) * N floats of scratch, allocated stream-ordered.
 //
-// dB and dC sum over channels, dA, dD and the bias gradient over batches:
-// a wave first sums over its 64 rows (when they share a batch) with lane
-// shuffles, then one lane adds the sum atomically.  This is the parity form
-// (few waves for few rows, many atomics); the summation order of the
-// atomics makes those sums order-dependent in the last bits.
+// dB and dC sum over channels.  At every step a wave sums its 64 rows'
+// contributions (2 x 16 values per group of 16 state elements) with a
+// transposed reduction -- two cross-row swap levels in registers, then a
+// wave-private LDS pass -- and stores the 32 sums with one coalesced store
+// into a per-wave partial buffer; a second kernel adds the partials of the
+// waves of each batch in a fixed order and writes dB and dC, so they are
+// deterministic.  (Atomic additions from every wave to the same (n, t) at the
+// same time serialised in the caches.)  A wave whose rows span several
+// batches reduces each batch's rows into a partial slot of its own.  dA, dD
+// and the bias gradient are added atomically once per lane at the end, so
+// their last bits depend on the order.
+#include <algorithm>
+
 #include "device_math.h"
 #include "internal.h"
 
@@ -35,27 +43,49 @@ namespace {
 template <int NS>
 constexpr int seg_steps() { return NS <= 4 ? 32 : NS <= 8 ? 16 : NS <= 16 ? 8 : NS <= 32 ? 4 : 2; }
 
-__device__ __forceinline__ float wave_sum(float v) {
+constexpr int kRedPitch = 36;   // LDS row pitch (floats) of the wave's reduction pass
+
+// Sum over the wave's 64 lanes of v[k], k < 32; lane l returns the sum for
+// k = l % 32.  v_permlane32_swap pairs lanes l and l + 32 for k and k + 16,
+// v_permlane16_swap rows (0, 1) and (2, 3) for k and k + 8, so that lane (row
+// r, column c) holds the four-row sums of k = 8 r + i, i < 8, for its column;
+// those go through LDS (row c of `red`), and each lane adds the 16 columns of
+// its k.  The same wave writes and reads `red`, in order, so no barrier.
+__device__ __forceinline__ float reduce32(const float (&v)[32], float *red) {
+    float w[16], x[8];
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
+    for (int k = 0; k < 16; ++k) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[k]), __float_as_uint(v[k + 16]),
+                                                        false, false);
+        w[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(w[k]), __float_as_uint(w[k + 8]),
+                                                        false, false);
+        x[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    const int lane = threadIdx.x & 63;
+    float4 *dst = reinterpret_cast<float4 *>(red + (lane & 15) * kRedPitch + 8 * (lane >> 4));
+    dst[0] = make_float4(x[0], x[1], x[2], x[3]);
+    dst[1] = make_float4(x[4], x[5], x[6], x[7]);
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) s += red[c * kRedPitch + (lane & 31)];
+    return s;
 }
 
-// v summed over the rows of this wave into *p: one atomic per wave when all
-// 64 rows share the address, else one per lane.
-__device__ __forceinline__ void add_rows(float *p, float v, bool shared, int lane) {
-    if (shared) {
-        v = wave_sum(v);
-        if (lane == 0) atomicAdd(p, v);
-    } else {
-        atomicAdd(p, v);
-    }
-}
+// Groups of 16 state elements the partial sums are formed in.
+template <int NS>
+constexpr int n_groups() { return (NS + 15) / 16; }
 
 template <typename T, int NS>
 __global__ __launch_bounds__(64) void scan_bwd_rowserial_kernel(BwdArgs a, float *__restrict__ ck,
-                                                                int nseg) {
+                                                                int nseg, float *__restrict__ part,
+                                                                int nslots) {
     constexpr int K = seg_steps<NS>();
+    constexpr int NG = n_groups<NS>();
+    __shared__ float red[16 * kRedPitch];
     const T *u = static_cast<const T *>(a.u);
     const T *delta = static_cast<const T *>(a.delta);
     const T *Bm = static_cast<const T *>(a.B);
@@ -77,6 +107,13 @@ __global__ __launch_bounds__(64) void scan_bwd_rowserial_kernel(BwdArgs a, float
     const int64_t r_first = static_cast<int64_t>(blockIdx.x) * 64;
     const int64_t r_last = min(r_first + 63, rows - 1);
     const bool one_batch = r_first / a.dim == r_last / a.dim;
+    // batches this wave's rows span (wave-uniform): slot s holds the sums over
+    // its rows of batch b_first + s
+    const int nspan = static_cast<int>(r_last / a.dim - r_first / a.dim) + 1;
+    const int64_t b_first = r_first / a.dim;
+    const bool want_bc = a.dB || a.dC;
+    // this wave's partial sums: [slot][t][NG][32]
+    float *pw = part + static_cast<int64_t>(blockIdx.x) * nslots * L * (NG * 32);
 
     float A2[NS];
 #pragma unroll
@@ -102,7 +139,7 @@ __global__ __launch_bounds__(64) void scan_bwd_rowserial_kernel(BwdArgs a, float
         for (int k = 0; k < K; ++k) {
             const int64_t t = static_cast<int64_t>(s) * K + k;
             if (t < L) {
-                const float dl = softplus_libm(Io<T>::load(delta, rb + t) + bias);
+                const float dl = softplus(Io<T>::load(delta, rb + t) + bias);
                 const float du = dl * Io<T>::load(u, rb + t);
 #pragma unroll
                 for (int n = 0; n < NS; ++n)
@@ -131,7 +168,7 @@ __global__ __launch_bounds__(64) void scan_bwd_rowserial_kernel(BwdArgs a, float
         for (int k = 0; k < K; ++k) {
             const int64_t t = t0 + k;
             if (t < L) {
-                const float dl = softplus_libm(Io<T>::load(delta, rb + t) + bias);
+                const float dl = softplus(Io<T>::load(delta, rb + t) + bias);
                 const float du = dl * Io<T>::load(u, rb + t);
 #pragma unroll
                 for (int n = 0; n < NS; ++n)
@@ -146,8 +183,8 @@ __global__ __launch_bounds__(64) void scan_bwd_rowserial_kernel(BwdArgs a, float
             const int64_t t = t0 + k;
             if (t >= L) continue;
             const float x = Io<T>::load(delta, rb + t) + bias;
-            const float dl = softplus_libm(x);
-            const float sig = 1.0f / (1.0f + expf(-x));
+            const float dl = softplus(x);
+            const float sig = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
             const float ut = Io<T>::load(u, rb + t);
             const float dyt = valid ? Io<T>::load(dy, rb + t) : 0.0f;
             float ds = dyt;
@@ -157,27 +194,54 @@ __global__ __launch_bounds__(64) void scan_bwd_rowserial_kernel(BwdArgs a, float
 #pragma unroll
                 for (int n = 0; n < NS; ++n)
                     if (n < N) sv = fmaf(Io<T>::load(Cb, n * L + t), hs[k][n], sv);
-                const float sz = 1.0f / (1.0f + expf(-zt));
+                const float sz = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zt * kLog2e));
                 ds = dyt * zt * sz;
                 if (valid && a.dz) a.dz[rb + t] = dyt * sv * sz * (1.0f + zt * (1.0f - sz));
             }
             dDacc = fmaf(ds, ut, dDacc);
             float dut = ds * skip, ddl = 0.0f;
+            // this row's dC (k < 16) and dB (k >= 16) terms of each group
+            // of 16 state elements
+            float vbc[NG][32];
 #pragma unroll
             for (int n = 0; n < NS; ++n) {
+                float cterm = 0.0f, bterm = 0.0f;
                 if (n < N) {
                     const float Bt = Io<T>::load(Bb, n * L + t);
                     const float Ct = Io<T>::load(Cb, n * L + t);
                     const float an = fast_exp2(dl * A2[n]);
                     const float hp = k > 0 ? hs[k > 0 ? k - 1 : 0][n] : hb[n];
                     dh[n] = fmaf(ds, Ct, dh[n]);
-                    if (a.dC) add_rows(a.dC + (b * N + n) * L + t, ds * hs[k][n], one_batch, lane);
+                    cterm = ds * hs[k][n];
                     const float ha = hp * an;
                     dAacc[n] = fmaf(dh[n] * ha, dl, dAacc[n]);
-                    if (a.dB) add_rows(a.dB + (b * N + n) * L + t, dh[n] * dl * ut, one_batch, lane);
+                    bterm = dh[n] * dl * ut;
                     dut = fmaf(dh[n] * dl, Bt, dut);
                     ddl = fmaf(dh[n], fmaf(ha, A2[n] * kLn2, Bt * ut), ddl);
                     dh[n] *= an;
+                }
+                vbc[n / 16][n % 16] = cterm;
+                vbc[n / 16][16 + n % 16] = bterm;
+            }
+#pragma unroll
+            for (int n = NS; n < NG * 16; ++n) {
+                vbc[n / 16][n % 16] = 0.0f;
+                vbc[n / 16][16 + n % 16] = 0.0f;
+            }
+            if (want_bc) {
+                // sums over the wave's rows of each batch it holds, one
+                // coalesced store of 32 sums per group (lanes 0..31)
+                for (int slot = 0; slot < nspan; ++slot) {
+                    const bool mine = one_batch || b == b_first + slot;
+#pragma unroll
+                    for (int gi = 0; gi < NG; ++gi) {
+                        float vm[32];
+#pragma unroll
+                        for (int q = 0; q < 32; ++q) vm[q] = mine ? vbc[gi][q] : 0.0f;
+                        const float sum = reduce32(vm, red);
+                        if (lane < 32)
+                            pw[(static_cast<int64_t>(slot) * L + t) * (NG * 32) + gi * 32 + lane] = sum;
+                    }
                 }
             }
             if (valid) {
@@ -203,17 +267,61 @@ __global__ __launch_bounds__(64) void scan_bwd_rowserial_kernel(BwdArgs a, float
     }
 }
 
+// dB[b, n, t] and dC[b, n, t] from the per-wave partial sums: one thread per
+// (b, t, column) adds the partials of the waves holding rows of batch b, in
+// wave order (slot b - b_first for a wave whose first row is in batch
+// b_first).
+__global__ __launch_bounds__(256) void scan_bwd_bc_kernel(const float *__restrict__ part, int nslots,
+                                                          int ng, int64_t batch, int64_t dim,
+                                                          int64_t L, int N, float *dB, float *dC) {
+    const int64_t cols = static_cast<int64_t>(ng) * 32;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= batch * L * cols) return;
+    const int col = static_cast<int>(i % cols);
+    const int64_t t = (i / cols) % L;
+    const int64_t b = i / (cols * L);
+    const int gi = col / 32, kk = col % 32;
+    const int n = 16 * gi + kk % 16;
+    if (n >= N) return;
+    const int64_t w_lo = (b * dim) / 64, w_hi = ((b + 1) * dim - 1) / 64;
+    float s = 0.0f;
+    for (int64_t w = w_lo; w <= w_hi; ++w) {
+        const int64_t slot = b - (w * 64) / dim;
+        s += part[((w * nslots + slot) * L + t) * cols + col];
+    }
+    float *out = kk < 16 ? dC : dB;
+    if (out) out[(b * N + n) * L + t] = s;
+}
+
 template <typename T, int NS>
 hipError_t launch_typed(const BwdArgs &a, hipStream_t stream) {
     constexpr int K = seg_steps<NS>();
+    constexpr int NG = n_groups<NS>();
     const int64_t rows = a.batch * a.dim;
+    const int64_t waves = (rows + 63) / 64;
     const int nseg = static_cast<int>((a.L + K - 1) / K);
+    // partial slots: the most batches any 64 consecutive rows span
+    const int64_t span = a.dim % 64 == 0 ? 1 : 63 / a.dim + 2;
+    const int nslots = static_cast<int>(std::min<int64_t>(std::min<int64_t>(a.batch, span), 64));
+    const bool want_bc = a.dB || a.dC;
+    const size_t ck_bytes = static_cast<size_t>(rows) * nseg * a.N * sizeof(float);
+    const size_t part_bytes =
+        want_bc ? static_cast<size_t>(waves) * nslots * a.L * NG * 32 * sizeof(float) : 0;
     void *mem = nullptr;
-    hipError_t e = hipMallocAsync(&mem, static_cast<size_t>(rows) * nseg * a.N * sizeof(float), stream);
+    hipError_t e = hipMallocAsync(&mem, ck_bytes + part_bytes, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((scan_bwd_rowserial_kernel<T, NS>), dim3(static_cast<uint32_t>((rows + 63) / 64)),
-                       dim3(64), 0, stream, a, static_cast<float *>(mem), nseg);
+    float *ck = static_cast<float *>(mem);
+    float *part = reinterpret_cast<float *>(static_cast<char *>(mem) + ck_bytes);
+    hipLaunchKernelGGL((scan_bwd_rowserial_kernel<T, NS>), dim3(static_cast<uint32_t>(waves)), dim3(64), 0,
+                       stream, a, ck, nseg, part, nslots);
     e = hipGetLastError();
+    if (e == hipSuccess && want_bc) {
+        const int64_t n = a.batch * a.L * NG * 32;
+        hipLaunchKernelGGL(scan_bwd_bc_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0,
+                           stream, part, nslots, NG, a.batch, a.dim, a.L, static_cast<int>(a.N), a.dB,
+                           a.dC);
+        e = hipGetLastError();
+    }
     const hipError_t ef = hipFreeAsync(mem, stream);
     return e != hipSuccess ? e : ef;
 }
