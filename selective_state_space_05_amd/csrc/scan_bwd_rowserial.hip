@@ -328,29 +328,36 @@ hipError_t launch_typed(const BwdArgs &a, hipStream_t stream) {
 
 
 // ---------------------------------------------------------------------------
-// Quad form for N <= 16: four lanes per row, each with four state elements
-// (lane = 4 i + g: row i of the wave's 16, elements n = 4 g .. 4 g + 3), so a
-// layer has four times the waves of the one-lane-per-row form and each lane
-// a quarter of its serial work.  The row's scalars are formed by all four
-// lanes; sums over n (the output before the gate, du and d(dl)) are two quad
-// swaps; dB and dC use the per-wave partial buffer as above.
+// Lane-group forms for N <= 16: LPR lanes per row (4 or 8), each with NPL =
+// 16 / LPR state elements (lane = LPR i + g: row i of the wave's 64 / LPR,
+// elements n = NPL g .. NPL g + NPL - 1), so a layer has LPR times the waves
+// of the one-lane-per-row form and each lane 1 / LPR of its serial work.  The
+// row's scalars are formed by all LPR lanes; sums over n (the output before
+// the gate, du and d(dl)) are DPP swaps within the lane group; dB and dC use
+// the per-wave partial buffer as above.
 // ---------------------------------------------------------------------------
-constexpr int kQuadK = 16;        // steps per stored segment
-constexpr int kQuadRedPitch = 8;  // floats per column of the quad form's reduction pass
+constexpr int kQuadRedPitch = 8;  // floats per column of the four-lane form's reduction pass
 
-__device__ __forceinline__ float quad_sum(float v) {
-    // quad_perm [1,0,3,2] then [2,3,0,1]: every lane of a quad gets the sum
+template <int LPR> constexpr int grp_steps() { return LPR == 4 ? 16 : 32; }   // steps per stored segment
+
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+    // quad_perm [1,0,3,2] then [2,3,0,1]: every lane of a quad gets the quad's
+    // sum; for eight lanes, row_half_mirror then adds the other quad
     v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xb1, 0xf, 0xf, true));
     v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4e, 0xf, 0xf, true));
+    if (LPR == 8)
+        v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xf, 0xf, true));
     return v;
 }
 
-// Sum over the wave's 16 rows of v[q] (q < 4: dC terms of n = 4 g + q; q >= 4:
-// dB terms of n = 4 g + q - 4).  Lanes l and l + 32 are paired for q, q + 4
-// (v_permlane32_swap), then l and l + 16 for q, q + 2 (v_permlane16_swap), so
-// lane l holds the sums over its column l % 16 of q = 4 b5 + 2 b4 + {0, 1};
-// the four columns of group g go through LDS.  Lane o < 32 returns the sum
-// for group o % 4 and q = o / 4.
+// Four lanes per row: sum over the wave's 16 rows of v[q] (q < 4: dC terms of
+// n = 4 g + q; q >= 4: dB terms of n = 4 g + q - 4).  Lanes l and l + 32 are
+// paired for q, q + 4 (v_permlane32_swap), then l and l + 16 for q, q + 2
+// (v_permlane16_swap), so lane l holds the sums over its column l % 16 of
+// q = 4 b5 + 2 b4 + {0, 1}; the four columns of group g go through LDS.  Lane
+// o < 32 returns the sum for group o % 4 and q = o / 4, the partial column
+// (q < 4 ? 0 : 16) + 4 g + q % 4.
 __device__ __forceinline__ float reduce_quad8(const float (&v)[8], float *red) {
     float w[4], x[2];
 #pragma unroll
@@ -375,10 +382,32 @@ __device__ __forceinline__ float reduce_quad8(const float (&v)[8], float *red) {
     return s;
 }
 
-template <typename T>
-__global__ __launch_bounds__(64) void scan_bwd_quad_kernel(BwdArgs a, float *__restrict__ ck, int nseg,
-                                                           float *__restrict__ part, int nslots) {
-    constexpr int K = kQuadK;
+// Eight lanes per row: sum over the wave's 8 rows of v[q] (q < 2: dC terms of
+// n = 2 g + q; q >= 2: dB terms of n = 2 g + q - 2).  v_permlane32_swap pairs
+// lanes l, l + 32 for q, q + 2; v_permlane16_swap pairs l, l + 16 for the two
+// left; a row rotation by 8 adds the other row of the 16-lane DPP row.  Lane
+// l then holds the sum for group l % 8 and q = 2 b5 + b4, the partial column
+// (b5 ? 16 : 0) + 2 g + b4; the lanes with bit 3 clear store it.
+__device__ __forceinline__ float reduce_octo4(const float (&v)[4]) {
+    float w[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[k]), __float_as_uint(v[k + 2]),
+                                                        false, false);
+        w[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(w[0]), __float_as_uint(w[1]), false, false);
+    float x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xf, 0xf, true));
+    return x;
+}
+
+template <typename T, int LPR>
+__global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__restrict__ ck, int nseg,
+                                                            float *__restrict__ part, int nslots) {
+    constexpr int K = grp_steps<LPR>();
+    constexpr int NPL = 16 / LPR;     // state elements per lane
+    constexpr int RPW = 64 / LPR;     // rows per wave
     const T *u = static_cast<const T *>(a.u);
     const T *delta = static_cast<const T *>(a.delta);
     const T *Bm = static_cast<const T *>(a.B);
@@ -389,25 +418,25 @@ __global__ __launch_bounds__(64) void scan_bwd_quad_kernel(BwdArgs a, float *__r
     const int64_t rows = a.batch * a.dim, L = a.L;
     const int N = static_cast<int>(a.N);
     const int lane = threadIdx.x;
-    const int g = lane & 3;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + (lane >> 2);
+    const int g = lane % LPR;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * RPW + lane / LPR;
     const bool valid = row < rows;
     // lanes past the last row walk the last row with zero output gradients
     const int64_t r = valid ? row : rows - 1;
     const int64_t b = r / a.dim;
     const int64_t d = r - b * a.dim;
-    const int64_t r_first = static_cast<int64_t>(blockIdx.x) * 16;
-    const int64_t r_last = min(r_first + 15, rows - 1);
+    const int64_t r_first = static_cast<int64_t>(blockIdx.x) * RPW;
+    const int64_t r_last = min(r_first + RPW - 1, rows - 1);
     const int nspan = static_cast<int>(r_last / a.dim - r_first / a.dim) + 1;
     const int64_t b_first = r_first / a.dim;
     const bool want_bc = a.dB || a.dC;
     float *pw = part + static_cast<int64_t>(blockIdx.x) * nslots * L * 32;
 
-    float A2[4];
-    bool nok[4];
+    float A2[NPL];
+    bool nok[NPL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int n = 4 * g + i;
+    for (int i = 0; i < NPL; ++i) {
+        const int n = NPL * g + i;
         nok[i] = n < N;
         A2[i] = nok[i] ? a.A[d * N + n] * kLog2e : 0.0f;
     }
@@ -416,15 +445,18 @@ __global__ __launch_bounds__(64) void scan_bwd_quad_kernel(BwdArgs a, float *__r
     const int64_t rb = r * L;
     const T *Bb = Bm + b * N * L;
     const T *Cb = Cm + b * N * L;
-    // stored states: 16 floats per (row, segment), this lane's four at 4 g
-    float *ckr = ck + r * static_cast<int64_t>(nseg) * 16 + 4 * g;
+    // stored states: 16 floats per (row, segment), this lane's NPL at NPL g
+    float *ckr = ck + r * static_cast<int64_t>(nseg) * 16 + NPL * g;
 
     // ---- forward: the state before every segment ---------------------------
-    float h[4];
+    float h[NPL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) h[i] = (a.h0 && nok[i]) ? a.h0[r * N + 4 * g + i] : 0.0f;
+    for (int i = 0; i < NPL; ++i) h[i] = (a.h0 && nok[i]) ? a.h0[r * N + NPL * g + i] : 0.0f;
     for (int s = 0; s < nseg; ++s) {
-        if (valid) *reinterpret_cast<float4 *>(ckr + s * 16) = make_float4(h[0], h[1], h[2], h[3]);
+        if (valid) {
+#pragma unroll
+            for (int i = 0; i < NPL; ++i) ckr[s * 16 + i] = h[i];
+        }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int64_t t = static_cast<int64_t>(s) * K + k;
@@ -432,28 +464,29 @@ __global__ __launch_bounds__(64) void scan_bwd_quad_kernel(BwdArgs a, float *__r
                 const float dl = softplus(Io<T>::load(delta, rb + t) + bias);
                 const float du = dl * Io<T>::load(u, rb + t);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < NPL; ++i)
                     if (nok[i])
-                        h[i] = fmaf(fast_exp2(dl * A2[i]), h[i], du * Io<T>::load(Bb, (4 * g + i) * L + t));
+                        h[i] = fmaf(fast_exp2(dl * A2[i]), h[i], du * Io<T>::load(Bb, (NPL * g + i) * L + t));
             }
         }
     }
 
     // ---- reverse ---------------------------------------------------------
-    float dh[4], dAacc[4];
+    float dh[NPL], dAacc[NPL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        dh[i] = (valid && a.dh_last && nok[i]) ? a.dh_last[r * N + 4 * g + i] : 0.0f;
+    for (int i = 0; i < NPL; ++i) {
+        dh[i] = (valid && a.dh_last && nok[i]) ? a.dh_last[r * N + NPL * g + i] : 0.0f;
         dAacc[i] = 0.0f;
     }
     float dDacc = 0.0f, dbacc = 0.0f;
     for (int s = nseg - 1; s >= 0; --s) {
         const int64_t t0 = static_cast<int64_t>(s) * K;
-        const float4 hb4 = *reinterpret_cast<const float4 *>(ckr + s * 16);
-        const float hb[4] = {hb4.x, hb4.y, hb4.z, hb4.w};
-        float hs[K][4];
+        float hb[NPL];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = hb[i];
+        for (int i = 0; i < NPL; ++i) hb[i] = ckr[s * 16 + i];
+        float hs[K][NPL];
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) h[i] = hb[i];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int64_t t = t0 + k;
@@ -461,12 +494,12 @@ __global__ __launch_bounds__(64) void scan_bwd_quad_kernel(BwdArgs a, float *__r
                 const float dl = softplus(Io<T>::load(delta, rb + t) + bias);
                 const float du = dl * Io<T>::load(u, rb + t);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < NPL; ++i)
                     if (nok[i])
-                        h[i] = fmaf(fast_exp2(dl * A2[i]), h[i], du * Io<T>::load(Bb, (4 * g + i) * L + t));
+                        h[i] = fmaf(fast_exp2(dl * A2[i]), h[i], du * Io<T>::load(Bb, (NPL * g + i) * L + t));
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) hs[k][i] = h[i];
+            for (int i = 0; i < NPL; ++i) hs[k][i] = h[i];
         }
 #pragma unroll
         for (int k = K - 1; k >= 0; --k) {
@@ -482,22 +515,22 @@ __global__ __launch_bounds__(64) void scan_bwd_quad_kernel(BwdArgs a, float *__r
                 const float zt = Io<T>::load(z, rb + t);
                 float sp = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (nok[i]) sp = fmaf(Io<T>::load(Cb, (4 * g + i) * L + t), hs[k][i], sp);
-                const float sv = fmaf(skip, ut, quad_sum(sp));
+                for (int i = 0; i < NPL; ++i)
+                    if (nok[i]) sp = fmaf(Io<T>::load(Cb, (NPL * g + i) * L + t), hs[k][i], sp);
+                const float sv = fmaf(skip, ut, group_sum<LPR>(sp));
                 const float sz = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zt * kLog2e));
                 ds = dyt * zt * sz;
                 if (valid && g == 0 && a.dz) a.dz[rb + t] = dyt * sv * sz * (1.0f + zt * (1.0f - sz));
             }
             dDacc = fmaf(ds, ut, dDacc);
             float dup = 0.0f, ddlp = 0.0f;
-            float vbc[8];
+            float vbc[2 * NPL];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < NPL; ++i) {
                 float cterm = 0.0f, bterm = 0.0f;
                 if (nok[i]) {
-                    const float Bt = Io<T>::load(Bb, (4 * g + i) * L + t);
-                    const float Ct = Io<T>::load(Cb, (4 * g + i) * L + t);
+                    const float Bt = Io<T>::load(Bb, (NPL * g + i) * L + t);
+                    const float Ct = Io<T>::load(Cb, (NPL * g + i) * L + t);
                     const float an = fast_exp2(dl * A2[i]);
                     const float hp = k > 0 ? hs[k > 0 ? k - 1 : 0][i] : hb[i];
                     dh[i] = fmaf(ds, Ct, dh[i]);
@@ -510,37 +543,43 @@ __global__ __launch_bounds__(64) void scan_bwd_quad_kernel(BwdArgs a, float *__r
                     dh[i] *= an;
                 }
                 vbc[i] = cterm;
-                vbc[4 + i] = bterm;
+                vbc[NPL + i] = bterm;
             }
-            const float dut = fmaf(ds, skip, quad_sum(dup));
-            const float ddl = quad_sum(ddlp);
+            const float dut = fmaf(ds, skip, group_sum<LPR>(dup));
+            const float ddl = group_sum<LPR>(ddlp);
             if (valid && g == 0) {
                 a.du[rb + t] = dut;
                 a.ddelta[rb + t] = ddl * sig;
             }
             dbacc = fmaf(ddl, sig, dbacc);
             if (want_bc) {
-                // sums over the wave's rows of each batch it holds; lane o <
-                // 32 stores column dC n (q < 4) or 16 + dB n (q >= 4)
-                const int o = lane & 31, og = o & 3, oq = o >> 2;
-                const int col = (oq < 4 ? 0 : 16) + 4 * og + (oq & 3);
+                // sums over the wave's rows of each batch it holds, stored as
+                // partial column dC n (< 16) or 16 + dB n
                 for (int slot = 0; slot < nspan; ++slot) {
                     const bool mine = nspan == 1 || b == b_first + slot;
-                    float vm[8];
+                    float vm[2 * NPL];
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) vm[q] = mine ? vbc[q] : 0.0f;
-                    const float sum = reduce_quad8(vm, red);
-                    if (lane < 32) pw[(static_cast<int64_t>(slot) * L + t) * 32 + col] = sum;
+                    for (int q = 0; q < 2 * NPL; ++q) vm[q] = mine ? vbc[q] : 0.0f;
+                    float* dst = pw + (static_cast<int64_t>(slot) * L + t) * 32;
+                    if constexpr (LPR == 4) {
+                        const float sum = reduce_quad8(vm, red);
+                        const int o = lane & 31, og = o & 3, oq = o >> 2;
+                        if (lane < 32) dst[(oq < 4 ? 0 : 16) + 4 * og + (oq & 3)] = sum;
+                    } else {
+                        const float sum = reduce_octo4(vm);
+                        if ((lane & 8) == 0)
+                            dst[((lane >> 5) & 1 ? 16 : 0) + 2 * (lane & 7) + ((lane >> 4) & 1)] = sum;
+                    }
                 }
             }
         }
     }
     if (valid) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < NPL; ++i) {
             if (!nok[i]) continue;
-            if (a.dh0) a.dh0[r * N + 4 * g + i] = dh[i];
-            if (a.dA) atomicAdd(a.dA + d * N + 4 * g + i, dAacc[i]);
+            if (a.dh0) a.dh0[r * N + NPL * g + i] = dh[i];
+            if (a.dA) atomicAdd(a.dA + d * N + NPL * g + i, dAacc[i]);
         }
         if (g == 0) {
             if (a.dD) atomicAdd(a.dD + d, dDacc);
@@ -549,14 +588,16 @@ __global__ __launch_bounds__(64) void scan_bwd_quad_kernel(BwdArgs a, float *__r
     }
 }
 
-template <typename T>
-hipError_t launch_quad(const BwdArgs &a, hipStream_t stream) {
+template <typename T, int LPR>
+hipError_t launch_group(const BwdArgs &a, hipStream_t stream) {
+    constexpr int K = grp_steps<LPR>();
+    constexpr int RPW = 64 / LPR;
     const int64_t rows = a.batch * a.dim;
-    const int64_t waves = (rows + 15) / 16;
-    const int nseg = static_cast<int>((a.L + kQuadK - 1) / kQuadK);
-    // partial slots: the most batches any 16 consecutive rows span
-    const int64_t span = a.dim % 16 == 0 ? 1 : 15 / a.dim + 2;
-    const int nslots = static_cast<int>(std::min<int64_t>(std::min<int64_t>(a.batch, span), 16));
+    const int64_t waves = (rows + RPW - 1) / RPW;
+    const int nseg = static_cast<int>((a.L + K - 1) / K);
+    // partial slots: the most batches any RPW consecutive rows span
+    const int64_t span = a.dim % RPW == 0 ? 1 : (RPW - 1) / a.dim + 2;
+    const int nslots = static_cast<int>(std::min<int64_t>(std::min<int64_t>(a.batch, span), RPW));
     const bool want_bc = a.dB || a.dC;
     const size_t ck_bytes = static_cast<size_t>(rows) * nseg * 16 * sizeof(float);
     const size_t part_bytes = want_bc ? static_cast<size_t>(waves) * nslots * a.L * 32 * sizeof(float) : 0;
@@ -565,13 +606,13 @@ hipError_t launch_quad(const BwdArgs &a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     float *ck = static_cast<float *>(mem);
     float *part = reinterpret_cast<float *>(static_cast<char *>(mem) + ck_bytes);
-    hipLaunchKernelGGL((scan_bwd_quad_kernel<T>), dim3(static_cast<uint32_t>(waves)), dim3(64), 0, stream, a,
-                       ck, nseg, part, nslots);
+    hipLaunchKernelGGL((scan_bwd_group_kernel<T, LPR>), dim3(static_cast<uint32_t>(waves)), dim3(64), 0, stream,
+                       a, ck, nseg, part, nslots);
     e = hipGetLastError();
     if (e == hipSuccess && want_bc) {
         const int64_t n = a.batch * a.L * 32;
         hipLaunchKernelGGL(scan_bwd_bc_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0,
-                           stream, part, nslots, 1, 16, a.batch, a.dim, a.L, static_cast<int>(a.N), a.dB,
+                           stream, part, nslots, 1, RPW, a.batch, a.dim, a.L, static_cast<int>(a.N), a.dB,
                            a.dC);
         e = hipGetLastError();
     }
@@ -581,7 +622,8 @@ hipError_t launch_quad(const BwdArgs &a, hipStream_t stream) {
 
 template <typename T>
 hipError_t launch_by_n(const BwdArgs &a, hipStream_t stream) {
-    if (a.N <= 16) return launch_quad<T>(a, stream);
+    if (a.N <= 8) return launch_group<T, 4>(a, stream);
+    if (a.N <= 16) return launch_group<T, 8>(a, stream);
     if (a.N <= 32) return launch_typed<T, 32>(a, stream);
     return launch_typed<T, 64>(a, stream);
 }
@@ -589,7 +631,7 @@ hipError_t launch_by_n(const BwdArgs &a, hipStream_t stream) {
 }  // namespace
 
 bool scan_bwd_supported(const BwdArgs &a) {
-    return a.N >= 1 && a.N <= 64 && (a.batch * a.dim + 15) / 16 < (int64_t(1) << 31) &&
+    return a.N >= 1 && a.N <= 64 && (a.batch * a.dim + 7) / 8 < (int64_t(1) << 31) &&
            a.L < (int64_t(1) << 31);
 }
 
