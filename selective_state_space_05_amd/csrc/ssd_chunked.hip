@@ -580,12 +580,29 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
             const float et = fast_exp2(cum_t);
             const int t = t0 + tl;
             const uint32_t row = static_cast<uint32_t>(t < g.L ? t : 0) * static_cast<uint32_t>(rowX);
+            // Both head-dimension tiles, with the hi and lo parts of h_in in
+            // accumulators of their own: four independent chains of matrix-core
+            // products instead of one dependent chain per tile.  (Rows of a
+            // tile past the slice's columns compute values that are not
+            // stored.)
+            f16x yo2[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};
+#pragma unroll
+            for (int jn = 0; jn < KN; ++jn) {
+                const int n8 = 16 * jn + 8 * half;
+#pragma unroll
+                for (int pt = 0; pt < 2; ++pt) {
+                    const bf8 ah = *reinterpret_cast<const bf8 *>(&sm.Hh[(pt * 32 + l32) * HP + n8]);
+                    const bf8 al = *reinterpret_cast<const bf8 *>(&sm.Hl[(pt * 32 + l32) * HP + n8]);
+                    yo2[pt][0] = mfma(ah, cf[which][jn], yo2[pt][0]);
+                    yo2[pt][1] = mfma(al, cf[which][jn], yo2[pt][1]);
+                }
+            }
 #pragma unroll
             for (int pt = 0; pt < 2; ++pt) {
                 if (pt * 32 >= pcols) break;
                 // gate values of this lane's step for the tile's 16 head-dimension
-                // columns, loaded ahead of the products below (vector path; the
-                // element path loads them at the stores)
+                // columns (vector path; the element path loads them at the
+                // stores)
                 uint2 zq[4];
                 if (VEC && GATE) {
 #pragma unroll
@@ -594,15 +611,7 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
                         zq[q4] = p < pcols ? *reinterpret_cast<const uint2 *>(zg + row + p) : make_uint2(0, 0);
                     }
                 }
-                f16x yo = zero16();
-#pragma unroll
-                for (int jn = 0; jn < KN; ++jn) {
-                    const int n8 = 16 * jn + 8 * half;
-                    const bf8 ah = *reinterpret_cast<const bf8 *>(&sm.Hh[(pt * 32 + l32) * HP + n8]);
-                    const bf8 al = *reinterpret_cast<const bf8 *>(&sm.Hl[(pt * 32 + l32) * HP + n8]);
-                    yo = mfma(ah, cf[which][jn], yo);
-                    yo = mfma(al, cf[which][jn], yo);
-                }
+                const f16x yo = yo2[pt][0] + yo2[pt][1];
                 if (t < g.L) {
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
