@@ -285,6 +285,9 @@ __global__ __launch_bounds__(256) void scan_bwd_bc_kernel(const float *__restric
     if (n >= N) return;
     const int64_t w_lo = (b * dim) / rpw, w_hi = ((b + 1) * dim - 1) / rpw;
     float s = 0.0f;
+    // unrolled so that several waves' partials are in flight at once (the
+    // adds stay in wave order)
+#pragma unroll 8
     for (int64_t w = w_lo; w <= w_hi; ++w) {
         const int64_t slot = b - (w * rpw) / dim;
         s += part[((w * nslots + slot) * L + t) * cols + col];
