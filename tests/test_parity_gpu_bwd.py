@@ -42,6 +42,8 @@ BWD_CASES = [
     (1, 50, 70, 32, "f32", "scalar", True, True, True),
     (1, 33, 10, 64, "f32", "scalar", False, True, True),        # N = 64 (limit)
     (3, 1, 5, 8, "f32", "scalar", True, True, True),            # single step
+    (4, 40, 3, 12, "f32", "per_channel", True, True, True),     # 8-row waves over 3-4 batches
+    (2, 1024, 640, 16, "bf16", "scalar", True, True, True),     # 80 eight-row waves per batch
 ]
 
 
