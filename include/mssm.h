@@ -188,9 +188,13 @@ MSSM_API mssm_status mssm_selective_scan_fwd_conv(const void *x, const float *co
  *   dh0           (batch, dim, N) float32      nullable
  * dB and dC sum over channels in a fixed order (deterministic); dA, dD and
  * ddelta_bias sum over batches with float32 atomic additions, so their last
- * bits depend on the order.  Scratch (chunk states and per-wave partial
- * sums of dB and dC) is allocated stream-ordered.  Errors as for the
- * forward, plus MSSM_ERR_INVALID_ARG for dz without z or any output
+ * bits depend on the order.  Scratch is allocated and freed stream-ordered:
+ * the states every K steps (batch * dim * ceil(L / K) * 64 bytes, K = 32
+ * for 8 < N <= 16 and 16 for N <= 8) and, when dB or dC is requested,
+ * per-wave partial sums of about batch * dim / 8 * L * 128 bytes for
+ * 8 < N <= 16 (half that for N <= 8; 4.3 GB for L = 2^20 with 256
+ * channels); an allocation failure returns MSSM_ERR_HIP.  Errors as for
+ * the forward, plus MSSM_ERR_INVALID_ARG for dz without z or any output
  * overlapping an input or another output.
  */
 MSSM_API mssm_status mssm_selective_scan_bwd(const void *u, const void *delta,
