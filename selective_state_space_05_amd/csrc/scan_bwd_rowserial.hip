@@ -1,6 +1,8 @@
-// scan_bwd_rowserial.hip -- backward of the selective scan in its plainest
-// GPU form: one lane owns one (batch, channel) row, as in the row-serial
-// forward, and differentiates its walk in reverse.
+// scan_bwd_rowserial.hip -- backward of the selective scan, walking each
+// (batch, channel) row in reverse as the row-serial forward walks it forward.
+// For N <= 16 a group of 8 (or, for N <= 8, 4) lanes owns a row, each lane a
+// slice of its state elements (the lane-group kernel below); for larger N one
+// lane owns a row with all its state elements.
 //
 // Forward per step ("Mamba状态空间模型的硬件感知推理优化" (ybb.press) sections 1
 // and 3.1; www.mhpq.cn/news/984979 essay section 2.2; the tencentcloud.csdn.net
@@ -20,10 +22,10 @@
 // states in registers and walks them backwards.  The stored states take
 // rows * ceil(L / K) * N floats of scratch, allocated stream-ordered.
 //
-// dB and dC sum over channels.  At every step a wave sums its 64 rows'
+// dB and dC sum over channels.  At every step a wave sums its rows'
 // contributions (2 x 16 values per group of 16 state elements) with a
-// transposed reduction -- two cross-row swap levels in registers, then a
-// wave-private LDS pass -- and stores the 32 sums with one coalesced store
+// transposed reduction -- cross-row swaps in registers, then a wave-private
+// LDS pass or a row rotation -- and stores the 32 sums with one store
 // into a per-wave partial buffer; a second kernel adds the partials of the
 // waves of each batch in a fixed order and writes dB and dC, so they are
 // deterministic.  (Atomic additions from every wave to the same (n, t) at the
