@@ -189,8 +189,8 @@ MSSM_API mssm_status mssm_selective_scan_fwd_conv(const void *x, const float *co
  * dB and dC sum over channels in a fixed order (deterministic); dA, dD and
  * ddelta_bias sum over batches with float32 atomic additions, so their last
  * bits depend on the order.  Scratch is allocated and freed stream-ordered:
- * the states every K steps (batch * dim * ceil(L / K) * 64 bytes, K = 32
- * for 8 < N <= 16 and 16 for N <= 8) and, when dB or dC is requested,
+ * the states every 16 steps (batch * dim * ceil(L / 16) * 64 bytes for
+ * N <= 16) and, when dB or dC is requested,
  * per-wave partial sums of about batch * dim / 8 * L * 128 bytes for
  * 8 < N <= 16 (half that for N <= 8; 4.3 GB for L = 2^20 with 256
  * channels); an allocation failure returns MSSM_ERR_HIP.  Errors as for

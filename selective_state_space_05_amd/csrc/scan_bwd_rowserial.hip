@@ -343,7 +343,7 @@ hipError_t launch_typed(const BwdArgs &a, hipStream_t stream) {
 // ---------------------------------------------------------------------------
 constexpr int kQuadRedPitch = 8;  // floats per column of the four-lane form's reduction pass
 
-template <int LPR> constexpr int grp_steps() { return LPR == 4 ? 16 : 32; }   // steps per stored segment
+template <int LPR> constexpr int grp_steps() { return 16; }   // steps per stored segment
 
 template <int LPR>
 __device__ __forceinline__ float group_sum(float v) {
@@ -407,12 +407,36 @@ __device__ __forceinline__ float reduce_octo4(const float (&v)[4]) {
     return x;
 }
 
+// Value of v held by lane `src` of this lane's group of LPR lanes, through an
+// LDS-free swizzle (broadcast mode: and-mask keeps the group bits, or-mask
+// selects the lane).  src must fold to a constant.
+template <int LPR, int SRC>
+__device__ __forceinline__ float grp_bcast_c(float v) {
+    constexpr int pat = (0x20 - LPR) | (SRC << 5);
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), pat));
+}
+template <int LPR>
+__device__ __forceinline__ float grp_bcast(float v, int src) {
+    switch (src) {
+    case 0: return grp_bcast_c<LPR, 0>(v);
+    case 1: return grp_bcast_c<LPR, 1>(v);
+    case 2: return grp_bcast_c<LPR, 2>(v);
+    case 3: return grp_bcast_c<LPR, 3>(v);
+    case 4: return grp_bcast_c<LPR, 4 % LPR>(v);
+    case 5: return grp_bcast_c<LPR, 5 % LPR>(v);
+    case 6: return grp_bcast_c<LPR, 6 % LPR>(v);
+    default: return grp_bcast_c<LPR, 7 % LPR>(v);
+    }
+}
+
 template <typename T, int LPR>
 __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__restrict__ ck, int nseg,
                                                             float *__restrict__ part, int nslots) {
     constexpr int K = grp_steps<LPR>();
     constexpr int NPL = 16 / LPR;     // state elements per lane
     constexpr int RPW = 64 / LPR;     // rows per wave
+    constexpr int SPL = K / LPR;      // steps of a segment whose row scalars each lane forms
+    static_assert(SPL * LPR == K && LPR <= 8, "segment steps split evenly over the lane group");
     const T *u = static_cast<const T *>(a.u);
     const T *delta = static_cast<const T *>(a.delta);
     const T *Bm = static_cast<const T *>(a.B);
@@ -457,17 +481,30 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
     float h[NPL];
 #pragma unroll
     for (int i = 0; i < NPL; ++i) h[i] = (a.h0 && nok[i]) ? a.h0[r * N + NPL * g + i] : 0.0f;
+    // dl and dl*u of this lane's SPL steps of a segment (steps past L are
+    // read at L - 1 and never used)
+    auto seg_steps = [&](int64_t t0, float (&sdl)[SPL], float (&sdu)[SPL]) {
+#pragma unroll
+        for (int m = 0; m < SPL; ++m) {
+            const int64_t t = min(t0 + SPL * g + m, L - 1);
+            const float dl = softplus(Io<T>::load(delta, rb + t) + bias);
+            sdl[m] = dl;
+            sdu[m] = dl * Io<T>::load(u, rb + t);
+        }
+    };
     for (int s = 0; s < nseg; ++s) {
         if (valid) {
 #pragma unroll
             for (int i = 0; i < NPL; ++i) ckr[s * 16 + i] = h[i];
         }
+        float sdl[SPL], sdu[SPL];
+        seg_steps(static_cast<int64_t>(s) * K, sdl, sdu);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int64_t t = static_cast<int64_t>(s) * K + k;
             if (t < L) {
-                const float dl = softplus(Io<T>::load(delta, rb + t) + bias);
-                const float du = dl * Io<T>::load(u, rb + t);
+                const float dl = grp_bcast<LPR>(sdl[k % SPL], k / SPL);
+                const float du = grp_bcast<LPR>(sdu[k % SPL], k / SPL);
 #pragma unroll
                 for (int i = 0; i < NPL; ++i)
                     if (nok[i])
@@ -490,14 +527,16 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
 #pragma unroll
         for (int i = 0; i < NPL; ++i) hb[i] = ckr[s * 16 + i];
         float hs[K][NPL];
+        float sdl[SPL], sdu[SPL];
+        seg_steps(t0, sdl, sdu);
 #pragma unroll
         for (int i = 0; i < NPL; ++i) h[i] = hb[i];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int64_t t = t0 + k;
             if (t < L) {
-                const float dl = softplus(Io<T>::load(delta, rb + t) + bias);
-                const float du = dl * Io<T>::load(u, rb + t);
+                const float dl = grp_bcast<LPR>(sdl[k % SPL], k / SPL);
+                const float du = grp_bcast<LPR>(sdu[k % SPL], k / SPL);
 #pragma unroll
                 for (int i = 0; i < NPL; ++i)
                     if (nok[i])
@@ -506,26 +545,49 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
 #pragma unroll
             for (int i = 0; i < NPL; ++i) hs[k][i] = h[i];
         }
+        // this lane's SPL steps of the row's per-step scalars for the reverse:
+        // the logistic of x, u, ds = dy silu(z) and the gate-gradient factor
+        // dz / s = dy sigmoid(z) (1 + z (1 - sigmoid(z)))
+        float ssig[SPL], sut[SPL], sds[SPL], sdzf[SPL];
+#pragma unroll
+        for (int m = 0; m < SPL; ++m) {
+            const int64_t t = t0 + SPL * g + m;
+            const int64_t tc = min(t, L - 1);
+            const float x = Io<T>::load(delta, rb + tc) + bias;
+            ssig[m] = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
+            sut[m] = Io<T>::load(u, rb + tc);
+            const float dyt = (valid && t < L) ? Io<T>::load(dy, rb + tc) : 0.0f;
+            if (z) {
+                const float zt = Io<T>::load(z, rb + tc);
+                const float sz = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zt * kLog2e));
+                sds[m] = dyt * zt * sz;
+                sdzf[m] = dyt * sz * (1.0f + zt * (1.0f - sz));
+            } else {
+                sds[m] = dyt;
+                sdzf[m] = 0.0f;
+            }
+        }
+        // this lane's SPL steps of du, ddelta and dz, stored after the segment
+        float odu[SPL], odd[SPL], odz[SPL];
+#pragma unroll
+        for (int m = 0; m < SPL; ++m) odu[m] = odd[m] = odz[m] = 0.0f;
 #pragma unroll
         for (int k = K - 1; k >= 0; --k) {
             const int64_t t = t0 + k;
             if (t >= L) continue;
-            const float x = Io<T>::load(delta, rb + t) + bias;
-            const float dl = softplus(x);
-            const float sig = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
-            const float ut = Io<T>::load(u, rb + t);
-            const float dyt = valid ? Io<T>::load(dy, rb + t) : 0.0f;
-            float ds = dyt;
+            const int src = k / SPL, ms = k % SPL;
+            const float dl = grp_bcast<LPR>(sdl[ms], src);
+            const float sig = grp_bcast<LPR>(ssig[ms], src);
+            const float ut = grp_bcast<LPR>(sut[ms], src);
+            const float ds = grp_bcast<LPR>(sds[ms], src);
             if (z) {
-                const float zt = Io<T>::load(z, rb + t);
                 float sp = 0.0f;
 #pragma unroll
                 for (int i = 0; i < NPL; ++i)
                     if (nok[i]) sp = fmaf(Io<T>::load(Cb, (NPL * g + i) * L + t), hs[k][i], sp);
                 const float sv = fmaf(skip, ut, group_sum<LPR>(sp));
-                const float sz = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zt * kLog2e));
-                ds = dyt * zt * sz;
-                if (valid && g == 0 && a.dz) a.dz[rb + t] = dyt * sv * sz * (1.0f + zt * (1.0f - sz));
+                const float dzv = grp_bcast<LPR>(sdzf[ms], src) * sv;
+                if (g == src) odz[ms] = dzv;
             }
             dDacc = fmaf(ds, ut, dDacc);
             float dup = 0.0f, ddlp = 0.0f;
@@ -552,9 +614,9 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
             }
             const float dut = fmaf(ds, skip, group_sum<LPR>(dup));
             const float ddl = group_sum<LPR>(ddlp);
-            if (valid && g == 0) {
-                a.du[rb + t] = dut;
-                a.ddelta[rb + t] = ddl * sig;
+            if (g == src) {
+                odu[ms] = dut;
+                odd[ms] = ddl * sig;
             }
             dbacc = fmaf(ddl, sig, dbacc);
             if (want_bc) {
@@ -575,6 +637,18 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
                         if ((lane & 8) == 0)
                             dst[((lane >> 5) & 1 ? 16 : 0) + 2 * (lane & 7) + ((lane >> 4) & 1)] = sum;
                     }
+                }
+            }
+        }
+        // the segment's du, ddelta (and dz): SPL consecutive steps per lane
+        if (valid) {
+#pragma unroll
+            for (int m = 0; m < SPL; ++m) {
+                const int64_t t = t0 + SPL * g + m;
+                if (t < L) {
+                    a.du[rb + t] = odu[m];
+                    a.ddelta[rb + t] = odd[m];
+                    if (z && a.dz) a.dz[rb + t] = odz[m];
                 }
             }
         }
