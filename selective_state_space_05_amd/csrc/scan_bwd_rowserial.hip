@@ -429,6 +429,46 @@ __device__ __forceinline__ float grp_bcast(float v, int src) {
     }
 }
 
+// B or C of one state row over the K steps of a segment, as 32-bit words
+// (two bf16 per word, or one float).  Full segments of aligned rows come in
+// with 16-byte loads; otherwise element by element, zero past L.
+template <typename T, int K>
+struct SegRow {
+    static constexpr int W = K * static_cast<int>(sizeof(T)) / 4;
+    uint32_t w[W];
+    __device__ void load(const T *row, int64_t t0, int64_t L, bool vec) {
+        if (vec && t0 + K <= L) {
+#pragma unroll
+            for (int q = 0; q < W / 4; ++q) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(row + t0 + q * (16 / sizeof(T)));
+                w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < K; k += 4 / sizeof(T)) {
+                uint32_t v;
+                if constexpr (sizeof(T) == 4) {
+                    v = t0 + k < L ? __float_as_uint(row[t0 + k]) : 0u;
+                } else {
+                    const uint32_t lo = t0 + k < L ? row[t0 + k] : 0u;
+                    const uint32_t hi = t0 + k + 1 < L ? row[t0 + k + 1] : 0u;
+                    v = lo | (hi << 16);
+                }
+                w[k * sizeof(T) / 4] = v;
+            }
+        }
+    }
+    __device__ void zero() {
+#pragma unroll
+        for (int q = 0; q < W; ++q) w[q] = 0u;
+    }
+    // float32 value at step k of the segment
+    __device__ float at(int k) const {
+        if constexpr (sizeof(T) == 4) return __uint_as_float(w[k]);
+        else return __uint_as_float((k & 1) ? (w[k >> 1] & 0xffff0000u) : (w[k >> 1] << 16));
+    }
+};
+
 template <typename T, int LPR>
 __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__restrict__ ck, int nseg,
                                                             float *__restrict__ part, int nslots) {
@@ -476,6 +516,16 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
     const T *Cb = Cm + b * N * L;
     // stored states: 16 floats per (row, segment), this lane's NPL at NPL g
     float *ckr = ck + r * static_cast<int64_t>(nseg) * 16 + NPL * g;
+    // B and C rows 16-byte aligned at every segment start
+    const bool vbc = L % 8 == 0 &&
+                     ((reinterpret_cast<uintptr_t>(a.B) | reinterpret_cast<uintptr_t>(a.C)) & 15u) == 0;
+    auto load_rows = [&](SegRow<T, K> (&rows)[NPL], const T *base, int64_t t0) {
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+            if (nok[i]) rows[i].load(base + (NPL * g + i) * L, t0, L, vbc);
+            else rows[i].zero();
+        }
+    };
 
     // ---- forward: the state before every segment ---------------------------
     float h[NPL];
@@ -499,6 +549,8 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
         }
         float sdl[SPL], sdu[SPL];
         seg_steps(static_cast<int64_t>(s) * K, sdl, sdu);
+        SegRow<T, K> brow[NPL];
+        load_rows(brow, Bb, static_cast<int64_t>(s) * K);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int64_t t = static_cast<int64_t>(s) * K + k;
@@ -507,8 +559,7 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
                 const float du = grp_bcast<LPR>(sdu[k % SPL], k / SPL);
 #pragma unroll
                 for (int i = 0; i < NPL; ++i)
-                    if (nok[i])
-                        h[i] = fmaf(fast_exp2(dl * A2[i]), h[i], du * Io<T>::load(Bb, (NPL * g + i) * L + t));
+                    if (nok[i]) h[i] = fmaf(fast_exp2(dl * A2[i]), h[i], du * brow[i].at(k));
             }
         }
     }
@@ -529,6 +580,9 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
         float hs[K][NPL];
         float sdl[SPL], sdu[SPL];
         seg_steps(t0, sdl, sdu);
+        SegRow<T, K> brow[NPL], crow[NPL];
+        load_rows(brow, Bb, t0);
+        load_rows(crow, Cb, t0);
 #pragma unroll
         for (int i = 0; i < NPL; ++i) h[i] = hb[i];
 #pragma unroll
@@ -539,8 +593,7 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
                 const float du = grp_bcast<LPR>(sdu[k % SPL], k / SPL);
 #pragma unroll
                 for (int i = 0; i < NPL; ++i)
-                    if (nok[i])
-                        h[i] = fmaf(fast_exp2(dl * A2[i]), h[i], du * Io<T>::load(Bb, (NPL * g + i) * L + t));
+                    if (nok[i]) h[i] = fmaf(fast_exp2(dl * A2[i]), h[i], du * brow[i].at(k));
             }
 #pragma unroll
             for (int i = 0; i < NPL; ++i) hs[k][i] = h[i];
@@ -584,7 +637,7 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
                 float sp = 0.0f;
 #pragma unroll
                 for (int i = 0; i < NPL; ++i)
-                    if (nok[i]) sp = fmaf(Io<T>::load(Cb, (NPL * g + i) * L + t), hs[k][i], sp);
+                    if (nok[i]) sp = fmaf(crow[i].at(k), hs[k][i], sp);
                 const float sv = fmaf(skip, ut, group_sum<LPR>(sp));
                 const float dzv = grp_bcast<LPR>(sdzf[ms], src) * sv;
                 if (g == src) odz[ms] = dzv;
@@ -596,8 +649,8 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
             for (int i = 0; i < NPL; ++i) {
                 float cterm = 0.0f, bterm = 0.0f;
                 if (nok[i]) {
-                    const float Bt = Io<T>::load(Bb, (NPL * g + i) * L + t);
-                    const float Ct = Io<T>::load(Cb, (NPL * g + i) * L + t);
+                    const float Bt = brow[i].at(k);
+                    const float Ct = crow[i].at(k);
                     const float an = fast_exp2(dl * A2[i]);
                     const float hp = k > 0 ? hs[k > 0 ? k - 1 : 0][i] : hb[i];
                     dh[i] = fmaf(ds, Ct, dh[i]);
