@@ -470,7 +470,7 @@ struct SegRow {
 };
 
 template <typename T, int LPR>
-__global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__restrict__ ck, int nseg,
+__global__ __launch_bounds__(64, LPR == 8 ? 2 : 1) void scan_bwd_group_kernel(BwdArgs a, float *__restrict__ ck, int nseg,
                                                             float *__restrict__ part, int nslots) {
     constexpr int K = grp_steps<LPR>();
     constexpr int NPL = 16 / LPR;     // state elements per lane
@@ -527,30 +527,69 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
         }
     };
 
+    // Inputs of one segment for this lane, exactly as loaded: its SPL steps
+    // of the row's delta and u (and, for the reverse, dy, z and the stored
+    // state), and its rows of B (and C).  With eight lanes per row each pass
+    // loads segment s + 1 (or s - 1) into the second of two sets while
+    // segment s is worked on, so the loads' latency is covered by a segment
+    // of work; two sets used in turn need no copy (the kernel is held to two
+    // waves per SIMD, at the cost of a small register spill).  Steps past L
+    // are read at L - 1 and never used.
+    struct FwdIn {
+        T rd[SPL], ru[SPL];
+        SegRow<T, K> b[NPL];
+    };
+    struct RevIn {
+        float hb[NPL];
+        T rd[SPL], ru[SPL], ry[SPL], rz[SPL];
+        SegRow<T, K> b[NPL], c[NPL];
+    };
+    auto load_fwd = [&](int s, FwdIn &in) {
+        const int64_t t0 = static_cast<int64_t>(s) * K;
+#pragma unroll
+        for (int m = 0; m < SPL; ++m) {
+            const int64_t t = min(t0 + SPL * g + m, L - 1);
+            in.rd[m] = delta[rb + t];
+            in.ru[m] = u[rb + t];
+        }
+        load_rows(in.b, Bb, t0);
+    };
+    auto load_rev = [&](int s, RevIn &in) {
+        const int64_t t0 = static_cast<int64_t>(s) * K;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) in.hb[i] = ckr[s * 16 + i];
+#pragma unroll
+        for (int m = 0; m < SPL; ++m) {
+            const int64_t t = min(t0 + SPL * g + m, L - 1);
+            in.rd[m] = delta[rb + t];
+            in.ru[m] = u[rb + t];
+            in.ry[m] = dy[rb + t];
+            in.rz[m] = z ? z[rb + t] : T(0);
+        }
+        load_rows(in.b, Bb, t0);
+        load_rows(in.c, Cb, t0);
+    };
+    auto to_f = [](T v) -> float {
+        if constexpr (sizeof(T) == 4) return v;
+        else return __uint_as_float(static_cast<uint32_t>(v) << 16);
+    };
+
     // ---- forward: the state before every segment ---------------------------
     float h[NPL];
 #pragma unroll
     for (int i = 0; i < NPL; ++i) h[i] = (a.h0 && nok[i]) ? a.h0[r * N + NPL * g + i] : 0.0f;
-    // dl and dl*u of this lane's SPL steps of a segment (steps past L are
-    // read at L - 1 and never used)
-    auto seg_steps = [&](int64_t t0, float (&sdl)[SPL], float (&sdu)[SPL]) {
-#pragma unroll
-        for (int m = 0; m < SPL; ++m) {
-            const int64_t t = min(t0 + SPL * g + m, L - 1);
-            const float dl = softplus(Io<T>::load(delta, rb + t) + bias);
-            sdl[m] = dl;
-            sdu[m] = dl * Io<T>::load(u, rb + t);
-        }
-    };
-    for (int s = 0; s < nseg; ++s) {
+    auto fwd_seg = [&](int s, const FwdIn &in) {
         if (valid) {
 #pragma unroll
             for (int i = 0; i < NPL; ++i) ckr[s * 16 + i] = h[i];
         }
+        // dl and dl*u of this lane's SPL steps
         float sdl[SPL], sdu[SPL];
-        seg_steps(static_cast<int64_t>(s) * K, sdl, sdu);
-        SegRow<T, K> brow[NPL];
-        load_rows(brow, Bb, static_cast<int64_t>(s) * K);
+#pragma unroll
+        for (int m = 0; m < SPL; ++m) {
+            sdl[m] = softplus(to_f(in.rd[m]) + bias);
+            sdu[m] = sdl[m] * to_f(in.ru[m]);
+        }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int64_t t = static_cast<int64_t>(s) * K + k;
@@ -559,8 +598,28 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
                 const float du = grp_bcast<LPR>(sdu[k % SPL], k / SPL);
 #pragma unroll
                 for (int i = 0; i < NPL; ++i)
-                    if (nok[i]) h[i] = fmaf(fast_exp2(dl * A2[i]), h[i], du * brow[i].at(k));
+                    if (nok[i]) h[i] = fmaf(fast_exp2(dl * A2[i]), h[i], du * in.b[i].at(k));
             }
+        }
+    };
+    if constexpr (LPR == 8) {
+        FwdIn f0, f1;
+        load_fwd(0, f0);
+        int s = 0;
+        for (; s + 1 < nseg; s += 2) {
+            load_fwd(s + 1, f1);
+            fwd_seg(s, f0);
+            load_fwd(s + 2, f0);
+            fwd_seg(s + 1, f1);
+        }
+        if (s < nseg) fwd_seg(s, f0);
+    } else {
+        // four lanes per row hold twice the state elements per lane: one
+        // input set, loaded at each segment's start, keeps them in registers
+        for (int s = 0; s < nseg; ++s) {
+            FwdIn f0;
+            load_fwd(s, f0);
+            fwd_seg(s, f0);
         }
     }
 
@@ -572,19 +631,36 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
         dAacc[i] = 0.0f;
     }
     float dDacc = 0.0f, dbacc = 0.0f;
-    for (int s = nseg - 1; s >= 0; --s) {
+    auto rev_seg = [&](int s, const RevIn &in) {
         const int64_t t0 = static_cast<int64_t>(s) * K;
-        float hb[NPL];
+        // this lane's SPL steps of the row's per-step scalars: dl, dl*u, the
+        // logistic of x, u, ds = dy silu(z) and the gate-gradient factor
+        // dz / s = dy sigmoid(z) (1 + z (1 - sigmoid(z)))
+        float sdl[SPL], sdu[SPL], ssig[SPL], sut[SPL], sds[SPL], sdzf[SPL];
 #pragma unroll
-        for (int i = 0; i < NPL; ++i) hb[i] = ckr[s * 16 + i];
+        for (int m = 0; m < SPL; ++m) {
+            const int64_t t = t0 + SPL * g + m;
+            const float x = to_f(in.rd[m]) + bias;
+            const float ut = to_f(in.ru[m]);
+            sdl[m] = softplus(x);
+            sdu[m] = sdl[m] * ut;
+            ssig[m] = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
+            sut[m] = ut;
+            const float dyt = (valid && t < L) ? to_f(in.ry[m]) : 0.0f;
+            if (z) {
+                const float zt = to_f(in.rz[m]);
+                const float sz = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zt * kLog2e));
+                sds[m] = dyt * zt * sz;
+                sdzf[m] = dyt * sz * (1.0f + zt * (1.0f - sz));
+            } else {
+                sds[m] = dyt;
+                sdzf[m] = 0.0f;
+            }
+        }
+        // the segment's states, recomputed
         float hs[K][NPL];
-        float sdl[SPL], sdu[SPL];
-        seg_steps(t0, sdl, sdu);
-        SegRow<T, K> brow[NPL], crow[NPL];
-        load_rows(brow, Bb, t0);
-        load_rows(crow, Cb, t0);
 #pragma unroll
-        for (int i = 0; i < NPL; ++i) h[i] = hb[i];
+        for (int i = 0; i < NPL; ++i) h[i] = in.hb[i];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int64_t t = t0 + k;
@@ -593,32 +669,10 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
                 const float du = grp_bcast<LPR>(sdu[k % SPL], k / SPL);
 #pragma unroll
                 for (int i = 0; i < NPL; ++i)
-                    if (nok[i]) h[i] = fmaf(fast_exp2(dl * A2[i]), h[i], du * brow[i].at(k));
+                    if (nok[i]) h[i] = fmaf(fast_exp2(dl * A2[i]), h[i], du * in.b[i].at(k));
             }
 #pragma unroll
             for (int i = 0; i < NPL; ++i) hs[k][i] = h[i];
-        }
-        // this lane's SPL steps of the row's per-step scalars for the reverse:
-        // the logistic of x, u, ds = dy silu(z) and the gate-gradient factor
-        // dz / s = dy sigmoid(z) (1 + z (1 - sigmoid(z)))
-        float ssig[SPL], sut[SPL], sds[SPL], sdzf[SPL];
-#pragma unroll
-        for (int m = 0; m < SPL; ++m) {
-            const int64_t t = t0 + SPL * g + m;
-            const int64_t tc = min(t, L - 1);
-            const float x = Io<T>::load(delta, rb + tc) + bias;
-            ssig[m] = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * kLog2e));
-            sut[m] = Io<T>::load(u, rb + tc);
-            const float dyt = (valid && t < L) ? Io<T>::load(dy, rb + tc) : 0.0f;
-            if (z) {
-                const float zt = Io<T>::load(z, rb + tc);
-                const float sz = __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zt * kLog2e));
-                sds[m] = dyt * zt * sz;
-                sdzf[m] = dyt * sz * (1.0f + zt * (1.0f - sz));
-            } else {
-                sds[m] = dyt;
-                sdzf[m] = 0.0f;
-            }
         }
         // this lane's SPL steps of du, ddelta and dz, stored after the segment
         float odu[SPL], odd[SPL], odz[SPL];
@@ -637,7 +691,7 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
                 float sp = 0.0f;
 #pragma unroll
                 for (int i = 0; i < NPL; ++i)
-                    if (nok[i]) sp = fmaf(crow[i].at(k), hs[k][i], sp);
+                    if (nok[i]) sp = fmaf(in.c[i].at(k), hs[k][i], sp);
                 const float sv = fmaf(skip, ut, group_sum<LPR>(sp));
                 const float dzv = grp_bcast<LPR>(sdzf[ms], src) * sv;
                 if (g == src) odz[ms] = dzv;
@@ -649,10 +703,10 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
             for (int i = 0; i < NPL; ++i) {
                 float cterm = 0.0f, bterm = 0.0f;
                 if (nok[i]) {
-                    const float Bt = brow[i].at(k);
-                    const float Ct = crow[i].at(k);
+                    const float Bt = in.b[i].at(k);
+                    const float Ct = in.c[i].at(k);
                     const float an = fast_exp2(dl * A2[i]);
-                    const float hp = k > 0 ? hs[k > 0 ? k - 1 : 0][i] : hb[i];
+                    const float hp = k > 0 ? hs[k > 0 ? k - 1 : 0][i] : in.hb[i];
                     dh[i] = fmaf(ds, Ct, dh[i]);
                     cterm = ds * hs[k][i];
                     const float ha = hp * an;
@@ -704,6 +758,24 @@ __global__ __launch_bounds__(64) void scan_bwd_group_kernel(BwdArgs a, float *__
                     if (z && a.dz) a.dz[rb + t] = odz[m];
                 }
             }
+        }
+    };
+    if constexpr (LPR == 8) {
+        RevIn r0, r1;
+        load_rev(nseg - 1, r0);
+        int s = nseg - 1;
+        for (; s - 1 >= 0; s -= 2) {
+            load_rev(s - 1, r1);
+            rev_seg(s, r0);
+            if (s - 2 >= 0) load_rev(s - 2, r0);
+            rev_seg(s - 1, r1);
+        }
+        if (s >= 0) rev_seg(s, r0);
+    } else {
+        for (int s = nseg - 1; s >= 0; --s) {
+            RevIn r0;
+            load_rev(s, r0);
+            rev_seg(s, r0);
         }
     }
     if (valid) {
