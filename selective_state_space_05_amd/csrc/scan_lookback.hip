@@ -13,16 +13,19 @@
 //   1. walks its segment from h = 0 without output (the state-only walk of
 //      scan_core.h), giving h_loc, and forms P = exp(A * sum dl) in log space
 //      ("Mamba状态空间模型的硬件感知推理优化" (ybb.press) section 6.2);
-//   2. waits for the inclusive state of segment k-1 (the true state at its
-//      end), which is its incoming state h_in (the caller's initial state for
-//      the first segment), and publishes its own inclusive state
-//      P h_in + h_loc;
+//   2. publishes its pair (P, h_loc), waits for the pairs of segments
+//      0 .. k-1, and folds them in that order from the caller's initial
+//      state: h = P_j h + h_loc_j, one fused multiply-add per state element
+//      and predecessor, gives its incoming state h_in;
 //   3. walks its segment again from h_in, now forming y.
 //
 // Steps 1 and 3 -- all of the exponentials -- run in parallel over every
-// segment; only step 2, one fused multiply-add per state element, is
-// chained.  Waiting on the immediate predecessor alone (a look-back of one)
-// fixes the association order, so results are bitwise repeatable.
+// segment, and so does step 2: every segment folds its predecessors' pairs
+// itself instead of waiting for a chain of inclusive states handed from
+// segment to segment (which put one hand-over latency per segment on the
+// critical path).  The fold is the same sequence of fused multiply-adds, in
+// the same order, for every segment and every run, so results are bitwise
+// repeatable.
 //
 // Work is handed out by an atomic ticket in segment-major order, so a
 // workgroup only ever waits for a ticket taken before its own, by a
@@ -33,7 +36,10 @@
 // flag; a reader polls the flag, synchronises the workgroup, then loads.
 //
 // The result differs from the sequential loop only by the association of
-// the carried state across segment boundaries and the rounding of P.
+// the carried state across segment boundaries and the rounding of P.  Every
+// workgroup reads the initial state before it publishes its pair, so when h0
+// is the h_last buffer, the last segment (which waits for every pair before
+// its output walk) writes h_last after all the reads.
 #include <algorithm>
 
 #include "internal.h"
@@ -44,7 +50,7 @@ namespace {
 
 using core::kCh;
 
-constexpr uint32_t kFlagInclusive = 1;   // true state at the segment end published
+constexpr uint32_t kFlagPair = 1;        // the segment's pair (P, h_loc) published
 constexpr uint32_t kFlagTimedOut = 2;    // local marker: the wait gave up
 constexpr uint32_t kMaxSpins = 1u << 24;
 
@@ -63,9 +69,9 @@ __device__ __forceinline__ float load_agent(const float *p) {
                                              __HIP_MEMORY_SCOPE_AGENT));
 }
 
-// Scratch layout: per item (segment k, global group index gidx) the
-// inclusive state (`slots` floats), then one flag per item, then the ticket
-// counter.
+// Scratch layout: per item (segment k, global group index gidx) the pair:
+// P (`slots` floats) then h_loc (`slots` floats); then one flag per item, then
+// the ticket counter.
 struct Scratch {
     float *pay;
     uint32_t *flags;
@@ -109,53 +115,85 @@ __global__ __launch_bounds__(64 * W) void scan_lookback_kernel(
 #pragma unroll
     for (int g = 0; g < NPL; ++g) P[g] = fast_exp2(wk.A2[g] * sdl);
 
-    // ---- 2. carry-in from the predecessor, inclusive state out ----------------
+    // ---- 2. publish the pair, fold the predecessors' pairs ---------------------
     auto slot = [&](int g) { return (wk.prow * NPL + g) * kCh + wk.j; };
-    auto inc = [&](int seg) {
-        return s.pay + (static_cast<int64_t>(seg) * total_groups + gidx) * kSlots;
+    auto pair = [&](int seg) {
+        return s.pay + (static_cast<int64_t>(seg) * total_groups + gidx) * (2 * kSlots);
     };
-    // The first segment starts from the caller's initial state (lanes of
-    // channels past the last one mirror the last channel, whose y their
-    // owners store again, so they take its initial state).  When h0 is the
-    // h_last buffer, the write of h_last by the last segment comes after this
-    // read: it waits for the chain of inclusive states that this segment
-    // starts once it has read h0.
+    // The fold starts from the caller's initial state (lanes of channels past
+    // the last one mirror the last channel, whose y their owners store again,
+    // so they take its initial state).  It is read before the pair is
+    // published: the flag store below comes after the read has returned.
     float h_in[NPL];
     const bool row_ok = d0 + wk.j < dim;
     const int dS = min(d0 + wk.j, dim - 1);
 #pragma unroll
     for (int g = 0; g < NPL; ++g)
-        h_in[g] = (k == 0 && h0 && wk.nok[g])
+        h_in[g] = (h0 && wk.nok[g])
                       ? h0[(b * dim + dS) * static_cast<int64_t>(N) + wk.prow * NPL + g]
                       : 0.0f;
-    if (k > 0) {
-        if (tid == 0) {
-            const uint32_t *f = s.flags + static_cast<int64_t>(k - 1) * total_groups + gidx;
-            uint32_t v;
-            uint32_t spins = 0;
-            while ((v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
-                __builtin_amdgcn_s_sleep(2);
-                // Bounded wait (about a second): a predecessor that never
-                // publishes would be a bug; the state becomes NaN instead of
-                // the kernel hanging, so the failure is visible.
-                if (++spins == kMaxSpins) { v = kFlagTimedOut; break; }
-            }
-            sh_flag = v;
+    if (k < nseg - 1) {
+        float *mine = pair(k);
+#pragma unroll
+        for (int g = 0; g < NPL; ++g) {
+            store_agent(mine + slot(g), P[g]);
+            store_agent(mine + kSlots + slot(g), h[g]);
         }
-        __syncthreads();
-        const bool timed_out = sh_flag == kFlagTimedOut;
-#pragma unroll
-        for (int g = 0; g < NPL; ++g)
-            h_in[g] = timed_out ? __builtin_nanf("") : load_agent(inc(k - 1) + slot(g));
     }
-    // inclusive state of this segment: the pair (P, h_loc) applied to h_in
-#pragma unroll
-    for (int g = 0; g < NPL; ++g) store_agent(inc(k) + slot(g), fmaf(P[g], h_in[g], h[g]));
     stores_done();
     __syncthreads();
-    if (tid == 0)
-        __hip_atomic_store(s.flags + static_cast<int64_t>(k) * total_groups + gidx, kFlagInclusive,
+    if (tid == 0 && k < nseg - 1)
+        __hip_atomic_store(s.flags + static_cast<int64_t>(k) * total_groups + gidx, kFlagPair,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (k > 0) {
+        // The first wave polls the predecessors' flags, one lane per flag.
+        // Each of them publishes before it waits for anything, so every wait
+        // ends; the bound (about a second per lane) only guards against a
+        // bug: the state becomes NaN instead of the kernel hanging.
+        if (tid < 64) {
+            bool bad = false;
+            for (int j0 = 0; j0 < k; j0 += 64) {
+                const int j = j0 + tid;
+                if (j < k) {
+                    const uint32_t *f = s.flags + static_cast<int64_t>(j) * total_groups + gidx;
+                    uint32_t spins = 0;
+                    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+                        __builtin_amdgcn_s_sleep(2);
+                        if (++spins == kMaxSpins) { bad = true; break; }
+                    }
+                }
+            }
+            const bool any_bad = __any(bad);
+            if (tid == 0) sh_flag = any_bad ? kFlagTimedOut : kFlagPair;
+        }
+        __syncthreads();
+        if (sh_flag == kFlagTimedOut) {
+#pragma unroll
+            for (int g = 0; g < NPL; ++g) h_in[g] = __builtin_nanf("");
+        } else {
+            // h = P_j h + h_loc_j for j = 0 .. k-1, in that order.  The pairs
+            // are loaded a batch at a time so their latencies overlap.
+            constexpr int kBatch = NPL == 1 ? 16 : 4;
+            for (int j0 = 0; j0 < k; j0 += kBatch) {
+                float pv[kBatch][NPL], hv[kBatch][NPL];
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i) {
+                    const float *pj = pair(min(j0 + i, k - 1));   // past k-1: loaded, unused
+#pragma unroll
+                    for (int g = 0; g < NPL; ++g) {
+                        pv[i][g] = load_agent(pj + slot(g));
+                        hv[i][g] = load_agent(pj + kSlots + slot(g));
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i)
+                    if (j0 + i < k) {
+#pragma unroll
+                        for (int g = 0; g < NPL; ++g) h_in[g] = fmaf(pv[i][g], h_in[g], hv[i][g]);
+                    }
+            }
+        }
+    }
 
     // ---- 3. output walk from the true incoming state ---------------------------
 #pragma unroll
@@ -182,7 +220,7 @@ struct Plan {
 
 // Segments: about as many (segment, group) workgroups as the chip holds at
 // once (three per compute unit, 256 units), so every segment runs
-// concurrently and the chained hand-over never waits for a workgroup to be
+// concurrently and no segment waits for a predecessor that has not yet been
 // scheduled; each segment is a whole number of 32-step chunks and at least
 // 256 steps long.
 Plan make_plan(const ScanArgs &a) {
@@ -204,7 +242,7 @@ hipError_t launch_typed(const ScanArgs &a, hipStream_t stream) {
     constexpr int kSlots = 4 * W * NPL * kCh;
     const Plan p = make_plan(a);
     const int64_t items = static_cast<int64_t>(p.nseg) * p.total_groups;
-    const size_t pay_bytes = static_cast<size_t>(items) * kSlots * sizeof(float);
+    const size_t pay_bytes = static_cast<size_t>(items) * (2 * kSlots) * sizeof(float);
     const size_t flag_bytes = static_cast<size_t>(items + 1) * sizeof(uint32_t);
     void *mem = nullptr;
     hipError_t e = hipMallocAsync(&mem, pay_bytes + flag_bytes, stream);
