@@ -38,6 +38,8 @@
 // Products whose operands are not exact bf16 values (x * weight, the masked
 // decay matrix, the carried state) use a two-term bf16 split (hi + lo), so
 // each product carries about 16 significant bits; accumulation is float32.
+#include <type_traits>
+
 #include "device_math.h"
 #include "internal.h"
 
@@ -399,15 +401,25 @@ __device__ __forceinline__ void load_h(HRegs<NP> &r, const float *Hin, const Geo
     const int hh = run.h0 + item / g.npg, pbase = (item % g.npg) * kPG;
     const int pcols = g.P - pbase;
     const float *Hg = Hin + ((run.b * g.nch + run.c) * g.H + hh) * static_cast<int64_t>(g.P) * g.N;
+    // Every load is issued first, at an index clamped into the slice, and the
+    // masks are applied afterwards with selects: a load guarded by its mask
+    // is placed in a branch that waits for it, which serialises the loads.
+    float raw[HRegs<NP>::U][2];
+#pragma unroll
+    for (int k = 0; k < HRegs<NP>::U; ++k) {
+        const int u = tid + 256 * k;
+        const int p = u / (NP / 2), n2 = (u % (NP / 2)) * 2;
+        const int64_t base = static_cast<int64_t>(pbase + (p < pcols ? p : 0)) * g.N;
+        raw[k][0] = Hg[base + (n2 < g.N ? n2 : 0)];
+        raw[k][1] = Hg[base + (n2 + 1 < g.N ? n2 + 1 : 0)];
+    }
 #pragma unroll
     for (int k = 0; k < HRegs<NP>::U; ++k) {
         const int u = tid + 256 * k;
         const int p = u / (NP / 2), n2 = (u % (NP / 2)) * 2;
         const bool okp = p < pcols;
-        const int64_t base = static_cast<int64_t>(pbase + (okp ? p : 0)) * g.N;
-        const float h0 = Hg[base + (n2 < g.N ? n2 : 0)];
-        const float h1 = Hg[base + (n2 + 1 < g.N ? n2 + 1 : 0)];
-        r.v[k] = make_float2(okp && n2 < g.N ? h0 : 0.0f, okp && n2 + 1 < g.N ? h1 : 0.0f);
+        const bool m0 = okp & (n2 < g.N), m1 = okp & (n2 + 1 < g.N);
+        r.v[k] = make_float2(m0 ? raw[k][0] : 0.0f, m1 ? raw[k][1] : 0.0f);
     }
 }
 
@@ -518,16 +530,11 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
                 for (int jn = 0; jn < KN; ++jn) g = mfma(ab[jn], cf[which][jn], g);
                 return g;
             };
-            // Two-stage pipeline over the source blocks: block sb + 1's G'
-            // products are issued before block sb's decay tile is built, so
-            // the matrix cores work while the vector units do.  The last
-            // stage recomputes block tb's G' (a uniform branch-free loop;
-            // the result is unused).
-            f16x gnext = gblock(0);
-#pragma unroll 1
-            for (int sb = 0; sb <= tb; ++sb) {
-                const f16x gacc = gnext;
-                gnext = gblock(sb < tb ? sb + 1 : sb);
+            // One source block's contribution: build the masked decay tile from
+            // G' and add x^T M^T to the output tile.  DIAG (a compile-time tag)
+            // selects the diagonal block sb = tb.
+            auto mstep = [&](int sb, const f16x &gacc, auto diag_tag) {
+                constexpr bool DIAG = decltype(diag_tag)::value;
                 // x^T operands of the block: A operand row p reads x at
                 // s(8 kk + 0..3) and s(8 kk + 4..7), s(v) as below
                 bf8 xa[2][2];
@@ -547,7 +554,7 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
                 // 2^(cum_t - cb) fs[s], cb the cum at the end of block sb, both
                 // factors <= 1.
                 float mval[16];
-                if (sb < tb) {
+                if constexpr (!DIAG) {
                     const float et = fast_exp2(cum_t - sm.cum[sb * 32 + 31]);
 #pragma unroll
                     for (int v = 0; v < 16; ++v)
@@ -574,7 +581,21 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
                         yd[pt] = mfma(xa[kk][pt], bl, yd[pt]);
                     }
                 }
+            };
+            // Two-stage pipeline over the blocks below the diagonal: block
+            // sb + 1's G' products are issued in the same straight-line body as
+            // block sb's decay tile and output products, so the matrix cores
+            // work while the vector units build the tile.  The diagonal block,
+            // whose tile needs per-element exponentials and the causal mask,
+            // follows the loop.
+            f16x gnext = gblock(0);
+#pragma unroll 1
+            for (int sb = 0; sb < tb; ++sb) {
+                const f16x gacc = gnext;
+                gnext = gblock(sb + 1);
+                mstep(sb, gacc, std::false_type{});
             }
+            mstep(tb, gnext, std::true_type{});
             // Y_off^T[p][t] = sum_n h_in[p][n] C_t[n]; y = (Y_diag (with D x) +
             // 2^cum_t Y_off) * silu(z) when gated
             const float et = fast_exp2(cum_t);
