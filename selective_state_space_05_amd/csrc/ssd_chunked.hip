@@ -79,16 +79,46 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t 
 // reads are redirected to element 0 (always valid) and discarded, so the
 // load needs no branch.  VEC: rows 16-byte aligned and cols % 8 == 0.
 // Element offsets within a slice fit in 31 bits (checked by the launcher).
+//
+// Masks are applied with a bitwise AND on a mask the optimiser cannot see
+// through: a select between a freshly loaded value and zero is turned into a
+// branch around the load that waits for it, which serialises loads that
+// should all be in flight together.
+__device__ __forceinline__ uint32_t opaque_mask(bool ok) {
+    uint32_t m = ok ? ~0u : 0u;
+    asm("" : "+v"(m));
+    return m;
+}
+__device__ __forceinline__ uint4 and4(uint4 v, uint32_t m) {
+    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
+// The same without the mask applied: the load is issued at a clamped index
+// and m receives the mask for and4, so a prefetch stays in flight until the
+// value is used.
+template <bool VEC>
+__device__ __forceinline__ uint4 load_row8_raw(const uint16_t *base, int t, int c8, int rows,
+                                               int cols, int stride, uint32_t &m);
+
 template <bool VEC>
 __device__ __forceinline__ uint4 load_row8(const uint16_t *base, int t, int c8, int rows, int cols,
                                            int stride) {
+    uint32_t m;
+    const uint4 v = load_row8_raw<VEC>(base, t, c8, rows, cols, stride, m);
+    return VEC ? and4(v, m) : v;
+}
+
+template <bool VEC>
+__device__ __forceinline__ uint4 load_row8_raw(const uint16_t *base, int t, int c8, int rows,
+                                               int cols, int stride, uint32_t &m) {
     const bool okt = t < rows;
     if (VEC) {
         const bool ok = okt && c8 < cols;
         const uint32_t i = ok ? static_cast<uint32_t>(t) * static_cast<uint32_t>(stride) + c8 : 0u;
-        const uint4 v = *reinterpret_cast<const uint4 *>(base + i);
-        return ok ? v : make_uint4(0, 0, 0, 0);
+        m = opaque_mask(ok);
+        return *reinterpret_cast<const uint4 *>(base + i);
     }
+    m = ~0u;
     uint16_t e[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
@@ -169,7 +199,8 @@ template <int Q, int NT>
 struct XRegs {
     static constexpr int U = (Q / 2) * (kPG / 8) / NT;
     static_assert(U >= 1 && U * NT == (Q / 2) * (kPG / 8), "every thread holds whole units");
-    uint4 v[U][2];
+    uint4 v[U][2];       // raw loads; apply the masks m with and4 before use
+    uint32_t m[U][2];
     float dt;
 };
 
@@ -185,8 +216,8 @@ __device__ __forceinline__ void load_x(XRegs<Q, NT> &r, const uint16_t *x, const
     for (int k = 0; k < XRegs<Q, NT>::U; ++k) {
         const int u = tid + NT * k;
         const int s2 = 2 * (u / (kPG / 8)), p8 = (u % (kPG / 8)) * 8;
-        r.v[k][0] = load_row8<VEC>(xg, t0 + s2, p8, g.L, g.P - pbase, rowX);
-        r.v[k][1] = load_row8<VEC>(xg, t0 + s2 + 1, p8, g.L, g.P - pbase, rowX);
+        r.v[k][0] = load_row8_raw<VEC>(xg, t0 + s2, p8, g.L, g.P - pbase, rowX, r.m[k][0]);
+        r.v[k][1] = load_row8_raw<VEC>(xg, t0 + s2 + 1, p8, g.L, g.P - pbase, rowX, r.m[k][1]);
     }
     const int t = t0 + (tid < Q ? tid : 0);
     r.dt = bf16_to_f32(dt[run.b * g.L * static_cast<int64_t>(g.H) + (t < g.L ? t : g.L - 1) * g.H + hh]);
@@ -249,7 +280,11 @@ __global__ __launch_bounds__(state_threads<Q>()) void ssd_state_kernel(
     XRegs<Q, NT> xr;
     load_x<Q, NT, VEC>(xr, x, dt, g, run, 0);
     // B^T of the chunk, exact bf16 values re-packed as step pairs
-    for (int u = tid; u < (Q / 2) * (NP / 8); u += NT) {
+    constexpr int kTotBT = (Q / 2) * (NP / 8);
+#pragma unroll
+    for (int k = 0; k < (kTotBT + NT - 1) / NT; ++k) {
+        const int u = tid + NT * k;
+        if (kTotBT % NT != 0 && u >= kTotBT) break;
         const int s2 = 2 * (u / (NP / 8)), n8 = (u % (NP / 8)) * 8;
         const uint4 v0 = load_row8<VEC>(Bg, t0 + s2, n8, g.L, g.N, rowBC);
         const uint4 v1 = load_row8<VEC>(Bg, t0 + s2 + 1, n8, g.L, g.N, rowBC);
@@ -279,7 +314,7 @@ __global__ __launch_bounds__(state_threads<Q>()) void ssd_state_kernel(
             const int s2 = 2 * (u / (kPG / 8)), p8 = (u % (kPG / 8)) * 8;
             const float w0 = fast_exp2(cum_end - sm.cum[s2]) * sm.dl[s2];
             const float w1 = fast_exp2(cum_end - sm.cum[s2 + 1]) * sm.dl[s2 + 1];
-            const uint4 v0 = xr.v[k][0], v1 = xr.v[k][1];
+            const uint4 v0 = and4(xr.v[k][0], xr.m[k][0]), v1 = and4(xr.v[k][1], xr.m[k][1]);
             const uint32_t a[4] = {v0.x, v0.y, v0.z, v0.w}, e[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -449,7 +484,10 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
     XRegs<Q, 256> xr;
     load_x<Q, 256, VEC>(xr, x, dt, g, run, 0);
     // B of the chunk (rows s), shared by every head of the run
-    for (int u = tid; u < Q * (NP / 8); u += 256) {
+    static_assert(Q * (NP / 8) % 256 == 0, "whole units of B per thread");
+#pragma unroll
+    for (int k = 0; k < Q * (NP / 8) / 256; ++k) {
+        const int u = tid + 256 * k;
         const int s = u / (NP / 8), n8 = (u % (NP / 8)) * 8;
         *reinterpret_cast<uint4 *>(&sm.B[s * BP + n8]) = load_row8<VEC>(Bg, t0 + s, n8, g.L, g.N, rowBC);
     }
@@ -486,7 +524,7 @@ __global__ __launch_bounds__(256) void ssd_output_kernel(
         for (int k = 0; k < XRegs<Q, 256>::U; ++k) {
             const int u = tid + 256 * k;
             const int s2 = 2 * (u / (kPG / 8)), p8 = (u % (kPG / 8)) * 8;
-            const uint4 v0 = xr.v[k][0], v1 = xr.v[k][1];
+            const uint4 v0 = and4(xr.v[k][0], xr.m[k][0]), v1 = and4(xr.v[k][1], xr.m[k][1]);
             const uint32_t a[4] = {v0.x, v0.y, v0.z, v0.w}, e[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
