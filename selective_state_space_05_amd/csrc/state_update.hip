@@ -67,6 +67,15 @@ __device__ __forceinline__ void store_state4(float *p, float4 v) {
     __builtin_nontemporal_store(t, reinterpret_cast<vf4 *>(p));
 }
 
+// v where ok, else 0, through a mask the optimiser cannot see through: a
+// select between a freshly loaded value and zero is turned into a branch
+// around the load that waits for it, which serialises the loads.
+__device__ __forceinline__ float keep_if(float v, bool ok) {
+    uint32_t m = ok ? ~0u : 0u;
+    asm("" : "+v"(m));
+    return __uint_as_float(__float_as_uint(v) & m);
+}
+
 template <typename T, int GS, bool VEC>
 __global__ __launch_bounds__(256) void state_update_kernel(
     float *__restrict__ state, const T *__restrict__ x, const T *__restrict__ dt,
@@ -81,9 +90,14 @@ __global__ __launch_bounds__(256) void state_update_kernel(
     if (d >= dim) return;                                // whole groups leave together
     const int n0 = 4 * q;
     const bool live = n0 < N;
-    const float4 a = live ? load4<VEC>(A + static_cast<int64_t>(d) * N, n0, N) : make_float4(0, 0, 0, 0);
-    const float bias = dt_bias ? dt_bias[d] : 0.0f;
-    const float skip = Dskip ? Dskip[d] : 0.0f;
+    // Vector path: lanes past the last quad load quad 0 (in bounds) and their
+    // term of the sum is zeroed, so no load sits behind a branch.
+    const int nl = live ? n0 : 0;
+    const float4 a = VEC ? load4<true>(A + static_cast<int64_t>(d) * N, nl, N)
+                         : (live ? load4<false>(A + static_cast<int64_t>(d) * N, n0, N) : make_float4(0, 0, 0, 0));
+    // optional operands: read from a valid row (A has at least dim floats) and masked
+    const float bias = keep_if((dt_bias ? dt_bias : A)[d], dt_bias != nullptr);
+    const float skip = keep_if((Dskip ? Dskip : A)[d], Dskip != nullptr);
 
     // All loads first (sequences past the batch read the last one's operands
     // and store nothing), then the arithmetic.
@@ -95,8 +109,12 @@ __global__ __launch_bounds__(256) void state_update_kernel(
         const int64_t row = b * dim + d;
         xv[i] = Io<T>::load(x, row);
         dv[i] = Io<T>::load(dt, row);
-        zv[i] = z ? Io<T>::load(z, row) : 0.0f;
-        if (live) {
+        zv[i] = Io<T>::load(z ? z : x, row);   // used only when z is given
+        if (VEC) {
+            h[i] = load_state4(state + row * N + nl);
+            bq[i] = load4<true>(B + b * N, nl, N);
+            cq[i] = load4<true>(C + b * N, nl, N);
+        } else if (live) {
             h[i] = VEC ? load_state4(state + row * N + n0) : load4<VEC>(state + row * N, n0, N);
             bq[i] = load4<VEC>(B + b * N, n0, N);
             cq[i] = load4<VEC>(C + b * N, n0, N);
@@ -117,6 +135,7 @@ __global__ __launch_bounds__(256) void state_update_kernel(
         hn.z = fmaf(fast_exp2(s * a.z), h[i].z, dx * bq[i].z);
         hn.w = fmaf(fast_exp2(s * a.w), h[i].w, dx * bq[i].w);
         float acc = fmaf(cq[i].x, hn.x, fmaf(cq[i].y, hn.y, fmaf(cq[i].z, hn.z, cq[i].w * hn.w)));
+        if (VEC) acc = live ? acc : 0.0f;
         // sum over the group's lanes (aligned runs of GS lanes of one wave)
 #pragma unroll
         for (int m = GS / 2; m >= 1; m /= 2) acc += __shfl_xor(acc, m, GS);
