@@ -12,7 +12,8 @@
 //
 //   1. walks its segment from h = 0 without output (the state-only walk of
 //      scan_core.h), giving h_loc, and forms P = exp(A * sum dl) in log space
-//      ("Mamba状态空间模型的硬件感知推理优化" (ybb.press) section 6.2);
+//      ("Mamba状态空间模型的硬件感知推理优化" (ybb.press) section 6.2); the
+//      last segment, whose pair nobody reads, skips this walk;
 //   2. publishes its pair (P, h_loc), waits for the pairs of segments
 //      0 .. k-1, and folds them in that order from the caller's initial
 //      state: h = P_j h + h_loc_j, one fused multiply-add per state element
@@ -106,14 +107,16 @@ __global__ __launch_bounds__(64 * W) void scan_lookback_kernel(
     const int t_end = static_cast<int>(min(L, static_cast<int64_t>(t_begin) + seg_len));
 
     // ---- 1. local pair of the segment ---------------------------------------
-    float h[NPL];
+    // (the last segment's pair is never used: it skips this walk)
+    float h[NPL], P[NPL];
 #pragma unroll
-    for (int g = 0; g < NPL; ++g) h[g] = 0.0f;
-    wk.template walk<false>(t_begin, t_end, h, sm);
-    const float sdl = wk.channel_dl_sum(sm);
-    float P[NPL];
+    for (int g = 0; g < NPL; ++g) h[g] = 0.0f, P[g] = 0.0f;
+    if (k < nseg - 1) {
+        wk.template walk<false>(t_begin, t_end, h, sm);
+        const float sdl = wk.channel_dl_sum(sm);
 #pragma unroll
-    for (int g = 0; g < NPL; ++g) P[g] = fast_exp2(wk.A2[g] * sdl);
+        for (int g = 0; g < NPL; ++g) P[g] = fast_exp2(wk.A2[g] * sdl);
+    }
 
     // ---- 2. publish the pair, fold the predecessors' pairs ---------------------
     auto slot = [&](int g) { return (wk.prow * NPL + g) * kCh + wk.j; };
