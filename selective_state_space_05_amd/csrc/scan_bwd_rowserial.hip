@@ -276,26 +276,37 @@ __global__ __launch_bounds__(64) void scan_bwd_rowserial_kernel(BwdArgs a, float
 __global__ __launch_bounds__(256) void scan_bwd_bc_kernel(const float *__restrict__ part, int nslots,
                                                           int ng, int rpw, int64_t batch, int64_t dim,
                                                           int64_t L, int N, float *dB, float *dC) {
+    // one thread per four consecutive partial columns of one (batch, step):
+    // 16-byte loads, so a wave reads 1 KB of each wave's partial plane
     const int64_t cols = static_cast<int64_t>(ng) * 32;
+    const int64_t quads = cols / 4;
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (i >= batch * L * cols) return;
-    const int col = static_cast<int>(i % cols);
-    const int64_t t = (i / cols) % L;
-    const int64_t b = i / (cols * L);
+    if (i >= batch * L * quads) return;
+    const int col = static_cast<int>(i % quads) * 4;
+    const int64_t t = (i / quads) % L;
+    const int64_t b = i / (quads * L);
     const int gi = col / 32, kk = col % 32;
-    const int n = 16 * gi + kk % 16;
+    const int n = 16 * gi + kk % 16;            // state elements n .. n + 3
     if (n >= N) return;
     const int64_t w_lo = (b * dim) / rpw, w_hi = ((b + 1) * dim - 1) / rpw;
-    float s = 0.0f;
+    float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     // unrolled so that several waves' partials are in flight at once (the
     // adds stay in wave order)
 #pragma unroll 8
     for (int64_t w = w_lo; w <= w_hi; ++w) {
         const int64_t slot = b - (w * rpw) / dim;
-        s += part[((w * nslots + slot) * L + t) * cols + col];
+        const float4 v = *reinterpret_cast<const float4 *>(&part[((w * nslots + slot) * L + t) * cols + col]);
+        s[0] += v.x;
+        s[1] += v.y;
+        s[2] += v.z;
+        s[3] += v.w;
     }
     float *out = kk < 16 ? dC : dB;
-    if (out) out[(b * N + n) * L + t] = s;
+    if (out) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (n + k < N) out[(b * N + n + k) * L + t] = s[k];
+    }
 }
 
 template <typename T, int NS>
@@ -321,7 +332,7 @@ hipError_t launch_typed(const BwdArgs &a, hipStream_t stream) {
                        stream, a, ck, nseg, part, nslots);
     e = hipGetLastError();
     if (e == hipSuccess && want_bc) {
-        const int64_t n = a.batch * a.L * NG * 32;
+        const int64_t n = a.batch * a.L * NG * 32 / 4;   // column quads
         hipLaunchKernelGGL(scan_bwd_bc_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0,
                            stream, part, nslots, NG, 64, a.batch, a.dim, a.L, static_cast<int>(a.N), a.dB,
                            a.dC);
@@ -814,7 +825,7 @@ hipError_t launch_group(const BwdArgs &a, hipStream_t stream) {
                        a, ck, nseg, part, nslots);
     e = hipGetLastError();
     if (e == hipSuccess && want_bc) {
-        const int64_t n = a.batch * a.L * 32;
+        const int64_t n = a.batch * a.L * 32 / 4;   // column quads
         hipLaunchKernelGGL(scan_bwd_bc_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0,
                            stream, part, nslots, 1, RPW, a.batch, a.dim, a.L, static_cast<int>(a.N), a.dB,
                            a.dC);
