@@ -193,7 +193,7 @@ MSSM_API mssm_status mssm_selective_scan_fwd_conv(const void *x, const float *co
  * N <= 16) and, when dB or dC is requested,
  * per-wave partial sums of about batch * dim / 8 * L * 128 bytes for
  * 8 < N <= 16 (half that for N <= 8; 4.3 GB for L = 2^20 with 256
- * channels); an allocation failure returns MSSM_ERR_HIP.  Errors as for
+ * channels); an allocation failure returns MSSM_ERR_ALLOC.  Errors as for
  * the forward, plus MSSM_ERR_INVALID_ARG for dz without z or any output
  * overlapping an input or another output.
  */
@@ -351,6 +351,34 @@ MSSM_API const char *mssm_last_error(void);
 
 /* Library version as major*10000 + minor*100 + patch. */
 MSSM_API int mssm_version(void);
+
+/* Identity of the sources this binary was built from: 16 hex digits of a
+ * SHA-256 over the kernel and host sources, this header and the compile
+ * flags.  A binding compares it with the hash of the sources it ships with
+ * and refuses a binary built from others.  Never NULL. */
+MSSM_API const char *mssm_source_hash(void);
+
+/* Status bits that kernels set on a device while they run. */
+#define MSSM_DEVICE_LOOKBACK_TIMEOUT 0x1u /* a look-back wait gave up */
+
+/*
+ * Device status of the CURRENT device.  Waits for all work queued on the
+ * device (hipDeviceSynchronize), then writes into *bits the status bits set
+ * by this library's kernels since they were last cleared, and clears them
+ * when `clear` is nonzero.  The bits are the device's, shared by every
+ * stream and thread.
+ *
+ * MSSM_DEVICE_LOOKBACK_TIMEOUT: a workgroup of the look-back variant
+ * (MSSM_VARIANT_LOOKBACK) waited about a second per predecessor for a
+ * predecessor's published carry and gave up.  Predecessors always publish
+ * before they wait, so this marks a defect, not a slow device; that call's
+ * outputs from the affected segment on (y and h_last) are NaN rather than
+ * wrong numbers, and the call itself returned MSSM_OK when it was queued.
+ *
+ * Errors: MSSM_ERR_INVALID_ARG if bits is NULL; MSSM_ERR_HIP if the
+ * synchronisation or a copy fails (including a fault of earlier work).
+ */
+MSSM_API mssm_status mssm_device_status(uint32_t *bits, int clear);
 
 #ifdef __cplusplus
 }

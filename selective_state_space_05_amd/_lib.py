@@ -30,6 +30,7 @@ VARIANT_SSD_RECURRENT = 4
 VARIANT_SSD_CHUNKED = 5
 
 MAX_DSTATE = 64
+DEVICE_LOOKBACK_TIMEOUT = 0x1   # mssm_device_status bit
 CONV_WIDTH = 4
 SSD_MAX_DSTATE = 256
 SSD_MAX_HEADDIM = 256
@@ -49,6 +50,8 @@ EXPORTED = (
     "mssm_status_string",
     "mssm_last_error",
     "mssm_version",
+    "mssm_source_hash",
+    "mssm_device_status",
 )
 
 
@@ -115,7 +118,29 @@ def _declare(L):
     L.mssm_last_error.restype = ctypes.c_char_p
     L.mssm_version.argtypes = []
     L.mssm_version.restype = ctypes.c_int
+    L.mssm_source_hash.argtypes = []
+    L.mssm_source_hash.restype = ctypes.c_char_p
+    L.mssm_device_status.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]
+    L.mssm_device_status.restype = ctypes.c_int
     return L
+
+
+class StaleLibraryError(OSError):
+    """The library was built from sources other than those beside it."""
+
+
+def check_source_hash(L):
+    """Refuse a library built from other sources than the ones in this
+    package (a stale binary would silently run old kernels)."""
+    from . import build
+    if not os.path.isdir(build.CSRC):
+        return
+    want = build.source_hash()
+    got = L.mssm_source_hash().decode()
+    if got != want:
+        raise StaleLibraryError(
+            "libmssm.so was built from other sources (library %s, sources %s): rebuild it "
+            "(python -c 'import __graft_entry__ as g; g.build()')" % (got, want))
 
 
 def load(path: str = LIB_PATH):
@@ -124,7 +149,9 @@ def load(path: str = LIB_PATH):
         raise OSError(
             "libmssm.so not found at %s: build it first "
             "(python -c 'import __graft_entry__ as g; g.build()')" % path)
-    return _declare(ctypes.CDLL(path))
+    L = _declare(ctypes.CDLL(path))
+    check_source_hash(L)
+    return L
 
 
 def lib():

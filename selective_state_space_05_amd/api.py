@@ -57,6 +57,14 @@ def _need(t, name, dtype=None, device=None):
         raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
 
 
+def _need_shape(t, name, shape):
+    """Caller-supplied output buffers must have exactly the output's shape:
+    the C ABI sees only their addresses, so a smaller buffer would be written
+    past its end on the device."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
 def _stream_handle(device):
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -78,6 +86,15 @@ def forced_variant(variant: int):
 
 def last_variant() -> int:
     return int(_lib.lib().mssm_last_variant())
+
+
+def device_status(clear: bool = False) -> int:
+    """Status bits the library's kernels set on the current device
+    (``_lib.DEVICE_LOOKBACK_TIMEOUT``); waits for the device first."""
+    import ctypes
+    bits = ctypes.c_uint32(0)
+    _check(_lib.lib().mssm_device_status(ctypes.byref(bits), 1 if clear else 0))
+    return int(bits.value)
 
 
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
@@ -113,6 +130,8 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     for name, t in (("D", D), ("delta_bias", delta_bias)):
         if t is not None and tuple(t.shape) != (dim,):
             raise ValueError("%s must be (dim,)" % name)
+    _need_shape(out, "out", u.shape)
+    _need_shape(h_out, "h_out", (batch, dim, N))
     y = out if out is not None else torch.empty_like(u)
     _need(y, "out", io, dev)
     h_last = None
@@ -175,6 +194,8 @@ def selective_scan_conv_fwd(x, conv_w, delta, A, B, C, D=None, z=None, delta_bia
     for name, t in (("D", D), ("delta_bias", delta_bias)):
         if t is not None and tuple(t.shape) != (dim,):
             raise ValueError("%s must be (dim,)" % name)
+    _need_shape(out, "out", x.shape)
+    _need_shape(h_out, "h_out", (batch, dim, N))
     y = out if out is not None else torch.empty_like(x)
     _need(y, "out", io, dev)
     h_last = None
@@ -274,6 +295,8 @@ def ssd_scalar_fwd(x, dt, A, B, C, D=None, dt_bias=None, chunk=0,
     for name, t in (("A", A), ("D", D), ("dt_bias", dt_bias)):
         if t is not None and tuple(t.shape) != (H,):
             raise ValueError("%s must be (H,)" % name)
+    _need_shape(out, "out", x.shape)
+    _need_shape(h_out, "h_out", (batch, H, P, N))
     y = out if out is not None else torch.empty_like(x)
     _need(y, "out", io, dev)
     h_last = None
@@ -334,6 +357,7 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
     for name, t in (("D", D), ("dt_bias", dt_bias)):
         if t is not None and tuple(t.shape) != (dim,):
             raise ValueError("%s must be (dim,)" % name)
+    _need_shape(out, "out", x.shape)
     y = out if out is not None else torch.empty_like(x)
     _need(y, "out", io, dev)
     dims = _lib.StepDims(batch, dim, N)

@@ -9,6 +9,7 @@ one shared library exporting the C ABI of include/mssm.h.
 from __future__ import annotations
 
 import concurrent.futures
+import hashlib
 import os
 import shutil
 import subprocess
@@ -33,6 +34,25 @@ COMMON = [
 ]
 
 
+def source_hash() -> str:
+    """16 hex digits of a SHA-256 over every file under csrc/ and include/
+    (names and contents, in sorted order) and the compile flags.  build()
+    compiles it into the library (mssm_source_hash()), and the binding
+    refuses a library whose hash differs from that of the sources beside
+    it."""
+    h = hashlib.sha256()
+    for d in (CSRC, INCLUDE):
+        for name in sorted(os.listdir(d)):
+            path = os.path.join(d, name)
+            if os.path.isfile(path):
+                h.update(name.encode() + b"\0")
+                with open(path, "rb") as f:
+                    h.update(f.read())
+                h.update(b"\0")
+    h.update(" ".join(COMMON).encode())
+    return h.hexdigest()[:16]
+
+
 def sources():
     out = []
     for name in sorted(os.listdir(CSRC)):
@@ -41,9 +61,9 @@ def sources():
     return out
 
 
-def _compile(src, verbose):
+def _compile(src, verbose, extra=()):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, "-x", "hip", "-c", src, "-o", obj] + COMMON
+    cmd = [HIPCC, "-x", "hip", "-c", src, "-o", obj] + COMMON + list(extra)
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -61,8 +81,14 @@ def build(verbose: bool = False) -> str:
     """Compile every source and link libmssm.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
+    tag = ['-DMSSM_SOURCE_HASH="%s"' % source_hash()]
+
+    def one(src):
+        # the hash goes into the host front end only
+        return _compile(src, verbose, tag if src.endswith("mssm_api.cpp") else ())
+
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        objs = list(ex.map(one, srcs))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:

@@ -121,6 +121,10 @@ bool scan_rows_vectorizable(const ScanArgs &a);
 hipError_t launch_scan_lookback(const ScanArgs &a, hipStream_t stream);
 bool scan_lookback_supported(const ScanArgs &a);
 
+// Status bits of the current device (mssm_device_status): waits for the
+// device, reads them into *bits and clears them when asked.
+hipError_t device_status(uint32_t *bits, bool clear);
+
 // Backward: one lane per (batch, channel) row; stream-ordered scratch for the
 // stored states.
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t stream);

@@ -519,4 +519,17 @@ const char *mssm_last_error(void) { return g_last_error.c_str(); }
 
 int mssm_version(void) { return 100; }
 
+mssm_status mssm_device_status(uint32_t *bits, int clear) {
+    g_last_error.clear();
+    if (!bits) return fail(MSSM_ERR_INVALID_ARG, "bits is null");
+    const hipError_t e = mssm::device_status(bits, clear != 0);
+    if (e != hipSuccess) return hip_fail(e, "device status read");
+    return MSSM_OK;
+}
+
+#ifndef MSSM_SOURCE_HASH
+#define MSSM_SOURCE_HASH "unknown"
+#endif
+const char *mssm_source_hash(void) { return MSSM_SOURCE_HASH; }
+
 }  // extern "C"

@@ -44,9 +44,16 @@
 #include <algorithm>
 
 #include "internal.h"
+#include "mssm.h"
 #include "scan_core.h"
 
 namespace mssm {
+
+// Status bits of this device (mssm_device_status): kernels set them with an
+// atomic OR, the host reads and clears them.  Each device's copy of the code
+// object holds its own word.
+__device__ uint32_t g_device_status_bits;
+
 namespace {
 
 using core::kCh;
@@ -152,7 +159,8 @@ __global__ __launch_bounds__(64 * W) void scan_lookback_kernel(
         // The first wave polls the predecessors' flags, one lane per flag.
         // Each of them publishes before it waits for anything, so every wait
         // ends; the bound (about a second per lane) only guards against a
-        // bug: the state becomes NaN instead of the kernel hanging.
+        // bug: the state becomes NaN instead of the kernel hanging, and the
+        // device's MSSM_DEVICE_LOOKBACK_TIMEOUT status bit is set.
         if (tid < 64) {
             bool bad = false;
             for (int j0 = 0; j0 < k; j0 += 64) {
@@ -167,7 +175,12 @@ __global__ __launch_bounds__(64 * W) void scan_lookback_kernel(
                 }
             }
             const bool any_bad = __any(bad);
-            if (tid == 0) sh_flag = any_bad ? kFlagTimedOut : kFlagPair;
+            if (tid == 0) {
+                sh_flag = any_bad ? kFlagTimedOut : kFlagPair;
+                if (any_bad)
+                    __hip_atomic_fetch_or(&g_device_status_bits, MSSM_DEVICE_LOOKBACK_TIMEOUT,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
         __syncthreads();
         if (sh_flag == kFlagTimedOut) {
@@ -296,6 +309,18 @@ bool scan_lookback_supported(const ScanArgs &a) {
     if (groups >= (int64_t(1) << 20)) return false;
     const Plan p = make_plan(a);
     return static_cast<int64_t>(p.nseg) * p.total_groups < (int64_t(1) << 31);
+}
+
+hipError_t device_status(uint32_t *bits, bool clear) {
+    void *p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_device_status_bits));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemcpy(bits, p, sizeof(uint32_t), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && clear) {
+        const uint32_t zero = 0;
+        e = hipMemcpy(p, &zero, sizeof(uint32_t), hipMemcpyHostToDevice);
+    }
+    return e;
 }
 
 hipError_t launch_scan_lookback(const ScanArgs &a, hipStream_t stream) {

@@ -119,6 +119,24 @@ def _sampled(p, variant, dev, nrows=12, seed=0):
     assert np.all(np.isfinite(y)) and np.all(np.isfinite(h))
 
 
+@pytest.mark.parametrize("variant", [_lib.VARIANT_AUTO] + SCAN_VARIANTS)
+def test_scan_tiny_workload_as_stated(dev, variant):
+    """The tiny workload exactly as stated: batch 1, L 64, 8 channels, N 4,
+    float32, seed 0, bias 0.5, skip term, no gate, h0 = 0; every element of
+    y and h_last against the oracle (which the CPU tests pin to the
+    brute-force closed form on these very inputs)."""
+    p = inputs.TINY
+    assert (p.seed, p.gate, p.skip, p.bias, p.io) == (0, False, True, "scalar", "f32")
+    announce("scan variant=%d workload=%s" % (variant, p.name))
+    x = inputs.scan_inputs(p)
+    assert x["z"] is None
+    y, h = run_scan(scan_to_dev(x, p.io, dev), variant)
+    yo, ho = oracle.selective_scan(x["u"], x["delta"], x["A"], x["B"], x["C"],
+                                   x["D"], x["z"], x["delta_bias"])
+    gates.check(y, yo, p.io, "y")
+    gates.check_state(h, ho, p.io, "h_last")
+
+
 FULL = [inputs.MAMBA_130M, inputs.MAMBA_2_8B, inputs.MILLION]
 
 
@@ -229,12 +247,16 @@ def run_ssd(t, variant=_lib.VARIANT_AUTO, chunk=0):
 
 
 def ssd_rows_of(y):
-    """(batch, L, H, P) -> rows (batch, H) of length L*P.
+    """(batch, L, H, P) -> the rows of the normwise gate.
 
-    A head's whole output block is one row for the normwise gate, so that a
-    row never degenerates to a single bf16-rounded element (L = 1)."""
+    A row is one (b, h, p) sequence of L outputs.  With L = 1 such a row is
+    a single bf16-rounded element, whose rounding alone can exceed the
+    tolerance, so there a head's whole block (batch, H) of P outputs is one
+    row."""
     b, L, H, P = y.shape
-    return np.ascontiguousarray(np.moveaxis(y, 2, 1)).reshape(b, H, L * P)
+    if L == 1:
+        return np.ascontiguousarray(np.moveaxis(y, 2, 1)).reshape(b, H, L * P)
+    return np.ascontiguousarray(np.transpose(y, (0, 2, 3, 1)))   # (b, H, P, L)
 
 
 SSD_SMALL = [
@@ -335,3 +357,52 @@ def test_ssd_zero_length_zero_fills_state(dev):
     y, h = mssm.ssd_scalar_fwd(x, dt, A, B, B.clone(), h_out=h_out)
     torch.cuda.synchronize()
     assert torch.all(h == 0)
+
+
+def test_wrong_shaped_outputs_rejected(dev):
+    """Caller-supplied out / h_out buffers of the wrong shape are refused by
+    the binding before anything is queued (the C ABI sees only addresses)."""
+    import selective_state_space_05_amd as mssm
+    announce("wrong-shaped outputs")
+    p = scan_problem(2, 64, 8, 4, "f32", 11)
+    t = scan_to_dev(inputs.scan_inputs(p), "f32", dev)
+    small_y = torch.full((2, 8, 32), 5.0, device=dev)
+    small_h = torch.full((2, 8, 3), 5.0, device=dev)
+    args = (t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"])
+    with pytest.raises(ValueError):
+        mssm.selective_scan_fwd(*args, out=small_y)
+    with pytest.raises(ValueError):
+        mssm.selective_scan_fwd(*args, h_out=small_h)
+    conv_w = torch.zeros((8, 4), device=dev)
+    with pytest.raises(ValueError):
+        mssm.selective_scan_conv_fwd(t["u"], conv_w, t["delta"], t["A"], t["B"], t["C"],
+                                     out=small_y)
+    with pytest.raises(ValueError):
+        mssm.selective_scan_conv_fwd(t["u"], conv_w, t["delta"], t["A"], t["B"], t["C"],
+                                     h_out=small_h)
+    sp = inputs.SSDProblem("case", 1, 40, 2, 8, 16, 1, "f32", 12)
+    s = ssd_to_dev(inputs.ssd_inputs(sp), "f32", dev)
+    sargs = (s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["dt_bias"])
+    with pytest.raises(ValueError):
+        mssm.ssd_scalar_fwd(*sargs, out=torch.empty((1, 40, 2, 4), device=dev))
+    with pytest.raises(ValueError):
+        mssm.ssd_scalar_fwd(*sargs, h_out=torch.empty((1, 2, 8, 8), device=dev))
+    state = torch.zeros((2, 8, 4), device=dev)
+    with pytest.raises(ValueError):
+        mssm.selective_state_update(state, t["u"][..., 0].contiguous(),
+                                    t["delta"][..., 0].contiguous(), t["A"],
+                                    t["B"][..., 0].contiguous(), t["C"][..., 0].contiguous(),
+                                    out=torch.empty((2, 4), device=dev))
+    torch.cuda.synchronize()
+    assert torch.all(small_y == 5.0) and torch.all(small_h == 5.0)
+    assert torch.all(state == 0.0)
+
+
+def test_device_status_clear_after_lookback(dev):
+    """A look-back run that completes leaves the device's timeout bit clear."""
+    from selective_state_space_05_amd.api import device_status
+    announce("device status after a look-back run")
+    device_status(clear=True)
+    p = scan_problem(1, 8192, 32, 16, "bf16", 8)
+    run_scan(scan_to_dev(inputs.scan_inputs(p), "bf16", dev), _lib.VARIANT_LOOKBACK)
+    assert device_status() & _lib.DEVICE_LOOKBACK_TIMEOUT == 0

@@ -98,3 +98,39 @@ def test_scan_backward_zero_length(dev):
     torch.cuda.synchronize()
     assert torch.equal(g["dh0"], dhl)
     assert torch.all(g["dA"] == 0) and torch.all(g["dD"] == 0) and torch.all(g["ddelta_bias"] == 0)
+
+
+def test_scan_backward_full_size():
+    """The Mamba-2.8B layer's backward at full size, in the configuration the
+    benchmark times (dy and dh_last drawn by inputs.output_grads, no h0).
+    The oracle's backward runs over the whole layer; dA, dD and the bias
+    gradient are compared in full, dB and dC over every (batch, n) row, and
+    du, ddelta and dz over every (batch, channel) row."""
+    import selective_state_space_05_amd as mssm
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dev = torch.device("cuda:0")
+    p = inputs.BWD_PROBLEMS["mamba2.8b_layer_bwd_bf16"]
+    announce("scan backward workload=%s" % p.name)
+    x = inputs.scan_inputs(p)
+    gr = inputs.output_grads(p)
+    t = scan_to_dev({k: v for k, v in x.items() if k not in ("conv_w", "conv_b")}, p.io, dev)
+    g = mssm.selective_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"],
+                                to_dev(gr["dy"], p.io, dev), D=t["D"], z=t["z"],
+                                delta_bias=t["delta_bias"],
+                                dh_last=torch.from_numpy(gr["dh_last"]).to(dev))
+    torch.cuda.synchronize()
+    got = {k: f64(v) for k, v in g.items()}
+    del g, t
+    print("[gpu case] oracle backward over the whole layer", flush=True)
+    o = oracle.selective_scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], gr["dy"], D=x["D"],
+                                  z=x["z"], delta_bias=x["delta_bias"], dh_last=gr["dh_last"])
+    f = "f32"
+    gates.check_state(got["dA"], o["dA"], f, "dA")
+    gates.check_state(got["dD"][None], o["dD"][None], f, "dD")
+    gates.check_state(got["ddelta_bias"][None], o["ddelta_bias"][None], f, "ddelta_bias")
+    gates.check_state(got["dB"], o["dB"], f, "dB")
+    gates.check_state(got["dC"], o["dC"], f, "dC")
+    gates.check(got["du"], o["du"], f, "du")
+    gates.check(got["ddelta"], o["ddelta"], f, "ddelta")
+    gates.check(got["dz"], o["dz"], f, "dz")
