@@ -49,7 +49,10 @@ def source_hash() -> str:
                 with open(path, "rb") as f:
                     h.update(f.read())
                 h.update(b"\0")
-    h.update(" ".join(COMMON).encode())
+    # the include paths are absolute: hash them relative to the repository,
+    # so a copy of the tree elsewhere hashes the same
+    flags = [f.replace(ROOT, "<root>") for f in COMMON]
+    h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 
