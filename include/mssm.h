@@ -275,6 +275,37 @@ MSSM_API mssm_status mssm_ssd_scalar_fwd_h0(const void *x, const void *dt,
                                    void *stream);
 
 /*
+ * mssm_selective_scan_fwd_h0 for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  It calls no hipMalloc, hipMallocAsync, hipFree or other
+ * allocating routine.  The look-back variant's scratch (its published
+ * carries, flags and work ticket) lives in a fixed device array of
+ * MSSM_NOALLOC_SCRATCH_BYTES on each device the library runs on, held until
+ * the process ends; the other variants need no scratch.  The flags and the
+ * ticket are cleared by a kernel at the start of each call.
+ *
+ * Arguments, layouts, variants and results are those of
+ * mssm_selective_scan_fwd_h0 (bitwise the same outputs).  The caller still
+ * provides every input and output.
+ * Limit: a problem whose look-back scratch exceeds the array returns
+ * MSSM_ERR_UNSUPPORTED before anything is queued (the look-back variant
+ * needs about 2 KB per (segment, 16-channel group) for N <= 16 and up to
+ * 8 KB for larger N, with about 768 of them when AUTO chooses it: 1.5 MB for
+ * a million-step sequence of 256 channels).
+ * Every call on a device shares that device's array, so calls that overlap
+ * on one device (on different streams or threads) race and must be
+ * serialised by the caller.
+ */
+#define MSSM_NOALLOC_SCRATCH_BYTES (8u << 20)
+MSSM_API mssm_status mssm_selective_scan_fwd_h0_noalloc(const void *u, const void *delta,
+                                               const float *delta_bias, const float *A,
+                                               const void *B, const void *C,
+                                               const float *D, const void *z,
+                                               const float *h0, void *y, float *h_last,
+                                               mssm_scan_dims dims, mssm_dtypes dtypes,
+                                               void *stream);
+
+/*
  * The SSD forward with a SiLU gate on its output ([csdn] section 3: a SiLU
  * branch gates the SSM output; the same reading as the selective scan's z):
  *

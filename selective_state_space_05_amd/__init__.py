@@ -13,10 +13,12 @@ from .api import (  # noqa: F401
     selective_scan_bwd,
     selective_scan_conv_fwd,
     selective_scan_fwd,
+    selective_scan_fwd_noalloc,
     selective_state_update,
     ssd_scalar_fwd,
     version,
 )
 
-__all__ = ["MssmError", "selective_scan_bwd", "selective_scan_conv_fwd", "selective_scan_fwd", "selective_state_update",
+__all__ = ["MssmError", "selective_scan_bwd", "selective_scan_conv_fwd", "selective_scan_fwd",
+           "selective_scan_fwd_noalloc", "selective_state_update",
            "ssd_scalar_fwd", "version"]

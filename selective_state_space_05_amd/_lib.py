@@ -31,6 +31,7 @@ VARIANT_SSD_CHUNKED = 5
 
 MAX_DSTATE = 64
 DEVICE_LOOKBACK_TIMEOUT = 0x1   # mssm_device_status bit
+NOALLOC_SCRATCH_BYTES = 8 << 20  # scratch array of the no-alloc entry point
 CONV_WIDTH = 4
 SSD_MAX_DSTATE = 256
 SSD_MAX_HEADDIM = 256
@@ -52,6 +53,7 @@ EXPORTED = (
     "mssm_version",
     "mssm_source_hash",
     "mssm_device_status",
+    "mssm_selective_scan_fwd_h0_noalloc",
 )
 
 
@@ -92,6 +94,9 @@ def _declare(L):
     L.mssm_selective_scan_fwd_h0.argtypes = [vp, vp, fp, fp, vp, vp, fp, vp, fp,
                                              vp, fp, ScanDims, DTypes, vp]
     L.mssm_selective_scan_fwd_h0.restype = ctypes.c_int
+    L.mssm_selective_scan_fwd_h0_noalloc.argtypes = [vp, vp, fp, fp, vp, vp, fp, vp, fp,
+                                                     vp, fp, ScanDims, DTypes, vp]
+    L.mssm_selective_scan_fwd_h0_noalloc.restype = ctypes.c_int
     L.mssm_selective_scan_fwd_conv.argtypes = [vp, fp, fp, vp, fp, fp, vp, vp, fp, vp, fp,
                                                vp, fp, ScanDims, DTypes, vp]
     L.mssm_selective_scan_fwd_conv.restype = ctypes.c_int

@@ -156,6 +156,50 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
     return y, h_last
 
 
+def selective_scan_fwd_noalloc(u, delta, A, B, C, D=None, z=None, delta_bias=None, h0=None,
+                               *, out, h_out):
+    """``selective_scan_fwd`` through the entry point that allocates nothing
+    on the device (mssm_selective_scan_fwd_h0_noalloc): the caller passes
+    the outputs ``out`` (like u) and ``h_out`` ((batch, dim, N) float32,
+    or None), and scratch comes from the library's fixed per-device array.
+    Calls that overlap on one device race on that array."""
+    L = _lib.lib()
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU device")
+    io = u.dtype
+    for name, t in (("u", u), ("delta", delta), ("B", B), ("C", C), ("z", z)):
+        _need(t, name, io, dev)
+    for name, t in (("A", A), ("D", D), ("delta_bias", delta_bias), ("h0", h0)):
+        _need(t, name, torch.float32, dev)
+    if out is None:
+        raise ValueError("out is required")
+    batch, dim, seqlen = u.shape
+    N = A.shape[1]
+    if delta.shape != u.shape or (z is not None and z.shape != u.shape):
+        raise ValueError("u, delta, z must share one (batch, dim, L) shape")
+    if tuple(A.shape) != (dim, N):
+        raise ValueError("A must be (dim, N)")
+    if tuple(B.shape) != (batch, N, seqlen) or tuple(C.shape) != (batch, N, seqlen):
+        raise ValueError("B and C must be (batch, N, L)")
+    for name, t in (("D", D), ("delta_bias", delta_bias)):
+        if t is not None and tuple(t.shape) != (dim,):
+            raise ValueError("%s must be (dim,)" % name)
+    for name, t in (("h0", h0), ("h_out", h_out)):
+        _need_shape(t, name, (batch, dim, N))
+    _need_shape(out, "out", u.shape)
+    _need(out, "out", io, dev)
+    _need(h_out, "h_out", torch.float32, dev)
+    dims = _lib.ScanDims(batch, seqlen, dim, N)
+    dtp = _lib.DTypes(_io_dtype(u), _lib.MSSM_F32)
+    with torch.cuda.device(dev):
+        st = L.mssm_selective_scan_fwd_h0_noalloc(
+            _ptr(u), _ptr(delta), _ptr(delta_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+            _ptr(z), _ptr(h0), _ptr(out), _ptr(h_out), dims, dtp, _stream_handle(dev))
+    _check(st)
+    return out, h_out
+
+
 def selective_scan_conv_fwd(x, conv_w, delta, A, B, C, D=None, z=None, delta_bias=None,
                             conv_b=None, h0=None, return_last_state=True, out=None, h_out=None):
     """Selective-scan forward fed by its convolution prologue on the GPU:

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mssm.h"
+
 namespace mssm {
 
 enum IoType : int { IO_F32 = 0, IO_BF16 = 1 };
@@ -120,6 +122,12 @@ bool scan_rows_vectorizable(const ScanArgs &a);
 // Chunk-parallel variant; allocates its look-back scratch stream-ordered.
 hipError_t launch_scan_lookback(const ScanArgs &a, hipStream_t stream);
 bool scan_lookback_supported(const ScanArgs &a);
+// Bytes of look-back scratch a problem needs, and the variant that takes it
+// from the device's fixed array of kNoAllocScratchBytes instead of
+// allocating (the caller checks the size first).
+constexpr size_t kNoAllocScratchBytes = MSSM_NOALLOC_SCRATCH_BYTES;
+size_t scan_lookback_scratch_bytes(const ScanArgs &a);
+hipError_t launch_scan_lookback_noalloc(const ScanArgs &a, hipStream_t stream);
 
 // Status bits of the current device (mssm_device_status): waits for the
 // device, reads them into *bits and clears them when asked.

@@ -122,7 +122,8 @@ mssm_status check_overlaps(const Range *ins, int nin, const Range *outs, int nou
 mssm_status scan_fwd(const void *u, const void *delta, const float *delta_bias, const float *A,
                      const void *B, const void *C, const float *D, const void *z, const float *h0,
                      void *y, float *h_last, mssm_scan_dims dims, mssm_dtypes dtypes,
-                     void *stream, const float *conv_w = nullptr, const float *conv_b = nullptr) {
+                     void *stream, const float *conv_w = nullptr, const float *conv_b = nullptr,
+                     bool no_alloc = false) {
     g_last_error.clear();
     if (mssm_status s = check_dtypes(dtypes)) return s;
     const int64_t batch = dims.batch, L = dims.seqlen, dim = dims.dim, N = dims.dstate;
@@ -196,7 +197,16 @@ mssm_status scan_fwd(const void *u, const void *delta, const float *delta_bias, 
         case MSSM_VARIANT_LOOKBACK:
             if (!mssm::scan_lookback_supported(a))
                 return fail(MSSM_ERR_UNSUPPORTED, "look-back variant does not support this shape");
-            e = mssm::launch_scan_lookback(a, st);
+            if (no_alloc) {
+                const size_t need = mssm::scan_lookback_scratch_bytes(a);
+                if (need > mssm::kNoAllocScratchBytes)
+                    return fail(MSSM_ERR_UNSUPPORTED,
+                                "look-back scratch of %zu bytes exceeds the %zu bytes of the "
+                                "no-alloc entry point", need, mssm::kNoAllocScratchBytes);
+                e = mssm::launch_scan_lookback_noalloc(a, st);
+            } else {
+                e = mssm::launch_scan_lookback(a, st);
+            }
             break;
         default:
             return fail(MSSM_ERR_UNSUPPORTED, "variant %d does not apply to the selective scan",
@@ -320,6 +330,16 @@ mssm_status mssm_selective_scan_fwd_h0(const void *u, const void *delta,
                                        float *h_last, mssm_scan_dims dims,
                                        mssm_dtypes dtypes, void *stream) {
     return scan_fwd(u, delta, delta_bias, A, B, C, D, z, h0, y, h_last, dims, dtypes, stream);
+}
+
+mssm_status mssm_selective_scan_fwd_h0_noalloc(const void *u, const void *delta,
+                                               const float *delta_bias, const float *A,
+                                               const void *B, const void *C, const float *D,
+                                               const void *z, const float *h0, void *y,
+                                               float *h_last, mssm_scan_dims dims,
+                                               mssm_dtypes dtypes, void *stream) {
+    return scan_fwd(u, delta, delta_bias, A, B, C, D, z, h0, y, h_last, dims, dtypes, stream,
+                    nullptr, nullptr, true);
 }
 
 mssm_status mssm_selective_scan_fwd_conv(const void *x, const float *conv_w,

@@ -42,6 +42,7 @@
 // is the h_last buffer, the last segment (which waits for every pair before
 // its output walk) writes h_last after all the reads.
 #include <algorithm>
+#include <mutex>
 
 #include "internal.h"
 #include "mssm.h"
@@ -53,6 +54,12 @@ namespace mssm {
 // atomic OR, the host reads and clears them.  Each device's copy of the code
 // object holds its own word.
 __device__ uint32_t g_device_status_bits;
+
+// Scratch of the entry point that allocates nothing: a fixed array per
+// device, held until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): it
+// takes the device address from hipGetSymbolAddress once per device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -253,16 +260,31 @@ Plan make_plan(const ScanArgs &a) {
     return p;
 }
 
-template <typename T, int W, int NPL, bool CONV>
-hipError_t launch_typed(const ScanArgs &a, hipStream_t stream) {
+// Layout of the look-back scratch: the pairs of every (segment, group) item
+// (2 * kSlots floats each), then one flag per item and the ticket.
+template <int W, int NPL>
+void scratch_layout(const ScanArgs &a, int64_t *items, size_t *pay_bytes, size_t *flag_bytes) {
     constexpr int kSlots = 4 * W * NPL * kCh;
     const Plan p = make_plan(a);
-    const int64_t items = static_cast<int64_t>(p.nseg) * p.total_groups;
-    const size_t pay_bytes = static_cast<size_t>(items) * (2 * kSlots) * sizeof(float);
-    const size_t flag_bytes = static_cast<size_t>(items + 1) * sizeof(uint32_t);
-    void *mem = nullptr;
-    hipError_t e = hipMallocAsync(&mem, pay_bytes + flag_bytes, stream);
-    if (e != hipSuccess) return e;
+    *items = static_cast<int64_t>(p.nseg) * p.total_groups;
+    *pay_bytes = static_cast<size_t>(*items) * (2 * kSlots) * sizeof(float);
+    *flag_bytes = static_cast<size_t>(*items + 1) * sizeof(uint32_t);
+}
+
+// `pre`: caller-provided scratch of at least the layout's size (the no-alloc
+// entry point); null: allocated and freed stream-ordered here.
+template <typename T, int W, int NPL, bool CONV>
+hipError_t launch_typed(const ScanArgs &a, hipStream_t stream, void *pre) {
+    const Plan p = make_plan(a);
+    int64_t items;
+    size_t pay_bytes, flag_bytes;
+    scratch_layout<W, NPL>(a, &items, &pay_bytes, &flag_bytes);
+    void *mem = pre;
+    hipError_t e = hipSuccess;
+    if (!pre) {
+        e = hipMallocAsync(&mem, pay_bytes + flag_bytes, stream);
+        if (e != hipSuccess) return e;
+    }
     Scratch s;
     s.pay = static_cast<float *>(mem);
     s.flags = reinterpret_cast<uint32_t *>(static_cast<char *>(mem) + pay_bytes);
@@ -285,23 +307,65 @@ hipError_t launch_typed(const ScanArgs &a, hipStream_t stream) {
                            p.nseg, s, a.conv_w, a.conv_b);
         e = hipGetLastError();
     }
+    if (pre) return e;
     const hipError_t ef = hipFreeAsync(mem, stream);
     return e != hipSuccess ? e : ef;
 }
 
 template <typename T, int W, int NPL>
-hipError_t launch_conv(const ScanArgs &a, hipStream_t stream) {
-    return a.conv_w ? launch_typed<T, W, NPL, true>(a, stream) : launch_typed<T, W, NPL, false>(a, stream);
+hipError_t launch_conv(const ScanArgs &a, hipStream_t stream, void *pre) {
+    return a.conv_w ? launch_typed<T, W, NPL, true>(a, stream, pre)
+                    : launch_typed<T, W, NPL, false>(a, stream, pre);
 }
 
 template <typename T>
-hipError_t launch_by_n(const ScanArgs &a, hipStream_t stream) {
-    if (a.N <= 16) return launch_conv<T, 4, 1>(a, stream);
-    if (a.N <= 32) return launch_conv<T, 2, 4>(a, stream);
-    return launch_conv<T, 4, 4>(a, stream);
+hipError_t launch_by_n(const ScanArgs &a, hipStream_t stream, void *pre) {
+    if (a.N <= 16) return launch_conv<T, 4, 1>(a, stream, pre);
+    if (a.N <= 32) return launch_conv<T, 2, 4>(a, stream, pre);
+    return launch_conv<T, 4, 4>(a, stream, pre);
+}
+
+// Device address of this device's scratch array, looked up once per device
+// (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t device_scratch(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace
+
+size_t scan_lookback_scratch_bytes(const ScanArgs &a) {
+    int64_t items;
+    size_t pay, flags;
+    if (a.N <= 16) scratch_layout<4, 1>(a, &items, &pay, &flags);
+    else if (a.N <= 32) scratch_layout<2, 4>(a, &items, &pay, &flags);
+    else scratch_layout<4, 4>(a, &items, &pay, &flags);
+    return pay + flags;
+}
+
+hipError_t launch_scan_lookback_noalloc(const ScanArgs &a, hipStream_t stream) {
+    if (scan_lookback_scratch_bytes(a) > kNoAllocScratchBytes) return hipErrorInvalidValue;
+    void *pre = nullptr;
+    const hipError_t e = device_scratch(&pre);
+    if (e != hipSuccess) return e;
+    if (a.io == IO_F32) return launch_by_n<float>(a, stream, pre);
+    return launch_by_n<uint16_t>(a, stream, pre);
+}
 
 bool scan_lookback_supported(const ScanArgs &a) {
     if (a.N < 1 || a.N > 64 || !scan_offsets_fit(a)) return false;
@@ -324,8 +388,8 @@ hipError_t device_status(uint32_t *bits, bool clear) {
 }
 
 hipError_t launch_scan_lookback(const ScanArgs &a, hipStream_t stream) {
-    if (a.io == IO_F32) return launch_by_n<float>(a, stream);
-    return launch_by_n<uint16_t>(a, stream);
+    if (a.io == IO_F32) return launch_by_n<float>(a, stream, nullptr);
+    return launch_by_n<uint16_t>(a, stream, nullptr);
 }
 
 }  // namespace mssm

@@ -426,3 +426,37 @@ def test_device_status_bit_matches_header():
     src = open(HEADER).read()
     assert int(re.search(r"#define MSSM_DEVICE_LOOKBACK_TIMEOUT (0x[0-9a-f]+)u", src).group(1),
                16) == _lib.DEVICE_LOOKBACK_TIMEOUT
+
+
+def test_noalloc_rejects_scratch_beyond_its_array(L):
+    """Forced to the look-back variant, a problem of 5000 channel groups
+    would need about 10 MB of scratch: refused before anything is queued."""
+    prev = L.mssm_force_variant(_lib.VARIANT_LOOKBACK)
+    try:
+        p = [fake(i) for i in range(1, 12)]
+        st = L.mssm_selective_scan_fwd_h0_noalloc(
+            p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], None, p[8], p[9],
+            _lib.ScanDims(1, 4096, 16 * 5000, 16), _lib.DTypes(1, 0), None)
+    finally:
+        L.mssm_force_variant(prev)
+    assert st == _lib.MSSM_ERR_UNSUPPORTED
+    assert b"no-alloc" in L.mssm_last_error()
+
+
+def test_noalloc_validation_matches_scan(L):
+    """The no-alloc entry point validates exactly like the allocating one."""
+    p = [fake(i) for i in range(1, 12)]
+    dims = _lib.ScanDims(2, 64, 8, 4)
+    dt = _lib.DTypes(0, 0)
+    for args in ([None] + p[1:8] + [None, p[8], p[9]],
+                 p[:8] + [None, None, p[9]],
+                 p[:8] + [None, p[0], p[9]]):
+        a = L.mssm_selective_scan_fwd_h0(*args, dims, dt, None)
+        b = L.mssm_selective_scan_fwd_h0_noalloc(*args, dims, dt, None)
+        assert a == b != 0
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(HEADER).read()
+    assert re.search(r"#define MSSM_NOALLOC_SCRATCH_BYTES \(8u << 20\)", src)
+    assert _lib.NOALLOC_SCRATCH_BYTES == 8 << 20
