@@ -23,11 +23,25 @@ Prints one JSON line:
   cpu_baseline        the float64 CPU oracle timed on this host
   parity              sampled-row comparison with the oracle
 
+Timing: an untimed ramp (steps until the per-launch time settles, at most
+--ramp-s seconds), W untimed warmup steps, then K steps with an event
+recorded on the library's stream before the first and after every step:
+ms_per_step is their mean; "timing" adds the per-launch median, min and max.
+After the timed steps the library's probes (include/mssm_probes.h) measure
+the copy ceiling and the fma / 2^x / log2 x / 1/x issue rates; the roofline
+charges each transcendental its measured cost and reports
+t_roof = max(t_HBM, t_ALU at the measured rates).  amd-smi's clock and
+temperature readings are recorded before and after the timed region.  The
+CPU baseline times the oracle on one thread and on all the host threads the
+process may use (OMP_NUM_THREADS, else every core).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--variant auto|rowserial|chunked|...] [--no-cpu]
-                       [--copy-probe-mib M]
+                       [--no-probes] [--ramp-s S] [--copy-probe-mib M]
        python bench.py --workload NAME --steps K --warmup W --copy-probe-mib M
-                       --counters FETCH_CSV WRITE_CSV      (summary only)
+                       --counters FETCH_CSV WRITE_CSV      (summary only; the
+                       two rocprofv3 runs pass --ramp-s 0 --no-probes, so that
+                       every library dispatch is one of the W + K steps)
 """
 from __future__ import annotations
 
@@ -56,20 +70,37 @@ VARIANTS = {"auto": 0, "rowserial": 1, "chunked": 2, "lookback": 3,
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 
 
-def scan_slots(p) -> float:
-    """Algorithmic VALU issue slots of one selective-scan step.
+def scan_ops(p) -> dict:
+    """Algorithmic vector-ALU operations of one selective-scan step, by kind
+    (fma: any single-issue multiply, add or fused multiply-add; exp, log,
+    rcp: the hardware 2^x, log2 x and 1/x).
 
-    Per element (b, t, d, n): dl*A (1), 2^x (1 transcendental = 2 slots, it
-    issues at half rate), (dl*u)*B (1), state FMA (1), output FMA (1) = 6.
-    Per (b, t, d): softplus (exp + log = 4 slots + 3), dl*u (1), D*u (1),
-    with a gate silu (exp + rcp = 4 slots + 2) and the product (1), and with
-    the convolution prologue 4 FMAs and a silu (4 slots + 2).
+    Per element (b, t, d, n): dl*A, (dl*u)*B, the state FMA and the output
+    FMA (4 fma) and one 2^x.  Per (b, t, d): softplus (one 2^x, one log2 x,
+    3 fma), dl*u (1), with a skip term D*u (1), with a gate silu (2^x, 1/x,
+    2 fma) and the product (1), with the convolution prologue 4 FMAs and a
+    silu (2^x, 1/x, 2 fma).
     """
-    per_elem = 6
-    per_row_step = 4 + 3 + 1 + (1 if p.skip else 0) + (4 + 2 + 1 if p.gate else 0)
-    per_row_step += (4 + 4 + 2) if getattr(p, "conv", False) else 0
     rows_steps = p.batch * p.dim * p.seqlen
-    return per_elem * p.elements + per_row_step * rows_steps
+    gate, conv = bool(p.gate), bool(getattr(p, "conv", False))
+    return {
+        "fma": 4 * p.elements + rows_steps * (3 + 1 + (1 if p.skip else 0) + (3 if gate else 0)
+                                              + (6 if conv else 0)),
+        "exp": p.elements + rows_steps * (1 + (1 if gate else 0) + (1 if conv else 0)),
+        "log": rows_steps,
+        "rcp": rows_steps * ((1 if gate else 0) + (1 if conv else 0)),
+    }
+
+
+# Issue cost of each transcendental in multiply-add slots when no probe ran:
+# the probe measures v_exp_f32, v_log_f32 and v_rcp_f32 at about half the
+# multiply-add rate.
+DEFAULT_COSTS = {"exp": 2.0, "log": 2.0, "rcp": 2.0}
+
+
+def alu_slots(ops: dict, costs: dict) -> float:
+    """Multiply-add issue slots of an operation count at the given costs."""
+    return ops["fma"] + sum(costs[k] * ops[k] for k in ("exp", "log", "rcp"))
 
 
 def ssd_flops(p, chunk: int = 256) -> float:
@@ -156,7 +187,7 @@ def summarize_counters(workload: str, fetch_csv: str, write_csv: str, probe_mib:
                 if r["Counter_Name"] != counter:
                     continue
                 name, d, v = r["Kernel_Name"], r["Dispatch_Id"], float(r["Counter_Value"])
-                if "mssm::" in name:
+                if "mssm::" in name and "probe_" not in name:
                     key = name.replace("(anonymous namespace)::", "").split("(")[0]
                     key = key.replace("void ", "")
                     lib.setdefault(key, {}).setdefault(d, 0.0)
@@ -186,6 +217,130 @@ def summarize_counters(workload: str, fetch_csv: str, write_csv: str, probe_mib:
             per_step += sum(ds.values()) * 1024.0 * scale / steps
     out["hbm_bytes_per_launch"] = per_step
     return out
+
+
+def alu_roofline(ops: dict, min_bytes: int, sec: float, peaks: dict) -> dict:
+    """Roofline of a vector-ALU kernel from its operation counts.
+
+    achieved: issue slots per second, a transcendental costing what the
+    probes measured (the multiply-add rate over its own rate; DEFAULT_COSTS
+    without probes), against the published VALU peak.  t_roof = max(t_HBM
+    at the 8 TB/s peak, t_ALU at the rates the probes measured), and
+    roof_frac = t_roof / the measured kernel time."""
+    costs = peaks.get("costs") or DEFAULT_COSTS
+    slots = alu_slots(ops, costs)
+    a = slots / sec / 1e12
+    t_hbm = min_bytes / (HBM_PEAK_GBS * 1e9)
+    rates = peaks.get("valu_tlanes")
+    if rates:
+        t_alu = sum(ops[k] / (rates[k] * 1e12) for k in ("fma", "exp", "log", "rcp"))
+    else:
+        t_alu = slots / (VALU_PEAK_TSLOTS * 1e12)
+    t_roof = max(t_alu, t_hbm)
+    return {"bound": "alu" if t_alu >= t_hbm else "hbm", "achieved": a, "peak": VALU_PEAK_TSLOTS,
+            "unit": "T VALU lane-slots/s", "frac": a / VALU_PEAK_TSLOTS,
+            "slots_per_launch": slots, "ops_per_launch": ops, "slot_costs": costs,
+            "t_alu_us": t_alu * 1e6, "t_hbm_us": t_hbm * 1e6, "t_roof_us": t_roof * 1e6,
+            "roof_frac": t_roof / sec}
+
+
+def measure_peaks(torch, dev, api, copy_mib=1024):
+    """Ceilings measured on this device with the library's probes
+    (include/mssm_probes.h): the streaming-copy rate over copy_mib MiB (read
+    + write bytes per second, beyond the 256 MB Infinity Cache), and the
+    issue rates of fma, 2^x, log2 x and 1/x in T lane-operations per second.
+    Each probe runs twice untimed, then three timed launches on the current
+    stream."""
+    from selective_state_space_05_amd import _lib
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, reps=3):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    nbytes = copy_mib << 20
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    t = timed(lambda: api.probe_copy(src, dst))
+    copy_gbs = 2 * nbytes / t / 1e9
+    del src, dst
+    out = torch.empty(_lib.PROBE_VALU_THREADS, dtype=torch.float32, device=dev)
+    rates = {}
+    for name, op, iters in (("fma", _lib.PROBE_FMA, 4000), ("exp", _lib.PROBE_EXP2, 2000),
+                            ("log", _lib.PROBE_LOG2, 2000), ("rcp", _lib.PROBE_RCP, 2000)):
+        lane_ops = _lib.PROBE_VALU_THREADS * iters * _lib.PROBE_VALU_OPS_PER_ITER
+        t = timed(lambda: api.probe_valu(op, iters, out))
+        rates[name] = lane_ops / t / 1e12
+    costs = {k: rates["fma"] / rates[k] for k in ("exp", "log", "rcp")}
+    return {"copy_gbs": copy_gbs, "copy_mib": copy_mib, "valu_tlanes": rates, "costs": costs}
+
+
+def amd_smi_snapshot():
+    """Clock and temperature of GPU 0 as amd-smi reports them (a compact
+    summary; the error text if amd-smi is missing or fails)."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-t", "--json"],
+                           capture_output=True, text=True, timeout=30)
+    except (OSError, subprocess.SubprocessError) as e:
+        return {"error": str(e)[:200]}
+    if r.returncode != 0:
+        return {"error": (r.stderr or r.stdout).strip()[-300:]}
+    try:
+        data = json.loads(r.stdout)
+    except ValueError:
+        return {"error": "unparsed output", "raw": r.stdout[:400]}
+    out = {"gfx_clk_mhz": [], "temperature_c": {}}
+
+    def value(v):
+        if isinstance(v, dict):
+            v = v.get("value")
+        try:
+            return float(v)
+        except (TypeError, ValueError):
+            return None
+
+    def walk(o):
+        if isinstance(o, dict):
+            for k, v in o.items():
+                if k == "clock" and isinstance(v, dict):
+                    for ck, cv in v.items():
+                        if ck.startswith("gfx") and isinstance(cv, dict):
+                            x = value(cv.get("clk"))
+                            if x is not None:
+                                out["gfx_clk_mhz"].append(x)
+                elif k == "temperature" and isinstance(v, dict):
+                    for tk, tv in v.items():
+                        x = value(tv)
+                        if x is not None:
+                            out["temperature_c"][tk] = x
+                else:
+                    walk(v)
+        elif isinstance(o, list):
+            for v in o:
+                walk(v)
+
+    walk(data)
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def g1(a, r):
@@ -227,12 +382,8 @@ class ScanBench:
             self.api.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"],
                                         t["z"], t["delta_bias"], out=t["y"], h_out=t["h"])
 
-    def roofline(self, sec):
-        slots = scan_slots(self.p)
-        a = slots / sec / 1e12
-        return {"bound": "alu", "achieved": a, "peak": VALU_PEAK_TSLOTS,
-                "unit": "T VALU lane-slots/s", "frac": a / VALU_PEAK_TSLOTS,
-                "slots_per_launch": slots}
+    def roofline(self, sec, peaks):
+        return alu_roofline(scan_ops(self.p), self.p.min_traffic_bytes(), sec, peaks)
 
     def _u_rows(self):
         """The scan input the oracle sees: u itself, or with the convolution
@@ -259,7 +410,7 @@ class ScanBench:
         hs = np.stack([hg[b, d] for b, d in rows])
         return len(rows), g1(ys, yo), g1(hs, ho)
 
-    def cpu_baseline(self, threads, budget_s=15.0, min_wall_s=2.0):
+    def cpu_baseline(self, threads, budget_s=8.0, min_wall_s=2.0):
         """Time the oracle on whole (batch, channel) rows: as many as about
         `budget_s` seconds of work at the measured single-row rate, in passes
         repeated for at least `min_wall_s` seconds."""
@@ -340,12 +491,16 @@ class SSDBench:
         self.api.ssd_scalar_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["dt_bias"],
                                 chunk=self.chunk, out=t["y"], h_out=t["h"])
 
-    def roofline(self, sec):
+    def roofline(self, sec, peaks):
         fl = ssd_flops(self.p, self.chunk)
         a = fl / sec / 1e12
+        t_mfma = fl / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+        t_hbm = self.p.min_traffic_bytes() / (HBM_PEAK_GBS * 1e9)
+        t_roof = max(t_mfma, t_hbm)
         return {"bound": "mfma", "achieved": a, "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": a / MFMA_BF16_PEAK_TFLOPS,
-                "flops_per_launch": fl}
+                "flops_per_launch": fl, "t_mfma_us": t_mfma * 1e6, "t_hbm_us": t_hbm * 1e6,
+                "t_roof_us": t_roof * 1e6, "roof_frac": t_roof / sec}
 
     def parity(self, t):
         from oracle import oracle
@@ -362,7 +517,7 @@ class SSDBench:
         hs = np.stack([hg[b, hh, pp] for b, hh, pp in rows])
         return len(rows), g1(ys, yo), g1(hs, ho)
 
-    def cpu_baseline(self, threads, budget_s=15.0):
+    def cpu_baseline(self, threads, budget_s=6.0):
         """Time the oracle on whole (batch, head) blocks, as many as about
         `budget_s` seconds of work at the measured single-head rate."""
         from oracle import oracle
@@ -406,18 +561,22 @@ class SSDBench:
                 "chunk": self.chunk}
 
 
-def bwd_slots(p) -> float:
-    """Algorithmic VALU issue slots of one backward.
+def bwd_ops(p) -> dict:
+    """Algorithmic vector-ALU operations of one backward, by kind.
 
     Per element (b, t, d, n): the forward recomputed twice (state pass and
-    segment recompute: 2 x (dl*A, 2^x = 2, (dl*u)*B, FMA) = 10) and the
-    reverse step (2^x = 2, dh FMA, dC product, dA 2, dB product, du FMA,
-    d(dl) 2, carry = 10).  Per (b, t, d): softplus three times (7 each),
-    the logistic of x (4), dl*u twice, the gate's silu and derivative (10).
+    segment recompute: dl*A, (dl*u)*B, FMA and a 2^x each) and the reverse
+    step (dh FMA, dC product, dA 2, dB product, du FMA, d(dl) 2, carry, and
+    a 2^x): 14 fma and 3 exp.  Per (b, t, d): softplus three times (2^x,
+    log2 x, 3 fma each), the logistic of x (2^x, 1/x), two products and,
+    with a gate, its silu and derivative (2^x, 1/x, 6 fma).
     """
-    per_elem = 20
-    per_row_step = 3 * 7 + 4 + 2 + (10 if p.gate else 0)
-    return per_elem * p.elements + per_row_step * p.batch * p.dim * p.seqlen
+    rows_steps = p.batch * p.dim * p.seqlen
+    g = 1 if p.gate else 0
+    return {"fma": 14 * p.elements + rows_steps * (9 + 2 + 6 * g),
+            "exp": 3 * p.elements + rows_steps * (3 + 1 + g),
+            "log": 3 * rows_steps,
+            "rcp": rows_steps * (1 + g)}
 
 
 class BwdBench(ScanBench):
@@ -439,12 +598,8 @@ class BwdBench(ScanBench):
                                                  D=t["D"], z=t["z"], delta_bias=t["delta_bias"],
                                                  dh_last=t["dh_last"])
 
-    def roofline(self, sec):
-        slots = bwd_slots(self.p)
-        a = slots / sec / 1e12
-        return {"bound": "alu", "achieved": a, "peak": VALU_PEAK_TSLOTS,
-                "unit": "T VALU lane-slots/s", "frac": a / VALU_PEAK_TSLOTS,
-                "slots_per_launch": slots}
+    def roofline(self, sec, peaks):
+        return alu_roofline(bwd_ops(self.p), self.p.min_traffic_bytes(), sec, peaks)
 
     def _row_oracle(self, b, d, nthreads=0):
         from oracle import oracle
@@ -473,17 +628,20 @@ class BwdBench(ScanBench):
         return (len(rows), g1(np.stack([a for a, _ in gu]), np.stack([r for _, r in gu])),
                 g1(np.stack([a for a, _ in gd]), np.stack([r for _, r in gd])))
 
-    cpu_cores = 1   # the oracle's backward runs on one thread
-
-    def cpu_baseline(self, threads, budget_s=10.0):
-        """The oracle's backward on whole rows (single-threaded, as the
-        oracle is), as many as fit in about ``budget_s``."""
+    def cpu_baseline(self, threads, budget_s=6.0):
+        """The oracle's backward on whole rows for about ``budget_s``: one
+        row per call (the oracle's backward is single-threaded), with
+        ``threads`` calls in flight on as many Python threads (the calls
+        release the interpreter lock)."""
+        import concurrent.futures
         p = self.p
         t0 = time.time()
         done = 0
-        while done == 0 or time.time() - t0 < budget_s:
-            self._row_oracle(done % p.batch, done % p.dim)
-            done += 1
+        with concurrent.futures.ThreadPoolExecutor(max_workers=threads) as ex:
+            while done == 0 or time.time() - t0 < budget_s:
+                rows = [((done + i) % p.batch, (done + i) % p.dim) for i in range(threads)]
+                list(ex.map(lambda r: self._row_oracle(*r), rows))
+                done += threads
         cpu_s = time.time() - t0
         return done * p.seqlen * p.dstate / cpu_s, "%d (batch, channel) rows, full length %d, float64, %.1f s" % (
             done, p.seqlen, cpu_s)
@@ -521,11 +679,13 @@ class StepBench:
         self.api.selective_state_update(t["state"], t["x"], t["dt"], t["A"], t["B"], t["C"],
                                         t["D"], t["z"], t["dt_bias"], out=t["y"])
 
-    def roofline(self, sec):
+    def roofline(self, sec, peaks):
         nbytes = self.p.min_traffic_bytes()
         a = nbytes / sec / 1e9
+        t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
         return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": a / HBM_PEAK_GBS, "bytes_per_launch": nbytes}
+                "frac": a / HBM_PEAK_GBS, "bytes_per_launch": nbytes, "t_roof_us": t_hbm * 1e6,
+                "roof_frac": t_hbm / sec}
 
     def _oracle(self, nthreads=0):
         from oracle import oracle
@@ -549,7 +709,7 @@ class StepBench:
         hg = fresh["state"].cpu().numpy().astype(np.float64)
         return self.p.batch, g1(yg, yo[..., 0]), g1(hg, ho)
 
-    def cpu_baseline(self, threads, budget_s=10.0):
+    def cpu_baseline(self, threads, budget_s=4.0):
         """The oracle on the whole step, repeated for about `budget_s`."""
         reps, t0 = 0, time.time()
         while reps == 0 or time.time() - t0 < budget_s:
@@ -569,13 +729,18 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=50,
+    ap.add_argument("--warmup", type=int, default=10,
                     help="untimed steps before the timed ones (also lets the GPU clock ramp up)")
     ap.add_argument("--workload", default="mamba2.8b_layer_bf16")
     ap.add_argument("--variant", default="auto", choices=sorted(VARIANTS))
     ap.add_argument("--chunk", type=int, default=256, help="SSD chunk length")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the copy and ALU peak probes (transcendentals then cost 2 slots)")
+    ap.add_argument("--ramp-s", type=float, default=2.0,
+                    help="at most this many seconds of untimed steps before the warmup, until the "
+                         "per-launch time settles (0: none)")
     ap.add_argument("--rotate", type=int, default=0,
                     help="input/output buffer sets cycled across steps (0: enough to exceed the "
                          "256 MB Infinity Cache)")
@@ -635,36 +800,49 @@ def main():
     rotate = args.rotate or max(1, min(4, -(-(1 << 30) // footprint)))
     sets = [wb.upload() for _ in range(rotate)]
     torch.cuda.synchronize()
+    smi_before = amd_smi_snapshot()
 
     variant = VARIANTS[args.variant]
-    print("[bench] warmup %d, timed %d steps, %d buffer sets" % (args.warmup, args.steps, rotate),
-          file=sys.stderr, flush=True)
+    # the library launches on torch's current stream; every event is
+    # recorded on that same stream
+    stream = torch.cuda.current_stream(dev)
     with api.forced_variant(variant):
+        print("[bench] clock ramp", file=sys.stderr, flush=True)
+        ramp = ramp_up(torch, stream, lambda i: wb.step(sets[i % rotate]), args.ramp_s)
+        print("[bench] warmup %d, timed %d steps, %d buffer sets" % (args.warmup, args.steps, rotate),
+              file=sys.stderr, flush=True)
         for i in range(args.warmup):
             wb.step(sets[i % rotate])
         torch.cuda.synchronize()
         used = VARIANT_NAMES.get(api.last_variant(), str(api.last_variant()))
-        # the library launches on torch's current stream; the events are
-        # recorded on that same stream
-        stream = torch.cuda.current_stream(dev)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        # one event before the first step and one after every step: the K
+        # per-launch durations and their sum
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         torch.cuda.synchronize()
-        e0.record(stream)
+        ev[0].record(stream)
         for i in range(args.steps):
             wb.step(sets[i % rotate])
-        e1.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    total_ms = ev[0].elapsed_time(ev[-1])
+    per_launch = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    smi_after = amd_smi_snapshot()
+    ms_step = total_ms / args.steps
     sec = ms_step / 1e3
 
+    peaks = {}
+    if not args.no_probes:
+        print("[bench] peak probes", file=sys.stderr, flush=True)
+        peaks = measure_peaks(torch, dev, api)
+
     hbm_gbs = footprint / sec / 1e9
-    roof = wb.roofline(sec)
+    roof = wb.roofline(sec, peaks)
     sha = kernel_source_sha(workload_family(p.name))
     roof["traffic"] = load_traffic(p.name, sha)
     roof["kernel_source_sha"] = sha
     cfg = wb.config()
     cfg.update({"variant": used, "buffer_sets": rotate})
+    from selective_state_space_05_amd import _lib
 
     out = {
         "metric": METRIC,
@@ -680,10 +858,19 @@ def main():
         "dtype": wb.dtype,
         "data": "synthetic (seeded numpy draws; no dataset or trained weights)",
         "config": cfg,
+        "timing": {"mean_us": ms_step * 1e3, "median_us": per_launch[len(per_launch) // 2] * 1e3,
+                   "min_us": per_launch[0] * 1e3, "max_us": per_launch[-1] * 1e3,
+                   "launches": args.steps, "ramp": ramp},
         "hbm": {"min_traffic_bytes": footprint, "achieved_gbs": hbm_gbs,
                 "peak_gbs": HBM_PEAK_GBS, "frac": hbm_gbs / HBM_PEAK_GBS},
         "roofline": roof,
+        "peaks_measured": peaks or None,
+        "gpu_state": {"before": smi_before, "after": smi_after},
+        "lib_source_hash": _lib.lib().mssm_source_hash().decode(),
     }
+    if peaks:
+        out["copy_ceiling_gbs"] = peaks["copy_gbs"]
+        out["hbm"]["frac_of_copy_ceiling"] = hbm_gbs / peaks["copy_gbs"]
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 18          # float32 elements
@@ -704,14 +891,47 @@ def main():
                          "ok": bool(ey <= tol and eh <= tol)}
 
     if not args.no_cpu:
-        threads = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", "16")), 16)
-        print("[bench] CPU oracle baseline (%d threads)" % threads, file=sys.stderr, flush=True)
-        v, sample = wb.cpu_baseline(threads)
-        out["cpu_baseline"] = {"value": v, "unit": "elements/s",
-                               "cores": getattr(wb, "cpu_cores", threads),
-                               "kind": "oracle", "sample": sample}
+        # all host threads this process may use: the CPU share set by
+        # OMP_NUM_THREADS where the environment sets one, else every core
+        share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+        threads = max(1, min(os.cpu_count() or 1, share))
+        print("[bench] CPU oracle baseline: 1 thread, then %d threads" % threads,
+              file=sys.stderr, flush=True)
+        v1, sample1 = wb.cpu_baseline(1)
+        vn, samplen = wb.cpu_baseline(threads)
+        out["cpu_baseline"] = {"value": vn, "unit": "elements/s", "cores": threads,
+                               "kind": "oracle", "sample": samplen,
+                               "single_thread": {"value": v1, "sample": sample1},
+                               "cpu_count": os.cpu_count(), "cpu_model": cpu_model()}
 
     print(json.dumps(out), flush=True)
+
+
+def ramp_up(torch, stream, step, max_s, min_s=0.5, batch_ms=20.0, tol=0.015):
+    """Untimed steps until the per-launch time settles (the GPU clock ramps
+    up under load): batches of about batch_ms, until two consecutive batch
+    means agree within tol after at least min_s, or max_s has passed."""
+    if max_s <= 0:
+        return None
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.time()
+    n = 1
+    means, i = [], 0
+    while True:
+        e0.record(stream)
+        for _ in range(n):
+            step(i)
+            i += 1
+        e1.record(stream)
+        torch.cuda.synchronize()
+        means.append(e0.elapsed_time(e1) / n)
+        n = max(1, int(batch_ms / max(means[-1], 1e-3)))
+        el = time.time() - t0
+        if (el >= min_s and len(means) >= 3 and abs(means[-1] - means[-2]) <= tol * means[-1]) \
+                or el >= max_s:
+            break
+    return {"steps": i, "seconds": round(time.time() - t0, 3), "first_us": means[0] * 1e3,
+            "last_us": means[-1] * 1e3, "batches": len(means)}
 
 
 if __name__ == "__main__":

@@ -55,6 +55,14 @@ EXPORTED = (
     "mssm_device_status",
     "mssm_selective_scan_fwd_h0_noalloc",
 )
+# Every symbol include/mssm_probes.h declares (measurement probes).
+EXPORTED_PROBES = (
+    "mssm_probe_copy",
+    "mssm_probe_valu",
+)
+PROBE_FMA, PROBE_EXP2, PROBE_LOG2, PROBE_RCP = 0, 1, 2, 3
+PROBE_VALU_THREADS = 2048 * 256
+PROBE_VALU_OPS_PER_ITER = 128
 
 
 class ScanDims(ctypes.Structure):
@@ -123,6 +131,10 @@ def _declare(L):
     L.mssm_last_error.restype = ctypes.c_char_p
     L.mssm_version.argtypes = []
     L.mssm_version.restype = ctypes.c_int
+    L.mssm_probe_copy.argtypes = [vp, vp, ctypes.c_int64, vp]
+    L.mssm_probe_copy.restype = ctypes.c_int
+    L.mssm_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int32, fp, vp]
+    L.mssm_probe_valu.restype = ctypes.c_int
     L.mssm_source_hash.argtypes = []
     L.mssm_source_hash.restype = ctypes.c_char_p
     L.mssm_device_status.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int]

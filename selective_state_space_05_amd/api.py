@@ -412,3 +412,31 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None,
             _ptr(D), _ptr(z), _ptr(y), dims, dtp, _stream_handle(dev))
     _check(st)
     return y
+
+
+def probe_copy(src, dst):
+    """Launch the streaming copy probe (mssm_probe_copy) from ``src`` to
+    ``dst`` (contiguous device tensors of the same byte size) on the current
+    stream."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must hold the same number of bytes")
+    _need(src, "src")
+    _need(dst, "dst")
+    with torch.cuda.device(src.device):
+        _check(_lib.lib().mssm_probe_copy(_ptr(src), _ptr(dst), nbytes,
+                                          _stream_handle(src.device)))
+
+
+def probe_valu(op: int, iters: int, out):
+    """Launch the ALU issue-rate probe (mssm_probe_valu) for operation ``op``
+    (``_lib.PROBE_*``); ``out`` is a float32 device tensor of at least
+    ``_lib.PROBE_VALU_THREADS`` elements.  Returns the lane-operations the
+    launch performs."""
+    _need(out, "out", torch.float32)
+    if out.numel() < _lib.PROBE_VALU_THREADS:
+        raise ValueError("out needs %d elements" % _lib.PROBE_VALU_THREADS)
+    with torch.cuda.device(out.device):
+        _check(_lib.lib().mssm_probe_valu(int(op), int(iters), _ptr(out),
+                                          _stream_handle(out.device)))
+    return _lib.PROBE_VALU_THREADS * int(iters) * _lib.PROBE_VALU_OPS_PER_ITER

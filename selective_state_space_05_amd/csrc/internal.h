@@ -138,6 +138,10 @@ hipError_t device_status(uint32_t *bits, bool clear);
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t stream);
 bool scan_bwd_supported(const BwdArgs &a);
 
+// Measurement probes (include/mssm_probes.h); arguments already checked.
+hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);
+hipError_t launch_probe_valu(int op, int iters, float *out, hipStream_t stream);
+
 hipError_t launch_state_update(const StepArgs &a, hipStream_t stream);
 bool state_update_supported(const StepArgs &a);
 

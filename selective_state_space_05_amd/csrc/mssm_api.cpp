@@ -12,6 +12,7 @@
 
 #include "internal.h"
 #include "mssm.h"
+#include "mssm_probes.h"
 
 namespace {
 
@@ -544,6 +545,32 @@ mssm_status mssm_device_status(uint32_t *bits, int clear) {
     if (!bits) return fail(MSSM_ERR_INVALID_ARG, "bits is null");
     const hipError_t e = mssm::device_status(bits, clear != 0);
     if (e != hipSuccess) return hip_fail(e, "device status read");
+    return MSSM_OK;
+}
+
+mssm_status mssm_probe_copy(const void *src, void *dst, int64_t bytes, void *stream) {
+    g_last_error.clear();
+    if (!src || !dst) return fail(MSSM_ERR_INVALID_ARG, "src and dst must not be null");
+    if (bytes <= 0 || bytes % 16 != 0 || bytes >= (int64_t(1) << 43))
+        return fail(MSSM_ERR_INVALID_ARG,
+                    "bytes must be a positive multiple of 16 below 2^43, got %lld", (long long)bytes);
+    if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u)
+        return fail(MSSM_ERR_INVALID_ARG, "src and dst must be 16-byte aligned");
+    if (overlaps(range("src", src, bytes), range("dst", dst, bytes)))
+        return fail(MSSM_ERR_INVALID_ARG, "src and dst overlap");
+    const hipError_t e = mssm::launch_probe_copy(src, dst, bytes, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "copy probe launch");
+    return MSSM_OK;
+}
+
+mssm_status mssm_probe_valu(int op, int32_t iters, float *out, void *stream) {
+    g_last_error.clear();
+    if (op < MSSM_PROBE_FMA || op > MSSM_PROBE_RCP)
+        return fail(MSSM_ERR_INVALID_ARG, "unknown probe operation %d", op);
+    if (iters < 1) return fail(MSSM_ERR_INVALID_ARG, "iters must be >= 1");
+    if (!out) return fail(MSSM_ERR_INVALID_ARG, "out is null");
+    const hipError_t e = mssm::launch_probe_valu(op, iters, out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "ALU probe launch");
     return MSSM_OK;
 }
 

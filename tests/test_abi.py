@@ -27,13 +27,23 @@ def L():
     return _lib.lib()
 
 
-def header_functions():
-    src = open(HEADER).read()
-    return sorted(set(re.findall(r"MSSM_API\s+[\w\s\*]+?\b(mssm_\w+)\s*\(", src)))
+PROBES_HEADER = os.path.join(ROOT, "include", "mssm_probes.h")
+
+
+def header_functions(path=None):
+    """Functions declared by one header, or by every header under include/."""
+    paths = [path] if path else [os.path.join(ROOT, "include", f)
+                                 for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+                                 if f.endswith(".h")]
+    names = set()
+    for p in paths:
+        names |= set(re.findall(r"MSSM_API\s+[\w\s\*]+?\b(mssm_\w+)\s*\(", open(p).read()))
+    return sorted(names)
 
 
 def test_header_declares_expected_functions():
-    assert header_functions() == sorted(_lib.EXPORTED)
+    assert header_functions(HEADER) == sorted(_lib.EXPORTED)
+    assert header_functions(PROBES_HEADER) == sorted(_lib.EXPORTED_PROBES)
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -46,7 +56,7 @@ def test_only_the_c_abi_is_exported():
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     syms = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
-    assert {s for s in syms if s.startswith("mssm")} == set(_lib.EXPORTED)
+    assert {s for s in syms if s.startswith("mssm")} == set(_lib.EXPORTED) | set(_lib.EXPORTED_PROBES)
     assert not [s for s in syms if s.startswith("_ZN4mssm")]
 
 
@@ -460,3 +470,25 @@ def test_noalloc_scratch_size_matches_header():
     src = open(HEADER).read()
     assert re.search(r"#define MSSM_NOALLOC_SCRATCH_BYTES \(8u << 20\)", src)
     assert _lib.NOALLOC_SCRATCH_BYTES == 8 << 20
+
+
+def test_probe_constants_match_binding():
+    src = open(PROBES_HEADER).read()
+    for name, val in (("FMA", _lib.PROBE_FMA), ("EXP2", _lib.PROBE_EXP2),
+                      ("LOG2", _lib.PROBE_LOG2), ("RCP", _lib.PROBE_RCP)):
+        assert int(re.search(r"#define MSSM_PROBE_%s (\d+)" % name, src).group(1)) == val
+    assert re.search(r"#define MSSM_PROBE_VALU_THREADS \(2048 \* 256\)", src)
+    assert _lib.PROBE_VALU_THREADS == 2048 * 256
+    assert int(re.search(r"#define MSSM_PROBE_VALU_OPS_PER_ITER (\d+)", src).group(1)) == \
+        _lib.PROBE_VALU_OPS_PER_ITER
+
+
+def test_probe_validation(L):
+    assert L.mssm_probe_copy(None, fake(2), 1024, None) == _lib.MSSM_ERR_INVALID_ARG
+    assert L.mssm_probe_copy(fake(1), fake(2), 1000, None) == _lib.MSSM_ERR_INVALID_ARG
+    assert L.mssm_probe_copy(fake(1), fake(1) + 512, 1024, None) == _lib.MSSM_ERR_INVALID_ARG
+    assert b"overlap" in L.mssm_last_error()
+    assert L.mssm_probe_copy(fake(1) + 4, fake(2), 1024, None) == _lib.MSSM_ERR_INVALID_ARG
+    assert L.mssm_probe_valu(7, 10, fake(1), None) == _lib.MSSM_ERR_INVALID_ARG
+    assert L.mssm_probe_valu(0, 0, fake(1), None) == _lib.MSSM_ERR_INVALID_ARG
+    assert L.mssm_probe_valu(0, 10, None, None) == _lib.MSSM_ERR_INVALID_ARG
