@@ -66,7 +66,7 @@ VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 VARIANTS = {"auto": 0, "rowserial": 1, "chunked": 2, "lookback": 3,
-            "ssd_recurrent": 4, "ssd_chunked": 5}
+            "ssd_recurrent": 4, "ssd_chunked": 5, "pairscan": 6, "pairscan2": 7}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 
 

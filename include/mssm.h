@@ -78,7 +78,11 @@ typedef enum {
     MSSM_VARIANT_CHUNKED = 2,   /* lanes over (row, n), L walked in chunks     */
     MSSM_VARIANT_LOOKBACK = 3,  /* L split across workgroups, decoupled carry  */
     MSSM_VARIANT_SSD_RECURRENT = 4,
-    MSSM_VARIANT_SSD_CHUNKED = 5
+    MSSM_VARIANT_SSD_CHUNKED = 5,
+    MSSM_VARIANT_PAIRSCAN = 6,  /* steps of a chunk split across lanes: pair
+                                   scan across rows, N <= 16, no prologue   */
+    MSSM_VARIANT_PAIRSCAN2 = 7  /* the same with two slices of waves per
+                                   chunk, combined through LDS               */
 } mssm_variant;
 
 /* Sizes of a selective-scan problem. */

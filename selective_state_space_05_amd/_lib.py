@@ -28,6 +28,8 @@ VARIANT_CHUNKED = 2
 VARIANT_LOOKBACK = 3
 VARIANT_SSD_RECURRENT = 4
 VARIANT_SSD_CHUNKED = 5
+VARIANT_PAIRSCAN = 6
+VARIANT_PAIRSCAN2 = 7
 
 MAX_DSTATE = 64
 DEVICE_LOOKBACK_TIMEOUT = 0x1   # mssm_device_status bit

@@ -119,6 +119,11 @@ int64_t scan_chunked_waves(const ScanArgs &a);
 bool scan_offsets_fit(const ScanArgs &a);
 bool scan_rows_vectorizable(const ScanArgs &a);
 
+// Steps of each chunk split across the lanes of the workgroup (a scan of
+// (decay, state) pairs across rows and, with slices = 2, across waves).
+hipError_t launch_scan_pairscan(const ScanArgs &a, hipStream_t stream, int slices);
+bool scan_pairscan_supported(const ScanArgs &a);
+
 // Chunk-parallel variant; allocates its look-back scratch stream-ordered.
 hipError_t launch_scan_lookback(const ScanArgs &a, hipStream_t stream);
 bool scan_lookback_supported(const ScanArgs &a);

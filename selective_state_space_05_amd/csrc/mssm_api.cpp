@@ -209,6 +209,13 @@ mssm_status scan_fwd(const void *u, const void *delta, const float *delta_bias, 
                 e = mssm::launch_scan_lookback(a, st);
             }
             break;
+        case MSSM_VARIANT_PAIRSCAN:
+        case MSSM_VARIANT_PAIRSCAN2:
+            if (!mssm::scan_pairscan_supported(a))
+                return fail(MSSM_ERR_UNSUPPORTED, "pair-scan variant does not support this shape "
+                            "(N <= 16, no convolution prologue)");
+            e = mssm::launch_scan_pairscan(a, st, v == MSSM_VARIANT_PAIRSCAN2 ? 2 : 1);
+            break;
         default:
             return fail(MSSM_ERR_UNSUPPORTED, "variant %d does not apply to the selective scan",
                         static_cast<int>(v));

@@ -137,10 +137,72 @@ def test_scan_tiny_workload_as_stated(dev, variant):
     gates.check_state(h, ho, p.io, "h_last")
 
 
+PAIR_VARIANTS = [_lib.VARIANT_PAIRSCAN, _lib.VARIANT_PAIRSCAN2]
+
+
+@pytest.mark.parametrize("variant", PAIR_VARIANTS)
+@pytest.mark.parametrize("case", [c for c in SMALL_CASES if c[3] <= 16] + [
+    (2, 64 * 5 + 64, 16, 16, "f32", "per_channel", True, True),   # whole chunks only
+    (1, 64 * 3 + 17, 48, 16, "bf16", "scalar", True, True),       # three channel groups, tail
+    (1, 1000, 16, 9, "f32", "scalar", False, False),              # no optional inputs
+])
+def test_scan_pairscan_small_full_compare(dev, variant, case):
+    """The pair-scan variants (steps of each chunk split across lanes) on
+    every small case they support (N <= 16), element by element."""
+    batch, L, dim, N, io, bias, gate, skip = case
+    p = scan_problem(batch, L, dim, N, io, 1000 + L + dim, bias, gate, skip)
+    announce("scan variant=%d %s" % (variant, case))
+    x = inputs.scan_inputs(p)
+    y, h = run_scan(scan_to_dev(x, io, dev), variant)
+    yo, ho = oracle.selective_scan(x["u"], x["delta"], x["A"], x["B"], x["C"],
+                                   x["D"], x["z"], x["delta_bias"])
+    gates.check(y, yo, io, "y")
+    gates.check_state(h, ho, io, "h_last")
+
+
+@pytest.mark.parametrize("variant", PAIR_VARIANTS)
+def test_scan_pairscan_from_initial_state(dev, variant):
+    p = scan_problem(2, 777, 24, 16, "bf16", 71, bias="per_channel")
+    announce("scan variant=%d from h0" % variant)
+    x = inputs.scan_inputs(p)
+    h0 = inputs.initial_state((2, 24, 16), 72)
+    t = scan_to_dev(x, "bf16", dev)
+    import selective_state_space_05_amd as mssm
+    from selective_state_space_05_amd.api import forced_variant
+    with forced_variant(variant):
+        y, h = mssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"],
+                                       t["delta_bias"], h0=torch.from_numpy(h0).to(dev))
+    torch.cuda.synchronize()
+    yo, ho = oracle.selective_scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"],
+                                   x["delta_bias"], h0=h0)
+    gates.check(y.float().cpu().numpy().astype(np.float64), yo, "bf16", "y")
+    gates.check_state(h.cpu().numpy().astype(np.float64), ho, "bf16", "h_last")
+
+
+@pytest.mark.parametrize("variant", PAIR_VARIANTS)
+def test_scan_pairscan_deterministic(dev, variant):
+    p = scan_problem(2, 3000, 40, 16, "bf16", 73)
+    t = scan_to_dev(inputs.scan_inputs(p), "bf16", dev)
+    announce("scan variant=%d determinism" % variant)
+    y1, h1 = run_scan(t, variant)
+    y2, h2 = run_scan(t, variant)
+    assert np.array_equal(y1, y2) and np.array_equal(h1, h2)
+
+
+def test_scan_pairscan_rejects_large_state(dev):
+    import selective_state_space_05_amd as mssm
+    from selective_state_space_05_amd.api import MssmError, forced_variant
+    p = scan_problem(1, 256, 16, 32, "f32", 74)
+    t = scan_to_dev(inputs.scan_inputs(p), "f32", dev)
+    with forced_variant(_lib.VARIANT_PAIRSCAN):
+        with pytest.raises(MssmError):
+            mssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"])
+
+
 FULL = [inputs.MAMBA_130M, inputs.MAMBA_2_8B, inputs.MILLION]
 
 
-@pytest.mark.parametrize("variant", [_lib.VARIANT_AUTO] + SCAN_VARIANTS)
+@pytest.mark.parametrize("variant", [_lib.VARIANT_AUTO] + SCAN_VARIANTS + PAIR_VARIANTS)
 @pytest.mark.parametrize("p", FULL, ids=[q.name for q in FULL])
 def test_scan_full_size_sampled_rows(dev, variant, p):
     _sampled(p, variant, dev)
