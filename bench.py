@@ -123,18 +123,21 @@ def ssd_flops(p, chunk: int = 256) -> float:
 # summary is tied to their hash, so a change to those kernels (and only to
 # those) retires it.
 KERNEL_SOURCES = {
-    "scan": ("device_math.h", "scan_core.h", "scan_chunked.hip", "scan_lookback.hip",
-             "scan_rowserial.hip"),
+    "scan_chunked": ("device_math.h", "scan_core.h", "scan_chunked.hip"),
+    "scan_lookback": ("device_math.h", "scan_core.h", "scan_lookback.hip"),
     "ssd": ("device_math.h", "ssd_chunked.hip", "ssd_recurrent.hip"),
     "step": ("device_math.h", "state_update.hip"),
     "bwd": ("device_math.h", "scan_bwd_rowserial.hip"),
 }
+# the scan workloads whose AUTO variant is the look-back kernel (few channels,
+# very long rows); the others take the chunked kernel
+LOOKBACK_WORKLOADS = ("million_step_bf16",)
 
 
 def workload_family(workload: str) -> str:
     from selective_state_space_05_amd import inputs
     if workload in inputs.SCAN_PROBLEMS:
-        return "scan"
+        return "scan_lookback" if workload in LOOKBACK_WORKLOADS else "scan_chunked"
     if workload in inputs.SSD_PROBLEMS:
         return "ssd"
     if workload in inputs.STEP_PROBLEMS:
