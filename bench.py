@@ -582,6 +582,23 @@ def bwd_ops(p) -> dict:
             "rcp": rows_steps * (1 + g)}
 
 
+def bwd_min_traffic_bytes(p) -> int:
+    """Every input of the backward read once and every gradient written once:
+    u, delta, dy (and z) in the I/O dtype, B and C, A, D, the bias and
+    dh_last; du, ddelta (and dz) float32 like u, dB and dC float32 like B,
+    dA, dD, the bias gradient and dh0."""
+    s = 2 if p.io == "bf16" else 4
+    rows_l = p.batch * p.dim * p.seqlen
+    bc_l = p.batch * p.dstate * p.seqlen
+    nact = 4 if p.gate else 3
+    reads = nact * rows_l * s + 2 * bc_l * s + 4 * p.dim * p.dstate
+    reads += 4 * p.dim * ((1 if p.skip else 0) + (1 if p.bias else 0))
+    reads += 4 * p.batch * p.dim * p.dstate                     # dh_last
+    writes = (nact - 1) * rows_l * 4 + 2 * bc_l * 4 + 4 * p.dim * p.dstate
+    writes += 4 * p.dim * 2 + 4 * p.batch * p.dim * p.dstate    # dD, dbias, dh0
+    return reads + writes
+
+
 class BwdBench(ScanBench):
     """Backward of the selective scan (mssm_selective_scan_bwd)."""
 
@@ -602,7 +619,10 @@ class BwdBench(ScanBench):
                                                  dh_last=t["dh_last"])
 
     def roofline(self, sec, peaks):
-        return alu_roofline(bwd_ops(self.p), self.p.min_traffic_bytes(), sec, peaks)
+        return alu_roofline(bwd_ops(self.p), bwd_min_traffic_bytes(self.p), sec, peaks)
+
+    def min_traffic_bytes(self):
+        return bwd_min_traffic_bytes(self.p)
 
     def _row_oracle(self, b, d, nthreads=0):
         from oracle import oracle
@@ -799,7 +819,7 @@ def main():
             args.workload, sorted(inputs.SCAN_PROBLEMS) + sorted(inputs.SSD_PROBLEMS) +
             sorted(inputs.STEP_PROBLEMS) + sorted(inputs.BWD_PROBLEMS)))
 
-    footprint = p.min_traffic_bytes()
+    footprint = wb.min_traffic_bytes() if hasattr(wb, "min_traffic_bytes") else p.min_traffic_bytes()
     rotate = args.rotate or max(1, min(4, -(-(1 << 30) // footprint)))
     sets = [wb.upload() for _ in range(rotate)]
     torch.cuda.synchronize()

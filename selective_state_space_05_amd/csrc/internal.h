@@ -142,6 +142,11 @@ hipError_t device_status(uint32_t *bits, bool clear);
 // stored states.
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t stream);
 bool scan_bwd_supported(const BwdArgs &a);
+// Backward with the chunked forward's decomposition (N <= 16): lanes over
+// (channel, state element), states stored every 32 steps, per-workgroup
+// partial sums of dB and dC; stream-ordered scratch.
+hipError_t launch_scan_bwd_chunked(const BwdArgs &a, hipStream_t stream);
+bool scan_bwd_chunked_supported(const BwdArgs &a);
 
 // Measurement probes (include/mssm_probes.h); arguments already checked.
 hipError_t launch_probe_copy(const void *src, void *dst, int64_t bytes, hipStream_t stream);

@@ -444,12 +444,26 @@ mssm_status mssm_selective_scan_bwd(const void *u, const void *delta, const floa
     mssm::BwdArgs a{u, delta, delta_bias, A, B, C, D, z, h0, dy, dh_last, du, ddelta, ddelta_bias,
                     dA, dB, dC, dD, dz, dh0, batch, L, dim, N,
                     dtypes.io == MSSM_F32 ? mssm::IO_F32 : mssm::IO_BF16};
-    if (!mssm::scan_bwd_supported(a))
-        return fail(MSSM_ERR_UNSUPPORTED, "backward does not support this shape");
+    // AUTO: the chunked backward where it applies (N <= 16), else the
+    // row-serial one; either can be forced
+    mssm_variant v = g_forced;
+    if (v == MSSM_VARIANT_AUTO)
+        v = mssm::scan_bwd_chunked_supported(a) ? MSSM_VARIANT_CHUNKED : MSSM_VARIANT_ROWSERIAL;
+    if (v == MSSM_VARIANT_CHUNKED) {
+        if (!mssm::scan_bwd_chunked_supported(a))
+            return fail(MSSM_ERR_UNSUPPORTED, "chunked backward needs N <= 16");
+    } else if (v == MSSM_VARIANT_ROWSERIAL) {
+        if (!mssm::scan_bwd_supported(a))
+            return fail(MSSM_ERR_UNSUPPORTED, "backward does not support this shape");
+    } else {
+        return fail(MSSM_ERR_UNSUPPORTED, "variant %d does not apply to the backward",
+                    static_cast<int>(v));
+    }
     hipError_t e = zero_sums();
-    if (e == hipSuccess) e = mssm::launch_scan_bwd(a, st);
+    if (e == hipSuccess)
+        e = v == MSSM_VARIANT_CHUNKED ? mssm::launch_scan_bwd_chunked(a, st) : mssm::launch_scan_bwd(a, st);
     if (e != hipSuccess) return hip_fail(e, "selective-scan backward launch");
-    g_last_variant = MSSM_VARIANT_ROWSERIAL;
+    g_last_variant = v;
     return MSSM_OK;
 }
 
