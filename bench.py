@@ -127,7 +127,7 @@ KERNEL_SOURCES = {
     "scan_lookback": ("device_math.h", "scan_core.h", "scan_lookback.hip"),
     "ssd": ("device_math.h", "ssd_chunked.hip", "ssd_recurrent.hip"),
     "step": ("device_math.h", "state_update.hip"),
-    "bwd": ("device_math.h", "scan_bwd_rowserial.hip"),
+    "bwd": ("device_math.h", "scan_core.h", "scan_bwd_chunked.hip"),
 }
 # the scan workloads whose AUTO variant is the look-back kernel (few channels,
 # very long rows); the others take the chunked kernel

@@ -263,6 +263,27 @@ struct BwdWalker {
         *reinterpret_cast<float2 *>(sm.ds + at) = make_float2(dsv[0], dsv[1]);
     }
 
+    // The same for the 16 steps of half `half` of the chunk: lane (row r,
+    // column j) writes the four-row sums of steps 16 half + 4 r .. + 3
+    // (v_permlane32_swap pairs rows {0,1}/{2,3} for steps k, k + 8, then
+    // v_permlane16_swap rows 0/1 and 2/3 for k, k + 4).
+    __device__ void reduce_store16(const float (&p)[16], BwdSmem &sm, int q, int half) const {
+        float z[8], s[4];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[k]), __float_as_uint(p[k + 8]),
+                                                            false, false);
+            z[k] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(z[k]), __float_as_uint(z[k + 4]),
+                                                            false, false);
+            s[k] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+        }
+        *reinterpret_cast<float4 *>(sm.p[q][w] + j * kPitch + 16 * half + 4 * r) = make_float4(s[0], s[1], s[2], s[3]);
+    }
+
     // The wave's four state rows of p summed (cross-row swaps), then to LDS
     // slot q: lane (row r, column j) writes steps 8 r .. 8 r + 7.
     __device__ void reduce_store(const float (&p)[kT], BwdSmem &sm, int q) const {
@@ -404,25 +425,28 @@ __global__ __launch_bounds__(256, 2) void scan_bwd_chunked_kernel(BwdArgs a, con
             }
             if (GATE) bw.reduce_store(pc, sm, 0);
         }
-        // reverse walk: steps 31 .. 16, the tile of channel sums, 15 .. 0
-        float pu[kT], pq[kT];
+        // reverse walk: steps 31 .. 16, the tile of channel sums, 15 .. 0;
+        // the per-step scalars are read from LDS again (fewer live registers)
+        float pu[kHalf], pq[kHalf];
         auto rev_step = [&](auto s_, auto qq_) {
             constexpr int S = decltype(s_)::value;      // lane of the row broadcast
             constexpr int QQ = decltype(qq_)::value;    // half of the chunk
             constexpr int s = 16 * QQ + S;
             const int qq = QQ;
             const float dsv = sm.ds[bw.j * kPitch + s];
+            const float dlv = sm.dl[bw.j * kPitch + s];
+            const float duv = sm.du[bw.j * kPitch + s];
             const float dh = fmaf(row_bcast<S>(ccv[qq]), dsv, g);
             float hp;
             if constexpr (s > 0) hp = hs[s - 1];
             else hp = hstart;
             sm.cb[0][bw.n * kCbN + S * kCbT + bw.j] = dsv * hs[s];       // dC term
-            sm.cb[1][bw.n * kCbN + S * kCbT + bw.j] = dh * dus[s];       // dB term
-            pu[s] = row_bcast<S>(cbv[qq]) * dh;
+            sm.cb[1][bw.n * kCbN + S * kCbT + bw.j] = dh * duv;          // dB term
+            pu[S] = row_bcast<S>(cbv[qq]) * dh;
             g = as[s] * dh;
             const float q = g * hp;
-            dA = fmaf(q, dls[s], dA);
-            pq[s] = q * bw.Aval;
+            dA = fmaf(q, dlv, dA);
+            pq[S] = q * bw.Aval;
         };
         auto rev_half = [&](auto qq_) {
 #define MSSM_REV(S) rev_step(std::integral_constant<int, S>{}, qq_);
@@ -432,12 +456,14 @@ __global__ __launch_bounds__(256, 2) void scan_bwd_chunked_kernel(BwdArgs a, con
 #undef MSSM_REV
         };
         rev_half(std::integral_constant<int, 1>{});
+        bw.reduce_store16(pu, sm, 1, 1);
+        bw.reduce_store16(pq, sm, 2, 1);
         __syncthreads();
         if (want_bc) BW::channel_sums(t0, 1, L, sm, pg);
         __syncthreads();
         rev_half(std::integral_constant<int, 0>{});
-        bw.reduce_store(pu, sm, 1);
-        bw.reduce_store(pq, sm, 2);
+        bw.reduce_store16(pu, sm, 1, 0);
+        bw.reduce_store16(pq, sm, 2, 0);
         __syncthreads();
         bw.owner_outputs(t0, own, sm, a, orow, dD, dbias);
         if (want_bc) BW::channel_sums(t0, 0, L, sm, pg);
