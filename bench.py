@@ -24,9 +24,10 @@ Prints one JSON line:
   parity              sampled-row comparison with the oracle
 
 Timing: an untimed ramp (steps until the per-launch time settles, at most
---ramp-s seconds), W untimed warmup steps, then K steps with an event
-recorded on the library's stream before the first and after every step:
-ms_per_step is their mean; "timing" adds the per-launch median, min and max.
+--ramp-s seconds), W untimed warmup steps, then K steps between two events
+recorded on the library's stream: ms_per_step is their mean.  A second pass
+of K steps with an event after every step gives "timing"'s per-launch
+median, min and max.
 After the timed steps the library's probes (include/mssm_probes.h) measure
 the copy ceiling and the fma / 2^x / log2 x / 1/x issue rates; the roofline
 charges each transcendental its measured cost and reports
@@ -838,8 +839,20 @@ def main():
             wb.step(sets[i % rotate])
         torch.cuda.synchronize()
         used = VARIANT_NAMES.get(api.last_variant(), str(api.last_variant()))
-        # one event before the first step and one after every step: the K
-        # per-launch durations and their sum
+        # the K timed steps between one event pair: ms_per_step
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            wb.step(sets[i % rotate])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        total_ms = e0.elapsed_time(e1)
+        # then K more with an event after every step, for the per-launch
+        # median / min / max (an event record per step slows the host loop,
+        # which for a kernel of a few tens of us shows up as idle gaps, so
+        # these are not the timed steps)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         torch.cuda.synchronize()
         ev[0].record(stream)
@@ -847,7 +860,6 @@ def main():
             wb.step(sets[i % rotate])
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
-    total_ms = ev[0].elapsed_time(ev[-1])
     per_launch = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
     smi_after = amd_smi_snapshot()
     ms_step = total_ms / args.steps
@@ -883,6 +895,7 @@ def main():
         "config": cfg,
         "timing": {"mean_us": ms_step * 1e3, "median_us": per_launch[len(per_launch) // 2] * 1e3,
                    "min_us": per_launch[0] * 1e3, "max_us": per_launch[-1] * 1e3,
+                   "per_launch_mean_us": sum(per_launch) / len(per_launch) * 1e3,
                    "launches": args.steps, "ramp": ramp},
         "hbm": {"min_traffic_bytes": footprint, "achieved_gbs": hbm_gbs,
                 "peak_gbs": HBM_PEAK_GBS, "frac": hbm_gbs / HBM_PEAK_GBS},
