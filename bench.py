@@ -180,7 +180,7 @@ def summarize_counters(workload: str, fetch_csv: str, write_csv: str, probe_mib:
     read and written) divided by what the same counter reads, per dispatch,
     for the copy kernel.  The library's kernels (mssm namespace) are summed
     over all their dispatches and divided by the number of steps the run
-    made (warmup + timed).
+    made (warmup + timed + the per-launch pass).
     """
     import csv
 
@@ -781,8 +781,9 @@ def main():
     if args.counters:
         if args.copy_probe_mib <= 0:
             raise SystemExit("--counters needs the --copy-probe-mib the runs used")
+        # the runs made W warm-up steps, K timed steps and K per-launch steps
         res = summarize_counters(args.workload, args.counters[0], args.counters[1],
-                                 args.copy_probe_mib, args.steps + args.warmup)
+                                 args.copy_probe_mib, 2 * args.steps + args.warmup)
         path = os.path.join(ROOT, "profiles", "counters_%s.json" % args.workload)
         with open(path, "w") as f:
             json.dump(res, f, indent=1)
