@@ -38,6 +38,7 @@
 // dA, dD and the bias gradient are added atomically once per lane or owner,
 // so their last bits depend on the order.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "internal.h"
@@ -60,56 +61,7 @@ constexpr int kCbT = 20;                // floats per step in the channel-sum ti
 constexpr int kCbN = kHalf * kCbT + 4;  // floats per state element in the tile (bank offset)
 
 // ---------------------------------------------------------------------------
-// 1. checkpoints: the state at the start of every chunk
-// ---------------------------------------------------------------------------
-template <typename T, bool VEC>
-__global__ __launch_bounds__(256) void scan_bwd_ckpt_kernel(BwdArgs a, float *__restrict__ ck, int nch,
-                                                             int groups_per_batch) {
-    using Wk = core::Walker<T, 4, 1, false, VEC, false>;
-    __shared__ core::Smem<4> sm;
-    const int grp = blockIdx.x;
-    const int64_t b = grp / groups_per_batch;
-    const int d0 = (grp - static_cast<int>(b) * groups_per_batch) * kCh;
-    const int dim = static_cast<int>(a.dim), N = static_cast<int>(a.N);
-    Wk wk;
-    wk.init(static_cast<const T *>(a.u), static_cast<const T *>(a.delta), a.delta_bias, a.A,
-            static_cast<const T *>(a.B), static_cast<const T *>(a.C), nullptr, nullptr, nullptr, a.L, dim,
-            N, b, d0);
-    const int dS = min(d0 + wk.j, dim - 1);
-    float h[1];
-    h[0] = (a.h0 && wk.nok[0]) ? a.h0[(b * dim + dS) * static_cast<int64_t>(N) + wk.prow] : 0.0f;
-    float *cg = ck + static_cast<int64_t>(grp) * nch * 256 + threadIdx.x;
-    const int L = static_cast<int>(a.L);
-    const int nfull = L / kT;
-    typename Wk::In x0, x1;
-    wk.template load<false>(0, x0);
-    int c = 0;
-    // two input sets used in turn, loads one chunk ahead (as the forward's
-    // state-only walk); chunk c's state is stored before the chunk
-    for (; c + 1 < nfull; c += 2) {
-        wk.template load<false>((c + 1) * kT, x1);
-        cg[static_cast<int64_t>(c) * 256] = h[0];
-        wk.template state_chunk<true>(c * kT, L, x0, h, sm, 0);
-        wk.template load<false>((c + 2) * kT, x0);
-        cg[static_cast<int64_t>(c + 1) * 256] = h[0];
-        wk.template state_chunk<true>((c + 1) * kT, L, x1, h, sm, 1);
-    }
-    if (c < nfull) {
-        wk.template load<false>((c + 1) * kT, x1);
-        cg[static_cast<int64_t>(c) * 256] = h[0];
-        wk.template state_chunk<true>(c * kT, L, x0, h, sm, 0);
-        if (c + 1 < nch) {
-            cg[static_cast<int64_t>(c + 1) * 256] = h[0];
-            wk.template state_chunk<false>((c + 1) * kT, L, x1, h, sm, 1);
-        }
-    } else if (c < nch) {
-        cg[static_cast<int64_t>(c) * 256] = h[0];
-        wk.template state_chunk<false>(c * kT, L, x0, h, sm, 0);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// 2. the reverse walk
+// The walker of the reverse walk (shared with the adjoint-only walk)
 // ---------------------------------------------------------------------------
 struct BwdSmem {
     float dl[kCh * kPitch], du[kCh * kPitch], ds[kCh * kPitch];  // per (channel, step)
@@ -225,15 +177,17 @@ struct BwdWalker {
         else return __uint_as_float(static_cast<uint32_t>(v) << 16);
     }
 
-    // Owner: the chunk's per-step scalars.  Steps past L and channels past the
-    // last one get dl = dl*u = ds = 0, so they contribute nothing.
-    __device__ void owner_scalars(int t0, const In &in, BwdSmem &sm, Own &o) const {
+    // Owner: the per-step scalars of its OS steps.  Steps past L and
+    // channels past the last one get dl = dl*u = ds = 0, so they contribute
+    // nothing.  The reverse walk and the adjoint-only walk both take them
+    // from here, so the two compute identical values.
+    __device__ void step_scalars(int t0, const In &in, float (&dl)[OS], float (&du)[OS], float (&dsv)[OS],
+                                 Own &o) const {
         float u[OS], dr[OS], dy[OS], zz[OS];
         Pack<T, OS>::unpack(in.ru, u);
         Pack<T, OS>::unpack(in.rd, dr);
         Pack<T, OS>::unpack(in.ry, dy);
         if (GATE) Pack<T, OS>::unpack(in.rz, zz);
-        float dl[OS], du[OS], dsv[OS];
 #pragma unroll
         for (int i = 0; i < OS; ++i) {
             const bool ok_t = ochok && t0 + OS * ok + i < L;
@@ -257,9 +211,27 @@ struct BwdWalker {
             o.dl[i] = dl[i];
             o.ok[i] = ok_t;
         }
+    }
+
+    // Owner: the chunk's per-step scalars published in LDS, and kept for its
+    // outputs.
+    __device__ void owner_scalars(int t0, const In &in, BwdSmem &sm, Own &o) const {
+        float dl[OS], du[OS], dsv[OS];
+        step_scalars(t0, in, dl, du, dsv, o);
         const int at = oc * kPitch + OS * ok;
         *reinterpret_cast<float2 *>(sm.dl + at) = make_float2(dl[0], dl[1]);
         *reinterpret_cast<float2 *>(sm.du + at) = make_float2(du[0], du[1]);
+        *reinterpret_cast<float2 *>(sm.ds + at) = make_float2(dsv[0], dsv[1]);
+    }
+
+    // Owner, adjoint-only walk: dl and ds only.
+    template <typename Sm>
+    __device__ void owner_adjoint(int t0, const In &in, Sm &sm) const {
+        float dl[OS], du[OS], dsv[OS];
+        Own o;
+        step_scalars(t0, in, dl, du, dsv, o);
+        const int at = oc * kPitch + OS * ok;
+        *reinterpret_cast<float2 *>(sm.dl + at) = make_float2(dl[0], dl[1]);
         *reinterpret_cast<float2 *>(sm.ds + at) = make_float2(dsv[0], dsv[1]);
     }
 
@@ -354,12 +326,178 @@ struct BwdWalker {
     }
 };
 
+// ---------------------------------------------------------------------------
+// 1. checkpoints: the state at the start of every chunk, and the adjoint
+//    carries where the reverse walk of a group is cut into parts
+// ---------------------------------------------------------------------------
+// LDS of the adjoint-only walk: the chunk's dl and ds, double-buffered so a
+// chunk needs one barrier.
+struct AdjSmem {
+    float dl[2][kCh * kPitch], ds[2][kCh * kPitch];
+};
+struct AdjBuf {
+    float *dl, *ds;
+};
+union CkptSmem {
+    core::Smem<4> walk;
+    AdjSmem adj;
+};
+
+// How the reverse walk of the last groups is cut: the first n_whole groups
+// are walked whole; each of the others is cut into `parts` ranges of whole
+// chunks, part p covering chunks [p nch / parts, (p + 1) nch / parts).
+struct BwdSplit {
+    int n_whole, parts;
+};
+
+// Adjoint-only walk of group grp from the end down to the end of its first
+// part: per chunk, the owners' dl and ds, then per lane, in the reverse
+// walk's order and with its arithmetic,
+//   dh = ds C + g,   g <- exp(dl A) dh,
+// so that g at each cut equals, bit for bit, the carry the whole walk would
+// reach there.  out[p * 256 + thread] receives the carry entering part p
+// (p < parts - 1) from the parts after it.
+template <typename T, bool GATE, bool VEC>
+__device__ void adjoint_walk(const BwdArgs &a, int grp, int groups_per_batch, int nch, int parts,
+                             float *__restrict__ out, AdjSmem &sm) {
+    using BW = BwdWalker<T, GATE, VEC>;
+    const int64_t b = grp / groups_per_batch;
+    const int d0 = (grp - static_cast<int>(b) * groups_per_batch) * kCh;
+    BW bw;
+    bw.init(a, b, d0);
+    const int L = bw.L;
+    const int N = static_cast<int>(a.N);
+    float g = (a.dh_last && bw.nok && bw.chok)
+                  ? a.dh_last[(b * a.dim + d0 + bw.j) * static_cast<int64_t>(N) + bw.n]
+                  : 0.0f;
+    const int c_stop = nch / parts;   // the first part's end
+    typename BW::In xa, xb;
+    bw.load((nch - 1) * kT, xa);
+    // (a buffer is rewritten two chunks after it was read, with this
+    // chunk's barrier between)
+    auto chunk = [&](int k, typename BW::In &cur, typename BW::In &nxt) {
+        const int t0 = k * kT;
+        if (k > c_stop) bw.load(t0 - kT, nxt);
+        AdjBuf buf{sm.dl[k & 1], sm.ds[k & 1]};
+        bw.owner_adjoint(t0, cur, buf);
+        __syncthreads();
+        float ccv[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const bool tok = t0 + 16 * q + bw.j < L;
+            ccv[q] = tok ? BW::to_f32(cur.rc[q]) : 0.0f;
+        }
+        const float4 *pdl = reinterpret_cast<const float4 *>(buf.dl + bw.j * kPitch);
+        const float4 *pds = reinterpret_cast<const float4 *>(buf.ds + bw.j * kPitch);
+#pragma unroll
+        for (int qq = 1; qq >= 0; --qq) {
+            float dlh[16], dsh[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 x = pdl[4 * qq + q], y = pds[4 * qq + q];
+                dlh[4 * q] = x.x; dlh[4 * q + 1] = x.y; dlh[4 * q + 2] = x.z; dlh[4 * q + 3] = x.w;
+                dsh[4 * q] = y.x; dsh[4 * q + 1] = y.y; dsh[4 * q + 2] = y.z; dsh[4 * q + 3] = y.w;
+            }
+#define MSSM_ADJ(S)                                                                    \
+    {                                                                                  \
+        const float av = fast_exp2(dlh[S] * bw.A2);                                    \
+        const float dh = fmaf(row_bcast<S>(ccv[qq]), dsh[S], g);                       \
+        g = av * dh;                                                                   \
+    }
+            MSSM_ADJ(15) MSSM_ADJ(14) MSSM_ADJ(13) MSSM_ADJ(12) MSSM_ADJ(11) MSSM_ADJ(10)
+            MSSM_ADJ(9) MSSM_ADJ(8) MSSM_ADJ(7) MSSM_ADJ(6) MSSM_ADJ(5) MSSM_ADJ(4)
+            MSSM_ADJ(3) MSSM_ADJ(2) MSSM_ADJ(1) MSSM_ADJ(0)
+#undef MSSM_ADJ
+        }
+        for (int p = 0; p + 1 < parts; ++p)
+            if (k == (p + 1) * nch / parts) out[p * 256 + threadIdx.x] = g;
+    };
+    int k = nch - 1;
+    for (; k >= c_stop + 1; k -= 2) {
+        chunk(k, xa, xb);
+        chunk(k - 1, xb, xa);
+    }
+    if (k == c_stop) chunk(k, xa, xb);
+}
+
+// Workgroups [0, groups) store the checkpoints of their group; workgroup
+// groups + i walks the adjoint carries of group split.n_whole + i.
+template <typename T, bool GATE, bool VEC>
+__global__ __launch_bounds__(256) void scan_bwd_ckpt_kernel(BwdArgs a, float *__restrict__ ck, int nch,
+                                                             int groups_per_batch, int groups, BwdSplit split,
+                                                             float *__restrict__ adj) {
+    using Wk = core::Walker<T, 4, 1, false, VEC, false>;
+    __shared__ CkptSmem smu;
+    if (static_cast<int>(blockIdx.x) >= groups) {
+        const int i = static_cast<int>(blockIdx.x) - groups;
+        adjoint_walk<T, GATE, VEC>(a, split.n_whole + i, groups_per_batch, nch, split.parts,
+                                   adj + static_cast<int64_t>(i) * (split.parts - 1) * 256, smu.adj);
+        return;
+    }
+    core::Smem<4> &sm = smu.walk;
+    const int grp = blockIdx.x;
+    const int64_t b = grp / groups_per_batch;
+    const int d0 = (grp - static_cast<int>(b) * groups_per_batch) * kCh;
+    const int dim = static_cast<int>(a.dim), N = static_cast<int>(a.N);
+    Wk wk;
+    wk.init(static_cast<const T *>(a.u), static_cast<const T *>(a.delta), a.delta_bias, a.A,
+            static_cast<const T *>(a.B), static_cast<const T *>(a.C), nullptr, nullptr, nullptr, a.L, dim,
+            N, b, d0);
+    const int dS = min(d0 + wk.j, dim - 1);
+    float h[1];
+    h[0] = (a.h0 && wk.nok[0]) ? a.h0[(b * dim + dS) * static_cast<int64_t>(N) + wk.prow] : 0.0f;
+    float *cg = ck + static_cast<int64_t>(grp) * nch * 256 + threadIdx.x;
+    const int L = static_cast<int>(a.L);
+    const int nfull = L / kT;
+    typename Wk::In x0, x1;
+    wk.template load<false>(0, x0);
+    int c = 0;
+    // two input sets used in turn, loads one chunk ahead (as the forward's
+    // state-only walk); chunk c's state is stored before the chunk
+    for (; c + 1 < nfull; c += 2) {
+        wk.template load<false>((c + 1) * kT, x1);
+        cg[static_cast<int64_t>(c) * 256] = h[0];
+        wk.template state_chunk<true>(c * kT, L, x0, h, sm, 0);
+        wk.template load<false>((c + 2) * kT, x0);
+        cg[static_cast<int64_t>(c + 1) * 256] = h[0];
+        wk.template state_chunk<true>((c + 1) * kT, L, x1, h, sm, 1);
+    }
+    if (c < nfull) {
+        wk.template load<false>((c + 1) * kT, x1);
+        cg[static_cast<int64_t>(c) * 256] = h[0];
+        wk.template state_chunk<true>(c * kT, L, x0, h, sm, 0);
+        if (c + 1 < nch) {
+            cg[static_cast<int64_t>(c + 1) * 256] = h[0];
+            wk.template state_chunk<false>((c + 1) * kT, L, x1, h, sm, 1);
+        }
+    } else if (c < nch) {
+        cg[static_cast<int64_t>(c) * 256] = h[0];
+        wk.template state_chunk<false>(c * kT, L, x0, h, sm, 0);
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// 2. the reverse walk
+// ---------------------------------------------------------------------------
 template <typename T, bool GATE, bool VEC>
 __global__ __launch_bounds__(256, 2) void scan_bwd_chunked_kernel(BwdArgs a, const float *__restrict__ ck, int nch,
-                                                                   int groups_per_batch, float *__restrict__ part) {
+                                                                   int groups_per_batch, float *__restrict__ part,
+                                                                   BwdSplit split, const float *__restrict__ adj) {
     using BW = BwdWalker<T, GATE, VEC>;
     __shared__ BwdSmem sm;
-    const int grp = blockIdx.x;
+    // Workgroups [0, n_whole) walk their group whole; the others walk part p
+    // of group n_whole + i, starting from the carry the adjoint-only walk
+    // stored for it (the last part from dh_last, as a whole group).
+    int grp = blockIdx.x, c_begin = 0, c_end = nch;
+    const float *g_in = nullptr;
+    if (grp >= split.n_whole) {
+        const int i = (grp - split.n_whole) / split.parts, pp = (grp - split.n_whole) % split.parts;
+        grp = split.n_whole + i;
+        c_begin = pp * nch / split.parts;
+        c_end = (pp + 1) * nch / split.parts;
+        if (pp + 1 < split.parts) g_in = adj + (static_cast<int64_t>(i) * (split.parts - 1) + pp) * 256;
+    }
     const int64_t b = grp / groups_per_batch;
     const int d0 = (grp - static_cast<int>(b) * groups_per_batch) * kCh;
     BW bw;
@@ -371,16 +509,17 @@ __global__ __launch_bounds__(256, 2) void scan_bwd_chunked_kernel(BwdArgs a, con
     const float *cg = ck + static_cast<int64_t>(grp) * nch * 256 + threadIdx.x;
     const int64_t orow = (b * a.dim + (d0 + bw.oc)) * a.L;   // owner's output row
     // carry g = a_{t+1} dh_{t+1}: dh_last at the end
-    float g = (a.dh_last && bw.nok && bw.chok)
-                  ? a.dh_last[(b * a.dim + d0 + bw.j) * static_cast<int64_t>(N) + bw.n]
-                  : 0.0f;
+    float g = g_in ? g_in[threadIdx.x]
+                   : ((a.dh_last && bw.nok && bw.chok)
+                          ? a.dh_last[(b * a.dim + d0 + bw.j) * static_cast<int64_t>(N) + bw.n]
+                          : 0.0f);
     float dA = 0.0f, dD = 0.0f, dbias = 0.0f;
 
     typename BW::In xa, xb;
-    bw.load((nch - 1) * kT, xa);
+    bw.load((c_end - 1) * kT, xa);
     auto chunk = [&](int k, typename BW::In &cur, typename BW::In &nxt) {
         const int t0 = k * kT;
-        if (k > 0) bw.load(t0 - kT, nxt);
+        if (k > c_begin) bw.load(t0 - kT, nxt);
         typename BW::Own own;
         bw.owner_scalars(t0, cur, sm, own);
         __syncthreads();
@@ -470,16 +609,16 @@ __global__ __launch_bounds__(256, 2) void scan_bwd_chunked_kernel(BwdArgs a, con
         // (the next chunk's owners rewrite dl / du / ds after all of this
         // chunk's readers passed the barrier above)
     };
-    int k = nch - 1;
-    for (; k >= 1; k -= 2) {
+    int k = c_end - 1;
+    for (; k >= c_begin + 1; k -= 2) {
         chunk(k, xa, xb);
         chunk(k - 1, xb, xa);
     }
-    if (k == 0) chunk(0, xa, xb);
+    if (k == c_begin) chunk(k, xa, xb);
 
     if (bw.nok && bw.chok) {
         const int64_t d = d0 + bw.j;
-        if (a.dh0) a.dh0[(b * a.dim + d) * static_cast<int64_t>(N) + bw.n] = g;
+        if (a.dh0 && c_begin == 0) a.dh0[(b * a.dim + d) * static_cast<int64_t>(N) + bw.n] = g;
         if (a.dA) atomicAdd(a.dA + d * N + bw.n, dA);
     }
     if (bw.ochok) {
@@ -520,25 +659,66 @@ __global__ __launch_bounds__(256) void scan_bwd_chunked_bc_kernel(const float *_
     }
 }
 
+// Compute units of the current device, queried once per device (0 if the
+// query fails).
+int device_cus() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lk(mu);
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = -1;
+        cache[dev] = n;
+    }
+    return cache[dev] > 0 ? cache[dev] : 0;
+}
+
+// The reverse kernel holds two workgroups per compute unit (its registers
+// and LDS), so U units walk 2 U groups at a time.  When the last round is
+// partly empty (r = groups mod 2 U > 0, with at least one full round before
+// it), the last r groups are each cut into parts = min(4, 2 U / r) ranges,
+// which fill the last round with shorter work; every part is at least four
+// chunks long.
+BwdSplit plan_bwd_split(int64_t groups, int nch) {
+    BwdSplit sp{static_cast<int>(groups), 1};
+    const int cus = device_cus();
+    const int64_t slots = 2 * static_cast<int64_t>(cus);
+    if (cus <= 0 || groups <= slots) return sp;
+    const int64_t r = groups % slots;
+    if (r == 0) return sp;
+    const int parts = static_cast<int>(std::min<int64_t>(4, slots / r));
+    if (parts < 2 || nch < 4 * parts) return sp;
+    sp.n_whole = static_cast<int>(groups - r);
+    sp.parts = parts;
+    return sp;
+}
+
 template <typename T, bool GATE, bool VEC>
 hipError_t launch_typed(const BwdArgs &a, hipStream_t stream) {
     const int gpb = static_cast<int>((a.dim + kCh - 1) / kCh);
     const int64_t total = a.batch * gpb;
     const int nch = static_cast<int>((a.L + kT - 1) / kT);
     const bool want_bc = a.dB || a.dC;
+    const BwdSplit sp = plan_bwd_split(total, nch);
+    const int n_cut = static_cast<int>(total) - sp.n_whole;   // groups walked in parts
     const size_t ck_bytes = static_cast<size_t>(total) * nch * 256 * sizeof(float);
     const size_t part_bytes = want_bc ? static_cast<size_t>(total) * a.L * 32 * sizeof(float) : 0;
+    const size_t adj_bytes = static_cast<size_t>(n_cut) * (sp.parts - 1) * 256 * sizeof(float);
     void *mem = nullptr;
-    hipError_t e = hipMallocAsync(&mem, ck_bytes + part_bytes, stream);
+    hipError_t e = hipMallocAsync(&mem, ck_bytes + part_bytes + adj_bytes, stream);
     if (e != hipSuccess) return e;
     float *ck = static_cast<float *>(mem);
     float *part = want_bc ? reinterpret_cast<float *>(static_cast<char *>(mem) + ck_bytes) : nullptr;
-    hipLaunchKernelGGL((scan_bwd_ckpt_kernel<T, VEC>), dim3(static_cast<uint32_t>(total)), dim3(256), 0,
-                       stream, a, ck, nch, gpb);
+    float *adj = reinterpret_cast<float *>(static_cast<char *>(mem) + ck_bytes + part_bytes);
+    hipLaunchKernelGGL((scan_bwd_ckpt_kernel<T, GATE, VEC>), dim3(static_cast<uint32_t>(total + n_cut)), dim3(256),
+                       0, stream, a, ck, nch, gpb, static_cast<int>(total), sp, adj);
     e = hipGetLastError();
     if (e == hipSuccess) {
-        hipLaunchKernelGGL((scan_bwd_chunked_kernel<T, GATE, VEC>), dim3(static_cast<uint32_t>(total)),
-                           dim3(256), 0, stream, a, ck, nch, gpb, part);
+        const int64_t grid = sp.n_whole + static_cast<int64_t>(n_cut) * sp.parts;
+        hipLaunchKernelGGL((scan_bwd_chunked_kernel<T, GATE, VEC>), dim3(static_cast<uint32_t>(grid)),
+                           dim3(256), 0, stream, a, ck, nch, gpb, part, sp, adj);
         e = hipGetLastError();
     }
     if (e == hipSuccess && want_bc) {

@@ -134,3 +134,48 @@ def test_scan_backward_full_size():
     gates.check(got["du"], o["du"], f, "du")
     gates.check(got["ddelta"], o["ddelta"], f, "ddelta")
     gates.check(got["dz"], o["dz"], f, "dz")
+
+
+def test_scan_backward_split_walk_is_bitwise_whole(dev):
+    """On the Mamba-2.8B backward shape the grid of 640 (batch, 16-channel)
+    groups has more groups than the device holds at once, and the groups of
+    the partly empty last round are walked in parts, each starting from the
+    carry an adjoint-only walk stored for it.  Every (batch, channel) row's
+    du, ddelta, dz and dh0 must equal, bit for bit, those of calls on blocks
+    of 1024 channels of one batch (64 groups: never cut), with h0 and
+    dh_last given.  The summed gradients are compared to those calls' sums
+    with the float32 gates (their order of addition differs)."""
+    import selective_state_space_05_amd as mssm
+    p = inputs.BWD_PROBLEMS["mamba2.8b_layer_bwd_bf16"]
+    announce("scan backward split vs whole, workload=%s" % p.name)
+    x = inputs.scan_inputs(p)
+    gr = inputs.output_grads(p)
+    rng = np.random.default_rng(77)
+    h0 = (0.5 * rng.standard_normal((p.batch, p.dim, p.dstate))).astype(np.float32)
+    t = scan_to_dev({k: v for k, v in x.items() if k not in ("conv_w", "conv_b")}, p.io, dev)
+    dy = to_dev(gr["dy"], p.io, dev)
+    dhl = torch.from_numpy(gr["dh_last"]).to(dev)
+    h0d = torch.from_numpy(h0).to(dev)
+    full = mssm.selective_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], dy, D=t["D"], z=t["z"],
+                                   delta_bias=t["delta_bias"], h0=h0d, dh_last=dhl)
+    torch.cuda.synchronize()
+    blk = 1024
+    sums = {k: torch.zeros_like(full[k]) for k in ("dB", "dC")}
+    for b in range(p.batch):
+        for d0 in range(0, p.dim, blk):
+            d1 = min(p.dim, d0 + blk)
+            print("[gpu case] block batch %d channels %d..%d" % (b, d0, d1), flush=True)
+            sl = lambda v: v[b:b + 1, d0:d1].contiguous()
+            g = mssm.selective_scan_bwd(sl(t["u"]), sl(t["delta"]), t["A"][d0:d1].contiguous(),
+                                        t["B"][b:b + 1].contiguous(), t["C"][b:b + 1].contiguous(), sl(dy),
+                                        D=t["D"][d0:d1].contiguous(), z=sl(t["z"]),
+                                        delta_bias=t["delta_bias"][d0:d1].contiguous(), h0=sl(h0d),
+                                        dh_last=sl(dhl))
+            torch.cuda.synchronize()
+            for k in ("du", "ddelta", "dz", "dh0"):
+                assert torch.equal(g[k][0], full[k][b, d0:d1]), (k, b, d0)
+            sums["dB"][b] += g["dB"][0]
+            sums["dC"][b] += g["dC"][0]
+            del g
+    for k in ("dB", "dC"):
+        gates.check_state(f64(full[k]), f64(sums[k]), "f32", k)
