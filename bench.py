@@ -126,19 +126,27 @@ def ssd_flops(p, chunk: int = 256) -> float:
 KERNEL_SOURCES = {
     "scan_chunked": ("device_math.h", "scan_core.h", "scan_chunked.hip"),
     "scan_lookback": ("device_math.h", "scan_core.h", "scan_lookback.hip"),
+    "scan_pairscan": ("device_math.h", "scan_core.h", "scan_pairscan.hip"),
+    "scan_rowserial": ("device_math.h", "scan_rowserial.hip"),
     "ssd": ("device_math.h", "ssd_chunked.hip", "ssd_recurrent.hip"),
     "step": ("device_math.h", "state_update.hip"),
     "bwd": ("device_math.h", "scan_core.h", "scan_bwd_chunked.hip"),
 }
-# the scan workloads whose AUTO variant is the look-back kernel (few channels,
-# very long rows); the others take the chunked kernel
-LOOKBACK_WORKLOADS = ("million_step_bf16",)
+# the scan workloads whose AUTO variant is the look-back kernel (long rows
+# whose channels fill under four fifths of the SIMDs); the others take the
+# chunked kernel
+LOOKBACK_WORKLOADS = ("million_step_bf16", "mamba130m_layer_f32")
 
 
-def workload_family(workload: str) -> str:
+def workload_family(workload: str, used: str = None) -> str:
+    """The kernel family of a workload: of the variant a run used (as
+    api.last_variant() names it), else of its AUTO variant."""
     from selective_state_space_05_amd import inputs
     if workload in inputs.SCAN_PROBLEMS:
-        return "scan_lookback" if workload in LOOKBACK_WORKLOADS else "scan_chunked"
+        if used is None:
+            return "scan_lookback" if workload in LOOKBACK_WORKLOADS else "scan_chunked"
+        return {"lookback": "scan_lookback", "pairscan": "scan_pairscan", "pairscan2": "scan_pairscan",
+                "rowserial": "scan_rowserial"}.get(used, "scan_chunked")
     if workload in inputs.SSD_PROBLEMS:
         return "ssd"
     if workload in inputs.STEP_PROBLEMS:
@@ -873,7 +881,7 @@ def main():
 
     hbm_gbs = footprint / sec / 1e9
     roof = wb.roofline(sec, peaks)
-    sha = kernel_source_sha(workload_family(p.name))
+    sha = kernel_source_sha(workload_family(p.name, used if p.name in inputs.SCAN_PROBLEMS else None))
     roof["traffic"] = load_traffic(p.name, sha)
     roof["kernel_source_sha"] = sha
     cfg = wb.config()

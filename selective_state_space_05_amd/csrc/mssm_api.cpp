@@ -84,16 +84,19 @@ mssm_status check_dtypes(mssm_dtypes dt) {
 
 // Shape-based choice.  Short sequences take the row-serial walk (its single
 // lane per row has nothing to amortise).  Long sequences whose channels give
-// the chunked kernel fewer than 512 waves (half a wave per SIMD on the chip)
-// are cut into segments and take the look-back kernel; everything else takes
-// the chunked kernel, which walks each row in order.  The look-back kernel
-// walks every segment twice (state only, then with output), so it pays only
-// when the chunked grid leaves most compute units idle: measured on the
-// Mamba-130M layer (768 waves), the chunked kernel takes 248 us against
-// 298 us for the look-back kernel.
+// the chunked kernel waves for under four fifths of the 1024 SIMDs of the
+// chip are cut into segments and take the look-back kernel; everything else
+// takes the chunked kernel, which walks each row in order.  The look-back
+// kernel walks every segment twice (state only, then with output), about
+// 1.47 times the chunked kernel's vector instructions, but keeps three
+// workgroups on every compute unit: measured on the Mamba-130M layer (768
+// waves, three quarters of the SIMDs), 237 us against 244 us for the
+// chunked kernel, which at one wave per SIMD keeps its SIMDs about 58 %
+// busy against the look-back's 66 %.  Nearer a full chip of waves the
+// second walk no longer pays.
 mssm_variant choose_scan_variant(const mssm::ScanArgs &a) {
     if (a.L < 128 || !mssm::scan_chunked_supported(a)) return MSSM_VARIANT_ROWSERIAL;
-    if (a.L >= 2048 && mssm::scan_chunked_waves(a) < 512 && mssm::scan_lookback_supported(a))
+    if (a.L >= 2048 && 5 * mssm::scan_chunked_waves(a) < 4 * 1024 && mssm::scan_lookback_supported(a))
         return MSSM_VARIANT_LOOKBACK;
     return MSSM_VARIANT_CHUNKED;
 }
