@@ -200,12 +200,19 @@ def test_scan_pairscan_rejects_large_state(dev):
 
 
 FULL = [inputs.MAMBA_130M, inputs.MAMBA_2_8B, inputs.MILLION]
+# AUTO's kernel on each layer shape: the look-back kernel where the chunked
+# grid fills under four fifths of the 1024 SIMDs and the rows are long
+AUTO_CHOICE = {inputs.MAMBA_130M.name: _lib.VARIANT_LOOKBACK,
+               inputs.MAMBA_2_8B.name: _lib.VARIANT_CHUNKED,
+               inputs.MILLION.name: _lib.VARIANT_LOOKBACK}
 
 
 @pytest.mark.parametrize("variant", [_lib.VARIANT_AUTO] + SCAN_VARIANTS + PAIR_VARIANTS)
 @pytest.mark.parametrize("p", FULL, ids=[q.name for q in FULL])
 def test_scan_full_size_sampled_rows(dev, variant, p):
+    from selective_state_space_05_amd.api import last_variant
     _sampled(p, variant, dev)
+    assert last_variant() == (AUTO_CHOICE[p.name] if variant == _lib.VARIANT_AUTO else variant)
 
 
 @pytest.mark.parametrize("p", FULL, ids=[q.name for q in FULL])
