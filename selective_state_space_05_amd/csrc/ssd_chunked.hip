@@ -1,5 +1,5 @@
 // ssd_chunked.hip -- Mamba-2 scalar-decay (SSD) forward in the chunked matrix
-// form on the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16), parallel over
+// form on the gfx950 matrix cores (v_mfma_f32_16x16x32_bf16), parallel over
 // chunks.
 //
 // Per batch b and head h, with dl_t = softplus(dt_t + dt_bias[h]) and the log
@@ -11,35 +11,32 @@
 //
 //   S[p,n]      = sum_s exp(cum_end - cum_s) dl_s x_s[p] B_s[n]      (chunk state)
 //   h_out       = exp(cum_end) h_in + S                                (state pass)
-//   Y_diag[t,p] = sum_{s<=t} (C_t . B_s) exp(cum_t - cum_s) dl_s x_s[p]
-//   Y_off[t,p]  = exp(cum_t) sum_n C_t[n] h_in[p,n]
-//   y[t,p]      = (Y_diag + Y_off + D[h] x_t[p]) silu(z[t,p])   (gate optional)
+//   y[t,p]      = (C_t . h_t[p,:] + D[h] x_t[p]) silu(z[t,p])   (gate optional)
 //
-// which is the recurrence S_t = a_t S_{t-1} + dl_t x_t B_t^T, y = C_t S_t +
-// D x_t unrolled over a chunk (the cumulative-product closed form of the
-// same ybb.press section; its chunk-by-chunk state carry is section 5).
+// where h_t is the state after step t of the recurrence
+// h_t = a_t h_{t-1} + dl_t x_t B_t^T started from h_in (the cumulative-product
+// closed form of the same ybb.press section; its chunk-by-chunk state carry
+// is section 5).
 //
 // Three kernels, so that every chunk is worked on at once:
-//   1. ssd_state_kernel: the chunk state S as a matrix-core product
-//      (x * weight)^T B over the chunk's steps, and the chunk's total log2
+//   1. ssd_state_kernel: the chunk state S, accumulated block by block of 32
+//      steps as a matrix-core product (x w)^T B, and the chunk's total log2
 //      decay;
 //   2. ssd_pass_kernel: walks the chunks of each (batch, head) in order,
 //      elementwise over the P x N state and starting from the initial state
 //      (zero unless given), replacing each chunk state by the state entering
 //      that chunk and writing h_last;
-//   3. ssd_output_kernel: the outputs, computed transposed
-//      (Y^T = X^T M^T + H C^T) so that each lane owns one step t: the decay
-//      factors become per-lane scalars and each lane stores four consecutive
-//      head-dimension values at once.
-// Kernels 1 and 3 give each workgroup one (batch, chunk) and a run of heads
-// of one B / C group: B (and C) of the chunk are staged once and serve every
-// head of the run, and the next head's x rows are prefetched into registers
-// while the current head is computed.
+//   3. ssd_output_kernel: the outputs, walking the chunk's 32-step blocks from
+//      h_in with the state carried in matrix-core accumulators; within a block
+//      the outputs come from the state entering it and the block's own 32 x 32
+//      decay-masked C B^T tile.
+// Both walks give each workgroup one (batch, chunk, head, 64-column slice of
+// the head dimension) and each of its four waves 16 columns, and stage a
+// block's B, C and x in LDS (transposed where a product contracts over the
+// steps) while the next blocks' rows are in flight.
 // Products whose operands are not exact bf16 values (x * weight, the masked
-// decay matrix, the carried state) use a two-term bf16 split (hi + lo), so
-// each product carries about 16 significant bits; accumulation is float32.
-#include <type_traits>
-
+// decay tile, the carried state) use a two-term bf16 split (hi + lo), so each
+// product carries about 16 significant bits; accumulation is float32.
 #include "device_math.h"
 #include "internal.h"
 
@@ -47,32 +44,8 @@ namespace mssm {
 namespace {
 
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
-typedef float f16x __attribute__((ext_vector_type(16)));
 
-constexpr int kPG = 64;     // head-dimension columns per workgroup (two 32-wide tiles)
-
-__device__ __forceinline__ f16x mfma(bf8 a, bf8 b, f16x c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f16x zero16() {
-    f16x z;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) z[v] = 0.0f;
-    return z;
-}
-
-// Two floats rounded to bf16 (nearest even), packed low half first.
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-    const bf2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
-    return __builtin_bit_cast(uint32_t, v);
-}
-// Two-term split of two floats: hi = bf16(v), lo = bf16(v - hi).
-__device__ __forceinline__ void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
-    hi = pack2(a, b);
-    lo = pack2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
-}
+constexpr int kPG = 64;     // head-dimension columns per workgroup (four 16-wide wave slices)
 
 // Eight consecutive bf16 of row t starting at column c8 of a row-major slice
 // with row stride `stride`; zero past the last row or column.  Out-of-range
@@ -139,88 +112,180 @@ struct Geom {
     int L, H, P, N, G, nch, npg;
 };
 
-// Work item of the state and output kernels: one (batch, chunk) and a run of
-// heads that read the same B / C group, so B and C are staged once and reused
-// by every head of the run; within a run, item i covers head h0 + i / npg and
-// head-dimension slice i % npg.
-struct Run {
-    int64_t b;
-    int c, h0, items, grp;
-};
+typedef float f4x __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ Run decode_run(const Geom &g, int runs_per_chunk, int heads_per_run) {
-    int64_t id = blockIdx.x;
-    const int r = static_cast<int>(id % runs_per_chunk);
-    id /= runs_per_chunk;
-    Run run;
-    run.c = static_cast<int>(id % g.nch);
-    run.b = id / g.nch;
-    run.h0 = r * heads_per_run;
-    const int h1 = min(g.H, run.h0 + heads_per_run);
-    run.items = (h1 - run.h0) * g.npg;
-    run.grp = run.h0 / (g.H / g.G);
-    return run;
+__device__ __forceinline__ f4x mfma16(bf8 a, bf8 b, f4x c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-
-// ---------------------------------------------------------------------------
-// 1. chunk states
-// ---------------------------------------------------------------------------
-// Threads of the chunk-state kernel: eight waves (two per SIMD, so one
-// wave's matrix-core work overlaps the other's staging) when the chunk has
-// enough steps to give each thread a unit of x.
-template <int Q>
-constexpr int state_threads() { return Q >= 128 ? 512 : 256; }
-
-// Row pitches (elements) of the transposed tiles.  B^T rows are read as
-// 16-byte pieces (pitch a multiple of 8).  The x tiles are written as 4-byte
-// step pairs by groups of 8 lanes whose rows lie 8 apart, and read as 8-byte
-// pieces: a pitch of Q + 4 (an odd number of 8-byte pieces) spreads those
-// 8 rows over 4 bank groups instead of 2.
-template <int Q, int NP>
-struct __align__(16) StateSmem {
-    static constexpr int XP = Q + 8;     // B^T row pitch
-    static constexpr int XQ = Q + 4;     // (x w)^T row pitch
-    uint16_t BT[NP * XP];                // B^T of the chunk
-    uint16_t Xh[kPG * XQ], Xl[kPG * XQ]; // (x * weight)^T, bf16 high / low parts
-    float cum[Q], dl[Q], wsum[8];
-};
-
-// Eight consecutive bf16 of an LDS row as two 8-byte reads (8-byte aligned).
-__device__ __forceinline__ bf8 lds_read8(const uint16_t *p) {
-    const uint2 a = *reinterpret_cast<const uint2 *>(p);
-    const uint2 b = *reinterpret_cast<const uint2 *>(p + 4);
+__device__ __forceinline__ f4x zero4() {
+    f4x z = {0.0f, 0.0f, 0.0f, 0.0f};
+    return z;
+}
+__device__ __forceinline__ bf8 cat8(uint2 a, uint2 b) {
     return __builtin_bit_cast(bf8, make_uint4(a.x, a.y, b.x, b.y));
 }
+// Column of step s in row r of a transposed (rows x 32 steps) LDS tile:
+// steps are swizzled by 8 ((r / 16) mod 4), which keeps every aligned run of
+// four steps contiguous, gives the 16 rows read together one swizzle, and
+// spreads the step-pair writes of rows 8 apart (the staging pattern below)
+// over distinct banks.
+__device__ __forceinline__ int swz(int s, int r) { return s ^ (8 * ((r >> 4) & 3)); }
+// Two floats rounded to bf16 (nearest even) and packed, low half first, as
+// one instruction the optimiser cannot re-derive: the split below then
+// widens the packed halves with a shift and a mask, six instructions per
+// pair in all.
+__device__ __forceinline__ uint32_t cvt_pk(float lo, float hi) {
+    uint32_t r;
+    asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+    return r;
+}
+__device__ __forceinline__ void split_pk(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = cvt_pk(a, b);
+    lo = cvt_pk(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
 
-// x rows of one item, prefetched into registers by NT threads: unit u of
-// this thread covers steps 2 s2, 2 s2 + 1 and head-dimension columns
-// p8 .. p8 + 7.
-template <int Q, int NT>
-struct XRegs {
-    static constexpr int U = (Q / 2) * (kPG / 8) / NT;
-    static_assert(U >= 1 && U * NT == (Q / 2) * (kPG / 8), "every thread holds whole units");
-    uint4 v[U][2];       // raw loads; apply the masks m with and4 before use
-    uint32_t m[U][2];
-    float dt;
+// Buffer resources (gfx9 raw-buffer format word): a load at a byte offset
+// at or past `bytes` returns zero, a store there is dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void *base, int64_t bytes) {
+    const int32_t n = static_cast<int32_t>(bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes));
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// One 32-step block of B, C and x in LDS.
+template <int NP>
+struct __align__(16) BlockStage {
+    static constexpr int TP = 36;        // BT / XT row pitch (elements; rows 8-byte aligned)
+    static constexpr int CP = NP + 4;    // CR row pitch (8-byte reads of 16 rows: distinct banks)
+    uint16_t BT[NP * TP];                // BT[n][s] = B at step s, state n
+    uint16_t CR[32 * CP];                // CR[t][n] = C at step t, state n
+    uint16_t XT[kPG * TP];               // XT[p][s] = x at step s, column p
+};
+template <int Q, int NP>
+struct __align__(16) OutSmem {
+    BlockStage<NP> st[2];                // blocks k and k + 1 of the walk
+    uint4 M[2][2][64];                   // diagonal decay tile: [t tile][hi, lo][lane]
+    float cum[Q], dl[Q];
+    float fs[Q];                         // 2^(cum at the end of s's block - cum_s) dl_s
+    float wsum[4];
 };
 
-template <int Q, int NT, bool VEC>
-__device__ __forceinline__ void load_x(XRegs<Q, NT> &r, const uint16_t *x, const uint16_t *dt,
-                                       const Geom &g, const Run &run, int item) {
+// A block's B, C and x rows as loaded.  Unit u of B and x: step pair
+// 2 (u / (NP / 8)) (x: 2 (u / 8)) of the block, 8 states (columns) from
+// 8 (u % (NP / 8)) (x: 8 (u % 8)), so consecutive lanes read consecutive
+// 16-byte pieces of a row; unit u of C:
+// step u / (NP / 8), 8 states.  Rows past the sequence end are read as zero
+// (vector path) or clamped (element path); their values meet only zero
+// weights (dl = 0 there) and outputs that are not stored.  States past N
+// are zeroed (cm, bm): they would enter the sums over n.  Columns past the
+// slice's head dimension are not masked: every column p is computed on its
+// own and those are not stored.
+template <int NP, bool WC = true>
+struct BlockRegs {
+    static constexpr int NCU = WC ? (4 * NP + 255) / 256 : 0;   // C units per thread
+    uint4 b[2], x[2], c[NCU > 0 ? NCU : 1];
+};
+
+// Per-thread load geometry, fixed over the walk.
+template <int NP, bool WC = true>
+struct BlockGeom {
+    static constexpr int NC = BlockRegs<NP, WC>::NCU > 0 ? BlockRegs<NP, WC>::NCU : 1;
+    uint32_t ob, ox, oc[NC];                     // byte offsets within a block
+    uint32_t bm, cm[NC];                         // state masks of the B and C units
+    int sb, sx, scu[NC];                         // step of the unit
+    int nb, px, ncu[NC];                         // first state / column of the unit
+};
+
+template <int NP, bool WC>
+__device__ __forceinline__ void block_geom(BlockGeom<NP, WC> &q, const Geom &g, int rowBC, int rowX) {
     const int tid = threadIdx.x;
-    const int hh = run.h0 + item / g.npg, pbase = (item % g.npg) * kPG;
-    const int t0 = run.c * Q;
-    const int rowX = g.H * g.P;
-    const uint16_t *xg = x + run.b * g.L * static_cast<int64_t>(rowX) + hh * g.P + pbase;
-#pragma unroll
-    for (int k = 0; k < XRegs<Q, NT>::U; ++k) {
-        const int u = tid + NT * k;
-        const int s2 = 2 * (u / (kPG / 8)), p8 = (u % (kPG / 8)) * 8;
-        r.v[k][0] = load_row8_raw<VEC>(xg, t0 + s2, p8, g.L, g.P - pbase, rowX, r.m[k][0]);
-        r.v[k][1] = load_row8_raw<VEC>(xg, t0 + s2 + 1, p8, g.L, g.P - pbase, rowX, r.m[k][1]);
+    {
+        const int u = min(tid, 2 * NP - 1);
+        q.sb = 2 * (u / (NP / 8));
+        q.nb = (u % (NP / 8)) * 8;
+        q.ob = static_cast<uint32_t>(q.sb * rowBC + q.nb) * 2u;
+        q.bm = q.nb < g.N ? ~0u : 0u;
     }
-    const int t = t0 + (tid < Q ? tid : 0);
-    r.dt = bf16_to_f32(dt[run.b * g.L * static_cast<int64_t>(g.H) + (t < g.L ? t : g.L - 1) * g.H + hh]);
+    {
+        const int u = tid & 127;
+        q.sx = 2 * (u / (kPG / 8));
+        q.px = (u % (kPG / 8)) * 8;
+        q.ox = static_cast<uint32_t>(q.sx * rowX + q.px) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < BlockRegs<NP, WC>::NCU; ++i) {
+        const int u = min(tid + 256 * i, 4 * NP - 1);
+        q.scu[i] = u / (NP / 8);
+        q.ncu[i] = (u % (NP / 8)) * 8;
+        q.oc[i] = static_cast<uint32_t>(q.scu[i] * rowBC + q.ncu[i]) * 2u;
+        q.cm[i] = q.ncu[i] < g.N ? ~0u : 0u;
+    }
+}
+
+template <int NP, bool VEC, bool WC>
+__device__ __forceinline__ void load_block(BlockRegs<NP, WC> &r, const BlockGeom<NP, WC> &q, const uint16_t *Bg,
+                                           const uint16_t *Cg, const uint16_t *xg, int tb, const Geom &g,
+                                           int rowBC, int rowX, int pcols) {
+    if (VEC) {
+        // resources from the block's first row to the end of the sequence
+        const int64_t rows = g.L - tb;
+        const auto rB = brsrc(Bg + static_cast<int64_t>(tb) * rowBC, rows * rowBC * 2 - (rowBC - g.N) * 2);
+        const auto rX = brsrc(xg + static_cast<int64_t>(tb) * rowX, rows * rowX * 2 - (rowX - pcols) * 2);
+        r.b[0] = bload16(rB, q.ob);
+        r.b[1] = bload16(rB, q.ob + rowBC * 2);
+        r.x[0] = bload16(rX, q.ox);
+        r.x[1] = bload16(rX, q.ox + rowX * 2);
+        if constexpr (WC) {
+            const auto rC = brsrc(Cg + static_cast<int64_t>(tb) * rowBC, rows * rowBC * 2 - (rowBC - g.N) * 2);
+#pragma unroll
+            for (int i = 0; i < BlockRegs<NP, WC>::NCU; ++i) r.c[i] = bload16(rC, q.oc[i]);
+        }
+    } else {
+        uint32_t m;
+        r.b[0] = load_row8_raw<false>(Bg, tb + q.sb, q.nb, g.L, g.N, rowBC, m);
+        r.b[1] = load_row8_raw<false>(Bg, tb + q.sb + 1, q.nb, g.L, g.N, rowBC, m);
+        r.x[0] = load_row8_raw<false>(xg, tb + q.sx, q.px, g.L, pcols, rowX, m);
+        r.x[1] = load_row8_raw<false>(xg, tb + q.sx + 1, q.px, g.L, pcols, rowX, m);
+#pragma unroll
+        for (int i = 0; i < BlockRegs<NP, WC>::NCU; ++i)
+            r.c[i] = load_row8_raw<false>(Cg, tb + q.scu[i], q.ncu[i], g.L, g.N, rowBC, m);
+    }
+}
+
+// `nmask`: N < NP (workgroup-uniform), so state columns past N are zeroed.
+template <int NP, bool VEC, bool WC, class Stage>
+__device__ __forceinline__ void store_block(const BlockRegs<NP, WC> &r, const BlockGeom<NP, WC> &q, bool nmask,
+                                            Stage &st) {
+    constexpr int TP = Stage::TP;
+    const int tid = threadIdx.x;
+    // two step rows as 4-byte step pairs of the transposed tiles (the eight
+    // rows of a unit share one swizzle)
+    auto pairs = [](uint16_t *T, int row8, int s2, uint4 v0, uint4 v1) {
+        const uint32_t a[4] = {v0.x, v0.y, v0.z, v0.w}, e[4] = {v1.x, v1.y, v1.z, v1.w};
+        const int sc = swz(s2, row8);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            *reinterpret_cast<uint32_t *>(&T[(row8 + 2 * k) * TP + sc]) = (a[k] & 0xffffu) | (e[k] << 16);
+            *reinterpret_cast<uint32_t *>(&T[(row8 + 2 * k + 1) * TP + sc]) = (a[k] >> 16) | (e[k] & 0xffff0000u);
+        }
+    };
+    const bool vm = VEC && nmask;
+    if (tid < 2 * NP) pairs(st.BT, q.nb, q.sb, vm ? and4(r.b[0], q.bm) : r.b[0], vm ? and4(r.b[1], q.bm) : r.b[1]);
+    if (tid < 128) pairs(st.XT, q.px, q.sx, r.x[0], r.x[1]);
+    if constexpr (WC) {
+        constexpr int CP = Stage::CP;
+#pragma unroll
+        for (int i = 0; i < BlockRegs<NP, WC>::NCU; ++i) {
+            if (tid + 256 * i < 4 * NP) {
+                const uint4 v = vm ? and4(r.c[i], q.cm[i]) : r.c[i];
+                *reinterpret_cast<uint2 *>(&st.CR[q.scu[i] * CP + q.ncu[i]]) = make_uint2(v.x, v.y);
+                *reinterpret_cast<uint2 *>(&st.CR[q.scu[i] * CP + q.ncu[i] + 4]) = make_uint2(v.z, v.w);
+            }
+        }
+    }
 }
 
 // dl and the inclusive sum of the log2 decay over the chunk's Q steps from a
@@ -254,115 +319,128 @@ __device__ void chunk_decay_from(float dr, int t0, int L, float A2, float bias,
     __syncthreads();
 }
 
+// ---------------------------------------------------------------------------
+// 1. chunk states, block-walk form
+// ---------------------------------------------------------------------------
+// S[p][n] = sum_s w_s x_s[p] B_s[n], w_s = 2^(cum_end - cum_s) dl_s: the
+// output kernel's state update (section 3) without the outputs.  One
+// workgroup per (batch, chunk, head, 64-column slice); wave w accumulates
+// columns p = 16 w + 0..15 over the chunk's 32-step blocks with the same
+// operand orders (B^T rows n and K = steps; (x w) columns p).
+template <int NP>
+struct __align__(16) StateStage {
+    static constexpr int TP = 36;
+    uint16_t BT[NP * TP];                // BT[n][s]
+    uint16_t XT[kPG * TP];               // XT[p][s]
+};
+template <int Q, int NP>
+struct __align__(16) StateSmem {
+    StateStage<NP> st[2];
+    float cum[Q], dl[Q], w[Q];
+    float wsum[4];
+};
+
 template <int Q, int NP, bool VEC>
-__global__ __launch_bounds__(state_threads<Q>()) void ssd_state_kernel(
+__global__ __launch_bounds__(256, VEC ? 4 : 2) void ssd_state_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt,
     const float *__restrict__ dt_bias, const float *__restrict__ A,
-    const uint16_t *__restrict__ Bm, float *__restrict__ S, float *__restrict__ ce, Geom g,
-    int runs_per_chunk, int heads_per_run) {
-    using Sm = StateSmem<Q, NP>;
-    constexpr int XP = Sm::XP, XQ = Sm::XQ;
-    constexpr int NT = state_threads<Q>();
-    constexpr int kWaves = NT / 64;
-    // output tiles of 32 x 32: eight waves take one each (pt = wave & 1,
-    // nt = wave / 2), four waves take both head-dimension tiles of one nt
-    constexpr int kPtPerWave = kWaves == 8 ? 1 : 2;
-    __shared__ Sm sm;
+    const uint16_t *__restrict__ Bm, float *__restrict__ S, float *__restrict__ ce, Geom g) {
+    constexpr int NB = Q / 32;
+    constexpr int NJ = NP / 16;
+    constexpr int TP = StateStage<NP>::TP;
+    __shared__ StateSmem<Q, NP> sm;
     const int tid = threadIdx.x;
-    // wave index as a scalar, so control flow that depends on it stays uniform
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-    const Run run = decode_run(g, runs_per_chunk, heads_per_run);
-    const int t0 = run.c * Q;
-    const int rowBC = g.G * g.N;
-    const uint16_t *Bg = Bm + run.b * g.L * static_cast<int64_t>(rowBC) + run.grp * g.N;
+    const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
 
-    XRegs<Q, NT> xr;
-    load_x<Q, NT, VEC>(xr, x, dt, g, run, 0);
-    // B^T of the chunk, exact bf16 values re-packed as step pairs
-    constexpr int kTotBT = (Q / 2) * (NP / 8);
+    int64_t id = blockIdx.x;
+    const int pg = static_cast<int>(id % g.npg);
+    id /= g.npg;
+    const int hh = static_cast<int>(id % g.H);
+    id /= g.H;
+    const int c = static_cast<int>(id % g.nch);
+    const int64_t b = id / g.nch;
+    const int pbase = pg * kPG, pcols = g.P - pbase;
+    const int t0 = c * Q;
+    const int rowX = g.H * g.P, rowBC = g.G * g.N;
+    const int grp = hh / (g.H / g.G);
+    const uint16_t *Bg = Bm + b * g.L * static_cast<int64_t>(rowBC) + grp * g.N;
+    const uint16_t *xg = x + b * g.L * static_cast<int64_t>(rowX) + hh * g.P + pbase;
+    const bool nmask = g.N < NP;
+    const int pl = 16 * wave + l16;
+
+    // dt first, then the first three blocks (register sets as in the output
+    // kernel)
+    const int tdt = t0 + (tid < Q ? tid : 0);
+    const float dtr = bf16_to_f32(dt[b * g.L * static_cast<int64_t>(g.H) + static_cast<int64_t>(tdt < g.L ? tdt : g.L - 1) * g.H + hh]);
+    BlockGeom<NP, false> q;
+    block_geom<NP, false>(q, g, rowBC, rowX);
+    BlockRegs<NP, false> r0, ra, rb;
+    load_block<NP, VEC, false>(r0, q, Bg, nullptr, xg, t0, g, rowBC, rowX, pcols);
+    if (NB > 1) load_block<NP, VEC, false>(ra, q, Bg, nullptr, xg, t0 + 32, g, rowBC, rowX, pcols);
+    if (NB > 2) load_block<NP, VEC, false>(rb, q, Bg, nullptr, xg, t0 + 64, g, rowBC, rowX, pcols);
+    chunk_decay_from<Q>(dtr, t0, g.L, A[hh] * kLog2e, dt_bias ? dt_bias[hh] : 0.0f, sm.cum, sm.dl, sm.wsum);
+    const float cum_end = sm.cum[Q - 1];
+    if (tid < Q) sm.w[tid] = fast_exp2(cum_end - sm.cum[tid]) * sm.dl[tid];
+    store_block<NP, VEC, false>(r0, q, nmask, sm.st[0]);
+    __syncthreads();
+
+    f4x acc[NJ];
 #pragma unroll
-    for (int k = 0; k < (kTotBT + NT - 1) / NT; ++k) {
-        const int u = tid + NT * k;
-        if (kTotBT % NT != 0 && u >= kTotBT) break;
-        const int s2 = 2 * (u / (NP / 8)), n8 = (u % (NP / 8)) * 8;
-        const uint4 v0 = load_row8<VEC>(Bg, t0 + s2, n8, g.L, g.N, rowBC);
-        const uint4 v1 = load_row8<VEC>(Bg, t0 + s2 + 1, n8, g.L, g.N, rowBC);
-        const uint32_t a[4] = {v0.x, v0.y, v0.z, v0.w}, e[4] = {v1.x, v1.y, v1.z, v1.w};
+    for (int j = 0; j < NJ; ++j) acc[j] = zero4();
+    auto step = [&](const int k, BlockRegs<NP, false> &rg) {
+        const StateStage<NP> &st = sm.st[k & 1];
+        const int base = 32 * k;
+        // (x w) of the block: column p = pl, K slots s = 16 (i / 4) + 4 g4 + i % 4
+        const uint16_t *xp = &st.XT[pl * TP];
+        const uint2 x0 = *reinterpret_cast<const uint2 *>(xp + swz(4 * g4, pl));
+        const uint2 x1 = *reinterpret_cast<const uint2 *>(xp + swz(16 + 4 * g4, pl));
+        const float4 f0 = *reinterpret_cast<const float4 *>(&sm.w[base + 4 * g4]);
+        const float4 f1 = *reinterpret_cast<const float4 *>(&sm.w[base + 16 + 4 * g4]);
+        uint32_t xh[4], xl[4];
+        split_pk(bits_lo(x0.x) * f0.x, bits_hi(x0.x) * f0.y, xh[0], xl[0]);
+        split_pk(bits_lo(x0.y) * f0.z, bits_hi(x0.y) * f0.w, xh[1], xl[1]);
+        split_pk(bits_lo(x1.x) * f1.x, bits_hi(x1.x) * f1.y, xh[2], xl[2]);
+        split_pk(bits_lo(x1.y) * f1.z, bits_hi(x1.y) * f1.w, xh[3], xl[3]);
+        const bf8 xwh = __builtin_bit_cast(bf8, make_uint4(xh[0], xh[1], xh[2], xh[3]));
+        const bf8 xwl = __builtin_bit_cast(bf8, make_uint4(xl[0], xl[1], xl[2], xl[3]));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            *reinterpret_cast<uint32_t *>(&sm.BT[(n8 + 2 * r) * XP + s2]) = (a[r] & 0xffffu) | (e[r] << 16);
-            *reinterpret_cast<uint32_t *>(&sm.BT[(n8 + 2 * r + 1) * XP + s2]) = (a[r] >> 16) | (e[r] & 0xffff0000u);
+        for (int j = 0; j < NJ; ++j) {
+            const uint16_t *bp = &st.BT[(16 * j + l16) * TP];
+            const bf8 bt = cat8(*reinterpret_cast<const uint2 *>(bp + swz(4 * g4, 16 * j)),
+                                *reinterpret_cast<const uint2 *>(bp + swz(16 + 4 * g4, 16 * j)));
+            acc[j] = mfma16(bt, xwh, acc[j]);
+            acc[j] = mfma16(bt, xwl, acc[j]);
         }
-    }
-    const int nt = kWaves == 8 ? wave >> 1 : wave;     // 32-wide tile of the state index
-    const int pt0 = kWaves == 8 ? wave & 1 : 0;        // first 32-wide head-dimension tile
+        if (k + 1 < NB) {
+            // the next block into LDS: its buffer was last read in the
+            // previous block, before that block's barrier
+            store_block<NP, VEC, false>(rg, q, nmask, sm.st[(k + 1) & 1]);
+            __syncthreads();
+            if (k + 3 < NB) load_block<NP, VEC, false>(rg, q, Bg, nullptr, xg, t0 + base + 96, g, rowBC, rowX, pcols);
+        }
+    };
 #pragma unroll 1
-    for (int item = 0; item < run.items; ++item) {
-        const int hh = run.h0 + item / g.npg, pbase = (item % g.npg) * kPG;
-        const int pcols = g.P - pbase;
-        // (the decay scan starts with a barrier: the previous item's MFMA
-        // reads of Xh / Xl are done before they are overwritten below)
-        __syncthreads();
-        chunk_decay_from<Q>(xr.dt, t0, g.L, A[hh] * kLog2e, dt_bias ? dt_bias[hh] : 0.0f, sm.cum,
-                            sm.dl, sm.wsum);
-        const float cum_end = sm.cum[Q - 1];
-        // (x * w)^T with w_s = 2^(cum_end - cum_s) dl_s, split into bf16 parts
-#pragma unroll
-        for (int k = 0; k < XRegs<Q, NT>::U; ++k) {
-            const int u = tid + NT * k;
-            const int s2 = 2 * (u / (kPG / 8)), p8 = (u % (kPG / 8)) * 8;
-            const float w0 = fast_exp2(cum_end - sm.cum[s2]) * sm.dl[s2];
-            const float w1 = fast_exp2(cum_end - sm.cum[s2 + 1]) * sm.dl[s2 + 1];
-            const uint4 v0 = and4(xr.v[k][0], xr.m[k][0]), v1 = and4(xr.v[k][1], xr.m[k][1]);
-            const uint32_t a[4] = {v0.x, v0.y, v0.z, v0.w}, e[4] = {v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                uint32_t hi, lo;
-                split2(bits_lo(a[r]) * w0, bits_lo(e[r]) * w1, hi, lo);
-                *reinterpret_cast<uint32_t *>(&sm.Xh[(p8 + 2 * r) * XQ + s2]) = hi;
-                *reinterpret_cast<uint32_t *>(&sm.Xl[(p8 + 2 * r) * XQ + s2]) = lo;
-                split2(bits_hi(a[r]) * w0, bits_hi(e[r]) * w1, hi, lo);
-                *reinterpret_cast<uint32_t *>(&sm.Xh[(p8 + 2 * r + 1) * XQ + s2]) = hi;
-                *reinterpret_cast<uint32_t *>(&sm.Xl[(p8 + 2 * r + 1) * XQ + s2]) = lo;
-            }
-        }
-        __syncthreads();
-        // next item's x (the last item re-reads its own rows; unused)
-        load_x<Q, NT, VEC>(xr, x, dt, g, run, item + 1 < run.items ? item + 1 : item);
-        // S[p][n] = sum_s (x w)^T[p][s] B^T[n][s]: A rows p, B operand columns n
-        f16x acc[kPtPerWave];
-#pragma unroll
-        for (int i = 0; i < kPtPerWave; ++i) acc[i] = zero16();
-        if (nt * 32 < NP) {
-#pragma unroll 2
-            for (int kq = 0; kq < Q / 16; ++kq) {
-                const int s8 = 16 * kq + 8 * half;
-                const bf8 bb = *reinterpret_cast<const bf8 *>(&sm.BT[(nt * 32 + l32) * XP + s8]);
-#pragma unroll
-                for (int i = 0; i < kPtPerWave; ++i) {
-                    const int pt = pt0 + i;
-                    const bf8 ah = lds_read8(&sm.Xh[(pt * 32 + l32) * XQ + s8]);
-                    const bf8 al = lds_read8(&sm.Xl[(pt * 32 + l32) * XQ + s8]);
-                    acc[i] = mfma(ah, bb, acc[i]);
-                    acc[i] = mfma(al, bb, acc[i]);
-                }
-            }
-            // lane (column n, half) holds S[p(v)][n], p(v) = 8 (v / 4) + 4 half + v % 4
-            const int n = nt * 32 + l32;
-            if (n < g.N) {
-                float *Sg = S + ((run.b * g.nch + run.c) * g.H + hh) * static_cast<int64_t>(g.P) * g.N;
-#pragma unroll
-                for (int i = 0; i < kPtPerWave; ++i)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int p = (pt0 + i) * 32 + 8 * (v / 4) + 4 * half + (v % 4);
-                        if (p < pcols) Sg[static_cast<int64_t>(pbase + p) * g.N + n] = acc[i][v];
-                    }
-            }
-        }
-        if (pbase == 0 && tid == 0) ce[(run.b * g.nch + run.c) * g.H + hh] = cum_end;
+    for (int k = 0; k < NB; k += 2) {
+        step(k, ra);
+        step(k + 1, rb);
     }
+    // lane (l16, g4) holds S[pl][16 j + 4 g4 + v]
+    if (pl < pcols) {
+        float *Sg = S + (((b * g.nch + c) * g.H + hh) * static_cast<int64_t>(g.P) + pbase + pl) * g.N;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int n4 = 16 * j + 4 * g4;
+            if (VEC) {
+                if (n4 < g.N) *reinterpret_cast<float4 *>(Sg + n4) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (n4 + v < g.N) Sg[n4 + v] = acc[j][v];
+            }
+        }
+    }
+    if (pbase == 0 && tid == 0) ce[(b * g.nch + c) * g.H + hh] = cum_end;
 }
 
 // ---------------------------------------------------------------------------
@@ -406,320 +484,336 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(float *__restrict__ S,
 }
 
 // ---------------------------------------------------------------------------
-// 3. outputs
+// 3. outputs, block-state form
 // ---------------------------------------------------------------------------
-template <int Q, int NP>
-struct __align__(16) OutSmem {
-    static constexpr int BP = NP + 8;    // B row pitch (elements)
-    static constexpr int XP = Q + 4;     // x^T row pitch (8-byte reads; see StateSmem)
-    static constexpr int HP = NP + 8;    // h_in row pitch
-    uint16_t B[Q * BP];                  // B of the chunk, exact bf16
-    uint16_t XT[kPG * XP];               // x^T, exact bf16
-    uint16_t Hh[kPG * HP], Hl[kPG * HP]; // state entering the chunk, bf16 parts
-    float cum[Q], dl[Q];
-    float fs[Q];   // 2^(cum at the end of s's 32-step block - cum_s) dl_s
-    float wsum[4];
-};
-
-// h_in of one item prefetched into registers: unit u covers row p, columns
-// n2, n2 + 1 of the 64 x NP tile.
+// One workgroup per (batch, chunk, head, 64-column head-dimension slice).  The
+// chunk is walked in 32-step blocks k carrying the slice's state: with c_k
+// the cumulative log2 decay before block k (c_0 = 0), e_k the one at its end
+// and H_k the state entering it (H_0 = h_in),
+//
+//   y_t     = 2^(cum_t - c_k) C_t . H_k[p,:]
+//             + sum_{s in block k, s <= t} (C_t . B_s) 2^(cum_t - cum_s) dl_s x_s[p]
+//             + D x_t[p]
+//   H_{k+1} = 2^(e_k - c_k) H_k + sum_{s in block k} 2^(e_k - cum_s) dl_s x_s[p] B_s
+//
+// -- the chunk's unrolled recurrence ("Mamba状态空间模型的硬件感知推理优化"
+// (ybb.press) section 4) taken block by block, with the state carried from
+// block to block as section 5 carries it from chunk to chunk.  Only the
+// 32 x 32 diagonal tile of each block needs a decay matrix; everything before
+// the block reaches y through the carried state.
+//
+// Products run on v_mfma_f32_16x16x32_bf16 (A: lane l holds row l % 16 and K
+// indices 8 (l / 16) + 0..7; B: column l % 16 and the same K indices; D:
+// column l % 16, rows 4 (l / 16) + 0..3).  Wave w owns head-dimension columns
+// p = 16 w + 0..15 and keeps H^T of them as accumulators: lane (l16 = l % 16,
+// g = l / 16) holds H[16 w + l16][16 j + 4 g + v] of state tile j.  As the A
+// operand of the output product (rows p, K = n) those registers put state
+// index 32 kk + 16 (i / 4) + 4 g + i % 4 in K slot 8 g + i, and the C operand
+// is read in the same order.  Every product over the steps s of a block uses
+// the order s = 16 (i / 4) + 4 g + i % 4 likewise, so the diagonal tile's
+// accumulators (rows s, column t) are already B operands of its product with
+// x.  Waves 0-2 form the tile's three causal 16 x 16 quadrants one block
+// ahead and share them through LDS.
+// Waves 0, 1, 2: quadrant (sq, tq) = (0, 0), (0, 1), (1, 1) of the diagonal
+// tile of the block at chunk step `base`:
+//   M[t][s] = (C_t . B_s) 2^(cum_t - cum_s) dl_s for s < t, plus D at s = t,
+// written split into bf16 parts as K slots 4 sq .. 4 sq + 3 of the B operand
+// of t tile tq.  le[v] (1 for s <= t, else 0) and sk[v] (D at s = t, else 0)
+// depend only on the lane, not on the block.
 template <int NP>
-struct HRegs {
-    static constexpr int U = kPG * (NP / 2) / 256;
-    float2 v[U];
-};
-
-template <int Q, int NP>
-__device__ __forceinline__ void load_h(HRegs<NP> &r, const float *Hin, const Geom &g, const Run &run,
-                                       int item) {
-    const int tid = threadIdx.x;
-    const int hh = run.h0 + item / g.npg, pbase = (item % g.npg) * kPG;
-    const int pcols = g.P - pbase;
-    const float *Hg = Hin + ((run.b * g.nch + run.c) * g.H + hh) * static_cast<int64_t>(g.P) * g.N;
-    // Every load is issued first, at an index clamped into the slice, and the
-    // masks are applied afterwards with selects: a load guarded by its mask
-    // is placed in a branch that waits for it, which serialises the loads.
-    float raw[HRegs<NP>::U][2];
+__device__ __forceinline__ void diag_tile(const BlockStage<NP> &st, uint4 (&Mo)[2][2][64], const float *cum,
+                                          const float *dl, int base, const float (&le)[4],
+                                          const float (&sk)[4], int wave, int lane) {
+    constexpr int TP = BlockStage<NP>::TP, CP = BlockStage<NP>::CP;
+    const int sq = wave == 2 ? 1 : 0, tq = wave == 0 ? 0 : 1;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    f4x G = zero4();
 #pragma unroll
-    for (int k = 0; k < HRegs<NP>::U; ++k) {
-        const int u = tid + 256 * k;
-        const int p = u / (NP / 2), n2 = (u % (NP / 2)) * 2;
-        const int64_t base = static_cast<int64_t>(pbase + (p < pcols ? p : 0)) * g.N;
-        raw[k][0] = Hg[base + (n2 < g.N ? n2 : 0)];
-        raw[k][1] = Hg[base + (n2 + 1 < g.N ? n2 + 1 : 0)];
-    }
+    for (int kk = 0; kk < NP / 32; ++kk) {
+        // A: B at step 16 sq + l16, states 32 kk + 8 g4 + 0..7; B operand: C
+        // at step 16 tq + l16, the same states
+        uint16_t av[8];
 #pragma unroll
-    for (int k = 0; k < HRegs<NP>::U; ++k) {
-        const int u = tid + 256 * k;
-        const int p = u / (NP / 2), n2 = (u % (NP / 2)) * 2;
-        const bool okp = p < pcols;
-        const bool m0 = okp & (n2 < g.N), m1 = okp & (n2 + 1 < g.N);
-        r.v[k] = make_float2(m0 ? raw[k][0] : 0.0f, m1 ? raw[k][1] : 0.0f);
+        for (int i = 0; i < 8; ++i) {
+            const int n = 32 * kk + 8 * g4 + i;
+            av[i] = st.BT[n * TP + swz(16 * sq + l16, n)];
+        }
+        bf8 a;
+        __builtin_memcpy(&a, av, 16);
+        const uint16_t *cp = &st.CR[(16 * tq + l16) * CP + 32 * kk + 8 * g4];
+        const bf8 cb = cat8(*reinterpret_cast<const uint2 *>(cp), *reinterpret_cast<const uint2 *>(cp + 4));
+        G = mfma16(a, cb, G);
     }
+    // G[v]: step s = base + 16 sq + 4 g4 + v, column t = base + 16 tq + l16
+    const int t = base + 16 * tq + l16, s0 = base + 16 * sq + 4 * g4;
+    const float ct = cum[t];
+    const float4 cs = *reinterpret_cast<const float4 *>(&cum[s0]);
+    const float4 ds = *reinterpret_cast<const float4 *>(&dl[s0]);
+    const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, dsv[4] = {ds.x, ds.y, ds.z, ds.w};
+    float mv[4];
+    // (2^(ct - cs) overflows only where s > t, and le = 0 there selects 0)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const float m = G[v] * fast_exp2(ct - csv[v]) * dsv[v];
+        mv[v] = le[v] != 0.0f ? m + sk[v] : 0.0f;
+    }
+    uint32_t h0, l0, h1, l1;
+    split_pk(mv[0], mv[1], h0, l0);
+    split_pk(mv[2], mv[3], h1, l1);
+    reinterpret_cast<uint2 *>(&Mo[tq][0][lane])[sq] = make_uint2(h0, h1);
+    reinterpret_cast<uint2 *>(&Mo[tq][1][lane])[sq] = make_uint2(l0, l1);
 }
 
+// Three workgroups per compute unit on the vector path without a gate
+// (LDS and registers allow it); two otherwise, where the gate values or the
+// element loads need more registers.
 template <int Q, int NP, bool VEC, bool GATE>
-__global__ __launch_bounds__(256) void ssd_output_kernel(
+__global__ __launch_bounds__(256, (VEC && !GATE) ? 3 : 2) void ssd_output_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt,
     const float *__restrict__ dt_bias, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm,
     const float *__restrict__ Dskip, const uint16_t *__restrict__ z, const float *__restrict__ Hin,
-    uint16_t *__restrict__ y, Geom g, int runs_per_chunk, int heads_per_run) {
-    using Sm = OutSmem<Q, NP>;
-    constexpr int BP = Sm::BP, XP = Sm::XP, HP = Sm::HP;
-    constexpr int NT = Q / 32;          // 32-step blocks per chunk
-    constexpr int KN = NP / 16;         // K steps over the state index
-    __shared__ Sm sm;
+    uint16_t *__restrict__ y, Geom g) {
+    constexpr int NB = Q / 32;          // blocks per chunk
+    constexpr int NJ = NP / 16;         // 16-wide state tiles
+    constexpr int KK = NP / 32;         // K steps over the state index
+    using St = BlockStage<NP>;
+    constexpr int TP = St::TP, CP = St::CP;
+    __shared__ OutSmem<Q, NP> sm;
     const int tid = threadIdx.x;
-    // wave index as a scalar, so control flow that depends on it stays uniform
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, l32 = lane & 31, half = lane >> 5;
-    const Run run = decode_run(g, runs_per_chunk, heads_per_run);
-    const int t0 = run.c * Q;
-    const int rowX = g.H * g.P;
-    const int rowBC = g.G * g.N;
-    const uint16_t *Bg = Bm + run.b * g.L * static_cast<int64_t>(rowBC) + run.grp * g.N;
-    const uint16_t *Cg = Cm + run.b * g.L * static_cast<int64_t>(rowBC) + run.grp * g.N;
+    const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
 
-    XRegs<Q, 256> xr;
-    load_x<Q, 256, VEC>(xr, x, dt, g, run, 0);
-    // B of the chunk (rows s), shared by every head of the run
-    static_assert(Q * (NP / 8) % 256 == 0, "whole units of B per thread");
-#pragma unroll
-    for (int k = 0; k < Q * (NP / 8) / 256; ++k) {
-        const int u = tid + 256 * k;
-        const int s = u / (NP / 8), n8 = (u % (NP / 8)) * 8;
-        *reinterpret_cast<uint4 *>(&sm.B[s * BP + n8]) = load_row8<VEC>(Bg, t0 + s, n8, g.L, g.N, rowBC);
-    }
-    // Each wave owns the 32-step blocks tb = wave and NT-1-wave (balanced
-    // causal work); with fewer than 8 blocks only the first NT/2 waves work.
-    // C_t fragments of those blocks: row t, state indices 16 jn + 8 half ...
-    const bool active = 2 * wave < NT;
-    bf8 cf[2][KN];
-#pragma unroll
-    for (int which = 0; which < 2; ++which) {
-        const int tb = which == 0 ? wave : NT - 1 - wave;
-#pragma unroll
-        for (int jn = 0; jn < KN; ++jn)
-            cf[which][jn] = __builtin_bit_cast(
-                bf8, load_row8<VEC>(Cg, t0 + (active ? tb : 0) * 32 + l32, 16 * jn + 8 * half, g.L, g.N, rowBC));
-    }
+    int64_t id = blockIdx.x;
+    const int pg = static_cast<int>(id % g.npg);
+    id /= g.npg;
+    const int hh = static_cast<int>(id % g.H);
+    id /= g.H;
+    const int c = static_cast<int>(id % g.nch);
+    const int64_t b = id / g.nch;
+    const int pbase = pg * kPG, pcols = g.P - pbase;
+    const int t0 = c * Q;
+    const int rowX = g.H * g.P, rowBC = g.G * g.N;
+    const int grp = hh / (g.H / g.G);
+    const uint16_t *Bg = Bm + b * g.L * static_cast<int64_t>(rowBC) + grp * g.N;
+    const uint16_t *Cg = Cm + b * g.L * static_cast<int64_t>(rowBC) + grp * g.N;
+    const int64_t xoff = b * g.L * static_cast<int64_t>(rowX) + hh * g.P + pbase;
+    const uint16_t *xg = x + xoff;
+    uint16_t *yg = y + xoff;
+    const float skip = Dskip ? Dskip[hh] : 0.0f;
+    const bool nmask = g.N < NP;
+    const int pl = 16 * wave + l16;     // column of this lane's A rows / B columns
+    const int p4 = 16 * wave + 4 * g4;  // first of this lane's four output columns
 
+    // the first two blocks' rows, and the state entering the chunk
+    // dt first (the decay scan waits for it), then the first three blocks'
+    // rows: block j + 1 is stored to LDS at the end of block j, from the
+    // register set ra (j even) or rb (j odd), which then receives block j + 3
+    const int tdt = t0 + (tid < Q ? tid : 0);
+    const float dtr = bf16_to_f32(dt[b * g.L * static_cast<int64_t>(g.H) + static_cast<int64_t>(tdt < g.L ? tdt : g.L - 1) * g.H + hh]);
+    BlockGeom<NP, true> q;
+    block_geom<NP, true>(q, g, rowBC, rowX);
+    BlockRegs<NP, true> r0, ra, rb;
+    load_block<NP, VEC, true>(r0, q, Bg, Cg, xg, t0, g, rowBC, rowX, pcols);
+    if (NB > 1) load_block<NP, VEC, true>(ra, q, Bg, Cg, xg, t0 + 32, g, rowBC, rowX, pcols);
+    if (NB > 2) load_block<NP, VEC, true>(rb, q, Bg, Cg, xg, t0 + 64, g, rowBC, rowX, pcols);
+    f4x H[NJ];
+    {
+        const float *Hg = Hin + ((b * g.nch + c) * g.H + hh) * static_cast<int64_t>(g.P) * g.N;
+        const bool okp = pl < pcols;
+        const float *hrow = Hg + static_cast<int64_t>(okp ? pbase + pl : 0) * g.N;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int n4 = 16 * j + 4 * g4;
+            if (VEC) {
+                // N % 8 == 0: the four states are all inside the row or all past it
+                const bool ok = okp && n4 < g.N;
+                const uint32_t m = opaque_mask(ok);
+                const float4 v = *reinterpret_cast<const float4 *>(hrow + (ok ? n4 : 0));
+                H[j][0] = __uint_as_float(__float_as_uint(v.x) & m);
+                H[j][1] = __uint_as_float(__float_as_uint(v.y) & m);
+                H[j][2] = __uint_as_float(__float_as_uint(v.z) & m);
+                H[j][3] = __uint_as_float(__float_as_uint(v.w) & m);
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const bool ok = okp && n4 + v < g.N;
+                    const float e = hrow[ok ? n4 + v : 0];
+                    H[j][v] = ok ? e : 0.0f;
+                }
+            }
+        }
+    }
+    chunk_decay_from<Q>(dtr, t0, g.L, A[hh] * kLog2e, dt_bias ? dt_bias[hh] : 0.0f, sm.cum, sm.dl, sm.wsum);
+    if (tid < Q) sm.fs[tid] = fast_exp2(sm.cum[tid | 31] - sm.cum[tid]) * sm.dl[tid];
+    // K slots 4..7 of t tile 0 (steps 16..31, after every step of the tile)
+    // stay zero; no quadrant writes them
+    if (wave == 3) {
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl) reinterpret_cast<uint2 *>(&sm.M[0][hl][lane])[1] = make_uint2(0, 0);
+    }
+    // causal mask of this lane's diagonal-tile quadrant (waves 0-2)
+    float le[4], sk[4];
+    {
+        const int sq = wave == 2 ? 1 : 0, tq = wave == 0 ? 0 : 1;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int sr = 16 * sq + 4 * g4 + v, tr = 16 * tq + l16;
+            le[v] = sr <= tr ? 1.0f : 0.0f;
+            sk[v] = sr == tr ? skip : 0.0f;
+        }
+    }
+    store_block<NP, VEC, true>(r0, q, nmask, sm.st[0]);
+    __syncthreads();
+    if (wave < 3) diag_tile<NP>(sm.st[0], sm.M, sm.cum, sm.dl, 0, le, sk, wave, lane);
+    // gate values of this lane's steps of the current block, four columns each
+    uint2 zr[2] = {make_uint2(0, 0), make_uint2(0, 0)};
+    auto load_z = [&](int kb) {
+#pragma unroll
+        for (int tq = 0; tq < 2; ++tq) {
+            const int t = t0 + 32 * kb + 16 * tq + l16;
+            const int tc = t < g.L ? t : g.L - 1;
+            const uint16_t *zp = z + xoff + static_cast<int64_t>(tc) * rowX;
+            if (VEC) {
+                const uint32_t m = opaque_mask(p4 < pcols);
+                const uint2 v = *reinterpret_cast<const uint2 *>(zp + (p4 < pcols ? p4 : 0));
+                zr[tq] = make_uint2(v.x & m, v.y & m);
+            } else {
+                uint16_t e[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) e[v] = p4 + v < pcols ? zp[p4 + v] : 0;
+                zr[tq] = make_uint2(e[0] | (static_cast<uint32_t>(e[1]) << 16), e[2] | (static_cast<uint32_t>(e[3]) << 16));
+            }
+        }
+    };
+    if (GATE) load_z(0);
+    // y of the chunk's rows, stores past the sequence end dropped
+    const auto ry = brsrc(yg + static_cast<int64_t>(t0) * rowX,
+                          static_cast<int64_t>(g.L - t0) * rowX * 2 - static_cast<int64_t>(rowX - pcols) * 2);
+    __syncthreads();
+
+    // The state is carried as H = sig * Hs with sig a workgroup-uniform
+    // scalar, so a block's decay multiplies sig (and the block's new terms
+    // by 1 / sig) instead of every state element; when sig would fall below
+    // 2^-64 it is folded back into Hs.
+    float sig = 1.0f;
+    auto step = [&](const int k, BlockRegs<NP, true> &rg) {
+        const St &st = sm.st[k & 1];
+        const int base = 32 * k;
+        const float ck = k > 0 ? sm.cum[base - 1] : 0.0f;
+        // x of the block: row p = pl, K slots s = 16 (i / 4) + 4 g4 + i % 4
+        const uint16_t *xp = &st.XT[pl * TP];
+        const uint2 x0 = *reinterpret_cast<const uint2 *>(xp + swz(4 * g4, pl));
+        const uint2 x1 = *reinterpret_cast<const uint2 *>(xp + swz(16 + 4 * g4, pl));
+        const bf8 xa = cat8(x0, x1);
+        // output: Y^T = Hs_k C^T (state part; hi and lo parts of Hs_k in
+        // chains of their own) and the diagonal tile's x^T M^T
+        f4x ys[2][2], yd[2];
+#pragma unroll
+        for (int tq = 0; tq < 2; ++tq) ys[tq][0] = ys[tq][1] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            uint32_t hw[4], lw[4];
+            split_pk(H[2 * kk][0], H[2 * kk][1], hw[0], lw[0]);
+            split_pk(H[2 * kk][2], H[2 * kk][3], hw[1], lw[1]);
+            split_pk(H[2 * kk + 1][0], H[2 * kk + 1][1], hw[2], lw[2]);
+            split_pk(H[2 * kk + 1][2], H[2 * kk + 1][3], hw[3], lw[3]);
+            const bf8 ah = __builtin_bit_cast(bf8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+            const bf8 al = __builtin_bit_cast(bf8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+#pragma unroll
+            for (int tq = 0; tq < 2; ++tq) {
+                const uint16_t *cp = &st.CR[(16 * tq + l16) * CP + 32 * kk + 4 * g4];
+                const bf8 cb = cat8(*reinterpret_cast<const uint2 *>(cp), *reinterpret_cast<const uint2 *>(cp + 16));
+                ys[tq][0] = mfma16(ah, cb, ys[tq][0]);
+                ys[tq][1] = mfma16(al, cb, ys[tq][1]);
+            }
+        }
+#pragma unroll
+        for (int tq = 0; tq < 2; ++tq) {
+            const bf8 mh = __builtin_bit_cast(bf8, sm.M[tq][0][lane]);
+            const bf8 ml = __builtin_bit_cast(bf8, sm.M[tq][1][lane]);
+            yd[tq] = mfma16(xa, mh, zero4());
+            yd[tq] = mfma16(xa, ml, yd[tq]);
+        }
+        const float sig_k = sig;
+        // state entering the next block: H_{k+1} = 2^(e_k - c_k) H_k + dH_k
+        if (k + 1 < NB) {
+            const float rk = fast_exp2(sm.cum[base + 31] - ck);
+            const float sn = sig * rk;
+            float wsc = 1.0f;             // weight of the block's new terms
+            if (sn >= 0x1p-64f) {
+                wsc = __builtin_amdgcn_rcpf(sn);
+                sig = sn;
+            } else {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) H[j] = H[j] * sn;
+                sig = 1.0f;
+            }
+            const float4 f0 = *reinterpret_cast<const float4 *>(&sm.fs[base + 4 * g4]);
+            const float4 f1 = *reinterpret_cast<const float4 *>(&sm.fs[base + 16 + 4 * g4]);
+            uint32_t xh[4], xl[4];
+            split_pk(bits_lo(x0.x) * f0.x * wsc, bits_hi(x0.x) * f0.y * wsc, xh[0], xl[0]);
+            split_pk(bits_lo(x0.y) * f0.z * wsc, bits_hi(x0.y) * f0.w * wsc, xh[1], xl[1]);
+            split_pk(bits_lo(x1.x) * f1.x * wsc, bits_hi(x1.x) * f1.y * wsc, xh[2], xl[2]);
+            split_pk(bits_lo(x1.y) * f1.z * wsc, bits_hi(x1.y) * f1.w * wsc, xh[3], xl[3]);
+            const bf8 xwh = __builtin_bit_cast(bf8, make_uint4(xh[0], xh[1], xh[2], xh[3]));
+            const bf8 xwl = __builtin_bit_cast(bf8, make_uint4(xl[0], xl[1], xl[2], xl[3]));
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const uint16_t *bp = &st.BT[(16 * j + l16) * TP];
+                const bf8 bt = cat8(*reinterpret_cast<const uint2 *>(bp + swz(4 * g4, 16 * j)),
+                                    *reinterpret_cast<const uint2 *>(bp + swz(16 + 4 * g4, 16 * j)));
+                H[j] = mfma16(bt, xwh, H[j]);
+                H[j] = mfma16(bt, xwl, H[j]);
+            }
+        }
+        // y at this lane's steps of the block, four columns each
+#pragma unroll
+        for (int tq = 0; tq < 2; ++tq) {
+            const int tl = base + 16 * tq + l16;
+            const float ft = fast_exp2(sm.cum[tl] - ck) * sig_k;
+            float yv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) yv[v] = fmaf(ft, ys[tq][0][v] + ys[tq][1][v], yd[tq][v]);
+            if (GATE) {
+                yv[0] *= silu(bits_lo(zr[tq].x));
+                yv[1] *= silu(bits_hi(zr[tq].x));
+                yv[2] *= silu(bits_lo(zr[tq].y));
+                yv[3] *= silu(bits_hi(zr[tq].y));
+            }
+            if (VEC) {
+                // rows past the sequence end fall outside the resource
+                if (p4 < pcols)
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        __builtin_bit_cast(__attribute__((ext_vector_type(2))) uint32_t,
+                                           make_uint2(cvt_pk(yv[0], yv[1]), cvt_pk(yv[2], yv[3]))),
+                        ry, static_cast<uint32_t>((tl * rowX + p4) * 2), 0, 0);
+            } else if (t0 + tl < g.L) {
+                uint16_t *py = yg + static_cast<int64_t>(t0 + tl) * rowX + p4;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (p4 + v < pcols) py[v] = f32_to_bf16(yv[v]);
+            }
+        }
+        if (k + 1 < NB) {
+            // the next block into LDS (its buffer was last read in the
+            // previous block, before that block's first barrier), then --
+            // after every read of this block's decay tile -- its decay tile;
+            // rg then receives the rows of block k + 3
+            store_block<NP, VEC, true>(rg, q, nmask, sm.st[(k + 1) & 1]);
+            __syncthreads();
+            if (wave < 3) diag_tile<NP>(sm.st[(k + 1) & 1], sm.M, sm.cum, sm.dl, base + 32, le, sk, wave, lane);
+            if (k + 3 < NB) load_block<NP, VEC, true>(rg, q, Bg, Cg, xg, t0 + base + 96, g, rowBC, rowX, pcols);
+            if (GATE) load_z(k + 1);
+            __syncthreads();
+        }
+    };
+    // NB is even
 #pragma unroll 1
-    for (int item = 0; item < run.items; ++item) {
-        const int hh = run.h0 + item / g.npg, pbase = (item % g.npg) * kPG;
-        const int pcols = g.P - pbase;
-        const float skip = Dskip ? Dskip[hh] : 0.0f;
-        uint16_t *yg = y + run.b * g.L * static_cast<int64_t>(rowX) + hh * g.P + pbase;
-        const uint16_t *zg = GATE ? z + run.b * g.L * static_cast<int64_t>(rowX) + hh * g.P + pbase : nullptr;
-        __syncthreads();   // the previous item's LDS reads are done
-        // state entering the chunk; its loads overlap the decay scan
-        HRegs<NP> hr;
-        load_h<Q, NP>(hr, Hin, g, run, item);
-        chunk_decay_from<Q>(xr.dt, t0, g.L, A[hh] * kLog2e, dt_bias ? dt_bias[hh] : 0.0f, sm.cum,
-                            sm.dl, sm.wsum);
-        if (tid < Q) sm.fs[tid] = fast_exp2(sm.cum[tid | 31] - sm.cum[tid]) * sm.dl[tid];
-        // x^T as step pairs; h_in split into bf16 parts
-#pragma unroll
-        for (int k = 0; k < XRegs<Q, 256>::U; ++k) {
-            const int u = tid + 256 * k;
-            const int s2 = 2 * (u / (kPG / 8)), p8 = (u % (kPG / 8)) * 8;
-            const uint4 v0 = and4(xr.v[k][0], xr.m[k][0]), v1 = and4(xr.v[k][1], xr.m[k][1]);
-            const uint32_t a[4] = {v0.x, v0.y, v0.z, v0.w}, e[4] = {v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                *reinterpret_cast<uint32_t *>(&sm.XT[(p8 + 2 * r) * XP + s2]) = (a[r] & 0xffffu) | (e[r] << 16);
-                *reinterpret_cast<uint32_t *>(&sm.XT[(p8 + 2 * r + 1) * XP + s2]) = (a[r] >> 16) | (e[r] & 0xffff0000u);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < HRegs<NP>::U; ++k) {
-            const int u = tid + 256 * k;
-            const int p = u / (NP / 2), n2 = (u % (NP / 2)) * 2;
-            uint32_t hi, lo;
-            split2(hr.v[k].x, hr.v[k].y, hi, lo);
-            *reinterpret_cast<uint32_t *>(&sm.Hh[p * HP + n2]) = hi;
-            *reinterpret_cast<uint32_t *>(&sm.Hl[p * HP + n2]) = lo;
-        }
-        __syncthreads();
-        // next item's x (the last item re-reads its own; unused)
-        load_x<Q, 256, VEC>(xr, x, dt, g, run, item + 1 < run.items ? item + 1 : item);
-        if (!active) continue;
-
-        // Output tiles Y^T[p][t]: lane (column t, half) holds rows
-        // p(v) = 8 (v / 4) + 4 half + v % 4.
-#pragma unroll
-        for (int which = 0; which < 2; ++which) {
-            const int tb = which == 0 ? wave : NT - 1 - wave;
-            const int tl = tb * 32 + l32;            // this lane's step within the chunk
-            const float cum_t = sm.cum[tl];
-            f16x yd[2] = {zero16(), zero16()};
-            // G'[s][t] = B_s . C_t of source block sb: A operand rows s of B.
-            // The block's LDS operands are all read up front, so their
-            // latencies overlap one another and the matrix-core work instead
-            // of being exposed one product at a time.
-            auto gblock = [&](int sb) {
-                bf8 ab[KN];
-#pragma unroll
-                for (int jn = 0; jn < KN; ++jn)
-                    ab[jn] = *reinterpret_cast<const bf8 *>(&sm.B[(sb * 32 + l32) * BP + 16 * jn + 8 * half]);
-                f16x g = zero16();
-#pragma unroll
-                for (int jn = 0; jn < KN; ++jn) g = mfma(ab[jn], cf[which][jn], g);
-                return g;
-            };
-            // One source block's contribution: build the masked decay tile from
-            // G' and add x^T M^T to the output tile.  DIAG (a compile-time tag)
-            // selects the diagonal block sb = tb.
-            auto mstep = [&](int sb, const f16x &gacc, auto diag_tag) {
-                constexpr bool DIAG = decltype(diag_tag)::value;
-                // x^T operands of the block: A operand row p reads x at
-                // s(8 kk + 0..3) and s(8 kk + 4..7), s(v) as below
-                bf8 xa[2][2];
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                    for (int pt = 0; pt < 2; ++pt) {
-                        const uint16_t *xp = &sm.XT[(pt * 32 + l32) * XP + sb * 32 + 16 * kk + 4 * half];
-                        const uint2 lo4 = *reinterpret_cast<const uint2 *>(xp);
-                        const uint2 hi4 = *reinterpret_cast<const uint2 *>(xp + 8);
-                        xa[kk][pt] = __builtin_bit_cast(bf8, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
-                    }
-                // M[t][s] = G'[s][t] 2^(cum_t - cum_s) dl_s for s <= t (else 0),
-                // at s(v) = 32 sb + 8 (v / 4) + 4 half + v % 4, plus the skip
-                // weight D on the diagonal s = t, so the product with x^T also
-                // forms D x_t.  Off the diagonal block the decay factors as
-                // 2^(cum_t - cb) fs[s], cb the cum at the end of block sb, both
-                // factors <= 1.
-                float mval[16];
-                if constexpr (!DIAG) {
-                    const float et = fast_exp2(cum_t - sm.cum[sb * 32 + 31]);
-#pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        mval[v] = gacc[v] * (et * sm.fs[sb * 32 + 8 * (v / 4) + 4 * half + (v % 4)]);
-                } else {
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int sl = sb * 32 + 8 * (v / 4) + 4 * half + (v % 4);
-                        const float mv = gacc[v] * fast_exp2(cum_t - sm.cum[sl]) * sm.dl[sl];
-                        mval[v] = sl < tl ? mv : (sl == tl ? mv + skip : 0.0f);
-                    }
-                }
-                uint32_t mh[8], ml[8];
-#pragma unroll
-                for (int v = 0; v < 16; v += 2) split2(mval[v], mval[v + 1], mh[v / 2], ml[v / 2]);
-                // Y^T[p][t] += sum_s x^T[p][s] M[t][s], K slot order s(v) as above
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const bf8 bh = __builtin_bit_cast(bf8, make_uint4(mh[4 * kk], mh[4 * kk + 1], mh[4 * kk + 2], mh[4 * kk + 3]));
-                    const bf8 bl = __builtin_bit_cast(bf8, make_uint4(ml[4 * kk], ml[4 * kk + 1], ml[4 * kk + 2], ml[4 * kk + 3]));
-#pragma unroll
-                    for (int pt = 0; pt < 2; ++pt) {
-                        yd[pt] = mfma(xa[kk][pt], bh, yd[pt]);
-                        yd[pt] = mfma(xa[kk][pt], bl, yd[pt]);
-                    }
-                }
-            };
-            // Two-stage pipeline over the blocks below the diagonal: block
-            // sb + 1's G' products are issued in the same straight-line body as
-            // block sb's decay tile and output products, so the matrix cores
-            // work while the vector units build the tile.  The diagonal block,
-            // whose tile needs per-element exponentials and the causal mask,
-            // follows the loop.
-            f16x gnext = gblock(0);
-#pragma unroll 1
-            for (int sb = 0; sb < tb; ++sb) {
-                const f16x gacc = gnext;
-                gnext = gblock(sb + 1);
-                mstep(sb, gacc, std::false_type{});
-            }
-            mstep(tb, gnext, std::true_type{});
-            // Y_off^T[p][t] = sum_n h_in[p][n] C_t[n]; y = (Y_diag (with D x) +
-            // 2^cum_t Y_off) * silu(z) when gated
-            const float et = fast_exp2(cum_t);
-            const int t = t0 + tl;
-            const uint32_t row = static_cast<uint32_t>(t < g.L ? t : 0) * static_cast<uint32_t>(rowX);
-            // Both head-dimension tiles, with the hi and lo parts of h_in in
-            // accumulators of their own: four independent chains of matrix-core
-            // products instead of one dependent chain per tile.  (Rows of a
-            // tile past the slice's columns compute values that are not
-            // stored.)
-            f16x yo2[2][2] = {{zero16(), zero16()}, {zero16(), zero16()}};
-#pragma unroll
-            for (int jn = 0; jn < KN; ++jn) {
-                const int n8 = 16 * jn + 8 * half;
-#pragma unroll
-                for (int pt = 0; pt < 2; ++pt) {
-                    const bf8 ah = *reinterpret_cast<const bf8 *>(&sm.Hh[(pt * 32 + l32) * HP + n8]);
-                    const bf8 al = *reinterpret_cast<const bf8 *>(&sm.Hl[(pt * 32 + l32) * HP + n8]);
-                    yo2[pt][0] = mfma(ah, cf[which][jn], yo2[pt][0]);
-                    yo2[pt][1] = mfma(al, cf[which][jn], yo2[pt][1]);
-                }
-            }
-#pragma unroll
-            for (int pt = 0; pt < 2; ++pt) {
-                if (pt * 32 >= pcols) break;
-                // gate values of this lane's step for the tile's 16 head-dimension
-                // columns (vector path; the element path loads them at the
-                // stores)
-                uint2 zq[4];
-                if (VEC && GATE) {
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const int p = pt * 32 + 8 * q4 + 4 * half;
-                        zq[q4] = p < pcols ? *reinterpret_cast<const uint2 *>(zg + row + p) : make_uint2(0, 0);
-                    }
-                }
-                const f16x yo = yo2[pt][0] + yo2[pt][1];
-                if (t < g.L) {
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        // four consecutive p = pt*32 + 8 q4 + 4 half + 0..3
-                        const int p = pt * 32 + 8 * q4 + 4 * half;
-                        float yv[4];
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) yv[k] = fmaf(et, yo[4 * q4 + k], yd[pt][4 * q4 + k]);
-                        if (GATE) {
-                            float zf[4];
-                            if (VEC) {
-                                zf[0] = bits_lo(zq[q4].x);
-                                zf[1] = bits_hi(zq[q4].x);
-                                zf[2] = bits_lo(zq[q4].y);
-                                zf[3] = bits_hi(zq[q4].y);
-                            } else {
-#pragma unroll
-                                for (int k = 0; k < 4; ++k)
-                                    zf[k] = p + k < pcols ? bf16_to_f32(zg[row + p + k]) : 0.0f;
-                            }
-#pragma unroll
-                            for (int k = 0; k < 4; ++k) yv[k] *= silu(zf[k]);
-                        }
-                        if (VEC) {
-                            if (p < pcols)
-                                *reinterpret_cast<uint2 *>(yg + row + p) =
-                                    make_uint2(pack2(yv[0], yv[1]), pack2(yv[2], yv[3]));
-                        } else {
-#pragma unroll
-                            for (int k = 0; k < 4; ++k)
-                                if (p + k < pcols) yg[row + p + k] = f32_to_bf16(yv[k]);
-                        }
-                    }
-                }
-            }
-        }
+    for (int k = 0; k < NB; k += 2) {
+        step(k, ra);
+        step(k + 1, rb);
     }
-}
-
-// Heads per run: runs never straddle a B / C group, and the grid keeps at
-// least two runs per compute unit when the problem allows.
-int heads_per_run(const SSDArgs &a, int64_t nch) {
-    const int hpg = static_cast<int>(a.H / a.G);
-    int best = 1;
-    for (int d = 1; d <= hpg; ++d) {
-        if (hpg % d) continue;
-        if (a.batch * nch * a.G * (hpg / d) >= 512) best = d;
-    }
-    return best;
 }
 
 template <int Q, int NP>
@@ -735,8 +829,6 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     auto aligned = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
     const bool vecB = a.N % 8 == 0 && aligned(a.B) && aligned(a.C);
     const bool vecX = a.P % 8 == 0 && aligned(a.x) && aligned(a.y) && (!a.z || aligned(a.z));
-    const int hpr = heads_per_run(a, g.nch);
-    const int rpc = static_cast<int>((a.H + hpr - 1) / hpr);
 
     const int64_t chunks = a.batch * g.nch * a.H;
     const int64_t PN = a.P * a.N;
@@ -753,15 +845,15 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     const auto *B = static_cast<const uint16_t *>(a.B);
     const auto *C = static_cast<const uint16_t *>(a.C);
     const auto *zz = static_cast<const uint16_t *>(a.z);
-    const int64_t grid = a.batch * g.nch * rpc;
     const bool vec = vecB && vecX;
-    constexpr int nts = state_threads<Q>();
+    // one workgroup per (batch, chunk, head, 64-column head-dimension slice)
+    const dim3 grid(static_cast<uint32_t>(a.batch * g.nch * a.H * g.npg));
     if (vec)
-        hipLaunchKernelGGL((ssd_state_kernel<Q, NP, true>), dim3(static_cast<uint32_t>(grid)), dim3(nts), 0,
-                           stream, x, dt, a.dt_bias, a.A, B, S, ce, g, rpc, hpr);
+        hipLaunchKernelGGL((ssd_state_kernel<Q, NP, true>), grid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A, B, S,
+                           ce, g);
     else
-        hipLaunchKernelGGL((ssd_state_kernel<Q, NP, false>), dim3(static_cast<uint32_t>(grid)), dim3(nts), 0,
-                           stream, x, dt, a.dt_bias, a.A, B, S, ce, g, rpc, hpr);
+        hipLaunchKernelGGL((ssd_state_kernel<Q, NP, false>), grid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A, B, S,
+                           ce, g);
     e = hipGetLastError();
     if (e == hipSuccess) {
         const int bph = static_cast<int>((PN + 255) / 256);
@@ -773,8 +865,8 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
         decltype(&ssd_output_kernel<Q, NP, true, true>) kern;
         if (zz) kern = vec ? ssd_output_kernel<Q, NP, true, true> : ssd_output_kernel<Q, NP, false, true>;
         else kern = vec ? ssd_output_kernel<Q, NP, true, false> : ssd_output_kernel<Q, NP, false, false>;
-        hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, stream, x, dt, a.dt_bias,
-                           a.A, B, C, a.D, zz, S, static_cast<uint16_t *>(a.y), g, rpc, hpr);
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A, B, C, a.D, zz, S,
+                           static_cast<uint16_t *>(a.y), g);
         e = hipGetLastError();
     }
     const hipError_t ef = hipFreeAsync(mem, stream);
@@ -796,6 +888,8 @@ bool ssd_chunked_supported(const SSDArgs &a) {
     // element offsets within one batch's x and B / C slices fit in 31 bits
     const int64_t lim = int64_t(1) << 31;
     if (a.L * a.H * a.P >= lim || a.L * a.G * a.N >= lim || a.L * a.H >= lim) return false;
+    // byte offsets of a chunk's rows from its first row fit in 31 bits
+    if (a.chunk * a.H * a.P * 2 >= lim || a.chunk * a.G * a.N * 2 >= lim) return false;
     return a.io == IO_BF16 && a.N >= 1 && a.N <= 128 && a.P >= 1 &&
            (a.chunk == 64 || a.chunk == 128 || a.chunk == 256) &&
            a.batch * nch * a.H * ((a.P + kPG - 1) / kPG) < (int64_t(1) << 31) &&

@@ -342,12 +342,11 @@ SSD_SMALL = [
 ]
 
 
-def test_ssd_runs_of_heads(dev):
-    """Many chunks: each workgroup of the matrix-core form serves a run of
-    several heads of one B / C group (two groups here), reusing the staged
-    chunk of B for each of them."""
+def test_ssd_many_chunks_two_groups(dev):
+    """Many chunks (96 per sequence) and two B / C groups: every workgroup of
+    the matrix-core form reads the B and C rows of its head's group."""
     p = inputs.SSDProblem("case", 2, 24576, 8, 32, 32, 2, "bf16", 91)
-    announce("ssd runs of heads %s" % (p,))
+    announce("ssd many chunks, two groups %s" % (p,))
     s = inputs.ssd_inputs(p)
     y, h = run_ssd(ssd_to_dev(s, p.io, dev), _lib.VARIANT_SSD_CHUNKED)
     rng = np.random.default_rng(5)
