@@ -158,6 +158,7 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 // One 32-step block of B, C and x in LDS.
 template <int NP>
 struct __align__(16) BlockStage {
+    static constexpr int XH = 1;         // heads of x staged
     static constexpr int TP = 36;        // BT / XT row pitch (elements; rows 8-byte aligned)
     static constexpr int CP = NP + 4;    // CR row pitch (8-byte reads of 16 rows: distinct banks)
     uint16_t BT[NP * TP];                // BT[n][s] = B at step s, state n
@@ -274,7 +275,9 @@ __device__ __forceinline__ void store_block(const BlockRegs<NP, WC> &r, const Bl
     };
     const bool vm = VEC && nmask;
     if (tid < 2 * NP) pairs(st.BT, q.nb, q.sb, vm ? and4(r.b[0], q.bm) : r.b[0], vm ? and4(r.b[1], q.bm) : r.b[1]);
-    if (tid < 128) pairs(st.XT, q.px, q.sx, r.x[0], r.x[1]);
+    // x: threads 128 q + u hold unit u of head q's tile (Stage::XH heads)
+    if (Stage::XH == 2) pairs(st.XT + (tid >> 7) * (kPG * TP), q.px, q.sx, r.x[0], r.x[1]);
+    else if (tid < 128) pairs(st.XT, q.px, q.sx, r.x[0], r.x[1]);
     if constexpr (WC) {
         constexpr int CP = Stage::CP;
 #pragma unroll
@@ -324,31 +327,35 @@ __device__ void chunk_decay_from(float dr, int t0, int L, float A2, float bias,
 // ---------------------------------------------------------------------------
 // S[p][n] = sum_s w_s x_s[p] B_s[n], w_s = 2^(cum_end - cum_s) dl_s: the
 // output kernel's state update (section 3) without the outputs.  One
-// workgroup per (batch, chunk, head, 64-column slice); wave w accumulates
-// columns p = 16 w + 0..15 over the chunk's 32-step blocks with the same
-// operand orders (B^T rows n and K = steps; (x w) columns p).
-template <int NP>
+// workgroup per (batch, chunk, 64-column slice) and HPW heads of one B / C
+// group (two where the group's head count is even): the block's B^T is
+// staged once and each of its operand reads serves both heads.  Wave w
+// accumulates columns p = 16 w + 0..15 of every head over the chunk's
+// 32-step blocks with the same operand orders (B^T rows n and K = steps;
+// (x w) columns p).
+template <int NP, int HPW>
 struct __align__(16) StateStage {
+    static constexpr int XH = HPW;
     static constexpr int TP = 36;
     uint16_t BT[NP * TP];                // BT[n][s]
-    uint16_t XT[kPG * TP];               // XT[p][s]
+    uint16_t XT[HPW * kPG * TP];         // XT[head][p][s]
 };
-template <int Q, int NP>
+template <int Q, int NP, int HPW>
 struct __align__(16) StateSmem {
-    StateStage<NP> st[2];
-    float cum[Q], dl[Q], w[Q];
+    StateStage<NP, HPW> st[2];
+    float cum[HPW][Q], dl[HPW][Q], w[HPW][Q];
     float wsum[4];
 };
 
-template <int Q, int NP, bool VEC>
-__global__ __launch_bounds__(256, VEC ? 4 : 2) void ssd_state_kernel(
+template <int Q, int NP, bool VEC, int HPW>
+__global__ __launch_bounds__(256, HPW == 2 ? 3 : (VEC ? 4 : 2)) void ssd_state_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt,
     const float *__restrict__ dt_bias, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, float *__restrict__ S, float *__restrict__ ce, Geom g) {
     constexpr int NB = Q / 32;
     constexpr int NJ = NP / 16;
-    constexpr int TP = StateStage<NP>::TP;
-    __shared__ StateSmem<Q, NP> sm;
+    constexpr int TP = StateStage<NP, HPW>::TP;
+    __shared__ StateSmem<Q, NP, HPW> sm;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
@@ -356,61 +363,82 @@ __global__ __launch_bounds__(256, VEC ? 4 : 2) void ssd_state_kernel(
     int64_t id = blockIdx.x;
     const int pg = static_cast<int>(id % g.npg);
     id /= g.npg;
-    const int hh = static_cast<int>(id % g.H);
-    id /= g.H;
+    const int h0 = static_cast<int>(id % (g.H / HPW)) * HPW;
+    id /= g.H / HPW;
     const int c = static_cast<int>(id % g.nch);
     const int64_t b = id / g.nch;
     const int pbase = pg * kPG, pcols = g.P - pbase;
     const int t0 = c * Q;
     const int rowX = g.H * g.P, rowBC = g.G * g.N;
-    const int grp = hh / (g.H / g.G);
+    const int grp = h0 / (g.H / g.G);
     const uint16_t *Bg = Bm + b * g.L * static_cast<int64_t>(rowBC) + grp * g.N;
-    const uint16_t *xg = x + b * g.L * static_cast<int64_t>(rowX) + hh * g.P + pbase;
+    // x rows of this thread's staging head (wave-uniform: waves 0-1 head 0)
+    const int hx = HPW == 2 ? (wave >> 1) : 0;
+    const uint16_t *xg = x + b * g.L * static_cast<int64_t>(rowX) + (h0 + hx) * g.P + pbase;
     const bool nmask = g.N < NP;
     const int pl = 16 * wave + l16;
 
     // dt first, then the first three blocks (register sets as in the output
     // kernel)
     const int tdt = t0 + (tid < Q ? tid : 0);
-    const float dtr = bf16_to_f32(dt[b * g.L * static_cast<int64_t>(g.H) + static_cast<int64_t>(tdt < g.L ? tdt : g.L - 1) * g.H + hh]);
+    const int64_t dto = b * g.L * static_cast<int64_t>(g.H) + static_cast<int64_t>(tdt < g.L ? tdt : g.L - 1) * g.H + h0;
+    float dtr[HPW];
+#pragma unroll
+    for (int hd = 0; hd < HPW; ++hd) dtr[hd] = bf16_to_f32(dt[dto + hd]);
     BlockGeom<NP, false> q;
     block_geom<NP, false>(q, g, rowBC, rowX);
     BlockRegs<NP, false> r0, ra, rb;
     load_block<NP, VEC, false>(r0, q, Bg, nullptr, xg, t0, g, rowBC, rowX, pcols);
     if (NB > 1) load_block<NP, VEC, false>(ra, q, Bg, nullptr, xg, t0 + 32, g, rowBC, rowX, pcols);
     if (NB > 2) load_block<NP, VEC, false>(rb, q, Bg, nullptr, xg, t0 + 64, g, rowBC, rowX, pcols);
-    chunk_decay_from<Q>(dtr, t0, g.L, A[hh] * kLog2e, dt_bias ? dt_bias[hh] : 0.0f, sm.cum, sm.dl, sm.wsum);
-    const float cum_end = sm.cum[Q - 1];
-    if (tid < Q) sm.w[tid] = fast_exp2(cum_end - sm.cum[tid]) * sm.dl[tid];
+    float cum_end[HPW];
+#pragma unroll
+    for (int hd = 0; hd < HPW; ++hd) {
+        const int hh = h0 + hd;
+        chunk_decay_from<Q>(dtr[hd], t0, g.L, A[hh] * kLog2e, dt_bias ? dt_bias[hh] : 0.0f, sm.cum[hd], sm.dl[hd],
+                            sm.wsum);
+        cum_end[hd] = sm.cum[hd][Q - 1];
+        if (tid < Q) sm.w[hd][tid] = fast_exp2(cum_end[hd] - sm.cum[hd][tid]) * sm.dl[hd][tid];
+    }
     store_block<NP, VEC, false>(r0, q, nmask, sm.st[0]);
     __syncthreads();
 
-    f4x acc[NJ];
+    f4x acc[HPW][NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[j] = zero4();
+    for (int hd = 0; hd < HPW; ++hd)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[hd][j] = zero4();
     auto step = [&](const int k, BlockRegs<NP, false> &rg) {
-        const StateStage<NP> &st = sm.st[k & 1];
+        const StateStage<NP, HPW> &st = sm.st[k & 1];
         const int base = 32 * k;
-        // (x w) of the block: column p = pl, K slots s = 16 (i / 4) + 4 g4 + i % 4
-        const uint16_t *xp = &st.XT[pl * TP];
-        const uint2 x0 = *reinterpret_cast<const uint2 *>(xp + swz(4 * g4, pl));
-        const uint2 x1 = *reinterpret_cast<const uint2 *>(xp + swz(16 + 4 * g4, pl));
-        const float4 f0 = *reinterpret_cast<const float4 *>(&sm.w[base + 4 * g4]);
-        const float4 f1 = *reinterpret_cast<const float4 *>(&sm.w[base + 16 + 4 * g4]);
-        uint32_t xh[4], xl[4];
-        split_pk(bits_lo(x0.x) * f0.x, bits_hi(x0.x) * f0.y, xh[0], xl[0]);
-        split_pk(bits_lo(x0.y) * f0.z, bits_hi(x0.y) * f0.w, xh[1], xl[1]);
-        split_pk(bits_lo(x1.x) * f1.x, bits_hi(x1.x) * f1.y, xh[2], xl[2]);
-        split_pk(bits_lo(x1.y) * f1.z, bits_hi(x1.y) * f1.w, xh[3], xl[3]);
-        const bf8 xwh = __builtin_bit_cast(bf8, make_uint4(xh[0], xh[1], xh[2], xh[3]));
-        const bf8 xwl = __builtin_bit_cast(bf8, make_uint4(xl[0], xl[1], xl[2], xl[3]));
+        // (x w) of the block for each head: column p = pl, K slots
+        // s = 16 (i / 4) + 4 g4 + i % 4
+        bf8 xwh[HPW], xwl[HPW];
+#pragma unroll
+        for (int hd = 0; hd < HPW; ++hd) {
+            const uint16_t *xp = &st.XT[(hd * kPG + pl) * TP];
+            const uint2 x0 = *reinterpret_cast<const uint2 *>(xp + swz(4 * g4, pl));
+            const uint2 x1 = *reinterpret_cast<const uint2 *>(xp + swz(16 + 4 * g4, pl));
+            const float4 f0 = *reinterpret_cast<const float4 *>(&sm.w[hd][base + 4 * g4]);
+            const float4 f1 = *reinterpret_cast<const float4 *>(&sm.w[hd][base + 16 + 4 * g4]);
+            uint32_t xh[4], xl[4];
+            split_pk(bits_lo(x0.x) * f0.x, bits_hi(x0.x) * f0.y, xh[0], xl[0]);
+            split_pk(bits_lo(x0.y) * f0.z, bits_hi(x0.y) * f0.w, xh[1], xl[1]);
+            split_pk(bits_lo(x1.x) * f1.x, bits_hi(x1.x) * f1.y, xh[2], xl[2]);
+            split_pk(bits_lo(x1.y) * f1.z, bits_hi(x1.y) * f1.w, xh[3], xl[3]);
+            xwh[hd] = __builtin_bit_cast(bf8, make_uint4(xh[0], xh[1], xh[2], xh[3]));
+            xwl[hd] = __builtin_bit_cast(bf8, make_uint4(xl[0], xl[1], xl[2], xl[3]));
+        }
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const uint16_t *bp = &st.BT[(16 * j + l16) * TP];
             const bf8 bt = cat8(*reinterpret_cast<const uint2 *>(bp + swz(4 * g4, 16 * j)),
                                 *reinterpret_cast<const uint2 *>(bp + swz(16 + 4 * g4, 16 * j)));
-            acc[j] = mfma16(bt, xwh, acc[j]);
-            acc[j] = mfma16(bt, xwl, acc[j]);
+#pragma unroll
+            for (int hd = 0; hd < HPW; ++hd) {
+                acc[hd][j] = mfma16(bt, xwh[hd], acc[hd][j]);
+                acc[hd][j] = mfma16(bt, xwl[hd], acc[hd][j]);
+            }
         }
         if (k + 1 < NB) {
             // the next block into LDS: its buffer was last read in the
@@ -425,22 +453,26 @@ __global__ __launch_bounds__(256, VEC ? 4 : 2) void ssd_state_kernel(
         step(k, ra);
         step(k + 1, rb);
     }
-    // lane (l16, g4) holds S[pl][16 j + 4 g4 + v]
+    // lane (l16, g4) holds S[pl][16 j + 4 g4 + v] of each head
     if (pl < pcols) {
-        float *Sg = S + (((b * g.nch + c) * g.H + hh) * static_cast<int64_t>(g.P) + pbase + pl) * g.N;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int n4 = 16 * j + 4 * g4;
-            if (VEC) {
-                if (n4 < g.N) *reinterpret_cast<float4 *>(Sg + n4) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
-            } else {
+        for (int hd = 0; hd < HPW; ++hd) {
+            float *Sg = S + (((b * g.nch + c) * g.H + h0 + hd) * static_cast<int64_t>(g.P) + pbase + pl) * g.N;
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (n4 + v < g.N) Sg[n4 + v] = acc[j][v];
+            for (int j = 0; j < NJ; ++j) {
+                const int n4 = 16 * j + 4 * g4;
+                if (VEC) {
+                    if (n4 < g.N)
+                        *reinterpret_cast<float4 *>(Sg + n4) = make_float4(acc[hd][j][0], acc[hd][j][1], acc[hd][j][2], acc[hd][j][3]);
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (n4 + v < g.N) Sg[n4 + v] = acc[hd][j][v];
+                }
             }
         }
     }
-    if (pbase == 0 && tid == 0) ce[(b * g.nch + c) * g.H + hh] = cum_end;
+    if (pbase == 0 && tid < HPW) ce[(b * g.nch + c) * g.H + h0 + tid] = cum_end[tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -848,12 +880,22 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     const bool vec = vecB && vecX;
     // one workgroup per (batch, chunk, head, 64-column head-dimension slice)
     const dim3 grid(static_cast<uint32_t>(a.batch * g.nch * a.H * g.npg));
-    if (vec)
-        hipLaunchKernelGGL((ssd_state_kernel<Q, NP, true>), grid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A, B, S,
-                           ce, g);
+    // chunk states: two heads per workgroup where each group's head count is
+    // even
+    const bool pairs = (a.H / a.G) % 2 == 0;
+    const dim3 sgrid(static_cast<uint32_t>(a.batch * g.nch * (pairs ? a.H / 2 : a.H) * g.npg));
+    if (vec && pairs)
+        hipLaunchKernelGGL((ssd_state_kernel<Q, NP, true, 2>), sgrid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A,
+                           B, S, ce, g);
+    else if (vec)
+        hipLaunchKernelGGL((ssd_state_kernel<Q, NP, true, 1>), sgrid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A,
+                           B, S, ce, g);
+    else if (pairs)
+        hipLaunchKernelGGL((ssd_state_kernel<Q, NP, false, 2>), sgrid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A,
+                           B, S, ce, g);
     else
-        hipLaunchKernelGGL((ssd_state_kernel<Q, NP, false>), grid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A, B, S,
-                           ce, g);
+        hipLaunchKernelGGL((ssd_state_kernel<Q, NP, false, 1>), sgrid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A,
+                           B, S, ce, g);
     e = hipGetLastError();
     if (e == hipSuccess) {
         const int bph = static_cast<int>((PN + 255) / 256);
