@@ -156,21 +156,21 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 
 // One 32-step block of B, C and x in LDS.
-template <int NP>
+template <int NP, int HPW = 1>
 struct __align__(16) BlockStage {
-    static constexpr int XH = 1;         // heads of x staged
+    static constexpr int XH = HPW;       // heads of x staged
     static constexpr int TP = 36;        // BT / XT row pitch (elements; rows 8-byte aligned)
     static constexpr int CP = NP + 4;    // CR row pitch (8-byte reads of 16 rows: distinct banks)
     uint16_t BT[NP * TP];                // BT[n][s] = B at step s, state n
     uint16_t CR[32 * CP];                // CR[t][n] = C at step t, state n
-    uint16_t XT[kPG * TP];               // XT[p][s] = x at step s, column p
+    uint16_t XT[HPW * kPG * TP];         // XT[head][p][s] = x at step s, column p
 };
-template <int Q, int NP>
+template <int Q, int NP, int HPW>
 struct __align__(16) OutSmem {
-    BlockStage<NP> st[2];                // blocks k and k + 1 of the walk
-    uint4 M[2][2][64];                   // diagonal decay tile: [t tile][hi, lo][lane]
-    float cum[Q], dl[Q];
-    float fs[Q];                         // 2^(cum at the end of s's block - cum_s) dl_s
+    BlockStage<NP, HPW> st[2];           // blocks k and k + 1 of the walk
+    uint4 M[HPW][2][2][64];              // diagonal decay tile: [head][t tile][hi, lo][lane]
+    float cum[HPW][Q], dl[HPW][Q];
+    float fs[HPW][Q];                    // 2^(cum at the end of s's block - cum_s) dl_s
     float wsum[4];
 };
 
@@ -547,16 +547,16 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(float *__restrict__ S,
 // x.  Waves 0-2 form the tile's three causal 16 x 16 quadrants one block
 // ahead and share them through LDS.
 // Waves 0, 1, 2: quadrant (sq, tq) = (0, 0), (0, 1), (1, 1) of the diagonal
-// tile of the block at chunk step `base`:
+// tile of the block at chunk step `base`, for each of the HPW heads:
 //   M[t][s] = (C_t . B_s) 2^(cum_t - cum_s) dl_s for s < t, plus D at s = t,
 // written split into bf16 parts as K slots 4 sq .. 4 sq + 3 of the B operand
-// of t tile tq.  le[v] (1 for s <= t, else 0) and sk[v] (D at s = t, else 0)
+// of t tile tq.  The product C . B is the same for every head of the group.
+// le[v] (1 for s <= t, else 0) and sk[h][v] (head h's D at s = t, else 0)
 // depend only on the lane, not on the block.
-template <int NP>
-__device__ __forceinline__ void diag_tile(const BlockStage<NP> &st, uint4 (&Mo)[2][2][64], const float *cum,
-                                          const float *dl, int base, const float (&le)[4],
-                                          const float (&sk)[4], int wave, int lane) {
-    constexpr int TP = BlockStage<NP>::TP, CP = BlockStage<NP>::CP;
+template <int Q, int NP, int HPW>
+__device__ __forceinline__ void diag_tile(const BlockStage<NP, HPW> &st, OutSmem<Q, NP, HPW> &sm, int base,
+                                          const float (&le)[4], const float (&sk)[HPW][4], int wave, int lane) {
+    constexpr int TP = BlockStage<NP, HPW>::TP, CP = BlockStage<NP, HPW>::CP;
     const int sq = wave == 2 ? 1 : 0, tq = wave == 0 ? 0 : 1;
     const int l16 = lane & 15, g4 = lane >> 4;
     f4x G = zero4();
@@ -578,29 +578,34 @@ __device__ __forceinline__ void diag_tile(const BlockStage<NP> &st, uint4 (&Mo)[
     }
     // G[v]: step s = base + 16 sq + 4 g4 + v, column t = base + 16 tq + l16
     const int t = base + 16 * tq + l16, s0 = base + 16 * sq + 4 * g4;
-    const float ct = cum[t];
-    const float4 cs = *reinterpret_cast<const float4 *>(&cum[s0]);
-    const float4 ds = *reinterpret_cast<const float4 *>(&dl[s0]);
-    const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, dsv[4] = {ds.x, ds.y, ds.z, ds.w};
-    float mv[4];
-    // (2^(ct - cs) overflows only where s > t, and le = 0 there selects 0)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const float m = G[v] * fast_exp2(ct - csv[v]) * dsv[v];
-        mv[v] = le[v] != 0.0f ? m + sk[v] : 0.0f;
+    for (int hd = 0; hd < HPW; ++hd) {
+        const float ct = sm.cum[hd][t];
+        const float4 cs = *reinterpret_cast<const float4 *>(&sm.cum[hd][s0]);
+        const float4 ds = *reinterpret_cast<const float4 *>(&sm.dl[hd][s0]);
+        const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, dsv[4] = {ds.x, ds.y, ds.z, ds.w};
+        float mv[4];
+        // (2^(ct - cs) overflows only where s > t, and le = 0 there selects 0)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float m = G[v] * fast_exp2(ct - csv[v]) * dsv[v];
+            mv[v] = le[v] != 0.0f ? m + sk[hd][v] : 0.0f;
+        }
+        uint32_t h0, l0, h1, l1;
+        split_pk(mv[0], mv[1], h0, l0);
+        split_pk(mv[2], mv[3], h1, l1);
+        reinterpret_cast<uint2 *>(&sm.M[hd][tq][0][lane])[sq] = make_uint2(h0, h1);
+        reinterpret_cast<uint2 *>(&sm.M[hd][tq][1][lane])[sq] = make_uint2(l0, l1);
     }
-    uint32_t h0, l0, h1, l1;
-    split_pk(mv[0], mv[1], h0, l0);
-    split_pk(mv[2], mv[3], h1, l1);
-    reinterpret_cast<uint2 *>(&Mo[tq][0][lane])[sq] = make_uint2(h0, h1);
-    reinterpret_cast<uint2 *>(&Mo[tq][1][lane])[sq] = make_uint2(l0, l1);
 }
 
-// Three workgroups per compute unit on the vector path without a gate
-// (LDS and registers allow it); two otherwise, where the gate values or the
-// element loads need more registers.
-template <int Q, int NP, bool VEC, bool GATE>
-__global__ __launch_bounds__(256, (VEC && !GATE) ? 3 : 2) void ssd_output_kernel(
+// HPW heads of one B / C group per workgroup: two share the block's staged
+// B and C, its C . B quadrants and every B and C operand read, and give each
+// wave two independent chains; one otherwise (a group with an odd head
+// count).  Workgroups per compute unit: three for one head on the vector
+// path without a gate (LDS and registers allow it), two otherwise.
+template <int Q, int NP, bool VEC, bool GATE, int HPW>
+__global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_output_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt,
     const float *__restrict__ dt_bias, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm,
@@ -609,9 +614,9 @@ __global__ __launch_bounds__(256, (VEC && !GATE) ? 3 : 2) void ssd_output_kernel
     constexpr int NB = Q / 32;          // blocks per chunk
     constexpr int NJ = NP / 16;         // 16-wide state tiles
     constexpr int KK = NP / 32;         // K steps over the state index
-    using St = BlockStage<NP>;
+    using St = BlockStage<NP, HPW>;
     constexpr int TP = St::TP, CP = St::CP;
-    __shared__ OutSmem<Q, NP> sm;
+    __shared__ OutSmem<Q, NP, HPW> sm;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
@@ -619,39 +624,47 @@ __global__ __launch_bounds__(256, (VEC && !GATE) ? 3 : 2) void ssd_output_kernel
     int64_t id = blockIdx.x;
     const int pg = static_cast<int>(id % g.npg);
     id /= g.npg;
-    const int hh = static_cast<int>(id % g.H);
-    id /= g.H;
+    const int h0 = static_cast<int>(id % (g.H / HPW)) * HPW;
+    id /= g.H / HPW;
     const int c = static_cast<int>(id % g.nch);
     const int64_t b = id / g.nch;
     const int pbase = pg * kPG, pcols = g.P - pbase;
     const int t0 = c * Q;
     const int rowX = g.H * g.P, rowBC = g.G * g.N;
-    const int grp = hh / (g.H / g.G);
+    const int grp = h0 / (g.H / g.G);
     const uint16_t *Bg = Bm + b * g.L * static_cast<int64_t>(rowBC) + grp * g.N;
     const uint16_t *Cg = Cm + b * g.L * static_cast<int64_t>(rowBC) + grp * g.N;
-    const int64_t xoff = b * g.L * static_cast<int64_t>(rowX) + hh * g.P + pbase;
-    const uint16_t *xg = x + xoff;
-    uint16_t *yg = y + xoff;
-    const float skip = Dskip ? Dskip[hh] : 0.0f;
+    // element offset of head h0's slice in its batch's first row (head
+    // h0 + hd: hd P further)
+    const int64_t xoff = b * g.L * static_cast<int64_t>(rowX) + h0 * g.P + pbase;
+    // x rows of this thread's staging head (wave-uniform: waves 0-1 head 0)
+    const uint16_t *xg = x + xoff + (HPW == 2 ? (wave >> 1) : 0) * g.P;
     const bool nmask = g.N < NP;
     const int pl = 16 * wave + l16;     // column of this lane's A rows / B columns
     const int p4 = 16 * wave + 4 * g4;  // first of this lane's four output columns
+    float skip[HPW];
+#pragma unroll
+    for (int hd = 0; hd < HPW; ++hd) skip[hd] = Dskip ? Dskip[h0 + hd] : 0.0f;
 
-    // the first two blocks' rows, and the state entering the chunk
     // dt first (the decay scan waits for it), then the first three blocks'
     // rows: block j + 1 is stored to LDS at the end of block j, from the
-    // register set ra (j even) or rb (j odd), which then receives block j + 3
+    // register set ra (j even) or rb (j odd), which then receives block j + 3;
+    // then the state entering the chunk
     const int tdt = t0 + (tid < Q ? tid : 0);
-    const float dtr = bf16_to_f32(dt[b * g.L * static_cast<int64_t>(g.H) + static_cast<int64_t>(tdt < g.L ? tdt : g.L - 1) * g.H + hh]);
+    const int64_t dto = b * g.L * static_cast<int64_t>(g.H) + static_cast<int64_t>(tdt < g.L ? tdt : g.L - 1) * g.H + h0;
+    float dtr[HPW];
+#pragma unroll
+    for (int hd = 0; hd < HPW; ++hd) dtr[hd] = bf16_to_f32(dt[dto + hd]);
     BlockGeom<NP, true> q;
     block_geom<NP, true>(q, g, rowBC, rowX);
     BlockRegs<NP, true> r0, ra, rb;
     load_block<NP, VEC, true>(r0, q, Bg, Cg, xg, t0, g, rowBC, rowX, pcols);
     if (NB > 1) load_block<NP, VEC, true>(ra, q, Bg, Cg, xg, t0 + 32, g, rowBC, rowX, pcols);
     if (NB > 2) load_block<NP, VEC, true>(rb, q, Bg, Cg, xg, t0 + 64, g, rowBC, rowX, pcols);
-    f4x H[NJ];
-    {
-        const float *Hg = Hin + ((b * g.nch + c) * g.H + hh) * static_cast<int64_t>(g.P) * g.N;
+    f4x H[HPW][NJ];
+#pragma unroll
+    for (int hd = 0; hd < HPW; ++hd) {
+        const float *Hg = Hin + ((b * g.nch + c) * g.H + h0 + hd) * static_cast<int64_t>(g.P) * g.N;
         const bool okp = pl < pcols;
         const float *hrow = Hg + static_cast<int64_t>(okp ? pbase + pl : 0) * g.N;
 #pragma unroll
@@ -662,179 +675,230 @@ __global__ __launch_bounds__(256, (VEC && !GATE) ? 3 : 2) void ssd_output_kernel
                 const bool ok = okp && n4 < g.N;
                 const uint32_t m = opaque_mask(ok);
                 const float4 v = *reinterpret_cast<const float4 *>(hrow + (ok ? n4 : 0));
-                H[j][0] = __uint_as_float(__float_as_uint(v.x) & m);
-                H[j][1] = __uint_as_float(__float_as_uint(v.y) & m);
-                H[j][2] = __uint_as_float(__float_as_uint(v.z) & m);
-                H[j][3] = __uint_as_float(__float_as_uint(v.w) & m);
+                H[hd][j][0] = __uint_as_float(__float_as_uint(v.x) & m);
+                H[hd][j][1] = __uint_as_float(__float_as_uint(v.y) & m);
+                H[hd][j][2] = __uint_as_float(__float_as_uint(v.z) & m);
+                H[hd][j][3] = __uint_as_float(__float_as_uint(v.w) & m);
             } else {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const bool ok = okp && n4 + v < g.N;
                     const float e = hrow[ok ? n4 + v : 0];
-                    H[j][v] = ok ? e : 0.0f;
+                    H[hd][j][v] = ok ? e : 0.0f;
                 }
             }
         }
     }
-    chunk_decay_from<Q>(dtr, t0, g.L, A[hh] * kLog2e, dt_bias ? dt_bias[hh] : 0.0f, sm.cum, sm.dl, sm.wsum);
-    if (tid < Q) sm.fs[tid] = fast_exp2(sm.cum[tid | 31] - sm.cum[tid]) * sm.dl[tid];
+#pragma unroll
+    for (int hd = 0; hd < HPW; ++hd) {
+        const int hh = h0 + hd;
+        chunk_decay_from<Q>(dtr[hd], t0, g.L, A[hh] * kLog2e, dt_bias ? dt_bias[hh] : 0.0f, sm.cum[hd], sm.dl[hd],
+                            sm.wsum);
+        if (tid < Q) sm.fs[hd][tid] = fast_exp2(sm.cum[hd][tid | 31] - sm.cum[hd][tid]) * sm.dl[hd][tid];
+    }
     // K slots 4..7 of t tile 0 (steps 16..31, after every step of the tile)
     // stay zero; no quadrant writes them
     if (wave == 3) {
 #pragma unroll
-        for (int hl = 0; hl < 2; ++hl) reinterpret_cast<uint2 *>(&sm.M[0][hl][lane])[1] = make_uint2(0, 0);
+        for (int hd = 0; hd < HPW; ++hd)
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) reinterpret_cast<uint2 *>(&sm.M[hd][0][hl][lane])[1] = make_uint2(0, 0);
     }
     // causal mask of this lane's diagonal-tile quadrant (waves 0-2)
-    float le[4], sk[4];
+    float le[4], sk[HPW][4];
     {
         const int sq = wave == 2 ? 1 : 0, tq = wave == 0 ? 0 : 1;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int sr = 16 * sq + 4 * g4 + v, tr = 16 * tq + l16;
             le[v] = sr <= tr ? 1.0f : 0.0f;
-            sk[v] = sr == tr ? skip : 0.0f;
+#pragma unroll
+            for (int hd = 0; hd < HPW; ++hd) sk[hd][v] = sr == tr ? skip[hd] : 0.0f;
         }
     }
     store_block<NP, VEC, true>(r0, q, nmask, sm.st[0]);
     __syncthreads();
-    if (wave < 3) diag_tile<NP>(sm.st[0], sm.M, sm.cum, sm.dl, 0, le, sk, wave, lane);
+    if (wave < 3) diag_tile<Q, NP, HPW>(sm.st[0], sm, 0, le, sk, wave, lane);
     // gate values of this lane's steps of the current block, four columns each
-    uint2 zr[2] = {make_uint2(0, 0), make_uint2(0, 0)};
+    uint2 zr[HPW][2];
+#pragma unroll
+    for (int hd = 0; hd < HPW; ++hd) zr[hd][0] = zr[hd][1] = make_uint2(0, 0);
     auto load_z = [&](int kb) {
 #pragma unroll
-        for (int tq = 0; tq < 2; ++tq) {
-            const int t = t0 + 32 * kb + 16 * tq + l16;
-            const int tc = t < g.L ? t : g.L - 1;
-            const uint16_t *zp = z + xoff + static_cast<int64_t>(tc) * rowX;
-            if (VEC) {
-                const uint32_t m = opaque_mask(p4 < pcols);
-                const uint2 v = *reinterpret_cast<const uint2 *>(zp + (p4 < pcols ? p4 : 0));
-                zr[tq] = make_uint2(v.x & m, v.y & m);
-            } else {
-                uint16_t e[4];
+        for (int hd = 0; hd < HPW; ++hd)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) e[v] = p4 + v < pcols ? zp[p4 + v] : 0;
-                zr[tq] = make_uint2(e[0] | (static_cast<uint32_t>(e[1]) << 16), e[2] | (static_cast<uint32_t>(e[3]) << 16));
+            for (int tq = 0; tq < 2; ++tq) {
+                const int t = t0 + 32 * kb + 16 * tq + l16;
+                const int tc = t < g.L ? t : g.L - 1;
+                const uint16_t *zp = z + xoff + hd * g.P + static_cast<int64_t>(tc) * rowX;
+                if (VEC) {
+                    const uint32_t m = opaque_mask(p4 < pcols);
+                    const uint2 v = *reinterpret_cast<const uint2 *>(zp + (p4 < pcols ? p4 : 0));
+                    zr[hd][tq] = make_uint2(v.x & m, v.y & m);
+                } else {
+                    uint16_t e[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) e[v] = p4 + v < pcols ? zp[p4 + v] : 0;
+                    zr[hd][tq] = make_uint2(e[0] | (static_cast<uint32_t>(e[1]) << 16),
+                                            e[2] | (static_cast<uint32_t>(e[3]) << 16));
+                }
             }
-        }
     };
     if (GATE) load_z(0);
-    // y of the chunk's rows, stores past the sequence end dropped
+    // y of the chunk's rows from head h0's slice on (the second head's columns
+    // are P further), stores past the sequence end dropped
+    uint16_t *yg = y + xoff;
     const auto ry = brsrc(yg + static_cast<int64_t>(t0) * rowX,
-                          static_cast<int64_t>(g.L - t0) * rowX * 2 - static_cast<int64_t>(rowX - pcols) * 2);
+                          static_cast<int64_t>(g.L - t0) * rowX * 2 -
+                              static_cast<int64_t>(rowX - pcols - (HPW - 1) * g.P) * 2);
     __syncthreads();
 
-    // The state is carried as H = sig * Hs with sig a workgroup-uniform
-    // scalar, so a block's decay multiplies sig (and the block's new terms
-    // by 1 / sig) instead of every state element; when sig would fall below
-    // 2^-64 it is folded back into Hs.
-    float sig = 1.0f;
+    // Each head's state is carried as H = sig * Hs with sig a
+    // workgroup-uniform scalar, so a block's decay multiplies sig (and the
+    // block's new terms by 1 / sig) instead of every state element; when sig
+    // would fall below 2^-64 it is folded back into Hs.
+    float sig[HPW];
+#pragma unroll
+    for (int hd = 0; hd < HPW; ++hd) sig[hd] = 1.0f;
     auto step = [&](const int k, BlockRegs<NP, true> &rg) {
         const St &st = sm.st[k & 1];
         const int base = 32 * k;
-        const float ck = k > 0 ? sm.cum[base - 1] : 0.0f;
-        // x of the block: row p = pl, K slots s = 16 (i / 4) + 4 g4 + i % 4
-        const uint16_t *xp = &st.XT[pl * TP];
-        const uint2 x0 = *reinterpret_cast<const uint2 *>(xp + swz(4 * g4, pl));
-        const uint2 x1 = *reinterpret_cast<const uint2 *>(xp + swz(16 + 4 * g4, pl));
-        const bf8 xa = cat8(x0, x1);
-        // output: Y^T = Hs_k C^T (state part; hi and lo parts of Hs_k in
-        // chains of their own) and the diagonal tile's x^T M^T
-        f4x ys[2][2], yd[2];
+        float ck[HPW];
+        uint2 x0[HPW], x1[HPW];
+        bf8 xa[HPW];
 #pragma unroll
-        for (int tq = 0; tq < 2; ++tq) ys[tq][0] = ys[tq][1] = zero4();
+        for (int hd = 0; hd < HPW; ++hd) {
+            ck[hd] = k > 0 ? sm.cum[hd][base - 1] : 0.0f;
+            // x of the block: row p = pl, K slots s = 16 (i / 4) + 4 g4 + i % 4
+            const uint16_t *xp = &st.XT[(hd * kPG + pl) * TP];
+            x0[hd] = *reinterpret_cast<const uint2 *>(xp + swz(4 * g4, pl));
+            x1[hd] = *reinterpret_cast<const uint2 *>(xp + swz(16 + 4 * g4, pl));
+            xa[hd] = cat8(x0[hd], x1[hd]);
+        }
+        // output: Y^T = Hs_k C^T (state part; one head: hi and lo parts of Hs_k
+        // in chains of their own) and the diagonal tile's x^T M^T
+        constexpr int YC = HPW == 1 ? 2 : 1;
+        f4x ys[HPW][2][YC], yd[HPW][2];
+#pragma unroll
+        for (int hd = 0; hd < HPW; ++hd)
+#pragma unroll
+            for (int tq = 0; tq < 2; ++tq)
+#pragma unroll
+                for (int e = 0; e < YC; ++e) ys[hd][tq][e] = zero4();
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            uint32_t hw[4], lw[4];
-            split_pk(H[2 * kk][0], H[2 * kk][1], hw[0], lw[0]);
-            split_pk(H[2 * kk][2], H[2 * kk][3], hw[1], lw[1]);
-            split_pk(H[2 * kk + 1][0], H[2 * kk + 1][1], hw[2], lw[2]);
-            split_pk(H[2 * kk + 1][2], H[2 * kk + 1][3], hw[3], lw[3]);
-            const bf8 ah = __builtin_bit_cast(bf8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-            const bf8 al = __builtin_bit_cast(bf8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+            bf8 cb[2];
 #pragma unroll
             for (int tq = 0; tq < 2; ++tq) {
                 const uint16_t *cp = &st.CR[(16 * tq + l16) * CP + 32 * kk + 4 * g4];
-                const bf8 cb = cat8(*reinterpret_cast<const uint2 *>(cp), *reinterpret_cast<const uint2 *>(cp + 16));
-                ys[tq][0] = mfma16(ah, cb, ys[tq][0]);
-                ys[tq][1] = mfma16(al, cb, ys[tq][1]);
+                cb[tq] = cat8(*reinterpret_cast<const uint2 *>(cp), *reinterpret_cast<const uint2 *>(cp + 16));
+            }
+#pragma unroll
+            for (int hd = 0; hd < HPW; ++hd) {
+                uint32_t hw[4], lw[4];
+                split_pk(H[hd][2 * kk][0], H[hd][2 * kk][1], hw[0], lw[0]);
+                split_pk(H[hd][2 * kk][2], H[hd][2 * kk][3], hw[1], lw[1]);
+                split_pk(H[hd][2 * kk + 1][0], H[hd][2 * kk + 1][1], hw[2], lw[2]);
+                split_pk(H[hd][2 * kk + 1][2], H[hd][2 * kk + 1][3], hw[3], lw[3]);
+                const bf8 ah = __builtin_bit_cast(bf8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+                const bf8 al = __builtin_bit_cast(bf8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+#pragma unroll
+                for (int tq = 0; tq < 2; ++tq) {
+                    ys[hd][tq][0] = mfma16(ah, cb[tq], ys[hd][tq][0]);
+                    ys[hd][tq][YC - 1] = mfma16(al, cb[tq], ys[hd][tq][YC - 1]);
+                }
             }
         }
 #pragma unroll
-        for (int tq = 0; tq < 2; ++tq) {
-            const bf8 mh = __builtin_bit_cast(bf8, sm.M[tq][0][lane]);
-            const bf8 ml = __builtin_bit_cast(bf8, sm.M[tq][1][lane]);
-            yd[tq] = mfma16(xa, mh, zero4());
-            yd[tq] = mfma16(xa, ml, yd[tq]);
-        }
-        const float sig_k = sig;
+        for (int hd = 0; hd < HPW; ++hd)
+#pragma unroll
+            for (int tq = 0; tq < 2; ++tq) {
+                const bf8 mh = __builtin_bit_cast(bf8, sm.M[hd][tq][0][lane]);
+                const bf8 ml = __builtin_bit_cast(bf8, sm.M[hd][tq][1][lane]);
+                yd[hd][tq] = mfma16(xa[hd], mh, zero4());
+                yd[hd][tq] = mfma16(xa[hd], ml, yd[hd][tq]);
+            }
+        float sig_k[HPW];
+#pragma unroll
+        for (int hd = 0; hd < HPW; ++hd) sig_k[hd] = sig[hd];
         // state entering the next block: H_{k+1} = 2^(e_k - c_k) H_k + dH_k
         if (k + 1 < NB) {
-            const float rk = fast_exp2(sm.cum[base + 31] - ck);
-            const float sn = sig * rk;
-            float wsc = 1.0f;             // weight of the block's new terms
-            if (sn >= 0x1p-64f) {
-                wsc = __builtin_amdgcn_rcpf(sn);
-                sig = sn;
-            } else {
+            bf8 xwh[HPW], xwl[HPW];
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) H[j] = H[j] * sn;
-                sig = 1.0f;
+            for (int hd = 0; hd < HPW; ++hd) {
+                const float rk = fast_exp2(sm.cum[hd][base + 31] - ck[hd]);
+                const float sn = sig[hd] * rk;
+                float wsc = 1.0f;             // weight of the block's new terms
+                if (sn >= 0x1p-64f) {
+                    wsc = __builtin_amdgcn_rcpf(sn);
+                    sig[hd] = sn;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) H[hd][j] = H[hd][j] * sn;
+                    sig[hd] = 1.0f;
+                }
+                const float4 f0 = *reinterpret_cast<const float4 *>(&sm.fs[hd][base + 4 * g4]);
+                const float4 f1 = *reinterpret_cast<const float4 *>(&sm.fs[hd][base + 16 + 4 * g4]);
+                uint32_t xh[4], xl[4];
+                split_pk(bits_lo(x0[hd].x) * f0.x * wsc, bits_hi(x0[hd].x) * f0.y * wsc, xh[0], xl[0]);
+                split_pk(bits_lo(x0[hd].y) * f0.z * wsc, bits_hi(x0[hd].y) * f0.w * wsc, xh[1], xl[1]);
+                split_pk(bits_lo(x1[hd].x) * f1.x * wsc, bits_hi(x1[hd].x) * f1.y * wsc, xh[2], xl[2]);
+                split_pk(bits_lo(x1[hd].y) * f1.z * wsc, bits_hi(x1[hd].y) * f1.w * wsc, xh[3], xl[3]);
+                xwh[hd] = __builtin_bit_cast(bf8, make_uint4(xh[0], xh[1], xh[2], xh[3]));
+                xwl[hd] = __builtin_bit_cast(bf8, make_uint4(xl[0], xl[1], xl[2], xl[3]));
             }
-            const float4 f0 = *reinterpret_cast<const float4 *>(&sm.fs[base + 4 * g4]);
-            const float4 f1 = *reinterpret_cast<const float4 *>(&sm.fs[base + 16 + 4 * g4]);
-            uint32_t xh[4], xl[4];
-            split_pk(bits_lo(x0.x) * f0.x * wsc, bits_hi(x0.x) * f0.y * wsc, xh[0], xl[0]);
-            split_pk(bits_lo(x0.y) * f0.z * wsc, bits_hi(x0.y) * f0.w * wsc, xh[1], xl[1]);
-            split_pk(bits_lo(x1.x) * f1.x * wsc, bits_hi(x1.x) * f1.y * wsc, xh[2], xl[2]);
-            split_pk(bits_lo(x1.y) * f1.z * wsc, bits_hi(x1.y) * f1.w * wsc, xh[3], xl[3]);
-            const bf8 xwh = __builtin_bit_cast(bf8, make_uint4(xh[0], xh[1], xh[2], xh[3]));
-            const bf8 xwl = __builtin_bit_cast(bf8, make_uint4(xl[0], xl[1], xl[2], xl[3]));
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const uint16_t *bp = &st.BT[(16 * j + l16) * TP];
                 const bf8 bt = cat8(*reinterpret_cast<const uint2 *>(bp + swz(4 * g4, 16 * j)),
                                     *reinterpret_cast<const uint2 *>(bp + swz(16 + 4 * g4, 16 * j)));
-                H[j] = mfma16(bt, xwh, H[j]);
-                H[j] = mfma16(bt, xwl, H[j]);
+#pragma unroll
+                for (int hd = 0; hd < HPW; ++hd) {
+                    H[hd][j] = mfma16(bt, xwh[hd], H[hd][j]);
+                    H[hd][j] = mfma16(bt, xwl[hd], H[hd][j]);
+                }
             }
         }
         // y at this lane's steps of the block, four columns each
 #pragma unroll
-        for (int tq = 0; tq < 2; ++tq) {
-            const int tl = base + 16 * tq + l16;
-            const float ft = fast_exp2(sm.cum[tl] - ck) * sig_k;
-            float yv[4];
+        for (int hd = 0; hd < HPW; ++hd)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) yv[v] = fmaf(ft, ys[tq][0][v] + ys[tq][1][v], yd[tq][v]);
-            if (GATE) {
-                yv[0] *= silu(bits_lo(zr[tq].x));
-                yv[1] *= silu(bits_hi(zr[tq].x));
-                yv[2] *= silu(bits_lo(zr[tq].y));
-                yv[3] *= silu(bits_hi(zr[tq].y));
-            }
-            if (VEC) {
-                // rows past the sequence end fall outside the resource
-                if (p4 < pcols)
-                    __builtin_amdgcn_raw_buffer_store_b64(
-                        __builtin_bit_cast(__attribute__((ext_vector_type(2))) uint32_t,
-                                           make_uint2(cvt_pk(yv[0], yv[1]), cvt_pk(yv[2], yv[3]))),
-                        ry, static_cast<uint32_t>((tl * rowX + p4) * 2), 0, 0);
-            } else if (t0 + tl < g.L) {
-                uint16_t *py = yg + static_cast<int64_t>(t0 + tl) * rowX + p4;
+            for (int tq = 0; tq < 2; ++tq) {
+                const int tl = base + 16 * tq + l16;
+                const float ft = fast_exp2(sm.cum[hd][tl] - ck[hd]) * sig_k[hd];
+                float yv[4];
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    if (p4 + v < pcols) py[v] = f32_to_bf16(yv[v]);
+                    yv[v] = fmaf(ft, YC == 2 ? ys[hd][tq][0][v] + ys[hd][tq][YC - 1][v] : ys[hd][tq][0][v],
+                                 yd[hd][tq][v]);
+                if (GATE) {
+                    yv[0] *= silu(bits_lo(zr[hd][tq].x));
+                    yv[1] *= silu(bits_hi(zr[hd][tq].x));
+                    yv[2] *= silu(bits_lo(zr[hd][tq].y));
+                    yv[3] *= silu(bits_hi(zr[hd][tq].y));
+                }
+                if (VEC) {
+                    // rows past the sequence end fall outside the resource
+                    if (p4 < pcols)
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            __builtin_bit_cast(__attribute__((ext_vector_type(2))) uint32_t,
+                                               make_uint2(cvt_pk(yv[0], yv[1]), cvt_pk(yv[2], yv[3]))),
+                            ry, static_cast<uint32_t>((tl * rowX + hd * g.P + p4) * 2), 0, 0);
+                } else if (t0 + tl < g.L) {
+                    uint16_t *py = yg + hd * g.P + static_cast<int64_t>(t0 + tl) * rowX + p4;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (p4 + v < pcols) py[v] = f32_to_bf16(yv[v]);
+                }
             }
-        }
         if (k + 1 < NB) {
             // the next block into LDS (its buffer was last read in the
             // previous block, before that block's first barrier), then --
-            // after every read of this block's decay tile -- its decay tile;
+            // after every read of this block's decay tiles -- its decay tiles;
             // rg then receives the rows of block k + 3
             store_block<NP, VEC, true>(rg, q, nmask, sm.st[(k + 1) & 1]);
             __syncthreads();
-            if (wave < 3) diag_tile<NP>(sm.st[(k + 1) & 1], sm.M, sm.cum, sm.dl, base + 32, le, sk, wave, lane);
+            if (wave < 3) diag_tile<Q, NP, HPW>(sm.st[(k + 1) & 1], sm, base + 32, le, sk, wave, lane);
             if (k + 3 < NB) load_block<NP, VEC, true>(rg, q, Bg, Cg, xg, t0 + base + 96, g, rowBC, rowX, pcols);
             if (GATE) load_z(k + 1);
             __syncthreads();
@@ -879,9 +943,8 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     const auto *zz = static_cast<const uint16_t *>(a.z);
     const bool vec = vecB && vecX;
     // one workgroup per (batch, chunk, head, 64-column head-dimension slice)
-    const dim3 grid(static_cast<uint32_t>(a.batch * g.nch * a.H * g.npg));
-    // chunk states: two heads per workgroup where each group's head count is
-    // even
+    // both walks take two heads per workgroup where each group's head count
+    // is even
     const bool pairs = (a.H / a.G) % 2 == 0;
     const dim3 sgrid(static_cast<uint32_t>(a.batch * g.nch * (pairs ? a.H / 2 : a.H) * g.npg));
     if (vec && pairs)
@@ -904,10 +967,13 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
-        decltype(&ssd_output_kernel<Q, NP, true, true>) kern;
-        if (zz) kern = vec ? ssd_output_kernel<Q, NP, true, true> : ssd_output_kernel<Q, NP, false, true>;
-        else kern = vec ? ssd_output_kernel<Q, NP, true, false> : ssd_output_kernel<Q, NP, false, false>;
-        hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A, B, C, a.D, zz, S,
+        // (the element path takes one head: two would spill)
+        decltype(&ssd_output_kernel<Q, NP, true, true, 1>) kern;
+        if (pairs && vec) kern = zz ? ssd_output_kernel<Q, NP, true, true, 2> : ssd_output_kernel<Q, NP, true, false, 2>;
+        else if (zz) kern = vec ? ssd_output_kernel<Q, NP, true, true, 1> : ssd_output_kernel<Q, NP, false, true, 1>;
+        else kern = vec ? ssd_output_kernel<Q, NP, true, false, 1> : ssd_output_kernel<Q, NP, false, false, 1>;
+        const dim3 ogrid(static_cast<uint32_t>(a.batch * g.nch * (pairs && vec ? a.H / 2 : a.H) * g.npg));
+        hipLaunchKernelGGL(kern, ogrid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A, B, C, a.D, zz, S,
                            static_cast<uint16_t *>(a.y), g);
         e = hipGetLastError();
     }
