@@ -41,7 +41,10 @@
  *   - Arithmetic is float32 with float32 state whatever the I/O dtype; bf16
  *     outputs are rounded to nearest even.
  *   - Scratch memory, where a kernel variant needs it, is allocated and freed
- *     stream-ordered on `stream` (hipMallocAsync/hipFreeAsync).
+ *     stream-ordered on `stream` from a memory pool the library creates per
+ *     device (hipMallocFromPoolAsync/hipFreeAsync).  The pool keeps freed
+ *     memory for later calls (its release threshold is unlimited), so it
+ *     holds up to the largest scratch in use at once until the process ends.
  */
 #ifndef MSSM_H
 #define MSSM_H

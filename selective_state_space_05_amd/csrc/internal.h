@@ -37,6 +37,15 @@ struct ScanArgs {
     const float *conv_b = nullptr;
 };
 
+// Scratch memory of the variants that need it, stream-ordered on `stream`,
+// from a memory pool the library keeps per device.  The pool keeps freed
+// memory (release threshold: unlimited) instead of returning it at every
+// synchronisation, so calls separated by synchronisations reuse it rather
+// than map it again; it holds up to the largest scratch in use at once until
+// the process ends.
+hipError_t scratch_alloc(void **ptr, size_t bytes, hipStream_t stream);
+hipError_t scratch_free(void *ptr, hipStream_t stream);
+
 // One SSD problem, already validated.  Layouts as in mssm.h.
 struct SSDArgs {
     const void *x;

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "internal.h"
@@ -321,6 +322,50 @@ mssm_status ssd_fwd(const void *x, const void *dt, const float *dt_bias, const f
 }
 
 }  // namespace
+
+namespace mssm {
+
+namespace {
+constexpr int kPoolDevices = 64;
+std::mutex g_pool_mu;
+hipMemPool_t g_pool[kPoolDevices] = {};
+}  // namespace
+
+// The current device's scratch pool, created on first use with an unlimited
+// release threshold.
+hipError_t scratch_alloc(void **ptr, size_t bytes, hipStream_t stream) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kPoolDevices) return hipErrorInvalidDevice;
+    hipMemPool_t pool;
+    {
+        std::lock_guard<std::mutex> lk(g_pool_mu);
+        if (!g_pool[dev]) {
+            hipMemPoolProps props;
+            std::memset(&props, 0, sizeof props);
+            props.allocType = hipMemAllocationTypePinned;
+            props.location.type = hipMemLocationTypeDevice;
+            props.location.id = dev;
+            hipMemPool_t p = nullptr;
+            e = hipMemPoolCreate(&p, &props);
+            if (e != hipSuccess) return e;
+            uint64_t keep = UINT64_MAX;
+            e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
+            if (e != hipSuccess) {
+                (void)hipMemPoolDestroy(p);
+                return e;
+            }
+            g_pool[dev] = p;
+        }
+        pool = g_pool[dev];
+    }
+    return hipMallocFromPoolAsync(ptr, bytes, pool, stream);
+}
+
+hipError_t scratch_free(void *ptr, hipStream_t stream) { return hipFreeAsync(ptr, stream); }
+
+}  // namespace mssm
 
 extern "C" {
 

@@ -707,7 +707,7 @@ hipError_t launch_typed(const BwdArgs &a, hipStream_t stream) {
     const size_t part_bytes = want_bc ? static_cast<size_t>(total) * a.L * 32 * sizeof(float) : 0;
     const size_t adj_bytes = static_cast<size_t>(n_cut) * (sp.parts - 1) * 256 * sizeof(float);
     void *mem = nullptr;
-    hipError_t e = hipMallocAsync(&mem, ck_bytes + part_bytes + adj_bytes, stream);
+    hipError_t e = scratch_alloc(&mem, ck_bytes + part_bytes + adj_bytes, stream);
     if (e != hipSuccess) return e;
     float *ck = static_cast<float *>(mem);
     float *part = want_bc ? reinterpret_cast<float *>(static_cast<char *>(mem) + ck_bytes) : nullptr;
@@ -727,7 +727,7 @@ hipError_t launch_typed(const BwdArgs &a, hipStream_t stream) {
                            0, stream, part, gpb, a.batch, a.L, static_cast<int>(a.N), a.dB, a.dC);
         e = hipGetLastError();
     }
-    const hipError_t ef = hipFreeAsync(mem, stream);
+    const hipError_t ef = scratch_free(mem, stream);
     return e != hipSuccess ? e : ef;
 }
 

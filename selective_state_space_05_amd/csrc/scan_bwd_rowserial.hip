@@ -324,7 +324,7 @@ hipError_t launch_typed(const BwdArgs &a, hipStream_t stream) {
     const size_t part_bytes =
         want_bc ? static_cast<size_t>(waves) * nslots * a.L * NG * 32 * sizeof(float) : 0;
     void *mem = nullptr;
-    hipError_t e = hipMallocAsync(&mem, ck_bytes + part_bytes, stream);
+    hipError_t e = scratch_alloc(&mem, ck_bytes + part_bytes, stream);
     if (e != hipSuccess) return e;
     float *ck = static_cast<float *>(mem);
     float *part = reinterpret_cast<float *>(static_cast<char *>(mem) + ck_bytes);
@@ -338,7 +338,7 @@ hipError_t launch_typed(const BwdArgs &a, hipStream_t stream) {
                            a.dC);
         e = hipGetLastError();
     }
-    const hipError_t ef = hipFreeAsync(mem, stream);
+    const hipError_t ef = scratch_free(mem, stream);
     return e != hipSuccess ? e : ef;
 }
 
@@ -817,7 +817,7 @@ hipError_t launch_group(const BwdArgs &a, hipStream_t stream) {
     const size_t ck_bytes = static_cast<size_t>(rows) * nseg * 16 * sizeof(float);
     const size_t part_bytes = want_bc ? static_cast<size_t>(waves) * nslots * a.L * 32 * sizeof(float) : 0;
     void *mem = nullptr;
-    hipError_t e = hipMallocAsync(&mem, ck_bytes + part_bytes, stream);
+    hipError_t e = scratch_alloc(&mem, ck_bytes + part_bytes, stream);
     if (e != hipSuccess) return e;
     float *ck = static_cast<float *>(mem);
     float *part = reinterpret_cast<float *>(static_cast<char *>(mem) + ck_bytes);
@@ -831,7 +831,7 @@ hipError_t launch_group(const BwdArgs &a, hipStream_t stream) {
                            a.dC);
         e = hipGetLastError();
     }
-    const hipError_t ef = hipFreeAsync(mem, stream);
+    const hipError_t ef = scratch_free(mem, stream);
     return e != hipSuccess ? e : ef;
 }
 

@@ -282,7 +282,7 @@ hipError_t launch_typed(const ScanArgs &a, hipStream_t stream, void *pre) {
     void *mem = pre;
     hipError_t e = hipSuccess;
     if (!pre) {
-        e = hipMallocAsync(&mem, pay_bytes + flag_bytes, stream);
+        e = scratch_alloc(&mem, pay_bytes + flag_bytes, stream);
         if (e != hipSuccess) return e;
     }
     Scratch s;
@@ -308,7 +308,7 @@ hipError_t launch_typed(const ScanArgs &a, hipStream_t stream, void *pre) {
         e = hipGetLastError();
     }
     if (pre) return e;
-    const hipError_t ef = hipFreeAsync(mem, stream);
+    const hipError_t ef = scratch_free(mem, stream);
     return e != hipSuccess ? e : ef;
 }
 

@@ -931,7 +931,7 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     const size_t s_bytes = static_cast<size_t>(chunks * PN) * sizeof(float);
     const size_t ce_bytes = static_cast<size_t>(chunks) * sizeof(float);
     void *mem = nullptr;
-    hipError_t e = hipMallocAsync(&mem, s_bytes + ce_bytes, stream);
+    hipError_t e = scratch_alloc(&mem, s_bytes + ce_bytes, stream);
     if (e != hipSuccess) return e;
     float *S = static_cast<float *>(mem);
     float *ce = reinterpret_cast<float *>(static_cast<char *>(mem) + s_bytes);
@@ -977,7 +977,7 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
                            static_cast<uint16_t *>(a.y), g);
         e = hipGetLastError();
     }
-    const hipError_t ef = hipFreeAsync(mem, stream);
+    const hipError_t ef = scratch_free(mem, stream);
     return e != hipSuccess ? e : ef;
 }
 
