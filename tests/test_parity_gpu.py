@@ -339,6 +339,8 @@ SSD_SMALL = [
     (2, 2048, 4, 32, 64, 2, "bf16"),
     (1, 600, 2, 80, 96, 1, "bf16"),       # two 64-column head-dim slices, N tile 96
     (1, 520, 2, 20, 24, 2, "bf16"),       # P, N not multiples of 8: scalar loads
+    (1, 700, 3, 64, 64, 1, "bf16"),       # odd head count per group: one head per workgroup
+    (2, 1100, 6, 64, 128, 2, "bf16"),     # two heads per workgroup in each of two groups
 ]
 
 

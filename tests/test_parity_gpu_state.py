@@ -195,6 +195,7 @@ SSD_GATED_CASES = [
     (1, 1000, 3, 40, 7, 3, "bf16", False),    # two head-dim tiles, element path
     (1, 600, 2, 80, 96, 1, "bf16", True),     # two 64-column head-dim slices
     (1, 77, 6, 5, 7, 3, "f32", True),
+    (1, 700, 3, 64, 64, 1, "bf16", True),     # odd head count per group, from h0
 ]
 
 
