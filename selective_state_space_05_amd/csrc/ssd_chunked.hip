@@ -171,7 +171,7 @@ struct __align__(16) OutSmem {
     uint4 M[HPW][2][2][64];              // diagonal decay tile: [head][t tile][hi, lo][lane]
     float cum[HPW][Q], dl[HPW][Q];
     float fs[HPW][Q];                    // 2^(cum at the end of s's block - cum_s) dl_s
-    float wsum[4];
+    float wsum[HPW][4];
 };
 
 // A block's B, C and x rows as loaded.  Unit u of B and x: step pair
@@ -291,33 +291,48 @@ __device__ __forceinline__ void store_block(const BlockRegs<NP, WC> &r, const Bl
     }
 }
 
-// dl and the inclusive sum of the log2 decay over the chunk's Q steps from a
-// prefetched raw dt value (thread s < Q holds step s; s_wsum holds one float
-// per wave of the workgroup).  Ends with a barrier.
-template <int Q>
-__device__ void chunk_decay_from(float dr, int t0, int L, float A2, float bias,
-                                 float *s_cum, float *s_dl, float *s_wsum) {
+// dl and the inclusive sum of the log2 decay over the chunk's Q steps for
+// HPW heads at once, from prefetched raw dt values (thread s < Q holds step
+// s of every head; wsum holds one float per head and wave).  The scans of
+// the heads are interleaved and share the two barriers; each is the same
+// sequence of additions as a scan of one head.  Ends with a barrier.
+template <int Q, int HPW>
+__device__ void chunk_decay(const float (&dr)[HPW], int t0, int L, const float (&A2)[HPW],
+                            const float (&bias)[HPW], float (*s_cum)[Q], float (*s_dl)[Q], float (*s_wsum)[4]) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    float dlv = 0.0f, ell = 0.0f;
-    if (tid < Q && t0 + tid < L) {
-        dlv = softplus(dr + bias);
-        ell = dlv * A2;
+    float dlv[HPW], sc[HPW];
+#pragma unroll
+    for (int hd = 0; hd < HPW; ++hd) {
+        dlv[hd] = 0.0f;
+        sc[hd] = 0.0f;
+        if (tid < Q && t0 + tid < L) {
+            dlv[hd] = softplus(dr[hd] + bias[hd]);
+            sc[hd] = dlv[hd] * A2[hd];
+        }
     }
-    float sc = ell;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(sc, off, 64);
-        if (lane >= off) sc += o;
+#pragma unroll
+        for (int hd = 0; hd < HPW; ++hd) {
+            const float o = __shfl_up(sc[hd], off, 64);
+            if (lane >= off) sc[hd] += o;
+        }
     }
-    if (lane == 63) s_wsum[wave] = sc;
+    if (lane == 63) {
+#pragma unroll
+        for (int hd = 0; hd < HPW; ++hd) s_wsum[hd][wave] = sc[hd];
+    }
     __syncthreads();
     if (tid < Q) {
-        float base = 0.0f;
-        for (int w2 = 0; w2 < wave; ++w2) base += s_wsum[w2];
-        s_cum[tid] = sc + base;
-        s_dl[tid] = dlv;
+#pragma unroll
+        for (int hd = 0; hd < HPW; ++hd) {
+            float base = 0.0f;
+            for (int w2 = 0; w2 < wave; ++w2) base += s_wsum[hd][w2];
+            s_cum[hd][tid] = sc[hd] + base;
+            s_dl[hd][tid] = dlv[hd];
+        }
     }
     __syncthreads();
 }
@@ -344,7 +359,7 @@ template <int Q, int NP, int HPW>
 struct __align__(16) StateSmem {
     StateStage<NP, HPW> st[2];
     float cum[HPW][Q], dl[HPW][Q], w[HPW][Q];
-    float wsum[4];
+    float wsum[HPW][4];
 };
 
 template <int Q, int NP, bool VEC, int HPW>
@@ -391,12 +406,15 @@ __global__ __launch_bounds__(256, HPW == 2 ? 3 : (VEC ? 4 : 2)) void ssd_state_k
     load_block<NP, VEC, false>(r0, q, Bg, nullptr, xg, t0, g, rowBC, rowX, pcols);
     if (NB > 1) load_block<NP, VEC, false>(ra, q, Bg, nullptr, xg, t0 + 32, g, rowBC, rowX, pcols);
     if (NB > 2) load_block<NP, VEC, false>(rb, q, Bg, nullptr, xg, t0 + 64, g, rowBC, rowX, pcols);
-    float cum_end[HPW];
+    float cum_end[HPW], a2[HPW], bs[HPW];
 #pragma unroll
     for (int hd = 0; hd < HPW; ++hd) {
-        const int hh = h0 + hd;
-        chunk_decay_from<Q>(dtr[hd], t0, g.L, A[hh] * kLog2e, dt_bias ? dt_bias[hh] : 0.0f, sm.cum[hd], sm.dl[hd],
-                            sm.wsum);
+        a2[hd] = A[h0 + hd] * kLog2e;
+        bs[hd] = dt_bias ? dt_bias[h0 + hd] : 0.0f;
+    }
+    chunk_decay<Q, HPW>(dtr, t0, g.L, a2, bs, sm.cum, sm.dl, sm.wsum);
+#pragma unroll
+    for (int hd = 0; hd < HPW; ++hd) {
         cum_end[hd] = sm.cum[hd][Q - 1];
         if (tid < Q) sm.w[hd][tid] = fast_exp2(cum_end[hd] - sm.cum[hd][tid]) * sm.dl[hd][tid];
     }
@@ -689,13 +707,18 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
             }
         }
     }
+    {
+        float a2[HPW], bs[HPW];
 #pragma unroll
-    for (int hd = 0; hd < HPW; ++hd) {
-        const int hh = h0 + hd;
-        chunk_decay_from<Q>(dtr[hd], t0, g.L, A[hh] * kLog2e, dt_bias ? dt_bias[hh] : 0.0f, sm.cum[hd], sm.dl[hd],
-                            sm.wsum);
-        if (tid < Q) sm.fs[hd][tid] = fast_exp2(sm.cum[hd][tid | 31] - sm.cum[hd][tid]) * sm.dl[hd][tid];
+        for (int hd = 0; hd < HPW; ++hd) {
+            a2[hd] = A[h0 + hd] * kLog2e;
+            bs[hd] = dt_bias ? dt_bias[h0 + hd] : 0.0f;
+        }
+        chunk_decay<Q, HPW>(dtr, t0, g.L, a2, bs, sm.cum, sm.dl, sm.wsum);
     }
+#pragma unroll
+    for (int hd = 0; hd < HPW; ++hd)
+        if (tid < Q) sm.fs[hd][tid] = fast_exp2(sm.cum[hd][tid | 31] - sm.cum[hd][tid]) * sm.dl[hd][tid];
     // K slots 4..7 of t tile 0 (steps 16..31, after every step of the tile)
     // stay zero; no quadrant writes them
     if (wave == 3) {
