@@ -18,22 +18,27 @@
 // closed form of the same ybb.press section; its chunk-by-chunk state carry
 // is section 5).
 //
-// Three kernels, so that every chunk is worked on at once:
-//   1. ssd_state_kernel: the chunk state S, accumulated block by block of 32
-//      steps as a matrix-core product (x w)^T B, and the chunk's total log2
-//      decay;
-//   2. ssd_pass_kernel: walks the chunks of each (batch, head) in order,
+// Three kernels, so that every pair of consecutive chunks is worked on at
+// once:
+//   1. ssd_state_kernel: the state of each pair of chunks (2 m, 2 m + 1) from
+//      zero, 2^(e_{2m+1}) S_{2m} + S_{2m+1} (e: a chunk's total log2 decay),
+//      accumulated block by block of 32 steps as a matrix-core product
+//      (x w)^T B, and the pair's total log2 decay;
+//   2. ssd_pass_kernel: walks the pairs of each (batch, head) in order,
 //      elementwise over the P x N state and starting from the initial state
-//      (zero unless given), replacing each chunk state by the state entering
-//      that chunk and writing h_last;
-//   3. ssd_output_kernel: the outputs, walking the chunk's 32-step blocks from
-//      h_in with the state carried in matrix-core accumulators; within a block
-//      the outputs come from the state entering it and the block's own 32 x 32
-//      decay-masked C B^T tile.
-// Both walks give each workgroup one (batch, chunk, head, 64-column slice of
-// the head dimension) and each of its four waves 16 columns, and stage a
-// block's B, C and x in LDS (transposed where a product contracts over the
-// steps) while the next blocks' rows are in flight.
+//      (zero unless given), replacing each pair's state by the state entering
+//      its first chunk and writing h_last;
+//   3. ssd_output_kernel: the outputs, walking the 32-step blocks of both
+//      chunks of a pair from the state entering the first, with the state
+//      carried in matrix-core accumulators; within a block the outputs come
+//      from the state entering it and the block's own 32 x 32 decay-masked
+//      C B^T tile.
+// A pair rather than a single chunk per workgroup halves the chunk states
+// written, passed and read again.  Both walks give each workgroup a pair of
+// chunks of one batch and a 64-column slice of the head dimension, and each
+// of its four waves 16 columns, and stage a block's B, C and x in LDS
+// (transposed where a product contracts over the steps) while the next
+// blocks' rows are in flight.
 // Products whose operands are not exact bf16 values (x * weight, the masked
 // decay tile, the carried state) use a two-term bf16 split (hi + lo), so each
 // product carries about 16 significant bits; accumulation is float32.
@@ -342,9 +347,11 @@ __device__ void chunk_decay(const float (&dr)[HPW], int t0, int L, const float (
 // ---------------------------------------------------------------------------
 // S[p][n] = sum_s w_s x_s[p] B_s[n], w_s = 2^(cum_end - cum_s) dl_s: the
 // output kernel's state update (section 3) without the outputs.  One
-// workgroup per (batch, chunk, 64-column slice) and HPW heads of one B / C
-// group (two where the group's head count is even): the block's B^T is
-// staged once and each of its operand reads serves both heads.  Wave w
+// workgroup per (batch, chunk pair, 64-column slice) and HPW heads of one
+// B / C group (two where the group's head count is even): the block's B^T is
+// staged once and each of its operand reads serves both heads.  The second
+// chunk of a pair continues from the first one's state decayed over the
+// second chunk, so the pair's state is written once.  Wave w
 // accumulates columns p = 16 w + 0..15 of every head over the chunk's
 // 32-step blocks with the same operand orders (B^T rows n and K = steps;
 // (x w) columns p).
@@ -375,15 +382,16 @@ __global__ __launch_bounds__(256, HPW == 2 ? 3 : (VEC ? 4 : 2)) void ssd_state_k
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
 
+    // (batch, chunk pair m, heads h0.., slice pg): chunks 2 m and 2 m + 1
     int64_t id = blockIdx.x;
     const int pg = static_cast<int>(id % g.npg);
     id /= g.npg;
     const int h0 = static_cast<int>(id % (g.H / HPW)) * HPW;
     id /= g.H / HPW;
-    const int c = static_cast<int>(id % g.nch);
-    const int64_t b = id / g.nch;
+    const int npair = (g.nch + 1) / 2;
+    const int m = static_cast<int>(id % npair);
+    const int64_t b = id / npair;
     const int pbase = pg * kPG, pcols = g.P - pbase;
-    const int t0 = c * Q;
     const int rowX = g.H * g.P, rowBC = g.G * g.N;
     const int grp = h0 / (g.H / g.G);
     const uint16_t *Bg = Bm + b * g.L * static_cast<int64_t>(rowBC) + grp * g.N;
@@ -392,110 +400,143 @@ __global__ __launch_bounds__(256, HPW == 2 ? 3 : (VEC ? 4 : 2)) void ssd_state_k
     const uint16_t *xg = x + b * g.L * static_cast<int64_t>(rowX) + (h0 + hx) * g.P + pbase;
     const bool nmask = g.N < NP;
     const int pl = 16 * wave + l16;
-
-    // dt first, then the first three blocks (register sets as in the output
-    // kernel)
-    const int tdt = t0 + (tid < Q ? tid : 0);
-    const int64_t dto = b * g.L * static_cast<int64_t>(g.H) + static_cast<int64_t>(tdt < g.L ? tdt : g.L - 1) * g.H + h0;
-    float dtr[HPW];
-#pragma unroll
-    for (int hd = 0; hd < HPW; ++hd) dtr[hd] = bf16_to_f32(dt[dto + hd]);
-    BlockGeom<NP, false> q;
-    block_geom<NP, false>(q, g, rowBC, rowX);
-    BlockRegs<NP, false> r0, ra, rb;
-    load_block<NP, VEC, false>(r0, q, Bg, nullptr, xg, t0, g, rowBC, rowX, pcols);
-    if (NB > 1) load_block<NP, VEC, false>(ra, q, Bg, nullptr, xg, t0 + 32, g, rowBC, rowX, pcols);
-    if (NB > 2) load_block<NP, VEC, false>(rb, q, Bg, nullptr, xg, t0 + 64, g, rowBC, rowX, pcols);
-    float cum_end[HPW], a2[HPW], bs[HPW];
+    float a2[HPW], bs[HPW];
 #pragma unroll
     for (int hd = 0; hd < HPW; ++hd) {
         a2[hd] = A[h0 + hd] * kLog2e;
         bs[hd] = dt_bias ? dt_bias[h0 + hd] : 0.0f;
     }
-    chunk_decay<Q, HPW>(dtr, t0, g.L, a2, bs, sm.cum, sm.dl, sm.wsum);
-#pragma unroll
-    for (int hd = 0; hd < HPW; ++hd) {
-        cum_end[hd] = sm.cum[hd][Q - 1];
-        if (tid < Q) sm.w[hd][tid] = fast_exp2(cum_end[hd] - sm.cum[hd][tid]) * sm.dl[hd][tid];
-    }
-    store_block<NP, VEC, false>(r0, q, nmask, sm.st[0]);
-    __syncthreads();
+    BlockGeom<NP, false> q;
+    block_geom<NP, false>(q, g, rowBC, rowX);
 
     f4x acc[HPW][NJ];
+    float ce_pair[HPW];
 #pragma unroll
-    for (int hd = 0; hd < HPW; ++hd)
+    for (int hd = 0; hd < HPW; ++hd) {
+        ce_pair[hd] = 0.0f;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[hd][j] = zero4();
-    auto step = [&](const int k, BlockRegs<NP, false> &rg) {
-        const StateStage<NP, HPW> &st = sm.st[k & 1];
-        const int base = 32 * k;
-        // (x w) of the block for each head: column p = pl, K slots
-        // s = 16 (i / 4) + 4 g4 + i % 4
-        bf8 xwh[HPW], xwl[HPW];
+    }
+#pragma unroll 1
+    for (int cc = 0; cc < 2; ++cc) {
+        const int c = 2 * m + cc;
+        if (c >= g.nch) break;
+        if (cc > 0) __syncthreads();   // every read of the previous chunk's LDS is done
+        const int t0 = c * Q;
+        // dt first, then the first three blocks (register sets as in the
+        // output kernel)
+        const int tdt = t0 + (tid < Q ? tid : 0);
+        const int64_t dto = b * g.L * static_cast<int64_t>(g.H) + static_cast<int64_t>(tdt < g.L ? tdt : g.L - 1) * g.H + h0;
+        float dtr[HPW];
+#pragma unroll
+        for (int hd = 0; hd < HPW; ++hd) dtr[hd] = bf16_to_f32(dt[dto + hd]);
+        BlockRegs<NP, false> r0, ra, rb;
+        load_block<NP, VEC, false>(r0, q, Bg, nullptr, xg, t0, g, rowBC, rowX, pcols);
+        if (NB > 1) load_block<NP, VEC, false>(ra, q, Bg, nullptr, xg, t0 + 32, g, rowBC, rowX, pcols);
+        if (NB > 2) load_block<NP, VEC, false>(rb, q, Bg, nullptr, xg, t0 + 64, g, rowBC, rowX, pcols);
+        float cum_end[HPW];
+        chunk_decay<Q, HPW>(dtr, t0, g.L, a2, bs, sm.cum, sm.dl, sm.wsum);
 #pragma unroll
         for (int hd = 0; hd < HPW; ++hd) {
-            const uint16_t *xp = &st.XT[(hd * kPG + pl) * TP];
-            const uint2 x0 = *reinterpret_cast<const uint2 *>(xp + swz(4 * g4, pl));
-            const uint2 x1 = *reinterpret_cast<const uint2 *>(xp + swz(16 + 4 * g4, pl));
-            const float4 f0 = *reinterpret_cast<const float4 *>(&sm.w[hd][base + 4 * g4]);
-            const float4 f1 = *reinterpret_cast<const float4 *>(&sm.w[hd][base + 16 + 4 * g4]);
-            uint32_t xh[4], xl[4];
-            split_pk(bits_lo(x0.x) * f0.x, bits_hi(x0.x) * f0.y, xh[0], xl[0]);
-            split_pk(bits_lo(x0.y) * f0.z, bits_hi(x0.y) * f0.w, xh[1], xl[1]);
-            split_pk(bits_lo(x1.x) * f1.x, bits_hi(x1.x) * f1.y, xh[2], xl[2]);
-            split_pk(bits_lo(x1.y) * f1.z, bits_hi(x1.y) * f1.w, xh[3], xl[3]);
-            xwh[hd] = __builtin_bit_cast(bf8, make_uint4(xh[0], xh[1], xh[2], xh[3]));
-            xwl[hd] = __builtin_bit_cast(bf8, make_uint4(xl[0], xl[1], xl[2], xl[3]));
-        }
+            cum_end[hd] = sm.cum[hd][Q - 1];
+            if (tid < Q) sm.w[hd][tid] = fast_exp2(cum_end[hd] - sm.cum[hd][tid]) * sm.dl[hd][tid];
+            // the second chunk continues from the first one's state:
+            // acc = 2^(its decay) S_{2m} + (its own terms) = the pair's
+            // aggregate
+            if (cc > 0) {
+                const float a = fast_exp2(cum_end[hd]);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const uint16_t *bp = &st.BT[(16 * j + l16) * TP];
-            const bf8 bt = cat8(*reinterpret_cast<const uint2 *>(bp + swz(4 * g4, 16 * j)),
-                                *reinterpret_cast<const uint2 *>(bp + swz(16 + 4 * g4, 16 * j)));
+                for (int j = 0; j < NJ; ++j) acc[hd][j] = acc[hd][j] * a;
+            }
+            ce_pair[hd] += cum_end[hd];
+        }
+        store_block<NP, VEC, false>(r0, q, nmask, sm.st[0]);
+        __syncthreads();
+
+        auto step = [&](const int k, BlockRegs<NP, false> &rg) {
+            const StateStage<NP, HPW> &st = sm.st[k & 1];
+            const int base = 32 * k;
+            // (x w) of the block for each head: column p = pl, K slots
+            // s = 16 (i / 4) + 4 g4 + i % 4
+            bf8 xwh[HPW], xwl[HPW];
 #pragma unroll
             for (int hd = 0; hd < HPW; ++hd) {
-                acc[hd][j] = mfma16(bt, xwh[hd], acc[hd][j]);
-                acc[hd][j] = mfma16(bt, xwl[hd], acc[hd][j]);
+                const uint16_t *xp = &st.XT[(hd * kPG + pl) * TP];
+                const uint2 x0 = *reinterpret_cast<const uint2 *>(xp + swz(4 * g4, pl));
+                const uint2 x1 = *reinterpret_cast<const uint2 *>(xp + swz(16 + 4 * g4, pl));
+                const float4 f0 = *reinterpret_cast<const float4 *>(&sm.w[hd][base + 4 * g4]);
+                const float4 f1 = *reinterpret_cast<const float4 *>(&sm.w[hd][base + 16 + 4 * g4]);
+                uint32_t xh[4], xl[4];
+                split_pk(bits_lo(x0.x) * f0.x, bits_hi(x0.x) * f0.y, xh[0], xl[0]);
+                split_pk(bits_lo(x0.y) * f0.z, bits_hi(x0.y) * f0.w, xh[1], xl[1]);
+                split_pk(bits_lo(x1.x) * f1.x, bits_hi(x1.x) * f1.y, xh[2], xl[2]);
+                split_pk(bits_lo(x1.y) * f1.z, bits_hi(x1.y) * f1.w, xh[3], xl[3]);
+                xwh[hd] = __builtin_bit_cast(bf8, make_uint4(xh[0], xh[1], xh[2], xh[3]));
+                xwl[hd] = __builtin_bit_cast(bf8, make_uint4(xl[0], xl[1], xl[2], xl[3]));
             }
-        }
-        if (k + 1 < NB) {
-            // the next block into LDS: its buffer was last read in the
-            // previous block, before that block's barrier
-            store_block<NP, VEC, false>(rg, q, nmask, sm.st[(k + 1) & 1]);
-            __syncthreads();
-            if (k + 3 < NB) load_block<NP, VEC, false>(rg, q, Bg, nullptr, xg, t0 + base + 96, g, rowBC, rowX, pcols);
-        }
-    };
-#pragma unroll 1
-    for (int k = 0; k < NB; k += 2) {
-        step(k, ra);
-        step(k + 1, rb);
-    }
-    // lane (l16, g4) holds S[pl][16 j + 4 g4 + v] of each head
-    if (pl < pcols) {
-#pragma unroll
-        for (int hd = 0; hd < HPW; ++hd) {
-            float *Sg = S + (((b * g.nch + c) * g.H + h0 + hd) * static_cast<int64_t>(g.P) + pbase + pl) * g.N;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const int n4 = 16 * j + 4 * g4;
-                if (VEC) {
-                    if (n4 < g.N)
-                        *reinterpret_cast<float4 *>(Sg + n4) = make_float4(acc[hd][j][0], acc[hd][j][1], acc[hd][j][2], acc[hd][j][3]);
-                } else {
+                const uint16_t *bp = &st.BT[(16 * j + l16) * TP];
+                const bf8 bt = cat8(*reinterpret_cast<const uint2 *>(bp + swz(4 * g4, 16 * j)),
+                                    *reinterpret_cast<const uint2 *>(bp + swz(16 + 4 * g4, 16 * j)));
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        if (n4 + v < g.N) Sg[n4 + v] = acc[hd][j][v];
+                for (int hd = 0; hd < HPW; ++hd) {
+                    acc[hd][j] = mfma16(bt, xwh[hd], acc[hd][j]);
+                    acc[hd][j] = mfma16(bt, xwl[hd], acc[hd][j]);
+                }
+            }
+            if (k + 1 < NB) {
+                // the next block into LDS: its buffer was last read in the
+                // previous block, before that block's barrier
+                store_block<NP, VEC, false>(rg, q, nmask, sm.st[(k + 1) & 1]);
+                __syncthreads();
+                if (k + 3 < NB)
+                    load_block<NP, VEC, false>(rg, q, Bg, nullptr, xg, t0 + base + 96, g, rowBC, rowX, pcols);
+            }
+        };
+#pragma unroll 1
+        for (int k = 0; k < NB; k += 2) {
+            step(k, ra);
+            step(k + 1, rb);
+        }
+    }
+    // the pair's aggregate (a last chunk without a partner: its own state)
+    // and total log2 decay.  Lane (l16, g4) holds [pl][16 j + 4 g4 + v] of
+    // each head.
+    {
+        if (pl < pcols) {
+#pragma unroll
+            for (int hd = 0; hd < HPW; ++hd) {
+                float *Sg = S + (((b * npair + m) * g.H + h0 + hd) * static_cast<int64_t>(g.P) + pbase + pl) * g.N;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const int n4 = 16 * j + 4 * g4;
+                    if (VEC) {
+                        if (n4 < g.N)
+                            *reinterpret_cast<float4 *>(Sg + n4) =
+                                make_float4(acc[hd][j][0], acc[hd][j][1], acc[hd][j][2], acc[hd][j][3]);
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            if (n4 + v < g.N) Sg[n4 + v] = acc[hd][j][v];
+                    }
                 }
             }
         }
+        if (pbase == 0 && tid < HPW) ce[(b * npair + m) * g.H + h0 + tid] = ce_pair[tid];
     }
-    if (pbase == 0 && tid < HPW) ce[(b * g.nch + c) * g.H + h0 + tid] = cum_end[tid];
 }
 
 // ---------------------------------------------------------------------------
-// 2. state pass: S[chunk] <- state entering the chunk; h_last <- final state
+// 2. state pass over chunk pairs: slot m <- state entering chunk 2 m;
+//    h_last <- final state
 // ---------------------------------------------------------------------------
+// Slot m holds the aggregate of chunks 2 m and 2 m + 1,
+// 2^(e_{2m+1}) S_{2m} + S_{2m+1} (e: a chunk's total log2 decay, S: its state
+// from zero; a last chunk without a partner: its own S), and ce[m] the pair's
+// total decay, so one fused multiply-add per pair, h <- 2^(ce[m]) h + slot,
+// carries the state across two chunks.  The output kernel walks both chunks
+// of a pair from the state entering the first.
 __global__ __launch_bounds__(256) void ssd_pass_kernel(float *__restrict__ S,
                                                        const float *__restrict__ ce,
                                                        const float *h0, float *h_last, Geom g,
@@ -506,14 +547,15 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(float *__restrict__ S,
     if (e >= PN) return;
     const int64_t b = bh / g.H, hh = bh % g.H;
     float h = h0 ? h0[bh * PN + e] : 0.0f;   // state entering the first chunk
-    constexpr int U = 4;    // chunks whose states are loaded ahead of the chain
-    int c = 0;
-    for (; c + U <= g.nch; c += U) {
+    const int npair = (g.nch + 1) / 2;
+    constexpr int U = 4;    // pairs whose aggregates are loaded ahead of the chain
+    int m = 0;
+    for (; m + U <= npair; m += U) {
         float s[U], a[U];
         int64_t idx[U];
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            const int64_t bc = (b * g.nch + c + k) * g.H + hh;
+            const int64_t bc = (b * npair + m + k) * g.H + hh;
             idx[k] = bc * PN + e;
             s[k] = S[idx[k]];
             a[k] = fast_exp2(ce[bc]);
@@ -524,8 +566,8 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(float *__restrict__ S,
             h = fmaf(a[k], h, s[k]);
         }
     }
-    for (; c < g.nch; ++c) {
-        const int64_t bc = (b * g.nch + c) * g.H + hh;
+    for (; m < npair; ++m) {
+        const int64_t bc = (b * npair + m) * g.H + hh;
         const float s = S[bc * PN + e];
         S[bc * PN + e] = h;
         h = fmaf(fast_exp2(ce[bc]), h, s);
@@ -569,11 +611,9 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(float *__restrict__ S,
 //   M[t][s] = (C_t . B_s) 2^(cum_t - cum_s) dl_s for s < t, plus D at s = t,
 // written split into bf16 parts as K slots 4 sq .. 4 sq + 3 of the B operand
 // of t tile tq.  The product C . B is the same for every head of the group.
-// le[v] (1 for s <= t, else 0) and sk[h][v] (head h's D at s = t, else 0)
-// depend only on the lane, not on the block.
 template <int Q, int NP, int HPW>
 __device__ __forceinline__ void diag_tile(const BlockStage<NP, HPW> &st, OutSmem<Q, NP, HPW> &sm, int base,
-                                          const float (&le)[4], const float (&sk)[HPW][4], int wave, int lane) {
+                                          const float (&skip)[HPW], int wave, int lane) {
     constexpr int TP = BlockStage<NP, HPW>::TP, CP = BlockStage<NP, HPW>::CP;
     const int sq = wave == 2 ? 1 : 0, tq = wave == 0 ? 0 : 1;
     const int l16 = lane & 15, g4 = lane >> 4;
@@ -603,11 +643,13 @@ __device__ __forceinline__ void diag_tile(const BlockStage<NP, HPW> &st, OutSmem
         const float4 ds = *reinterpret_cast<const float4 *>(&sm.dl[hd][s0]);
         const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, dsv[4] = {ds.x, ds.y, ds.z, ds.w};
         float mv[4];
-        // (2^(ct - cs) overflows only where s > t, and le = 0 there selects 0)
+        // causal mask s <= t, D on the diagonal (2^(ct - cs) overflows only
+        // where s > t, which the mask replaces by 0)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const float m = G[v] * fast_exp2(ct - csv[v]) * dsv[v];
-            mv[v] = le[v] != 0.0f ? m + sk[hd][v] : 0.0f;
+            const int sv = 16 * sq + 4 * g4 + v, tv = 16 * tq + l16;
+            mv[v] = sv <= tv ? m + (sv == tv ? skip[hd] : 0.0f) : 0.0f;
         }
         uint32_t h0, l0, h1, l1;
         split_pk(mv[0], mv[1], h0, l0);
@@ -617,18 +659,20 @@ __device__ __forceinline__ void diag_tile(const BlockStage<NP, HPW> &st, OutSmem
     }
 }
 
-// HPW heads of one B / C group per workgroup: two share the block's staged
-// B and C, its C . B quadrants and every B and C operand read, and give each
-// wave two independent chains; one otherwise (a group with an odd head
-// count).  Workgroups per compute unit: three for one head on the vector
-// path without a gate (LDS and registers allow it), two otherwise.
+// Both chunks of a pair per workgroup: the walk over the first ends holding
+// the state entering the second, so only the pair's entering state is read.
+// HPW heads of one B / C group per workgroup (the launcher takes one, so
+// that the layer's pairs and heads fill the chip in whole rounds; two would
+// share the block's staged B and C, its C . B quadrants and every B and C
+// operand read).  Workgroups per compute unit: three for one head on the
+// vector path without a gate (LDS and registers allow it), two otherwise.
 template <int Q, int NP, bool VEC, bool GATE, int HPW>
 __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_output_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt,
     const float *__restrict__ dt_bias, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm,
     const float *__restrict__ Dskip, const uint16_t *__restrict__ z, const float *__restrict__ Hin,
-    uint16_t *__restrict__ y, Geom g) {
+    const float *__restrict__ ce, uint16_t *__restrict__ y, Geom g) {
     constexpr int NB = Q / 32;          // blocks per chunk
     constexpr int NJ = NP / 16;         // 16-wide state tiles
     constexpr int KK = NP / 32;         // K steps over the state index
@@ -644,10 +688,10 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
     id /= g.npg;
     const int h0 = static_cast<int>(id % (g.H / HPW)) * HPW;
     id /= g.H / HPW;
-    const int c = static_cast<int>(id % g.nch);
-    const int64_t b = id / g.nch;
+    const int npair = (g.nch + 1) / 2;
+    const int m = static_cast<int>(id % npair);      // chunks 2 m and 2 m + 1
+    const int64_t b = id / npair;
     const int pbase = pg * kPG, pcols = g.P - pbase;
-    const int t0 = c * Q;
     const int rowX = g.H * g.P, rowBC = g.G * g.N;
     const int grp = h0 / (g.H / g.G);
     const uint16_t *Bg = Bm + b * g.L * static_cast<int64_t>(rowBC) + grp * g.N;
@@ -664,25 +708,12 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
 #pragma unroll
     for (int hd = 0; hd < HPW; ++hd) skip[hd] = Dskip ? Dskip[h0 + hd] : 0.0f;
 
-    // dt first (the decay scan waits for it), then the first three blocks'
-    // rows: block j + 1 is stored to LDS at the end of block j, from the
-    // register set ra (j even) or rb (j odd), which then receives block j + 3;
-    // then the state entering the chunk
-    const int tdt = t0 + (tid < Q ? tid : 0);
-    const int64_t dto = b * g.L * static_cast<int64_t>(g.H) + static_cast<int64_t>(tdt < g.L ? tdt : g.L - 1) * g.H + h0;
-    float dtr[HPW];
-#pragma unroll
-    for (int hd = 0; hd < HPW; ++hd) dtr[hd] = bf16_to_f32(dt[dto + hd]);
-    BlockGeom<NP, true> q;
-    block_geom<NP, true>(q, g, rowBC, rowX);
-    BlockRegs<NP, true> r0, ra, rb;
-    load_block<NP, VEC, true>(r0, q, Bg, Cg, xg, t0, g, rowBC, rowX, pcols);
-    if (NB > 1) load_block<NP, VEC, true>(ra, q, Bg, Cg, xg, t0 + 32, g, rowBC, rowX, pcols);
-    if (NB > 2) load_block<NP, VEC, true>(rb, q, Bg, Cg, xg, t0 + 64, g, rowBC, rowX, pcols);
+    // the state entering chunk 2 m, from the pass
     f4x H[HPW][NJ];
+    const int64_t PNs = static_cast<int64_t>(g.P) * g.N;
 #pragma unroll
     for (int hd = 0; hd < HPW; ++hd) {
-        const float *Hg = Hin + ((b * g.nch + c) * g.H + h0 + hd) * static_cast<int64_t>(g.P) * g.N;
+        const float *Hg = Hin + ((b * npair + m) * g.H + h0 + hd) * PNs;
         const bool okp = pl < pcols;
         const float *hrow = Hg + static_cast<int64_t>(okp ? pbase + pl : 0) * g.N;
 #pragma unroll
@@ -691,12 +722,12 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
             if (VEC) {
                 // N % 8 == 0: the four states are all inside the row or all past it
                 const bool ok = okp && n4 < g.N;
-                const uint32_t m = opaque_mask(ok);
+                const uint32_t mk = opaque_mask(ok);
                 const float4 v = *reinterpret_cast<const float4 *>(hrow + (ok ? n4 : 0));
-                H[hd][j][0] = __uint_as_float(__float_as_uint(v.x) & m);
-                H[hd][j][1] = __uint_as_float(__float_as_uint(v.y) & m);
-                H[hd][j][2] = __uint_as_float(__float_as_uint(v.z) & m);
-                H[hd][j][3] = __uint_as_float(__float_as_uint(v.w) & m);
+                H[hd][j][0] = __uint_as_float(__float_as_uint(v.x) & mk);
+                H[hd][j][1] = __uint_as_float(__float_as_uint(v.y) & mk);
+                H[hd][j][2] = __uint_as_float(__float_as_uint(v.z) & mk);
+                H[hd][j][3] = __uint_as_float(__float_as_uint(v.w) & mk);
             } else {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
@@ -707,18 +738,12 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
             }
         }
     }
-    {
-        float a2[HPW], bs[HPW];
+    float a2[HPW], bs[HPW];
 #pragma unroll
-        for (int hd = 0; hd < HPW; ++hd) {
-            a2[hd] = A[h0 + hd] * kLog2e;
-            bs[hd] = dt_bias ? dt_bias[h0 + hd] : 0.0f;
-        }
-        chunk_decay<Q, HPW>(dtr, t0, g.L, a2, bs, sm.cum, sm.dl, sm.wsum);
+    for (int hd = 0; hd < HPW; ++hd) {
+        a2[hd] = A[h0 + hd] * kLog2e;
+        bs[hd] = dt_bias ? dt_bias[h0 + hd] : 0.0f;
     }
-#pragma unroll
-    for (int hd = 0; hd < HPW; ++hd)
-        if (tid < Q) sm.fs[hd][tid] = fast_exp2(sm.cum[hd][tid | 31] - sm.cum[hd][tid]) * sm.dl[hd][tid];
     // K slots 4..7 of t tile 0 (steps 16..31, after every step of the tile)
     // stay zero; no quadrant writes them
     if (wave == 3) {
@@ -727,21 +752,45 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
 #pragma unroll
             for (int hl = 0; hl < 2; ++hl) reinterpret_cast<uint2 *>(&sm.M[hd][0][hl][lane])[1] = make_uint2(0, 0);
     }
-    // causal mask of this lane's diagonal-tile quadrant (waves 0-2)
-    float le[4], sk[HPW][4];
-    {
-        const int sq = wave == 2 ? 1 : 0, tq = wave == 0 ? 0 : 1;
+    BlockGeom<NP, true> q;
+    block_geom<NP, true>(q, g, rowBC, rowX);
+    uint16_t *yg = y + xoff;
+    // Each head's state is carried as H = sig * Hs with sig a
+    // workgroup-uniform scalar, so a block's decay multiplies sig (and the
+    // block's new terms by 1 / sig) instead of every state element; when sig
+    // would fall below 2^-64 it is folded back into Hs.  It carries on from
+    // the first chunk of the pair to the second.
+    float sig[HPW];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int sr = 16 * sq + 4 * g4 + v, tr = 16 * tq + l16;
-            le[v] = sr <= tr ? 1.0f : 0.0f;
+    for (int hd = 0; hd < HPW; ++hd) sig[hd] = 1.0f;
+
+#pragma unroll 1
+    for (int cc = 0; cc < 2; ++cc) {
+    const int c = 2 * m + cc;
+    if (c >= g.nch) break;
+    if (cc > 0) __syncthreads();   // every read of the first chunk's LDS is done
+    const int t0 = c * Q;
+    // the walk continues into the pair's second chunk after this one's last block
+    const bool cont = cc == 0 && c + 1 < g.nch;
+    // dt first (the decay scan waits for it), then the first three blocks'
+    // rows: block j + 1 is stored to LDS at the end of block j, from the
+    // register set ra (j even) or rb (j odd), which then receives block j + 3
+    const int tdt = t0 + (tid < Q ? tid : 0);
+    const int64_t dto = b * g.L * static_cast<int64_t>(g.H) + static_cast<int64_t>(tdt < g.L ? tdt : g.L - 1) * g.H + h0;
+    float dtr[HPW];
 #pragma unroll
-            for (int hd = 0; hd < HPW; ++hd) sk[hd][v] = sr == tr ? skip[hd] : 0.0f;
-        }
-    }
+    for (int hd = 0; hd < HPW; ++hd) dtr[hd] = bf16_to_f32(dt[dto + hd]);
+    BlockRegs<NP, true> r0, ra, rb;
+    load_block<NP, VEC, true>(r0, q, Bg, Cg, xg, t0, g, rowBC, rowX, pcols);
+    if (NB > 1) load_block<NP, VEC, true>(ra, q, Bg, Cg, xg, t0 + 32, g, rowBC, rowX, pcols);
+    if (NB > 2) load_block<NP, VEC, true>(rb, q, Bg, Cg, xg, t0 + 64, g, rowBC, rowX, pcols);
+    chunk_decay<Q, HPW>(dtr, t0, g.L, a2, bs, sm.cum, sm.dl, sm.wsum);
+#pragma unroll
+    for (int hd = 0; hd < HPW; ++hd)
+        if (tid < Q) sm.fs[hd][tid] = fast_exp2(sm.cum[hd][tid | 31] - sm.cum[hd][tid]) * sm.dl[hd][tid];
     store_block<NP, VEC, true>(r0, q, nmask, sm.st[0]);
     __syncthreads();
-    if (wave < 3) diag_tile<Q, NP, HPW>(sm.st[0], sm, 0, le, sk, wave, lane);
+    if (wave < 3) diag_tile<Q, NP, HPW>(sm.st[0], sm, 0, skip, wave, lane);
     // gate values of this lane's steps of the current block, four columns each
     uint2 zr[HPW][2];
 #pragma unroll
@@ -755,9 +804,9 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
                 const int tc = t < g.L ? t : g.L - 1;
                 const uint16_t *zp = z + xoff + hd * g.P + static_cast<int64_t>(tc) * rowX;
                 if (VEC) {
-                    const uint32_t m = opaque_mask(p4 < pcols);
+                    const uint32_t mk = opaque_mask(p4 < pcols);
                     const uint2 v = *reinterpret_cast<const uint2 *>(zp + (p4 < pcols ? p4 : 0));
-                    zr[hd][tq] = make_uint2(v.x & m, v.y & m);
+                    zr[hd][tq] = make_uint2(v.x & mk, v.y & mk);
                 } else {
                     uint16_t e[4];
 #pragma unroll
@@ -770,19 +819,11 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
     if (GATE) load_z(0);
     // y of the chunk's rows from head h0's slice on (the second head's columns
     // are P further), stores past the sequence end dropped
-    uint16_t *yg = y + xoff;
     const auto ry = brsrc(yg + static_cast<int64_t>(t0) * rowX,
                           static_cast<int64_t>(g.L - t0) * rowX * 2 -
                               static_cast<int64_t>(rowX - pcols - (HPW - 1) * g.P) * 2);
     __syncthreads();
 
-    // Each head's state is carried as H = sig * Hs with sig a
-    // workgroup-uniform scalar, so a block's decay multiplies sig (and the
-    // block's new terms by 1 / sig) instead of every state element; when sig
-    // would fall below 2^-64 it is folded back into Hs.
-    float sig[HPW];
-#pragma unroll
-    for (int hd = 0; hd < HPW; ++hd) sig[hd] = 1.0f;
     auto step = [&](const int k, BlockRegs<NP, true> &rg) {
         const St &st = sm.st[k & 1];
         const int base = 32 * k;
@@ -845,7 +886,8 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
 #pragma unroll
         for (int hd = 0; hd < HPW; ++hd) sig_k[hd] = sig[hd];
         // state entering the next block: H_{k+1} = 2^(e_k - c_k) H_k + dH_k
-        if (k + 1 < NB) {
+        // (after the chunk's last block: the state entering the next chunk)
+        if (k + 1 < NB || cont) {
             bf8 xwh[HPW], xwl[HPW];
 #pragma unroll
             for (int hd = 0; hd < HPW; ++hd) {
@@ -921,7 +963,7 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
             // rg then receives the rows of block k + 3
             store_block<NP, VEC, true>(rg, q, nmask, sm.st[(k + 1) & 1]);
             __syncthreads();
-            if (wave < 3) diag_tile<Q, NP, HPW>(sm.st[(k + 1) & 1], sm, base + 32, le, sk, wave, lane);
+            if (wave < 3) diag_tile<Q, NP, HPW>(sm.st[(k + 1) & 1], sm, base + 32, skip, wave, lane);
             if (k + 3 < NB) load_block<NP, VEC, true>(rg, q, Bg, Cg, xg, t0 + base + 96, g, rowBC, rowX, pcols);
             if (GATE) load_z(k + 1);
             __syncthreads();
@@ -932,6 +974,7 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
     for (int k = 0; k < NB; k += 2) {
         step(k, ra);
         step(k + 1, rb);
+    }
     }
 }
 
@@ -949,7 +992,8 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     const bool vecB = a.N % 8 == 0 && aligned(a.B) && aligned(a.C);
     const bool vecX = a.P % 8 == 0 && aligned(a.x) && aligned(a.y) && (!a.z || aligned(a.z));
 
-    const int64_t chunks = a.batch * g.nch * a.H;
+    // chunk-pair states and decays (one per pair of consecutive chunks)
+    const int64_t chunks = a.batch * ((g.nch + 1) / 2) * a.H;
     const int64_t PN = a.P * a.N;
     const size_t s_bytes = static_cast<size_t>(chunks * PN) * sizeof(float);
     const size_t ce_bytes = static_cast<size_t>(chunks) * sizeof(float);
@@ -965,11 +1009,12 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     const auto *C = static_cast<const uint16_t *>(a.C);
     const auto *zz = static_cast<const uint16_t *>(a.z);
     const bool vec = vecB && vecX;
-    // one workgroup per (batch, chunk, head, 64-column head-dimension slice)
-    // both walks take two heads per workgroup where each group's head count
-    // is even
+    // one workgroup per (batch, pair of consecutive chunks, 64-column
+    // head-dimension slice) and one head, or in the state kernel two where
+    // each group's head count is even
     const bool pairs = (a.H / a.G) % 2 == 0;
-    const dim3 sgrid(static_cast<uint32_t>(a.batch * g.nch * (pairs ? a.H / 2 : a.H) * g.npg));
+    const int64_t npair = (g.nch + 1) / 2;
+    const dim3 sgrid(static_cast<uint32_t>(a.batch * npair * (pairs ? a.H / 2 : a.H) * g.npg));
     if (vec && pairs)
         hipLaunchKernelGGL((ssd_state_kernel<Q, NP, true, 2>), sgrid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A,
                            B, S, ce, g);
@@ -990,13 +1035,12 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
-        // (the element path takes one head: two would spill)
+        // one head and both chunks of a pair per workgroup
         decltype(&ssd_output_kernel<Q, NP, true, true, 1>) kern;
-        if (pairs && vec) kern = zz ? ssd_output_kernel<Q, NP, true, true, 2> : ssd_output_kernel<Q, NP, true, false, 2>;
-        else if (zz) kern = vec ? ssd_output_kernel<Q, NP, true, true, 1> : ssd_output_kernel<Q, NP, false, true, 1>;
+        if (zz) kern = vec ? ssd_output_kernel<Q, NP, true, true, 1> : ssd_output_kernel<Q, NP, false, true, 1>;
         else kern = vec ? ssd_output_kernel<Q, NP, true, false, 1> : ssd_output_kernel<Q, NP, false, false, 1>;
-        const dim3 ogrid(static_cast<uint32_t>(a.batch * g.nch * (pairs && vec ? a.H / 2 : a.H) * g.npg));
-        hipLaunchKernelGGL(kern, ogrid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A, B, C, a.D, zz, S,
+        const dim3 ogrid(static_cast<uint32_t>(a.batch * npair * a.H * g.npg));
+        hipLaunchKernelGGL(kern, ogrid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A, B, C, a.D, zz, S, ce,
                            static_cast<uint16_t *>(a.y), g);
         e = hipGetLastError();
     }
