@@ -23,7 +23,9 @@
 //   1. ssd_state_kernel: the state of each pair of chunks (2 m, 2 m + 1) from
 //      zero, 2^(e_{2m+1}) S_{2m} + S_{2m+1} (e: a chunk's total log2 decay),
 //      accumulated block by block of 32 steps as a matrix-core product
-//      (x w)^T B, and the pair's total log2 decay;
+//      (x w)^T B, and the pair's total log2 decay; extra workgroups of the
+//      same launch form the C . B Gram products within each 32-step block,
+//      which depend on the group only;
 //   2. ssd_pass_kernel: walks the pairs of each (batch, head) in order,
 //      elementwise over the P x N state and starting from the initial state
 //      (zero unless given), replacing each pair's state by the state entering
@@ -32,7 +34,7 @@
 //      chunks of a pair from the state entering the first, with the state
 //      carried in matrix-core accumulators; within a block the outputs come
 //      from the state entering it and the block's own 32 x 32 decay-masked
-//      C B^T tile.
+//      C B^T tile (the Gram products scaled by the decays).
 // A pair rather than a single chunk per workgroup halves the chunk states
 // written, passed and read again.  Both walks give each workgroup a pair of
 // chunks of one batch and a 64-column slice of the head dimension, and each
@@ -343,6 +345,65 @@ __device__ void chunk_decay(const float (&dr)[HPW], int t0, int L, const float (
 }
 
 // ---------------------------------------------------------------------------
+// Gram tiles of the blocks' diagonals (formed by extra workgroups of the
+// state kernel's launch, which the output kernel reads)
+// ---------------------------------------------------------------------------
+// C_t . B_s for s, t in the same 32-step block, in the three 16 x 16
+// quadrants (s tile, t tile) = (0, 0), (0, 1), (1, 1) that hold every s <= t.
+// They depend only on the B / C group, not on the head, so they are formed
+// once instead of in each of the group's heads' output workgroups, whose LDS
+// operand layouts (steps along a row) would need a gather per element for
+// this contraction over the states.  One wave per task = ((b G + group) nblk
+// + block) 3 + quadrant w, with the states in K slots 8 g + i of K step kk
+// (state 32 kk + 8 g + i; past N: zero; rows past the sequence end: zero).
+// Stored as one float4 per lane at Gm[task * 64 + lane], D layout (column
+// t = l16, rows s = 4 g + v of the quadrant).
+template <int NP, bool VEC>
+__device__ __forceinline__ void gram_quadrant(const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm,
+                                              f4x *__restrict__ Gm, const Geom &g, int nblk, int64_t task,
+                                              int lane) {
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const int w = static_cast<int>(task % 3);
+    int64_t id = task / 3;
+    const int blk = static_cast<int>(id % nblk);
+    id /= nblk;
+    const int grp = static_cast<int>(id % g.G);
+    const int64_t b = id / g.G;
+    const int sq = w == 2 ? 1 : 0, tq = w == 0 ? 0 : 1;
+    const int rowBC = g.G * g.N;
+    const int s = 32 * blk + 16 * sq + l16, t = 32 * blk + 16 * tq + l16;
+    const bool oks = s < g.L, okt = t < g.L;
+    const uint16_t *bp = Bm + (b * g.L + (oks ? s : 0)) * static_cast<int64_t>(rowBC) + grp * g.N;
+    const uint16_t *cp = Cm + (b * g.L + (okt ? t : 0)) * static_cast<int64_t>(rowBC) + grp * g.N;
+    f4x G = zero4();
+#pragma unroll
+    for (int kk = 0; kk < NP / 32; ++kk) {
+        const int n0 = 32 * kk + 8 * g4;
+        uint4 av, cv;
+        if (VEC) {
+            // N % 8 == 0: the eight states are all inside the row or all past it
+            const bool ia = oks && n0 < g.N, ic = okt && n0 < g.N;
+            const uint4 a4 = *reinterpret_cast<const uint4 *>(bp + (ia ? n0 : 0));
+            const uint4 c4 = *reinterpret_cast<const uint4 *>(cp + (ic ? n0 : 0));
+            av = ia ? a4 : make_uint4(0, 0, 0, 0);
+            cv = ic ? c4 : make_uint4(0, 0, 0, 0);
+        } else {
+            uint16_t ae[8], ce[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const bool in = n0 + i < g.N;
+                ae[i] = oks && in ? bp[n0 + i] : 0;
+                ce[i] = okt && in ? cp[n0 + i] : 0;
+            }
+            __builtin_memcpy(&av, ae, 16);
+            __builtin_memcpy(&cv, ce, 16);
+        }
+        G = mfma16(__builtin_bit_cast(bf8, av), __builtin_bit_cast(bf8, cv), G);
+    }
+    Gm[task * 64 + lane] = G;
+}
+
+// ---------------------------------------------------------------------------
 // 1. chunk states, block-walk form
 // ---------------------------------------------------------------------------
 // S[p][n] = sum_s w_s x_s[p] B_s[n], w_s = 2^(cum_end - cum_s) dl_s: the
@@ -373,7 +434,8 @@ template <int Q, int NP, bool VEC, int HPW>
 __global__ __launch_bounds__(256, HPW == 2 ? 3 : (VEC ? 4 : 2)) void ssd_state_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt,
     const float *__restrict__ dt_bias, const float *__restrict__ A,
-    const uint16_t *__restrict__ Bm, float *__restrict__ S, float *__restrict__ ce, Geom g) {
+    const uint16_t *__restrict__ Bm, float *__restrict__ S, float *__restrict__ ce, Geom g,
+    const uint16_t *__restrict__ Cm, f4x *__restrict__ Gm, int nstate, int nblk, int ntask) {
     constexpr int NB = Q / 32;
     constexpr int NJ = NP / 16;
     constexpr int TP = StateStage<NP, HPW>::TP;
@@ -382,6 +444,12 @@ __global__ __launch_bounds__(256, HPW == 2 ? 3 : (VEC ? 4 : 2)) void ssd_state_k
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
 
+    // workgroups past the states' ones: four Gram quadrants each
+    if (static_cast<int>(blockIdx.x) >= nstate) {
+        const int64_t task = static_cast<int64_t>(blockIdx.x - nstate) * 4 + wave;
+        if (task < ntask) gram_quadrant<NP, VEC>(Bm, Cm, Gm, g, nblk, task, lane);
+        return;
+    }
     // (batch, chunk pair m, heads h0.., slice pg): chunks 2 m and 2 m + 1
     int64_t id = blockIdx.x;
     const int pg = static_cast<int>(id % g.npg);
@@ -609,32 +677,17 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(float *__restrict__ S,
 // Waves 0, 1, 2: quadrant (sq, tq) = (0, 0), (0, 1), (1, 1) of the diagonal
 // tile of the block at chunk step `base`, for each of the HPW heads:
 //   M[t][s] = (C_t . B_s) 2^(cum_t - cum_s) dl_s for s < t, plus D at s = t,
-// written split into bf16 parts as K slots 4 sq .. 4 sq + 3 of the B operand
-// of t tile tq.  The product C . B is the same for every head of the group.
+// split into bf16 parts (hi pair 0-1, hi pair 2-3, lo pair 0-1, lo pair 2-3)
+// that diag_store writes as K slots 4 sq .. 4 sq + 3 of the B operand of t
+// tile tq.  G holds the quadrant's C_t . B_s as ssd_gram_kernel laid it out:
+// G[v] at step s = 16 sq + 4 g + v, column t = 16 tq + l16 of the block.
+// (Wave 3 may form the values of quadrant (0, 1) too; it stores none.)
 template <int Q, int NP, int HPW>
-__device__ __forceinline__ void diag_tile(const BlockStage<NP, HPW> &st, OutSmem<Q, NP, HPW> &sm, int base,
-                                          const float (&skip)[HPW], int wave, int lane) {
-    constexpr int TP = BlockStage<NP, HPW>::TP, CP = BlockStage<NP, HPW>::CP;
+__device__ __forceinline__ void diag_vals(const f4x G, const OutSmem<Q, NP, HPW> &sm, int base,
+                                          const float (&skip)[HPW], int wave, int lane,
+                                          uint4 (&mv)[HPW]) {
     const int sq = wave == 2 ? 1 : 0, tq = wave == 0 ? 0 : 1;
     const int l16 = lane & 15, g4 = lane >> 4;
-    f4x G = zero4();
-#pragma unroll
-    for (int kk = 0; kk < NP / 32; ++kk) {
-        // A: B at step 16 sq + l16, states 32 kk + 8 g4 + 0..7; B operand: C
-        // at step 16 tq + l16, the same states
-        uint16_t av[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int n = 32 * kk + 8 * g4 + i;
-            av[i] = st.BT[n * TP + swz(16 * sq + l16, n)];
-        }
-        bf8 a;
-        __builtin_memcpy(&a, av, 16);
-        const uint16_t *cp = &st.CR[(16 * tq + l16) * CP + 32 * kk + 8 * g4];
-        const bf8 cb = cat8(*reinterpret_cast<const uint2 *>(cp), *reinterpret_cast<const uint2 *>(cp + 4));
-        G = mfma16(a, cb, G);
-    }
-    // G[v]: step s = base + 16 sq + 4 g4 + v, column t = base + 16 tq + l16
     const int t = base + 16 * tq + l16, s0 = base + 16 * sq + 4 * g4;
 #pragma unroll
     for (int hd = 0; hd < HPW; ++hd) {
@@ -642,20 +695,27 @@ __device__ __forceinline__ void diag_tile(const BlockStage<NP, HPW> &st, OutSmem
         const float4 cs = *reinterpret_cast<const float4 *>(&sm.cum[hd][s0]);
         const float4 ds = *reinterpret_cast<const float4 *>(&sm.dl[hd][s0]);
         const float csv[4] = {cs.x, cs.y, cs.z, cs.w}, dsv[4] = {ds.x, ds.y, ds.z, ds.w};
-        float mv[4];
+        float m[4];
         // causal mask s <= t, D on the diagonal (2^(ct - cs) overflows only
         // where s > t, which the mask replaces by 0)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const float m = G[v] * fast_exp2(ct - csv[v]) * dsv[v];
+            const float e = G[v] * fast_exp2(ct - csv[v]) * dsv[v];
             const int sv = 16 * sq + 4 * g4 + v, tv = 16 * tq + l16;
-            mv[v] = sv <= tv ? m + (sv == tv ? skip[hd] : 0.0f) : 0.0f;
+            m[v] = sv <= tv ? e + (sv == tv ? skip[hd] : 0.0f) : 0.0f;
         }
-        uint32_t h0, l0, h1, l1;
-        split_pk(mv[0], mv[1], h0, l0);
-        split_pk(mv[2], mv[3], h1, l1);
-        reinterpret_cast<uint2 *>(&sm.M[hd][tq][0][lane])[sq] = make_uint2(h0, h1);
-        reinterpret_cast<uint2 *>(&sm.M[hd][tq][1][lane])[sq] = make_uint2(l0, l1);
+        split_pk(m[0], m[1], mv[hd].x, mv[hd].z);
+        split_pk(m[2], m[3], mv[hd].y, mv[hd].w);
+    }
+}
+template <int Q, int NP, int HPW>
+__device__ __forceinline__ void diag_store(OutSmem<Q, NP, HPW> &sm, const uint4 (&mv)[HPW], int wave,
+                                           int lane) {
+    const int sq = wave == 2 ? 1 : 0, tq = wave == 0 ? 0 : 1;
+#pragma unroll
+    for (int hd = 0; hd < HPW; ++hd) {
+        reinterpret_cast<uint2 *>(&sm.M[hd][tq][0][lane])[sq] = make_uint2(mv[hd].x, mv[hd].y);
+        reinterpret_cast<uint2 *>(&sm.M[hd][tq][1][lane])[sq] = make_uint2(mv[hd].z, mv[hd].w);
     }
 }
 
@@ -672,7 +732,7 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
     const float *__restrict__ dt_bias, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm,
     const float *__restrict__ Dskip, const uint16_t *__restrict__ z, const float *__restrict__ Hin,
-    const float *__restrict__ ce, uint16_t *__restrict__ y, Geom g) {
+    const f4x *__restrict__ Gm, uint16_t *__restrict__ y, Geom g) {
     constexpr int NB = Q / 32;          // blocks per chunk
     constexpr int NJ = NP / 16;         // 16-wide state tiles
     constexpr int KK = NP / 32;         // K steps over the state index
@@ -763,6 +823,9 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
     float sig[HPW];
 #pragma unroll
     for (int hd = 0; hd < HPW; ++hd) sig[hd] = 1.0f;
+    // this wave's Gram quadrant of the group's first block (waves 0-2; one
+    // block further: 3 * 64 float4)
+    const f4x *Gw = Gm + ((b * g.G + grp) * static_cast<int64_t>(g.nch) * NB * 3 + (wave < 3 ? wave : 0)) * 64 + lane;
 
 #pragma unroll 1
     for (int cc = 0; cc < 2; ++cc) {
@@ -780,6 +843,9 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
     float dtr[HPW];
 #pragma unroll
     for (int hd = 0; hd < HPW; ++hd) dtr[hd] = bf16_to_f32(dt[dto + hd]);
+    // Gram quadrant of block 0, then (in flight through each block) of the
+    // block after the next
+    f4x gq = Gw[static_cast<int64_t>(c * NB) * 192];
     BlockRegs<NP, true> r0, ra, rb;
     load_block<NP, VEC, true>(r0, q, Bg, Cg, xg, t0, g, rowBC, rowX, pcols);
     if (NB > 1) load_block<NP, VEC, true>(ra, q, Bg, Cg, xg, t0 + 32, g, rowBC, rowX, pcols);
@@ -790,7 +856,12 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
         if (tid < Q) sm.fs[hd][tid] = fast_exp2(sm.cum[hd][tid | 31] - sm.cum[hd][tid]) * sm.dl[hd][tid];
     store_block<NP, VEC, true>(r0, q, nmask, sm.st[0]);
     __syncthreads();
-    if (wave < 3) diag_tile<Q, NP, HPW>(sm.st[0], sm, 0, skip, wave, lane);
+    {
+        uint4 mv[HPW];
+        diag_vals<Q, NP, HPW>(gq, sm, 0, skip, wave, lane, mv);
+        if (wave < 3) diag_store<Q, NP, HPW>(sm, mv, wave, lane);
+    }
+    gq = Gw[static_cast<int64_t>(c * NB + 1) * 192];
     // gate values of this lane's steps of the current block, four columns each
     uint2 zr[HPW][2];
 #pragma unroll
@@ -924,6 +995,13 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
                 }
             }
         }
+        // the next block's decay tile values (stored after this block's
+        // reads of M), then the Gram quadrant of the block after it; past
+        // the chunk's last block both are formed from in-range indices and
+        // left unused
+        uint4 mv[HPW];
+        diag_vals<Q, NP, HPW>(gq, sm, k + 1 < NB ? base + 32 : base, skip, wave, lane, mv);
+        gq = Gw[static_cast<int64_t>(c * NB + (k + 2 < NB ? k + 2 : NB - 1)) * 192];
         // y at this lane's steps of the block, four columns each
 #pragma unroll
         for (int hd = 0; hd < HPW; ++hd)
@@ -963,7 +1041,7 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
             // rg then receives the rows of block k + 3
             store_block<NP, VEC, true>(rg, q, nmask, sm.st[(k + 1) & 1]);
             __syncthreads();
-            if (wave < 3) diag_tile<Q, NP, HPW>(sm.st[(k + 1) & 1], sm, base + 32, skip, wave, lane);
+            if (wave < 3) diag_store<Q, NP, HPW>(sm, mv, wave, lane);
             if (k + 3 < NB) load_block<NP, VEC, true>(rg, q, Bg, Cg, xg, t0 + base + 96, g, rowBC, rowX, pcols);
             if (GATE) load_z(k + 1);
             __syncthreads();
@@ -997,11 +1075,17 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     const int64_t PN = a.P * a.N;
     const size_t s_bytes = static_cast<size_t>(chunks * PN) * sizeof(float);
     const size_t ce_bytes = static_cast<size_t>(chunks) * sizeof(float);
+    // Gram quadrants: 3 x 64 float4 per (batch, group, 32-step block)
+    const int nblk = g.nch * (Q / 32);
+    const size_t g_bytes = static_cast<size_t>(a.batch * a.G * nblk) * 3 * 64 * sizeof(f4x);
+    // (each part 256-byte aligned)
+    const size_t s_pad = (s_bytes + 255) & ~size_t(255), ce_pad = (ce_bytes + 255) & ~size_t(255);
     void *mem = nullptr;
-    hipError_t e = scratch_alloc(&mem, s_bytes + ce_bytes, stream);
+    hipError_t e = scratch_alloc(&mem, s_pad + ce_pad + g_bytes, stream);
     if (e != hipSuccess) return e;
     float *S = static_cast<float *>(mem);
-    float *ce = reinterpret_cast<float *>(static_cast<char *>(mem) + s_bytes);
+    float *ce = reinterpret_cast<float *>(static_cast<char *>(mem) + s_pad);
+    f4x *Gq = reinterpret_cast<f4x *>(static_cast<char *>(mem) + s_pad + ce_pad);
 
     const auto *x = static_cast<const uint16_t *>(a.x);
     const auto *dt = static_cast<const uint16_t *>(a.dt);
@@ -1014,19 +1098,22 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     // each group's head count is even
     const bool pairs = (a.H / a.G) % 2 == 0;
     const int64_t npair = (g.nch + 1) / 2;
-    const dim3 sgrid(static_cast<uint32_t>(a.batch * npair * (pairs ? a.H / 2 : a.H) * g.npg));
+    // the state workgroups, then those of the Gram quadrants (four each)
+    const int nstate = static_cast<int>(a.batch * npair * (pairs ? a.H / 2 : a.H) * g.npg);
+    const int ntask = static_cast<int>(a.batch * a.G * nblk * 3);
+    const dim3 sgrid(static_cast<uint32_t>(nstate + (ntask + 3) / 4));
     if (vec && pairs)
         hipLaunchKernelGGL((ssd_state_kernel<Q, NP, true, 2>), sgrid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A,
-                           B, S, ce, g);
+                           B, S, ce, g, C, Gq, nstate, nblk, ntask);
     else if (vec)
         hipLaunchKernelGGL((ssd_state_kernel<Q, NP, true, 1>), sgrid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A,
-                           B, S, ce, g);
+                           B, S, ce, g, C, Gq, nstate, nblk, ntask);
     else if (pairs)
         hipLaunchKernelGGL((ssd_state_kernel<Q, NP, false, 2>), sgrid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A,
-                           B, S, ce, g);
+                           B, S, ce, g, C, Gq, nstate, nblk, ntask);
     else
         hipLaunchKernelGGL((ssd_state_kernel<Q, NP, false, 1>), sgrid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A,
-                           B, S, ce, g);
+                           B, S, ce, g, C, Gq, nstate, nblk, ntask);
     e = hipGetLastError();
     if (e == hipSuccess) {
         const int bph = static_cast<int>((PN + 255) / 256);
@@ -1040,7 +1127,7 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
         if (zz) kern = vec ? ssd_output_kernel<Q, NP, true, true, 1> : ssd_output_kernel<Q, NP, false, true, 1>;
         else kern = vec ? ssd_output_kernel<Q, NP, true, false, 1> : ssd_output_kernel<Q, NP, false, false, 1>;
         const dim3 ogrid(static_cast<uint32_t>(a.batch * npair * a.H * g.npg));
-        hipLaunchKernelGGL(kern, ogrid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A, B, C, a.D, zz, S, ce,
+        hipLaunchKernelGGL(kern, ogrid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A, B, C, a.D, zz, S, Gq,
                            static_cast<uint16_t *>(a.y), g);
         e = hipGetLastError();
     }
@@ -1065,10 +1152,16 @@ bool ssd_chunked_supported(const SSDArgs &a) {
     if (a.L * a.H * a.P >= lim || a.L * a.G * a.N >= lim || a.L * a.H >= lim) return false;
     // byte offsets of a chunk's rows from its first row fit in 31 bits
     if (a.chunk * a.H * a.P * 2 >= lim || a.chunk * a.G * a.N * 2 >= lim) return false;
-    return a.io == IO_BF16 && a.N >= 1 && a.N <= 128 && a.P >= 1 &&
-           (a.chunk == 64 || a.chunk == 128 || a.chunk == 256) &&
-           a.batch * nch * a.H * ((a.P + kPG - 1) / kPG) < (int64_t(1) << 31) &&
-           nch < (int64_t(1) << 30);
+    if (!(a.io == IO_BF16 && a.N >= 1 && a.N <= 128 && a.P >= 1 &&
+          (a.chunk == 64 || a.chunk == 128 || a.chunk == 256) && nch < (int64_t(1) << 30)))
+        return false;
+    // each launch's grid in work-items (256 per workgroup) stays below 2^32
+    const int64_t wmax = int64_t(1) << 24;
+    const int64_t npair = (nch + 1) / 2, npg = (a.P + kPG - 1) / kPG;
+    const int64_t nstate = a.batch * npair * a.H * npg;
+    const int64_t ntask = a.batch * a.G * nch * (a.chunk / 32) * 3;
+    return nstate < wmax && nstate + (ntask + 3) / 4 < wmax &&
+           a.batch * a.H * ((a.P * a.N + 255) / 256) < wmax;
 }
 
 hipError_t launch_ssd_chunked(const SSDArgs &a, hipStream_t stream) {
