@@ -246,11 +246,13 @@ def ssd(x, dt, A, B, C, D=None, dt_bias=None, h0=None, nthreads: int = 0,
     return y, h_last
 
 
-def ssd_rows(rows, x, dt, A, B, C, D=None, dt_bias=None, nthreads: int = 0, z=None):
+def ssd_rows(rows, x, dt, A, B, C, D=None, dt_bias=None, nthreads: int = 0, z=None,
+             h0=None):
     """Oracle on sampled independent (b, h, p) rows of a large SSD problem.
 
     With a scalar decay per (b, t, h), every headdim index p evolves its own
-    N-vector of state, independent of the other p.  Returns
+    N-vector of state, independent of the other p (h0, when given, supplies
+    each row's own starting N-vector).  Returns
     ``(y_rows (R, L), h_rows (R, N))``.
     """
     ys, hs = [], []
@@ -263,6 +265,7 @@ def ssd_rows(rows, x, dt, A, B, C, D=None, dt_bias=None, nthreads: int = 0, z=No
             A[h:h + 1], B[b:b + 1, :, g:g + 1], C[b:b + 1, :, g:g + 1],
             None if D is None else D[h:h + 1],
             None if dt_bias is None else dt_bias[h:h + 1],
+            h0=None if h0 is None else h0[b:b + 1, h:h + 1, p:p + 1],
             nthreads=nthreads,
             z=None if z is None else z[b:b + 1, :, h:h + 1, p:p + 1])
         ys.append(y[0, :, 0, 0])

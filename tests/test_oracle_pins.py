@@ -352,6 +352,23 @@ def test_ssd_rows_sampling(oracle_mod):
         assert np.array_equal(hs[i], hl[b, h, p])
 
 
+def test_ssd_rows_sampling_from_h0_gated(oracle_mod):
+    """Sampled rows from an initial state and with a gate are the same rows
+    of the whole problem."""
+    s = _ssd_small(2, 20, 4, 3, 5, 2, 13)
+    rng = np.random.default_rng(4)
+    h0 = rng.standard_normal((2, 4, 3, 5))
+    z = rng.standard_normal(s["x"].shape)
+    y, hl = oracle_mod.ssd(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["dt_bias"],
+                           h0=h0, z=z)
+    rows = [(0, 3, 2), (1, 0, 0), (1, 2, 1)]
+    ys, hs = oracle_mod.ssd_rows(rows, s["x"], s["dt"], s["A"], s["B"], s["C"],
+                                 s["D"], s["dt_bias"], z=z, h0=h0)
+    for i, (b, h, p) in enumerate(rows):
+        assert np.array_equal(ys[i], y[b, :, h, p])
+        assert np.array_equal(hs[i], hl[b, h, p])
+
+
 def test_ssd_resume(oracle_mod):
     s = _ssd_small(1, 40, 2, 3, 4, 1, 5)
     y, hl = _ssd_run(oracle_mod, s)

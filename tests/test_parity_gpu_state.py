@@ -244,6 +244,42 @@ def test_ssd_gated_full_size_sampled_rows(dev):
     gates.check_state(np.stack([h[b, hh, pp] for b, hh, pp in rows]), ho, p.io, "h_last")
 
 
+# Many heads (grids of 768 and more workgroups) with ragged chunk counts:
+# the output workgroups walk chunk pairs, the last pair without a partner
+# where the count is odd; sampled rows, with a gate and from h0.
+SSD_WIDE_CASES = [
+    # batch, L, H, P, N, G, gate, with h0
+    (1, 1300, 384, 64, 64, 4, False, False),   # 6 chunks
+    (2, 1700, 192, 64, 128, 2, True, True),    # 7 chunks: a chunk without a partner
+    (1, 1025, 384, 80, 32, 1, False, True),    # 5 chunks; two head-dim slices
+]
+
+
+@pytest.mark.parametrize("case", SSD_WIDE_CASES)
+def test_ssd_wide_grid_sampled_rows(dev, case):
+    import selective_state_space_05_amd as mssm
+    from selective_state_space_05_amd.api import forced_variant
+    batch, L, H, P, N, G, gate, with_h0 = case
+    announce("ssd wide grid %s" % (case,))
+    p = inputs.SSDProblem("case", batch, L, H, P, N, G, "bf16", 400 + L, gate=gate)
+    s = inputs.ssd_inputs(p)
+    h0 = inputs.initial_state((batch, H, P, N), 3 + N) if with_h0 else None
+    t = ssd_to_dev(s, "bf16", dev)
+    with forced_variant(_lib.VARIANT_SSD_CHUNKED):
+        y, h = mssm.ssd_scalar_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"],
+                                   t["dt_bias"], z=t["z"] if gate else None,
+                                   h0=None if h0 is None else torch.from_numpy(h0).to(dev))
+    torch.cuda.synchronize()
+    y, h = f64(y), f64(h)
+    rng = np.random.default_rng(L)
+    rows = [(0, 0, 0), (batch - 1, H - 1, P - 1)] + [
+        (int(rng.integers(batch)), int(rng.integers(H)), int(rng.integers(P))) for _ in range(8)]
+    yo, ho = oracle.ssd_rows(rows, s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"],
+                             s["dt_bias"], z=s["z"] if gate else None, h0=h0)
+    gates.check(np.stack([y[b, :, hh, pp] for b, hh, pp in rows]), yo, "bf16", "y")
+    gates.check_state(np.stack([h[b, hh, pp] for b, hh, pp in rows]), ho, "bf16", "h_last")
+
+
 # ---------------------------------------------------------------------------
 # decode step
 # ---------------------------------------------------------------------------
