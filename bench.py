@@ -769,7 +769,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--no-probes", action="store_true",
-                    help="skip the copy and ALU peak probes (transcendentals then cost 2 slots)")
+                    help="skip the copy and ALU peak probes (transcendentals then cost 2 slots) "
+                         "and the amd-smi clock snapshots: the profiler passes, whose preloaded "
+                         "library would also attach to amd-smi's own process")
     ap.add_argument("--ramp-s", type=float, default=2.0,
                     help="at most this many seconds of untimed steps before the warmup, until the "
                          "per-launch time settles (0: none)")
@@ -833,7 +835,7 @@ def main():
     rotate = args.rotate or max(1, min(4, -(-(1 << 30) // footprint)))
     sets = [wb.upload() for _ in range(rotate)]
     torch.cuda.synchronize()
-    smi_before = amd_smi_snapshot()
+    smi_before = None if args.no_probes else amd_smi_snapshot()
 
     variant = VARIANTS[args.variant]
     # the library launches on torch's current stream; every event is
@@ -870,7 +872,7 @@ def main():
             ev[i + 1].record(stream)
         torch.cuda.synchronize()
     per_launch = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
-    smi_after = amd_smi_snapshot()
+    smi_after = None if args.no_probes else amd_smi_snapshot()
     ms_step = total_ms / args.steps
     sec = ms_step / 1e3
 
