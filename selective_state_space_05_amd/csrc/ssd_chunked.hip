@@ -835,9 +835,9 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
     const int t0 = c * Q;
     // the walk continues into the pair's second chunk after this one's last block
     const bool cont = cc == 0 && c + 1 < g.nch;
-    // dt first (the decay scan waits for it), then the first three blocks'
-    // rows: block j + 1 is stored to LDS at the end of block j, from the
-    // register set ra (j even) or rb (j odd), which then receives block j + 3
+    // dt first (the decay scan waits for it), then the first two blocks'
+    // rows: block j + 1 is stored to LDS at the end of block j from the
+    // register set ra, which then receives block j + 2
     const int tdt = t0 + (tid < Q ? tid : 0);
     const int64_t dto = b * g.L * static_cast<int64_t>(g.H) + static_cast<int64_t>(tdt < g.L ? tdt : g.L - 1) * g.H + h0;
     float dtr[HPW];
@@ -846,10 +846,9 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
     // Gram quadrant of block 0, then (in flight through each block) of the
     // block after the next
     f4x gq = Gw[static_cast<int64_t>(c * NB) * 192];
-    BlockRegs<NP, true> r0, ra, rb;
+    BlockRegs<NP, true> r0, ra;
     load_block<NP, VEC, true>(r0, q, Bg, Cg, xg, t0, g, rowBC, rowX, pcols);
     if (NB > 1) load_block<NP, VEC, true>(ra, q, Bg, Cg, xg, t0 + 32, g, rowBC, rowX, pcols);
-    if (NB > 2) load_block<NP, VEC, true>(rb, q, Bg, Cg, xg, t0 + 64, g, rowBC, rowX, pcols);
     chunk_decay<Q, HPW>(dtr, t0, g.L, a2, bs, sm.cum, sm.dl, sm.wsum);
 #pragma unroll
     for (int hd = 0; hd < HPW; ++hd)
@@ -1038,11 +1037,11 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
             // the next block into LDS (its buffer was last read in the
             // previous block, before that block's first barrier), then --
             // after every read of this block's decay tiles -- its decay tiles;
-            // rg then receives the rows of block k + 3
+            // rg then receives the rows of block k + 2
             store_block<NP, VEC, true>(rg, q, nmask, sm.st[(k + 1) & 1]);
             __syncthreads();
             if (wave < 3) diag_store<Q, NP, HPW>(sm, mv, wave, lane);
-            if (k + 3 < NB) load_block<NP, VEC, true>(rg, q, Bg, Cg, xg, t0 + base + 96, g, rowBC, rowX, pcols);
+            if (k + 2 < NB) load_block<NP, VEC, true>(rg, q, Bg, Cg, xg, t0 + base + 64, g, rowBC, rowX, pcols);
             if (GATE) load_z(k + 1);
             __syncthreads();
         }
@@ -1051,7 +1050,7 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
 #pragma unroll 1
     for (int k = 0; k < NB; k += 2) {
         step(k, ra);
-        step(k + 1, rb);
+        step(k + 1, ra);
     }
     }
 }
