@@ -431,7 +431,7 @@ struct __align__(16) StateSmem {
 };
 
 template <int Q, int NP, bool VEC, int HPW>
-__global__ __launch_bounds__(256, HPW == 2 ? 3 : (VEC ? 4 : 2)) void ssd_state_kernel(
+__global__ __launch_bounds__(256, VEC ? (HPW == 2 ? 3 : 4) : 2) void ssd_state_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt,
     const float *__restrict__ dt_bias, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, float *__restrict__ S, float *__restrict__ ce, Geom g,
@@ -491,17 +491,16 @@ __global__ __launch_bounds__(256, HPW == 2 ? 3 : (VEC ? 4 : 2)) void ssd_state_k
         if (c >= g.nch) break;
         if (cc > 0) __syncthreads();   // every read of the previous chunk's LDS is done
         const int t0 = c * Q;
-        // dt first, then the first three blocks (register sets as in the
-        // output kernel)
+        // dt first, then the first two blocks (one register set ahead, as in
+        // the output kernel)
         const int tdt = t0 + (tid < Q ? tid : 0);
         const int64_t dto = b * g.L * static_cast<int64_t>(g.H) + static_cast<int64_t>(tdt < g.L ? tdt : g.L - 1) * g.H + h0;
         float dtr[HPW];
 #pragma unroll
         for (int hd = 0; hd < HPW; ++hd) dtr[hd] = bf16_to_f32(dt[dto + hd]);
-        BlockRegs<NP, false> r0, ra, rb;
+        BlockRegs<NP, false> r0, ra;
         load_block<NP, VEC, false>(r0, q, Bg, nullptr, xg, t0, g, rowBC, rowX, pcols);
         if (NB > 1) load_block<NP, VEC, false>(ra, q, Bg, nullptr, xg, t0 + 32, g, rowBC, rowX, pcols);
-        if (NB > 2) load_block<NP, VEC, false>(rb, q, Bg, nullptr, xg, t0 + 64, g, rowBC, rowX, pcols);
         float cum_end[HPW];
         chunk_decay<Q, HPW>(dtr, t0, g.L, a2, bs, sm.cum, sm.dl, sm.wsum);
 #pragma unroll
@@ -558,14 +557,14 @@ __global__ __launch_bounds__(256, HPW == 2 ? 3 : (VEC ? 4 : 2)) void ssd_state_k
                 // previous block, before that block's barrier
                 store_block<NP, VEC, false>(rg, q, nmask, sm.st[(k + 1) & 1]);
                 __syncthreads();
-                if (k + 3 < NB)
-                    load_block<NP, VEC, false>(rg, q, Bg, nullptr, xg, t0 + base + 96, g, rowBC, rowX, pcols);
+                if (k + 2 < NB)
+                    load_block<NP, VEC, false>(rg, q, Bg, nullptr, xg, t0 + base + 64, g, rowBC, rowX, pcols);
             }
         };
 #pragma unroll 1
         for (int k = 0; k < NB; k += 2) {
             step(k, ra);
-            step(k + 1, rb);
+            step(k + 1, ra);
         }
     }
     // the pair's aggregate (a last chunk without a partner: its own state)
