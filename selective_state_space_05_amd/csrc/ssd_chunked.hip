@@ -595,15 +595,18 @@ __global__ __launch_bounds__(256, VEC ? (HPW == 2 ? 3 : 4) : 2) void ssd_state_k
 }
 
 // ---------------------------------------------------------------------------
-// 2. state pass over chunk pairs: slot m <- state entering chunk 2 m;
+// 2. state pass over chunk pairs: slot j <- state entering chunk 2 GSZ j;
 //    h_last <- final state
 // ---------------------------------------------------------------------------
 // Slot m holds the aggregate of chunks 2 m and 2 m + 1,
 // 2^(e_{2m+1}) S_{2m} + S_{2m+1} (e: a chunk's total log2 decay, S: its state
 // from zero; a last chunk without a partner: its own S), and ce[m] the pair's
 // total decay, so one fused multiply-add per pair, h <- 2^(ce[m]) h + slot,
-// carries the state across two chunks.  The output kernel walks both chunks
-// of a pair from the state entering the first.
+// carries the state across two chunks.  The output kernel walks GSZ pairs
+// (GSZ = 1 or 2) from the state entering the first, so only every GSZ-th
+// entering state is stored, into slot m / GSZ (a slot already read: the
+// aggregates are read ahead of the stores).
+template <int GSZ>
 __global__ __launch_bounds__(256) void ssd_pass_kernel(float *__restrict__ S,
                                                        const float *__restrict__ ce,
                                                        const float *h0, float *h_last, Geom g,
@@ -619,24 +622,22 @@ __global__ __launch_bounds__(256) void ssd_pass_kernel(float *__restrict__ S,
     int m = 0;
     for (; m + U <= npair; m += U) {
         float s[U], a[U];
-        int64_t idx[U];
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             const int64_t bc = (b * npair + m + k) * g.H + hh;
-            idx[k] = bc * PN + e;
-            s[k] = S[idx[k]];
+            s[k] = S[bc * PN + e];
             a[k] = fast_exp2(ce[bc]);
         }
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            S[idx[k]] = h;
+            if ((m + k) % GSZ == 0) S[((b * npair + (m + k) / GSZ) * g.H + hh) * PN + e] = h;
             h = fmaf(a[k], h, s[k]);
         }
     }
     for (; m < npair; ++m) {
         const int64_t bc = (b * npair + m) * g.H + hh;
         const float s = S[bc * PN + e];
-        S[bc * PN + e] = h;
+        if (m % GSZ == 0) S[((b * npair + m / GSZ) * g.H + hh) * PN + e] = h;
         h = fmaf(fast_exp2(ce[bc]), h, s);
     }
     if (h_last) h_last[bh * PN + e] = h;
@@ -731,7 +732,7 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
     const float *__restrict__ dt_bias, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm,
     const float *__restrict__ Dskip, const uint16_t *__restrict__ z, const float *__restrict__ Hin,
-    const f4x *__restrict__ Gm, uint16_t *__restrict__ y, Geom g) {
+    const f4x *__restrict__ Gm, uint16_t *__restrict__ y, Geom g, int cpw) {
     constexpr int NB = Q / 32;          // blocks per chunk
     constexpr int NJ = NP / 16;         // 16-wide state tiles
     constexpr int KK = NP / 32;         // K steps over the state index
@@ -747,9 +748,9 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
     id /= g.npg;
     const int h0 = static_cast<int>(id % (g.H / HPW)) * HPW;
     id /= g.H / HPW;
-    const int npair = (g.nch + 1) / 2;
-    const int m = static_cast<int>(id % npair);      // chunks 2 m and 2 m + 1
-    const int64_t b = id / npair;
+    const int npair = (g.nch + 1) / 2, ngrp = (g.nch + cpw - 1) / cpw;
+    const int m = static_cast<int>(id % ngrp);       // chunks cpw m .. cpw m + cpw - 1
+    const int64_t b = id / ngrp;
     const int pbase = pg * kPG, pcols = g.P - pbase;
     const int rowX = g.H * g.P, rowBC = g.G * g.N;
     const int grp = h0 / (g.H / g.G);
@@ -767,7 +768,7 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
 #pragma unroll
     for (int hd = 0; hd < HPW; ++hd) skip[hd] = Dskip ? Dskip[h0 + hd] : 0.0f;
 
-    // the state entering chunk 2 m, from the pass
+    // the state entering chunk cpw m, from the pass (slot m)
     f4x H[HPW][NJ];
     const int64_t PNs = static_cast<int64_t>(g.P) * g.N;
 #pragma unroll
@@ -827,13 +828,13 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
     const f4x *Gw = Gm + ((b * g.G + grp) * static_cast<int64_t>(g.nch) * NB * 3 + (wave < 3 ? wave : 0)) * 64 + lane;
 
 #pragma unroll 1
-    for (int cc = 0; cc < 2; ++cc) {
-    const int c = 2 * m + cc;
+    for (int cc = 0; cc < cpw; ++cc) {
+    const int c = cpw * m + cc;
     if (c >= g.nch) break;
-    if (cc > 0) __syncthreads();   // every read of the first chunk's LDS is done
+    if (cc > 0) __syncthreads();   // every read of the previous chunk's LDS is done
     const int t0 = c * Q;
-    // the walk continues into the pair's second chunk after this one's last block
-    const bool cont = cc == 0 && c + 1 < g.nch;
+    // the walk continues into the next chunk after this one's last block
+    const bool cont = cc + 1 < cpw && c + 1 < g.nch;
     // dt first (the decay scan waits for it), then the first two blocks'
     // rows: block j + 1 is stored to LDS at the end of block j from the
     // register set ra, which then receives block j + 2
@@ -1096,6 +1097,10 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     // each group's head count is even
     const bool pairs = (a.H / a.G) % 2 == 0;
     const int64_t npair = (g.nch + 1) / 2;
+    // chunks per output workgroup: four where that still gives at least
+    // three workgroups per compute unit of a 256-CU device (half the
+    // entering states stored and read), else two
+    const int cpw = a.batch * ((g.nch + 3) / 4) * a.H * g.npg >= 768 ? 4 : 2;
     // the state workgroups, then those of the Gram quadrants (four each)
     const int nstate = static_cast<int>(a.batch * npair * (pairs ? a.H / 2 : a.H) * g.npg);
     const int ntask = static_cast<int>(a.batch * a.G * nblk * 3);
@@ -1115,18 +1120,21 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     e = hipGetLastError();
     if (e == hipSuccess) {
         const int bph = static_cast<int>((PN + 255) / 256);
-        hipLaunchKernelGGL(ssd_pass_kernel, dim3(static_cast<uint32_t>(a.batch * a.H * bph)),
-                           dim3(256), 0, stream, S, ce, a.h0, a.h_last, g, bph);
+        const dim3 pgrid(static_cast<uint32_t>(a.batch * a.H * bph));
+        if (cpw == 4)
+            hipLaunchKernelGGL(ssd_pass_kernel<2>, pgrid, dim3(256), 0, stream, S, ce, a.h0, a.h_last, g, bph);
+        else
+            hipLaunchKernelGGL(ssd_pass_kernel<1>, pgrid, dim3(256), 0, stream, S, ce, a.h0, a.h_last, g, bph);
         e = hipGetLastError();
     }
     if (e == hipSuccess) {
-        // one head and both chunks of a pair per workgroup
+        // one head and cpw consecutive chunks per workgroup
         decltype(&ssd_output_kernel<Q, NP, true, true, 1>) kern;
         if (zz) kern = vec ? ssd_output_kernel<Q, NP, true, true, 1> : ssd_output_kernel<Q, NP, false, true, 1>;
         else kern = vec ? ssd_output_kernel<Q, NP, true, false, 1> : ssd_output_kernel<Q, NP, false, false, 1>;
-        const dim3 ogrid(static_cast<uint32_t>(a.batch * npair * a.H * g.npg));
+        const dim3 ogrid(static_cast<uint32_t>(a.batch * ((g.nch + cpw - 1) / cpw) * a.H * g.npg));
         hipLaunchKernelGGL(kern, ogrid, dim3(256), 0, stream, x, dt, a.dt_bias, a.A, B, C, a.D, zz, S, Gq,
-                           static_cast<uint16_t *>(a.y), g);
+                           static_cast<uint16_t *>(a.y), g, cpw);
         e = hipGetLastError();
     }
     const hipError_t ef = scratch_free(mem, stream);
