@@ -912,6 +912,10 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
         // output: Y^T = Hs_k C^T (state part; one head: hi and lo parts of Hs_k
         // in chains of their own) and the diagonal tile's x^T M^T
         constexpr int YC = HPW == 1 ? 2 : 1;
+        // the block's products at raised wave priority (back to normal for
+        // the outputs and the staging): a wave that reaches them issues
+        // first, so its matrix-core work overlaps the other waves' vector work
+        __builtin_amdgcn_s_setprio(1);
         f4x ys[HPW][2][YC], yd[HPW][2];
 #pragma unroll
         for (int hd = 0; hd < HPW; ++hd)
@@ -994,6 +998,7 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
                 }
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         // the next block's decay tile values (stored after this block's
         // reads of M), then the Gram quadrant of the block after it; past
         // the chunk's last block both are formed from in-range indices and
