@@ -28,19 +28,19 @@
 //      which depend on the group only;
 //   2. ssd_pass_kernel: walks the pairs of each (batch, head) in order,
 //      elementwise over the P x N state and starting from the initial state
-//      (zero unless given), replacing each pair's state by the state entering
-//      its first chunk and writing h_last;
-//   3. ssd_output_kernel: the outputs, walking the 32-step blocks of both
-//      chunks of a pair from the state entering the first, with the state
-//      carried in matrix-core accumulators; within a block the outputs come
-//      from the state entering it and the block's own 32 x 32 decay-masked
-//      C B^T tile (the Gram products scaled by the decays).
-// A pair rather than a single chunk per workgroup halves the chunk states
-// written, passed and read again.  Both walks give each workgroup a pair of
-// chunks of one batch and a 64-column slice of the head dimension, and each
-// of its four waves 16 columns, and stage a block's B, C and x in LDS
-// (transposed where a product contracts over the steps) while the next
-// blocks' rows are in flight.
+//      (zero unless given), storing the state entering every pair (or every
+//      other pair) over the aggregates already read, and writing h_last;
+//   3. ssd_output_kernel: the outputs, walking the 32-step blocks of two or
+//      four consecutive chunks from the state entering the first, with the
+//      state carried in matrix-core accumulators; within a block the outputs
+//      come from the state entering it and the block's own 32 x 32
+//      decay-masked C B^T tile (the Gram products scaled by the decays).
+// Two or four chunks rather than one per workgroup halve (or quarter) the
+// chunk states written, passed and read again.  Both walks give each
+// workgroup a 64-column slice of the head dimension and each of its four
+// waves 16 columns, and stage a block's B, C and x in LDS (transposed where
+// a product contracts over the steps) while the next block's rows are in
+// flight.
 // Products whose operands are not exact bf16 values (x * weight, the masked
 // decay tile, the carried state) use a two-term bf16 split (hi + lo), so each
 // product carries about 16 significant bits; accumulation is float32.
@@ -719,11 +719,11 @@ __device__ __forceinline__ void diag_store(OutSmem<Q, NP, HPW> &sm, const uint4 
     }
 }
 
-// Both chunks of a pair per workgroup: the walk over the first ends holding
-// the state entering the second, so only the pair's entering state is read.
-// HPW heads of one B / C group per workgroup (the launcher takes one, so
-// that the layer's pairs and heads fill the chip in whole rounds; two would
-// share the block's staged B and C, its C . B quadrants and every B and C
+// cpw (2 or 4) consecutive chunks per workgroup: the walk over one chunk
+// ends holding the state entering the next, so only the state entering the
+// first is read.  HPW heads of one B / C group per workgroup (the launcher
+// takes one, so that the layer's chunk groups and heads fill the chip in
+// whole rounds; two would share the block's staged B and C and every B and C
 // operand read).  Workgroups per compute unit: three for one head on the
 // vector path without a gate (LDS and registers allow it), two otherwise.
 template <int Q, int NP, bool VEC, bool GATE, int HPW>
