@@ -915,6 +915,13 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
         // the block's products at raised wave priority (back to normal for
         // the outputs and the staging): a wave that reaches them issues
         // first, so its matrix-core work overlaps the other waves' vector work
+        // the next block into LDS first (its buffer was last read in the
+        // previous block, before that block's barriers), so that the writes
+        // overlap this block's products; rg then receives block k + 2
+        if (k + 1 < NB) {
+            store_block<NP, VEC, true>(rg, q, nmask, sm.st[(k + 1) & 1]);
+            if (k + 2 < NB) load_block<NP, VEC, true>(rg, q, Bg, Cg, xg, t0 + base + 64, g, rowBC, rowX, pcols);
+        }
         __builtin_amdgcn_s_setprio(1);
         f4x ys[HPW][2][YC], yd[HPW][2];
 #pragma unroll
@@ -1039,14 +1046,10 @@ __global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_o
                 }
             }
         if (k + 1 < NB) {
-            // the next block into LDS (its buffer was last read in the
-            // previous block, before that block's first barrier), then --
-            // after every read of this block's decay tiles -- its decay tiles;
-            // rg then receives the rows of block k + 2
-            store_block<NP, VEC, true>(rg, q, nmask, sm.st[(k + 1) & 1]);
+            // the next block's decay tiles, after every read of this block's
+            // (the first barrier also publishes the next block's rows)
             __syncthreads();
             if (wave < 3) diag_store<Q, NP, HPW>(sm, mv, wave, lane);
-            if (k + 2 < NB) load_block<NP, VEC, true>(rg, q, Bg, Cg, xg, t0 + base + 64, g, rowBC, rowX, pcols);
             if (GATE) load_z(k + 1);
             __syncthreads();
         }
