@@ -364,6 +364,20 @@ def test_ssd_validation(L, kw, status):
     assert L.mssm_last_error()
 
 
+def test_ssd_chunked_refuses_grids_past_its_limit(L):
+    """The matrix-core SSD form launches one workgroup of 256 work-items per
+    (batch, chunk pair, head, 64-column slice); a grid of 2^24 or more such
+    workgroups would pass 2^32 work-items, so the forced variant refuses the
+    shape before any launch (here 2^15 x 1 x 1024 x 1 workgroups)."""
+    prev = L.mssm_force_variant(_lib.VARIANT_SSD_CHUNKED)
+    try:
+        st = ssd_call(L, batch=1 << 15, seqlen=64, H=1024, P=8, N=16, io=1)
+    finally:
+        L.mssm_force_variant(prev)
+    assert st == _lib.MSSM_ERR_UNSUPPORTED
+    assert b"variant" in L.mssm_last_error()
+
+
 def test_ssd_output_aliasing(L):
     assert ssd_call(L, y=fake(20), x=fake(20) + 2) == _lib.MSSM_ERR_INVALID_ARG
     assert ssd_call(L, h_last=fake(20), B=fake(20) + 4) == _lib.MSSM_ERR_INVALID_ARG
