@@ -1107,8 +1107,11 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     const int64_t npair = (g.nch + 1) / 2;
     // chunks per output workgroup: four where that still gives at least
     // three workgroups per compute unit of a 256-CU device (half the
-    // entering states stored and read), else two
-    const int cpw = a.batch * ((g.nch + 3) / 4) * a.H * g.npg >= 768 ? 4 : 2;
+    // entering states stored and read), else two.  Only the vector path
+    // without a gate runs three output workgroups per CU; the others run two,
+    // where four-chunk walks would leave a half-filled last round.
+    const bool three_per_cu = vec && a.z == nullptr;
+    const int cpw = three_per_cu && a.batch * ((g.nch + 3) / 4) * a.H * g.npg >= 768 ? 4 : 2;
     // the state workgroups, then those of the Gram quadrants (four each)
     const int nstate = static_cast<int>(a.batch * npair * (pairs ? a.H / 2 : a.H) * g.npg);
     const int ntask = static_cast<int>(a.batch * a.G * nblk * 3);
