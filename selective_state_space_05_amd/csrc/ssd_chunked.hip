@@ -725,9 +725,9 @@ __device__ __forceinline__ void diag_store(OutSmem<Q, NP, HPW> &sm, const uint4 
 // takes one, so that the layer's chunk groups and heads fill the chip in
 // whole rounds; two would share the block's staged B and C and every B and C
 // operand read).  Workgroups per compute unit: three for one head on the
-// vector path without a gate (LDS and registers allow it), two otherwise.
+// vector path, gated or not (LDS and registers allow it), two otherwise.
 template <int Q, int NP, bool VEC, bool GATE, int HPW>
-__global__ __launch_bounds__(256, (HPW == 1 && VEC && !GATE) ? 3 : 2) void ssd_output_kernel(
+__global__ __launch_bounds__(256, (HPW == 1 && VEC) ? 3 : 2) void ssd_output_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ dt,
     const float *__restrict__ dt_bias, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm,
@@ -1108,9 +1108,9 @@ hipError_t launch_typed(const SSDArgs &a, hipStream_t stream) {
     // chunks per output workgroup: four where that still gives at least
     // three workgroups per compute unit of a 256-CU device (half the
     // entering states stored and read), else two.  Only the vector path
-    // without a gate runs three output workgroups per CU; the others run two,
-    // where four-chunk walks would leave a half-filled last round.
-    const bool three_per_cu = vec && a.z == nullptr;
+    // runs three output workgroups per CU; the element path runs two, where
+    // four-chunk walks would leave a half-filled last round.
+    const bool three_per_cu = vec;
     const int cpw = three_per_cu && a.batch * ((g.nch + 3) / 4) * a.H * g.npg >= 768 ? 4 : 2;
     // the state workgroups, then those of the Gram quadrants (four each)
     const int nstate = static_cast<int>(a.batch * npair * (pairs ? a.H / 2 : a.H) * g.npg);
